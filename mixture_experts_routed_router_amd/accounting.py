@@ -1,0 +1,71 @@
+"""Algorithmic work of each step of the routed-expert layer: the flops and HBM
+bytes the method itself needs, used to place measured kernel times on the
+MI355X roofline.
+
+Flops count routed rows only: 2 flops per multiply-add, so the two expert GEMMs
+are 4*R*H*I (gate and up) and 2*R*H*I (down), 6*R*H*I in all -- twice the active
+expert parameters per routed token, the 6*N*D forward-and-backward rule's
+forward third [prime-rl PR 3885, Pipeline-parallel push: MFU is 6ND].  Pad rows
+of the layout are not counted as flops.
+
+Bytes count each buffer once at its algorithmic size: every active expert's
+weights read once (an expert with no rows reads none [PocketLLM "Qwen4-Exp
+Heterogeneous TP4 Performance", Confirmed architecture decisions: active-only
+traffic]), the activation buffers each written once and read once, the index
+maps once.  P below is the number of rows actually used by the padded layout
+(offsets[E]); it includes pad rows because they are written and read.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+# MI355X published peaks (dense, no sparsity).
+PEAK_HBM_BYTES_PER_S = 8.0e12
+PEAK_BF16_FLOPS = 2.5e15
+
+
+@dataclass(frozen=True)
+class StepWork:
+    name: str
+    flops: float
+    bytes: float
+
+    def roofline_seconds(self, peak_flops=PEAK_BF16_FLOPS, peak_bw=PEAK_HBM_BYTES_PER_S) -> float:
+        return max(self.flops / peak_flops, self.bytes / peak_bw)
+
+    def bound(self, peak_flops=PEAK_BF16_FLOPS, peak_bw=PEAK_HBM_BYTES_PER_S) -> str:
+        return "mfma" if self.flops / peak_flops >= self.bytes / peak_bw else "hbm"
+
+
+def layer_flops(T: int, H: int, k: int, I: int) -> float:
+    """Forward flops of the routed experts: 6 * T * k * H * I."""
+    return 6.0 * T * k * H * I
+
+
+def step_work(T: int, H: int, E: int, k: int, I: int, P: int, active_experts: int):
+    """Per-step algorithmic work for one layer call (list of StepWork, path order)."""
+    R = T * k
+    bf, i32, f32 = 2, 4, 4
+    route = StepWork("route_topk", 0.0, T * E * f32 + R * (i32 + f32))
+    permute = StepWork(
+        "permute",
+        0.0,
+        R * i32            # topk_idx read
+        + T * H * bf       # x read once
+        + P * H * bf       # x_perm written, pad rows included
+        + R * i32          # route_row written
+        + P * i32          # row_token written
+        + (2 * E + 1) * i32,
+    )
+    glu = StepWork(
+        "grouped_glu_gemm",
+        4.0 * R * H * I,
+        active_experts * 2 * I * H * bf + P * H * bf + P * I * bf + (2 * E + 1) * i32,
+    )
+    down = StepWork(
+        "grouped_down_gemm",
+        2.0 * R * H * I,
+        active_experts * H * I * bf + P * I * bf + P * H * bf + (2 * E + 1) * i32,
+    )
+    combine = StepWork("combine", 0.0, R * H * bf + R * (i32 + f32) + T * H * bf)
+    return [route, permute, glu, down, combine]

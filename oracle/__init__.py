@@ -1,0 +1,225 @@
+"""CPU oracle for the routed-expert MoE forward path -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package. The GPU library never loads it, and the
+two share no code: this is a plain C implementation (``moe_oracle.c``) built
+with gcc, wrapped here with numpy arrays.
+
+Every function follows the page passage cited in ``moe_oracle.c``:
+routing [PocketLLM "Qwen4-Exp Heterogeneous TP4 Performance", Runtime
+architecture], layout and combine [prime-rl PR 3885, Changes: single-pass local
+layout], grouped experts [Halo "Performance", Levers that help].
+
+All floating-point results are float64 and exact up to rounding order: bf16
+inputs are widened exactly and nothing in the chain is rounded.
+
+Pins: each function is checked by ``tests/test_oracle_pins.py`` against brute
+force, closed forms and invariants that do not reuse this code.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+from .build import build_oracle, build_variant, library_path
+
+_LIB = None
+
+_i32p = ctypes.POINTER(ctypes.c_int32)
+_i64p = ctypes.POINTER(ctypes.c_int64)
+_u16p = ctypes.POINTER(ctypes.c_uint16)
+_f32p = ctypes.POINTER(ctypes.c_float)
+_f64p = ctypes.POINTER(ctypes.c_double)
+
+_ERRORS = {-1: "invalid argument", -2: "non-finite logit", -3: "index out of range"}
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def _load(path: str):
+    lib = ctypes.CDLL(path)
+    i64, i32 = ctypes.c_int64, ctypes.c_int32
+    lib.moe_oracle_route_topk.argtypes = [_f32p, i64, i32, i32, _i32p, _f64p]
+    lib.moe_oracle_layout.argtypes = [_i32p, i64, i32, i32, i32, i64, _i32p, _i32p, _i32p, _i32p]
+    lib.moe_oracle_gather.argtypes = [_u16p, _i32p, i64, i64, i32, _u16p]
+    lib.moe_oracle_glu.argtypes = [_u16p, _u16p, _i32p, _i32p, i32, i32, i32, _f64p]
+    lib.moe_oracle_down.argtypes = [_f64p, _u16p, _i32p, _i32p, i32, i32, i32, _f64p]
+    lib.moe_oracle_combine.argtypes = [_f64p, _i32p, _f64p, i64, i32, i32, i64, _f64p]
+    lib.moe_oracle_forward.argtypes = [_u16p, _f32p, _u16p, _u16p, i64, i32, i32, i32, i32,
+                                       _i64p, i64, _f64p]
+    for name in ("moe_oracle_route_topk", "moe_oracle_layout", "moe_oracle_gather",
+                 "moe_oracle_glu", "moe_oracle_down", "moe_oracle_combine",
+                 "moe_oracle_forward"):
+        getattr(lib, name).restype = ctypes.c_int
+    return lib
+
+
+def _lib():
+    global _LIB
+    if _LIB is None:
+        path = library_path()
+        if not os.path.exists(path):
+            build_oracle()
+        _LIB = _load(path)
+    return _LIB
+
+
+def _p(a: np.ndarray, ptype):
+    assert a.flags["C_CONTIGUOUS"], "oracle arrays must be C-contiguous"
+    return a.ctypes.data_as(ptype)
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        raise OracleError(f"{what}: {_ERRORS.get(rc, rc)}")
+
+
+def _u16(a) -> np.ndarray:
+    a = np.ascontiguousarray(a)
+    if a.dtype != np.uint16:
+        raise TypeError("bf16 tensors are passed as their raw uint16 bits")
+    return a
+
+
+def route_topk(logits: np.ndarray, k: int, lib=None):
+    """Top-k expert ids (int32 [T,k]) and softmax-over-selected weights (float64 [T,k])."""
+    logits = np.ascontiguousarray(logits, dtype=np.float32)
+    T, E = logits.shape
+    idx = np.empty((T, k), np.int32)
+    w = np.empty((T, k), np.float64)
+    _check((lib or _lib()).moe_oracle_route_topk(_p(logits, _f32p), T, E, k, _p(idx, _i32p),
+                                        _p(w, _f64p)), "route_topk")
+    return idx, w
+
+
+def padded_rows_max(T: int, k: int, E: int, align: int) -> int:
+    """Rows the padded layout can need: every route plus at most align-1 pad rows per expert."""
+    return T * k + E * (align - 1)
+
+
+def layout(topk_idx: np.ndarray, E: int, align: int, P_max: int | None = None, lib=None):
+    """counts[E], offsets[E+1], route_row[T*k], row_token[P_max] (all int32)."""
+    topk_idx = np.ascontiguousarray(topk_idx, dtype=np.int32)
+    T, k = topk_idx.shape
+    if P_max is None:
+        P_max = padded_rows_max(T, k, E, align)
+    counts = np.empty(E, np.int32)
+    offsets = np.empty(E + 1, np.int32)
+    route_row = np.empty(T * k, np.int32)
+    row_token = np.empty(P_max, np.int32)
+    _check((lib or _lib()).moe_oracle_layout(_p(topk_idx, _i32p), T, k, E, align, P_max,
+                                    _p(counts, _i32p), _p(offsets, _i32p),
+                                    _p(route_row, _i32p), _p(row_token, _i32p)), "layout")
+    return counts, offsets, route_row, row_token
+
+
+def gather(x_bits: np.ndarray, row_token: np.ndarray, rows: int | None = None, lib=None) -> np.ndarray:
+    """x_perm bits [rows, H]: token rows copied bit for bit, zero rows where row_token is -1."""
+    x_bits = _u16(x_bits)
+    row_token = np.ascontiguousarray(row_token, dtype=np.int32)
+    T, H = x_bits.shape
+    if rows is None:
+        rows = row_token.shape[0]
+    out = np.empty((rows, H), np.uint16)
+    _check((lib or _lib()).moe_oracle_gather(_p(x_bits, _u16p), _p(row_token, _i32p), T, rows, H,
+                                    _p(out, _u16p)), "gather")
+    return out
+
+
+def glu(x_perm_bits, w_gu_bits, counts, offsets, I: int, lib=None) -> np.ndarray:
+    """h (float64 [rows, I]) = silu(x W_gate^T) * (x W_up^T) on every valid row; other rows NaN."""
+    x_perm_bits = _u16(x_perm_bits)
+    w_gu_bits = _u16(w_gu_bits)
+    counts = np.ascontiguousarray(counts, dtype=np.int32)
+    offsets = np.ascontiguousarray(offsets, dtype=np.int32)
+    rows, H = x_perm_bits.shape
+    E = counts.shape[0]
+    assert w_gu_bits.shape == (E, 2 * I, H)
+    h = np.full((rows, I), np.nan)
+    _check((lib or _lib()).moe_oracle_glu(_p(x_perm_bits, _u16p), _p(w_gu_bits, _u16p),
+                                 _p(counts, _i32p), _p(offsets, _i32p), E, H, I,
+                                 _p(h, _f64p)), "glu")
+    return h
+
+
+def down(h: np.ndarray, w_d_bits, counts, offsets, lib=None) -> np.ndarray:
+    """y (float64 [rows, H]) = h W_down^T on every valid row; other rows NaN."""
+    h = np.ascontiguousarray(h, dtype=np.float64)
+    w_d_bits = _u16(w_d_bits)
+    counts = np.ascontiguousarray(counts, dtype=np.int32)
+    offsets = np.ascontiguousarray(offsets, dtype=np.int32)
+    rows, I = h.shape
+    E, H, I2 = w_d_bits.shape
+    assert I2 == I and counts.shape[0] == E
+    y = np.full((rows, H), np.nan)
+    _check((lib or _lib()).moe_oracle_down(_p(h, _f64p), _p(w_d_bits, _u16p), _p(counts, _i32p),
+                                  _p(offsets, _i32p), E, H, I, _p(y, _f64p)), "down")
+    return y
+
+
+def combine(y: np.ndarray, route_row, topk_w, lib=None) -> np.ndarray:
+    """out (float64 [T, H]) = sum_j w[t,j] * y[route_row[t*k+j]]."""
+    y = np.ascontiguousarray(y, dtype=np.float64)
+    topk_w = np.ascontiguousarray(topk_w, dtype=np.float64)
+    route_row = np.ascontiguousarray(route_row, dtype=np.int32).reshape(-1)
+    T, k = topk_w.shape
+    P_max, H = y.shape
+    out = np.empty((T, H), np.float64)
+    _check((lib or _lib()).moe_oracle_combine(_p(y, _f64p), _p(route_row, _i32p), _p(topk_w, _f64p),
+                                     T, H, k, P_max, _p(out, _f64p)), "combine")
+    return out
+
+
+def forward(x_bits, logits, w_gu_bits, w_d_bits, k: int, tokens=None, lib=None) -> np.ndarray:
+    """The whole layer as a per-token loop; out float64 [len(tokens) or T, H]."""
+    x_bits = _u16(x_bits)
+    logits = np.ascontiguousarray(logits, dtype=np.float32)
+    w_gu_bits = _u16(w_gu_bits)
+    w_d_bits = _u16(w_d_bits)
+    T, H = x_bits.shape
+    E, two_i, H2 = w_gu_bits.shape
+    I = two_i // 2
+    assert H2 == H and logits.shape == (T, E) and w_d_bits.shape == (E, H, I)
+    if tokens is None:
+        tok_p, n = None, T
+    else:
+        tokens = np.ascontiguousarray(tokens, dtype=np.int64)
+        tok_p, n = _p(tokens, _i64p), tokens.shape[0]
+    out = np.empty((n, H), np.float64)
+    _check((lib or _lib()).moe_oracle_forward(_p(x_bits, _u16p), _p(logits, _f32p), _p(w_gu_bits, _u16p),
+                                     _p(w_d_bits, _u16p), T, H, E, k, I, tok_p, n,
+                                     _p(out, _f64p)), "forward")
+    return out
+
+
+class Oracle:
+    """The oracle's functions bound to one built library (the default build, or
+    a variant that a test compiled from an edited copy of the source)."""
+
+    def __init__(self, path: str | None = None):
+        self.lib = _lib() if path is None else _load(path)
+
+    def route_topk(self, *a, **kw):
+        return route_topk(*a, lib=self.lib, **kw)
+
+    def layout(self, *a, **kw):
+        return layout(*a, lib=self.lib, **kw)
+
+    def gather(self, *a, **kw):
+        return gather(*a, lib=self.lib, **kw)
+
+    def glu(self, *a, **kw):
+        return glu(*a, lib=self.lib, **kw)
+
+    def down(self, *a, **kw):
+        return down(*a, lib=self.lib, **kw)
+
+    def combine(self, *a, **kw):
+        return combine(*a, lib=self.lib, **kw)
+
+    def forward(self, *a, **kw):
+        return forward(*a, lib=self.lib, **kw)

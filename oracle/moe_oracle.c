@@ -1,0 +1,305 @@
+/*
+ * moe_oracle.c -- TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, obviously correct CPU implementation of the routed-expert
+ * forward path of a Mixture-of-Experts layer. Only the test suite, the smoke
+ * check and the bench's CPU-baseline leg may load it; the product path never
+ * does, and this file shares no code, header or constant with the GPU library.
+ *
+ * Sources (page title, section):
+ *   [Halo]      Halo, "Performance": Levers that help; Levers that do not help here
+ *   [PocketLLM] "Qwen4-Exp Heterogeneous TP4 Performance": Runtime architecture;
+ *               Decode ceiling
+ *   [prime-rl]  prime-rl pull request 3885 (DeepSeek-V4.1 Flash performance work):
+ *               Changes; Known numerics
+ *
+ * What is computed, for T tokens of hidden size H, E experts, top-k routing and
+ * expert intermediate size I (all tensors row-major):
+ *   routing   per token, the k experts with the largest router logits, and their
+ *             weights = softmax over those k logits;
+ *   layout    a padded, expert-grouped row layout of the routed tokens, built by a
+ *             stable counting sort of the flat routes r = t*k + j;
+ *   experts   per routed row, h = silu(x W_gate^T) * (x W_up^T) and y = h W_down^T;
+ *   combine   per token, the score-weighted sum of its k expert outputs, gathered.
+ *
+ * Precision: bf16 inputs are widened exactly; all arithmetic is in double and
+ * no intermediate is rounded, so these functions give the exact value that the
+ * GPU path reaches with bf16 storage and fp32 accumulation. Sums run in plain
+ * ascending index order.
+ *
+ * Every function returns 0 on success and a negative code on invalid
+ * arguments (nothing is written then).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_EINVAL (-1)
+#define ORACLE_ENONFINITE (-2)
+#define ORACLE_ERANGE (-3)
+
+/* bf16 -> double: a bf16 value is the top 16 bits of an IEEE binary32. */
+static double bf(uint16_t b) {
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* silu(g) = g * sigmoid(g) = g / (1 + exp(-g)).  SwiGLU is silu(gate) * up
+ * [prime-rl, Changes: fused FP8 shared expert -- gate and up projections feed
+ * a SwiGLU whose output is the down projection's input]. */
+static double silu(double g) { return g / (1.0 + exp(-g)); }
+
+/* "a is ranked before b" in the routing order: larger logit first, and on an
+ * exact tie (float ==, so -0 == +0) the lower expert id first. */
+static int ranks_before(float la, int32_t a, float lb, int32_t b) {
+    if (la > lb) return 1;
+    if (la < lb) return 0;
+    return a < b;
+}
+
+/*
+ * Top-k routing [PocketLLM, Runtime architecture: 512 routed experts with
+ * top-10 routing; prime-rl, Changes: top-k weights feed a score-weighted sum].
+ * Per token t: k passes, each picking the best expert not yet picked; then
+ * w[t,j] = exp(L_j - L_0) / sum_i exp(L_i - L_0) over the k picks (softmax over
+ * the selected logits; L_0 is the largest, so every exponent is <= 0).
+ * Logits must be finite.
+ */
+int moe_oracle_route_topk(const float *logits, int64_t T, int32_t E, int32_t k,
+                          int32_t *topk_idx, double *topk_w) {
+    if (!logits || !topk_idx || !topk_w || T < 0 || E < 1 || k < 1 || k > E)
+        return ORACLE_EINVAL;
+    for (int64_t i = 0; i < T * (int64_t)E; ++i)
+        if (!isfinite(logits[i])) return ORACLE_ENONFINITE;
+    char *taken = (char *)malloc((size_t)E);
+    if (!taken) return ORACLE_EINVAL;
+    for (int64_t t = 0; t < T; ++t) {
+        const float *L = logits + t * (int64_t)E;
+        memset(taken, 0, (size_t)E);
+        for (int32_t j = 0; j < k; ++j) {
+            int32_t best = -1;
+            for (int32_t e = 0; e < E; ++e) {
+                if (taken[e]) continue;
+                if (best < 0 || ranks_before(L[e], e, L[best], best)) best = e;
+            }
+            taken[best] = 1;
+            topk_idx[t * k + j] = best;
+        }
+        double m = (double)L[topk_idx[t * k]];
+        double s = 0.0;
+        for (int32_t j = 0; j < k; ++j) s += exp((double)L[topk_idx[t * k + j]] - m);
+        for (int32_t j = 0; j < k; ++j)
+            topk_w[t * k + j] = exp((double)L[topk_idx[t * k + j]] - m) / s;
+    }
+    free(taken);
+    return 0;
+}
+
+/*
+ * Padded expert-grouped layout [prime-rl, Changes: single-pass local layout --
+ * one gather into the padded expert-grouped layout; Halo, Levers that help:
+ * the atomic-free expert permute].
+ *   counts[e]      number of routes r with topk_idx[r] == e
+ *   offsets[0]     0
+ *   offsets[e+1]   offsets[e] + counts[e] rounded up to a multiple of align
+ *   route_row[r]   the row of route r: routes of expert e fill rows
+ *                  offsets[e], offsets[e]+1, ... in ascending r (a stable sort)
+ *   row_token[p]   r / k for the row p = route_row[r]; -1 on every other row
+ *                  in [0, P_max)
+ * Requires every topk_idx in [0, E) and offsets[E] <= P_max < 2^31.
+ */
+int moe_oracle_layout(const int32_t *topk_idx, int64_t T, int32_t k, int32_t E,
+                      int32_t align, int64_t P_max, int32_t *counts, int32_t *offsets,
+                      int32_t *route_row, int32_t *row_token) {
+    if (!topk_idx || !counts || !offsets || !route_row || !row_token || T < 0 ||
+        k < 1 || E < 1 || align < 1 || P_max < 0 || P_max >= ((int64_t)1 << 31))
+        return ORACLE_EINVAL;
+    const int64_t R = T * (int64_t)k;
+    for (int64_t r = 0; r < R; ++r)
+        if (topk_idx[r] < 0 || topk_idx[r] >= E) return ORACLE_ERANGE;
+    int64_t *cnt = (int64_t *)calloc((size_t)E, sizeof(int64_t));
+    int64_t *off = (int64_t *)calloc((size_t)E + 1, sizeof(int64_t));
+    if (!cnt || !off) { free(cnt); free(off); return ORACLE_EINVAL; }
+    for (int64_t r = 0; r < R; ++r) cnt[topk_idx[r]] += 1;
+    off[0] = 0;
+    for (int32_t e = 0; e < E; ++e)
+        off[e + 1] = off[e] + (cnt[e] + align - 1) / align * align;
+    if (off[E] > P_max) { free(cnt); free(off); return ORACLE_ERANGE; }
+    for (int32_t e = 0; e < E; ++e) counts[e] = (int32_t)cnt[e];
+    for (int32_t e = 0; e <= E; ++e) offsets[e] = (int32_t)off[e];
+    for (int64_t p = 0; p < P_max; ++p) row_token[p] = -1;
+    /* cursor[e] walks expert e's rows; visiting r in ascending order makes the
+     * placement stable. */
+    int64_t *cursor = off; /* reuse: off is no longer needed as such */
+    for (int64_t r = 0; r < R; ++r) {
+        int32_t e = topk_idx[r];
+        int64_t p = cursor[e]++;
+        route_row[r] = (int32_t)p;
+        row_token[p] = (int32_t)(r / k);
+    }
+    free(cnt);
+    free(off);
+    return 0;
+}
+
+/* Gather of token rows into the layout: x_perm[p] = x[row_token[p]] bit for
+ * bit, and a zero row where row_token[p] == -1.  rows = how many rows to fill. */
+int moe_oracle_gather(const uint16_t *x, const int32_t *row_token, int64_t T, int64_t rows,
+                      int32_t H, uint16_t *x_perm) {
+    if (!x || !row_token || !x_perm || rows < 0 || H < 1) return ORACLE_EINVAL;
+    for (int64_t p = 0; p < rows; ++p) {
+        int32_t t = row_token[p];
+        if (t >= T) return ORACLE_ERANGE;
+        for (int32_t c = 0; c < H; ++c)
+            x_perm[p * H + c] = (t >= 0) ? x[(int64_t)t * H + c] : (uint16_t)0;
+    }
+    return 0;
+}
+
+/*
+ * Gate/up projections and SwiGLU for every routed row of every expert
+ * [Halo, Levers that help: one grouped matmul over all experts computes what a
+ * per-expert loop computes -- this is that loop].  W_gu[e] is [2I, H]: rows
+ * [0, I) are the gate projection and rows [I, 2I) the up projection.
+ *   g = sum_c x_perm[p,c] W_gu[e,i,c];  u = sum_c x_perm[p,c] W_gu[e,I+i,c]
+ *   h[p,i] = silu(g) * u
+ * Only rows offsets[e] .. offsets[e]+counts[e]-1 are written.
+ */
+int moe_oracle_glu(const uint16_t *x_perm, const uint16_t *w_gu, const int32_t *counts,
+                   const int32_t *offsets, int32_t E, int32_t H, int32_t I, double *h) {
+    if (!x_perm || !w_gu || !counts || !offsets || !h || E < 1 || H < 1 || I < 1)
+        return ORACLE_EINVAL;
+    for (int32_t e = 0; e < E; ++e) {
+        const uint16_t *W = w_gu + (int64_t)e * 2 * I * H;
+        int64_t p0 = offsets[e], n = counts[e];
+#pragma omp parallel for schedule(static)
+        for (int64_t p = p0; p < p0 + n; ++p) {
+            const uint16_t *xr = x_perm + p * H;
+            for (int32_t i = 0; i < I; ++i) {
+                const uint16_t *wg = W + (int64_t)i * H;
+                const uint16_t *wu = W + (int64_t)(I + i) * H;
+                double g = 0.0, u = 0.0;
+                for (int32_t c = 0; c < H; ++c) {
+                    g += bf(xr[c]) * bf(wg[c]);
+                    u += bf(xr[c]) * bf(wu[c]);
+                }
+                h[p * I + i] = silu(g) * u;
+            }
+        }
+    }
+    return 0;
+}
+
+/*
+ * Down projection for every routed row: y[p,c] = sum_i h[p,i] W_d[e,c,i], with
+ * W_d[e] = [H, I].  h is taken as double so that the oracle's own chain never
+ * rounds; a bf16 input is widened by the caller.
+ */
+int moe_oracle_down(const double *h, const uint16_t *w_d, const int32_t *counts,
+                    const int32_t *offsets, int32_t E, int32_t H, int32_t I, double *y) {
+    if (!h || !w_d || !counts || !offsets || !y || E < 1 || H < 1 || I < 1)
+        return ORACLE_EINVAL;
+    for (int32_t e = 0; e < E; ++e) {
+        const uint16_t *W = w_d + (int64_t)e * H * I;
+        int64_t p0 = offsets[e], n = counts[e];
+#pragma omp parallel for schedule(static)
+        for (int64_t p = p0; p < p0 + n; ++p) {
+            const double *hr = h + p * I;
+            for (int32_t c = 0; c < H; ++c) {
+                const uint16_t *wr = W + (int64_t)c * I;
+                double s = 0.0;
+                for (int32_t i = 0; i < I; ++i) s += hr[i] * bf(wr[i]);
+                y[p * H + c] = s;
+            }
+        }
+    }
+    return 0;
+}
+
+/*
+ * Score-weighted gather-sum back to token order [prime-rl, Changes: one
+ * score-weighted gather-sum back]: out[t,c] = sum_{j<k} w[t,j] y[route_row[t*k+j], c],
+ * summed over j ascending.  A gather per token, not a scatter-add.
+ */
+int moe_oracle_combine(const double *y, const int32_t *route_row, const double *topk_w,
+                       int64_t T, int32_t H, int32_t k, int64_t P_max, double *out) {
+    if (!y || !route_row || !topk_w || !out || T < 0 || H < 1 || k < 1) return ORACLE_EINVAL;
+    for (int64_t r = 0; r < T * (int64_t)k; ++r)
+        if (route_row[r] < 0 || route_row[r] >= P_max) return ORACLE_ERANGE;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        for (int32_t c = 0; c < H; ++c) {
+            double s = 0.0;
+            for (int32_t j = 0; j < k; ++j)
+                s += topk_w[t * k + j] * y[(int64_t)route_row[t * k + j] * H + c];
+            out[t * H + c] = s;
+        }
+    }
+    return 0;
+}
+
+/*
+ * The whole layer as a plain per-token loop (the definition the grouped path
+ * reorganises): for each token, route it, run each of its k experts on it and
+ * add the expert output scaled by its routing weight.  No layout is built.
+ * tokens: the token ids to evaluate (NULL = all T, in order); out is
+ * [n_tokens, H] in the order of `tokens`.
+ */
+int moe_oracle_forward(const uint16_t *x, const float *logits, const uint16_t *w_gu,
+                       const uint16_t *w_d, int64_t T, int32_t H, int32_t E, int32_t k,
+                       int32_t I, const int64_t *tokens, int64_t n_tokens, double *out) {
+    if (!x || !logits || !w_gu || !w_d || !out || T < 0 || H < 1 || E < 1 || k < 1 ||
+        k > E || I < 1)
+        return ORACLE_EINVAL;
+    if (!tokens) n_tokens = T;
+    for (int64_t n = 0; n < n_tokens; ++n) {
+        int64_t t = tokens ? tokens[n] : n;
+        if (t < 0 || t >= T) return ORACLE_ERANGE;
+        for (int32_t e = 0; e < E; ++e)
+            if (!isfinite(logits[t * E + e])) return ORACLE_ENONFINITE;
+    }
+    int err = 0;
+#pragma omp parallel
+    {
+        int32_t *idx = (int32_t *)malloc(sizeof(int32_t) * (size_t)k);
+        double *w = (double *)malloc(sizeof(double) * (size_t)k);
+        double *a = (double *)malloc(sizeof(double) * (size_t)I);
+        if (!idx || !w || !a) {
+#pragma omp atomic write
+            err = 1;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t n = 0; n < n_tokens; ++n) {
+                int64_t t = tokens ? tokens[n] : n;
+                const uint16_t *xr = x + t * H;
+                moe_oracle_route_topk(logits + t * E, 1, E, k, idx, w);
+                double *acc = out + n * H;
+                for (int32_t c = 0; c < H; ++c) acc[c] = 0.0;
+                for (int32_t j = 0; j < k; ++j) {
+                    const uint16_t *Wgu = w_gu + (int64_t)idx[j] * 2 * I * H;
+                    const uint16_t *Wd = w_d + (int64_t)idx[j] * H * I;
+                    for (int32_t i = 0; i < I; ++i) {
+                        double g = 0.0, u = 0.0;
+                        for (int32_t c = 0; c < H; ++c) {
+                            g += bf(xr[c]) * bf(Wgu[(int64_t)i * H + c]);
+                            u += bf(xr[c]) * bf(Wgu[(int64_t)(I + i) * H + c]);
+                        }
+                        a[i] = silu(g) * u;
+                    }
+                    for (int32_t c = 0; c < H; ++c) {
+                        double y = 0.0;
+                        for (int32_t i = 0; i < I; ++i) y += a[i] * bf(Wd[(int64_t)c * I + i]);
+                        acc[c] += w[j] * y;
+                    }
+                }
+            }
+        }
+        free(idx);
+        free(w);
+        free(a);
+    }
+    return err ? ORACLE_EINVAL : 0;
+}

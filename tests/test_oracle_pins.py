@@ -1,0 +1,425 @@
+"""Pins of the CPU oracle to things other than itself (CPU only, no GPU).
+
+Each check compares the oracle with brute force, a closed form, a library
+routine or an invariant that the method's definition fixes, never with a retyped
+copy of its own formula.  The checks are plain functions of an oracle instance
+so that ``test_oracle_mutants.py`` can run them against builds of the oracle
+with a mistake planted in them and show that they fail.
+"""
+from __future__ import annotations
+
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from mixture_experts_routed_router_amd import accounting, inputs as gen
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def f32(bits):
+    return gen.bf16_bits_to_f32(bits)
+
+
+# --------------------------------------------------------------------------------------
+# routing
+# --------------------------------------------------------------------------------------
+
+def _before(la, a, lb, b):
+    """Routing order by definition: larger logit first; an exact tie (float ==,
+    so -0 == +0) goes to the lower expert id."""
+    return la > lb or (la == lb and a < b)
+
+
+def brute_topk(row, k):
+    """Enumerate every k-subset; exactly one has each member ranked before every
+    non-member.  Its members are then ordered by how many members precede them."""
+    row = [float(v) for v in row]
+    E = len(row)
+    winners = []
+    for S in itertools.combinations(range(E), k):
+        rest = [e for e in range(E) if e not in S]
+        if all(_before(row[a], a, row[b], b) for a in S for b in rest):
+            winners.append(S)
+    assert len(winners) == 1, "the routing order must single out one subset"
+    S = winners[0]
+    return sorted(S, key=lambda a: sum(_before(row[b], b, row[a], a) for b in S))
+
+
+def check_topk_brute_force(orc):
+    for case, (E, k) in enumerate([(1, 1), (2, 1), (2, 2), (4, 2), (5, 3), (7, 4), (8, 2), (8, 8)]):
+        for logits in (gen.tied_logits(24, E, seed=case), gen.tied_logits(24, E, seed=100 + case, levels=2),
+                       np.random.default_rng(case).standard_normal((24, E)).astype(np.float32)):
+            idx, _ = orc.route_topk(logits, k)
+            for t in range(logits.shape[0]):
+                assert list(idx[t]) == brute_topk(logits[t], k), (E, k, t, logits[t])
+
+
+def check_topk_lexsort(orc):
+    rng = np.random.default_rng(5)
+    for E, k in [(128, 8), (512, 10), (32, 4)]:
+        logits = rng.standard_normal((200, E)).astype(np.float32)
+        logits[:, ::7] = logits[:, :1]  # plant exact ties with column 0
+        idx, _ = orc.route_topk(logits, k)
+        for t in range(logits.shape[0]):
+            order = np.lexsort((np.arange(E), -logits[t]))  # primary: logit desc, then id asc
+            assert list(idx[t]) == list(order[:k])
+
+
+def check_topk_special_cases(orc):
+    # all-equal logits: the first k ids, equal weights 1/k
+    idx, w = orc.route_topk(np.full((3, 9), 0.25, np.float32), 4)
+    assert (idx == np.arange(4)).all()
+    assert np.all(np.abs(w - 0.25) <= 1e-15)
+    # +0 and -0 compare equal: a tie resolved by id
+    idx, _ = orc.route_topk(np.array([[-0.0, 0.0, -1.0]], np.float32), 2)
+    assert list(idx[0]) == [0, 1]
+    # k = 1: the argmax with the lowest id, weight exactly 1
+    logits = np.random.default_rng(1).standard_normal((50, 16)).astype(np.float32)
+    idx, w = orc.route_topk(logits, 1)
+    assert (idx[:, 0] == np.argmax(logits, axis=1)).all()  # numpy's argmax takes the first max
+    assert (w == 1.0).all()
+    # k = E: the full order
+    idx, _ = orc.route_topk(logits, 16)
+    for t in range(50):
+        assert list(idx[t]) == list(np.lexsort((np.arange(16), -logits[t])))
+
+
+def check_softmax_weights(orc):
+    rng = np.random.default_rng(2)
+    logits = (rng.standard_normal((300, 64)) * 3).astype(np.float32)
+    k = 6
+    idx, w = orc.route_topk(logits, k)
+    sel = np.take_along_axis(logits, idx, 1).astype(np.float64)
+    assert np.all(np.abs(w.sum(1) - 1.0) <= 1e-14)            # a distribution over the k picks
+    assert np.all(np.diff(w, axis=1) <= 0)                      # non-increasing in the slot
+    # closed form of the softmax ratio: w_i / w_j = exp(L_i - L_j)
+    ratio = w[:, 1:] / w[:, :1]
+    assert np.allclose(ratio, np.exp(sel[:, 1:] - sel[:, :1]), rtol=1e-13, atol=0)
+    # two selected logits that differ by ln 3 get weights 3/4 and 1/4
+    L = np.array([[math.log(3.0), 0.0, -50.0]], np.float32)
+    _, w2 = orc.route_topk(L, 2)
+    d = float(np.float32(math.log(3.0)))  # the logit actually stored
+    assert abs(w2[0, 0] - 1.0 / (1.0 + math.exp(-d))) < 1e-15
+    assert abs(w2[0, 0] - 0.75) < 1e-7
+
+
+# --------------------------------------------------------------------------------------
+# layout
+# --------------------------------------------------------------------------------------
+
+def check_layout(orc, topk_idx, E, align):
+    T, k = topk_idx.shape
+    P_max = T * k + E * (align - 1)
+    counts, offsets, route_row, row_token = orc.layout(topk_idx, E, align, P_max)
+    flat = topk_idx.reshape(-1)
+    assert (counts == np.bincount(flat, minlength=E)).all()
+    assert counts.sum() == T * k
+    padded = (counts + align - 1) // align * align
+    assert offsets[0] == 0 and (np.diff(offsets) == padded).all() and (offsets % align == 0).all()
+    assert offsets[-1] <= P_max
+    # placement = a stable sort of the flat routes by expert, laid out from offsets[e]
+    order = np.argsort(flat, kind="stable")
+    expect = np.empty(T * k, np.int64)
+    pos = 0
+    for e in range(E):
+        rs = order[pos:pos + counts[e]]
+        expect[rs] = offsets[e] + np.arange(counts[e])
+        pos += counts[e]
+    assert (route_row == expect).all()
+    # row_token: every token exactly k times, -1 everywhere else, ascending inside a segment
+    assert (row_token[route_row] == np.arange(T * k) // k).all()
+    assert np.bincount(row_token[row_token >= 0], minlength=T).tolist() == [k] * T
+    assert (row_token >= 0).sum() == T * k
+    for e in range(E):
+        seg = row_token[offsets[e]:offsets[e] + counts[e]]
+        assert (seg >= 0).all() and (np.diff(seg) > 0).all()
+        assert (row_token[offsets[e] + counts[e]:offsets[e + 1]] == -1).all()
+    assert (row_token[offsets[-1]:] == -1).all()
+    return counts, offsets, route_row, row_token
+
+
+def check_layout_cases(orc):
+    rng = np.random.default_rng(3)
+    check_layout(orc, gen.balanced_topk_idx(64, 8, 2), 8, 32)
+    check_layout(orc, gen.balanced_topk_idx(100, 128, 8), 128, 16)
+    idx, _ = orc.route_topk(rng.standard_normal((300, 40)).astype(np.float32), 5)
+    check_layout(orc, idx, 40, 8)
+    check_layout(orc, idx, 40, 1)
+    # every token to the same experts (the rest get zero rows)
+    check_layout(orc, np.tile(np.array([[3, 1]], np.int32), (50, 1)), 6, 32)
+
+
+def check_gather(orc):
+    rng = np.random.default_rng(4)
+    T, H, E, k, a = 40, 64, 6, 2, 16
+    x = gen.random_bf16((T, H), seed=4)
+    idx, _ = orc.route_topk(rng.standard_normal((T, E)).astype(np.float32), k)
+    counts, offsets, route_row, row_token = orc.layout(idx, E, a)
+    xp = orc.gather(x, row_token, rows=int(offsets[-1]))
+    assert (xp[route_row] == x[np.arange(T * k) // k]).all()
+    pad = np.ones(int(offsets[-1]), bool)
+    pad[route_row] = False
+    assert (xp[pad] == 0).all()
+
+
+# --------------------------------------------------------------------------------------
+# expert MLPs and the whole layer
+# --------------------------------------------------------------------------------------
+
+def _silu(g):
+    return g / (1.0 + np.exp(-g))
+
+
+def check_dense_swiglu_reduction(orc):
+    """E = 1, k = 1: the layer is a dense SwiGLU MLP (numpy float64 matmuls)."""
+    T, H, I = 24, 64, 48
+    x = gen.random_bf16((T, H), seed=11)
+    w_gu = gen.random_bf16((1, 2 * I, H), seed=12, std=0.1)
+    w_d = gen.random_bf16((1, H, I), seed=13, std=0.1)
+    logits = np.random.default_rng(0).standard_normal((T, 1)).astype(np.float32)
+    X = f32(x).astype(np.float64)
+    Wg, Wu = f32(w_gu[0, :I]).astype(np.float64), f32(w_gu[0, I:]).astype(np.float64)
+    Wd = f32(w_d[0]).astype(np.float64)
+    ref = (_silu(X @ Wg.T) * (X @ Wu.T)) @ Wd.T
+    out = orc.forward(x, logits, w_gu, w_d, 1)
+    assert np.max(np.abs(out - ref)) <= 1e-12 * np.max(np.abs(ref))
+
+
+def dense_masked_reference(x, logits, w_gu, w_d, k):
+    """Every expert on every token (the dense work the routed layer avoids), then a
+    gate matrix that is zero off each token's top-k (selected by lexsort)."""
+    T, H = x.shape
+    E, two_i, _ = w_gu.shape
+    I = two_i // 2
+    X = f32(x).astype(np.float64)
+    gate = np.zeros((T, E))
+    for t in range(T):
+        sel = np.lexsort((np.arange(E), -logits[t]))[:k]
+        z = np.exp(logits[t, sel].astype(np.float64) - float(logits[t, sel[0]]))
+        gate[t, sel] = z / z.sum()
+    out = np.zeros((T, H))
+    for e in range(E):
+        Wg = f32(w_gu[e, :I]).astype(np.float64)
+        Wu = f32(w_gu[e, I:]).astype(np.float64)
+        Wd = f32(w_d[e]).astype(np.float64)
+        out += gate[:, e:e + 1] * ((_silu(X @ Wg.T) * (X @ Wu.T)) @ Wd.T)
+    return out
+
+
+def check_dense_masked(orc, cfg):
+    d = gen.make_inputs(cfg)
+    ref = dense_masked_reference(d["x"], d["logits"], d["w_gu"], d["w_d"], cfg.k)
+    out = orc.forward(d["x"], d["logits"], d["w_gu"], d["w_d"], cfg.k)
+    assert np.max(np.abs(out - ref)) <= 1e-11 * np.max(np.abs(ref))
+    return d, out
+
+
+def check_structured_closed_form(orc):
+    """Weights with a closed-form answer: gate = a_e * Id, up = b_e * Id, down =
+    c_e * (permutation pi_e), so y_e[c] = c_e * silu(a_e x[pi_e(c)]) * b_e x[pi_e(c)]."""
+    T, n, E, k = 16, 32, 4, 2
+    rng = np.random.default_rng(9)
+    a = np.array([0.5, 1.25, -2.0, 0.75])
+    b = np.array([1.5, -0.5, 0.25, 2.0])
+    c = np.array([-1.0, 0.5, 1.75, -0.25])
+    perms = [rng.permutation(n) for _ in range(E)]
+    w_gu = np.zeros((E, 2 * n, n), np.float32)
+    w_d = np.zeros((E, n, n), np.float32)
+    for e in range(E):
+        w_gu[e, :n] = a[e] * np.eye(n)
+        w_gu[e, n:] = b[e] * np.eye(n)
+        w_d[e][np.arange(n), perms[e]] = c[e]       # row c reads input pi_e(c)
+    x = gen.random_bf16((T, n), seed=9)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    out = orc.forward(x, logits, gen.f32_to_bf16_bits(w_gu), gen.f32_to_bf16_bits(w_d), k)
+    X = f32(x).astype(np.float64)
+    for t in range(T):
+        sel = np.lexsort((np.arange(E), -logits[t]))[:k]
+        z = np.exp(logits[t, sel].astype(np.float64) - float(logits[t, sel[0]]))
+        w = z / z.sum()
+        expect = np.zeros(n)
+        for j, e in enumerate(sel):
+            xs = X[t, perms[e]]
+            expect += w[j] * c[e] * _silu(a[e] * xs) * (b[e] * xs)
+        assert np.max(np.abs(out[t] - expect)) <= 1e-13 * max(1.0, np.max(np.abs(expect))), t
+
+
+def check_steps_compose(orc):
+    """layout -> gather -> glu -> down -> combine equals the per-token loop."""
+    cfg = gen.CONFIGS["tiny"]
+    d = gen.make_inputs(cfg)
+    idx, w = orc.route_topk(d["logits"], cfg.k)
+    counts, offsets, route_row, row_token = orc.layout(idx, cfg.E, cfg.align)
+    xp = orc.gather(d["x"], row_token)
+    h = orc.glu(xp, d["w_gu"], counts, offsets, cfg.I)
+    y = orc.down(np.nan_to_num(h), d["w_d"], counts, offsets)
+    out = orc.combine(np.nan_to_num(y), route_row, w)
+    ref = orc.forward(d["x"], d["logits"], d["w_gu"], d["w_d"], cfg.k)
+    assert np.max(np.abs(out - ref)) <= 1e-12 * np.max(np.abs(ref))
+
+
+def check_identity_experts(orc):
+    """Identity experts reproduce the input: combine applied to the gathered rows
+    themselves.  k = 1 gives weight 1.0 and an exact copy; for k > 1 the weights
+    sum to 1 within a few ulps of double."""
+    T, H, E = 50, 64, 8
+    x = gen.random_bf16((T, H), seed=21)
+    X = f32(x).astype(np.float64)
+    logits = np.random.default_rng(21).standard_normal((T, E)).astype(np.float32)
+    for k in (1, 3, 8):
+        idx, w = orc.route_topk(logits, k)
+        counts, offsets, route_row, row_token = orc.layout(idx, E, 16)
+        xp = orc.gather(x, row_token)
+        out = orc.combine(f32(xp).astype(np.float64), route_row, w)
+        if k == 1:
+            assert (out == X).all()
+        else:
+            assert np.max(np.abs(out - X)) <= 8 * k * 2.0 ** -52 * np.max(np.abs(X))
+
+
+def check_linearity_and_symmetry(orc):
+    cfg = gen.CONFIGS["tiny"]
+    d = gen.make_inputs(cfg)
+    x, logits, w_gu, w_d = d["x"], d["logits"], d["w_gu"], d["w_d"]
+    out = orc.forward(x, logits, w_gu, w_d, cfg.k)
+    # doubling W_down doubles the output exactly
+    w_d2 = gen.f32_to_bf16_bits(f32(w_d) * 2)
+    assert (orc.forward(x, logits, w_gu, w_d2, cfg.k) == 2 * out).all()
+    # permuting tokens permutes output rows bit for bit
+    perm = np.random.default_rng(1).permutation(cfg.T)
+    assert (orc.forward(x[perm], logits[perm], w_gu, w_d, cfg.k) == out[perm]).all()
+    # relabelling experts consistently leaves the output unchanged (no ties here)
+    sigma = np.random.default_rng(2).permutation(cfg.E)   # new id of old expert e is sigma[e]
+    inv = np.argsort(sigma)
+    out2 = orc.forward(x, logits[:, inv], w_gu[inv], w_d[inv], cfg.k)
+    assert (out2 == out).all()
+    # a token subset gives the same rows
+    toks = np.array([5, 0, 63, 17])
+    assert (orc.forward(x, logits, w_gu, w_d, cfg.k, tokens=toks) == out[toks]).all()
+
+
+# --------------------------------------------------------------------------------------
+# tests
+# --------------------------------------------------------------------------------------
+
+@pytest.fixture(scope="module")
+def orc():
+    return oracle.Oracle()
+
+
+def test_topk_brute_force(orc):
+    check_topk_brute_force(orc)
+
+
+def test_topk_lexsort(orc):
+    check_topk_lexsort(orc)
+
+
+def test_topk_special_cases(orc):
+    check_topk_special_cases(orc)
+
+
+def test_softmax_weights(orc):
+    check_softmax_weights(orc)
+
+
+def test_layout(orc):
+    check_layout_cases(orc)
+
+
+def test_gather(orc):
+    check_gather(orc)
+
+
+def test_dense_swiglu_reduction(orc):
+    check_dense_swiglu_reduction(orc)
+
+
+@pytest.mark.parametrize("cfg", [gen.CONFIGS["tiny"],
+                                 gen.CONFIGS["tiny"].with_(name="tiny_hot", weight_std=0.2, seed=10),
+                                 gen.MoEConfig("odd", 37, 64, 5, 3, 64, 6, "gaussian")])
+def test_dense_masked(orc, cfg):
+    check_dense_masked(orc, cfg)
+
+
+def test_structured_closed_form(orc):
+    check_structured_closed_form(orc)
+
+
+def test_steps_compose(orc):
+    check_steps_compose(orc)
+
+
+def test_identity_experts(orc):
+    check_identity_experts(orc)
+
+
+def test_linearity_and_symmetry(orc):
+    check_linearity_and_symmetry(orc)
+
+
+def test_rejects_bad_inputs(orc):
+    bad = np.zeros((2, 4), np.float32)
+    bad[1, 2] = np.inf
+    with pytest.raises(oracle.OracleError):
+        orc.route_topk(bad, 2)
+    with pytest.raises(oracle.OracleError):
+        orc.layout(np.array([[0, 7]], np.int32), 4, 8)
+
+
+# ---- figures the pages print --------------------------------------------------------
+
+def _golden():
+    with open(os.path.join(GOLDEN, "page_figures.json")) as f:
+        return json.load(f)
+
+
+def test_uniform_routing_distinct_experts(orc):
+    """Gaussian logits + top-10 of 512: 8 tokens touch 74.7 distinct experts
+    (closed form 512 * (1 - (1 - 10/512)^8) = 74.74)."""
+    page = _golden()["distinct_experts_8_tokens_top10_of_512"]["value"]
+    closed = 512 * (1 - (1 - 10 / 512) ** 8)
+    assert abs(closed - page) < 0.05
+    cfg = gen.MoEConfig("u", 8 * 1500, 64, 512, 10, 64, 77, "gaussian")
+    idx, _ = orc.route_topk(gen.draw_logits(cfg), 10)
+    distinct = [len(np.unique(idx[g * 8:(g + 1) * 8])) for g in range(1500)]
+    assert abs(np.mean(distinct) - page) < 0.3
+
+
+def test_expert_size_and_flop_accounting():
+    g = _golden()
+    cfg = gen.CONFIGS["fine_grained_512"]
+    mib = 3 * cfg.H * cfg.I * 2 / 2 ** 20
+    assert mib == g["bf16_expert_mib_512_expert_layer"]["value"]
+    # the routed-MoE floor on the page: 1.326 s over 48 layers, one quarter of the
+    # 8192-token layer's flops per rank at the measured 7.50 TFLOP/s bf16 GEMM roof
+    f = g["routed_moe_floor_ms_per_layer_per_rank"]
+    assert abs(f["total_s"] / f["layers"] * 1e3 - f["value"]) < 0.05
+    per_rank_s = accounting.layer_flops(cfg.T, cfg.H, cfg.k, cfg.I) / f["ranks"] / (f["bf16_gemm_tflops"] * 1e12)
+    assert abs(per_rank_s * 1e3 - f["value"]) / f["value"] < 0.05
+
+
+def test_skew_generator(orc):
+    """Zipf(1.2) bias: a heavy max load, close to its bound E/k (a token takes an
+    expert at most once), with many near-idle experts.  Real routers reach ~20x
+    the mean at other shapes (the page's figure)."""
+    cfg = gen.CONFIGS["skewed_zipf"]
+    idx, _ = orc.route_topk(gen.draw_logits(cfg), cfg.k)
+    counts = np.bincount(idx.reshape(-1), minlength=cfg.E)
+    mean = cfg.T * cfg.k / cfg.E
+    assert 12 < counts.max() / mean <= cfg.E / cfg.k
+    assert (counts <= 32).sum() >= 20
+    assert np.sort(counts)[::-1][:8].sum() > 0.5 * cfg.T * cfg.k
+
+
+def test_gaussian_generator_balanced(orc):
+    cfg = gen.CONFIGS["qwen3_30b_a3b"]
+    idx, _ = orc.route_topk(gen.draw_logits(cfg), cfg.k)
+    counts = np.bincount(idx.reshape(-1), minlength=cfg.E)
+    assert counts.min() > 400 and counts.max() < 640  # mean 512, binomial spread
