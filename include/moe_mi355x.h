@@ -1,0 +1,178 @@
+/*
+ * moe_mi355x.h -- C ABI of the routed-expert Mixture-of-Experts forward path on
+ * one AMD Instinct MI355X (gfx950).
+ *
+ * The layer, for T tokens of hidden size H, E experts, top-k routing and expert
+ * intermediate size I, runs as five calls on one HIP stream:
+ *
+ *   moe_route_topk         router logits -> top-k expert ids and weights
+ *   moe_permute            atomic-free counting sort + gather into a padded,
+ *                          expert-grouped row layout
+ *   moe_grouped_glu_gemm   one grouped GEMM for every expert's gate and up
+ *                          projections, SwiGLU fused into its epilogue
+ *   moe_grouped_down_gemm  one grouped GEMM for every expert's down projection
+ *   moe_combine            fp32 score-weighted gather-sum back to token order
+ *
+ * Sources (page title, section):
+ *   [Halo]      Halo, "Performance": Levers that help (grouped GEMM instead of a
+ *               per-expert loop; the atomic-free expert permute; fused GLU);
+ *               Levers that do not help here (small-M experts are bound by
+ *               weight bandwidth)
+ *   [PocketLLM] "Qwen4-Exp Heterogeneous TP4 Performance": Runtime architecture
+ *               (top-10 of 512 routed experts); Confirmed architecture decisions
+ *               (only active experts move weight bytes)
+ *   [prime-rl]  prime-rl pull request 3885: Changes (single-pass local layout: one
+ *               gather into the padded expert-grouped layout and one fp32
+ *               score-weighted gather-sum back; 32-bit row offsets must not
+ *               overflow silently)
+ *
+ * Conventions
+ *   - Every tensor pointer is a DEVICE pointer, row-major, 16-byte aligned.
+ *     bf16 tensors are raw 16-bit values (moe_bf16).
+ *   - The caller owns every buffer. The library never allocates, frees or keeps
+ *     a pointer after a call returns; buffers must stay alive until the stream
+ *     work that uses them completes.
+ *   - Every call validates its arguments on the host first. On an error it
+ *     returns a nonzero moe_status, enqueues nothing and leaves outputs untouched;
+ *     moe_last_error_message() then describes the error (thread-local text).
+ *   - On success the work is only enqueued on `stream` (NULL = the default
+ *     stream). No call synchronises, copies device->host or needs expert counts
+ *     on the host: the GEMMs read counts and offsets on the device, and the
+ *     layout buffers are sized by P_max, the largest row count any routing can
+ *     need. Device faults surface at the caller's next synchronisation.
+ *   - Results are deterministic: no atomics anywhere, fixed reduction orders,
+ *     so the same inputs give bitwise-identical outputs.
+ *   - Row indices are int32 (P_max < 2^31); element offsets are 64-bit.
+ *   - Calls are thread-safe; concurrent calls on different streams do not
+ *     interact except through buffers the caller shares.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t moe_bf16;   /* raw bf16 bits */
+typedef void *moe_stream_t;  /* a hipStream_t; NULL = default stream */
+
+typedef enum moe_status {
+    MOE_OK = 0,
+    MOE_ERR_NULL_POINTER = 1,       /* a required pointer is NULL */
+    MOE_ERR_INVALID_SHAPE = 2,      /* a size is out of range (see each call) */
+    MOE_ERR_INVALID_ALIGN = 3,      /* align is not a power of two in [1, 256] */
+    MOE_ERR_SIZE_OVERFLOW = 4,      /* P_max too small, or rows would reach 2^31 */
+    MOE_ERR_MISALIGNED_POINTER = 5, /* a tensor pointer is not 16-byte aligned */
+    MOE_ERR_WORKSPACE_TOO_SMALL = 6,
+    MOE_ERR_HIP = 7                 /* a HIP call failed; see moe_last_error_message */
+} moe_status;
+
+#define MOE_MAX_K 32    /* largest top-k */
+#define MOE_MAX_E 1024  /* most experts */
+#define MOE_MAX_ALIGN 256
+
+/* Static text for a status code. */
+const char *moe_status_string(int status);
+
+/* Text of the last error returned on this thread ("" if none). */
+const char *moe_last_error_message(void);
+
+/* Rows the padded layout can need: T*k + E*(align-1) (each expert's segment is
+ * rounded up to a multiple of align). -1 if an argument is out of range. */
+int64_t moe_padded_rows_max(int64_t T, int32_t k, int32_t E, int32_t align);
+
+/* Device workspace bytes moe_permute needs for T tokens, top-k, E experts. */
+moe_status moe_permute_workspace_size(int64_t T, int32_t k, int32_t E, size_t *bytes);
+
+/*
+ * Top-k routing [PocketLLM, Runtime architecture: top-10 routing over 512
+ * experts; prime-rl, Changes: the top-k scores weight the gather-sum].
+ *   logits    [T, E] fp32, finite (unchecked; non-finite input gives
+ *             unspecified ids)
+ *   topk_idx  [T, k] int32 out: per token the k experts with the largest logits,
+ *             larger logit first; an exact tie (float ==, so -0 == +0) goes to the
+ *             lower expert id
+ *   topk_w    [T, k] fp32 out: softmax over the k selected logits,
+ *             w_j = exp(l_j - l_0) / sum_i exp(l_i - l_0)
+ * Shapes: 1 <= E <= MOE_MAX_E, 1 <= k <= min(E, MOE_MAX_K), T >= 0.
+ */
+moe_status moe_route_topk(const float *logits, int64_t T, int32_t E, int32_t k,
+                          int32_t *topk_idx, float *topk_w, moe_stream_t stream);
+
+/*
+ * Padded expert-grouped layout and token gather, without atomics [Halo, Levers
+ * that help: the atomic-free expert permute; prime-rl, Changes: one gather into
+ * the padded expert-grouped layout].  Over the flat routes r = t*k + j:
+ *   expert_counts   [E] int32 out: routes per expert
+ *   expert_offsets  [E+1] int32 out: offsets[0] = 0, offsets[e+1] = offsets[e]
+ *                   + counts[e] rounded up to a multiple of align
+ *   route_row       [T*k] int32 out: the layout row of route r; the routes of
+ *                   expert e fill rows offsets[e], offsets[e]+1, ... in ascending r
+ *   row_token       [P_max] int32 out: the token of each row, -1 on pad rows and
+ *                   on every row at or past offsets[E]
+ *   x_perm          [P_max, H] bf16 out: x_perm[p] = x[row_token[p]] bit for bit
+ *                   on routed rows, zero on pad rows inside a segment; rows at or
+ *                   past offsets[E] are not written
+ *   x               [T, H] bf16;  topk_idx [T, k] int32, each in [0, E) and
+ *                   distinct per token (unchecked)
+ *   workspace       device scratch of moe_permute_workspace_size() bytes
+ * Shapes: H % 64 == 0, align a power of two <= MOE_MAX_ALIGN,
+ *         moe_padded_rows_max(T,k,E,align) <= P_max < 2^31.
+ */
+moe_status moe_permute(const moe_bf16 *x, const int32_t *topk_idx, int64_t T, int32_t H,
+                       int32_t E, int32_t k, int32_t align, int64_t P_max,
+                       int32_t *expert_counts, int32_t *expert_offsets, int32_t *route_row,
+                       int32_t *row_token, moe_bf16 *x_perm, void *workspace,
+                       size_t workspace_bytes, moe_stream_t stream);
+
+/*
+ * Grouped gate/up GEMM with SwiGLU [Halo, Levers that help: one grouped expert
+ * matmul instead of a per-expert loop, fused GLU; prime-rl, Changes: gate and up
+ * run as one GEMM ahead of a SwiGLU].  For every expert e and every row p of its
+ * padded segment [offsets[e], offsets[e+1]):
+ *   g = x_perm[p] . w_gate_up[e, i, :],  u = x_perm[p] . w_gate_up[e, I+i, :]
+ *   h[p, i] = bf16_rne(silu(g) * u)      (fp32 accumulation and epilogue)
+ *   w_gate_up       [E, 2I, H] bf16: rows [0, I) gate, rows [I, 2I) up
+ *   expert_counts, expert_offsets as produced by moe_permute (device)
+ *   h               [P_max, I] bf16 out; rows at or past offsets[E] not written
+ * An expert with no rows reads none of its weights.
+ * Shapes: H % 64 == 0, I % 64 == 0, 1 <= E <= MOE_MAX_E, 0 < P_max < 2^31.
+ */
+moe_status moe_grouped_glu_gemm(const moe_bf16 *x_perm, const moe_bf16 *w_gate_up,
+                                const int32_t *expert_counts, const int32_t *expert_offsets,
+                                int32_t E, int32_t H, int32_t I, int64_t P_max, moe_bf16 *h,
+                                moe_stream_t stream);
+
+/*
+ * Grouped down GEMM [Halo, Levers that help: grouped GEMM].  For every expert e
+ * and every row p of its padded segment:
+ *   y[p, c] = bf16_rne(h[p] . w_down[e, c, :])   (fp32 accumulation)
+ *   w_down  [E, H, I] bf16;  y [P_max, H] bf16 out (rows past offsets[E] not written)
+ * Shapes as for moe_grouped_glu_gemm.
+ */
+moe_status moe_grouped_down_gemm(const moe_bf16 *h, const moe_bf16 *w_down,
+                                 const int32_t *expert_counts, const int32_t *expert_offsets,
+                                 int32_t E, int32_t H, int32_t I, int64_t P_max, moe_bf16 *y,
+                                 moe_stream_t stream);
+
+/*
+ * Score-weighted gather-sum [prime-rl, Changes: one fp32 score-weighted
+ * gather-sum back].  Per token t, a gather (no scatter-add):
+ *   out[t, c] = bf16_rne( sum_{j=0..k-1} topk_w[t, j] * y[route_row[t*k+j], c] )
+ * summed in fp32 in ascending j.
+ *   y [P_max, H] bf16;  route_row [T*k] int32 in [0, P_max) (unchecked);
+ *   topk_w [T, k] fp32;  out [T, H] bf16 out
+ * Shapes: H % 64 == 0, 1 <= k <= MOE_MAX_K.
+ */
+moe_status moe_combine(const moe_bf16 *y, const int32_t *route_row, const float *topk_w,
+                       int64_t T, int32_t H, int32_t k, int64_t P_max, moe_bf16 *out,
+                       moe_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

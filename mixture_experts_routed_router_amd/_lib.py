@@ -1,0 +1,236 @@
+"""Python binding of the C ABI in ``include/moe_mi355x.h`` (argument marshalling only).
+
+Every step of the layer runs in the HIP library ``libmoe_mi355x.so``; this
+module only checks tensor dtypes/devices/shapes, allocates outputs with torch
+(device memory) and passes raw pointers plus torch's current HIP stream.  There
+is no CPU or torch fallback: if the library is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch  # loads the HIP runtime that the library then shares
+
+from .build import library_path
+
+_LIB = None
+
+_c_i32, _c_i64, _c_sz, _c_vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
+
+MOE_MAX_K = 32
+MOE_MAX_E = 1024
+
+
+class MoEError(RuntimeError):
+    """A nonzero moe_status returned by the library."""
+
+    def __init__(self, fn: str, status: int, message: str):
+        super().__init__(f"{fn}: {status_string(status)}: {message}")
+        self.status = status
+
+
+def load():
+    """Load the built library, building it first only if nothing is built.
+    A failed build or load raises: there is no fallback path."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        from .build import build
+        build()
+    lib = ctypes.CDLL(path)
+    lib.moe_status_string.argtypes = [ctypes.c_int]
+    lib.moe_status_string.restype = ctypes.c_char_p
+    lib.moe_last_error_message.argtypes = []
+    lib.moe_last_error_message.restype = ctypes.c_char_p
+    lib.moe_padded_rows_max.argtypes = [_c_i64, _c_i32, _c_i32, _c_i32]
+    lib.moe_padded_rows_max.restype = _c_i64
+    lib.moe_permute_workspace_size.argtypes = [_c_i64, _c_i32, _c_i32, ctypes.POINTER(_c_sz)]
+    lib.moe_route_topk.argtypes = [_c_vp, _c_i64, _c_i32, _c_i32, _c_vp, _c_vp, _c_vp]
+    lib.moe_permute.argtypes = [_c_vp, _c_vp, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64,
+                                _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_sz, _c_vp]
+    lib.moe_grouped_glu_gemm.argtypes = [_c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32,
+                                         _c_i64, _c_vp, _c_vp]
+    lib.moe_grouped_down_gemm.argtypes = [_c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32,
+                                          _c_i64, _c_vp, _c_vp]
+    lib.moe_combine.argtypes = [_c_vp, _c_vp, _c_vp, _c_i64, _c_i32, _c_i32, _c_i64, _c_vp, _c_vp]
+    for fn in ("moe_permute_workspace_size", "moe_route_topk", "moe_permute",
+               "moe_grouped_glu_gemm", "moe_grouped_down_gemm", "moe_combine"):
+        getattr(lib, fn).restype = ctypes.c_int
+    _LIB = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().moe_status_string(status).decode()
+
+
+def _call(fn: str, *args):
+    lib = load()
+    st = getattr(lib, fn)(*args)
+    if st != 0:
+        raise MoEError(fn, st, lib.moe_last_error_message().decode())
+
+
+def _stream(stream=None) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _ptr(t: torch.Tensor, dtype, name: str, shape=None) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t.data_ptr()
+
+
+def padded_rows_max(T: int, k: int, E: int, align: int) -> int:
+    return int(load().moe_padded_rows_max(T, k, E, align))
+
+
+def permute_workspace_size(T: int, k: int, E: int) -> int:
+    n = _c_sz(0)
+    _call("moe_permute_workspace_size", T, k, E, ctypes.byref(n))
+    return int(n.value)
+
+
+# ---- the five calls -----------------------------------------------------------------
+
+def route_topk(logits: torch.Tensor, k: int, topk_idx=None, topk_w=None, stream=None):
+    T, E = logits.shape
+    dev = logits.device
+    if topk_idx is None:
+        topk_idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    if topk_w is None:
+        topk_w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    _call("moe_route_topk", _ptr(logits, torch.float32, "logits"), T, E, k,
+          _ptr(topk_idx, torch.int32, "topk_idx", (T, k)),
+          _ptr(topk_w, torch.float32, "topk_w", (T, k)), _stream(stream))
+    return topk_idx, topk_w
+
+
+@dataclass
+class Layout:
+    counts: torch.Tensor     # [E] int32
+    offsets: torch.Tensor    # [E+1] int32
+    route_row: torch.Tensor  # [T*k] int32
+    row_token: torch.Tensor  # [P_max] int32
+    x_perm: torch.Tensor     # [P_max, H] bf16
+    P_max: int
+
+
+def alloc_layout(T: int, H: int, E: int, k: int, P_max: int, device) -> Layout:
+    return Layout(torch.empty(E, dtype=torch.int32, device=device),
+                  torch.empty(E + 1, dtype=torch.int32, device=device),
+                  torch.empty(T * k, dtype=torch.int32, device=device),
+                  torch.empty(P_max, dtype=torch.int32, device=device),
+                  torch.empty((P_max, H), dtype=torch.bfloat16, device=device), P_max)
+
+
+def permute(x: torch.Tensor, topk_idx: torch.Tensor, E: int, align: int = 32, P_max=None,
+            out: Layout | None = None, workspace: torch.Tensor | None = None, stream=None) -> Layout:
+    T, H = x.shape
+    k = topk_idx.shape[1]
+    if P_max is None:
+        P_max = padded_rows_max(T, k, E, align)
+    if out is None:
+        out = alloc_layout(T, H, E, k, P_max, x.device)
+    ws_bytes = permute_workspace_size(T, k, E)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=x.device)
+    _call("moe_permute", _ptr(x, torch.bfloat16, "x"), _ptr(topk_idx, torch.int32, "topk_idx", (T, k)),
+          T, H, E, k, align, P_max,
+          _ptr(out.counts, torch.int32, "counts", (E,)),
+          _ptr(out.offsets, torch.int32, "offsets", (E + 1,)),
+          _ptr(out.route_row, torch.int32, "route_row", (T * k,)),
+          _ptr(out.row_token, torch.int32, "row_token", (P_max,)),
+          _ptr(out.x_perm, torch.bfloat16, "x_perm", (P_max, H)),
+          _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream))
+    return out
+
+
+def grouped_glu_gemm(x_perm, w_gate_up, counts, offsets, h=None, stream=None):
+    P_max, H = x_perm.shape
+    E, two_i, H2 = w_gate_up.shape
+    I = two_i // 2
+    if H2 != H or two_i != 2 * I:
+        raise ValueError("w_gate_up must be [E, 2I, H]")
+    if h is None:
+        h = torch.empty((P_max, I), dtype=torch.bfloat16, device=x_perm.device)
+    _call("moe_grouped_glu_gemm", _ptr(x_perm, torch.bfloat16, "x_perm"),
+          _ptr(w_gate_up, torch.bfloat16, "w_gate_up"), _ptr(counts, torch.int32, "counts", (E,)),
+          _ptr(offsets, torch.int32, "offsets", (E + 1,)), E, H, I, P_max,
+          _ptr(h, torch.bfloat16, "h", (P_max, I)), _stream(stream))
+    return h
+
+
+def grouped_down_gemm(h, w_down, counts, offsets, y=None, stream=None):
+    P_max, I = h.shape
+    E, H, I2 = w_down.shape
+    if I2 != I:
+        raise ValueError("w_down must be [E, H, I]")
+    if y is None:
+        y = torch.empty((P_max, H), dtype=torch.bfloat16, device=h.device)
+    _call("moe_grouped_down_gemm", _ptr(h, torch.bfloat16, "h"), _ptr(w_down, torch.bfloat16, "w_down"),
+          _ptr(counts, torch.int32, "counts", (E,)), _ptr(offsets, torch.int32, "offsets", (E + 1,)),
+          E, H, I, P_max, _ptr(y, torch.bfloat16, "y", (P_max, H)), _stream(stream))
+    return y
+
+
+def combine(y, route_row, topk_w, out=None, stream=None):
+    P_max, H = y.shape
+    T, k = topk_w.shape
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=y.device)
+    _call("moe_combine", _ptr(y, torch.bfloat16, "y"), _ptr(route_row, torch.int32, "route_row", (T * k,)),
+          _ptr(topk_w, torch.float32, "topk_w", (T, k)), T, H, k, P_max,
+          _ptr(out, torch.bfloat16, "out", (T, H)), _stream(stream))
+    return out
+
+
+# ---- the whole layer -----------------------------------------------------------------
+
+class MoELayer:
+    """Preallocated buffers for repeated layer calls of one shape; ``__call__``
+    enqueues the five library calls on the current stream and allocates nothing."""
+
+    def __init__(self, T: int, H: int, E: int, k: int, I: int, align: int = 32, device="cuda"):
+        self.T, self.H, self.E, self.k, self.I, self.align = T, H, E, k, I, align
+        self.P_max = padded_rows_max(T, k, E, align)
+        dev = torch.device(device)
+        self.topk_idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+        self.topk_w = torch.empty((T, k), dtype=torch.float32, device=dev)
+        self.layout = alloc_layout(T, H, E, k, self.P_max, dev)
+        self.workspace = torch.empty(max(permute_workspace_size(T, k, E), 256), dtype=torch.uint8,
+                                     device=dev)
+        self.h = torch.empty((self.P_max, I), dtype=torch.bfloat16, device=dev)
+        self.y = torch.empty((self.P_max, H), dtype=torch.bfloat16, device=dev)
+        self.out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+
+    def __call__(self, x, logits, w_gate_up, w_down, stream=None):
+        route_topk(logits, self.k, self.topk_idx, self.topk_w, stream=stream)
+        permute(x, self.topk_idx, self.E, self.align, self.P_max, out=self.layout,
+                workspace=self.workspace, stream=stream)
+        L = self.layout
+        grouped_glu_gemm(L.x_perm, w_gate_up, L.counts, L.offsets, h=self.h, stream=stream)
+        grouped_down_gemm(self.h, w_down, L.counts, L.offsets, y=self.y, stream=stream)
+        combine(self.y, L.route_row, self.topk_w, out=self.out, stream=stream)
+        return self.out
+
+
+def moe_forward(x, logits, w_gate_up, w_down, k: int, align: int = 32):
+    """One layer call with fresh buffers: returns out [T, H] bf16."""
+    T, H = x.shape
+    E, two_i, _ = w_gate_up.shape
+    layer = MoELayer(T, H, E, k, two_i // 2, align, device=x.device)
+    return layer(x, logits, w_gate_up, w_down).clone()

@@ -1,0 +1,203 @@
+// api.hip -- the C ABI of the MoE path: argument validation on the host, then
+// launches on the caller's stream.  Nothing is enqueued unless every check passes.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "../../include/moe_mi355x.h"
+#include "common.hpp"
+
+namespace moe {
+hipError_t launch_route_topk(const float*, int64_t, int, int, int32_t*, float*, hipStream_t);
+hipError_t launch_permute(const uint16_t*, const int32_t*, int64_t, int, int, int, int, int64_t,
+                          int32_t*, int32_t*, int32_t*, int32_t*, uint16_t*, void*, hipStream_t);
+size_t permute_workspace_bytes(int64_t R, int E);
+hipError_t launch_grouped_glu_gemm(const uint16_t*, const uint16_t*, const int32_t*, int, int, int,
+                                   uint16_t*, hipStream_t);
+hipError_t launch_grouped_down_gemm(const uint16_t*, const uint16_t*, const int32_t*, int, int, int,
+                                    uint16_t*, hipStream_t);
+hipError_t launch_combine(const uint16_t*, const int32_t*, const float*, int64_t, int, int,
+                          int64_t, uint16_t*, hipStream_t);
+}  // namespace moe
+
+namespace {
+
+thread_local char g_err[512];
+
+moe_status fail(moe_status s, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+moe_status ok() {
+    g_err[0] = '\0';
+    return MOE_OK;
+}
+
+moe_status hip_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return ok();
+    return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+#define REQUIRE_PTR(p)                                                             \
+    do {                                                                           \
+        if (!(p)) return fail(MOE_ERR_NULL_POINTER, "%s is NULL", #p);             \
+        if (!aligned16(p))                                                         \
+            return fail(MOE_ERR_MISALIGNED_POINTER, "%s is not 16-byte aligned", #p); \
+    } while (0)
+
+moe_status check_ek(int32_t E, int32_t k) {
+    if (E < 1 || E > MOE_MAX_E) return fail(MOE_ERR_INVALID_SHAPE, "E=%d outside [1, %d]", E, MOE_MAX_E);
+    if (k < 1 || k > MOE_MAX_K || k > E)
+        return fail(MOE_ERR_INVALID_SHAPE, "k=%d outside [1, min(E=%d, %d)]", k, E, MOE_MAX_K);
+    return MOE_OK;
+}
+
+moe_status check_dim64(const char* name, int32_t v) {
+    if (v < 64 || v % 64 != 0)
+        return fail(MOE_ERR_INVALID_SHAPE, "%s=%d must be a positive multiple of 64", name, v);
+    return MOE_OK;
+}
+
+moe_status check_pmax(int64_t P_max) {
+    if (P_max < 1 || P_max >= ((int64_t)1 << 31))
+        return fail(MOE_ERR_SIZE_OVERFLOW, "P_max=%lld outside [1, 2^31)", (long long)P_max);
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(int s) {
+    switch (s) {
+        case MOE_OK: return "MOE_OK";
+        case MOE_ERR_NULL_POINTER: return "MOE_ERR_NULL_POINTER";
+        case MOE_ERR_INVALID_SHAPE: return "MOE_ERR_INVALID_SHAPE";
+        case MOE_ERR_INVALID_ALIGN: return "MOE_ERR_INVALID_ALIGN";
+        case MOE_ERR_SIZE_OVERFLOW: return "MOE_ERR_SIZE_OVERFLOW";
+        case MOE_ERR_MISALIGNED_POINTER: return "MOE_ERR_MISALIGNED_POINTER";
+        case MOE_ERR_WORKSPACE_TOO_SMALL: return "MOE_ERR_WORKSPACE_TOO_SMALL";
+        case MOE_ERR_HIP: return "MOE_ERR_HIP";
+        default: return "MOE_ERR_UNKNOWN";
+    }
+}
+
+const char* moe_last_error_message(void) { return g_err; }
+
+int64_t moe_padded_rows_max(int64_t T, int32_t k, int32_t E, int32_t align) {
+    if (T < 0 || k < 1 || E < 1 || align < 1 || T > ((int64_t)1 << 40)) return -1;
+    return T * k + (int64_t)E * (align - 1);
+}
+
+moe_status moe_permute_workspace_size(int64_t T, int32_t k, int32_t E, size_t* bytes) {
+    if (!bytes) return fail(MOE_ERR_NULL_POINTER, "bytes is NULL");
+    if (T < 0) return fail(MOE_ERR_INVALID_SHAPE, "T=%lld < 0", (long long)T);
+    moe_status s = check_ek(E, k);
+    if (s != MOE_OK) return s;
+    *bytes = moe::permute_workspace_bytes(T * k, E);
+    return ok();
+}
+
+moe_status moe_route_topk(const float* logits, int64_t T, int32_t E, int32_t k, int32_t* topk_idx,
+                          float* topk_w, moe_stream_t stream) {
+    REQUIRE_PTR(logits);
+    REQUIRE_PTR(topk_idx);
+    REQUIRE_PTR(topk_w);
+    if (T < 0 || T >= ((int64_t)1 << 31)) return fail(MOE_ERR_INVALID_SHAPE, "T=%lld outside [0, 2^31)", (long long)T);
+    moe_status s = check_ek(E, k);
+    if (s != MOE_OK) return s;
+    return hip_status(moe::launch_route_topk(logits, T, E, k, topk_idx, topk_w, (hipStream_t)stream),
+                      "moe_route_topk launch");
+}
+
+moe_status moe_permute(const moe_bf16* x, const int32_t* topk_idx, int64_t T, int32_t H, int32_t E,
+                       int32_t k, int32_t align, int64_t P_max, int32_t* expert_counts,
+                       int32_t* expert_offsets, int32_t* route_row, int32_t* row_token,
+                       moe_bf16* x_perm, void* workspace, size_t workspace_bytes,
+                       moe_stream_t stream) {
+    REQUIRE_PTR(x);
+    REQUIRE_PTR(topk_idx);
+    REQUIRE_PTR(expert_counts);
+    REQUIRE_PTR(expert_offsets);
+    REQUIRE_PTR(route_row);
+    REQUIRE_PTR(row_token);
+    REQUIRE_PTR(x_perm);
+    REQUIRE_PTR(workspace);
+    if (T < 0) return fail(MOE_ERR_INVALID_SHAPE, "T=%lld < 0", (long long)T);
+    moe_status s = check_ek(E, k);
+    if (s != MOE_OK) return s;
+    if ((s = check_dim64("H", H)) != MOE_OK) return s;
+    if (align < 1 || align > MOE_MAX_ALIGN || (align & (align - 1)) != 0)
+        return fail(MOE_ERR_INVALID_ALIGN, "align=%d is not a power of two in [1, %d]", align, MOE_MAX_ALIGN);
+    if ((s = check_pmax(P_max)) != MOE_OK) return s;
+    const int64_t need = moe_padded_rows_max(T, k, E, align);
+    if (need < 0 || need > P_max)
+        return fail(MOE_ERR_SIZE_OVERFLOW, "P_max=%lld < T*k + E*(align-1) = %lld", (long long)P_max,
+                    (long long)need);
+    const size_t ws = moe::permute_workspace_bytes(T * k, E);
+    if (workspace_bytes < ws)
+        return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", workspace_bytes, ws);
+    return hip_status(moe::launch_permute(x, topk_idx, T, H, E, k, align, P_max, expert_counts,
+                                          expert_offsets, route_row, row_token, x_perm, workspace,
+                                          (hipStream_t)stream),
+                      "moe_permute launch");
+}
+
+static moe_status check_gemm(const void* a, const void* w, const int32_t* counts,
+                             const int32_t* offsets, int32_t E, int32_t H, int32_t I,
+                             int64_t P_max, const void* out) {
+    REQUIRE_PTR(a);
+    REQUIRE_PTR(w);
+    REQUIRE_PTR(counts);
+    REQUIRE_PTR(offsets);
+    REQUIRE_PTR(out);
+    if (E < 1 || E > MOE_MAX_E) return fail(MOE_ERR_INVALID_SHAPE, "E=%d outside [1, %d]", E, MOE_MAX_E);
+    moe_status s;
+    if ((s = check_dim64("H", H)) != MOE_OK) return s;
+    if ((s = check_dim64("I", I)) != MOE_OK) return s;
+    return check_pmax(P_max);
+}
+
+moe_status moe_grouped_glu_gemm(const moe_bf16* x_perm, const moe_bf16* w_gate_up,
+                                const int32_t* expert_counts, const int32_t* expert_offsets,
+                                int32_t E, int32_t H, int32_t I, int64_t P_max, moe_bf16* h,
+                                moe_stream_t stream) {
+    moe_status s = check_gemm(x_perm, w_gate_up, expert_counts, expert_offsets, E, H, I, P_max, h);
+    if (s != MOE_OK) return s;
+    return hip_status(moe::launch_grouped_glu_gemm(x_perm, w_gate_up, expert_offsets, E, H, I, h,
+                                                   (hipStream_t)stream),
+                      "moe_grouped_glu_gemm launch");
+}
+
+moe_status moe_grouped_down_gemm(const moe_bf16* h, const moe_bf16* w_down,
+                                 const int32_t* expert_counts, const int32_t* expert_offsets,
+                                 int32_t E, int32_t H, int32_t I, int64_t P_max, moe_bf16* y,
+                                 moe_stream_t stream) {
+    moe_status s = check_gemm(h, w_down, expert_counts, expert_offsets, E, H, I, P_max, y);
+    if (s != MOE_OK) return s;
+    return hip_status(moe::launch_grouped_down_gemm(h, w_down, expert_offsets, E, H, I, y,
+                                                    (hipStream_t)stream),
+                      "moe_grouped_down_gemm launch");
+}
+
+moe_status moe_combine(const moe_bf16* y, const int32_t* route_row, const float* topk_w, int64_t T,
+                       int32_t H, int32_t k, int64_t P_max, moe_bf16* out, moe_stream_t stream) {
+    REQUIRE_PTR(y);
+    REQUIRE_PTR(route_row);
+    REQUIRE_PTR(topk_w);
+    REQUIRE_PTR(out);
+    if (T < 0 || T >= ((int64_t)1 << 31)) return fail(MOE_ERR_INVALID_SHAPE, "T=%lld outside [0, 2^31)", (long long)T);
+    if (k < 1 || k > MOE_MAX_K) return fail(MOE_ERR_INVALID_SHAPE, "k=%d outside [1, %d]", k, MOE_MAX_K);
+    moe_status s;
+    if ((s = check_dim64("H", H)) != MOE_OK) return s;
+    if ((s = check_pmax(P_max)) != MOE_OK) return s;
+    return hip_status(moe::launch_combine(y, route_row, topk_w, T, H, k, P_max, out, (hipStream_t)stream),
+                      "moe_combine launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,225 @@
+// permute.hip -- atomic-free counting sort of the routes into a padded,
+// expert-grouped row layout, and the gather of token rows into it.
+//
+// [Halo "Performance", Levers that help: the atomic-free expert permute;
+//  prime-rl PR 3885, Changes: one gather into the padded expert-grouped layout]
+//
+// The flat routes r = t*k + j are cut into chunks of kChunk routes, one chunk
+// per wavefront. Inside a wave, lanes holding the same expert id find each other
+// with ballots over the id's bits (match_peers): the lowest such lane is the
+// group's leader and popcount gives the group size and each lane's rank. Every
+// wave keeps its own histogram / cursor array in LDS, so no two lanes ever
+// update the same counter in one step and nothing needs an atomic.
+//
+//   1. hist:    per chunk c and expert e, the count hist[c][e]        (workspace)
+//   2. scan:    counts[e] = sum_c hist[c][e]; offsets = exclusive scan of the
+//               counts rounded up to align; hist[c][e] becomes the first row of
+//               chunk c's routes to e; pad rows get row_token = -1
+//   3. scatter: route_row[r] = base + rank among earlier equal ids (stable in r),
+//               row_token[route_row[r]] = r / k
+//   4. gather:  x_perm[p] = x[row_token[p]] (zero row if -1), 16-byte lanes
+#include "common.hpp"
+
+namespace moe {
+
+constexpr int kChunk = 1024;          // routes per wavefront chunk
+constexpr int kSteps = kChunk / kWave;
+constexpr int kScanThreads = 1024;
+
+static __device__ __forceinline__ int key_bits(int E) { return E <= 1 ? 0 : 32 - __clz(E - 1); }
+
+__global__ __launch_bounds__(256) void permute_hist_kernel(const int32_t* __restrict__ topk_idx,
+                                                           int64_t R, int E, int64_t nchunks,
+                                                           int32_t* __restrict__ hist) {
+    extern __shared__ int32_t lds_hist[];  // [4][E]
+    const int wave = threadIdx.x / kWave, lane = lane_id();
+    const int64_t c = (int64_t)blockIdx.x * 4 + wave;
+    if (c >= nchunks) return;
+    int32_t* h = lds_hist + wave * E;
+    for (int e = lane; e < E; e += kWave) h[e] = 0;
+    const int nbits = key_bits(E);
+    const int64_t r0 = c * kChunk;
+    for (int s = 0; s < kSteps; ++s) {
+        const int64_t r = r0 + s * kWave + lane;
+        const uint32_t id = r < R ? (uint32_t)topk_idx[r] : 0xffffffffu;
+        const bool active = id < (uint32_t)E;  // out-of-range ids take no part
+        const uint32_t key = active ? id : 0u;
+        const uint64_t peers = match_peers(key, nbits, active);
+        if (active && (__ffsll((unsigned long long)peers) - 1) == lane) h[key] += __popcll(peers);
+    }
+    int32_t* out = hist + c * E;
+    for (int e = lane; e < E; e += kWave) out[e] = h[e];
+}
+
+// One workgroup of 1024 threads. Thread (s, e) owns expert e over the s-th
+// contiguous range of chunks, so the chunk loop reads hist rows coalesced.
+__global__ __launch_bounds__(kScanThreads) void permute_scan_kernel(
+    int32_t* __restrict__ hist, int64_t nchunks, int E, int align, int64_t P_max,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ row_token) {
+    __shared__ int32_t part[kScanThreads];
+    __shared__ int32_t scan[kScanThreads];
+    __shared__ int32_t cnt[kScanThreads];
+    const int tid = threadIdx.x;
+    const int nseg = E >= kScanThreads ? 1 : kScanThreads / E;
+    const int e = tid % E, s = tid / E;
+    const bool owner = s < nseg;
+    const int64_t per = (nchunks + nseg - 1) / nseg;
+    const int64_t c0 = owner ? s * per : 0;
+    const int64_t c1 = owner ? (c0 + per < nchunks ? c0 + per : nchunks) : 0;
+
+    int32_t sum = 0;
+    for (int64_t c = c0; c < c1; ++c) sum += hist[c * E + e];
+    if (owner) part[s * E + e] = sum;
+    __syncthreads();
+
+    int32_t padded = 0;
+    if (tid < E) {
+        int32_t run = 0;
+        for (int q = 0; q < nseg; ++q) {
+            const int32_t v = part[q * E + tid];
+            part[q * E + tid] = run;
+            run += v;
+        }
+        cnt[tid] = run;
+        counts[tid] = run;
+        padded = (run + align - 1) / align * align;
+    }
+    // inclusive scan of the padded sizes over experts (Hillis-Steele)
+    scan[tid] = padded;
+    __syncthreads();
+    for (int d = 1; d < kScanThreads; d <<= 1) {
+        const int32_t v = tid >= d ? scan[tid - d] : 0;
+        __syncthreads();
+        scan[tid] += v;
+        __syncthreads();
+    }
+    const int32_t total = scan[E - 1];
+    if (tid < E) offsets[tid] = scan[tid] - padded;
+    if (tid == 0) offsets[E] = total;
+
+    if (owner) {
+        int32_t run = (scan[e] - ((cnt[e] + align - 1) / align * align)) + part[s * E + e];
+        for (int64_t c = c0; c < c1; ++c) {
+            const int32_t v = hist[c * E + e];
+            hist[c * E + e] = run;
+            run += v;
+        }
+    }
+    // pad rows inside each segment, then every row past the last segment
+    if (tid < E) {
+        const int32_t end = scan[tid];
+        for (int32_t p = end - ((cnt[tid] + align - 1) / align * align) + cnt[tid]; p < end; ++p)
+            row_token[p] = -1;
+    }
+    for (int64_t p = (int64_t)total + tid; p < P_max; p += kScanThreads) row_token[p] = -1;
+}
+
+__global__ __launch_bounds__(256) void permute_scatter_kernel(const int32_t* __restrict__ topk_idx,
+                                                              int64_t R, int E, int k,
+                                                              int64_t nchunks,
+                                                              const int32_t* __restrict__ base,
+                                                              int32_t* __restrict__ route_row,
+                                                              int32_t* __restrict__ row_token) {
+    extern __shared__ int32_t lds_cursor[];  // [4][E]
+    const int wave = threadIdx.x / kWave, lane = lane_id();
+    const int64_t c = (int64_t)blockIdx.x * 4 + wave;
+    if (c >= nchunks) return;
+    int32_t* cur = lds_cursor + wave * E;
+    for (int e = lane; e < E; e += kWave) cur[e] = base[c * E + e];
+    const int nbits = key_bits(E);
+    const uint64_t lt = lanemask_lt();
+    const int64_t r0 = c * kChunk;
+    for (int s = 0; s < kSteps; ++s) {
+        const int64_t r = r0 + s * kWave + lane;
+        const uint32_t id = r < R ? (uint32_t)topk_idx[r] : 0xffffffffu;
+        const bool active = id < (uint32_t)E;
+        const uint32_t key = active ? id : 0u;
+        const uint64_t peers = match_peers(key, nbits, active);
+        if (active) {
+            const int32_t dest = cur[key] + __popcll(peers & lt);
+            route_row[r] = dest;
+            row_token[dest] = (int32_t)(r / k);
+        } else if (r < R) {
+            route_row[r] = -1;  // an out-of-range id gets no row
+        }
+        if (active && (__ffsll((unsigned long long)peers) - 1) == lane) cur[key] += __popcll(peers);
+    }
+}
+
+// One wavefront per row; each lane moves 16-byte pieces, up to kPieces of them
+// in flight before any store.
+constexpr int kPieces = 4;
+
+__global__ __launch_bounds__(256) void permute_gather_kernel(const uint4* __restrict__ x,
+                                                             const int32_t* __restrict__ row_token,
+                                                             const int32_t* __restrict__ offsets,
+                                                             int E, int pieces_per_row,
+                                                             uint4* __restrict__ x_perm) {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int64_t p = (int64_t)blockIdx.x * 4 + wave;
+    const int32_t used = offsets[E];
+    if (p >= used) return;
+    const int32_t t = row_token[p];
+    const int lane = lane_id();
+    uint4* dst = x_perm + p * pieces_per_row;
+    if (t < 0) {
+        const uint4 z = {0u, 0u, 0u, 0u};
+        for (int c = lane; c < pieces_per_row; c += kWave) dst[c] = z;
+        return;
+    }
+    const uint4* src = x + (int64_t)t * pieces_per_row;
+    for (int c0 = 0; c0 < pieces_per_row; c0 += kWave * kPieces) {
+        uint4 v[kPieces];
+#pragma unroll
+        for (int i = 0; i < kPieces; ++i) {
+            const int c = c0 + i * kWave + lane;
+            if (c < pieces_per_row) v[i] = src[c];
+        }
+#pragma unroll
+        for (int i = 0; i < kPieces; ++i) {
+            const int c = c0 + i * kWave + lane;
+            if (c < pieces_per_row) dst[c] = v[i];
+        }
+    }
+}
+
+int64_t permute_chunks(int64_t R) { return (R + kChunk - 1) / kChunk; }
+
+size_t permute_workspace_bytes(int64_t R, int E) {
+    const size_t b = (size_t)permute_chunks(R) * (size_t)E * sizeof(int32_t);
+    return (b + 255) / 256 * 256;
+}
+
+hipError_t launch_permute(const uint16_t* x, const int32_t* topk_idx, int64_t T, int H, int E,
+                          int k, int align, int64_t P_max, int32_t* counts, int32_t* offsets,
+                          int32_t* route_row, int32_t* row_token, uint16_t* x_perm,
+                          void* workspace, hipStream_t stream) {
+    const int64_t R = T * k;
+    const int64_t nchunks = permute_chunks(R);
+    int32_t* hist = (int32_t*)workspace;
+    const size_t lds = 4 * (size_t)E * sizeof(int32_t);
+    if (nchunks > 0) {
+        hipLaunchKernelGGL(permute_hist_kernel, dim3((unsigned)((nchunks + 3) / 4)), dim3(256), lds,
+                           stream, topk_idx, R, E, nchunks, hist);
+        hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+    }
+    hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, hist, nchunks,
+                       E, align, P_max, counts, offsets, row_token);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    if (nchunks > 0) {
+        hipLaunchKernelGGL(permute_scatter_kernel, dim3((unsigned)((nchunks + 3) / 4)), dim3(256),
+                           lds, stream, topk_idx, R, E, k, nchunks, (const int32_t*)hist,
+                           route_row, row_token);
+        err = hipGetLastError();
+        if (err != hipSuccess) return err;
+    }
+    const int pieces = H / 8;  // 16-byte pieces per row
+    hipLaunchKernelGGL(permute_gather_kernel, dim3((unsigned)((P_max + 3) / 4)), dim3(256), 0,
+                       stream, (const uint4*)x, (const int32_t*)row_token,
+                       (const int32_t*)offsets, E, pieces, (uint4*)x_perm);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -51,6 +51,8 @@ def _load(path: str):
     lib.moe_oracle_combine.argtypes = [_f64p, _i32p, _f64p, i64, i32, i32, i64, _f64p]
     lib.moe_oracle_forward.argtypes = [_u16p, _f32p, _u16p, _u16p, i64, i32, i32, i32, i32,
                                        _i64p, i64, _f64p]
+    lib.moe_oracle_num_threads.argtypes = []
+    lib.moe_oracle_num_threads.restype = ctypes.c_int
     for name in ("moe_oracle_route_topk", "moe_oracle_layout", "moe_oracle_gather",
                  "moe_oracle_glu", "moe_oracle_down", "moe_oracle_combine",
                  "moe_oracle_forward"):
@@ -66,6 +68,11 @@ def _lib():
             build_oracle()
         _LIB = _load(path)
     return _LIB
+
+
+def num_threads(lib=None) -> int:
+    """OpenMP threads the oracle's loops run on."""
+    return int((lib or _lib()).moe_oracle_num_threads())
 
 
 def _p(a: np.ndarray, ptype):

@@ -31,6 +31,7 @@
  * arguments (nothing is written then).
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -303,3 +304,6 @@ int moe_oracle_forward(const uint16_t *x, const float *logits, const uint16_t *w
     }
     return err ? ORACLE_EINVAL : 0;
 }
+
+/* Threads the OpenMP loops above use (for reporting the oracle's CPU time). */
+int moe_oracle_num_threads(void) { return omp_get_max_threads(); }

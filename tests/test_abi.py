@@ -1,0 +1,127 @@
+"""The C-ABI library: it loads, exports every symbol the header declares, and
+its host-side argument validation returns the documented status codes before
+anything is enqueued (CPU only: no call here reaches the GPU)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_mi355x.h")
+LIB = os.path.join(ROOT, "mixture_experts_routed_router_amd", "libmoe_mi355x.so")
+
+OK, NULLP, SHAPE, ALIGN, OVERFLOW, MISALIGNED, WORKSPACE, HIP = range(8)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        from mixture_experts_routed_router_amd.build import build
+        build()
+    lib = ctypes.CDLL(LIB)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    lib.moe_status_string.restype = ctypes.c_char_p
+    lib.moe_last_error_message.restype = ctypes.c_char_p
+    lib.moe_padded_rows_max.argtypes = [i64, i32, i32, i32]
+    lib.moe_padded_rows_max.restype = i64
+    lib.moe_permute_workspace_size.argtypes = [i64, i32, i32, ctypes.POINTER(sz)]
+    lib.moe_route_topk.argtypes = [vp, i64, i32, i32, vp, vp, vp]
+    lib.moe_permute.argtypes = [vp, vp, i64, i32, i32, i32, i32, i64, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.moe_grouped_glu_gemm.argtypes = [vp, vp, vp, vp, i32, i32, i32, i64, vp, vp]
+    lib.moe_grouped_down_gemm.argtypes = [vp, vp, vp, vp, i32, i32, i32, i64, vp, vp]
+    lib.moe_combine.argtypes = [vp, vp, vp, i64, i32, i32, i64, vp, vp]
+    return lib
+
+
+def test_header_declares_the_five_calls():
+    fns = declared_functions()
+    for name in ("moe_route_topk", "moe_permute", "moe_grouped_glu_gemm",
+                 "moe_grouped_down_gemm", "moe_combine"):
+        assert name in fns
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} declared in the header but not exported"
+
+
+def test_status_strings(lib):
+    assert lib.moe_status_string(0) == b"MOE_OK"
+    assert lib.moe_status_string(OVERFLOW) == b"MOE_ERR_SIZE_OVERFLOW"
+    assert lib.moe_status_string(99) == b"MOE_ERR_UNKNOWN"
+
+
+def test_padded_rows_and_workspace(lib):
+    assert lib.moe_padded_rows_max(8192, 8, 128, 32) == 8192 * 8 + 128 * 31
+    assert lib.moe_padded_rows_max(-1, 8, 128, 32) == -1
+    n = ctypes.c_size_t(0)
+    assert lib.moe_permute_workspace_size(8192, 8, 128, ctypes.byref(n)) == OK
+    assert n.value >= (8192 * 8 // 1024) * 128 * 4 and n.value % 256 == 0
+    assert lib.moe_permute_workspace_size(10, 3, 2, ctypes.byref(n)) == SHAPE  # k > E
+    assert lib.moe_permute_workspace_size(10, 2, 2, None) == NULLP
+
+
+FAKE = 0x10000  # a 16-byte-aligned non-null address; validation fails before any use
+
+
+def test_route_topk_validation(lib):
+    assert lib.moe_route_topk(None, 4, 8, 2, FAKE, FAKE, None) == NULLP
+    assert b"logits" in lib.moe_last_error_message()
+    assert lib.moe_route_topk(FAKE + 4, 4, 8, 2, FAKE, FAKE, None) == MISALIGNED
+    assert lib.moe_route_topk(FAKE, 4, 8, 9, FAKE, FAKE, None) == SHAPE       # k > E
+    assert lib.moe_route_topk(FAKE, 4, 8, 0, FAKE, FAKE, None) == SHAPE
+    assert lib.moe_route_topk(FAKE, 4, 2048, 8, FAKE, FAKE, None) == SHAPE    # E > 1024
+    assert lib.moe_route_topk(FAKE, 4, 64, 33, FAKE, FAKE, None) == SHAPE     # k > 32
+    assert lib.moe_route_topk(FAKE, -1, 8, 2, FAKE, FAKE, None) == SHAPE
+
+
+def _permute(lib, T=4, H=128, E=8, k=2, align=32, P_max=None, ws=1 << 20, x=FAKE):
+    if P_max is None:
+        P_max = T * k + E * (align - 1)
+    return lib.moe_permute(x, FAKE, T, H, E, k, align, P_max, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                           ws, None)
+
+
+def test_permute_validation(lib):
+    assert _permute(lib, x=None) == NULLP
+    assert _permute(lib, H=96) == SHAPE
+    assert _permute(lib, align=24) == ALIGN
+    assert _permute(lib, align=512) == ALIGN
+    assert _permute(lib, P_max=4 * 2 + 8 * 31 - 1) == OVERFLOW
+    assert _permute(lib, P_max=1 << 31) == OVERFLOW
+    assert _permute(lib, ws=0) == WORKSPACE
+    assert b"workspace" in lib.moe_last_error_message()
+
+
+def test_gemm_validation(lib):
+    for fn in (lib.moe_grouped_glu_gemm, lib.moe_grouped_down_gemm):
+        assert fn(FAKE, FAKE, FAKE, FAKE, 8, 128, 256, 1000, None, None) == NULLP
+        assert fn(FAKE, FAKE, FAKE, FAKE, 8, 100, 256, 1000, FAKE, None) == SHAPE   # H % 64
+        assert fn(FAKE, FAKE, FAKE, FAKE, 8, 128, 200, 1000, FAKE, None) == SHAPE   # I % 64
+        assert fn(FAKE, FAKE, FAKE, FAKE, 0, 128, 256, 1000, FAKE, None) == SHAPE
+        assert fn(FAKE, FAKE, FAKE, FAKE, 8, 128, 256, 0, FAKE, None) == OVERFLOW
+        assert fn(FAKE, FAKE + 8, FAKE, FAKE, 8, 128, 256, 1000, FAKE, None) == MISALIGNED
+
+
+def test_combine_validation(lib):
+    assert lib.moe_combine(FAKE, FAKE, FAKE, 4, 128, 2, 100, None, None) == NULLP
+    assert lib.moe_combine(FAKE, FAKE, FAKE, 4, 130, 2, 100, FAKE, None) == SHAPE
+    assert lib.moe_combine(FAKE, FAKE, FAKE, 4, 128, 33, 100, FAKE, None) == SHAPE
+    assert lib.moe_combine(FAKE, FAKE, FAKE, 4, 128, 2, 1 << 31, FAKE, None) == OVERFLOW
+
+
+def test_library_is_gfx950_only():
+    """The code object inside the library targets gfx950 and nothing else."""
+    data = open(LIB, "rb").read()
+    assert b"gfx950" in data
+    for other in (b"gfx942", b"gfx90a", b"gfx1100", b"sm_"):
+        assert b"amdgcn-amd-amdhsa--" + other not in data

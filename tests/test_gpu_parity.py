@@ -1,0 +1,318 @@
+"""GPU parity: every call of the HIP library, through its C ABI, against the CPU
+oracle on the same seeded inputs.  Index/layout results must match bit for bit;
+floating-point results within the tolerances documented in gpu_util.py.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mixture_experts_routed_router_amd import inputs as gen
+from gpu_util import (assert_close_bf16, dev, dev_bf16, host_bits, host_f64, sample_tokens)
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+# --------------------------------------------------------------------------------------
+# routing
+# --------------------------------------------------------------------------------------
+
+ROUTE_CASES = [
+    ("tiny", lambda: gen.draw_logits(gen.CONFIGS["tiny"]), 2),
+    ("gauss_E128_k8", lambda: np.random.default_rng(1).standard_normal((3000, 128)).astype(np.float32), 8),
+    ("gauss_E512_k10", lambda: np.random.default_rng(2).standard_normal((777, 512)).astype(np.float32), 10),
+    ("gauss_E32_k4", lambda: np.random.default_rng(3).standard_normal((129, 32)).astype(np.float32), 4),
+    ("ties_E16_k5", lambda: gen.tied_logits(500, 16, seed=4), 5),
+    ("ties2_E64_k8", lambda: gen.tied_logits(500, 64, seed=5, levels=2), 8),
+    ("k1_E40", lambda: np.random.default_rng(6).standard_normal((300, 40)).astype(np.float32), 1),
+    ("kE_E32", lambda: np.random.default_rng(7).standard_normal((100, 32)).astype(np.float32), 32),
+    ("E1_k1", lambda: np.random.default_rng(8).standard_normal((10, 1)).astype(np.float32), 1),
+    ("E1024_k32", lambda: np.random.default_rng(9).standard_normal((70, 1024)).astype(np.float32), 32),
+    ("E1000_k7", lambda: np.random.default_rng(10).standard_normal((70, 1000)).astype(np.float32), 7),
+    ("T1", lambda: np.random.default_rng(11).standard_normal((1, 128)).astype(np.float32), 8),
+    ("equal_logits", lambda: np.full((20, 24), -3.5, np.float32), 6),
+]
+
+
+@pytest.mark.parametrize("name,make,k", ROUTE_CASES, ids=[c[0] for c in ROUTE_CASES])
+def test_route_topk(gpu_lib, name, make, k):
+    _say(f"route_topk case {name}")
+    logits = make()
+    idx_ref, w_ref = oracle.route_topk(logits, k)
+    idx, w = gpu_lib.route_topk(dev(logits), k)
+    torch.cuda.synchronize()
+    assert (idx.cpu().numpy() == idx_ref).all()
+    assert np.max(np.abs(w.cpu().numpy().astype(np.float64) - w_ref)) <= 1e-6
+
+
+def test_route_topk_empty(gpu_lib):
+    idx, w = gpu_lib.route_topk(torch.empty((0, 16), dtype=torch.float32, device="cuda"), 4)
+    torch.cuda.synchronize()
+    assert idx.shape == (0, 4)
+
+
+# --------------------------------------------------------------------------------------
+# permute
+# --------------------------------------------------------------------------------------
+
+def _check_permute(gpu_lib, x_bits, topk_idx, E, align, full_rows=True):
+    T, H = x_bits.shape
+    k = topk_idx.shape[1]
+    P_max = T * k + E * (align - 1)
+    c_ref, o_ref, rr_ref, rt_ref = oracle.layout(topk_idx, E, align, P_max)
+    L = gpu_lib.permute(dev_bf16(x_bits), dev(topk_idx.astype(np.int32)), E, align, P_max)
+    torch.cuda.synchronize()
+    assert (L.counts.cpu().numpy() == c_ref).all()
+    assert (L.offsets.cpu().numpy() == o_ref).all()
+    assert (L.route_row.cpu().numpy() == rr_ref).all()
+    assert (L.row_token.cpu().numpy() == rt_ref).all()
+    used = int(o_ref[-1])
+    if full_rows:
+        xp = host_bits(L.x_perm[:used])
+        assert (xp == oracle.gather(x_bits, rt_ref, rows=used)).all()
+    else:  # sampled rows, pad rows included
+        rng = np.random.default_rng(0)
+        rows = np.unique(np.concatenate([rng.integers(0, used, 4096), np.where(rt_ref[:used] < 0)[0][:2048]]))
+        xp = host_bits(L.x_perm[dev(rows.astype(np.int64))])
+        assert (xp == oracle.gather(x_bits, rt_ref[rows], rows=len(rows))).all()
+    return L
+
+
+PERMUTE_CASES = [
+    # name, T, H, E, k, align, routing
+    ("tiny", 64, 128, 8, 2, 32, "gauss"),
+    ("balanced97", 1000, 256, 128, 8, 32, "balanced"),
+    ("align1", 777, 128, 40, 5, 1, "gauss"),
+    ("align8", 777, 128, 40, 5, 8, "gauss"),
+    ("align256", 300, 64, 16, 4, 256, "gauss"),
+    ("one_expert_takes_all", 500, 128, 16, 2, 32, "hot"),
+    ("zero_count_experts", 16, 128, 64, 2, 32, "gauss"),
+    ("H2880", 128, 2880, 32, 4, 32, "gauss"),
+    ("E1024", 700, 64, 1024, 16, 16, "gauss"),
+    ("E1", 50, 64, 1, 1, 32, "gauss"),
+    ("T1", 1, 192, 8, 2, 32, "gauss"),
+    ("several_chunks", 5000, 64, 128, 8, 32, "gauss"),
+]
+
+
+def _routing(kind, T, E, k, seed):
+    if kind == "balanced":
+        return gen.balanced_topk_idx(T, E, k)
+    logits = np.random.default_rng(seed).standard_normal((T, E)).astype(np.float32)
+    if kind == "hot":
+        logits[:, 3] += 100.0
+    idx, _ = oracle.route_topk(logits, k)
+    return idx
+
+
+@pytest.mark.parametrize("case", PERMUTE_CASES, ids=[c[0] for c in PERMUTE_CASES])
+def test_permute(gpu_lib, case):
+    name, T, H, E, k, align, kind = case
+    _say(f"permute case {name}")
+    x = gen.random_bf16((T, H), seed=T + H)
+    idx = _routing(kind, T, E, k, seed=len(name))
+    L = _check_permute(gpu_lib, x, idx, E, align)
+    if kind == "hot":
+        assert L.counts[3].item() == T
+
+
+def test_permute_empty(gpu_lib):
+    x = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
+    idx = torch.empty((0, 2), dtype=torch.int32, device="cuda")
+    L = gpu_lib.permute(x, idx, 8, 32)
+    torch.cuda.synchronize()
+    assert (L.counts.cpu() == 0).all() and (L.offsets.cpu() == 0).all()
+    assert (L.row_token.cpu() == -1).all()
+
+
+# --------------------------------------------------------------------------------------
+# grouped GEMMs, each on synthetic inputs of its own
+# --------------------------------------------------------------------------------------
+
+def _synthetic_layout(counts, align):
+    counts = np.asarray(counts, np.int32)
+    padded = (counts + align - 1) // align * align
+    offsets = np.concatenate([[0], np.cumsum(padded)]).astype(np.int32)
+    return counts, offsets
+
+
+def _rows_of(counts, offsets):
+    return np.concatenate([np.arange(offsets[e], offsets[e] + counts[e]) for e in range(len(counts))]
+                          + [np.zeros(0, np.int64)]).astype(np.int64)
+
+
+GEMM_CASES = [
+    # name, counts, align, H, I
+    ("ragged", [0, 1, 130, 257, 31, 64], 32, 256, 192),
+    ("tails_align8", [5, 0, 129, 3, 300], 8, 128, 128),
+    ("align1", [7, 1, 200], 1, 192, 64),
+    ("all_empty_but_one", [0, 0, 0, 500, 0], 32, 128, 256),
+    ("wide_H2880", [16, 9, 28, 0, 40], 32, 2880, 2880),
+    ("I640_H2560", [160, 114, 202], 32, 2560, 640),
+]
+
+
+@pytest.mark.parametrize("case", GEMM_CASES, ids=[c[0] for c in GEMM_CASES])
+def test_grouped_glu_gemm(gpu_lib, case):
+    name, counts, align, H, I = case
+    _say(f"glu gemm case {name}")
+    counts, offsets = _synthetic_layout(counts, align)
+    E, P = len(counts), int(offsets[-1])
+    P_max = P + 64
+    rows = _rows_of(counts, offsets)
+    x_perm = np.zeros((P_max, H), np.uint16)
+    x_perm[rows] = gen.random_bf16((len(rows), H), seed=1)
+    w_gu = gen.random_bf16((E, 2 * I, H), seed=2, std=0.02)
+    h = gpu_lib.grouped_glu_gemm(dev_bf16(x_perm), dev_bf16(w_gu), dev(counts), dev(offsets))
+    torch.cuda.synchronize()
+    h_ref = oracle.glu(x_perm, w_gu, counts, offsets, I)
+    hg = host_f64(h[:P])
+    assert_close_bf16(hg[rows], h_ref[rows], f"h[{name}]")
+    pad = np.setdiff1d(np.arange(P), rows)
+    assert (hg[pad] == 0).all()  # zero pad rows give silu(0) * 0 = 0
+
+
+@pytest.mark.parametrize("case", GEMM_CASES + [("N_tail_H320", [40, 70], 32, 320, 128)],
+                         ids=[c[0] for c in GEMM_CASES] + ["N_tail_H320"])
+def test_grouped_down_gemm(gpu_lib, case):
+    name, counts, align, H, I = case
+    _say(f"down gemm case {name}")
+    counts, offsets = _synthetic_layout(counts, align)
+    E, P = len(counts), int(offsets[-1])
+    P_max = P + 64
+    rows = _rows_of(counts, offsets)
+    h = np.zeros((P_max, I), np.uint16)
+    h[rows] = gen.random_bf16((len(rows), I), seed=3)
+    w_d = gen.random_bf16((E, H, I), seed=4, std=0.02)
+    y = gpu_lib.grouped_down_gemm(dev_bf16(h), dev_bf16(w_d), dev(counts), dev(offsets))
+    torch.cuda.synchronize()
+    y_ref = oracle.down(gen.bf16_bits_to_f32(h).astype(np.float64), w_d, counts, offsets)
+    assert_close_bf16(host_f64(y[:P])[rows], y_ref[rows], f"y[{name}]")
+
+
+# --------------------------------------------------------------------------------------
+# combine
+# --------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T,H,E,k", [(64, 128, 8, 2), (300, 2880, 32, 4), (257, 640, 512, 10),
+                                     (100, 64, 40, 32), (1, 2048, 128, 8)])
+def test_combine(gpu_lib, T, H, E, k):
+    _say(f"combine case T={T} H={H} E={E} k={k}")
+    logits = np.random.default_rng(T).standard_normal((T, E)).astype(np.float32)
+    idx, w64 = oracle.route_topk(logits, k)
+    w32 = w64.astype(np.float32)  # the weights both sides use
+    counts, offsets, route_row, _ = oracle.layout(idx, E, 32)
+    P_max = T * k + E * 31
+    y = gen.random_bf16((P_max, H), seed=5)
+    out = gpu_lib.combine(dev_bf16(y), dev(route_row), dev(w32))
+    torch.cuda.synchronize()
+    ref = oracle.combine(gen.bf16_bits_to_f32(y).astype(np.float64), route_row, w32.astype(np.float64))
+    assert_close_bf16(host_f64(out), ref, "out")
+
+
+def test_identity_experts(gpu_lib):
+    """permute -> combine on the gathered rows themselves (identity experts)
+    returns x bit for bit: k = 1 has weight 1, and for k > 1 the fp32 weight sum
+    differs from 1 by far less than half a bf16 ulp."""
+    for T, H, E, k in [(256, 512, 16, 1), (256, 512, 16, 4), (300, 2880, 32, 4), (1000, 2048, 128, 8)]:
+        x = gen.random_bf16((T, H), seed=T)
+        logits = np.random.default_rng(k).standard_normal((T, E)).astype(np.float32)
+        xd, ld = dev_bf16(x), dev(logits)
+        idx, w = gpu_lib.route_topk(ld, k)
+        L = gpu_lib.permute(xd, idx, E, 32)
+        out = gpu_lib.combine(L.x_perm, L.route_row, w)
+        torch.cuda.synchronize()
+        assert (host_bits(out) == x).all(), (T, H, E, k)
+
+
+# --------------------------------------------------------------------------------------
+# the whole layer
+# --------------------------------------------------------------------------------------
+
+def _run_layer(gpu_lib, d, stream=None):
+    cfg = d["cfg"]
+    layer = gpu_lib.MoELayer(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.align)
+    args = (dev_bf16(d["x"]), dev(d["logits"]), dev_bf16(d["w_gu"]), dev_bf16(d["w_d"]))
+    if stream is None:
+        layer(*args)
+    else:
+        with torch.cuda.stream(stream):
+            layer(*args)
+        stream.synchronize()
+    torch.cuda.synchronize()
+    return layer
+
+
+def _check_layer(gpu_lib, d, n_tokens=None, full_rows=True):
+    cfg = d["cfg"]
+    layer = _run_layer(gpu_lib, d)
+    idx_ref, w_ref = oracle.route_topk(d["logits"], cfg.k)
+    assert (layer.topk_idx.cpu().numpy() == idx_ref).all()
+    assert np.max(np.abs(layer.topk_w.cpu().numpy() - w_ref)) <= 1e-6
+    c_ref, o_ref, rr_ref, rt_ref = oracle.layout(idx_ref, cfg.E, cfg.align, layer.P_max)
+    L = layer.layout
+    assert (L.counts.cpu().numpy() == c_ref).all()
+    assert (L.offsets.cpu().numpy() == o_ref).all()
+    assert (L.route_row.cpu().numpy() == rr_ref).all()
+    assert (L.row_token.cpu().numpy() == rt_ref).all()
+    used = int(o_ref[-1])
+    if full_rows:
+        assert (host_bits(L.x_perm[:used]) == oracle.gather(d["x"], rt_ref, rows=used)).all()
+    toks = sample_tokens(cfg.T, n_tokens or cfg.T, cfg.seed)
+    ref = oracle.forward(d["x"], d["logits"], d["w_gu"], d["w_d"], cfg.k, tokens=toks)
+    got = host_f64(layer.out[dev(toks.astype(np.int64))])
+    rel = assert_close_bf16(got, ref, f"out[{cfg.name}]")
+    _say(f"  {cfg.name}: max|d|/max|ref| = {rel:.3e} over {len(toks)} tokens")
+    return layer
+
+
+SMALL_LAYERS = [
+    gen.CONFIGS["tiny"],
+    gen.CONFIGS["tiny"].with_(name="tiny_hot", weight_std=0.2, seed=10),
+    gen.MoEConfig("T1", 1, 128, 8, 2, 64, 20, "gaussian"),
+    gen.MoEConfig("k1", 200, 256, 16, 1, 128, 21, "gaussian"),
+    gen.MoEConfig("k_eq_E", 100, 128, 4, 4, 128, 22, "gaussian"),
+    gen.MoEConfig("E1", 100, 128, 1, 1, 192, 23, "gaussian"),
+    gen.MoEConfig("sparse_experts", 12, 192, 64, 2, 128, 24, "gaussian"),
+    gen.MoEConfig("align8", 333, 256, 24, 3, 320, 25, "gaussian", align=8),
+    gen.MoEConfig("skewed_small", 2048, 256, 32, 4, 128, 26, "zipf"),
+]
+
+
+@pytest.mark.parametrize("cfg", SMALL_LAYERS, ids=[c.name for c in SMALL_LAYERS])
+def test_layer_small(gpu_lib, cfg):
+    _say(f"layer case {cfg.name}")
+    _check_layer(gpu_lib, gen.make_inputs(cfg))
+
+
+# name -> tokens compared against the per-token oracle (routing and layout are
+# always compared in full)
+FULL_SIZE = [("gpt_oss_20b_small_m", None), ("qwen3_30b_a3b", 512), ("fine_grained_512", 384),
+             ("skewed_zipf", 384)]
+
+
+@pytest.mark.parametrize("name,n", FULL_SIZE, ids=[c[0] for c in FULL_SIZE])
+def test_layer_full_size(gpu_lib, name, n):
+    _say(f"full-size layer {name}: generating inputs")
+    d = gen.make_inputs(name)
+    _say(f"full-size layer {name}: running")
+    _check_layer(gpu_lib, d, n_tokens=n, full_rows=(name == "gpt_oss_20b_small_m"))
+
+
+def test_layer_deterministic_and_streams(gpu_lib):
+    d = gen.make_inputs(gen.MoEConfig("det", 1500, 512, 64, 6, 256, 30, "zipf"))
+    a = _run_layer(gpu_lib, d)
+    b = _run_layer(gpu_lib, d, stream=torch.cuda.Stream())
+    for name in ("topk_idx", "topk_w", "h", "y", "out"):
+        assert torch.equal(getattr(a, name).view(torch.int16) if getattr(a, name).dtype == torch.bfloat16
+                           else getattr(a, name),
+                           getattr(b, name).view(torch.int16) if getattr(b, name).dtype == torch.bfloat16
+                           else getattr(b, name)), name
+    used = int(a.layout.offsets[-1].item())
+    assert torch.equal(a.layout.x_perm[:used].view(torch.int16), b.layout.x_perm[:used].view(torch.int16))
