@@ -28,7 +28,8 @@
  *
  * Conventions
  *   - Every tensor pointer is a DEVICE pointer, row-major, 16-byte aligned.
- *     bf16 tensors are raw 16-bit values (moe_bf16).
+ *     bf16 tensors are raw 16-bit values (moe_bf16). When T == 0, pointers to
+ *     buffers whose size is proportional to T may be NULL.
  *   - The caller owns every buffer. The library never allocates, frees or keeps
  *     a pointer after a call returns; buffers must stay alive until the stream
  *     work that uses them completes.

@@ -50,6 +50,15 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
             return fail(MOE_ERR_MISALIGNED_POINTER, "%s is not 16-byte aligned", #p); \
     } while (0)
 
+// Buffers whose size is proportional to T may be NULL when T == 0 (an empty
+// allocation has no address); alignment is still required when present.
+#define REQUIRE_PTR_UNLESS_EMPTY(p, empty)                                         \
+    do {                                                                           \
+        if (!(empty)) REQUIRE_PTR(p);                                              \
+        else if ((p) && !aligned16(p))                                             \
+            return fail(MOE_ERR_MISALIGNED_POINTER, "%s is not 16-byte aligned", #p); \
+    } while (0)
+
 moe_status check_ek(int32_t E, int32_t k) {
     if (E < 1 || E > MOE_MAX_E) return fail(MOE_ERR_INVALID_SHAPE, "E=%d outside [1, %d]", E, MOE_MAX_E);
     if (k < 1 || k > MOE_MAX_K || k > E)
@@ -105,9 +114,9 @@ moe_status moe_permute_workspace_size(int64_t T, int32_t k, int32_t E, size_t* b
 
 moe_status moe_route_topk(const float* logits, int64_t T, int32_t E, int32_t k, int32_t* topk_idx,
                           float* topk_w, moe_stream_t stream) {
-    REQUIRE_PTR(logits);
-    REQUIRE_PTR(topk_idx);
-    REQUIRE_PTR(topk_w);
+    REQUIRE_PTR_UNLESS_EMPTY(logits, T == 0);
+    REQUIRE_PTR_UNLESS_EMPTY(topk_idx, T == 0);
+    REQUIRE_PTR_UNLESS_EMPTY(topk_w, T == 0);
     if (T < 0 || T >= ((int64_t)1 << 31)) return fail(MOE_ERR_INVALID_SHAPE, "T=%lld outside [0, 2^31)", (long long)T);
     moe_status s = check_ek(E, k);
     if (s != MOE_OK) return s;
@@ -120,14 +129,14 @@ moe_status moe_permute(const moe_bf16* x, const int32_t* topk_idx, int64_t T, in
                        int32_t* expert_offsets, int32_t* route_row, int32_t* row_token,
                        moe_bf16* x_perm, void* workspace, size_t workspace_bytes,
                        moe_stream_t stream) {
-    REQUIRE_PTR(x);
-    REQUIRE_PTR(topk_idx);
+    REQUIRE_PTR_UNLESS_EMPTY(x, T == 0);
+    REQUIRE_PTR_UNLESS_EMPTY(topk_idx, T == 0);
     REQUIRE_PTR(expert_counts);
     REQUIRE_PTR(expert_offsets);
-    REQUIRE_PTR(route_row);
+    REQUIRE_PTR_UNLESS_EMPTY(route_row, T == 0);
     REQUIRE_PTR(row_token);
     REQUIRE_PTR(x_perm);
-    REQUIRE_PTR(workspace);
+    REQUIRE_PTR_UNLESS_EMPTY(workspace, T == 0);
     if (T < 0) return fail(MOE_ERR_INVALID_SHAPE, "T=%lld < 0", (long long)T);
     moe_status s = check_ek(E, k);
     if (s != MOE_OK) return s;
@@ -188,9 +197,9 @@ moe_status moe_grouped_down_gemm(const moe_bf16* h, const moe_bf16* w_down,
 moe_status moe_combine(const moe_bf16* y, const int32_t* route_row, const float* topk_w, int64_t T,
                        int32_t H, int32_t k, int64_t P_max, moe_bf16* out, moe_stream_t stream) {
     REQUIRE_PTR(y);
-    REQUIRE_PTR(route_row);
-    REQUIRE_PTR(topk_w);
-    REQUIRE_PTR(out);
+    REQUIRE_PTR_UNLESS_EMPTY(route_row, T == 0);
+    REQUIRE_PTR_UNLESS_EMPTY(topk_w, T == 0);
+    REQUIRE_PTR_UNLESS_EMPTY(out, T == 0);
     if (T < 0 || T >= ((int64_t)1 << 31)) return fail(MOE_ERR_INVALID_SHAPE, "T=%lld outside [0, 2^31)", (long long)T);
     if (k < 1 || k > MOE_MAX_K) return fail(MOE_ERR_INVALID_SHAPE, "k=%d outside [1, %d]", k, MOE_MAX_K);
     moe_status s;

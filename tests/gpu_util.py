@@ -4,10 +4,12 @@ results back, and the comparison rules.
 Comparison rules (per element, over the compared region):
   * index and layout arrays, and bit copies: equal bit for bit;
   * topk_w: |gpu - ref| <= 1e-6;
-  * bf16 outputs: |gpu - ref| <= 1e-2 * max|ref| + 1e-3 (the gate), and also
-    max|gpu - ref| <= 2^-8 * max|ref|: every step rounds its result to bf16 once
-    (at most half an ulp, 2^-9 of the value) on top of fp32 sums whose error is
-    orders of magnitude smaller, so any larger error is a real mistake.
+  * bf16 outputs: |gpu - ref| <= 1e-2 * max|ref| + 1e-3 (the gate), and, for a
+    single step, also max|gpu - ref| <= 2^-8 * max|ref|: one step rounds its
+    result to bf16 once (at most half an ulp, 2^-9 of the value) on top of fp32
+    sums whose error is orders of magnitude smaller, so any larger error is a
+    real mistake.  The whole layer rounds three times (h, y, out) and is held to
+    the gate only.
 """
 from __future__ import annotations
 

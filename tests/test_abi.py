@@ -82,6 +82,9 @@ def test_route_topk_validation(lib):
     assert lib.moe_route_topk(FAKE, 4, 2048, 8, FAKE, FAKE, None) == SHAPE    # E > 1024
     assert lib.moe_route_topk(FAKE, 4, 64, 33, FAKE, FAKE, None) == SHAPE     # k > 32
     assert lib.moe_route_topk(FAKE, -1, 8, 2, FAKE, FAKE, None) == SHAPE
+    # no tokens: T-sized buffers may be NULL, and nothing is launched
+    assert lib.moe_route_topk(None, 0, 8, 2, None, None, None) == OK
+    assert lib.moe_route_topk(FAKE + 4, 0, 8, 2, None, None, None) == MISALIGNED
 
 
 def _permute(lib, T=4, H=128, E=8, k=2, align=32, P_max=None, ws=1 << 20, x=FAKE):

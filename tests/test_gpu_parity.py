@@ -267,7 +267,9 @@ def _check_layer(gpu_lib, d, n_tokens=None, full_rows=True):
     toks = sample_tokens(cfg.T, n_tokens or cfg.T, cfg.seed)
     ref = oracle.forward(d["x"], d["logits"], d["w_gu"], d["w_d"], cfg.k, tokens=toks)
     got = host_f64(layer.out[dev(toks.astype(np.int64))])
-    rel = assert_close_bf16(got, ref, f"out[{cfg.name}]")
+    # the layer rounds to bf16 three times (h, y, out), so only the layer gate
+    # applies here; the per-call tests hold each step to one rounding
+    rel = assert_close_bf16(got, ref, f"out[{cfg.name}]", tight=False)
     _say(f"  {cfg.name}: max|d|/max|ref| = {rel:.3e} over {len(toks)} tokens")
     return layer
 
@@ -309,10 +311,15 @@ def test_layer_deterministic_and_streams(gpu_lib):
     d = gen.make_inputs(gen.MoEConfig("det", 1500, 512, 64, 6, 256, 30, "zipf"))
     a = _run_layer(gpu_lib, d)
     b = _run_layer(gpu_lib, d, stream=torch.cuda.Stream())
-    for name in ("topk_idx", "topk_w", "h", "y", "out"):
-        assert torch.equal(getattr(a, name).view(torch.int16) if getattr(a, name).dtype == torch.bfloat16
-                           else getattr(a, name),
-                           getattr(b, name).view(torch.int16) if getattr(b, name).dtype == torch.bfloat16
-                           else getattr(b, name)), name
-    used = int(a.layout.offsets[-1].item())
-    assert torch.equal(a.layout.x_perm[:used].view(torch.int16), b.layout.x_perm[:used].view(torch.int16))
+    used = int(a.layout.offsets[-1].item())   # rows past offsets[E] are never written
+
+    def bits(t):
+        return t.view(torch.int16) if t.dtype == torch.bfloat16 else t
+
+    for name in ("topk_idx", "topk_w", "out"):
+        assert torch.equal(bits(getattr(a, name)), bits(getattr(b, name))), name
+    for name in ("h", "y"):
+        assert torch.equal(bits(getattr(a, name)[:used]), bits(getattr(b, name)[:used])), name
+    assert torch.equal(bits(a.layout.x_perm[:used]), bits(b.layout.x_perm[:used]))
+    for name in ("counts", "offsets", "route_row", "row_token"):
+        assert torch.equal(getattr(a.layout, name), getattr(b.layout, name)), name
