@@ -8,47 +8,74 @@
 //
 // GLU variant (gate/up projections): W[e] holds 2N rows, gate rows [0, N) and up
 // rows [N, 2N); each tile loads matching gate and up rows, so each wave holds
-// g and u for the same (row, column) in the same register and the SwiGLU
-// h = silu(g) * u runs in the epilogue without leaving registers [Halo,
+// g and u for the same (row, column) in the same register position and the
+// SwiGLU h = silu(g) * u runs in the epilogue without leaving registers [Halo,
 // Levers that help: fused GLU; prime-rl PR 3885, Changes: gate and up as one
-// GEMM ahead of a clamped SwiGLU -- here unclamped].
+// GEMM ahead of a SwiGLU].
 //
-// Scheduling: a persistent grid walks the tile list in expert-major order
-// (expert, then column tile, then row tile), so an expert's weights are read
-// about once and stay in L2 while its row tiles run [prime-rl PR 3885,
-// Required kernel commits: expert-major task order].  Tiles are dealt in
-// contiguous runs per XCD (workgroup b runs on XCD b % 8), so each expert's
-// tiles share one XCD's L2.  Counts and offsets are read on the device; an
-// expert with no rows owns no tiles and reads no weights [PocketLLM "Qwen4-Exp
+// Scheduling: a persistent grid (one workgroup per CU) walks the tile list in
+// expert-major order (expert, then column tile, then row tile), so an expert's
+// weights are read about once and stay in L2 while its row tiles run [prime-rl
+// PR 3885, Required kernel commits: expert-major task order].  The tile list is
+// dealt in contiguous runs per XCD (workgroup b runs on XCD b % 8), so each
+// expert's tiles share one XCD's L2.  Counts and offsets are read on the device;
+// an expert with no rows owns no tiles and reads no weights [PocketLLM "Qwen4-Exp
 // Heterogeneous TP4 Performance", Confirmed architecture decisions].  No
 // workgroup ever waits on another.
 //
-// Tile: 128 rows x 128 W-rows x 64 k, 4 waves in a 2x2 grid, each wave 64 rows x
-// two 32-column MFMA blocks (v_mfma_f32_32x32x16_bf16), LDS double-buffered with
-// an XOR swizzle of 16-byte pieces so the MFMA operand reads are free of bank
-// conflicts.  The output tile goes through LDS so that global stores are whole
-// 16-byte pieces.
+// Tile: 256 rows x 256 W-rows, k in steps of 32 through a 4-stage LDS ring that
+// is filled by direct global->LDS loads (no register staging). 8 waves (two per
+// SIMD, so one wave's MFMAs cover the other's waits) in a 2x4 grid; each wave
+// owns 128 rows x 64 W-rows = 4x2 blocks of v_mfma_f32_32x32x16_bf16 (128
+// accumulator registers).  16-byte pieces are XOR-swizzled in LDS so that the
+// MFMA operand reads are conflict-free.  The output tile is staged through LDS
+// so global stores are whole 16-byte pieces.
 #include "common.hpp"
 
 namespace moe {
 
-constexpr int BM = 128;  // rows per tile
-constexpr int BN = 128;  // W rows per tile (GLU: 64 gate + 64 up)
-constexpr int BK = 64;   // k per stage
-constexpr int kGemmThreads = 256;
+constexpr int BM = 256;       // rows per tile
+constexpr int BN = 256;       // W rows per tile (GLU: 128 gate + 128 up)
+#ifndef MOE_GEMM_BK
+#define MOE_GEMM_BK 32
+#endif
+#ifndef MOE_GEMM_STAGES
+#define MOE_GEMM_STAGES 4
+#endif
+constexpr int BK = MOE_GEMM_BK;          // k per stage
+constexpr int STAGES = MOE_GEMM_STAGES;  // LDS ring depth
+constexpr int PR = BK / 8;               // 16-byte pieces per row of a stage
+constexpr int RPB = 64 / PR;             // rows filled by one wave-wide 1 KB load
+constexpr int KSTEPS = BK / 16;          // MFMA k-steps per stage
+constexpr int kWaves = 8;                          // 2 per SIMD
+constexpr int kGemmThreads = kWaves * 64;
+constexpr int WGN = 4;                             // wave grid: 2 (rows) x 4 (W rows)
+constexpr int WTN = BN / WGN;                      // 64 W rows (output columns) per wave
 constexpr int kMaxE = 1024;
-constexpr int kTileElems = BM * BK;  // bf16 elements of one operand tile
+constexpr int kAElems = BM * BK;                   // bf16 elements of one A stage (16 KB)
+constexpr int kBElems = BN * BK;                   // one B stage (16 KB)
+constexpr int kStageElems = kAElems + kBElems;
+constexpr int kLdsElems = STAGES * kStageElems;    // 128 KB
+constexpr int kPiecesPerThread = (BM * PR) / kGemmThreads;  // of A (and of B) per stage
+constexpr int kLoadsPerStage = 2 * kPiecesPerThread;        // per thread: A + B 16-byte loads
+static_assert(BM == BN, "A and B stages share one load layout");
+static_assert(kLoadsPerStage * (STAGES - 2) < 64, "vmcnt is 6 bits");
+// The epilogue stages each wave's 128 x WTN bf16 output tile through the LDS ring;
+// it must fit, or it would overwrite the tile tables that follow the ring in LDS.
+static_assert(kWaves * 128 * WTN <= kLdsElems, "epilogue staging must fit in the LDS ring");
 
-// Piece (16 bytes = 8 bf16) c of row `row` of a [rows][64] tile lives at piece
-// c ^ swz(row). Consecutive 8 rows get 8 distinct pieces; rows r and r+8 of a
-// 16-row group land in opposite halves of a 256-byte bank window.
-__device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
-__device__ __forceinline__ int tile_off(int row, int piece) {
-    return row * BK + ((piece ^ swz(row)) << 3);
+// Rows of a stage are BK bf16 = PR pieces of 16 bytes. Piece p of row r is stored
+// at piece p ^ swz(r). For the same logical piece of any 8 consecutive rows (a
+// 128-byte, 32-bank window) and of any 16 consecutive rows (a 256-byte, 64-bank
+// window), the physical 16-byte slots are all distinct.
+__device__ __forceinline__ int swz(int row) {
+    if (PR == 4) return ((row >> 1) ^ (row >> 2)) & 3;
+    return (row ^ (row >> 3)) & 7;  // PR == 8
 }
+static_assert(PR == 4 || PR == 8, "BK must be 32 or 64");
 
-// Exclusive scan of one int per thread over a 256-thread block.
-__device__ __forceinline__ int block_exclusive_scan(int v, int* tmp /* >= 4 ints */) {
+// Exclusive scan of one int per thread over the workgroup.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* tmp /* >= kWaves ints */) {
     const int lane = lane_id(), wave = threadIdx.x / kWave;
     int incl = v;
 #pragma unroll
@@ -64,24 +91,194 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* tmp /* >= 4 ints
     return before + incl - v;
 }
 
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const uint16_t* p) {
+    return (uint32_t)(size_t)(__attribute__((address_space(3))) const uint16_t*)p;
+}
+
+// 16 bytes per lane from global memory straight into LDS (global_load_lds_dwordx4,
+// SGPR base + VGPR byte offset): lane l's piece lands at LDS byte lds_base + 16*l.
+// Issued through inline asm so that the compiler neither waits for these loads
+// before unrelated LDS reads nor counts them; every wait is explicit below.
+// M0 is written only here in this kernel (checked in its ISA).
+__device__ __forceinline__ void dma16(uint32_t lds_base, const void* sbase, uint32_t voff) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+                 :: "s"(lds_base), "v"(voff), "s"(sbase) : "memory");
+}
+
+// Wait until at most N of this wave's vector-memory operations are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+
+// Workgroup barrier after this wave's LDS reads have returned. Unlike
+// __syncthreads() it does not drain the in-flight global->LDS loads.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Everything one tile needs that does not depend on the live row-block count.
+struct TileArgs {
+    const uint16_t* a_tile;   // A + row0 * K
+    const uint16_t* w_exp;    // W + e * (W rows per expert) * K
+    uint16_t* c_tile;         // C + row0 * N
+    int K, N, nt, rows_valid;
+};
+
+// One tile: the k loop through the LDS ring, then the epilogue. NV = number of
+// this wave's 32-row blocks that hold segment rows (compile-time, so every MFMA
+// in the loop is unconditional and the accumulators never leave AGPRs).
+template <bool GLU, int NV>
+__device__ __forceinline__ void run_tile(const TileArgs& ta, uint16_t* lds, int wave, int lane,
+                                         const int (&rd_off)[KSTEPS]) {
+    const int wm = wave / WGN, wn = wave % WGN;
+    const int K = ta.K, N = ta.N, nt = ta.nt, rows_valid = ta.rows_valid;
+
+    // ---- this thread's A and B pieces of every stage. Wave w, load i fills LDS
+    // rows [RPB*(n*w+i), +RPB) (n = kPiecesPerThread); lane l fills row
+    // RPB*(n*w+i) + l/PR, physical piece l%PR, i.e. logical piece (l%PR) ^ swz(row). Rows past the
+    // segment (or past N) read a valid row instead; those results are never stored.
+    // Byte offsets are relative to the tile's row 0 (A) and the expert (W), so they
+    // stay fixed while the k stage moves the SGPR base.
+    uint32_t offa[kPiecesPerThread], offb[kPiecesPerThread];
+#pragma unroll
+    for (int i = 0; i < kPiecesPerThread; ++i) {
+        const int r = RPB * (kPiecesPerThread * wave + i) + lane / PR;
+        const int piece = (lane % PR) ^ swz(r);
+        const int ar = r < rows_valid ? r : 0;
+        offa[i] = (uint32_t)((ar * K + piece * 8) * 2);
+        int wr;
+        if (GLU) {
+            const int c = nt * 128 + (r & 127);  // output column of this W row
+            const int cc = c < N ? c : N - 1;
+            wr = r < 128 ? cc : N + cc;
+        } else {
+            const int c = nt * BN + r;
+            wr = c < N ? c : N - 1;
+        }
+        offb[i] = (uint32_t)(((int64_t)wr * K + piece * 8) * 2);
+    }
+    const uint32_t lds0 = lds_addr(lds);
+    auto issue_stage = [&](int kt) {
+        const uint32_t sa = lds0 + (uint32_t)((kt % STAGES) * kStageElems * 2);
+        const uint32_t sb = sa + kAElems * 2;
+        const uint16_t* ga = ta.a_tile + kt * BK;
+        const uint16_t* gb = ta.w_exp + kt * BK;
+#pragma unroll
+        for (int i = 0; i < kPiecesPerThread; ++i) {
+            dma16(sa + (kPiecesPerThread * wave + i) * 1024, ga, offa[i]);
+            dma16(sb + (kPiecesPerThread * wave + i) * 1024, gb, offb[i]);
+        }
+    };
+
+    int brow[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)  // GLU: block 0 gate columns, block 1 the matching up columns
+        brow[j] = GLU ? j * 128 + wn * 32 : wn * WTN + j * 32;
+
+    floatx16_t acc[NV > 0 ? NV : 1][2];
+#pragma unroll
+    for (int i = 0; i < (NV > 0 ? NV : 1); ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    const int nk = K / BK;
+    lds_barrier();  // the previous tile's epilogue is done with the LDS
+#pragma unroll
+    for (int s = 0; s < STAGES - 1; ++s)
+        if (s < nk) issue_stage(s);
+
+    for (int kt = 0; kt < nk; ++kt) {
+        // stage kt has landed once at most the later stages' loads are in flight
+        const int later = min(STAGES - 2, nk - 1 - kt);
+        if (STAGES >= 4 && later >= 2) wait_vmcnt<(STAGES >= 4 ? 2 : 0) * kLoadsPerStage>();
+        else if (STAGES >= 3 && later == 1) wait_vmcnt<(STAGES >= 3 ? 1 : 0) * kLoadsPerStage>();
+        else wait_vmcnt<0>();
+        lds_barrier();  // everyone's pieces of stage kt are in; stage kt-1 is free
+        if (kt + STAGES - 1 < nk) issue_stage(kt + STAGES - 1);
+        if (NV > 0) {
+            const uint16_t* sa = lds + (kt % STAGES) * kStageElems;
+            const uint16_t* sb = sa + kAElems;
+#pragma unroll
+            for (int ks = 0; ks < KSTEPS; ++ks) {
+                bf16x8_t a[NV > 0 ? NV : 1], b[2];
+#pragma unroll
+                for (int i = 0; i < NV; ++i)
+                    a[i] = *(const bf16x8_t*)(sa + (wm * 128 + i * 32) * BK + rd_off[ks]);
+#pragma unroll
+                for (int j = 0; j < 2; ++j) b[j] = *(const bf16x8_t*)(sb + brow[j] * BK + rd_off[ks]);
+#pragma unroll
+                for (int i = 0; i < NV; ++i)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+            }
+        }
+    }
+
+    // ---- epilogue: accumulators -> bf16 -> LDS (per-wave region) -> 16-byte stores.
+    // MFMA 32x32 output layout: lane l, register r holds
+    //   row = (r / 4) * 8 + (l / 32) * 4 + r % 4,  column = l % 32.
+    lds_barrier();  // all waves are done reading the last stage
+    if (NV == 0) return;
+    constexpr int OC = GLU ? 32 : WTN;  // output columns per wave
+    const int lrow = lane & 31;
+    uint16_t* so = lds + wave * (128 * OC);
+#pragma unroll
+    for (int i = 0; i < (NV > 0 ? NV : 1); ++i) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int row = i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+            if (GLU) {
+                const float g = acc[i][0][r], u = acc[i][1][r];
+                const float hval = g / (1.0f + __expf(-g)) * u;
+                so[row * OC + lrow] = (uint16_t)f32_to_bf16_rne(hval);
+            } else {
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    so[row * OC + j * 32 + lrow] = (uint16_t)f32_to_bf16_rne(acc[i][j][r]);
+            }
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes have landed
+    __builtin_amdgcn_wave_barrier();
+    constexpr int PPR = OC / 8;  // 16-byte pieces per output row of the wave
+    const int col0 = GLU ? nt * 128 + wn * 32 : nt * BN + wn * WTN;
+#pragma unroll 4
+    for (int i = 0; i < (NV * 32 * PPR) / kWave; ++i) {
+        const int id = lane + i * kWave;
+        const int row = id / PPR, pc = id % PPR;
+        const int grow = wm * 128 + row;
+        const int gcol = col0 + pc * 8;
+        if (grow < rows_valid && gcol < N)
+            *(uint4*)(ta.c_tile + (int64_t)grow * N + gcol) = *(const uint4*)(so + row * OC + pc * 8);
+    }
+}
+
 template <bool GLU>
-__global__ __launch_bounds__(kGemmThreads) void grouped_gemm_kernel(
+__global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_kernel(
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
     const int32_t* __restrict__ offsets, int E, int K, int N, uint16_t* __restrict__ C) {
-    __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][kTileElems];  // [stage][A,B]
+    __shared__ __attribute__((aligned(1024))) uint16_t lds[kLdsElems];
     __shared__ int32_t tile_start[kMaxE + 1];
     __shared__ int32_t seg_start[kMaxE + 1];
-    __shared__ int32_t scan_tmp[4];
+    __shared__ int32_t scan_tmp[kWaves];
 
-    const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
-    const int wm = wave >> 1, wn = wave & 1;
-    const int NT = GLU ? N / 64 : (N + BN - 1) / BN;    // column tiles per expert
-    const int NW = GLU ? 2 * N : N;                     // W rows per expert
+    const int tid = threadIdx.x, lane = lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int wm = wave / WGN;
+    // column tiles per expert: GLU tiles cover 128 output columns (128 gate + 128 up rows)
+    const int NT = GLU ? (N + 127) / 128 : (N + BN - 1) / BN;
+    const int NW = GLU ? 2 * N : N;  // W rows per expert
     const int64_t w_stride = (int64_t)NW * K;
 
-    // ---- per-expert tile counts -> prefix (each workgroup computes its own copy)
+    // ---- per-expert tile counts -> prefix (every workgroup builds its own copy)
     {
-        const int per = (E + kGemmThreads - 1) / kGemmThreads;  // <= 4
+        const int per = (E + kGemmThreads - 1) / kGemmThreads;  // <= 2
         int local = 0;
         for (int i = 0; i < per; ++i) {
             const int e = tid * per + i;
@@ -112,6 +309,13 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_kernel(
     const int chunk = (total + nxcd - 1) / nxcd;
     const int t_end = min(total, (xcd + 1) * chunk);
 
+    // lane-constant parts of the MFMA operand addresses: logical piece
+    // (2*ks + lane/32) of row (lane % 32) of each 32-row block
+    const int lrow = lane & 31;
+    int rd_off[KSTEPS];
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) rd_off[ks] = lrow * BK + (((2 * ks + (lane >> 5)) ^ swz(lrow)) << 3);
+
     for (int t = xcd * chunk + slot; t < t_end; t += per_xcd) {
         // expert e: the last e with tile_start[e] <= t (experts with no tiles repeat a value)
         int lo = 0, hi = E;  // invariant: tile_start[lo] <= t < tile_start[hi]
@@ -125,140 +329,24 @@ __global__ __launch_bounds__(kGemmThreads) void grouped_gemm_kernel(
         const int q = t - tile_start[e];
         const int nt = q / mt_e, mt = q - nt * mt_e;
         const int row0 = seg0 + mt * BM;
-        const int rows_valid = min(BM, seg1 - row0);
-        const uint16_t* We = W + (int64_t)e * w_stride;
-
-        // global -> register staging: thread owns pieces tid + 256*i of each tile.
-        // Row/column validity and W row indices do not depend on k: compute once.
-        const uint16_t* pa[4];
-        const uint16_t* pb[4];
-        bool oka[4], okb[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int id = tid + i * kGemmThreads;
-            const int row = id >> 3, pc = id & 7;
-            oka[i] = row < rows_valid;
-            pa[i] = A + (int64_t)(row0 + (oka[i] ? row : 0)) * K + pc * 8;
-            int wrow;
-            if (GLU) {
-                wrow = row < 64 ? nt * 64 + row : N + nt * 64 + (row - 64);
-                okb[i] = true;
-            } else {
-                wrow = nt * BN + row;
-                okb[i] = wrow < N;
-            }
-            pb[i] = We + (int64_t)(okb[i] ? wrow : 0) * K + pc * 8;
-        }
-        uint4 ra[4], rb[4];
-#define MOE_LOAD_STAGE(kt)                                                              \
-        _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                 \
-            ra[i] = oka[i] ? *(const uint4*)(pa[i] + (kt) * BK) : make_uint4(0u, 0u, 0u, 0u); \
-            rb[i] = okb[i] ? *(const uint4*)(pb[i] + (kt) * BK) : make_uint4(0u, 0u, 0u, 0u); \
-        }
-#define MOE_STORE_STAGE(buf)                                                            \
-        _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                 \
-            const int id = tid + i * kGemmThreads;                                      \
-            const int off = tile_off(id >> 3, id & 7);                                  \
-            *(uint4*)(&lds[(buf)][0][off]) = ra[i];                                     \
-            *(uint4*)(&lds[(buf)][1][off]) = rb[i];                                     \
-        }
-
-        floatx16_t acc[2][2];
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-        // which 32-row blocks / 32-column blocks this wave computes
-        const bool mb_on[2] = {wm * 64 < rows_valid, wm * 64 + 32 < rows_valid};
-        int brow[2];
-        bool nb_on[2];
-        if (GLU) {
-            brow[0] = wn * 32;          // gate block
-            brow[1] = 64 + wn * 32;     // up block
-            nb_on[0] = nb_on[1] = true;
-        } else {
-            brow[0] = wn * 64;
-            brow[1] = wn * 64 + 32;
-            nb_on[0] = nt * BN + brow[0] < N;
-            nb_on[1] = nt * BN + brow[1] < N;
-        }
-
-        const int nk = K / BK;
-        __syncthreads();  // previous tile's epilogue is done with the LDS
-        MOE_LOAD_STAGE(0)
-        MOE_STORE_STAGE(0)
-        __syncthreads();
-        for (int kt = 0; kt < nk; ++kt) {
-            const int buf = kt & 1;
-            if (kt + 1 < nk) { MOE_LOAD_STAGE(kt + 1) }
-            const uint16_t* sa = lds[buf][0];
-            const uint16_t* sb = lds[buf][1];
-#pragma unroll
-            for (int ks = 0; ks < BK / 16; ++ks) {
-                const int pc = ks * 2 + (lane >> 5);
-                bf16x8_t a[2], b[2];
-#pragma unroll
-                for (int i = 0; i < 2; ++i) {
-                    const int row = wm * 64 + i * 32 + (lane & 31);
-                    a[i] = *(const bf16x8_t*)(sa + tile_off(row, pc));
-                }
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const int row = brow[j] + (lane & 31);
-                    b[j] = *(const bf16x8_t*)(sb + tile_off(row, pc));
-                }
-#pragma unroll
-                for (int i = 0; i < 2; ++i)
-#pragma unroll
-                    for (int j = 0; j < 2; ++j)
-                        if (mb_on[i] && nb_on[j])
-                            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j],
-                                                                                 acc[i][j], 0, 0, 0);
-            }
-            if (kt + 1 < nk) { MOE_STORE_STAGE(buf ^ 1) }
-            __syncthreads();
-        }
-
-        // ---- epilogue: accumulators -> bf16 -> LDS (per-wave region) -> 16-byte stores.
-        // MFMA 32x32 output layout: lane l, register r holds
-        //   row = (r / 4) * 8 + (l / 32) * 4 + r % 4,  column = l % 32.
-        constexpr int OC = GLU ? 32 : 64;  // output columns per wave
-        uint16_t* so = &lds[0][0][0] + wave * (64 * OC);
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int row = i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-                if (GLU) {
-                    const float g = acc[i][0][r], u = acc[i][1][r];
-                    const float hval = g / (1.0f + __expf(-g)) * u;
-                    so[row * OC + (lane & 31)] = (uint16_t)f32_to_bf16_rne(hval);
-                } else {
-#pragma unroll
-                    for (int j = 0; j < 2; ++j)
-                        so[row * OC + j * 32 + (lane & 31)] = (uint16_t)f32_to_bf16_rne(acc[i][j][r]);
-                }
-            }
-        }
-        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes have landed
-        __builtin_amdgcn_wave_barrier();
-        constexpr int PPR = OC / 8;           // 16-byte pieces per output row of the wave
-        const int col0 = GLU ? nt * 64 + wn * 32 : nt * BN + wn * 64;
-#pragma unroll
-        for (int i = 0; i < (64 * PPR) / kWave; ++i) {
-            const int id = lane + i * kWave;
-            const int row = id / PPR, pc = id % PPR;
-            const int grow = wm * 64 + row;
-            const int gcol = col0 + pc * 8;
-            if (grow < rows_valid && gcol < N)
-                *(uint4*)(C + (int64_t)(row0 + grow) * N + gcol) = *(const uint4*)(so + row * OC + pc * 8);
+        TileArgs ta;
+        ta.a_tile = A + (int64_t)row0 * K;
+        ta.w_exp = W + (int64_t)e * w_stride;
+        ta.c_tile = C + (int64_t)row0 * N;
+        ta.K = K;
+        ta.N = N;
+        ta.nt = nt;
+        ta.rows_valid = min(BM, seg1 - row0);
+        // 32-row blocks of this wave that hold segment rows (uniform per wave)
+        const int nvb = max(0, min(4, (ta.rows_valid - wm * 128 + 31) / 32));
+        switch (nvb) {
+            case 4: run_tile<GLU, 4>(ta, lds, wave, lane, rd_off); break;
+            case 3: run_tile<GLU, 3>(ta, lds, wave, lane, rd_off); break;
+            case 2: run_tile<GLU, 2>(ta, lds, wave, lane, rd_off); break;
+            case 1: run_tile<GLU, 1>(ta, lds, wave, lane, rd_off); break;
+            default: run_tile<GLU, 0>(ta, lds, wave, lane, rd_off); break;
         }
     }
-#undef MOE_LOAD_STAGE
-#undef MOE_STORE_STAGE
 }
 
 static int g_cu_count[64];
@@ -276,8 +364,8 @@ static int cu_count() {
 }
 
 static unsigned persistent_grid() {
-    // two workgroups per CU (LDS: 2 x ~72 KB of 160 KB), a multiple of the 8 XCDs
-    const int n = cu_count() * 2;
+    // one workgroup of 8 waves per CU (128 KB of the 160 KB LDS), a multiple of the 8 XCDs
+    const int n = cu_count();
     return (unsigned)((n + 7) / 8 * 8);
 }
 
