@@ -47,10 +47,15 @@ constexpr int STAGES = MOE_GEMM_STAGES;  // LDS ring depth
 constexpr int PR = BK / 8;               // 16-byte pieces per row of a stage
 constexpr int RPB = 64 / PR;             // rows filled by one wave-wide 1 KB load
 constexpr int KSTEPS = BK / 16;          // MFMA k-steps per stage
-constexpr int kWaves = 8;                          // 2 per SIMD
+#ifndef MOE_GEMM_WAVES
+#define MOE_GEMM_WAVES 8
+#endif
+constexpr int kWaves = MOE_GEMM_WAVES;             // 4 (one per SIMD) or 8 (two per SIMD)
 constexpr int kGemmThreads = kWaves * 64;
-constexpr int WGN = 4;                             // wave grid: 2 (rows) x 4 (W rows)
-constexpr int WTN = BN / WGN;                      // 64 W rows (output columns) per wave
+constexpr int WGN = kWaves / 2;                    // wave grid: 2 (rows) x WGN (W rows)
+constexpr int WTN = BN / WGN;                      // W rows (output columns) per wave
+constexpr int NBN = WTN / 32;                      // 32-column MFMA blocks per wave
+static_assert(kWaves == 4 || kWaves == 8, "4 or 8 waves");
 constexpr int kMaxE = 1024;
 constexpr int kAElems = BM * BK;                   // bf16 elements of one A stage (16 KB)
 constexpr int kBElems = BN * BK;                   // one B stage (16 KB)
@@ -173,59 +178,129 @@ __device__ __forceinline__ void run_tile(const TileArgs& ta, uint16_t* lds, int 
         }
     };
 
-    int brow[2];
+    // LDS B row of each of this wave's 32-column blocks. GLU: the first half of
+    // the blocks are gate columns, the second half the matching up columns.
+    int brow[NBN];
 #pragma unroll
-    for (int j = 0; j < 2; ++j)  // GLU: block 0 gate columns, block 1 the matching up columns
-        brow[j] = GLU ? j * 128 + wn * 32 : wn * WTN + j * 32;
+    for (int j = 0; j < NBN; ++j)
+        brow[j] = GLU ? (j < NBN / 2 ? 0 : 128) + wn * (WTN / 2) + (j % (NBN / 2)) * 32
+                      : wn * WTN + j * 32;
 
-    floatx16_t acc[NV > 0 ? NV : 1][2];
+    floatx16_t acc[NV > 0 ? NV : 1][NBN];
 #pragma unroll
     for (int i = 0; i < (NV > 0 ? NV : 1); ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < NBN; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
+    // ---- main loop: two wave groups in ping-pong. Group 0 (waves 0-3) and group 1
+    // (waves 4-7) put one wave on each SIMD. Stage s is computed by group 0 in
+    // phase 2s and by group 1 in phase 2s+1; in each phase the other group is the
+    // memory group: it reads its fragments of the stage it computes next from LDS
+    // and issues its half of the direct-to-LDS loads of a stage three or four
+    // ahead. So in every phase one wave per SIMD issues nothing but its MFMAs, from
+    // registers, while the other wave's memory traffic overlaps them.
+    //   buffer of stage s: read by group 0 in phase 2s-1 and group 1 in phase 2s;
+    //   group 1's half of stage s+3 is issued in phase 2s (buffer of s-1 is free),
+    //   group 0's half of stage s+4 in phase 2s+1 (buffer of s is free);
+    //   each group waits for its own half of stage s+1 by the end of phase 2s.
+    static_assert(KSTEPS == 2, "the ping-pong schedule is written for BK = 32");
+    static_assert(kWaves == 8, "the ping-pong schedule needs two waves per SIMD");
+    constexpr int NA = NV > 0 ? NV : 1;
+    const int grp = wave >> 2;  // == wm
+    bf16x8_t fa[2][NA], fb[2][NBN];
+#define MOE_LOAD_STAGE_FRAGS(stage)                                                           \
+    do {                                                                                      \
+        const uint16_t* sa_ = lds + ((stage) % STAGES) * kStageElems;                         \
+        const uint16_t* sb_ = sa_ + kAElems;                                                  \
+        _Pragma("unroll") for (int ks = 0; ks < 2; ++ks) {                                    \
+            _Pragma("unroll") for (int i = 0; i < NV; ++i)                                    \
+                fa[ks][i] = *(const bf16x8_t*)(sa_ + ((2 * i + wm) * 32) * BK + rd_off[ks]);   \
+            _Pragma("unroll") for (int j = 0; j < NBN; ++j)                                   \
+                fb[ks][j] = *(const bf16x8_t*)(sb_ + brow[j] * BK + rd_off[ks]);               \
+        }                                                                                     \
+    } while (0)
+#define MOE_MMA_STAGE()                                                                       \
+    do {                                                                                      \
+        _Pragma("unroll") for (int ks = 0; ks < 2; ++ks)                                      \
+            _Pragma("unroll") for (int i = 0; i < NV; ++i)                                    \
+                _Pragma("unroll") for (int j = 0; j < NBN; ++j)                               \
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks][i], fb[ks][j], acc[i][j], 0, 0, 0); \
+    } while (0)
+    // outstanding halves of later stages this group may leave in flight when it
+    // needs stage s+1: group 0 has issued up to s+3, group 1 up to s+3 as well
+#define MOE_WAIT_NEXT(s)                                                                      \
+    do {                                                                                      \
+        const int later_ = min(2, nk - 2 - (s));                                              \
+        if (later_ >= 2) wait_vmcnt<2 * kLoadsPerStage>();                                    \
+        else if (later_ == 1) wait_vmcnt<kLoadsPerStage>();                                   \
+        else wait_vmcnt<0>();                                                                 \
+    } while (0)
+
     const int nk = K / BK;
+    // The previous tile's epilogue stores must be done before this tile's loads are
+    // issued: a compiler-visible wait here means the compiler sees no vector-memory
+    // operation pending inside the k loop (the loop's own loads are invisible to
+    // it), so it adds no drain of the prefetch there.
+    __builtin_amdgcn_s_waitcnt(0);
     lds_barrier();  // the previous tile's epilogue is done with the LDS
+    // prologue: both groups issue their halves of stages 0..2, group 0 also of 3
 #pragma unroll
     for (int s = 0; s < STAGES - 1; ++s)
         if (s < nk) issue_stage(s);
-
-    for (int kt = 0; kt < nk; ++kt) {
-        // stage kt has landed once at most the later stages' loads are in flight
-        const int later = min(STAGES - 2, nk - 1 - kt);
-        if (STAGES >= 4 && later >= 2) wait_vmcnt<(STAGES >= 4 ? 2 : 0) * kLoadsPerStage>();
-        else if (STAGES >= 3 && later == 1) wait_vmcnt<(STAGES >= 3 ? 1 : 0) * kLoadsPerStage>();
+    if (grp == 0 && STAGES - 1 < nk) issue_stage(STAGES - 1);
+    {
+        // stage 0 in: later stages of this group still allowed in flight
+        const int issued = min(nk, grp == 0 ? STAGES : STAGES - 1);
+        if (issued >= 4) wait_vmcnt<3 * kLoadsPerStage>();
+        else if (issued == 3) wait_vmcnt<2 * kLoadsPerStage>();
+        else if (issued == 2) wait_vmcnt<kLoadsPerStage>();
         else wait_vmcnt<0>();
-        lds_barrier();  // everyone's pieces of stage kt are in; stage kt-1 is free
-        if (kt + STAGES - 1 < nk) issue_stage(kt + STAGES - 1);
-        if (NV > 0) {
-            const uint16_t* sa = lds + (kt % STAGES) * kStageElems;
-            const uint16_t* sb = sa + kAElems;
-#pragma unroll
-            for (int ks = 0; ks < KSTEPS; ++ks) {
-                bf16x8_t a[NV > 0 ? NV : 1], b[2];
-#pragma unroll
-                for (int i = 0; i < NV; ++i)
-                    a[i] = *(const bf16x8_t*)(sa + (wm * 128 + i * 32) * BK + rd_off[ks]);
-#pragma unroll
-                for (int j = 0; j < 2; ++j) b[j] = *(const bf16x8_t*)(sb + brow[j] * BK + rd_off[ks]);
-#pragma unroll
-                for (int i = 0; i < NV; ++i)
-#pragma unroll
-                    for (int j = 0; j < 2; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-            }
+    }
+    lds_barrier();
+    if (grp == 0 && NV > 0) MOE_LOAD_STAGE_FRAGS(0);
+    lds_barrier();
+
+    // Each group runs its own straight-line loop; both pass two barriers per stage.
+    if (grp == 0) {
+        for (int kt = 0; kt < nk; ++kt) {
+            // phase 2kt: compute stage kt (fragments read in the previous phase)
+            __builtin_amdgcn_s_setprio(1);
+            if (NV > 0) MOE_MMA_STAGE();
+            __builtin_amdgcn_s_setprio(0);
+            MOE_WAIT_NEXT(kt);  // own half of stage kt+1 in; kt+2, kt+3 may stay in flight
+            lds_barrier();
+            // phase 2kt+1: refill the buffer of stage kt (both groups have read it)
+            // with stage kt+4, and read stage kt+1
+            if (kt + STAGES < nk) issue_stage(kt + STAGES);
+            if (NV > 0 && kt + 1 < nk) MOE_LOAD_STAGE_FRAGS(kt + 1);
+            lds_barrier();
+        }
+    } else {
+        for (int kt = 0; kt < nk; ++kt) {
+            // phase 2kt: read stage kt; issue stage kt+3 into the buffer of stage kt-1
+            if (NV > 0) MOE_LOAD_STAGE_FRAGS(kt);
+            if (kt + STAGES - 1 < nk) issue_stage(kt + STAGES - 1);
+            MOE_WAIT_NEXT(kt);  // own half of stage kt+1 in; kt+2, kt+3 may stay in flight
+            lds_barrier();
+            // phase 2kt+1: compute stage kt
+            __builtin_amdgcn_s_setprio(1);
+            if (NV > 0) MOE_MMA_STAGE();
+            __builtin_amdgcn_s_setprio(0);
+            lds_barrier();
         }
     }
+#undef MOE_LOAD_STAGE_FRAGS
+#undef MOE_MMA_STAGE
+#undef MOE_WAIT_NEXT
 
     // ---- epilogue: accumulators -> bf16 -> LDS (per-wave region) -> 16-byte stores.
     // MFMA 32x32 output layout: lane l, register r holds
     //   row = (r / 4) * 8 + (l / 32) * 4 + r % 4,  column = l % 32.
     lds_barrier();  // all waves are done reading the last stage
     if (NV == 0) return;
-    constexpr int OC = GLU ? 32 : WTN;  // output columns per wave
+    constexpr int OC = GLU ? WTN / 2 : WTN;  // output columns per wave
     const int lrow = lane & 31;
     uint16_t* so = lds + wave * (128 * OC);
 #pragma unroll
@@ -234,12 +309,15 @@ __device__ __forceinline__ void run_tile(const TileArgs& ta, uint16_t* lds, int 
         for (int r = 0; r < 16; ++r) {
             const int row = i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
             if (GLU) {
-                const float g = acc[i][0][r], u = acc[i][1][r];
-                const float hval = g / (1.0f + __expf(-g)) * u;
-                so[row * OC + lrow] = (uint16_t)f32_to_bf16_rne(hval);
+#pragma unroll
+                for (int j = 0; j < NBN / 2; ++j) {
+                    const float g = acc[i][j][r], u = acc[i][j + NBN / 2][r];
+                    const float hval = g / (1.0f + __expf(-g)) * u;
+                    so[row * OC + j * 32 + lrow] = (uint16_t)f32_to_bf16_rne(hval);
+                }
             } else {
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
+                for (int j = 0; j < NBN; ++j)
                     so[row * OC + j * 32 + lrow] = (uint16_t)f32_to_bf16_rne(acc[i][j][r]);
             }
         }
@@ -247,12 +325,12 @@ __device__ __forceinline__ void run_tile(const TileArgs& ta, uint16_t* lds, int 
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes have landed
     __builtin_amdgcn_wave_barrier();
     constexpr int PPR = OC / 8;  // 16-byte pieces per output row of the wave
-    const int col0 = GLU ? nt * 128 + wn * 32 : nt * BN + wn * WTN;
+    const int col0 = GLU ? nt * 128 + wn * (WTN / 2) : nt * BN + wn * WTN;
 #pragma unroll 4
     for (int i = 0; i < (NV * 32 * PPR) / kWave; ++i) {
         const int id = lane + i * kWave;
         const int row = id / PPR, pc = id % PPR;
-        const int grow = wm * 128 + row;
+        const int grow = ((row >> 5) * 2 + wm) * 32 + (row & 31);  // block row>>5 is block 2i+wm
         const int gcol = col0 + pc * 8;
         if (grow < rows_valid && gcol < N)
             *(uint4*)(ta.c_tile + (int64_t)grow * N + gcol) = *(const uint4*)(so + row * OC + pc * 8);
@@ -278,7 +356,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_kernel(
 
     // ---- per-expert tile counts -> prefix (every workgroup builds its own copy)
     {
-        const int per = (E + kGemmThreads - 1) / kGemmThreads;  // <= 2
+        const int per = (E + kGemmThreads - 1) / kGemmThreads;  // <= 4
         int local = 0;
         for (int i = 0; i < per; ++i) {
             const int e = tid * per + i;
@@ -337,8 +415,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_kernel(
         ta.N = N;
         ta.nt = nt;
         ta.rows_valid = min(BM, seg1 - row0);
-        // 32-row blocks of this wave that hold segment rows (uniform per wave)
-        const int nvb = max(0, min(4, (ta.rows_valid - wm * 128 + 31) / 32));
+        // live 32-row blocks of this wave: wave row wm owns blocks 2i + wm
+        const int nvb = max(0, min(4, ((ta.rows_valid + 31) / 32 - wm + 1) / 2));
         switch (nvb) {
             case 4: run_tile<GLU, 4>(ta, lds, wave, lane, rd_off); break;
             case 3: run_tile<GLU, 3>(ta, lds, wave, lane, rd_off); break;
