@@ -17,13 +17,14 @@
 //               chunk c's routes to e; pad rows get row_token = -1
 //   3. scatter: route_row[r] = base + rank among earlier equal ids (stable in r),
 //               row_token[route_row[r]] = r / k
-//   4. gather:  x_perm[p] = x[row_token[p]] (zero row if -1), 16-byte lanes
+//   4. gather:  x_perm[p] = x[row_token[p]] (zero row if -1), 16-byte lanes over
+//               consecutive layout bytes
 #include "common.hpp"
 
 namespace moe {
 
-constexpr int kChunk = 1024;          // routes per wavefront chunk
-constexpr int kSteps = kChunk / kWave;
+constexpr int kChunk = 256;           // routes per wavefront chunk
+constexpr int kSteps = kChunk / kWave;  // all of a chunk's ids are loaded before any is used
 constexpr int kScanThreads = 1024;
 
 static __device__ __forceinline__ int key_bits(int E) { return E <= 1 ? 0 : 32 - __clz(E - 1); }
@@ -39,11 +40,16 @@ __global__ __launch_bounds__(256) void permute_hist_kernel(const int32_t* __rest
     for (int e = lane; e < E; e += kWave) h[e] = 0;
     const int nbits = key_bits(E);
     const int64_t r0 = c * kChunk;
+    uint32_t ids[kSteps];
+#pragma unroll
     for (int s = 0; s < kSteps; ++s) {
         const int64_t r = r0 + s * kWave + lane;
-        const uint32_t id = r < R ? (uint32_t)topk_idx[r] : 0xffffffffu;
-        const bool active = id < (uint32_t)E;  // out-of-range ids take no part
-        const uint32_t key = active ? id : 0u;
+        ids[s] = r < R ? (uint32_t)topk_idx[r] : 0xffffffffu;
+    }
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) {
+        const bool active = ids[s] < (uint32_t)E;  // out-of-range ids take no part
+        const uint32_t key = active ? ids[s] : 0u;
         const uint64_t peers = match_peers(key, nbits, active);
         if (active && (__ffsll((unsigned long long)peers) - 1) == lane) h[key] += __popcll(peers);
     }
@@ -68,6 +74,7 @@ __global__ __launch_bounds__(kScanThreads) void permute_scan_kernel(
     const int64_t c1 = owner ? (c0 + per < nchunks ? c0 + per : nchunks) : 0;
 
     int32_t sum = 0;
+#pragma unroll 8
     for (int64_t c = c0; c < c1; ++c) sum += hist[c * E + e];
     if (owner) part[s * E + e] = sum;
     __syncthreads();
@@ -99,6 +106,7 @@ __global__ __launch_bounds__(kScanThreads) void permute_scan_kernel(
 
     if (owner) {
         int32_t run = (scan[e] - ((cnt[e] + align - 1) / align * align)) + part[s * E + e];
+#pragma unroll 8
         for (int64_t c = c0; c < c1; ++c) {
             const int32_t v = hist[c * E + e];
             hist[c * E + e] = run;
@@ -129,11 +137,17 @@ __global__ __launch_bounds__(256) void permute_scatter_kernel(const int32_t* __r
     const int nbits = key_bits(E);
     const uint64_t lt = lanemask_lt();
     const int64_t r0 = c * kChunk;
+    uint32_t ids[kSteps];
+#pragma unroll
     for (int s = 0; s < kSteps; ++s) {
         const int64_t r = r0 + s * kWave + lane;
-        const uint32_t id = r < R ? (uint32_t)topk_idx[r] : 0xffffffffu;
-        const bool active = id < (uint32_t)E;
-        const uint32_t key = active ? id : 0u;
+        ids[s] = r < R ? (uint32_t)topk_idx[r] : 0xffffffffu;
+    }
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) {
+        const int64_t r = r0 + s * kWave + lane;
+        const bool active = ids[s] < (uint32_t)E;
+        const uint32_t key = active ? ids[s] : 0u;
         const uint64_t peers = match_peers(key, nbits, active);
         if (active) {
             const int32_t dest = cur[key] + __popcll(peers & lt);
@@ -146,39 +160,35 @@ __global__ __launch_bounds__(256) void permute_scatter_kernel(const int32_t* __r
     }
 }
 
-// One wavefront per row; each lane moves 16-byte pieces, up to kPieces of them
-// in flight before any store.
-constexpr int kPieces = 4;
+// The gather, one 16-byte piece per lane: piece q of the layout is row q / ppr,
+// column piece q % ppr, so a wavefront covers 1 KB of consecutive layout bytes
+// (coalesced stores) read from the matching piece of the token's row. Each
+// thread has kGatherUnroll pieces in flight before its first store.
+constexpr int kGatherUnroll = 4;
+constexpr int kGatherThreads = 256;
 
-__global__ __launch_bounds__(256) void permute_gather_kernel(const uint4* __restrict__ x,
-                                                             const int32_t* __restrict__ row_token,
-                                                             const int32_t* __restrict__ offsets,
-                                                             int E, int pieces_per_row,
-                                                             uint4* __restrict__ x_perm) {
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int64_t p = (int64_t)blockIdx.x * 4 + wave;
-    const int32_t used = offsets[E];
-    if (p >= used) return;
-    const int32_t t = row_token[p];
-    const int lane = lane_id();
-    uint4* dst = x_perm + p * pieces_per_row;
-    if (t < 0) {
-        const uint4 z = {0u, 0u, 0u, 0u};
-        for (int c = lane; c < pieces_per_row; c += kWave) dst[c] = z;
-        return;
-    }
-    const uint4* src = x + (int64_t)t * pieces_per_row;
-    for (int c0 = 0; c0 < pieces_per_row; c0 += kWave * kPieces) {
-        uint4 v[kPieces];
+__global__ __launch_bounds__(kGatherThreads) void permute_gather_kernel(
+    const uint4* __restrict__ x, const int32_t* __restrict__ row_token,
+    const int32_t* __restrict__ offsets, int E, int ppr, uint4* __restrict__ x_perm) {
+    const int64_t used = (int64_t)offsets[E] * ppr;  // pieces of the used rows
+    const int64_t stride = (int64_t)gridDim.x * kGatherThreads * kGatherUnroll;
+    for (int64_t base = (int64_t)blockIdx.x * kGatherThreads * kGatherUnroll + threadIdx.x; base < used;
+         base += stride) {
+        uint4 v[kGatherUnroll];
 #pragma unroll
-        for (int i = 0; i < kPieces; ++i) {
-            const int c = c0 + i * kWave + lane;
-            if (c < pieces_per_row) v[i] = src[c];
+        for (int u = 0; u < kGatherUnroll; ++u) {
+            const int64_t q = base + u * kGatherThreads;
+            v[u] = make_uint4(0u, 0u, 0u, 0u);
+            if (q < used) {
+                const int64_t p = q / ppr;
+                const int32_t t = row_token[p];
+                if (t >= 0) v[u] = x[(int64_t)t * ppr + (q - p * ppr)];
+            }
         }
 #pragma unroll
-        for (int i = 0; i < kPieces; ++i) {
-            const int c = c0 + i * kWave + lane;
-            if (c < pieces_per_row) dst[c] = v[i];
+        for (int u = 0; u < kGatherUnroll; ++u) {
+            const int64_t q = base + u * kGatherThreads;
+            if (q < used) x_perm[q] = v[u];
         }
     }
 }
@@ -215,10 +225,15 @@ hipError_t launch_permute(const uint16_t* x, const int32_t* topk_idx, int64_t T,
         err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
-    const int pieces = H / 8;  // 16-byte pieces per row
-    hipLaunchKernelGGL(permute_gather_kernel, dim3((unsigned)((P_max + 3) / 4)), dim3(256), 0,
-                       stream, (const uint4*)x, (const int32_t*)row_token,
-                       (const int32_t*)offsets, E, pieces, (uint4*)x_perm);
+    const int ppr = H / 8;  // 16-byte pieces per row
+    // enough workgroups to cover P_max rows once, capped at a few waves of the chip
+    const int64_t pieces = P_max * (int64_t)ppr;
+    const int64_t per_wg = kGatherThreads * kGatherUnroll;
+    const int64_t want = (pieces + per_wg - 1) / per_wg;
+    const unsigned grid = (unsigned)(want < 4096 ? want : 4096);
+    hipLaunchKernelGGL(permute_gather_kernel, dim3(grid), dim3(kGatherThreads), 0, stream,
+                       (const uint4*)x, (const int32_t*)row_token, (const int32_t*)offsets, E, ppr,
+                       (uint4*)x_perm);
     return hipGetLastError();
 }
 
