@@ -9,6 +9,7 @@ namespace moe {
 constexpr int kWave = 64;  // CDNA wavefront width
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float floatx16_t;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float floatx4_t;
 typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;

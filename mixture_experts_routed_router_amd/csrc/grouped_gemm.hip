@@ -28,8 +28,9 @@
 // SIMD, so one wave's MFMAs cover the other's waits) in a 2x4 grid; each wave
 // owns 128 rows x 64 W-rows = 4x2 blocks of v_mfma_f32_32x32x16_bf16 (128
 // accumulator registers).  16-byte pieces are XOR-swizzled in LDS so that the
-// MFMA operand reads are conflict-free.  The output tile is staged through LDS
-// so global stores are whole 16-byte pieces.
+// MFMA operand reads are conflict-free.  The ring runs on from one tile to the
+// next (the next tile's first stages load during the last k steps), and the
+// output is written from registers, 8 bytes per lane, while the next tile runs.
 #include "common.hpp"
 
 namespace moe {
@@ -64,10 +65,10 @@ constexpr int kLdsElems = STAGES * kStageElems;    // 128 KB
 constexpr int kPiecesPerThread = (BM * PR) / kGemmThreads;  // of A (and of B) per stage
 constexpr int kLoadsPerStage = 2 * kPiecesPerThread;        // per thread: A + B 16-byte loads
 static_assert(BM == BN, "A and B stages share one load layout");
-static_assert(kLoadsPerStage * (STAGES - 2) < 64, "vmcnt is 6 bits");
-// The epilogue stages each wave's 128 x WTN bf16 output tile through the LDS ring;
-// it must fit, or it would overwrite the tile tables that follow the ring in LDS.
-static_assert(kWaves * 128 * WTN <= kLdsElems, "epilogue staging must fit in the LDS ring");
+// A wave's epilogue issues at most 4 blocks x NBN column blocks x 4 store
+// instructions; a wait may leave those and 3 stages of loads in flight.
+constexpr int kMaxStoresPerTile = 4 * NBN * 4;
+static_assert(3 * kLoadsPerStage + kMaxStoresPerTile < 64, "vmcnt is 6 bits");
 
 // Rows of a stage are BK bf16 = PR pieces of 16 bytes. Piece p of row r is stored
 // at piece p ^ swz(r). For the same logical piece of any 8 consecutive rows (a
@@ -124,59 +125,166 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// Everything one tile needs that does not depend on the live row-block count.
+// Wait until at most n of this wave's vector-memory operations are in flight;
+// n is rounded down to a multiple of 4 (waiting for more is always safe).
+__device__ __forceinline__ void wait_vmcnt_dyn(int n) {
+    switch (n >> 2) {
+        case 0: wait_vmcnt<0>(); break;
+        case 1: wait_vmcnt<4>(); break;
+        case 2: wait_vmcnt<8>(); break;
+        case 3: wait_vmcnt<12>(); break;
+        case 4: wait_vmcnt<16>(); break;
+        case 5: wait_vmcnt<20>(); break;
+        case 6: wait_vmcnt<24>(); break;
+        case 7: wait_vmcnt<28>(); break;
+        case 8: wait_vmcnt<32>(); break;
+        case 9: wait_vmcnt<36>(); break;
+        case 10: wait_vmcnt<40>(); break;
+        case 11: wait_vmcnt<44>(); break;
+        case 12: wait_vmcnt<48>(); break;
+        case 13: wait_vmcnt<52>(); break;
+        case 14: wait_vmcnt<56>(); break;
+        default: wait_vmcnt<60>(); break;
+    }
+}
+
+// Lane exchange inside each quad of lanes (DPP quad_perm): partner lane ^ 2 or ^ 1.
+__device__ __forceinline__ uint32_t quad_xor2(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true);  // [2,3,0,1]
+}
+__device__ __forceinline__ uint32_t quad_xor1(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true);  // [1,0,3,2]
+}
+
+__device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
+    bf16x2_t v;
+    v[0] = (__bf16)lo;  // round to nearest even (v_cvt_pk_bf16_f32)
+    v[1] = (__bf16)hi;
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// 4x4 transpose of bf16 values inside a quad of lanes. On entry lane p (= lane % 4)
+// holds column p of the block, v[m] = element (m, p); on exit it holds row p as
+// w0 = (p,0) | (p,1) << 16 and w1 = (p,2) | (p,3) << 16. Rows are swapped in
+// pairs with lane p^2, then single values with lane p^1; the byte selectors of
+// v_perm_b32 (bytes 0-3 of the second operand, 4-7 of the first) depend only on
+// the lane and are built once (QuadSel).
+struct QuadSel {
+    bool h;              // p & 2
+    uint32_t give;       // p odd: (kp.lo, y.lo), even: (kp.hi, y.hi)
+    uint32_t pa;         // columns {p, p^1} in order, from kp and t
+    uint32_t pb;         // columns {p^2, p^3} in order, from y and t
+};
+
+__device__ __forceinline__ QuadSel quad_sel(int lane) {
+    const int p = lane & 3;
+    const bool g = (p & 1) != 0;
+    QuadSel q;
+    q.h = (p & 2) != 0;
+    q.give = g ? 0x01000504u : 0x03020706u;
+    q.pa = g ? 0x07060100u : 0x01000504u;
+    q.pb = g ? 0x07060302u : 0x03020504u;
+    return q;
+}
+
+__device__ __forceinline__ void quad_transpose_bf16(float v0, float v1, float v2, float v3,
+                                                    const QuadSel& qs, uint32_t& w0, uint32_t& w1) {
+    const uint32_t b01 = pack2_bf16(v0, v1), b23 = pack2_bf16(v2, v3);  // lo = even row
+    const uint32_t kp = qs.h ? b23 : b01;           // rows 2h, 2h+1 of column p
+    const uint32_t y = quad_xor2(qs.h ? b01 : b23); // rows 2h, 2h+1 of column p^2
+    // this lane ends with row 2h+g; the partner p^1 needs row 2h+1-g of both
+    const uint32_t t = quad_xor1(__builtin_amdgcn_perm(kp, y, qs.give));  // row 2h+g of p^1 (lo), p^3 (hi)
+    const uint32_t pa = __builtin_amdgcn_perm(kp, t, qs.pa);
+    const uint32_t pb = __builtin_amdgcn_perm(y, t, qs.pb);
+    w0 = qs.h ? pb : pa;
+    w1 = qs.h ? pa : pb;
+}
+
+// Everything one tile needs.
 struct TileArgs {
     const uint16_t* a_tile;   // A + row0 * K
     const uint16_t* w_exp;    // W + e * (W rows per expert) * K
     uint16_t* c_tile;         // C + row0 * N
-    int K, N, nt, rows_valid;
+    int nt, rows_valid;
+    int nvb;                  // this wave's 32-row blocks that hold segment rows (0..4)
 };
 
-// One tile: the k loop through the LDS ring, then the epilogue. NV = number of
-// this wave's 32-row blocks that hold segment rows (compile-time, so every MFMA
-// in the loop is unconditional and the accumulators never leave AGPRs).
-template <bool GLU, int NV>
-__device__ __forceinline__ void run_tile(const TileArgs& ta, uint16_t* lds, int wave, int lane,
-                                         const int (&rd_off)[KSTEPS]) {
-    const int wm = wave / WGN, wn = wave % WGN;
-    const int K = ta.K, N = ta.N, nt = ta.nt, rows_valid = ta.rows_valid;
+// This thread's byte offsets of its A and B pieces of a stage, relative to the
+// tile's row 0 (A) and the expert (W), so they stay fixed while the k stage moves
+// the SGPR base. Wave w, load i fills LDS rows [RPB*(n*w+i), +RPB)
+// (n = kPiecesPerThread); lane l fills row RPB*(n*w+i) + l/PR, physical piece
+// l%PR, i.e. logical piece (l%PR) ^ swz(row). Rows past the segment (or past N)
+// read a valid row instead; those results are never stored.
+struct StageOffsets {
+    uint32_t a[kPiecesPerThread], b[kPiecesPerThread];
+};
 
-    // ---- this thread's A and B pieces of every stage. Wave w, load i fills LDS
-    // rows [RPB*(n*w+i), +RPB) (n = kPiecesPerThread); lane l fills row
-    // RPB*(n*w+i) + l/PR, physical piece l%PR, i.e. logical piece (l%PR) ^ swz(row). Rows past the
-    // segment (or past N) read a valid row instead; those results are never stored.
-    // Byte offsets are relative to the tile's row 0 (A) and the expert (W), so they
-    // stay fixed while the k stage moves the SGPR base.
-    uint32_t offa[kPiecesPerThread], offb[kPiecesPerThread];
+template <bool GLU>
+__device__ __forceinline__ StageOffsets stage_offsets(const TileArgs& ta, int K, int N, int wave, int lane) {
+    StageOffsets o;
 #pragma unroll
     for (int i = 0; i < kPiecesPerThread; ++i) {
         const int r = RPB * (kPiecesPerThread * wave + i) + lane / PR;
         const int piece = (lane % PR) ^ swz(r);
-        const int ar = r < rows_valid ? r : 0;
-        offa[i] = (uint32_t)((ar * K + piece * 8) * 2);
+        const int ar = r < ta.rows_valid ? r : 0;
+        o.a[i] = (uint32_t)((ar * K + piece * 8) * 2);
         int wr;
         if (GLU) {
-            const int c = nt * 128 + (r & 127);  // output column of this W row
+            const int c = ta.nt * 128 + (r & 127);  // output column of this W row
             const int cc = c < N ? c : N - 1;
             wr = r < 128 ? cc : N + cc;
         } else {
-            const int c = nt * BN + r;
+            const int c = ta.nt * BN + r;
             wr = c < N ? c : N - 1;
         }
-        offb[i] = (uint32_t)(((int64_t)wr * K + piece * 8) * 2);
+        o.b[i] = (uint32_t)(((int64_t)wr * K + piece * 8) * 2);
     }
-    const uint32_t lds0 = lds_addr(lds);
-    auto issue_stage = [&](int kt) {
-        const uint32_t sa = lds0 + (uint32_t)((kt % STAGES) * kStageElems * 2);
-        const uint32_t sb = sa + kAElems * 2;
-        const uint16_t* ga = ta.a_tile + kt * BK;
-        const uint16_t* gb = ta.w_exp + kt * BK;
+    return o;
+}
+
+// This thread's share of one stage: A and B pieces of k-stage kt of a tile into ring slot `slot`.
+__device__ __forceinline__ void issue_stage(uint32_t lds0, int slot, int wave, const uint16_t* ga,
+                                            const uint16_t* gb, const StageOffsets& o) {
+    const uint32_t sa = lds0 + (uint32_t)(slot * kStageElems * 2);
+    const uint32_t sb = sa + kAElems * 2;
 #pragma unroll
-        for (int i = 0; i < kPiecesPerThread; ++i) {
-            dma16(sa + (kPiecesPerThread * wave + i) * 1024, ga, offa[i]);
-            dma16(sb + (kPiecesPerThread * wave + i) * 1024, gb, offb[i]);
-        }
-    };
+    for (int i = 0; i < kPiecesPerThread; ++i) {
+        dma16(sa + (kPiecesPerThread * wave + i) * 1024, ga, o.a[i]);
+        dma16(sb + (kPiecesPerThread * wave + i) * 1024, gb, o.b[i]);
+    }
+}
+
+// Wave-constant values of the whole launch.
+struct WaveCtx {
+    uint16_t* lds;
+    uint32_t lds0;
+    int K, N, nk;
+    int wave, lane, wm, wn, grp;
+    int rd_off[KSTEPS];
+};
+
+// One tile: the k loop through the LDS ring, then the epilogue. NV = number of
+// this wave's 32-row blocks that hold segment rows (compile-time, so every MFMA
+// in the loop is unconditional and the accumulators stay in registers).
+//
+// The ring runs on across tiles: stage kt of a tile lives in slot (base + kt) % 4,
+// and when pf_next is set, the loads of the next tile's first stages are issued
+// during this tile's last k steps (group 1 issues stages 0-2, group 0 stages 0-3,
+// exactly what a prologue would). The next tile then starts with `prefetched` set
+// and no prologue.
+//
+// The epilogue writes straight from registers (no LDS): after a 4x4 transpose
+// inside each quad of lanes, a lane holds 4 consecutive bf16 of one output row,
+// an 8-byte store. This wave's stores of the previous tile (s_prev of them) were
+// issued after the prefetched stages; vector-memory operations complete in issue
+// order, so a wait for a prefetched stage may leave those stores in flight.
+template <bool GLU, int NV>
+__device__ __forceinline__ int run_tile(const WaveCtx& w, const TileArgs& ta, const TileArgs& tn,
+                                        int base, bool prefetched, bool pf_next, int s_prev) {
+    const int K = w.K, N = w.N, nk = w.nk, wave = w.wave, lane = w.lane, wm = w.wm, wn = w.wn;
+    const int grp = w.grp;
+    const StageOffsets oc = stage_offsets<GLU>(ta, K, N, wave, lane);
+    const StageOffsets on = stage_offsets<GLU>(tn, K, N, wave, lane);
 
     // LDS B row of each of this wave's 32-column blocks. GLU: the first half of
     // the blocks are gate columns, the second half the matching up columns.
@@ -205,20 +313,29 @@ __device__ __forceinline__ void run_tile(const TileArgs& ta, uint16_t* lds, int 
     //   group 1's half of stage s+3 is issued in phase 2s (buffer of s-1 is free),
     //   group 0's half of stage s+4 in phase 2s+1 (buffer of s is free);
     //   each group waits for its own half of stage s+1 by the end of phase 2s.
+    // Stages kt >= nk are the next tile's stages kt - nk.
     static_assert(KSTEPS == 2, "the ping-pong schedule is written for BK = 32");
     static_assert(kWaves == 8, "the ping-pong schedule needs two waves per SIMD");
     constexpr int NA = NV > 0 ? NV : 1;
-    const int grp = wave >> 2;  // == wm
     bf16x8_t fa[2][NA], fb[2][NBN];
+#define MOE_ISSUE(s)                                                                              \
+    do {                                                                                          \
+        const int s_ = (s);                                                                       \
+        const int slot_ = (base + s_) & (STAGES - 1);                                             \
+        if (s_ < nk)                                                                              \
+            issue_stage(w.lds0, slot_, wave, ta.a_tile + s_ * BK, ta.w_exp + s_ * BK, oc);        \
+        else if (pf_next)                                                                         \
+            issue_stage(w.lds0, slot_, wave, tn.a_tile + (s_ - nk) * BK, tn.w_exp + (s_ - nk) * BK, on); \
+    } while (0)
 #define MOE_LOAD_STAGE_FRAGS(stage)                                                           \
     do {                                                                                      \
-        const uint16_t* sa_ = lds + ((stage) % STAGES) * kStageElems;                         \
+        const uint16_t* sa_ = w.lds + ((base + (stage)) & (STAGES - 1)) * kStageElems;        \
         const uint16_t* sb_ = sa_ + kAElems;                                                  \
         _Pragma("unroll") for (int ks = 0; ks < 2; ++ks) {                                    \
             _Pragma("unroll") for (int i = 0; i < NV; ++i)                                    \
-                fa[ks][i] = *(const bf16x8_t*)(sa_ + ((2 * i + wm) * 32) * BK + rd_off[ks]);   \
+                fa[ks][i] = *(const bf16x8_t*)(sa_ + ((2 * i + wm) * 32) * BK + w.rd_off[ks]); \
             _Pragma("unroll") for (int j = 0; j < NBN; ++j)                                   \
-                fb[ks][j] = *(const bf16x8_t*)(sb_ + brow[j] * BK + rd_off[ks]);               \
+                fb[ks][j] = *(const bf16x8_t*)(sb_ + brow[j] * BK + w.rd_off[ks]);             \
         }                                                                                     \
     } while (0)
 #define MOE_MMA_STAGE()                                                                       \
@@ -228,39 +345,42 @@ __device__ __forceinline__ void run_tile(const TileArgs& ta, uint16_t* lds, int 
                 _Pragma("unroll") for (int j = 0; j < NBN; ++j)                               \
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks][i], fb[ks][j], acc[i][j], 0, 0, 0); \
     } while (0)
-    // outstanding halves of later stages this group may leave in flight when it
-    // needs stage s+1: group 0 has issued up to s+3, group 1 up to s+3 as well
-#define MOE_WAIT_NEXT(s)                                                                      \
+    // Wait for this group's half of stage kt+1. Its later stages kt+2, kt+3 (where
+    // they exist) may stay in flight, and so may the previous tile's stores when
+    // stage kt+1 was issued before them (prefetched stages 0..P).
+#define MOE_WAIT_NEXT(kt, P)                                                                  \
     do {                                                                                      \
-        const int later_ = min(2, nk - 2 - (s));                                              \
-        if (later_ >= 2) wait_vmcnt<2 * kLoadsPerStage>();                                    \
+        const int s2_ = (kt) + 2;                                                             \
+        const int later_ = (s2_ < nk || pf_next ? 1 : 0) + (s2_ + 1 < nk || pf_next ? 1 : 0);  \
+        if (prefetched && (kt) + 1 <= (P))                                                    \
+            wait_vmcnt_dyn(later_ * kLoadsPerStage + s_prev);                                 \
+        else if (later_ >= 2) wait_vmcnt<2 * kLoadsPerStage>();                               \
         else if (later_ == 1) wait_vmcnt<kLoadsPerStage>();                                   \
         else wait_vmcnt<0>();                                                                 \
     } while (0)
 
-    const int nk = K / BK;
-    // The previous tile's epilogue stores must be done before this tile's loads are
-    // issued: a compiler-visible wait here means the compiler sees no vector-memory
-    // operation pending inside the k loop (the loop's own loads are invisible to
-    // it), so it adds no drain of the prefetch there.
-    __builtin_amdgcn_s_waitcnt(0);
-    lds_barrier();  // the previous tile's epilogue is done with the LDS
-    // prologue: both groups issue their halves of stages 0..2, group 0 also of 3
+    if (!prefetched) {
+        // prologue: all waves are done with the ring; both groups issue their halves
+        // of stages 0..2, group 0 also of 3; wait for stage 0 (older stores of the
+        // previous tile complete first)
+        lds_barrier();
 #pragma unroll
-    for (int s = 0; s < STAGES - 1; ++s)
-        if (s < nk) issue_stage(s);
-    if (grp == 0 && STAGES - 1 < nk) issue_stage(STAGES - 1);
-    {
-        // stage 0 in: later stages of this group still allowed in flight
+        for (int s = 0; s < STAGES - 1; ++s)
+            if (s < nk) MOE_ISSUE(s);
+        if (grp == 0 && STAGES - 1 < nk) MOE_ISSUE(STAGES - 1);
         const int issued = min(nk, grp == 0 ? STAGES : STAGES - 1);
         if (issued >= 4) wait_vmcnt<3 * kLoadsPerStage>();
         else if (issued == 3) wait_vmcnt<2 * kLoadsPerStage>();
         else if (issued == 2) wait_vmcnt<kLoadsPerStage>();
         else wait_vmcnt<0>();
+        lds_barrier();
+        if (grp == 0) MOE_LOAD_STAGE_FRAGS(0);
+        lds_barrier();
+    } else if (grp == 0) {
+        // the stage is in (the previous tile's last wait and barrier); group 0 reads
+        // its fragments ahead of its first MFMAs, group 1 in its first phase as usual
+        MOE_LOAD_STAGE_FRAGS(0);
     }
-    lds_barrier();
-    if (grp == 0 && NV > 0) MOE_LOAD_STAGE_FRAGS(0);
-    lds_barrier();
 
     // Each group runs its own straight-line loop; both pass two barriers per stage.
     if (grp == 0) {
@@ -269,20 +389,20 @@ __device__ __forceinline__ void run_tile(const TileArgs& ta, uint16_t* lds, int 
             __builtin_amdgcn_s_setprio(1);
             if (NV > 0) MOE_MMA_STAGE();
             __builtin_amdgcn_s_setprio(0);
-            MOE_WAIT_NEXT(kt);  // own half of stage kt+1 in; kt+2, kt+3 may stay in flight
+            MOE_WAIT_NEXT(kt, 3);
             lds_barrier();
             // phase 2kt+1: refill the buffer of stage kt (both groups have read it)
             // with stage kt+4, and read stage kt+1
-            if (kt + STAGES < nk) issue_stage(kt + STAGES);
-            if (NV > 0 && kt + 1 < nk) MOE_LOAD_STAGE_FRAGS(kt + 1);
+            MOE_ISSUE(kt + STAGES);
+            if (kt + 1 < nk) MOE_LOAD_STAGE_FRAGS(kt + 1);
             lds_barrier();
         }
     } else {
         for (int kt = 0; kt < nk; ++kt) {
             // phase 2kt: read stage kt; issue stage kt+3 into the buffer of stage kt-1
-            if (NV > 0) MOE_LOAD_STAGE_FRAGS(kt);
-            if (kt + STAGES - 1 < nk) issue_stage(kt + STAGES - 1);
-            MOE_WAIT_NEXT(kt);  // own half of stage kt+1 in; kt+2, kt+3 may stay in flight
+            MOE_LOAD_STAGE_FRAGS(kt);
+            MOE_ISSUE(kt + STAGES - 1);
+            MOE_WAIT_NEXT(kt, 2);
             lds_barrier();
             // phase 2kt+1: compute stage kt
             __builtin_amdgcn_s_setprio(1);
@@ -291,50 +411,64 @@ __device__ __forceinline__ void run_tile(const TileArgs& ta, uint16_t* lds, int 
             lds_barrier();
         }
     }
+#undef MOE_ISSUE
 #undef MOE_LOAD_STAGE_FRAGS
 #undef MOE_MMA_STAGE
 #undef MOE_WAIT_NEXT
 
-    // ---- epilogue: accumulators -> bf16 -> LDS (per-wave region) -> 16-byte stores.
+    // ---- epilogue: accumulators -> bf16 -> global, straight from registers.
     // MFMA 32x32 output layout: lane l, register r holds
-    //   row = (r / 4) * 8 + (l / 32) * 4 + r % 4,  column = l % 32.
-    lds_barrier();  // all waves are done reading the last stage
-    if (NV == 0) return;
-    constexpr int OC = GLU ? WTN / 2 : WTN;  // output columns per wave
-    const int lrow = lane & 31;
-    uint16_t* so = lds + wave * (128 * OC);
+    //   row = (r / 4) * 8 + (l / 32) * 4 + r % 4,  column = l % 32,
+    // so registers 4q..4q+3 of the quad of lanes 4c..4c+3 form the 4x4 block of rows
+    // 8q + 4(l/32) + 0..3 and columns 4c + 0..3. Every store instruction covers 8 rows
+    // of one 32-column block; those with no row inside the segment are not issued,
+    // and the rest are counted.
+    int stores = 0;
+    if (NV > 0) {
+        // The tile's scalars pass through an empty asm here, so the compiler cannot
+        // compute the epilogue's addresses ahead of the k loop and hold them in
+        // registers across it.
+        int rows_valid = ta.rows_valid, n_cols = N, nt = ta.nt, zero = 0;
+        int ln = lane;
+        asm volatile("" : "+s"(rows_valid), "+s"(n_cols), "+s"(nt), "+s"(zero), "+v"(ln));
+        uint16_t* c_tile = ta.c_tile + zero;
+        const QuadSel qs = quad_sel(ln);
+        const int out_row = (ln >> 5) * 4 + (ln & 3);  // this lane's row in an 8-row group
+        // byte offset of this lane's 8 bytes from the group's (row 0, column 0)
+        const uint32_t out_off = (uint32_t)((out_row * n_cols + ((ln & 31) >> 2) * 4) * 2);
+        constexpr int OB = GLU ? NBN / 2 : NBN;    // 32-column output blocks per wave
+        const int col0 = GLU ? nt * 128 + wn * (WTN / 2) : nt * BN + wn * WTN;
 #pragma unroll
-    for (int i = 0; i < (NV > 0 ? NV : 1); ++i) {
+        for (int i = 0; i < NV; ++i) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int row = i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-            if (GLU) {
+            for (int jb = 0; jb < OB; ++jb) {
+                const int cb = col0 + jb * 32;
+                if (cb >= n_cols) continue;
 #pragma unroll
-                for (int j = 0; j < NBN / 2; ++j) {
-                    const float g = acc[i][j][r], u = acc[i][j + NBN / 2][r];
-                    const float hval = g / (1.0f + __expf(-g)) * u;
-                    so[row * OC + j * 32 + lrow] = (uint16_t)f32_to_bf16_rne(hval);
+                for (int q = 0; q < 4; ++q) {
+                    const int r0 = (2 * i + wm) * 32 + q * 8;
+                    if (r0 >= rows_valid) continue;
+                    float v[4];
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        if (GLU) {
+                            const float g = acc[i][jb][4 * q + m], u = acc[i][jb + NBN / 2][4 * q + m];
+                            v[m] = g / (1.0f + __expf(-g)) * u;
+                        } else {
+                            v[m] = acc[i][jb][4 * q + m];
+                        }
+                    }
+                    uint32_t w0, w1;
+                    quad_transpose_bf16(v[0], v[1], v[2], v[3], qs, w0, w1);
+                    char* grp0 = (char*)(c_tile + ((int64_t)r0 * n_cols + cb));
+                    if (out_row < rows_valid - r0)
+                        *(uint2*)(grp0 + out_off) = make_uint2(w0, w1);
+                    ++stores;
                 }
-            } else {
-#pragma unroll
-                for (int j = 0; j < NBN; ++j)
-                    so[row * OC + j * 32 + lrow] = (uint16_t)f32_to_bf16_rne(acc[i][j][r]);
             }
         }
     }
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes have landed
-    __builtin_amdgcn_wave_barrier();
-    constexpr int PPR = OC / 8;  // 16-byte pieces per output row of the wave
-    const int col0 = GLU ? nt * 128 + wn * (WTN / 2) : nt * BN + wn * WTN;
-#pragma unroll 4
-    for (int i = 0; i < (NV * 32 * PPR) / kWave; ++i) {
-        const int id = lane + i * kWave;
-        const int row = id / PPR, pc = id % PPR;
-        const int grow = ((row >> 5) * 2 + wm) * 32 + (row & 31);  // block row>>5 is block 2i+wm
-        const int gcol = col0 + pc * 8;
-        if (grow < rows_valid && gcol < N)
-            *(uint4*)(ta.c_tile + (int64_t)grow * N + gcol) = *(const uint4*)(so + row * OC + pc * 8);
-    }
+    return stores;
 }
 
 template <bool GLU>
@@ -346,9 +480,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_kernel(
     __shared__ int32_t seg_start[kMaxE + 1];
     __shared__ int32_t scan_tmp[kWaves];
 
-    const int tid = threadIdx.x, lane = lane_id();
-    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-    const int wm = wave / WGN;
+    const int tid = threadIdx.x;
     // column tiles per expert: GLU tiles cover 128 output columns (128 gate + 128 up rows)
     const int NT = GLU ? (N + 127) / 128 : (N + BN - 1) / BN;
     const int NW = GLU ? 2 * N : N;  // W rows per expert
@@ -356,7 +488,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_kernel(
 
     // ---- per-expert tile counts -> prefix (every workgroup builds its own copy)
     {
-        const int per = (E + kGemmThreads - 1) / kGemmThreads;  // <= 4
+        const int per = (E + kGemmThreads - 1) / kGemmThreads;  // <= 2
         int local = 0;
         for (int i = 0; i < per; ++i) {
             const int e = tid * per + i;
@@ -380,6 +512,26 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_kernel(
     }
     const int total = tile_start[E];
 
+    WaveCtx w;
+    w.lds = lds;
+    w.lds0 = lds_addr(lds);
+    w.K = K;
+    w.N = N;
+    w.nk = K / BK;
+    w.lane = lane_id();
+    w.wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    w.wm = w.wave / WGN;
+    w.wn = w.wave % WGN;
+    w.grp = w.wave >> 2;  // == wm
+    // lane-constant parts of the MFMA operand addresses: logical piece
+    // (2*ks + lane/32) of row (lane % 32) of each 32-row block
+    {
+        const int lrow = w.lane & 31;
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks)
+            w.rd_off[ks] = lrow * BK + (((2 * ks + (w.lane >> 5)) ^ swz(lrow)) << 3);
+    }
+
     // ---- XCD-aware split: XCD x takes the contiguous run [x*chunk, (x+1)*chunk)
     const int nxcd = 8;
     const int xcd = blockIdx.x % nxcd, slot = blockIdx.x / nxcd;
@@ -387,43 +539,59 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_kernel(
     const int chunk = (total + nxcd - 1) / nxcd;
     const int t_end = min(total, (xcd + 1) * chunk);
 
-    // lane-constant parts of the MFMA operand addresses: logical piece
-    // (2*ks + lane/32) of row (lane % 32) of each 32-row block
-    const int lrow = lane & 31;
-    int rd_off[KSTEPS];
-#pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) rd_off[ks] = lrow * BK + (((2 * ks + (lane >> 5)) ^ swz(lrow)) << 3);
-
-    for (int t = xcd * chunk + slot; t < t_end; t += per_xcd) {
+    auto tile_args = [&](int t) {
         // expert e: the last e with tile_start[e] <= t (experts with no tiles repeat a value)
         int lo = 0, hi = E;  // invariant: tile_start[lo] <= t < tile_start[hi]
         while (hi - lo > 1) {
             const int mid = (lo + hi) >> 1;
             if (tile_start[mid] <= t) lo = mid; else hi = mid;
         }
-        const int e = lo;
-        const int seg0 = seg_start[e], seg1 = seg_start[e + 1];
+        // every value below is uniform over the wave: keep it in scalar registers
+        const int e = __builtin_amdgcn_readfirstlane(lo);
+        const int seg0 = __builtin_amdgcn_readfirstlane(seg_start[e]);
+        const int seg1 = __builtin_amdgcn_readfirstlane(seg_start[e + 1]);
         const int mt_e = (seg1 - seg0 + BM - 1) / BM;
-        const int q = t - tile_start[e];
+        const int q = t - __builtin_amdgcn_readfirstlane(tile_start[e]);
         const int nt = q / mt_e, mt = q - nt * mt_e;
         const int row0 = seg0 + mt * BM;
         TileArgs ta;
         ta.a_tile = A + (int64_t)row0 * K;
         ta.w_exp = W + (int64_t)e * w_stride;
         ta.c_tile = C + (int64_t)row0 * N;
-        ta.K = K;
-        ta.N = N;
         ta.nt = nt;
         ta.rows_valid = min(BM, seg1 - row0);
         // live 32-row blocks of this wave: wave row wm owns blocks 2i + wm
-        const int nvb = max(0, min(4, ((ta.rows_valid + 31) / 32 - wm + 1) / 2));
-        switch (nvb) {
-            case 4: run_tile<GLU, 4>(ta, lds, wave, lane, rd_off); break;
-            case 3: run_tile<GLU, 3>(ta, lds, wave, lane, rd_off); break;
-            case 2: run_tile<GLU, 2>(ta, lds, wave, lane, rd_off); break;
-            case 1: run_tile<GLU, 1>(ta, lds, wave, lane, rd_off); break;
-            default: run_tile<GLU, 0>(ta, lds, wave, lane, rd_off); break;
+        ta.nvb = max(0, min(4, ((ta.rows_valid + 31) / 32 - w.wm + 1) / 2));
+        return ta;
+    };
+
+    // The next tile's first stages are prefetched when the ring can hold them
+    // (at least 4 k stages per tile).
+    const bool cross = w.nk >= STAGES;
+    int t = xcd * chunk + slot;
+    if (t >= t_end) return;
+    TileArgs cur = tile_args(t);
+    int base = 0, s_prev = 0;
+    bool prefetched = false;
+    for (;;) {
+        const int tn = t + per_xcd;
+        const bool has_next = tn < t_end;
+        const TileArgs nxt = has_next ? tile_args(tn) : cur;
+        const bool pf_next = has_next && cross;
+        int s;
+        switch (cur.nvb) {
+            case 4: s = run_tile<GLU, 4>(w, cur, nxt, base, prefetched, pf_next, s_prev); break;
+            case 3: s = run_tile<GLU, 3>(w, cur, nxt, base, prefetched, pf_next, s_prev); break;
+            case 2: s = run_tile<GLU, 2>(w, cur, nxt, base, prefetched, pf_next, s_prev); break;
+            case 1: s = run_tile<GLU, 1>(w, cur, nxt, base, prefetched, pf_next, s_prev); break;
+            default: s = run_tile<GLU, 0>(w, cur, nxt, base, prefetched, pf_next, s_prev); break;
         }
+        if (!has_next) break;
+        s_prev = s;
+        prefetched = pf_next;
+        base = (base + w.nk) & (STAGES - 1);
+        cur = nxt;
+        t = tn;
     }
 }
 

@@ -147,8 +147,23 @@ def _rows_of(counts, offsets):
                           + [np.zeros(0, np.int64)]).astype(np.int64)
 
 
+def _many_counts(E, hi, seed):
+    """Seeded per-expert row counts in [0, hi), about a fifth of them zero."""
+    r = np.random.default_rng(seed)
+    c = r.integers(0, hi, size=E)
+    c[r.random(E) < 0.2] = 0
+    return c.tolist()
+
+
 GEMM_CASES = [
     # name, counts, align, H, I
+    # enough tiles that every persistent workgroup runs several in a row, so the
+    # next tile's stages load during the previous tile's last steps (k >= 128)
+    ("many_tiles_k256", _many_counts(256, 800, 11), 32, 512, 256),
+    # several tiles per workgroup with k = 64: no prefetch across tiles
+    ("many_tiles_k64", _many_counts(256, 1500, 12), 32, 64, 64),
+    # rows per tile not a multiple of 8: partly masked 8-row store groups
+    ("many_tiles_align1", _many_counts(200, 700, 13), 1, 128, 128),
     ("ragged", [0, 1, 130, 257, 31, 64], 32, 256, 192),
     ("tails_align8", [5, 0, 129, 3, 300], 8, 128, 128),
     ("align1", [7, 1, 200], 1, 192, 64),
