@@ -14,9 +14,10 @@
 // GEMM ahead of a SwiGLU].
 //
 // Scheduling: a persistent grid (one workgroup per CU) walks the tile list in
-// expert-major order (expert, then column tile, then row tile), so an expert's
-// weights are read about once and stay in L2 while its row tiles run [prime-rl
-// PR 3885, Required kernel commits: expert-major task order].  The tile list is
+// expert-major order (expert, then row tile, then column tile), so an expert's
+// weights are read about once and stay in cache while its row tiles run [prime-rl
+// PR 3885, Required kernel commits: expert-major task order]; consecutive tiles
+// share a row tile of A.  The tile list is
 // dealt in contiguous runs per XCD (workgroup b runs on XCD b % 8), so each
 // expert's tiles share one XCD's L2.  Counts and offsets are read on the device;
 // an expert with no rows owns no tiles and reads no weights [PocketLLM "Qwen4-Exp
@@ -550,9 +551,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_kernel(
         const int e = __builtin_amdgcn_readfirstlane(lo);
         const int seg0 = __builtin_amdgcn_readfirstlane(seg_start[e]);
         const int seg1 = __builtin_amdgcn_readfirstlane(seg_start[e + 1]);
-        const int mt_e = (seg1 - seg0 + BM - 1) / BM;
         const int q = t - __builtin_amdgcn_readfirstlane(tile_start[e]);
-        const int nt = q / mt_e, mt = q - nt * mt_e;
+        const int mt = q / NT, nt = q - mt * NT;  // row tile, then column tile
         const int row0 = seg0 + mt * BM;
         TileArgs ta;
         ta.a_tile = A + (int64_t)row0 * K;
