@@ -5,11 +5,13 @@
 // gather-sum back].  Each output element is produced by exactly one lane from
 // its k inputs, so there is no scatter-add, no atomic and a fixed order.
 //
-// One wavefront per token; a lane owns 8 consecutive columns (one 16-byte piece)
-// per pass and has all k row pieces of that pass in flight before it sums them.
+// One wavefront per token; a lane owns two 16-byte pieces (8 columns each) per
+// pass and has all k row pieces of both in flight before it sums them.
 #include "common.hpp"
 
 namespace moe {
+
+constexpr int kCombinePieces = 2;  // 16-byte column pieces per lane per pass
 
 template <int KB>  // routes loaded per batch
 __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ y,
@@ -17,46 +19,60 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ 
                                                       const float* __restrict__ topk_w,
                                                       int64_t T, int pieces_per_row, int k, int64_t P_max,
                                                       uint4* __restrict__ out) {
+    constexpr int CP = kCombinePieces;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int64_t t = (int64_t)blockIdx.x * 4 + wave;
     if (t >= T) return;
     const int lane = lane_id();
     const int32_t* rows = route_row + t * k;   // wave-uniform addresses: scalar loads
     const float* ws = topk_w + t * k;
-    for (int c = lane; c < pieces_per_row; c += kWave) {
-        float acc[8];
+    for (int c0 = lane; c0 < pieces_per_row; c0 += kWave * CP) {
+        float acc[CP][8];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
+        for (int u = 0; u < CP; ++u)
+#pragma unroll
+            for (int q = 0; q < 8; ++q) acc[u][q] = 0.0f;
         for (int j0 = 0; j0 < k; j0 += KB) {
-            uint4 v[KB];
+            uint4 v[CP][KB];
             float w[KB];
 #pragma unroll
             for (int jj = 0; jj < KB; ++jj) {
                 const int j = j0 + jj;
                 const int32_t row = j < k ? rows[j] : -1;
                 // a row outside [0, P_max) contributes nothing (never read)
-                w[jj] = (row >= 0 && row < P_max) ? ws[j] : 0.0f;
-                v[jj] = (row >= 0 && row < P_max) ? y[(int64_t)row * pieces_per_row + c]
-                                                  : make_uint4(0u, 0u, 0u, 0u);
-            }
+                const bool ok = row >= 0 && row < P_max;
+                w[jj] = ok ? ws[j] : 0.0f;
 #pragma unroll
-            for (int jj = 0; jj < KB; ++jj) {
-                {
-                    const uint32_t p[4] = {v[jj].x, v[jj].y, v[jj].z, v[jj].w};
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        acc[2 * q] = fmaf(w[jj], bf16_lo(p[q]), acc[2 * q]);
-                        acc[2 * q + 1] = fmaf(w[jj], bf16_hi(p[q]), acc[2 * q + 1]);
-                    }
+                for (int u = 0; u < CP; ++u) {
+                    const int c = c0 + u * kWave;
+                    v[u][jj] = (ok && c < pieces_per_row) ? y[(int64_t)row * pieces_per_row + c]
+                                                          : make_uint4(0u, 0u, 0u, 0u);
                 }
             }
+#pragma unroll
+            for (int jj = 0; jj < KB; ++jj)
+#pragma unroll
+                for (int u = 0; u < CP; ++u) {
+                    const uint32_t p[4] = {v[u][jj].x, v[u][jj].y, v[u][jj].z, v[u][jj].w};
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        acc[u][2 * q] = fmaf(w[jj], bf16_lo(p[q]), acc[u][2 * q]);
+                        acc[u][2 * q + 1] = fmaf(w[jj], bf16_hi(p[q]), acc[u][2 * q + 1]);
+                    }
+                }
         }
-        uint4 o;
-        o.x = pack_bf16x2(acc[0], acc[1]);
-        o.y = pack_bf16x2(acc[2], acc[3]);
-        o.z = pack_bf16x2(acc[4], acc[5]);
-        o.w = pack_bf16x2(acc[6], acc[7]);
-        out[t * pieces_per_row + c] = o;
+#pragma unroll
+        for (int u = 0; u < CP; ++u) {
+            const int c = c0 + u * kWave;
+            if (c < pieces_per_row) {
+                uint4 o;
+                o.x = pack_bf16x2(acc[u][0], acc[u][1]);
+                o.y = pack_bf16x2(acc[u][2], acc[u][3]);
+                o.z = pack_bf16x2(acc[u][4], acc[u][5]);
+                o.w = pack_bf16x2(acc[u][6], acc[u][7]);
+                out[t * pieces_per_row + c] = o;
+            }
+        }
     }
 }
 

@@ -163,10 +163,14 @@ __global__ __launch_bounds__(256) void permute_scatter_kernel(const int32_t* __r
 // The gather, one 16-byte piece per lane: piece q of the layout is row q / ppr,
 // column piece q % ppr, so a wavefront covers 1 KB of consecutive layout bytes
 // (coalesced stores) read from the matching piece of the token's row. Each
-// thread has kGatherUnroll pieces in flight before its first store.
+// thread has kGatherUnroll pieces in flight before its first store. A layout
+// far larger than the 256 MB Infinity Cache is written with non-temporal
+// stores (NT), which do not evict the token rows still being read.
 constexpr int kGatherUnroll = 4;
 constexpr int kGatherThreads = 256;
+constexpr int64_t kStreamingLayoutBytes = 512ll << 20;
 
+template <bool NT>
 __global__ __launch_bounds__(kGatherThreads) void permute_gather_kernel(
     const uint4* __restrict__ x, const int32_t* __restrict__ row_token,
     const int32_t* __restrict__ offsets, int E, int ppr, uint4* __restrict__ x_perm) {
@@ -188,7 +192,14 @@ __global__ __launch_bounds__(kGatherThreads) void permute_gather_kernel(
 #pragma unroll
         for (int u = 0; u < kGatherUnroll; ++u) {
             const int64_t q = base + u * kGatherThreads;
-            if (q < used) x_perm[q] = v[u];
+            if (q < used) {
+                if (NT) {
+                    const u32x4_t t4 = {v[u].x, v[u].y, v[u].z, v[u].w};
+                    __builtin_nontemporal_store(t4, (u32x4_t*)(x_perm + q));
+                } else {
+                    x_perm[q] = v[u];
+                }
+            }
         }
     }
 }
@@ -231,9 +242,14 @@ hipError_t launch_permute(const uint16_t* x, const int32_t* topk_idx, int64_t T,
     const int64_t per_wg = kGatherThreads * kGatherUnroll;
     const int64_t want = (pieces + per_wg - 1) / per_wg;
     const unsigned grid = (unsigned)(want < 4096 ? want : 4096);
-    hipLaunchKernelGGL(permute_gather_kernel, dim3(grid), dim3(kGatherThreads), 0, stream,
-                       (const uint4*)x, (const int32_t*)row_token, (const int32_t*)offsets, E, ppr,
-                       (uint4*)x_perm);
+    if (P_max * (int64_t)H * 2 > kStreamingLayoutBytes)
+        hipLaunchKernelGGL(permute_gather_kernel<true>, dim3(grid), dim3(kGatherThreads), 0, stream,
+                           (const uint4*)x, (const int32_t*)row_token, (const int32_t*)offsets, E,
+                           ppr, (uint4*)x_perm);
+    else
+        hipLaunchKernelGGL(permute_gather_kernel<false>, dim3(grid), dim3(kGatherThreads), 0, stream,
+                           (const uint4*)x, (const int32_t*)row_token, (const int32_t*)offsets, E,
+                           ppr, (uint4*)x_perm);
     return hipGetLastError();
 }
 

@@ -116,7 +116,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(const float* 
 #pragma unroll
         for (int u = 0; u < kLanesPerToken; ++u) {
             const int j = jj * kLanesPerToken + u;
-            if (j >= k) break;
+            if (j >= k) continue;  // k <= KL: the loop unrolls fully
             float hv = lv[0];
             int hi = li[0];
             best_with<0xB1>(hv, hi);   // quad_perm [1,0,3,2]: lane ^ 1
