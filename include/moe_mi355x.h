@@ -10,6 +10,8 @@
  *                          expert-grouped row layout
  *   moe_grouped_glu_gemm   one grouped GEMM for every expert's gate and up
  *                          projections, SwiGLU fused into its epilogue
+ *   moe_grouped_glu_gemm_gather  the same GEMM reading token rows of x through
+ *                          row_token (the permute's gather folded into its loads)
  *   moe_grouped_down_gemm  one grouped GEMM for every expert's down projection
  *   moe_combine            fp32 score-weighted gather-sum back to token order
  *
@@ -116,7 +118,9 @@ moe_status moe_route_topk(const float *logits, int64_t T, int32_t E, int32_t k,
  *                   on every row at or past offsets[E]
  *   x_perm          [P_max, H] bf16 out: x_perm[p] = x[row_token[p]] bit for bit
  *                   on routed rows, zero on pad rows inside a segment; rows at or
- *                   past offsets[E] are not written
+ *                   past offsets[E] are not written. NULL skips the gather (the
+ *                   layout only, for moe_grouped_glu_gemm_gather); x may then be
+ *                   NULL too
  *   x               [T, H] bf16;  topk_idx [T, k] int32, each in [0, E) and
  *                   distinct per token (unchecked)
  *   workspace       device scratch of moe_permute_workspace_size() bytes
@@ -146,6 +150,24 @@ moe_status moe_grouped_glu_gemm(const moe_bf16 *x_perm, const moe_bf16 *w_gate_u
                                 const int32_t *expert_counts, const int32_t *expert_offsets,
                                 int32_t E, int32_t H, int32_t I, int64_t P_max, moe_bf16 *h,
                                 moe_stream_t stream);
+
+/*
+ * moe_grouped_glu_gemm with the permute's gather folded into the A loads
+ * [prime-rl, Changes: one gather into the padded expert-grouped layout -- here
+ * the layout rows are read in place from x].  For every routed row p:
+ *   h[p] = the h row moe_grouped_glu_gemm computes from x_perm[p] = x[row_token[p]]
+ *   x          [T, H] bf16, the tokens (not permuted)
+ *   row_token  [P_max] int32 from moe_permute (values in [0, T) or -1; unchecked)
+ * Rows of h that are pad rows of a segment hold unspecified values (their token
+ * is taken as 0); rows at or past offsets[E] are not written.
+ * Shapes as for moe_grouped_glu_gemm, plus T >= 1 and T * H * 2 < 2^32 (32-bit
+ * byte offsets into x), else MOE_ERR_SIZE_OVERFLOW.
+ */
+moe_status moe_grouped_glu_gemm_gather(const moe_bf16 *x, const int32_t *row_token,
+                                       const moe_bf16 *w_gate_up, const int32_t *expert_counts,
+                                       const int32_t *expert_offsets, int64_t T, int32_t E,
+                                       int32_t H, int32_t I, int64_t P_max, moe_bf16 *h,
+                                       moe_stream_t stream);
 
 /*
  * Grouped down GEMM [Halo, Levers that help: grouped GEMM].  For every expert e

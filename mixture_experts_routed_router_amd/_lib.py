@@ -54,11 +54,14 @@ def load():
                                 _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_sz, _c_vp]
     lib.moe_grouped_glu_gemm.argtypes = [_c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32,
                                          _c_i64, _c_vp, _c_vp]
+    lib.moe_grouped_glu_gemm_gather.argtypes = [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i32,
+                                                _c_i32, _c_i32, _c_i64, _c_vp, _c_vp]
     lib.moe_grouped_down_gemm.argtypes = [_c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32,
                                           _c_i64, _c_vp, _c_vp]
     lib.moe_combine.argtypes = [_c_vp, _c_vp, _c_vp, _c_i64, _c_i32, _c_i32, _c_i64, _c_vp, _c_vp]
     for fn in ("moe_permute_workspace_size", "moe_route_topk", "moe_permute",
-               "moe_grouped_glu_gemm", "moe_grouped_down_gemm", "moe_combine"):
+               "moe_grouped_glu_gemm", "moe_grouped_glu_gemm_gather", "moe_grouped_down_gemm",
+               "moe_combine"):
         getattr(lib, fn).restype = ctypes.c_int
     _LIB = lib
     return lib
@@ -125,26 +128,31 @@ class Layout:
     offsets: torch.Tensor    # [E+1] int32
     route_row: torch.Tensor  # [T*k] int32
     row_token: torch.Tensor  # [P_max] int32
-    x_perm: torch.Tensor     # [P_max, H] bf16
+    x_perm: torch.Tensor | None  # [P_max, H] bf16 (None: the layout only)
     P_max: int
 
 
-def alloc_layout(T: int, H: int, E: int, k: int, P_max: int, device) -> Layout:
+def alloc_layout(T: int, H: int, E: int, k: int, P_max: int, device, gather: bool = True) -> Layout:
     return Layout(torch.empty(E, dtype=torch.int32, device=device),
                   torch.empty(E + 1, dtype=torch.int32, device=device),
                   torch.empty(T * k, dtype=torch.int32, device=device),
                   torch.empty(P_max, dtype=torch.int32, device=device),
-                  torch.empty((P_max, H), dtype=torch.bfloat16, device=device), P_max)
+                  torch.empty((P_max, H), dtype=torch.bfloat16, device=device) if gather else None,
+                  P_max)
 
 
 def permute(x: torch.Tensor, topk_idx: torch.Tensor, E: int, align: int = 32, P_max=None,
-            out: Layout | None = None, workspace: torch.Tensor | None = None, stream=None) -> Layout:
+            out: Layout | None = None, workspace: torch.Tensor | None = None, stream=None,
+            gather: bool = True) -> Layout:
+    """The padded layout; with gather=False (or out.x_perm None) no x_perm is
+    written, for grouped_glu_gemm_gather."""
     T, H = x.shape
     k = topk_idx.shape[1]
     if P_max is None:
         P_max = padded_rows_max(T, k, E, align)
     if out is None:
-        out = alloc_layout(T, H, E, k, P_max, x.device)
+        out = alloc_layout(T, H, E, k, P_max, x.device, gather=gather)
+    gather = gather and out.x_perm is not None
     ws_bytes = permute_workspace_size(T, k, E)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=x.device)
@@ -154,7 +162,7 @@ def permute(x: torch.Tensor, topk_idx: torch.Tensor, E: int, align: int = 32, P_
           _ptr(out.offsets, torch.int32, "offsets", (E + 1,)),
           _ptr(out.route_row, torch.int32, "route_row", (T * k,)),
           _ptr(out.row_token, torch.int32, "row_token", (P_max,)),
-          _ptr(out.x_perm, torch.bfloat16, "x_perm", (P_max, H)),
+          _ptr(out.x_perm, torch.bfloat16, "x_perm", (P_max, H)) if gather else None,
           _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream))
     return out
 
@@ -170,6 +178,25 @@ def grouped_glu_gemm(x_perm, w_gate_up, counts, offsets, h=None, stream=None):
     _call("moe_grouped_glu_gemm", _ptr(x_perm, torch.bfloat16, "x_perm"),
           _ptr(w_gate_up, torch.bfloat16, "w_gate_up"), _ptr(counts, torch.int32, "counts", (E,)),
           _ptr(offsets, torch.int32, "offsets", (E + 1,)), E, H, I, P_max,
+          _ptr(h, torch.bfloat16, "h", (P_max, I)), _stream(stream))
+    return h
+
+
+def grouped_glu_gemm_gather(x, row_token, w_gate_up, counts, offsets, h=None, stream=None):
+    """grouped_glu_gemm on the layout rows x[row_token[p]] read in place (no x_perm);
+    h's pad rows are unspecified."""
+    T, H = x.shape
+    P_max = row_token.shape[0]
+    E, two_i, H2 = w_gate_up.shape
+    I = two_i // 2
+    if H2 != H or two_i != 2 * I:
+        raise ValueError("w_gate_up must be [E, 2I, H]")
+    if h is None:
+        h = torch.empty((P_max, I), dtype=torch.bfloat16, device=x.device)
+    _call("moe_grouped_glu_gemm_gather", _ptr(x, torch.bfloat16, "x"),
+          _ptr(row_token, torch.int32, "row_token", (P_max,)),
+          _ptr(w_gate_up, torch.bfloat16, "w_gate_up"), _ptr(counts, torch.int32, "counts", (E,)),
+          _ptr(offsets, torch.int32, "offsets", (E + 1,)), T, E, H, I, P_max,
           _ptr(h, torch.bfloat16, "h", (P_max, I)), _stream(stream))
     return h
 
@@ -202,15 +229,19 @@ def combine(y, route_row, topk_w, out=None, stream=None):
 
 class MoELayer:
     """Preallocated buffers for repeated layer calls of one shape; ``__call__``
-    enqueues the five library calls on the current stream and allocates nothing."""
+    enqueues the five library calls on the current stream and allocates nothing.
+    fused_gather=True runs the permute without its gather and the gate/up GEMM
+    reading token rows in place (moe_grouped_glu_gemm_gather); no x_perm exists."""
 
-    def __init__(self, T: int, H: int, E: int, k: int, I: int, align: int = 32, device="cuda"):
+    def __init__(self, T: int, H: int, E: int, k: int, I: int, align: int = 32, device="cuda",
+                 fused_gather: bool = False):
         self.T, self.H, self.E, self.k, self.I, self.align = T, H, E, k, I, align
+        self.fused_gather = fused_gather
         self.P_max = padded_rows_max(T, k, E, align)
         dev = torch.device(device)
         self.topk_idx = torch.empty((T, k), dtype=torch.int32, device=dev)
         self.topk_w = torch.empty((T, k), dtype=torch.float32, device=dev)
-        self.layout = alloc_layout(T, H, E, k, self.P_max, dev)
+        self.layout = alloc_layout(T, H, E, k, self.P_max, dev, gather=not fused_gather)
         self.workspace = torch.empty(max(permute_workspace_size(T, k, E), 256), dtype=torch.uint8,
                                      device=dev)
         self.h = torch.empty((self.P_max, I), dtype=torch.bfloat16, device=dev)
@@ -220,9 +251,13 @@ class MoELayer:
     def __call__(self, x, logits, w_gate_up, w_down, stream=None):
         route_topk(logits, self.k, self.topk_idx, self.topk_w, stream=stream)
         permute(x, self.topk_idx, self.E, self.align, self.P_max, out=self.layout,
-                workspace=self.workspace, stream=stream)
+                workspace=self.workspace, stream=stream, gather=not self.fused_gather)
         L = self.layout
-        grouped_glu_gemm(L.x_perm, w_gate_up, L.counts, L.offsets, h=self.h, stream=stream)
+        if self.fused_gather:
+            grouped_glu_gemm_gather(x, L.row_token, w_gate_up, L.counts, L.offsets, h=self.h,
+                                    stream=stream)
+        else:
+            grouped_glu_gemm(L.x_perm, w_gate_up, L.counts, L.offsets, h=self.h, stream=stream)
         grouped_down_gemm(self.h, w_down, L.counts, L.offsets, y=self.y, stream=stream)
         combine(self.y, L.route_row, self.topk_w, out=self.out, stream=stream)
         return self.out

@@ -13,6 +13,8 @@ hipError_t launch_permute(const uint16_t*, const int32_t*, int64_t, int, int, in
 size_t permute_workspace_bytes(int64_t R, int E);
 hipError_t launch_grouped_glu_gemm(const uint16_t*, const uint16_t*, const int32_t*, int, int, int,
                                    uint16_t*, hipStream_t);
+hipError_t launch_grouped_glu_gemm_gather(const uint16_t*, const int32_t*, const uint16_t*,
+                                          const int32_t*, int, int, int, uint16_t*, hipStream_t);
 hipError_t launch_grouped_down_gemm(const uint16_t*, const uint16_t*, const int32_t*, int, int, int,
                                     uint16_t*, hipStream_t);
 hipError_t launch_combine(const uint16_t*, const int32_t*, const float*, int64_t, int, int,
@@ -129,13 +131,14 @@ moe_status moe_permute(const moe_bf16* x, const int32_t* topk_idx, int64_t T, in
                        int32_t* expert_offsets, int32_t* route_row, int32_t* row_token,
                        moe_bf16* x_perm, void* workspace, size_t workspace_bytes,
                        moe_stream_t stream) {
-    REQUIRE_PTR_UNLESS_EMPTY(x, T == 0);
+    // x_perm == NULL: the layout only (no gather), and x is not read
+    REQUIRE_PTR_UNLESS_EMPTY(x, T == 0 || !x_perm);
     REQUIRE_PTR_UNLESS_EMPTY(topk_idx, T == 0);
     REQUIRE_PTR(expert_counts);
     REQUIRE_PTR(expert_offsets);
     REQUIRE_PTR_UNLESS_EMPTY(route_row, T == 0);
     REQUIRE_PTR(row_token);
-    REQUIRE_PTR(x_perm);
+    REQUIRE_PTR_UNLESS_EMPTY(x_perm, true);
     REQUIRE_PTR_UNLESS_EMPTY(workspace, T == 0);
     if (T < 0) return fail(MOE_ERR_INVALID_SHAPE, "T=%lld < 0", (long long)T);
     moe_status s = check_ek(E, k);
@@ -181,6 +184,22 @@ moe_status moe_grouped_glu_gemm(const moe_bf16* x_perm, const moe_bf16* w_gate_u
     return hip_status(moe::launch_grouped_glu_gemm(x_perm, w_gate_up, expert_offsets, E, H, I, h,
                                                    (hipStream_t)stream),
                       "moe_grouped_glu_gemm launch");
+}
+
+moe_status moe_grouped_glu_gemm_gather(const moe_bf16* x, const int32_t* row_token,
+                                       const moe_bf16* w_gate_up, const int32_t* expert_counts,
+                                       const int32_t* expert_offsets, int64_t T, int32_t E, int32_t H,
+                                       int32_t I, int64_t P_max, moe_bf16* h, moe_stream_t stream) {
+    moe_status s = check_gemm(x, w_gate_up, expert_counts, expert_offsets, E, H, I, P_max, h);
+    if (s != MOE_OK) return s;
+    REQUIRE_PTR(row_token);
+    if (T < 1) return fail(MOE_ERR_INVALID_SHAPE, "T=%lld < 1", (long long)T);
+    if ((uint64_t)T * (uint64_t)H * 2u >= ((uint64_t)1 << 32))
+        return fail(MOE_ERR_SIZE_OVERFLOW, "T*H*2 = %llu bytes of x reach 2^32 (32-bit offsets)",
+                    (unsigned long long)((uint64_t)T * (uint64_t)H * 2u));
+    return hip_status(moe::launch_grouped_glu_gemm_gather(x, row_token, w_gate_up, expert_offsets, E,
+                                                          H, I, h, (hipStream_t)stream),
+                      "moe_grouped_glu_gemm_gather launch");
 }
 
 moe_status moe_grouped_down_gemm(const moe_bf16* h, const moe_bf16* w_down,

@@ -203,10 +203,10 @@ __device__ __forceinline__ void quad_transpose_bf16(float v0, float v1, float v2
 
 // Everything one tile needs.
 struct TileArgs {
-    const uint16_t* a_tile;   // A + row0 * K
+    const uint16_t* a_tile;   // A + row0 * K (gathering A: the token matrix x itself)
     const uint16_t* w_exp;    // W + e * (W rows per expert) * K
     uint16_t* c_tile;         // C + row0 * N
-    int nt, rows_valid;
+    int row0, nt, rows_valid;
     int nvb;                  // this wave's 32-row blocks that hold segment rows (0..4)
 };
 
@@ -220,15 +220,23 @@ struct StageOffsets {
     uint32_t a[kPiecesPerThread], b[kPiecesPerThread];
 };
 
-template <bool GLU>
-__device__ __forceinline__ StageOffsets stage_offsets(const TileArgs& ta, int K, int N, int wave, int lane) {
+// GATHER: A is the token matrix x [T, K], and layout row p reads token row
+// row_token[p] -- the permute's gather folded into the loads. `tok` holds this
+// thread's token of each of its rows (issue_token_loads); a pad row (-1) reads
+// token 0 instead, its results are never read.
+template <bool GLU, bool GATHER>
+__device__ __forceinline__ StageOffsets stage_offsets(const TileArgs& ta, int K, int N, int wave, int lane,
+                                                      const uint32_t (&tok)[kPiecesPerThread]) {
     StageOffsets o;
 #pragma unroll
     for (int i = 0; i < kPiecesPerThread; ++i) {
         const int r = RPB * (kPiecesPerThread * wave + i) + lane / PR;
         const int piece = (lane % PR) ^ swz(r);
-        const int ar = r < ta.rows_valid ? r : 0;
-        o.a[i] = (uint32_t)((ar * K + piece * 8) * 2);
+        uint32_t ar;
+        if (GATHER) ar = (int32_t)tok[i] < 0 ? 0u : tok[i];
+        else ar = (uint32_t)(r < ta.rows_valid ? r : 0);
+        // 32-bit byte offset: the host guarantees rows * K * 2 < 2^32 (T * H * 2 when gathering)
+        o.a[i] = (ar * (uint32_t)K + (uint32_t)(piece * 8)) * 2u;
         int wr;
         if (GLU) {
             const int c = ta.nt * 128 + (r & 127);  // output column of this W row
@@ -241,6 +249,31 @@ __device__ __forceinline__ StageOffsets stage_offsets(const TileArgs& ta, int K,
         o.b[i] = (uint32_t)(((int64_t)wr * K + piece * 8) * 2);
     }
     return o;
+}
+
+// Gathering A: the tokens of a tile's rows go from row_token straight into LDS
+// (global_load_lds_dword, one instruction per wave, counted by vmcnt like the
+// stage loads; no register is written asynchronously). Wave w loads the tokens
+// of rows 32w .. 32w+31 -- the rows its stage loads cover -- into its own 64-slot
+// region (lanes 32..63 repeat them); rows past the segment read the tile's first
+// row. After the wave's own wait, read_tokens picks each thread's two rows; no
+// other wave touches the region, so no barrier is needed.
+constexpr int kTokSlots = 64;  // per wave and buffer
+
+__device__ __forceinline__ void issue_token_loads(const TileArgs& ta, const int32_t* row_token, int wave,
+                                                  int lane, uint32_t lds_region) {
+    const int r = 32 * wave + (lane & 31);
+    const uint32_t off = (uint32_t)(r < ta.rows_valid ? r : 0) * 4u;
+    const int32_t* base = row_token + ta.row0;
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2"
+                 :: "s"(lds_region), "v"(off), "s"(base) : "memory");
+}
+
+__device__ __forceinline__ void read_tokens(const int32_t* region, int lane,
+                                            uint32_t (&tok)[kPiecesPerThread]) {
+    static_assert(kPiecesPerThread * RPB == 32, "a wave's stage loads cover 32 rows");
+#pragma unroll
+    for (int i = 0; i < kPiecesPerThread; ++i) tok[i] = (uint32_t)region[RPB * i + lane / PR];
 }
 
 // This thread's share of one stage: A and B pieces of k-stage kt of a tile into ring slot `slot`.
@@ -262,6 +295,7 @@ struct WaveCtx {
     int K, N, nk;
     int wave, lane, wm, wn, grp;
     int rd_off[KSTEPS];
+    int32_t* tok_lds;    // gathering A: [2][kWaves][kTokSlots] token buffers
 };
 
 // One tile: the k loop through the LDS ring, then the epilogue. NV = number of
@@ -279,13 +313,33 @@ struct WaveCtx {
 // an 8-byte store. This wave's stores of the previous tile (s_prev of them) were
 // issued after the prefetched stages; vector-memory operations complete in issue
 // order, so a wait for a prefetched stage may leave those stores in flight.
-template <bool GLU, int NV>
+template <bool GLU, bool GATHER, int NV>
 __device__ __forceinline__ int run_tile(const WaveCtx& w, const TileArgs& ta, const TileArgs& tn,
-                                        int base, bool prefetched, bool pf_next, int s_prev) {
+                                        int base, bool prefetched, bool pf_next, int s_prev,
+                                        const int32_t* __restrict__ row_token, int tb) {
     const int K = w.K, N = w.N, nk = w.nk, wave = w.wave, lane = w.lane, wm = w.wm, wn = w.wn;
     const int grp = w.grp;
-    const StageOffsets oc = stage_offsets<GLU>(ta, K, N, wave, lane);
-    const StageOffsets on = stage_offsets<GLU>(tn, K, N, wave, lane);
+    // Gathering A: this tile's tokens are in token buffer tb (loaded during the
+    // previous tile when it prefetched this one, else loaded here); the next
+    // tile's go to buffer tb^1 now and are waited for just before its first stage
+    // is issued.
+    const int32_t* tok_cur = w.tok_lds + (tb * kWaves + wave) * kTokSlots;
+    const int32_t* tok_nxt = w.tok_lds + ((tb ^ 1) * kWaves + wave) * kTokSlots;
+    uint32_t tok[kPiecesPerThread] = {0u, 0u}, tkn[kPiecesPerThread] = {0u, 0u};
+    int n_tok = 0;  // token loads of the next tile in flight (issued after any prefetched stage)
+    if (GATHER) {
+        if (!prefetched) issue_token_loads(ta, row_token, wave, lane, lds_addr((const uint16_t*)tok_cur));
+        if (pf_next) {
+            issue_token_loads(tn, row_token, wave, lane, lds_addr((const uint16_t*)tok_nxt));
+            n_tok = 1;
+        }
+        if (!prefetched) {
+            if (n_tok) wait_vmcnt<1>();
+            else wait_vmcnt<0>();
+        }
+        read_tokens(tok_cur, lane, tok);
+    }
+    const StageOffsets oc = stage_offsets<GLU, GATHER>(ta, K, N, wave, lane, tok);
 
     // LDS B row of each of this wave's 32-column blocks. GLU: the first half of
     // the blocks are gate columns, the second half the matching up columns.
@@ -325,8 +379,10 @@ __device__ __forceinline__ int run_tile(const WaveCtx& w, const TileArgs& ta, co
         const int slot_ = (base + s_) & (STAGES - 1);                                             \
         if (s_ < nk)                                                                              \
             issue_stage(w.lds0, slot_, wave, ta.a_tile + s_ * BK, ta.w_exp + s_ * BK, oc);        \
-        else if (pf_next)                                                                         \
-            issue_stage(w.lds0, slot_, wave, tn.a_tile + (s_ - nk) * BK, tn.w_exp + (s_ - nk) * BK, on); \
+        else if (pf_next) {                                                                       \
+            const StageOffsets on_ = stage_offsets<GLU, GATHER>(tn, K, N, wave, lane, tkn);        \
+            issue_stage(w.lds0, slot_, wave, tn.a_tile + (s_ - nk) * BK, tn.w_exp + (s_ - nk) * BK, on_); \
+        }                                                                                         \
     } while (0)
 #define MOE_LOAD_STAGE_FRAGS(stage)                                                           \
     do {                                                                                      \
@@ -346,6 +402,18 @@ __device__ __forceinline__ int run_tile(const WaveCtx& w, const TileArgs& ta, co
                 _Pragma("unroll") for (int j = 0; j < NBN; ++j)                               \
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks][i], fb[ks][j], acc[i][j], 0, 0, 0); \
     } while (0)
+    // Before this group's first load of the next tile (issued at iteration FIRST_),
+    // wait for the next tile's token loads: since they were issued, this group has
+    // issued PRO_ prologue stages (none when this tile was prefetched) and one
+    // stage in each earlier iteration, all of which may stay in flight.
+#define MOE_WAIT_TOKENS(kt, FIRST_, PRO_)                                                     \
+    do {                                                                                      \
+        if (GATHER && pf_next && (kt) == (FIRST_)) {                                          \
+            const int younger_ = ((prefetched ? 0 : (PRO_)) + (kt)) * kLoadsPerStage;          \
+            wait_vmcnt_dyn(younger_ < 60 ? younger_ : 60);                                    \
+            read_tokens(tok_nxt, lane, tkn);                                                  \
+        }                                                                                     \
+    } while (0)
     // Wait for this group's half of stage kt+1. Its later stages kt+2, kt+3 (where
     // they exist) may stay in flight, and so may the previous tile's stores when
     // stage kt+1 was issued before them (prefetched stages 0..P).
@@ -354,7 +422,7 @@ __device__ __forceinline__ int run_tile(const WaveCtx& w, const TileArgs& ta, co
         const int s2_ = (kt) + 2;                                                             \
         const int later_ = (s2_ < nk || pf_next ? 1 : 0) + (s2_ + 1 < nk || pf_next ? 1 : 0);  \
         if (prefetched && (kt) + 1 <= (P))                                                    \
-            wait_vmcnt_dyn(later_ * kLoadsPerStage + s_prev);                                 \
+            wait_vmcnt_dyn(later_ * kLoadsPerStage + s_prev + n_tok);                         \
         else if (later_ >= 2) wait_vmcnt<2 * kLoadsPerStage>();                               \
         else if (later_ == 1) wait_vmcnt<kLoadsPerStage>();                                   \
         else wait_vmcnt<0>();                                                                 \
@@ -394,6 +462,7 @@ __device__ __forceinline__ int run_tile(const WaveCtx& w, const TileArgs& ta, co
             lds_barrier();
             // phase 2kt+1: refill the buffer of stage kt (both groups have read it)
             // with stage kt+4, and read stage kt+1
+            MOE_WAIT_TOKENS(kt, nk - STAGES, STAGES);
             MOE_ISSUE(kt + STAGES);
             if (kt + 1 < nk) MOE_LOAD_STAGE_FRAGS(kt + 1);
             lds_barrier();
@@ -402,6 +471,7 @@ __device__ __forceinline__ int run_tile(const WaveCtx& w, const TileArgs& ta, co
         for (int kt = 0; kt < nk; ++kt) {
             // phase 2kt: read stage kt; issue stage kt+3 into the buffer of stage kt-1
             MOE_LOAD_STAGE_FRAGS(kt);
+            MOE_WAIT_TOKENS(kt, nk - STAGES + 1, STAGES - 1);
             MOE_ISSUE(kt + STAGES - 1);
             MOE_WAIT_NEXT(kt, 2);
             lds_barrier();
@@ -416,6 +486,7 @@ __device__ __forceinline__ int run_tile(const WaveCtx& w, const TileArgs& ta, co
 #undef MOE_LOAD_STAGE_FRAGS
 #undef MOE_MMA_STAGE
 #undef MOE_WAIT_NEXT
+#undef MOE_WAIT_TOKENS
 
     // ---- epilogue: accumulators -> bf16 -> global, straight from registers.
     // MFMA 32x32 output layout: lane l, register r holds
@@ -472,14 +543,16 @@ __device__ __forceinline__ int run_tile(const WaveCtx& w, const TileArgs& ta, co
     return stores;
 }
 
-template <bool GLU>
+template <bool GLU, bool GATHER>
 __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_kernel(
-    const uint16_t* __restrict__ A, const uint16_t* __restrict__ W,
-    const int32_t* __restrict__ offsets, int E, int K, int N, uint16_t* __restrict__ C) {
+    const uint16_t* __restrict__ A, const int32_t* __restrict__ row_token,
+    const uint16_t* __restrict__ W, const int32_t* __restrict__ offsets, int E, int K, int N,
+    uint16_t* __restrict__ C) {
     __shared__ __attribute__((aligned(1024))) uint16_t lds[kLdsElems];
     __shared__ int32_t tile_start[kMaxE + 1];
     __shared__ int32_t seg_start[kMaxE + 1];
     __shared__ int32_t scan_tmp[kWaves];
+    __shared__ __attribute__((aligned(16))) int32_t tok_lds[GATHER ? 2 * kWaves * kTokSlots : 1];
 
     const int tid = threadIdx.x;
     // column tiles per expert: GLU tiles cover 128 output columns (128 gate + 128 up rows)
@@ -524,6 +597,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_kernel(
     w.wm = w.wave / WGN;
     w.wn = w.wave % WGN;
     w.grp = w.wave >> 2;  // == wm
+    w.tok_lds = tok_lds;
     // lane-constant parts of the MFMA operand addresses: logical piece
     // (2*ks + lane/32) of row (lane % 32) of each 32-row block
     {
@@ -555,7 +629,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_kernel(
         const int mt = q / NT, nt = q - mt * NT;  // row tile, then column tile
         const int row0 = seg0 + mt * BM;
         TileArgs ta;
-        ta.a_tile = A + (int64_t)row0 * K;
+        ta.a_tile = GATHER ? A : A + (int64_t)row0 * K;
+        ta.row0 = row0;
         ta.w_exp = W + (int64_t)e * w_stride;
         ta.c_tile = C + (int64_t)row0 * N;
         ta.nt = nt;
@@ -568,6 +643,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_kernel(
     // The next tile's first stages are prefetched when the ring can hold them
     // (at least 4 k stages per tile).
     const bool cross = w.nk >= STAGES;
+    int tb = 0;  // gathering A: the current tile's token buffer
     int t = xcd * chunk + slot;
     if (t >= t_end) return;
     TileArgs cur = tile_args(t);
@@ -580,16 +656,17 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_kernel(
         const bool pf_next = has_next && cross;
         int s;
         switch (cur.nvb) {
-            case 4: s = run_tile<GLU, 4>(w, cur, nxt, base, prefetched, pf_next, s_prev); break;
-            case 3: s = run_tile<GLU, 3>(w, cur, nxt, base, prefetched, pf_next, s_prev); break;
-            case 2: s = run_tile<GLU, 2>(w, cur, nxt, base, prefetched, pf_next, s_prev); break;
-            case 1: s = run_tile<GLU, 1>(w, cur, nxt, base, prefetched, pf_next, s_prev); break;
-            default: s = run_tile<GLU, 0>(w, cur, nxt, base, prefetched, pf_next, s_prev); break;
+            case 4: s = run_tile<GLU, GATHER, 4>(w, cur, nxt, base, prefetched, pf_next, s_prev, row_token, tb); break;
+            case 3: s = run_tile<GLU, GATHER, 3>(w, cur, nxt, base, prefetched, pf_next, s_prev, row_token, tb); break;
+            case 2: s = run_tile<GLU, GATHER, 2>(w, cur, nxt, base, prefetched, pf_next, s_prev, row_token, tb); break;
+            case 1: s = run_tile<GLU, GATHER, 1>(w, cur, nxt, base, prefetched, pf_next, s_prev, row_token, tb); break;
+            default: s = run_tile<GLU, GATHER, 0>(w, cur, nxt, base, prefetched, pf_next, s_prev, row_token, tb); break;
         }
         if (!has_next) break;
         s_prev = s;
         prefetched = pf_next;
         base = (base + w.nk) & (STAGES - 1);
+        tb ^= 1;
         cur = nxt;
         t = tn;
     }
@@ -618,15 +695,23 @@ static unsigned persistent_grid() {
 hipError_t launch_grouped_glu_gemm(const uint16_t* x_perm, const uint16_t* w_gu,
                                    const int32_t* offsets, int E, int H, int I, uint16_t* h,
                                    hipStream_t stream) {
-    hipLaunchKernelGGL(grouped_gemm_kernel<true>, dim3(persistent_grid()), dim3(kGemmThreads), 0,
-                       stream, x_perm, w_gu, offsets, E, H, I, h);
+    hipLaunchKernelGGL((grouped_gemm_kernel<true, false>), dim3(persistent_grid()), dim3(kGemmThreads),
+                       0, stream, x_perm, (const int32_t*)nullptr, w_gu, offsets, E, H, I, h);
+    return hipGetLastError();
+}
+
+hipError_t launch_grouped_glu_gemm_gather(const uint16_t* x, const int32_t* row_token,
+                                          const uint16_t* w_gu, const int32_t* offsets, int E, int H,
+                                          int I, uint16_t* h, hipStream_t stream) {
+    hipLaunchKernelGGL((grouped_gemm_kernel<true, true>), dim3(persistent_grid()), dim3(kGemmThreads),
+                       0, stream, x, row_token, w_gu, offsets, E, H, I, h);
     return hipGetLastError();
 }
 
 hipError_t launch_grouped_down_gemm(const uint16_t* h, const uint16_t* w_d, const int32_t* offsets,
                                     int E, int H, int I, uint16_t* y, hipStream_t stream) {
-    hipLaunchKernelGGL(grouped_gemm_kernel<false>, dim3(persistent_grid()), dim3(kGemmThreads), 0,
-                       stream, h, w_d, offsets, E, I, H, y);
+    hipLaunchKernelGGL((grouped_gemm_kernel<false, false>), dim3(persistent_grid()), dim3(kGemmThreads),
+                       0, stream, h, (const int32_t*)nullptr, w_d, offsets, E, I, H, y);
     return hipGetLastError();
 }
 

@@ -236,6 +236,7 @@ hipError_t launch_permute(const uint16_t* x, const int32_t* topk_idx, int64_t T,
         err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
+    if (!x_perm) return hipGetLastError();  // the layout only
     const int ppr = H / 8;  // 16-byte pieces per row
     // enough workgroups to cover P_max rows once, capped at a few waves of the chip
     const int64_t pieces = P_max * (int64_t)ppr;

@@ -38,6 +38,7 @@ def lib():
     lib.moe_permute.argtypes = [vp, vp, i64, i32, i32, i32, i32, i64, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.moe_grouped_glu_gemm.argtypes = [vp, vp, vp, vp, i32, i32, i32, i64, vp, vp]
     lib.moe_grouped_down_gemm.argtypes = [vp, vp, vp, vp, i32, i32, i32, i64, vp, vp]
+    lib.moe_grouped_glu_gemm_gather.argtypes = [vp, vp, vp, vp, vp, i64, i32, i32, i32, i64, vp, vp]
     lib.moe_combine.argtypes = [vp, vp, vp, i64, i32, i32, i64, vp, vp]
     return lib
 
@@ -87,10 +88,10 @@ def test_route_topk_validation(lib):
     assert lib.moe_route_topk(FAKE + 4, 0, 8, 2, None, None, None) == MISALIGNED
 
 
-def _permute(lib, T=4, H=128, E=8, k=2, align=32, P_max=None, ws=1 << 20, x=FAKE):
+def _permute(lib, T=4, H=128, E=8, k=2, align=32, P_max=None, ws=1 << 20, x=FAKE, x_perm=FAKE):
     if P_max is None:
         P_max = T * k + E * (align - 1)
-    return lib.moe_permute(x, FAKE, T, H, E, k, align, P_max, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+    return lib.moe_permute(x, FAKE, T, H, E, k, align, P_max, FAKE, FAKE, FAKE, FAKE, x_perm, FAKE,
                            ws, None)
 
 
@@ -103,6 +104,9 @@ def test_permute_validation(lib):
     assert _permute(lib, P_max=1 << 31) == OVERFLOW
     assert _permute(lib, ws=0) == WORKSPACE
     assert b"workspace" in lib.moe_last_error_message()
+    # x_perm NULL: the layout only, x is not needed (validation goes on to the shape check)
+    assert _permute(lib, x=None, x_perm=None, H=96) == SHAPE
+    assert _permute(lib, x=FAKE, x_perm=FAKE + 8) == MISALIGNED
 
 
 def test_gemm_validation(lib):
@@ -113,6 +117,17 @@ def test_gemm_validation(lib):
         assert fn(FAKE, FAKE, FAKE, FAKE, 0, 128, 256, 1000, FAKE, None) == SHAPE
         assert fn(FAKE, FAKE, FAKE, FAKE, 8, 128, 256, 0, FAKE, None) == OVERFLOW
         assert fn(FAKE, FAKE + 8, FAKE, FAKE, 8, 128, 256, 1000, FAKE, None) == MISALIGNED
+
+
+def test_gemm_gather_validation(lib):
+    fn = lib.moe_grouped_glu_gemm_gather
+    assert fn(FAKE, None, FAKE, FAKE, FAKE, 100, 8, 128, 256, 1000, FAKE, None) == NULLP
+    assert b"row_token" in lib.moe_last_error_message()
+    assert fn(FAKE, FAKE, FAKE, FAKE, FAKE, 0, 8, 128, 256, 1000, FAKE, None) == SHAPE       # T < 1
+    assert fn(FAKE, FAKE, FAKE, FAKE, FAKE, 100, 8, 100, 256, 1000, FAKE, None) == SHAPE     # H % 64
+    # T * H * 2 bytes of x must stay below 2^32 (32-bit offsets)
+    assert fn(FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, 8, 2048, 256, 1000, FAKE, None) == OVERFLOW
+    assert fn(FAKE + 8, FAKE, FAKE, FAKE, FAKE, 100, 8, 128, 256, 1000, FAKE, None) == MISALIGNED
 
 
 def test_combine_validation(lib):

@@ -193,6 +193,30 @@ def test_grouped_glu_gemm(gpu_lib, case):
     assert (hg[pad] == 0).all()  # zero pad rows give silu(0) * 0 = 0
 
 
+@pytest.mark.parametrize("case", GEMM_CASES, ids=[c[0] for c in GEMM_CASES])
+def test_grouped_glu_gemm_gather(gpu_lib, case):
+    """The gate/up GEMM reading layout rows x[row_token[p]] in place equals the
+    oracle GEMM on the gathered layout, on every routed row (pad rows unspecified)."""
+    name, counts, align, H, I = case
+    _say(f"glu gemm gather case {name}")
+    counts, offsets = _synthetic_layout(counts, align)
+    E, P = len(counts), int(offsets[-1])
+    P_max = P + 64
+    rows = _rows_of(counts, offsets)
+    T = max(1, len(rows) // 3 + 7)
+    r = np.random.default_rng(sum(name.encode()))
+    row_token = np.full(P_max, -1, np.int32)
+    row_token[rows] = r.integers(0, T, size=len(rows))
+    x = gen.random_bf16((T, H), seed=6)
+    w_gu = gen.random_bf16((E, 2 * I, H), seed=2, std=0.02)
+    h = gpu_lib.grouped_glu_gemm_gather(dev_bf16(x), dev(row_token), dev_bf16(w_gu), dev(counts),
+                                        dev(offsets))
+    torch.cuda.synchronize()
+    x_perm = oracle.gather(x, row_token, rows=P_max)
+    h_ref = oracle.glu(x_perm, w_gu, counts, offsets, I)
+    assert_close_bf16(host_f64(h[:P])[rows], h_ref[rows], f"h_gather[{name}]")
+
+
 @pytest.mark.parametrize("case", GEMM_CASES + [("N_tail_H320", [40, 70], 32, 320, 128)],
                          ids=[c[0] for c in GEMM_CASES] + ["N_tail_H320"])
 def test_grouped_down_gemm(gpu_lib, case):
@@ -250,9 +274,9 @@ def test_identity_experts(gpu_lib):
 # the whole layer
 # --------------------------------------------------------------------------------------
 
-def _run_layer(gpu_lib, d, stream=None):
+def _run_layer(gpu_lib, d, stream=None, fused_gather=False):
     cfg = d["cfg"]
-    layer = gpu_lib.MoELayer(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.align)
+    layer = gpu_lib.MoELayer(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.align, fused_gather=fused_gather)
     args = (dev_bf16(d["x"]), dev(d["logits"]), dev_bf16(d["w_gu"]), dev_bf16(d["w_d"]))
     if stream is None:
         layer(*args)
@@ -264,9 +288,9 @@ def _run_layer(gpu_lib, d, stream=None):
     return layer
 
 
-def _check_layer(gpu_lib, d, n_tokens=None, full_rows=True):
+def _check_layer(gpu_lib, d, n_tokens=None, full_rows=True, fused_gather=False):
     cfg = d["cfg"]
-    layer = _run_layer(gpu_lib, d)
+    layer = _run_layer(gpu_lib, d, fused_gather=fused_gather)
     idx_ref, w_ref = oracle.route_topk(d["logits"], cfg.k)
     assert (layer.topk_idx.cpu().numpy() == idx_ref).all()
     assert np.max(np.abs(layer.topk_w.cpu().numpy() - w_ref)) <= 1e-6
@@ -277,7 +301,9 @@ def _check_layer(gpu_lib, d, n_tokens=None, full_rows=True):
     assert (L.route_row.cpu().numpy() == rr_ref).all()
     assert (L.row_token.cpu().numpy() == rt_ref).all()
     used = int(o_ref[-1])
-    if full_rows:
+    if fused_gather:
+        assert L.x_perm is None  # the layout only: no x_perm exists
+    elif full_rows:
         assert (host_bits(L.x_perm[:used]) == oracle.gather(d["x"], rt_ref, rows=used)).all()
     toks = sample_tokens(cfg.T, n_tokens or cfg.T, cfg.seed)
     ref = oracle.forward(d["x"], d["logits"], d["w_gu"], d["w_d"], cfg.k, tokens=toks)
@@ -312,6 +338,20 @@ def test_layer_small(gpu_lib, cfg):
 # always compared in full)
 FULL_SIZE = [("gpt_oss_20b_small_m", None), ("qwen3_30b_a3b", 512), ("fine_grained_512", 384),
              ("skewed_zipf", 384)]
+
+
+@pytest.mark.parametrize("cfg", SMALL_LAYERS, ids=[c.name for c in SMALL_LAYERS])
+def test_layer_small_fused_gather(gpu_lib, cfg):
+    """The same layer with the permute's gather folded into the gate/up GEMM."""
+    _say(f"fused-gather layer case {cfg.name}")
+    _check_layer(gpu_lib, gen.make_inputs(cfg), fused_gather=True)
+
+
+@pytest.mark.parametrize("name,n", [("qwen3_30b_a3b", 256), ("skewed_zipf", 256)],
+                         ids=["qwen3_30b_a3b", "skewed_zipf"])
+def test_layer_full_size_fused_gather(gpu_lib, name, n):
+    _say(f"full-size fused-gather layer {name}")
+    _check_layer(gpu_lib, gen.make_inputs(name), n_tokens=n, full_rows=False, fused_gather=True)
 
 
 @pytest.mark.parametrize("name,n", FULL_SIZE, ids=[c[0] for c in FULL_SIZE])
