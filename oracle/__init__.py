@@ -8,10 +8,14 @@ with gcc, wrapped here with numpy arrays.
 Every function follows the page passage cited in ``moe_oracle.c``:
 routing [PocketLLM "Qwen4-Exp Heterogeneous TP4 Performance", Runtime
 architecture], layout and combine [prime-rl PR 3885, Changes: single-pass local
-layout], grouped experts [Halo "Performance", Levers that help].
+layout], grouped experts [Halo "Performance", Levers that help], FP8 expert
+weights [Halo "Performance", Levers that do not help here; prime-rl, Changes:
+FP8 expert weights quantized once per optimizer step].
 
 All floating-point results are float64 and exact up to rounding order: bf16
-inputs are widened exactly and nothing in the chain is rounded.
+inputs are widened exactly and nothing in the chain is rounded. The FP8
+quantizer is the one step that rounds, by its definition: fp32 scale and
+quotient, then the nearest E4M3 code.
 
 Pins: each function is checked by ``tests/test_oracle_pins.py`` against brute
 force, closed forms and invariants that do not reuse this code.
@@ -32,6 +36,7 @@ _i64p = ctypes.POINTER(ctypes.c_int64)
 _u16p = ctypes.POINTER(ctypes.c_uint16)
 _f32p = ctypes.POINTER(ctypes.c_float)
 _f64p = ctypes.POINTER(ctypes.c_double)
+_u8p = ctypes.POINTER(ctypes.c_uint8)
 
 _ERRORS = {-1: "invalid argument", -2: "non-finite logit", -3: "index out of range"}
 
@@ -51,11 +56,19 @@ def _load(path: str):
     lib.moe_oracle_combine.argtypes = [_f64p, _i32p, _f64p, i64, i32, i32, i64, _f64p]
     lib.moe_oracle_forward.argtypes = [_u16p, _f32p, _u16p, _u16p, i64, i32, i32, i32, i32,
                                        _i64p, i64, _f64p]
+    lib.moe_oracle_fp8_encode.argtypes = [_f32p, i64, _u8p]
+    lib.moe_oracle_fp8_decode.argtypes = [_u8p, i64, _f64p]
+    lib.moe_oracle_quantize_fp8.argtypes = [_u16p, i64, i32, i32, _u8p, _f32p]
+    lib.moe_oracle_dequantize_fp8.argtypes = [_u8p, _f32p, i64, i32, i32, _f64p]
+    lib.moe_oracle_glu_w64.argtypes = [_u16p, _f64p, _i32p, _i32p, i32, i32, i32, _f64p]
+    lib.moe_oracle_down_w64.argtypes = [_f64p, _f64p, _i32p, _i32p, i32, i32, i32, _f64p]
     lib.moe_oracle_num_threads.argtypes = []
     lib.moe_oracle_num_threads.restype = ctypes.c_int
     for name in ("moe_oracle_route_topk", "moe_oracle_layout", "moe_oracle_gather",
                  "moe_oracle_glu", "moe_oracle_down", "moe_oracle_combine",
-                 "moe_oracle_forward"):
+                 "moe_oracle_forward", "moe_oracle_fp8_encode", "moe_oracle_fp8_decode",
+                 "moe_oracle_quantize_fp8", "moe_oracle_dequantize_fp8", "moe_oracle_glu_w64",
+                 "moe_oracle_down_w64"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
 
@@ -203,6 +216,76 @@ def forward(x_bits, logits, w_gu_bits, w_d_bits, k: int, tokens=None, lib=None) 
     return out
 
 
+def fp8_encode(v, lib=None) -> np.ndarray:
+    """OCP E4M3 codes (uint8) of float32 values, nearest with ties to even; |v| <= 448."""
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    out = np.empty(v.shape, np.uint8)
+    _check((lib or _lib()).moe_oracle_fp8_encode(_p(v, _f32p), v.size, _p(out, _u8p)), "fp8_encode")
+    return out
+
+
+def fp8_decode(c, lib=None) -> np.ndarray:
+    """float64 values of OCP E4M3 codes (NaN for S.1111.111)."""
+    c = np.ascontiguousarray(c, dtype=np.uint8)
+    out = np.empty(c.shape, np.float64)
+    _check((lib or _lib()).moe_oracle_fp8_decode(_p(c, _u8p), c.size, _p(out, _f64p)), "fp8_decode")
+    return out
+
+
+def quantize_fp8(w_bits, lib=None):
+    """Block-scaled FP8 of expert weights [E, R, K] (bf16 bits): (w8 uint8 [E, R, K],
+    scale float32 [E, R // 64]), one scale per 64 rows."""
+    w_bits = _u16(w_bits)
+    E, R, K = w_bits.shape
+    w8 = np.empty((E, R, K), np.uint8)
+    scale = np.empty((E, R // 64), np.float32)
+    _check((lib or _lib()).moe_oracle_quantize_fp8(_p(w_bits, _u16p), E, R, K, _p(w8, _u8p),
+                                                   _p(scale, _f32p)), "quantize_fp8")
+    return w8, scale
+
+
+def dequantize_fp8(w8, scale, lib=None) -> np.ndarray:
+    """float64 [E, R, K] = scale[e, r // 64] * value(w8[e, r, c])."""
+    w8 = np.ascontiguousarray(w8, dtype=np.uint8)
+    scale = np.ascontiguousarray(scale, dtype=np.float32)
+    E, R, K = w8.shape
+    w = np.empty((E, R, K), np.float64)
+    _check((lib or _lib()).moe_oracle_dequantize_fp8(_p(w8, _u8p), _p(scale, _f32p), E, R, K,
+                                                     _p(w, _f64p)), "dequantize_fp8")
+    return w
+
+
+def glu_w64(x_perm_bits, w_gu, counts, offsets, I: int, lib=None) -> np.ndarray:
+    """glu() with float64 weights [E, 2I, H] (e.g. dequantized FP8)."""
+    x_perm_bits = _u16(x_perm_bits)
+    w_gu = np.ascontiguousarray(w_gu, dtype=np.float64)
+    counts = np.ascontiguousarray(counts, dtype=np.int32)
+    offsets = np.ascontiguousarray(offsets, dtype=np.int32)
+    rows, H = x_perm_bits.shape
+    E = counts.shape[0]
+    assert w_gu.shape == (E, 2 * I, H)
+    h = np.full((rows, I), np.nan)
+    _check((lib or _lib()).moe_oracle_glu_w64(_p(x_perm_bits, _u16p), _p(w_gu, _f64p),
+                                              _p(counts, _i32p), _p(offsets, _i32p), E, H, I,
+                                              _p(h, _f64p)), "glu_w64")
+    return h
+
+
+def down_w64(h: np.ndarray, w_d, counts, offsets, lib=None) -> np.ndarray:
+    """down() with float64 weights [E, H, I] (e.g. dequantized FP8)."""
+    h = np.ascontiguousarray(h, dtype=np.float64)
+    w_d = np.ascontiguousarray(w_d, dtype=np.float64)
+    counts = np.ascontiguousarray(counts, dtype=np.int32)
+    offsets = np.ascontiguousarray(offsets, dtype=np.int32)
+    rows, I = h.shape
+    E, H, I2 = w_d.shape
+    assert I2 == I and counts.shape[0] == E
+    y = np.full((rows, H), np.nan)
+    _check((lib or _lib()).moe_oracle_down_w64(_p(h, _f64p), _p(w_d, _f64p), _p(counts, _i32p),
+                                               _p(offsets, _i32p), E, H, I, _p(y, _f64p)), "down_w64")
+    return y
+
+
 class Oracle:
     """The oracle's functions bound to one built library (the default build, or
     a variant that a test compiled from an edited copy of the source)."""
@@ -230,3 +313,21 @@ class Oracle:
 
     def forward(self, *a, **kw):
         return forward(*a, lib=self.lib, **kw)
+
+    def fp8_encode(self, *a, **kw):
+        return fp8_encode(*a, lib=self.lib, **kw)
+
+    def fp8_decode(self, *a, **kw):
+        return fp8_decode(*a, lib=self.lib, **kw)
+
+    def quantize_fp8(self, *a, **kw):
+        return quantize_fp8(*a, lib=self.lib, **kw)
+
+    def dequantize_fp8(self, *a, **kw):
+        return dequantize_fp8(*a, lib=self.lib, **kw)
+
+    def glu_w64(self, *a, **kw):
+        return glu_w64(*a, lib=self.lib, **kw)
+
+    def down_w64(self, *a, **kw):
+        return down_w64(*a, lib=self.lib, **kw)

@@ -305,5 +305,163 @@ int moe_oracle_forward(const uint16_t *x, const float *logits, const uint16_t *w
     return err ? ORACLE_EINVAL : 0;
 }
 
+/*
+ * FP8 expert weights [Halo, "Performance", Levers that do not help here: lower
+ * precision shrinks expert-weight bytes (fp8: by half) rather than matmul time;
+ * prime-rl, Changes: FP8 expert weights quantized once per optimizer step,
+ * blockwise FP8 grouped GEMMs].
+ *
+ * Format: OCP 8-bit float E4M3 ("E4M3FN"): sign bit, 4 exponent bits with bias
+ * 7, 3 mantissa bits; exponent field 0 holds the subnormals m/8 * 2^-6; the
+ * all-ones code S.1111.111 is NaN and there is no infinity, so the largest
+ * finite magnitude is 1.75 * 2^8 = 448.
+ */
+static double e4m3_value(uint8_t c) {
+    const int e = (c >> 3) & 15, m = c & 7;
+    double v;
+    if (e == 15 && m == 7) return NAN;
+    if (e == 0) v = ldexp((double)m, -9);
+    else v = ldexp((double)(8 + m), e - 10);
+    return (c & 0x80) ? -v : v;
+}
+
+/* round to nearest, ties to even, of a non-negative double holding an integer + fraction */
+static double rne(double q) {
+    double f = floor(q);
+    double d = q - f;
+    if (d > 0.5) return f + 1.0;
+    if (d < 0.5) return f;
+    return fmod(f, 2.0) == 0.0 ? f : f + 1.0;
+}
+
+/* Nearest E4M3 code to v, ties to the even code; |v| must not exceed 448. */
+static int e4m3_encode(float v, uint8_t *out) {
+    if (!isfinite(v) || fabsf(v) > 448.0f) return ORACLE_ERANGE;
+    const uint8_t sign = signbit(v) ? 0x80 : 0;
+    const double a = fabs((double)v);
+    if (a < ldexp(1.0, -6)) {               /* subnormal range: step 2^-9 */
+        const double n = rne(a * 512.0);    /* 0..8; 8 is the smallest normal, code 8 */
+        *out = sign | (uint8_t)n;
+        return 0;
+    }
+    int e;
+    (void)frexp(a, &e);
+    e -= 1;                                 /* a = 1.f * 2^e */
+    double n = rne(ldexp(a, 3 - e));        /* 8 <= n <= 16 */
+    if (n >= 16.0) { n = 8.0; e += 1; }
+    *out = sign | (uint8_t)(((e + 7) << 3) | ((int)n - 8));
+    return 0;
+}
+
+int moe_oracle_fp8_encode(const float *v, int64_t n, uint8_t *out) {
+    if (!v || !out || n < 0) return ORACLE_EINVAL;
+    for (int64_t i = 0; i < n; ++i)
+        if (e4m3_encode(v[i], &out[i]) != 0) return ORACLE_ERANGE;
+    return 0;
+}
+
+int moe_oracle_fp8_decode(const uint8_t *c, int64_t n, double *out) {
+    if (!c || !out || n < 0) return ORACLE_EINVAL;
+    for (int64_t i = 0; i < n; ++i) out[i] = e4m3_value(c[i]);
+    return 0;
+}
+
+/*
+ * Block-scaled quantization of expert weights w [E, R, K] (bf16), one scale per
+ * block of 64 consecutive rows (output channels) over all K:
+ *   scale[e, b] = max |w[e, 64b .. 64b+63, :]| / 448      (fp32 division; 1 if
+ *                 the block is all zero)
+ *   w8[e, r, c] = E4M3 nearest-even of clamp(w[e, r, c] / scale[e, r / 64], +-448)
+ *                 (fp32 division; the clamp only catches a quotient one rounding
+ *                 past 448, which rounds to 448 anyway)
+ * and dequantizes to scale * e4m3_value(w8).
+ */
+int moe_oracle_quantize_fp8(const uint16_t *w, int64_t E, int32_t R, int32_t K, uint8_t *w8,
+                            float *scale) {
+    if (!w || !w8 || !scale || E < 1 || R < 64 || R % 64 != 0 || K < 1) return ORACLE_EINVAL;
+    const int32_t nb = R / 64;
+    for (int64_t e = 0; e < E; ++e) {
+        for (int32_t b = 0; b < nb; ++b) {
+            const int64_t base = (e * R + (int64_t)b * 64) * K;
+            float amax = 0.0f;
+            for (int64_t i = 0; i < (int64_t)64 * K; ++i) {
+                const float a = fabsf((float)bf(w[base + i]));
+                if (a > amax) amax = a;
+            }
+            const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
+            scale[e * nb + b] = s;
+            for (int64_t i = 0; i < (int64_t)64 * K; ++i) {
+                float q = (float)bf(w[base + i]) / s;
+                if (q > 448.0f) q = 448.0f;   /* amax / fl(amax / 448) can land an ulp past 448 */
+                if (q < -448.0f) q = -448.0f;
+                if (e4m3_encode(q, &w8[base + i]) != 0) return ORACLE_ERANGE;
+            }
+        }
+    }
+    return 0;
+}
+
+/* The dequantized weights in double: scale[e, r / 64] * e4m3_value(w8[e, r, c]). */
+int moe_oracle_dequantize_fp8(const uint8_t *w8, const float *scale, int64_t E, int32_t R,
+                              int32_t K, double *w) {
+    if (!w8 || !scale || !w || E < 1 || R < 64 || R % 64 != 0 || K < 1) return ORACLE_EINVAL;
+    const int32_t nb = R / 64;
+    for (int64_t e = 0; e < E; ++e)
+        for (int32_t r = 0; r < R; ++r) {
+            const double s = (double)scale[e * nb + r / 64];
+            const int64_t base = (e * R + r) * (int64_t)K;
+            for (int32_t c = 0; c < K; ++c) w[base + c] = s * e4m3_value(w8[base + c]);
+        }
+    return 0;
+}
+
+/* moe_oracle_glu with weights given in double (dequantized FP8 weights). */
+int moe_oracle_glu_w64(const uint16_t *x_perm, const double *w_gu, const int32_t *counts,
+                       const int32_t *offsets, int32_t E, int32_t H, int32_t I, double *h) {
+    if (!x_perm || !w_gu || !counts || !offsets || !h || E < 1 || H < 1 || I < 1)
+        return ORACLE_EINVAL;
+    for (int32_t e = 0; e < E; ++e) {
+        const double *W = w_gu + (int64_t)e * 2 * I * H;
+        int64_t p0 = offsets[e], n = counts[e];
+#pragma omp parallel for schedule(static)
+        for (int64_t p = p0; p < p0 + n; ++p) {
+            const uint16_t *xr = x_perm + p * H;
+            for (int32_t i = 0; i < I; ++i) {
+                const double *wg = W + (int64_t)i * H;
+                const double *wu = W + (int64_t)(I + i) * H;
+                double g = 0.0, u = 0.0;
+                for (int32_t c = 0; c < H; ++c) {
+                    g += bf(xr[c]) * wg[c];
+                    u += bf(xr[c]) * wu[c];
+                }
+                h[p * I + i] = silu(g) * u;
+            }
+        }
+    }
+    return 0;
+}
+
+/* moe_oracle_down with weights given in double (dequantized FP8 weights). */
+int moe_oracle_down_w64(const double *h, const double *w_d, const int32_t *counts,
+                        const int32_t *offsets, int32_t E, int32_t H, int32_t I, double *y) {
+    if (!h || !w_d || !counts || !offsets || !y || E < 1 || H < 1 || I < 1)
+        return ORACLE_EINVAL;
+    for (int32_t e = 0; e < E; ++e) {
+        const double *W = w_d + (int64_t)e * H * I;
+        int64_t p0 = offsets[e], n = counts[e];
+#pragma omp parallel for schedule(static)
+        for (int64_t p = p0; p < p0 + n; ++p) {
+            const double *hr = h + p * I;
+            for (int32_t c = 0; c < H; ++c) {
+                const double *wr = W + (int64_t)c * I;
+                double s = 0.0;
+                for (int32_t i = 0; i < I; ++i) s += hr[i] * wr[i];
+                y[p * H + c] = s;
+            }
+        }
+    }
+    return 0;
+}
+
 /* Threads the OpenMP loops above use (for reporting the oracle's CPU time). */
 int moe_oracle_num_threads(void) { return omp_get_max_threads(); }

@@ -43,6 +43,26 @@ MUTANTS = {
     "combine_drops_route": ([("for (int32_t j = 0; j < k; ++j)\n                s += topk_w",
                               "for (int32_t j = 1; j < k; ++j)\n                s += topk_w")],
                             [pins.check_identity_experts]),
+    # fp8: ties rounded away from zero instead of to even
+    "fp8_ties_away": ([("return fmod(f, 2.0) == 0.0 ? f : f + 1.0;", "return f + 1.0;")],
+                      [pins.check_fp8_encode]),
+    # fp8: exponent bias off by one in the decoding
+    "fp8_bias_off_by_one": ([("else v = ldexp((double)(8 + m), e - 10);",
+                              "else v = ldexp((double)(8 + m), e - 11);")], [pins.check_fp8_decode]),
+    # fp8: subnormal step taken as 2^-8
+    "fp8_subnormal_step": ([("const double n = rne(a * 512.0);", "const double n = rne(a * 256.0);")],
+                           [pins.check_fp8_encode]),
+    # fp8: block absmax over the first 32 rows of each block only
+    "fp8_short_block_amax": ([("for (int64_t i = 0; i < (int64_t)64 * K; ++i) {\n                const float a",
+                               "for (int64_t i = 0; i < (int64_t)32 * K; ++i) {\n                const float a")],
+                             [pins.check_fp8_quantize]),
+    # fp8: dequantization takes the wrong block's scale
+    "fp8_dequant_wrong_block": ([("const double s = (double)scale[e * nb + r / 64];",
+                                  "const double s = (double)scale[e * nb + r % nb];")],
+                                [pins.check_fp8_quantize]),
+    # fp8 weights: gate rows read from the up half
+    "w64_gate_from_up": ([("const double *wg = W + (int64_t)i * H;", "const double *wg = W + (int64_t)(I + i) * H;")],
+                         [pins.check_glu_down_w64]),
 }
 
 

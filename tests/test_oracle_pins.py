@@ -305,6 +305,116 @@ def check_linearity_and_symmetry(orc):
 
 
 # --------------------------------------------------------------------------------------
+# FP8 expert weights (OCP E4M3, block-scaled)
+# --------------------------------------------------------------------------------------
+
+def _torch_e4m3_codes(v):
+    """PyTorch's own float32 -> float8_e4m3fn cast (round to nearest even), as codes."""
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(v, np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def _torch_e4m3_values(codes):
+    import torch
+    c = torch.from_numpy(np.ascontiguousarray(codes, np.uint8))
+    return c.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def check_fp8_decode(orc):
+    codes = np.arange(256, dtype=np.uint8)
+    v = orc.fp8_decode(codes)
+    # the library's decoding of every code, NaN for S.1111.111 only
+    assert np.array_equal(v, _torch_e4m3_values(codes), equal_nan=True)
+    assert [c for c in range(256) if np.isnan(v[c])] == [0x7F, 0xFF]
+    # landmarks of the format: 1.0, the largest finite, the smallest subnormal and normal
+    assert v[0x38] == 1.0 and v[0x7E] == 448.0 and v[0x01] == 2.0 ** -9 and v[0x08] == 2.0 ** -6
+    # positive codes are strictly increasing; the sign bit mirrors them
+    assert np.all(np.diff(v[:0x7F]) > 0)
+    assert np.array_equal(v[0x80:0xFF], -v[:0x7F])
+
+
+def check_fp8_encode(orc):
+    codes = np.arange(256, dtype=np.uint8)
+    vals = _torch_e4m3_values(codes)
+    finite = codes[~np.isnan(vals)]
+    # every finite value encodes to its own code (the two zeros keep their signs)
+    assert np.array_equal(orc.fp8_encode(vals[finite].astype(np.float32)), finite)
+    # midpoints between neighbours go to the code with an even mantissa
+    pos = vals[:0x7F]
+    mids = ((pos[1:] + pos[:-1]) / 2).astype(np.float32)
+    assert np.array_equal(mids.astype(np.float64), (pos[1:] + pos[:-1]) / 2)  # held exactly
+    enc = orc.fp8_encode(mids)
+    assert np.all(enc % 2 == 0) and np.all((enc == np.arange(126)) | (enc == np.arange(1, 127)))
+    assert np.array_equal(orc.fp8_encode(-mids), enc | 0x80)
+    # nearest code by brute force over all finite codes, on values of every magnitude
+    rng = np.random.default_rng(11)
+    x = (rng.standard_normal(4000) * np.exp2(rng.uniform(-12, 9, 4000))).clip(-448, 448).astype(np.float32)
+    enc = orc.fp8_encode(x)
+    err = np.abs(x.astype(np.float64)[:, None] - vals[finite][None, :])
+    assert np.allclose(np.abs(x - orc.fp8_decode(enc)), err.min(axis=1), rtol=0, atol=0)
+    # and the library cast agrees code for code
+    assert np.array_equal(enc, _torch_e4m3_codes(x))
+    # out of range is refused, not saturated
+    with pytest.raises(oracle.OracleError):
+        orc.fp8_encode(np.array([448.5], np.float32))
+
+
+def check_fp8_quantize(orc):
+    rng = np.random.default_rng(12)
+    E, R, K = 3, 192, 40
+    w = (rng.standard_normal((E, R, K)) * np.exp2(rng.uniform(-6, 2, (E, R // 64, 1, 1)))
+         .repeat(64, axis=1).reshape(E, R, 1)).astype(np.float32)
+    w[1, 64:128] = 0.0                                   # an all-zero block
+    w[2, 0, 0] = -np.abs(w[2, :64]).max() * 2            # a block whose absmax is negative
+    bits = gen.f32_to_bf16_bits(w)
+    wf = f32(bits).astype(np.float32)
+    w8, scale = orc.quantize_fp8(bits)
+    assert w8.shape == (E, R, K) and scale.shape == (E, R // 64)
+    for e in range(E):
+        for b in range(R // 64):
+            blk = wf[e, 64 * b:64 * b + 64]
+            amax = np.abs(blk).max()
+            s = np.float32(amax / np.float32(448.0)) if amax > 0 else np.float32(1.0)
+            assert scale[e, b] == s
+            q = np.clip(blk / s, -448, 448).astype(np.float32)
+            assert np.array_equal(w8[e, 64 * b:64 * b + 64], _torch_e4m3_codes(q))
+            if amax > 0:  # the block's largest magnitude lands on the largest code
+                c = w8[e, 64 * b:64 * b + 64].reshape(-1)[np.argmax(np.abs(blk))]
+                assert c & 0x7F == 0x7E
+            else:
+                assert (w8[e, 64 * b:64 * b + 64] == 0).all()
+    # dequantized weights: within half a unit in the last place of E4M3 (2^-4 relative)
+    # of each normal value, and within half a subnormal step of the small ones
+    wd = orc.dequantize_fp8(w8, scale)
+    sc = np.repeat(scale.astype(np.float64), 64, axis=1)[:, :, None]
+    err = np.abs(wd - wf)
+    assert np.all(err <= np.maximum(np.abs(wf) * 2.0 ** -4, sc * 2.0 ** -10) * (1 + 1e-6))
+    # weights that already are block scale x E4M3 values round-trip exactly
+    codes = rng.integers(0, 0x7F, (2, 128, 16)).astype(np.uint8) | (rng.integers(0, 2, (2, 128, 16)) * 0x80).astype(np.uint8)
+    codes[:, 0, 0] = 0x7E                                 # each block holds the largest code
+    codes[:, 64, 0] = 0xFE
+    vals = _torch_e4m3_values(codes) * np.array([2.0 ** -7, 2.0 ** 3])[:, None, None]
+    w8b, scb = orc.quantize_fp8(gen.f32_to_bf16_bits(vals.astype(np.float32)))
+    assert np.array_equal(orc.dequantize_fp8(w8b, scb), vals)
+
+
+def check_glu_down_w64(orc):
+    """glu_w64 / down_w64 on weights that are exactly the bf16 weights give the
+    bf16 functions' results bit for bit."""
+    cfg = gen.CONFIGS["tiny"]
+    d = gen.make_inputs(cfg)
+    idx, _ = orc.route_topk(d["logits"], cfg.k)
+    counts, offsets, route_row, row_token = orc.layout(idx, cfg.E, 8)
+    xp = orc.gather(d["x"], row_token)
+    h = orc.glu(xp, d["w_gu"], counts, offsets, cfg.I)
+    h64 = orc.glu_w64(xp, f32(d["w_gu"]).astype(np.float64), counts, offsets, cfg.I)
+    assert np.array_equal(h, h64, equal_nan=True)
+    y = orc.down(h, d["w_d"], counts, offsets)
+    y64 = orc.down_w64(h, f32(d["w_d"]).astype(np.float64), counts, offsets)
+    assert np.array_equal(y, y64, equal_nan=True)
+
+
+# --------------------------------------------------------------------------------------
 # tests
 # --------------------------------------------------------------------------------------
 
@@ -362,6 +472,22 @@ def test_identity_experts(orc):
 
 def test_linearity_and_symmetry(orc):
     check_linearity_and_symmetry(orc)
+
+
+def test_fp8_decode(orc):
+    check_fp8_decode(orc)
+
+
+def test_fp8_encode(orc):
+    check_fp8_encode(orc)
+
+
+def test_fp8_quantize(orc):
+    check_fp8_quantize(orc)
+
+
+def test_glu_down_w64(orc):
+    check_glu_down_w64(orc)
 
 
 def test_rejects_bad_inputs(orc):
