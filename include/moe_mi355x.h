@@ -15,18 +15,24 @@
  *   moe_grouped_down_gemm  one grouped GEMM for every expert's down projection
  *   moe_combine            fp32 score-weighted gather-sum back to token order
  *
+ * FP8 expert weights (the same GEMMs reading OCP E4M3 weights, half the bytes):
+ *   moe_quantize_fp8       block-scaled E4M3 codes of bf16 expert weights
+ *   moe_grouped_glu_gemm_fp8w, moe_grouped_glu_gemm_gather_fp8w,
+ *   moe_grouped_down_gemm_fp8w
+ *
  * Sources (page title, section):
  *   [Halo]      Halo, "Performance": Levers that help (grouped GEMM instead of a
  *               per-expert loop; the atomic-free expert permute; fused GLU);
  *               Levers that do not help here (small-M experts are bound by
- *               weight bandwidth)
+ *               weight bandwidth; fp8 halves the expert-weight bytes)
  *   [PocketLLM] "Qwen4-Exp Heterogeneous TP4 Performance": Runtime architecture
  *               (top-10 of 512 routed experts); Confirmed architecture decisions
  *               (only active experts move weight bytes)
  *   [prime-rl]  prime-rl pull request 3885: Changes (single-pass local layout: one
  *               gather into the padded expert-grouped layout and one fp32
  *               score-weighted gather-sum back; 32-bit row offsets must not
- *               overflow silently)
+ *               overflow silently; FP8 expert weights quantized once per
+ *               optimizer step, blockwise FP8 grouped GEMMs)
  *
  * Conventions
  *   - Every tensor pointer is a DEVICE pointer, row-major, 16-byte aligned.
@@ -144,7 +150,8 @@ moe_status moe_permute(const moe_bf16 *x, const int32_t *topk_idx, int64_t T, in
  *   expert_counts, expert_offsets as produced by moe_permute (device)
  *   h               [P_max, I] bf16 out; rows at or past offsets[E] not written
  * An expert with no rows reads none of its weights.
- * Shapes: H % 64 == 0, I % 64 == 0, 1 <= E <= MOE_MAX_E, 0 < P_max < 2^31.
+ * Shapes: H % 64 == 0, I % 64 == 0, 1 <= E <= MOE_MAX_E, 0 < P_max < 2^31, 4*H*I < 2^32
+ * (one expert's weights addressed with 32-bit byte offsets).
  */
 moe_status moe_grouped_glu_gemm(const moe_bf16 *x_perm, const moe_bf16 *w_gate_up,
                                 const int32_t *expert_counts, const int32_t *expert_offsets,
@@ -193,6 +200,59 @@ moe_status moe_grouped_down_gemm(const moe_bf16 *h, const moe_bf16 *w_down,
 moe_status moe_combine(const moe_bf16 *y, const int32_t *route_row, const float *topk_w,
                        int64_t T, int32_t H, int32_t k, int64_t P_max, moe_bf16 *out,
                        moe_stream_t stream);
+
+/*
+ * Block-scaled FP8 expert weights [prime-rl, Changes: FP8 expert weights
+ * quantized once per optimizer step; Halo, Levers that do not help here: fp8
+ * halves the expert-weight bytes].  Format: OCP E4M3 (e4m3fn: bias 7, no
+ * infinity, S.1111.111 is NaN, largest finite 448).  w [E, R, K] is cut into
+ * blocks of 64 consecutive rows of one expert over all of K:
+ *   scale[e, b]  = max|w[e, 64b .. 64b+63, :]| / 448   (fp32; 1.0 if all zero)
+ *   w8[e, r, c]  = E4M3 code nearest to clamp(w[e, r, c] / scale[e, r/64], +-448),
+ *                  ties to the even code (fp32 division)
+ * so w[e, r, c] ~= scale[e, r/64] * value(w8[e, r, c]).
+ *   w      [E, R, K] bf16 (finite values; unchecked)
+ *   w8     [E, R, K] uint8 out;  scale [E, R/64] fp32 out
+ * Quantize w_gate_up as [E, 2I, H] (gate and up rows fall in separate blocks)
+ * and w_down as [E, H, I].
+ * Shapes: R % 64 == 0, K % 64 == 0, 1 <= E, E * R / 64 < 2^31.
+ */
+moe_status moe_quantize_fp8(const moe_bf16 *w, int64_t E, int32_t R, int32_t K, uint8_t *w8,
+                            float *scale, moe_stream_t stream);
+
+/*
+ * moe_grouped_glu_gemm with FP8 weights from moe_quantize_fp8 [prime-rl,
+ * Changes: blockwise FP8 grouped GEMMs].  For every routed row p of expert e:
+ *   g = scale_gu[e, i/64]     * (x_perm[p] . value(w8_gate_up[e, i, :]))
+ *   u = scale_gu[e, (I+i)/64] * (x_perm[p] . value(w8_gate_up[e, I+i, :]))
+ *   h[p, i] = bf16_rne(silu(g) * u)
+ * The codes are widened to bf16 exactly; products and sums in fp32, the scale
+ * applied to the fp32 sum.
+ *   w8_gate_up [E, 2I, H] uint8;  scale_gate_up [E, 2I/64] fp32
+ * Other arguments, outputs and shapes as for moe_grouped_glu_gemm.
+ */
+moe_status moe_grouped_glu_gemm_fp8w(const moe_bf16 *x_perm, const uint8_t *w8_gate_up,
+                                     const float *scale_gate_up, const int32_t *expert_counts,
+                                     const int32_t *expert_offsets, int32_t E, int32_t H, int32_t I,
+                                     int64_t P_max, moe_bf16 *h, moe_stream_t stream);
+
+/* moe_grouped_glu_gemm_gather with FP8 weights (as moe_grouped_glu_gemm_fp8w). */
+moe_status moe_grouped_glu_gemm_gather_fp8w(const moe_bf16 *x, const int32_t *row_token,
+                                            const uint8_t *w8_gate_up, const float *scale_gate_up,
+                                            const int32_t *expert_counts,
+                                            const int32_t *expert_offsets, int64_t T, int32_t E,
+                                            int32_t H, int32_t I, int64_t P_max, moe_bf16 *h,
+                                            moe_stream_t stream);
+
+/*
+ * moe_grouped_down_gemm with FP8 weights:
+ *   y[p, c] = bf16_rne(scale_down[e, c/64] * (h[p] . value(w8_down[e, c, :])))
+ *   w8_down [E, H, I] uint8;  scale_down [E, H/64] fp32
+ */
+moe_status moe_grouped_down_gemm_fp8w(const moe_bf16 *h, const uint8_t *w8_down,
+                                      const float *scale_down, const int32_t *expert_counts,
+                                      const int32_t *expert_offsets, int32_t E, int32_t H, int32_t I,
+                                      int64_t P_max, moe_bf16 *y, moe_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -59,9 +59,17 @@ def load():
     lib.moe_grouped_down_gemm.argtypes = [_c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32,
                                           _c_i64, _c_vp, _c_vp]
     lib.moe_combine.argtypes = [_c_vp, _c_vp, _c_vp, _c_i64, _c_i32, _c_i32, _c_i64, _c_vp, _c_vp]
+    lib.moe_quantize_fp8.argtypes = [_c_vp, _c_i64, _c_i32, _c_i32, _c_vp, _c_vp, _c_vp]
+    lib.moe_grouped_glu_gemm_fp8w.argtypes = [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32,
+                                              _c_i32, _c_i64, _c_vp, _c_vp]
+    lib.moe_grouped_glu_gemm_gather_fp8w.argtypes = [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64,
+                                                     _c_i32, _c_i32, _c_i32, _c_i64, _c_vp, _c_vp]
+    lib.moe_grouped_down_gemm_fp8w.argtypes = [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32,
+                                               _c_i32, _c_i64, _c_vp, _c_vp]
     for fn in ("moe_permute_workspace_size", "moe_route_topk", "moe_permute",
                "moe_grouped_glu_gemm", "moe_grouped_glu_gemm_gather", "moe_grouped_down_gemm",
-               "moe_combine"):
+               "moe_combine", "moe_quantize_fp8", "moe_grouped_glu_gemm_fp8w",
+               "moe_grouped_glu_gemm_gather_fp8w", "moe_grouped_down_gemm_fp8w"):
         getattr(lib, fn).restype = ctypes.c_int
     _LIB = lib
     return lib
@@ -225,13 +233,92 @@ def combine(y, route_row, topk_w, out=None, stream=None):
     return out
 
 
+# ---- FP8 expert weights ----------------------------------------------------------------
+
+@dataclass
+class FP8Weights:
+    """Block-scaled E4M3 expert weights: codes [E, R, K] uint8, one fp32 scale per
+    64 rows, scale [E, R // 64]."""
+    w8: torch.Tensor
+    scale: torch.Tensor
+
+    @property
+    def shape(self):
+        return tuple(self.w8.shape)
+
+
+def quantize_fp8(w: torch.Tensor, out: FP8Weights | None = None, stream=None) -> FP8Weights:
+    """Quantize bf16 expert weights [E, R, K] (w_gate_up as [E, 2I, H], w_down as [E, H, I])."""
+    E, R, K = w.shape
+    if out is None:
+        out = FP8Weights(torch.empty((E, R, K), dtype=torch.uint8, device=w.device),
+                         torch.empty((E, R // 64), dtype=torch.float32, device=w.device))
+    _call("moe_quantize_fp8", _ptr(w, torch.bfloat16, "w"), E, R, K,
+          _ptr(out.w8, torch.uint8, "w8", (E, R, K)),
+          _ptr(out.scale, torch.float32, "scale", (E, R // 64)), _stream(stream))
+    return out
+
+
+def _fp8_args(wq: FP8Weights, name: str):
+    E, R, K = wq.w8.shape
+    return (_ptr(wq.w8, torch.uint8, f"{name}.w8"),
+            _ptr(wq.scale, torch.float32, f"{name}.scale", (E, R // 64)))
+
+
+def grouped_glu_gemm_fp8w(x_perm, w_gate_up: FP8Weights, counts, offsets, h=None, stream=None):
+    P_max, H = x_perm.shape
+    E, two_i, H2 = w_gate_up.shape
+    I = two_i // 2
+    if H2 != H or two_i != 2 * I:
+        raise ValueError("w_gate_up must be [E, 2I, H]")
+    if h is None:
+        h = torch.empty((P_max, I), dtype=torch.bfloat16, device=x_perm.device)
+    _call("moe_grouped_glu_gemm_fp8w", _ptr(x_perm, torch.bfloat16, "x_perm"),
+          *_fp8_args(w_gate_up, "w_gate_up"), _ptr(counts, torch.int32, "counts", (E,)),
+          _ptr(offsets, torch.int32, "offsets", (E + 1,)), E, H, I, P_max,
+          _ptr(h, torch.bfloat16, "h", (P_max, I)), _stream(stream))
+    return h
+
+
+def grouped_glu_gemm_gather_fp8w(x, row_token, w_gate_up: FP8Weights, counts, offsets, h=None,
+                                 stream=None):
+    T, H = x.shape
+    P_max = row_token.shape[0]
+    E, two_i, H2 = w_gate_up.shape
+    I = two_i // 2
+    if H2 != H or two_i != 2 * I:
+        raise ValueError("w_gate_up must be [E, 2I, H]")
+    if h is None:
+        h = torch.empty((P_max, I), dtype=torch.bfloat16, device=x.device)
+    _call("moe_grouped_glu_gemm_gather_fp8w", _ptr(x, torch.bfloat16, "x"),
+          _ptr(row_token, torch.int32, "row_token", (P_max,)), *_fp8_args(w_gate_up, "w_gate_up"),
+          _ptr(counts, torch.int32, "counts", (E,)), _ptr(offsets, torch.int32, "offsets", (E + 1,)),
+          T, E, H, I, P_max, _ptr(h, torch.bfloat16, "h", (P_max, I)), _stream(stream))
+    return h
+
+
+def grouped_down_gemm_fp8w(h, w_down: FP8Weights, counts, offsets, y=None, stream=None):
+    P_max, I = h.shape
+    E, H, I2 = w_down.shape
+    if I2 != I:
+        raise ValueError("w_down must be [E, H, I]")
+    if y is None:
+        y = torch.empty((P_max, H), dtype=torch.bfloat16, device=h.device)
+    _call("moe_grouped_down_gemm_fp8w", _ptr(h, torch.bfloat16, "h"), *_fp8_args(w_down, "w_down"),
+          _ptr(counts, torch.int32, "counts", (E,)), _ptr(offsets, torch.int32, "offsets", (E + 1,)),
+          E, H, I, P_max, _ptr(y, torch.bfloat16, "y", (P_max, H)), _stream(stream))
+    return y
+
+
 # ---- the whole layer -----------------------------------------------------------------
 
 class MoELayer:
     """Preallocated buffers for repeated layer calls of one shape; ``__call__``
     enqueues the five library calls on the current stream and allocates nothing.
     fused_gather=True runs the permute without its gather and the gate/up GEMM
-    reading token rows in place (moe_grouped_glu_gemm_gather); no x_perm exists."""
+    reading token rows in place (moe_grouped_glu_gemm_gather); no x_perm exists.
+    Weights are bf16 tensors or FP8Weights (from quantize_fp8), which select the
+    FP8-weight GEMMs."""
 
     def __init__(self, T: int, H: int, E: int, k: int, I: int, align: int = 32, device="cuda",
                  fused_gather: bool = False):
@@ -253,12 +340,15 @@ class MoELayer:
         permute(x, self.topk_idx, self.E, self.align, self.P_max, out=self.layout,
                 workspace=self.workspace, stream=stream, gather=not self.fused_gather)
         L = self.layout
+        fp8_gu, fp8_d = isinstance(w_gate_up, FP8Weights), isinstance(w_down, FP8Weights)
         if self.fused_gather:
-            grouped_glu_gemm_gather(x, L.row_token, w_gate_up, L.counts, L.offsets, h=self.h,
-                                    stream=stream)
+            glu = grouped_glu_gemm_gather_fp8w if fp8_gu else grouped_glu_gemm_gather
+            glu(x, L.row_token, w_gate_up, L.counts, L.offsets, h=self.h, stream=stream)
         else:
-            grouped_glu_gemm(L.x_perm, w_gate_up, L.counts, L.offsets, h=self.h, stream=stream)
-        grouped_down_gemm(self.h, w_down, L.counts, L.offsets, y=self.y, stream=stream)
+            glu = grouped_glu_gemm_fp8w if fp8_gu else grouped_glu_gemm
+            glu(L.x_perm, w_gate_up, L.counts, L.offsets, h=self.h, stream=stream)
+        down = grouped_down_gemm_fp8w if fp8_d else grouped_down_gemm
+        down(self.h, w_down, L.counts, L.offsets, y=self.y, stream=stream)
         combine(self.y, L.route_row, self.topk_w, out=self.out, stream=stream)
         return self.out
 

@@ -11,12 +11,13 @@ hipError_t launch_route_topk(const float*, int64_t, int, int, int32_t*, float*, 
 hipError_t launch_permute(const uint16_t*, const int32_t*, int64_t, int, int, int, int, int64_t,
                           int32_t*, int32_t*, int32_t*, int32_t*, uint16_t*, void*, hipStream_t);
 size_t permute_workspace_bytes(int64_t R, int E);
-hipError_t launch_grouped_glu_gemm(const uint16_t*, const uint16_t*, const int32_t*, int, int, int,
-                                   uint16_t*, hipStream_t);
-hipError_t launch_grouped_glu_gemm_gather(const uint16_t*, const int32_t*, const uint16_t*,
+hipError_t launch_grouped_glu_gemm(const uint16_t*, const void*, const float*, const int32_t*, int,
+                                   int, int, uint16_t*, hipStream_t);
+hipError_t launch_grouped_glu_gemm_gather(const uint16_t*, const int32_t*, const void*, const float*,
                                           const int32_t*, int, int, int, uint16_t*, hipStream_t);
-hipError_t launch_grouped_down_gemm(const uint16_t*, const uint16_t*, const int32_t*, int, int, int,
-                                    uint16_t*, hipStream_t);
+hipError_t launch_grouped_down_gemm(const uint16_t*, const void*, const float*, const int32_t*, int,
+                                    int, int, uint16_t*, hipStream_t);
+hipError_t launch_quantize_fp8(const uint16_t*, int64_t, int, int, uint8_t*, float*, hipStream_t);
 hipError_t launch_combine(const uint16_t*, const int32_t*, const float*, int64_t, int, int,
                           int64_t, uint16_t*, hipStream_t);
 }  // namespace moe
@@ -172,6 +173,9 @@ static moe_status check_gemm(const void* a, const void* w, const int32_t* counts
     moe_status s;
     if ((s = check_dim64("H", H)) != MOE_OK) return s;
     if ((s = check_dim64("I", I)) != MOE_OK) return s;
+    // the kernels address one expert's weights with 32-bit byte offsets
+    if ((uint64_t)H * (uint64_t)I * 4u >= ((uint64_t)1 << 32))
+        return fail(MOE_ERR_SIZE_OVERFLOW, "one expert's weights (2*I*H bf16, H=%d, I=%d) reach 2^32 bytes", H, I);
     return check_pmax(P_max);
 }
 
@@ -181,9 +185,18 @@ moe_status moe_grouped_glu_gemm(const moe_bf16* x_perm, const moe_bf16* w_gate_u
                                 moe_stream_t stream) {
     moe_status s = check_gemm(x_perm, w_gate_up, expert_counts, expert_offsets, E, H, I, P_max, h);
     if (s != MOE_OK) return s;
-    return hip_status(moe::launch_grouped_glu_gemm(x_perm, w_gate_up, expert_offsets, E, H, I, h,
-                                                   (hipStream_t)stream),
+    return hip_status(moe::launch_grouped_glu_gemm(x_perm, w_gate_up, nullptr, expert_offsets, E, H, I,
+                                                   h, (hipStream_t)stream),
                       "moe_grouped_glu_gemm launch");
+}
+
+static moe_status check_gather(const int32_t* row_token, int64_t T, int32_t H) {
+    REQUIRE_PTR(row_token);
+    if (T < 1) return fail(MOE_ERR_INVALID_SHAPE, "T=%lld < 1", (long long)T);
+    if ((uint64_t)T * (uint64_t)H * 2u >= ((uint64_t)1 << 32))
+        return fail(MOE_ERR_SIZE_OVERFLOW, "T*H*2 = %llu bytes of x reach 2^32 (32-bit offsets)",
+                    (unsigned long long)((uint64_t)T * (uint64_t)H * 2u));
+    return MOE_OK;
 }
 
 moe_status moe_grouped_glu_gemm_gather(const moe_bf16* x, const int32_t* row_token,
@@ -192,13 +205,10 @@ moe_status moe_grouped_glu_gemm_gather(const moe_bf16* x, const int32_t* row_tok
                                        int32_t I, int64_t P_max, moe_bf16* h, moe_stream_t stream) {
     moe_status s = check_gemm(x, w_gate_up, expert_counts, expert_offsets, E, H, I, P_max, h);
     if (s != MOE_OK) return s;
-    REQUIRE_PTR(row_token);
-    if (T < 1) return fail(MOE_ERR_INVALID_SHAPE, "T=%lld < 1", (long long)T);
-    if ((uint64_t)T * (uint64_t)H * 2u >= ((uint64_t)1 << 32))
-        return fail(MOE_ERR_SIZE_OVERFLOW, "T*H*2 = %llu bytes of x reach 2^32 (32-bit offsets)",
-                    (unsigned long long)((uint64_t)T * (uint64_t)H * 2u));
-    return hip_status(moe::launch_grouped_glu_gemm_gather(x, row_token, w_gate_up, expert_offsets, E,
-                                                          H, I, h, (hipStream_t)stream),
+    if ((s = check_gather(row_token, T, H)) != MOE_OK) return s;
+    return hip_status(moe::launch_grouped_glu_gemm_gather(x, row_token, w_gate_up, nullptr,
+                                                          expert_offsets, E, H, I, h,
+                                                          (hipStream_t)stream),
                       "moe_grouped_glu_gemm_gather launch");
 }
 
@@ -208,9 +218,64 @@ moe_status moe_grouped_down_gemm(const moe_bf16* h, const moe_bf16* w_down,
                                  moe_stream_t stream) {
     moe_status s = check_gemm(h, w_down, expert_counts, expert_offsets, E, H, I, P_max, y);
     if (s != MOE_OK) return s;
-    return hip_status(moe::launch_grouped_down_gemm(h, w_down, expert_offsets, E, H, I, y,
+    return hip_status(moe::launch_grouped_down_gemm(h, w_down, nullptr, expert_offsets, E, H, I, y,
                                                     (hipStream_t)stream),
                       "moe_grouped_down_gemm launch");
+}
+
+moe_status moe_quantize_fp8(const moe_bf16* w, int64_t E, int32_t R, int32_t K, uint8_t* w8,
+                            float* scale, moe_stream_t stream) {
+    REQUIRE_PTR(w);
+    REQUIRE_PTR(w8);
+    REQUIRE_PTR(scale);
+    if (E < 1 || E > ((int64_t)1 << 20)) return fail(MOE_ERR_INVALID_SHAPE, "E=%lld outside [1, 2^20]", (long long)E);
+    moe_status s;
+    if ((s = check_dim64("R", R)) != MOE_OK) return s;
+    if ((s = check_dim64("K", K)) != MOE_OK) return s;
+    if (E * (R / 64) >= ((int64_t)1 << 31))
+        return fail(MOE_ERR_SIZE_OVERFLOW, "E*R/64 = %lld blocks reach 2^31", (long long)(E * (R / 64)));
+    return hip_status(moe::launch_quantize_fp8(w, E, R, K, w8, scale, (hipStream_t)stream),
+                      "moe_quantize_fp8 launch");
+}
+
+moe_status moe_grouped_glu_gemm_fp8w(const moe_bf16* x_perm, const uint8_t* w8_gate_up,
+                                     const float* scale_gate_up, const int32_t* expert_counts,
+                                     const int32_t* expert_offsets, int32_t E, int32_t H, int32_t I,
+                                     int64_t P_max, moe_bf16* h, moe_stream_t stream) {
+    moe_status s = check_gemm(x_perm, w8_gate_up, expert_counts, expert_offsets, E, H, I, P_max, h);
+    if (s != MOE_OK) return s;
+    REQUIRE_PTR(scale_gate_up);
+    return hip_status(moe::launch_grouped_glu_gemm(x_perm, w8_gate_up, scale_gate_up, expert_offsets, E,
+                                                   H, I, h, (hipStream_t)stream),
+                      "moe_grouped_glu_gemm_fp8w launch");
+}
+
+moe_status moe_grouped_glu_gemm_gather_fp8w(const moe_bf16* x, const int32_t* row_token,
+                                            const uint8_t* w8_gate_up, const float* scale_gate_up,
+                                            const int32_t* expert_counts,
+                                            const int32_t* expert_offsets, int64_t T, int32_t E,
+                                            int32_t H, int32_t I, int64_t P_max, moe_bf16* h,
+                                            moe_stream_t stream) {
+    moe_status s = check_gemm(x, w8_gate_up, expert_counts, expert_offsets, E, H, I, P_max, h);
+    if (s != MOE_OK) return s;
+    REQUIRE_PTR(scale_gate_up);
+    if ((s = check_gather(row_token, T, H)) != MOE_OK) return s;
+    return hip_status(moe::launch_grouped_glu_gemm_gather(x, row_token, w8_gate_up, scale_gate_up,
+                                                          expert_offsets, E, H, I, h,
+                                                          (hipStream_t)stream),
+                      "moe_grouped_glu_gemm_gather_fp8w launch");
+}
+
+moe_status moe_grouped_down_gemm_fp8w(const moe_bf16* h, const uint8_t* w8_down, const float* scale_down,
+                                      const int32_t* expert_counts, const int32_t* expert_offsets,
+                                      int32_t E, int32_t H, int32_t I, int64_t P_max, moe_bf16* y,
+                                      moe_stream_t stream) {
+    moe_status s = check_gemm(h, w8_down, expert_counts, expert_offsets, E, H, I, P_max, y);
+    if (s != MOE_OK) return s;
+    REQUIRE_PTR(scale_down);
+    return hip_status(moe::launch_grouped_down_gemm(h, w8_down, scale_down, expert_offsets, E, H, I, y,
+                                                    (hipStream_t)stream),
+                      "moe_grouped_down_gemm_fp8w launch");
 }
 
 moe_status moe_combine(const moe_bf16* y, const int32_t* route_row, const float* topk_w, int64_t T,

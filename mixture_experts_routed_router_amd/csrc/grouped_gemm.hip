@@ -32,6 +32,16 @@
 // MFMA operand reads are conflict-free.  The ring runs on from one tile to the
 // next (the next tile's first stages load during the last k steps), and the
 // output is written from registers, 8 bytes per lane, while the next tile runs.
+//
+// FP8-weight variant (W8): W holds OCP E4M3 codes with one fp32 scale per 64
+// consecutive W rows of an expert [Halo "Performance", Levers that do not help
+// here: the bytes of fine-grained experts' weights are what bounds them, and
+// fp8 halves them; prime-rl, Changes: blockwise FP8 expert weights]. A B stage
+// is then 32 bytes per W row (half the bytes), each lane reads its 16 codes
+// from LDS with one 16-byte read and widens them to bf16 exactly
+// (v_cvt_scalef32_pk_bf16_fp8 with scale 1), and the MFMAs run on bf16 as
+// before. The block scale is constant along k, so it multiplies the fp32
+// accumulator once in the epilogue.
 #include "common.hpp"
 
 namespace moe {
@@ -70,6 +80,9 @@ static_assert(BM == BN, "A and B stages share one load layout");
 // instructions; a wait may leave those and 3 stages of loads in flight.
 constexpr int kMaxStoresPerTile = 4 * NBN * 4;
 static_assert(3 * kLoadsPerStage + kMaxStoresPerTile < 64, "vmcnt is 6 bits");
+// FP8 weights: a B stage is BN rows x BK bytes (8 KB), one 16-byte piece per thread.
+constexpr int kLoadsPerStageW8 = kPiecesPerThread + 1;
+static_assert(BN * BK == 16 * kGemmThreads, "one fp8 B piece per thread and stage");
 
 // Rows of a stage are BK bf16 = PR pieces of 16 bytes. Piece p of row r is stored
 // at piece p ^ swz(r). For the same logical piece of any 8 consecutive rows (a
@@ -80,6 +93,12 @@ __device__ __forceinline__ int swz(int row) {
     return (row ^ (row >> 3)) & 7;  // PR == 8
 }
 static_assert(PR == 4 || PR == 8, "BK must be 32 or 64");
+
+// FP8 B stage: a row is BK = 32 bytes, two 16-byte pieces; piece p of row r is
+// stored at p ^ swz8(r). A wave's operand read covers 16 consecutive rows with
+// one piece each; flipping the piece every 8 rows puts the two halves of those
+// 512 bytes on disjoint banks.
+__device__ __forceinline__ int swz8(int row) { return (row >> 3) & 1; }
 
 // Exclusive scan of one int per thread over the workgroup.
 __device__ __forceinline__ int block_exclusive_scan(int v, int* tmp /* >= kWaves ints */) {
@@ -204,7 +223,8 @@ __device__ __forceinline__ void quad_transpose_bf16(float v0, float v1, float v2
 // Everything one tile needs.
 struct TileArgs {
     const uint16_t* a_tile;   // A + row0 * K (gathering A: the token matrix x itself)
-    const uint16_t* w_exp;    // W + e * (W rows per expert) * K
+    const char* w_exp;        // W + e * (W rows per expert) * K elements (as bytes)
+    const float* w_scale;     // FP8 weights: the expert's scales, one per 64 W rows
     uint16_t* c_tile;         // C + row0 * N
     int row0, nt, rows_valid;
     int nvb;                  // this wave's 32-row blocks that hold segment rows (0..4)
@@ -224,7 +244,7 @@ struct StageOffsets {
 // row_token[p] -- the permute's gather folded into the loads. `tok` holds this
 // thread's token of each of its rows (issue_token_loads); a pad row (-1) reads
 // token 0 instead, its results are never read.
-template <bool GLU, bool GATHER>
+template <bool GLU, bool GATHER, bool W8>
 __device__ __forceinline__ StageOffsets stage_offsets(const TileArgs& ta, int K, int N, int wave, int lane,
                                                       const uint32_t (&tok)[kPiecesPerThread]) {
     StageOffsets o;
@@ -246,7 +266,24 @@ __device__ __forceinline__ StageOffsets stage_offsets(const TileArgs& ta, int K,
             const int c = ta.nt * BN + r;
             wr = c < N ? c : N - 1;
         }
-        o.b[i] = (uint32_t)(((int64_t)wr * K + piece * 8) * 2);
+        if (!W8) o.b[i] = (uint32_t)(((int64_t)wr * K + piece * 8) * 2);
+    }
+    if (W8) {
+        // FP8 B: wave w fills W rows 32w .. 32w+31 of the stage, lane l row
+        // 32w + l/2, physical piece l%2 (logical (l%2) ^ swz8(row)). Byte offsets
+        // inside one expert's weights fit 32 bits (checked on the host).
+        const int r = 32 * wave + lane / 2;
+        const int piece = (lane & 1) ^ swz8(r);
+        int wr;
+        if (GLU) {
+            const int c = ta.nt * 128 + (r & 127);
+            const int cc = c < N ? c : N - 1;
+            wr = r < 128 ? cc : N + cc;
+        } else {
+            const int c = ta.nt * BN + r;
+            wr = c < N ? c : N - 1;
+        }
+        o.b[0] = (uint32_t)wr * (uint32_t)K + (uint32_t)(piece * 16);
     }
     return o;
 }
@@ -277,15 +314,26 @@ __device__ __forceinline__ void read_tokens(const int32_t* region, int lane,
 }
 
 // This thread's share of one stage: A and B pieces of k-stage kt of a tile into ring slot `slot`.
+template <bool W8>
 __device__ __forceinline__ void issue_stage(uint32_t lds0, int slot, int wave, const uint16_t* ga,
-                                            const uint16_t* gb, const StageOffsets& o) {
+                                            const char* gb, const StageOffsets& o) {
     const uint32_t sa = lds0 + (uint32_t)(slot * kStageElems * 2);
     const uint32_t sb = sa + kAElems * 2;
 #pragma unroll
     for (int i = 0; i < kPiecesPerThread; ++i) {
         dma16(sa + (kPiecesPerThread * wave + i) * 1024, ga, o.a[i]);
-        dma16(sb + (kPiecesPerThread * wave + i) * 1024, gb, o.b[i]);
+        if (!W8) dma16(sb + (kPiecesPerThread * wave + i) * 1024, gb, o.b[i]);
     }
+    if (W8) dma16(sb + wave * 1024, gb, o.b[0]);
+}
+
+// 8 E4M3 codes (two dwords, k order) -> 8 bf16, exactly (every E4M3 value is a bf16 value).
+__device__ __forceinline__ bf16x8_t fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
+    const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false);
+    const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true);
+    const bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false);
+    const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true);
+    return bf16x8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
 // Wave-constant values of the whole launch.
@@ -295,6 +343,7 @@ struct WaveCtx {
     int K, N, nk;
     int wave, lane, wm, wn, grp;
     int rd_off[KSTEPS];
+    int rd8_off;         // FP8 B: byte offset of this lane's 16 codes within a 32-row block
     int32_t* tok_lds;    // gathering A: [2][kWaves][kTokSlots] token buffers
 };
 
@@ -313,7 +362,7 @@ struct WaveCtx {
 // an 8-byte store. This wave's stores of the previous tile (s_prev of them) were
 // issued after the prefetched stages; vector-memory operations complete in issue
 // order, so a wait for a prefetched stage may leave those stores in flight.
-template <bool GLU, bool GATHER, int NV>
+template <bool GLU, bool GATHER, bool W8, int NV>
 __device__ __forceinline__ int run_tile(const WaveCtx& w, const TileArgs& ta, const TileArgs& tn,
                                         int base, bool prefetched, bool pf_next, int s_prev,
                                         const int32_t* __restrict__ row_token, int tb) {
@@ -339,7 +388,9 @@ __device__ __forceinline__ int run_tile(const WaveCtx& w, const TileArgs& ta, co
         }
         read_tokens(tok_cur, lane, tok);
     }
-    const StageOffsets oc = stage_offsets<GLU, GATHER>(ta, K, N, wave, lane, tok);
+    const StageOffsets oc = stage_offsets<GLU, GATHER, W8>(ta, K, N, wave, lane, tok);
+    constexpr int LPS = W8 ? kLoadsPerStageW8 : kLoadsPerStage;  // this thread's loads per stage
+    constexpr int WB = W8 ? 1 : 2;                                // bytes per weight
 
     // LDS B row of each of this wave's 32-column blocks. GLU: the first half of
     // the blocks are gate columns, the second half the matching up columns.
@@ -378,10 +429,11 @@ __device__ __forceinline__ int run_tile(const WaveCtx& w, const TileArgs& ta, co
         const int s_ = (s);                                                                       \
         const int slot_ = (base + s_) & (STAGES - 1);                                             \
         if (s_ < nk)                                                                              \
-            issue_stage(w.lds0, slot_, wave, ta.a_tile + s_ * BK, ta.w_exp + s_ * BK, oc);        \
+            issue_stage<W8>(w.lds0, slot_, wave, ta.a_tile + s_ * BK, ta.w_exp + s_ * BK * WB, oc); \
         else if (pf_next) {                                                                       \
-            const StageOffsets on_ = stage_offsets<GLU, GATHER>(tn, K, N, wave, lane, tkn);        \
-            issue_stage(w.lds0, slot_, wave, tn.a_tile + (s_ - nk) * BK, tn.w_exp + (s_ - nk) * BK, on_); \
+            const StageOffsets on_ = stage_offsets<GLU, GATHER, W8>(tn, K, N, wave, lane, tkn);    \
+            issue_stage<W8>(w.lds0, slot_, wave, tn.a_tile + (s_ - nk) * BK,                      \
+                            tn.w_exp + (s_ - nk) * BK * WB, on_);                                 \
         }                                                                                         \
     } while (0)
 #define MOE_LOAD_STAGE_FRAGS(stage)                                                           \
@@ -391,8 +443,20 @@ __device__ __forceinline__ int run_tile(const WaveCtx& w, const TileArgs& ta, co
         _Pragma("unroll") for (int ks = 0; ks < 2; ++ks) {                                    \
             _Pragma("unroll") for (int i = 0; i < NV; ++i)                                    \
                 fa[ks][i] = *(const bf16x8_t*)(sa_ + ((2 * i + wm) * 32) * BK + w.rd_off[ks]); \
+            if (!W8) {                                                                        \
+                _Pragma("unroll") for (int j = 0; j < NBN; ++j)                               \
+                    fb[ks][j] = *(const bf16x8_t*)(sb_ + brow[j] * BK + w.rd_off[ks]);         \
+            }                                                                                 \
+        }                                                                                     \
+        if (W8) {                                                                             \
+            const char* s8_ = (const char*)sb_;                                               \
+            u32x4_t raw_[NBN];                                                                \
             _Pragma("unroll") for (int j = 0; j < NBN; ++j)                                   \
-                fb[ks][j] = *(const bf16x8_t*)(sb_ + brow[j] * BK + w.rd_off[ks]);             \
+                raw_[j] = *(const u32x4_t*)(s8_ + brow[j] * BK + w.rd8_off);                  \
+            _Pragma("unroll") for (int j = 0; j < NBN; ++j) {                                 \
+                fb[0][j] = fp8x8_to_bf16(raw_[j][0], raw_[j][1]);                             \
+                fb[1][j] = fp8x8_to_bf16(raw_[j][2], raw_[j][3]);                             \
+            }                                                                                 \
         }                                                                                     \
     } while (0)
 #define MOE_MMA_STAGE()                                                                       \
@@ -409,7 +473,7 @@ __device__ __forceinline__ int run_tile(const WaveCtx& w, const TileArgs& ta, co
 #define MOE_WAIT_TOKENS(kt, FIRST_, PRO_)                                                     \
     do {                                                                                      \
         if (GATHER && pf_next && (kt) == (FIRST_)) {                                          \
-            const int younger_ = ((prefetched ? 0 : (PRO_)) + (kt)) * kLoadsPerStage;          \
+            const int younger_ = ((prefetched ? 0 : (PRO_)) + (kt)) * LPS;                     \
             wait_vmcnt_dyn(younger_ < 60 ? younger_ : 60);                                    \
             read_tokens(tok_nxt, lane, tkn);                                                  \
         }                                                                                     \
@@ -422,9 +486,9 @@ __device__ __forceinline__ int run_tile(const WaveCtx& w, const TileArgs& ta, co
         const int s2_ = (kt) + 2;                                                             \
         const int later_ = (s2_ < nk || pf_next ? 1 : 0) + (s2_ + 1 < nk || pf_next ? 1 : 0);  \
         if (prefetched && (kt) + 1 <= (P))                                                    \
-            wait_vmcnt_dyn(later_ * kLoadsPerStage + s_prev + n_tok);                         \
-        else if (later_ >= 2) wait_vmcnt<2 * kLoadsPerStage>();                               \
-        else if (later_ == 1) wait_vmcnt<kLoadsPerStage>();                                   \
+            wait_vmcnt_dyn(later_ * LPS + s_prev + n_tok);                                    \
+        else if (later_ >= 2) wait_vmcnt<2 * LPS>();                                          \
+        else if (later_ == 1) wait_vmcnt<LPS>();                                              \
         else wait_vmcnt<0>();                                                                 \
     } while (0)
 
@@ -438,9 +502,9 @@ __device__ __forceinline__ int run_tile(const WaveCtx& w, const TileArgs& ta, co
             if (s < nk) MOE_ISSUE(s);
         if (grp == 0 && STAGES - 1 < nk) MOE_ISSUE(STAGES - 1);
         const int issued = min(nk, grp == 0 ? STAGES : STAGES - 1);
-        if (issued >= 4) wait_vmcnt<3 * kLoadsPerStage>();
-        else if (issued == 3) wait_vmcnt<2 * kLoadsPerStage>();
-        else if (issued == 2) wait_vmcnt<kLoadsPerStage>();
+        if (issued >= 4) wait_vmcnt<3 * LPS>();
+        else if (issued == 3) wait_vmcnt<2 * LPS>();
+        else if (issued == 2) wait_vmcnt<LPS>();
         else wait_vmcnt<0>();
         lds_barrier();
         if (grp == 0) MOE_LOAD_STAGE_FRAGS(0);
@@ -503,6 +567,7 @@ __device__ __forceinline__ int run_tile(const WaveCtx& w, const TileArgs& ta, co
         int rows_valid = ta.rows_valid, n_cols = N, nt = ta.nt, zero = 0;
         int ln = lane;
         asm volatile("" : "+s"(rows_valid), "+s"(n_cols), "+s"(nt), "+s"(zero), "+v"(ln));
+        const float* w_scale = ta.w_scale + zero;
         uint16_t* c_tile = ta.c_tile + zero;
         const QuadSel qs = quad_sel(ln);
         const int out_row = (ln >> 5) * 4 + (ln & 3);  // this lane's row in an 8-row group
@@ -516,6 +581,13 @@ __device__ __forceinline__ int run_tile(const WaveCtx& w, const TileArgs& ta, co
             for (int jb = 0; jb < OB; ++jb) {
                 const int cb = col0 + jb * 32;
                 if (cb >= n_cols) continue;
+                // FP8 weights: a 32-column block lies inside one 64-row scale block
+                // (gate rows cb.., up rows n_cols + cb..), so its scales are wave-uniform
+                float sg = 1.0f, su = 1.0f;
+                if (W8) {
+                    sg = w_scale[cb >> 6];
+                    if (GLU) su = w_scale[(n_cols + cb) >> 6];
+                }
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const int r0 = (2 * i + wm) * 32 + q * 8;
@@ -524,10 +596,14 @@ __device__ __forceinline__ int run_tile(const WaveCtx& w, const TileArgs& ta, co
 #pragma unroll
                     for (int m = 0; m < 4; ++m) {
                         if (GLU) {
-                            const float g = acc[i][jb][4 * q + m], u = acc[i][jb + NBN / 2][4 * q + m];
+                            float g = acc[i][jb][4 * q + m], u = acc[i][jb + NBN / 2][4 * q + m];
+                            if (W8) {
+                                g *= sg;
+                                u *= su;
+                            }
                             v[m] = g / (1.0f + __expf(-g)) * u;
                         } else {
-                            v[m] = acc[i][jb][4 * q + m];
+                            v[m] = W8 ? acc[i][jb][4 * q + m] * sg : acc[i][jb][4 * q + m];
                         }
                     }
                     uint32_t w0, w1;
@@ -543,11 +619,11 @@ __device__ __forceinline__ int run_tile(const WaveCtx& w, const TileArgs& ta, co
     return stores;
 }
 
-template <bool GLU, bool GATHER>
+template <bool GLU, bool GATHER, bool W8>
 __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ row_token,
-    const uint16_t* __restrict__ W, const int32_t* __restrict__ offsets, int E, int K, int N,
-    uint16_t* __restrict__ C) {
+    const void* __restrict__ W, const float* __restrict__ w_scale, const int32_t* __restrict__ offsets,
+    int E, int K, int N, uint16_t* __restrict__ C) {
     __shared__ __attribute__((aligned(1024))) uint16_t lds[kLdsElems];
     __shared__ int32_t tile_start[kMaxE + 1];
     __shared__ int32_t seg_start[kMaxE + 1];
@@ -558,7 +634,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_kernel(
     // column tiles per expert: GLU tiles cover 128 output columns (128 gate + 128 up rows)
     const int NT = GLU ? (N + 127) / 128 : (N + BN - 1) / BN;
     const int NW = GLU ? 2 * N : N;  // W rows per expert
-    const int64_t w_stride = (int64_t)NW * K;
+    const int64_t w_stride = (int64_t)NW * K * (W8 ? 1 : 2);  // bytes per expert
 
     // ---- per-expert tile counts -> prefix (every workgroup builds its own copy)
     {
@@ -602,9 +678,16 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_kernel(
     // (2*ks + lane/32) of row (lane % 32) of each 32-row block
     {
         const int lrow = w.lane & 31;
+        // The k order inside a stage only has to match between A and B. bf16 B:
+        // k-step ks, lane half h reads k = 16ks + 8h + 0..7 (logical piece 2ks + h).
+        // FP8 B: lane half h reads the 16 codes k = 16h .. 16h+15 at once, so
+        // k-step ks takes k = 16h + 8ks + 0..7 of both operands (piece 2h + ks).
 #pragma unroll
-        for (int ks = 0; ks < KSTEPS; ++ks)
-            w.rd_off[ks] = lrow * BK + (((2 * ks + (w.lane >> 5)) ^ swz(lrow)) << 3);
+        for (int ks = 0; ks < KSTEPS; ++ks) {
+            const int piece = W8 ? 2 * (w.lane >> 5) + ks : 2 * ks + (w.lane >> 5);
+            w.rd_off[ks] = lrow * BK + ((piece ^ swz(lrow)) << 3);
+        }
+        w.rd8_off = lrow * BK + (((w.lane >> 5) ^ swz8(lrow)) << 4);
     }
 
     // ---- XCD-aware split: XCD x takes the contiguous run [x*chunk, (x+1)*chunk)
@@ -631,7 +714,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_kernel(
         TileArgs ta;
         ta.a_tile = GATHER ? A : A + (int64_t)row0 * K;
         ta.row0 = row0;
-        ta.w_exp = W + (int64_t)e * w_stride;
+        ta.w_exp = (const char*)W + (int64_t)e * w_stride;
+        ta.w_scale = W8 ? w_scale + (int64_t)e * (NW / 64) : w_scale;
         ta.c_tile = C + (int64_t)row0 * N;
         ta.nt = nt;
         ta.rows_valid = min(BM, seg1 - row0);
@@ -656,11 +740,11 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_kernel(
         const bool pf_next = has_next && cross;
         int s;
         switch (cur.nvb) {
-            case 4: s = run_tile<GLU, GATHER, 4>(w, cur, nxt, base, prefetched, pf_next, s_prev, row_token, tb); break;
-            case 3: s = run_tile<GLU, GATHER, 3>(w, cur, nxt, base, prefetched, pf_next, s_prev, row_token, tb); break;
-            case 2: s = run_tile<GLU, GATHER, 2>(w, cur, nxt, base, prefetched, pf_next, s_prev, row_token, tb); break;
-            case 1: s = run_tile<GLU, GATHER, 1>(w, cur, nxt, base, prefetched, pf_next, s_prev, row_token, tb); break;
-            default: s = run_tile<GLU, GATHER, 0>(w, cur, nxt, base, prefetched, pf_next, s_prev, row_token, tb); break;
+            case 4: s = run_tile<GLU, GATHER, W8, 4>(w, cur, nxt, base, prefetched, pf_next, s_prev, row_token, tb); break;
+            case 3: s = run_tile<GLU, GATHER, W8, 3>(w, cur, nxt, base, prefetched, pf_next, s_prev, row_token, tb); break;
+            case 2: s = run_tile<GLU, GATHER, W8, 2>(w, cur, nxt, base, prefetched, pf_next, s_prev, row_token, tb); break;
+            case 1: s = run_tile<GLU, GATHER, W8, 1>(w, cur, nxt, base, prefetched, pf_next, s_prev, row_token, tb); break;
+            default: s = run_tile<GLU, GATHER, W8, 0>(w, cur, nxt, base, prefetched, pf_next, s_prev, row_token, tb); break;
         }
         if (!has_next) break;
         s_prev = s;
@@ -692,26 +776,44 @@ static unsigned persistent_grid() {
     return (unsigned)((n + 7) / 8 * 8);
 }
 
-hipError_t launch_grouped_glu_gemm(const uint16_t* x_perm, const uint16_t* w_gu,
+// scale == NULL: bf16 weights; otherwise FP8 (E4M3) weights with one scale per 64 W rows.
+hipError_t launch_grouped_glu_gemm(const uint16_t* x_perm, const void* w_gu, const float* scale,
                                    const int32_t* offsets, int E, int H, int I, uint16_t* h,
                                    hipStream_t stream) {
-    hipLaunchKernelGGL((grouped_gemm_kernel<true, false>), dim3(persistent_grid()), dim3(kGemmThreads),
-                       0, stream, x_perm, (const int32_t*)nullptr, w_gu, offsets, E, H, I, h);
+    if (scale)
+        hipLaunchKernelGGL((grouped_gemm_kernel<true, false, true>), dim3(persistent_grid()),
+                           dim3(kGemmThreads), 0, stream, x_perm, (const int32_t*)nullptr, w_gu, scale,
+                           offsets, E, H, I, h);
+    else
+        hipLaunchKernelGGL((grouped_gemm_kernel<true, false, false>), dim3(persistent_grid()),
+                           dim3(kGemmThreads), 0, stream, x_perm, (const int32_t*)nullptr, w_gu, scale,
+                           offsets, E, H, I, h);
     return hipGetLastError();
 }
 
-hipError_t launch_grouped_glu_gemm_gather(const uint16_t* x, const int32_t* row_token,
-                                          const uint16_t* w_gu, const int32_t* offsets, int E, int H,
+hipError_t launch_grouped_glu_gemm_gather(const uint16_t* x, const int32_t* row_token, const void* w_gu,
+                                          const float* scale, const int32_t* offsets, int E, int H,
                                           int I, uint16_t* h, hipStream_t stream) {
-    hipLaunchKernelGGL((grouped_gemm_kernel<true, true>), dim3(persistent_grid()), dim3(kGemmThreads),
-                       0, stream, x, row_token, w_gu, offsets, E, H, I, h);
+    if (scale)
+        hipLaunchKernelGGL((grouped_gemm_kernel<true, true, true>), dim3(persistent_grid()),
+                           dim3(kGemmThreads), 0, stream, x, row_token, w_gu, scale, offsets, E, H, I, h);
+    else
+        hipLaunchKernelGGL((grouped_gemm_kernel<true, true, false>), dim3(persistent_grid()),
+                           dim3(kGemmThreads), 0, stream, x, row_token, w_gu, scale, offsets, E, H, I, h);
     return hipGetLastError();
 }
 
-hipError_t launch_grouped_down_gemm(const uint16_t* h, const uint16_t* w_d, const int32_t* offsets,
-                                    int E, int H, int I, uint16_t* y, hipStream_t stream) {
-    hipLaunchKernelGGL((grouped_gemm_kernel<false, false>), dim3(persistent_grid()), dim3(kGemmThreads),
-                       0, stream, h, (const int32_t*)nullptr, w_d, offsets, E, I, H, y);
+hipError_t launch_grouped_down_gemm(const uint16_t* h, const void* w_d, const float* scale,
+                                    const int32_t* offsets, int E, int H, int I, uint16_t* y,
+                                    hipStream_t stream) {
+    if (scale)
+        hipLaunchKernelGGL((grouped_gemm_kernel<false, false, true>), dim3(persistent_grid()),
+                           dim3(kGemmThreads), 0, stream, h, (const int32_t*)nullptr, w_d, scale,
+                           offsets, E, I, H, y);
+    else
+        hipLaunchKernelGGL((grouped_gemm_kernel<false, false, false>), dim3(persistent_grid()),
+                           dim3(kGemmThreads), 0, stream, h, (const int32_t*)nullptr, w_d, scale,
+                           offsets, E, I, H, y);
     return hipGetLastError();
 }
 

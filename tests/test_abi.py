@@ -40,6 +40,11 @@ def lib():
     lib.moe_grouped_down_gemm.argtypes = [vp, vp, vp, vp, i32, i32, i32, i64, vp, vp]
     lib.moe_grouped_glu_gemm_gather.argtypes = [vp, vp, vp, vp, vp, i64, i32, i32, i32, i64, vp, vp]
     lib.moe_combine.argtypes = [vp, vp, vp, i64, i32, i32, i64, vp, vp]
+    lib.moe_quantize_fp8.argtypes = [vp, i64, i32, i32, vp, vp, vp]
+    lib.moe_grouped_glu_gemm_fp8w.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i64, vp, vp]
+    lib.moe_grouped_down_gemm_fp8w.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i64, vp, vp]
+    lib.moe_grouped_glu_gemm_gather_fp8w.argtypes = [vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i64,
+                                                     vp, vp]
     return lib
 
 
@@ -128,6 +133,38 @@ def test_gemm_gather_validation(lib):
     # T * H * 2 bytes of x must stay below 2^32 (32-bit offsets)
     assert fn(FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, 8, 2048, 256, 1000, FAKE, None) == OVERFLOW
     assert fn(FAKE + 8, FAKE, FAKE, FAKE, FAKE, 100, 8, 128, 256, 1000, FAKE, None) == MISALIGNED
+
+
+def test_gemm_weight_size_limit(lib):
+    """One expert's weights are addressed with 32-bit byte offsets: 4*H*I < 2^32."""
+    for fn in (lib.moe_grouped_glu_gemm, lib.moe_grouped_down_gemm):
+        assert fn(FAKE, FAKE, FAKE, FAKE, 8, 32768, 32768, 1000, FAKE, None) == OVERFLOW
+        assert b"2^32" in lib.moe_last_error_message()
+
+
+def test_quantize_fp8_validation(lib):
+    fn = lib.moe_quantize_fp8
+    assert fn(None, 4, 128, 256, FAKE, FAKE, None) == NULLP
+    assert fn(FAKE, 4, 128, 256, FAKE, None, None) == NULLP
+    assert b"scale" in lib.moe_last_error_message()
+    assert fn(FAKE, 4, 96, 256, FAKE, FAKE, None) == SHAPE      # R % 64
+    assert fn(FAKE, 4, 128, 200, FAKE, FAKE, None) == SHAPE     # K % 64
+    assert fn(FAKE, 0, 128, 256, FAKE, FAKE, None) == SHAPE
+    assert fn(FAKE, 4, 128, 256, FAKE + 4, FAKE, None) == MISALIGNED
+
+
+def test_fp8_gemm_validation(lib):
+    for fn in (lib.moe_grouped_glu_gemm_fp8w, lib.moe_grouped_down_gemm_fp8w):
+        assert fn(FAKE, FAKE, None, FAKE, FAKE, 8, 128, 256, 1000, FAKE, None) == NULLP   # scale
+        assert fn(FAKE, FAKE, FAKE, FAKE, FAKE, 8, 128, 256, 1000, None, None) == NULLP
+        assert fn(FAKE, FAKE, FAKE, FAKE, FAKE, 8, 100, 256, 1000, FAKE, None) == SHAPE
+        assert fn(FAKE, FAKE, FAKE, FAKE, FAKE, 8, 128, 200, 1000, FAKE, None) == SHAPE
+        assert fn(FAKE, FAKE, FAKE + 4, FAKE, FAKE, 8, 128, 256, 1000, FAKE, None) == MISALIGNED
+    fn = lib.moe_grouped_glu_gemm_gather_fp8w
+    assert fn(FAKE, None, FAKE, FAKE, FAKE, FAKE, 100, 8, 128, 256, 1000, FAKE, None) == NULLP
+    assert fn(FAKE, FAKE, FAKE, None, FAKE, FAKE, 100, 8, 128, 256, 1000, FAKE, None) == NULLP
+    assert fn(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 8, 128, 256, 1000, FAKE, None) == SHAPE
+    assert fn(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, 8, 2048, 256, 1000, FAKE, None) == OVERFLOW
 
 
 def test_combine_validation(lib):

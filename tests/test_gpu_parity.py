@@ -236,6 +236,128 @@ def test_grouped_down_gemm(gpu_lib, case):
 
 
 # --------------------------------------------------------------------------------------
+# FP8 expert weights
+# --------------------------------------------------------------------------------------
+
+def _dev_fp8(gpu_lib, w8, scale):
+    return gpu_lib.FP8Weights(dev(w8), dev(scale))
+
+
+QUANT_CASES = [
+    # name, E, R, K, per-block std spread (log2), seed
+    ("small", 2, 128, 64, 6, 1),
+    ("gate_up_H512_I256", 5, 512, 512, 10, 2),
+    ("down_H320_I128", 3, 320, 128, 4, 3),
+    ("E1_R64_K2880", 1, 64, 2880, 8, 4),
+]
+
+
+def _quant_weights(E, R, K, spread, seed):
+    """bf16 weights whose 64-row blocks differ in scale by up to 2^spread, with an
+    all-zero block, a block whose absmax is negative, exact zeros of both signs
+    and values far below the block's E4M3 subnormal range."""
+    rng = np.random.default_rng(seed)
+    w = rng.standard_normal((E, R, K)) * 0.02
+    w *= np.exp2(rng.uniform(-spread, 0, (E, R // 64, 1, 1))).repeat(64, axis=1).reshape(E, R, 1)
+    w = w.astype(np.float32)
+    if R >= 128:
+        w[0, 64:128] = 0.0
+    w[-1, 0, 0] = -2 * np.abs(w[-1, :64]).max()
+    w[0, 0, 1], w[0, 0, 2] = 0.0, -0.0
+    w[0, 0, 3] = np.abs(w[0, :64]).max() * 2.0 ** -14
+    return gen.f32_to_bf16_bits(w)
+
+
+@pytest.mark.parametrize("case", QUANT_CASES, ids=[c[0] for c in QUANT_CASES])
+def test_quantize_fp8(gpu_lib, case):
+    """Codes and scales bit for bit equal to the oracle's quantizer."""
+    name, E, R, K, spread, seed = case
+    _say(f"quantize fp8 case {name}")
+    w = _quant_weights(E, R, K, spread, seed)
+    q = gpu_lib.quantize_fp8(dev_bf16(w))
+    torch.cuda.synchronize()
+    w8_ref, s_ref = oracle.quantize_fp8(w)
+    assert (q.scale.cpu().numpy().view(np.uint32) == s_ref.view(np.uint32)).all()
+    w8 = q.w8.cpu().numpy()
+    bad = np.argwhere(w8 != w8_ref)
+    assert len(bad) == 0, f"{len(bad)} codes differ, first at {bad[:4].tolist()}"
+
+
+def test_quantize_fp8_full_size_sampled(gpu_lib):
+    """The 128-expert gate/up weights of the 30B-A3B shape [128, 1536, 2048]:
+    every scale, and the codes of three whole experts, against the oracle."""
+    cfg = gen.CONFIGS["qwen3_30b_a3b"]
+    _say("quantize fp8 full size: generating weights")
+    w = gen.random_bf16((cfg.E, 2 * cfg.I, cfg.H), seed=cfg.seed, std=0.02)
+    q = gpu_lib.quantize_fp8(dev_bf16(w))
+    torch.cuda.synchronize()
+    scale = q.scale.cpu().numpy()
+    for e in (0, 77, cfg.E - 1):
+        w8_ref, s_ref = oracle.quantize_fp8(w[e:e + 1])
+        assert (q.w8[e].cpu().numpy() == w8_ref[0]).all(), e
+        assert (scale[e] == s_ref[0]).all(), e
+    # every block's scale is its absmax / 448 (exact max; fp32 division)
+    amax = np.abs(gen.bf16_bits_to_f32(w).reshape(cfg.E, -1, 64 * cfg.H)).max(axis=2)
+    assert (scale == (amax / np.float32(448.0)).astype(np.float32)).all()
+
+
+FP8_GEMM_CASES = [c for c in GEMM_CASES if c[0] in ("many_tiles_k256", "many_tiles_k64", "many_tiles_align1",
+                                                    "ragged", "tails_align8", "wide_H2880", "I640_H2560")]
+
+
+def _oracle_fp8(w_bits, seed):
+    w8, scale = oracle.quantize_fp8(w_bits)
+    return w8, scale, oracle.dequantize_fp8(w8, scale)
+
+
+@pytest.mark.parametrize("case", FP8_GEMM_CASES, ids=[c[0] for c in FP8_GEMM_CASES])
+@pytest.mark.parametrize("gather", [False, True], ids=["layout", "gather"])
+def test_grouped_glu_gemm_fp8w(gpu_lib, case, gather):
+    """Gate/up GEMM on the oracle's FP8 codes and scales against the oracle GEMM
+    on the dequantized weights (float64)."""
+    name, counts, align, H, I = case
+    _say(f"fp8 glu gemm case {name} gather={gather}")
+    counts, offsets = _synthetic_layout(counts, align)
+    E, P = len(counts), int(offsets[-1])
+    P_max = P + 64
+    rows = _rows_of(counts, offsets)
+    w8, scale, w_deq = _oracle_fp8(gen.random_bf16((E, 2 * I, H), seed=2, std=0.02), 2)
+    wq = _dev_fp8(gpu_lib, w8, scale)
+    if gather:
+        T = max(1, len(rows) // 3 + 7)
+        row_token = np.full(P_max, -1, np.int32)
+        row_token[rows] = np.random.default_rng(sum(name.encode())).integers(0, T, size=len(rows))
+        x = gen.random_bf16((T, H), seed=6)
+        x_perm = oracle.gather(x, row_token, rows=P_max)
+        h = gpu_lib.grouped_glu_gemm_gather_fp8w(dev_bf16(x), dev(row_token), wq, dev(counts), dev(offsets))
+    else:
+        x_perm = np.zeros((P_max, H), np.uint16)
+        x_perm[rows] = gen.random_bf16((len(rows), H), seed=1)
+        h = gpu_lib.grouped_glu_gemm_fp8w(dev_bf16(x_perm), wq, dev(counts), dev(offsets))
+    torch.cuda.synchronize()
+    h_ref = oracle.glu_w64(x_perm, w_deq, counts, offsets, I)
+    assert_close_bf16(host_f64(h[:P])[rows], h_ref[rows], f"h_fp8[{name}]")
+
+
+@pytest.mark.parametrize("case", FP8_GEMM_CASES + [("N_tail_H320", [40, 70], 32, 320, 128)],
+                         ids=[c[0] for c in FP8_GEMM_CASES] + ["N_tail_H320"])
+def test_grouped_down_gemm_fp8w(gpu_lib, case):
+    name, counts, align, H, I = case
+    _say(f"fp8 down gemm case {name}")
+    counts, offsets = _synthetic_layout(counts, align)
+    E, P = len(counts), int(offsets[-1])
+    P_max = P + 64
+    rows = _rows_of(counts, offsets)
+    h = np.zeros((P_max, I), np.uint16)
+    h[rows] = gen.random_bf16((len(rows), I), seed=3)
+    w8, scale, w_deq = _oracle_fp8(gen.random_bf16((E, H, I), seed=4, std=0.02), 4)
+    y = gpu_lib.grouped_down_gemm_fp8w(dev_bf16(h), _dev_fp8(gpu_lib, w8, scale), dev(counts), dev(offsets))
+    torch.cuda.synchronize()
+    y_ref = oracle.down_w64(gen.bf16_bits_to_f32(h).astype(np.float64), w_deq, counts, offsets)
+    assert_close_bf16(host_f64(y[:P])[rows], y_ref[rows], f"y_fp8[{name}]")
+
+
+# --------------------------------------------------------------------------------------
 # combine
 # --------------------------------------------------------------------------------------
 
@@ -360,6 +482,48 @@ def test_layer_full_size(gpu_lib, name, n):
     d = gen.make_inputs(name)
     _say(f"full-size layer {name}: running")
     _check_layer(gpu_lib, d, n_tokens=n, full_rows=(name == "gpt_oss_20b_small_m"))
+
+
+def _check_layer_fp8(gpu_lib, d, n_tokens=None, fused_gather=False):
+    """The layer with FP8 expert weights quantized on the GPU: the codes and scales
+    equal the oracle's, and the output rows of sampled tokens match the oracle
+    chain (route, layout, gather, glu_w64, down_w64, combine) run on those tokens
+    alone with the dequantized weights -- routing is per token, so a token's
+    output does not depend on the others."""
+    cfg = d["cfg"]
+    layer = gpu_lib.MoELayer(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.align, fused_gather=fused_gather)
+    q_gu = gpu_lib.quantize_fp8(dev_bf16(d["w_gu"]))
+    q_d = gpu_lib.quantize_fp8(dev_bf16(d["w_d"]))
+    layer(dev_bf16(d["x"]), dev(d["logits"]), q_gu, q_d)
+    torch.cuda.synchronize()
+    w8_gu, s_gu = oracle.quantize_fp8(d["w_gu"])
+    w8_d, s_d = oracle.quantize_fp8(d["w_d"])
+    assert (q_gu.w8.cpu().numpy() == w8_gu).all() and (q_gu.scale.cpu().numpy() == s_gu).all()
+    assert (q_d.w8.cpu().numpy() == w8_d).all() and (q_d.scale.cpu().numpy() == s_d).all()
+    toks = sample_tokens(cfg.T, n_tokens or cfg.T, cfg.seed)
+    idx, w = oracle.route_topk(d["logits"][toks], cfg.k)
+    counts, offsets, route_row, row_token = oracle.layout(idx, cfg.E, 8)
+    x_perm = oracle.gather(d["x"][toks], row_token)
+    h = oracle.glu_w64(x_perm, oracle.dequantize_fp8(w8_gu, s_gu), counts, offsets, cfg.I)
+    y = oracle.down_w64(h, oracle.dequantize_fp8(w8_d, s_d), counts, offsets)
+    ref = oracle.combine(y, route_row, w)
+    got = host_f64(layer.out[dev(toks.astype(np.int64))])
+    rel = assert_close_bf16(got, ref, f"out_fp8[{cfg.name}]", tight=False)
+    _say(f"  fp8 {cfg.name}: max|d|/max|ref| = {rel:.3e} over {len(toks)} tokens")
+
+
+@pytest.mark.parametrize("cfg", SMALL_LAYERS[:4] + SMALL_LAYERS[7:], ids=[c.name for c in SMALL_LAYERS[:4] + SMALL_LAYERS[7:]])
+@pytest.mark.parametrize("fused_gather", [False, True], ids=["layout", "gather"])
+def test_layer_small_fp8(gpu_lib, cfg, fused_gather):
+    _say(f"fp8 layer case {cfg.name} fused_gather={fused_gather}")
+    _check_layer_fp8(gpu_lib, gen.make_inputs(cfg), fused_gather=fused_gather)
+
+
+@pytest.mark.parametrize("name,n", [("gpt_oss_20b_small_m", None), ("qwen3_30b_a3b", 128)],
+                         ids=["gpt_oss_20b_small_m", "qwen3_30b_a3b"])
+def test_layer_full_size_fp8(gpu_lib, name, n):
+    _say(f"full-size fp8 layer {name}")
+    _check_layer_fp8(gpu_lib, gen.make_inputs(name), n_tokens=n, fused_gather=(name == "qwen3_30b_a3b"))
 
 
 def test_layer_deterministic_and_streams(gpu_lib):
