@@ -14,6 +14,10 @@ Heterogeneous TP4 Performance", Confirmed architecture decisions: active-only
 traffic]), the activation buffers each written once and read once, the index
 maps once.  P below is the number of rows actually used by the padded layout
 (offsets[E]); it includes pad rows because they are written and read.
+
+Variants: FP8 expert weights count one byte per weight plus a 4-byte scale per
+64 rows; the fused gather (layout-only permute, gate/up GEMM reading token rows
+in place) moves no x_perm, and its GEMM reads x once.
 """
 from __future__ import annotations
 
@@ -42,30 +46,40 @@ def layer_flops(T: int, H: int, k: int, I: int) -> float:
     return 6.0 * T * k * H * I
 
 
-def step_work(T: int, H: int, E: int, k: int, I: int, P: int, active_experts: int):
+def step_work(T: int, H: int, E: int, k: int, I: int, P: int, active_experts: int,
+              fp8_weights: bool = False, fused_gather: bool = False):
     """Per-step algorithmic work for one layer call (list of StepWork, path order)."""
     R = T * k
     bf, i32, f32 = 2, 4, 4
+    # bytes of one expert's gate/up and down weights
+    if fp8_weights:
+        w_gu_bytes = 2 * I * H + (2 * I // 64) * f32
+        w_d_bytes = H * I + (H // 64) * f32
+    else:
+        w_gu_bytes = 2 * I * H * bf
+        w_d_bytes = H * I * bf
     route = StepWork("route_topk", 0.0, T * E * f32 + R * (i32 + f32))
+    x_moved = 0 if fused_gather else T * H * bf + P * H * bf  # x read, x_perm written
     permute = StepWork(
         "permute",
         0.0,
         R * i32            # topk_idx read
-        + T * H * bf       # x read once
-        + P * H * bf       # x_perm written, pad rows included
+        + x_moved
         + R * i32          # route_row written
         + P * i32          # row_token written
         + (2 * E + 1) * i32,
     )
+    # gate/up A operand: x_perm (pad rows included), or x itself read once plus row_token
+    a_bytes = T * H * bf + P * i32 if fused_gather else P * H * bf
     glu = StepWork(
         "grouped_glu_gemm",
         4.0 * R * H * I,
-        active_experts * 2 * I * H * bf + P * H * bf + P * I * bf + (2 * E + 1) * i32,
+        active_experts * w_gu_bytes + a_bytes + P * I * bf + (2 * E + 1) * i32,
     )
     down = StepWork(
         "grouped_down_gemm",
         2.0 * R * H * I,
-        active_experts * H * I * bf + P * I * bf + P * H * bf + (2 * E + 1) * i32,
+        active_experts * w_d_bytes + P * I * bf + P * H * bf + (2 * E + 1) * i32,
     )
     combine = StepWork("combine", 0.0, R * H * bf + R * (i32 + f32) + T * H * bf)
     return [route, permute, glu, down, combine]
