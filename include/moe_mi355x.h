@@ -150,6 +150,11 @@ moe_status moe_permute(const moe_bf16 *x, const int32_t *topk_idx, int64_t T, in
  *   expert_counts, expert_offsets as produced by moe_permute (device)
  *   h               [P_max, I] bf16 out; rows at or past offsets[E] not written
  * An expert with no rows reads none of its weights.
+ * Kernel choice: 256-row MFMA tiles, except for the FP8-weight GEMMs when
+ * P_max <= 64*E -- few rows per expert, where the weights' bytes bound the GEMM
+ * [Halo, Levers that do not help here] -- which use a weight-streaming kernel
+ * that reads each active expert's weights once per 32 rows of its segment. Both
+ * compute the same values up to fp32 summation order.
  * Shapes: H % 64 == 0, I % 64 == 0, 1 <= E <= MOE_MAX_E, 0 < P_max < 2^31, 4*H*I < 2^32
  * (one expert's weights addressed with 32-bit byte offsets).
  */

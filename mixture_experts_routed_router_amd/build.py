@@ -16,8 +16,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
-SOURCES = ["api.hip", "route_topk.hip", "permute.hip", "grouped_gemm.hip", "combine.hip",
-           "quantize.hip"]
+SOURCES = ["api.hip", "route_topk.hip", "permute.hip", "grouped_gemm.hip", "grouped_gemm_small.hip",
+           "combine.hip", "quantize.hip"]
 LIB_NAME = "libmoe_mi355x.so"
 ARCH = "gfx950"
 

@@ -18,6 +18,8 @@ hipError_t launch_grouped_glu_gemm_gather(const uint16_t*, const int32_t*, const
 hipError_t launch_grouped_down_gemm(const uint16_t*, const void*, const float*, const int32_t*, int,
                                     int, int, uint16_t*, hipStream_t);
 hipError_t launch_quantize_fp8(const uint16_t*, int64_t, int, int, uint8_t*, float*, hipStream_t);
+hipError_t launch_grouped_gemm_small(bool, const uint16_t*, const int32_t*, const void*, const float*,
+                                     const int32_t*, int, int, int, uint16_t*, hipStream_t);
 hipError_t launch_combine(const uint16_t*, const int32_t*, const float*, int64_t, int, int,
                           int64_t, uint16_t*, hipStream_t);
 }  // namespace moe
@@ -73,6 +75,32 @@ moe_status check_dim64(const char* name, int32_t v) {
     if (v < 64 || v % 64 != 0)
         return fail(MOE_ERR_INVALID_SHAPE, "%s=%d must be a positive multiple of 64", name, v);
     return MOE_OK;
+}
+
+// FP8 weights and few rows per expert (P_max <= 64 E): the weight-streaming
+// kernel; otherwise 256-row tiles. P_max bounds the layout's rows, so the host
+// can choose without knowing the counts.
+constexpr int64_t kSmallRowsPerExpert = 64;
+bool use_small_m(int64_t P_max, int32_t E, const float* scale) {
+    return scale != nullptr && P_max <= kSmallRowsPerExpert * E;
+}
+
+// gate/up: C = h from W [E, 2I, H]; down: C = y from W [E, H, I]. scale NULL: bf16 weights.
+hipError_t launch_glu(const uint16_t* a, const int32_t* row_token, const void* w, const float* scale,
+                      const int32_t* offsets, int32_t E, int32_t H, int32_t I, int64_t P_max, uint16_t* h,
+                      hipStream_t stream) {
+    if (use_small_m(P_max, E, scale))
+        return moe::launch_grouped_gemm_small(true, a, row_token, w, scale, offsets, E, H, I, h, stream);
+    if (row_token)
+        return moe::launch_grouped_glu_gemm_gather(a, row_token, w, scale, offsets, E, H, I, h, stream);
+    return moe::launch_grouped_glu_gemm(a, w, scale, offsets, E, H, I, h, stream);
+}
+
+hipError_t launch_down(const uint16_t* h, const void* w, const float* scale, const int32_t* offsets,
+                       int32_t E, int32_t H, int32_t I, int64_t P_max, uint16_t* y, hipStream_t stream) {
+    if (use_small_m(P_max, E, scale))
+        return moe::launch_grouped_gemm_small(false, h, nullptr, w, scale, offsets, E, I, H, y, stream);
+    return moe::launch_grouped_down_gemm(h, w, scale, offsets, E, H, I, y, stream);
 }
 
 moe_status check_pmax(int64_t P_max) {
@@ -185,8 +213,8 @@ moe_status moe_grouped_glu_gemm(const moe_bf16* x_perm, const moe_bf16* w_gate_u
                                 moe_stream_t stream) {
     moe_status s = check_gemm(x_perm, w_gate_up, expert_counts, expert_offsets, E, H, I, P_max, h);
     if (s != MOE_OK) return s;
-    return hip_status(moe::launch_grouped_glu_gemm(x_perm, w_gate_up, nullptr, expert_offsets, E, H, I,
-                                                   h, (hipStream_t)stream),
+    return hip_status(launch_glu(x_perm, nullptr, w_gate_up, nullptr, expert_offsets, E, H, I, P_max, h,
+                                 (hipStream_t)stream),
                       "moe_grouped_glu_gemm launch");
 }
 
@@ -206,9 +234,8 @@ moe_status moe_grouped_glu_gemm_gather(const moe_bf16* x, const int32_t* row_tok
     moe_status s = check_gemm(x, w_gate_up, expert_counts, expert_offsets, E, H, I, P_max, h);
     if (s != MOE_OK) return s;
     if ((s = check_gather(row_token, T, H)) != MOE_OK) return s;
-    return hip_status(moe::launch_grouped_glu_gemm_gather(x, row_token, w_gate_up, nullptr,
-                                                          expert_offsets, E, H, I, h,
-                                                          (hipStream_t)stream),
+    return hip_status(launch_glu(x, row_token, w_gate_up, nullptr, expert_offsets, E, H, I, P_max, h,
+                                 (hipStream_t)stream),
                       "moe_grouped_glu_gemm_gather launch");
 }
 
@@ -218,8 +245,7 @@ moe_status moe_grouped_down_gemm(const moe_bf16* h, const moe_bf16* w_down,
                                  moe_stream_t stream) {
     moe_status s = check_gemm(h, w_down, expert_counts, expert_offsets, E, H, I, P_max, y);
     if (s != MOE_OK) return s;
-    return hip_status(moe::launch_grouped_down_gemm(h, w_down, nullptr, expert_offsets, E, H, I, y,
-                                                    (hipStream_t)stream),
+    return hip_status(launch_down(h, w_down, nullptr, expert_offsets, E, H, I, P_max, y, (hipStream_t)stream),
                       "moe_grouped_down_gemm launch");
 }
 
@@ -245,8 +271,8 @@ moe_status moe_grouped_glu_gemm_fp8w(const moe_bf16* x_perm, const uint8_t* w8_g
     moe_status s = check_gemm(x_perm, w8_gate_up, expert_counts, expert_offsets, E, H, I, P_max, h);
     if (s != MOE_OK) return s;
     REQUIRE_PTR(scale_gate_up);
-    return hip_status(moe::launch_grouped_glu_gemm(x_perm, w8_gate_up, scale_gate_up, expert_offsets, E,
-                                                   H, I, h, (hipStream_t)stream),
+    return hip_status(launch_glu(x_perm, nullptr, w8_gate_up, scale_gate_up, expert_offsets, E, H, I, P_max,
+                                 h, (hipStream_t)stream),
                       "moe_grouped_glu_gemm_fp8w launch");
 }
 
@@ -260,9 +286,8 @@ moe_status moe_grouped_glu_gemm_gather_fp8w(const moe_bf16* x, const int32_t* ro
     if (s != MOE_OK) return s;
     REQUIRE_PTR(scale_gate_up);
     if ((s = check_gather(row_token, T, H)) != MOE_OK) return s;
-    return hip_status(moe::launch_grouped_glu_gemm_gather(x, row_token, w8_gate_up, scale_gate_up,
-                                                          expert_offsets, E, H, I, h,
-                                                          (hipStream_t)stream),
+    return hip_status(launch_glu(x, row_token, w8_gate_up, scale_gate_up, expert_offsets, E, H, I, P_max, h,
+                                 (hipStream_t)stream),
                       "moe_grouped_glu_gemm_gather_fp8w launch");
 }
 
@@ -273,8 +298,8 @@ moe_status moe_grouped_down_gemm_fp8w(const moe_bf16* h, const uint8_t* w8_down,
     moe_status s = check_gemm(h, w8_down, expert_counts, expert_offsets, E, H, I, P_max, y);
     if (s != MOE_OK) return s;
     REQUIRE_PTR(scale_down);
-    return hip_status(moe::launch_grouped_down_gemm(h, w8_down, scale_down, expert_offsets, E, H, I, y,
-                                                    (hipStream_t)stream),
+    return hip_status(launch_down(h, w8_down, scale_down, expert_offsets, E, H, I, P_max, y,
+                                  (hipStream_t)stream),
                       "moe_grouped_down_gemm_fp8w launch");
 }
 

@@ -236,6 +236,90 @@ def test_grouped_down_gemm(gpu_lib, case):
 
 
 # --------------------------------------------------------------------------------------
+# few rows per expert: P_max <= 64 E selects the weight-streaming kernel for FP8
+# weights (bf16 weights keep the tiled kernel: both are checked on these shapes)
+# --------------------------------------------------------------------------------------
+
+SMALL_GEMM_CASES = [
+    # name, counts, align, H, I
+    ("c2_like", _many_counts(32, 29, 31), 32, 512, 384),
+    ("align1_k_tail", _many_counts(24, 40, 32), 1, 192, 320),   # 33..40-row experts: two passes
+    ("align8_one_big", [300, 0, 5, 17, 0, 0, 0, 1, 9, 0, 0, 0, 0, 0, 0, 2], 8, 256, 128),
+    ("k64", [3, 16, 0, 31], 16, 64, 64),                       # one k step (fp8), two (bf16)
+    ("wide_H2880", [16, 9, 28, 0, 12, 20, 7, 30], 32, 2880, 2880),
+]
+
+
+def _small_layout(counts, align):
+    counts, offsets = _synthetic_layout(counts, align)
+    E, P = len(counts), int(offsets[-1])
+    P_max = max(P, 64 * E)            # at the limit of the weight-streaming kernel's range
+    assert P_max <= 64 * E
+    return counts, offsets, E, P, P_max
+
+
+@pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "fp8"])
+@pytest.mark.parametrize("gather", [False, True], ids=["layout", "gather"])
+@pytest.mark.parametrize("case", SMALL_GEMM_CASES, ids=[c[0] for c in SMALL_GEMM_CASES])
+def test_small_m_glu_gemm(gpu_lib, case, gather, fp8):
+    name, counts, align, H, I = case
+    _say(f"small-M glu gemm case {name} gather={gather} fp8={fp8}")
+    counts, offsets, E, P, P_max = _small_layout(counts, align)
+    rows = _rows_of(counts, offsets)
+    w_bits = gen.random_bf16((E, 2 * I, H), seed=2, std=0.02)
+    if fp8:
+        w8, scale = oracle.quantize_fp8(w_bits)
+        w_ref, w_dev = oracle.dequantize_fp8(w8, scale), _dev_fp8(gpu_lib, w8, scale)
+    else:
+        w_ref, w_dev = gen.bf16_bits_to_f32(w_bits).astype(np.float64), dev_bf16(w_bits)
+    if gather:
+        T = max(1, len(rows) // 2 + 3)
+        row_token = np.full(P_max, -1, np.int32)
+        row_token[rows] = np.random.default_rng(sum(name.encode())).integers(0, T, size=len(rows))
+        x = gen.random_bf16((T, H), seed=6)
+        x_perm = oracle.gather(x, row_token, rows=P_max)
+        fn = gpu_lib.grouped_glu_gemm_gather_fp8w if fp8 else gpu_lib.grouped_glu_gemm_gather
+        h = fn(dev_bf16(x), dev(row_token), w_dev, dev(counts), dev(offsets))
+    else:
+        x_perm = np.zeros((P_max, H), np.uint16)
+        x_perm[rows] = gen.random_bf16((len(rows), H), seed=1)
+        fn = gpu_lib.grouped_glu_gemm_fp8w if fp8 else gpu_lib.grouped_glu_gemm
+        h = fn(dev_bf16(x_perm), w_dev, dev(counts), dev(offsets))
+    torch.cuda.synchronize()
+    h_ref = oracle.glu_w64(x_perm, w_ref, counts, offsets, I)
+    hg = host_f64(h[:P])
+    assert_close_bf16(hg[rows], h_ref[rows], f"h_small[{name}]")
+    if not gather:
+        pad = np.setdiff1d(np.arange(P), rows)
+        assert (hg[pad] == 0).all()
+
+
+@pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "fp8"])
+@pytest.mark.parametrize("case", SMALL_GEMM_CASES, ids=[c[0] for c in SMALL_GEMM_CASES])
+def test_small_m_down_gemm(gpu_lib, case, fp8):
+    name, counts, align, H, I = case
+    _say(f"small-M down gemm case {name} fp8={fp8}")
+    counts, offsets, E, P, P_max = _small_layout(counts, align)
+    rows = _rows_of(counts, offsets)
+    h = np.zeros((P_max, I), np.uint16)
+    h[rows] = gen.random_bf16((len(rows), I), seed=3)
+    w_bits = gen.random_bf16((E, H, I), seed=4, std=0.02)
+    if fp8:
+        w8, scale = oracle.quantize_fp8(w_bits)
+        w_ref = oracle.dequantize_fp8(w8, scale)
+        y = gpu_lib.grouped_down_gemm_fp8w(dev_bf16(h), _dev_fp8(gpu_lib, w8, scale), dev(counts), dev(offsets))
+    else:
+        w_ref = gen.bf16_bits_to_f32(w_bits).astype(np.float64)
+        y = gpu_lib.grouped_down_gemm(dev_bf16(h), dev_bf16(w_bits), dev(counts), dev(offsets))
+    torch.cuda.synchronize()
+    y_ref = oracle.down_w64(gen.bf16_bits_to_f32(h).astype(np.float64), w_ref, counts, offsets)
+    yg = host_f64(y[:P])
+    assert_close_bf16(yg[rows], y_ref[rows], f"y_small[{name}]")
+    pad = np.setdiff1d(np.arange(P), rows)
+    assert (yg[pad] == 0).all()
+
+
+# --------------------------------------------------------------------------------------
 # FP8 expert weights
 # --------------------------------------------------------------------------------------
 
