@@ -10,7 +10,9 @@ routing [PocketLLM "Qwen4-Exp Heterogeneous TP4 Performance", Runtime
 architecture], layout and combine [prime-rl PR 3885, Changes: single-pass local
 layout], grouped experts [Halo "Performance", Levers that help], FP8 expert
 weights [Halo "Performance", Levers that do not help here; prime-rl, Changes:
-FP8 expert weights quantized once per optimizer step].
+FP8 expert weights quantized once per optimizer step], and the backward of the
+path [prime-rl, Changes: gathers in backward too; forward, dgrad and wgrad
+grouped GEMMs].
 
 All floating-point results are float64 and exact up to rounding order: bf16
 inputs are widened exactly and nothing in the chain is rounded. The FP8
@@ -62,13 +64,24 @@ def _load(path: str):
     lib.moe_oracle_dequantize_fp8.argtypes = [_u8p, _f32p, i64, i32, i32, _f64p]
     lib.moe_oracle_glu_w64.argtypes = [_u16p, _f64p, _i32p, _i32p, i32, i32, i32, _f64p]
     lib.moe_oracle_down_w64.argtypes = [_f64p, _f64p, _i32p, _i32p, i32, i32, i32, _f64p]
+    lib.moe_oracle_combine_bwd.argtypes = [_f64p, _f64p, _i32p, _f64p, i64, i32, i32, i64, _f64p, _f64p]
+    lib.moe_oracle_route_bwd.argtypes = [_i32p, _f64p, _f64p, i64, i32, i32, _f64p]
+    lib.moe_oracle_swiglu.argtypes = [_f64p, i64, i32, _f64p]
+    lib.moe_oracle_swiglu_bwd.argtypes = [_f64p, _f64p, i64, i32, _f64p]
+    lib.moe_oracle_gemm_nn.argtypes = [_f64p, _u16p, _i32p, _i32p, i32, i32, i32, _f64p]
+    lib.moe_oracle_wgrad.argtypes = [_f64p, _f64p, _i32p, _i32p, i32, i32, i32, _f64p]
+    lib.moe_oracle_permute_bwd.argtypes = [_f64p, _i32p, i64, i32, i32, i64, _f64p]
+    lib.moe_oracle_backward.argtypes = [_u16p, _f32p, _u16p, _u16p, _f64p, i64, i32, i32, i32, i32,
+                                        _f64p, _f64p, _f64p, _f64p]
     lib.moe_oracle_num_threads.argtypes = []
     lib.moe_oracle_num_threads.restype = ctypes.c_int
     for name in ("moe_oracle_route_topk", "moe_oracle_layout", "moe_oracle_gather",
                  "moe_oracle_glu", "moe_oracle_down", "moe_oracle_combine",
                  "moe_oracle_forward", "moe_oracle_fp8_encode", "moe_oracle_fp8_decode",
                  "moe_oracle_quantize_fp8", "moe_oracle_dequantize_fp8", "moe_oracle_glu_w64",
-                 "moe_oracle_down_w64"):
+                 "moe_oracle_down_w64", "moe_oracle_combine_bwd", "moe_oracle_route_bwd",
+                 "moe_oracle_swiglu", "moe_oracle_swiglu_bwd", "moe_oracle_gemm_nn",
+                 "moe_oracle_wgrad", "moe_oracle_permute_bwd", "moe_oracle_backward"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
 
@@ -286,6 +299,117 @@ def down_w64(h: np.ndarray, w_d, counts, offsets, lib=None) -> np.ndarray:
     return y
 
 
+# ---- backward ----------------------------------------------------------------------
+
+def _f64(a):
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def combine_bwd(dout, y, route_row, topk_w, lib=None):
+    """(dy [P_max, H], dw [T, k]): dy rows of routes = w * dout[t], other rows 0;
+    dw = <dout[t], y[route_row]>."""
+    dout, y, topk_w = _f64(dout), _f64(y), _f64(topk_w)
+    route_row = np.ascontiguousarray(route_row, dtype=np.int32).reshape(-1)
+    T, k = topk_w.shape
+    P_max, H = y.shape
+    dy = np.empty((P_max, H))
+    dw = np.empty((T, k))
+    _check((lib or _lib()).moe_oracle_combine_bwd(_p(dout, _f64p), _p(y, _f64p), _p(route_row, _i32p),
+                                                  _p(topk_w, _f64p), T, H, k, P_max, _p(dy, _f64p),
+                                                  _p(dw, _f64p)), "combine_bwd")
+    return dy, dw
+
+
+def route_bwd(topk_idx, topk_w, dw, E: int, lib=None):
+    """dlogits [T, E] of the softmax over the selected logits."""
+    topk_idx = np.ascontiguousarray(topk_idx, dtype=np.int32)
+    topk_w, dw = _f64(topk_w), _f64(dw)
+    T, k = topk_idx.shape
+    out = np.empty((T, E))
+    _check((lib or _lib()).moe_oracle_route_bwd(_p(topk_idx, _i32p), _p(topk_w, _f64p), _p(dw, _f64p),
+                                                T, E, k, _p(out, _f64p)), "route_bwd")
+    return out
+
+
+def swiglu(gu, lib=None):
+    """h [rows, I] = silu(g) * u from gu = [g | u] [rows, 2I]."""
+    gu = _f64(gu)
+    rows, two_i = gu.shape
+    h = np.empty((rows, two_i // 2))
+    _check((lib or _lib()).moe_oracle_swiglu(_p(gu, _f64p), rows, two_i // 2, _p(h, _f64p)), "swiglu")
+    return h
+
+
+def swiglu_bwd(dh, gu, lib=None):
+    """dgu [rows, 2I] = [dh u silu'(g) | dh silu(g)]."""
+    dh, gu = _f64(dh), _f64(gu)
+    rows, I = dh.shape
+    assert gu.shape == (rows, 2 * I)
+    dgu = np.empty((rows, 2 * I))
+    _check((lib or _lib()).moe_oracle_swiglu_bwd(_p(dh, _f64p), _p(gu, _f64p), rows, I, _p(dgu, _f64p)),
+           "swiglu_bwd")
+    return dgu
+
+
+def gemm_nn(a, w_bits, counts, offsets, lib=None):
+    """C[p] = a[p] W[e] on routed rows, W [E, K, N] bf16 bits; other rows NaN."""
+    a = _f64(a)
+    w_bits = _u16(w_bits)
+    counts = np.ascontiguousarray(counts, dtype=np.int32)
+    offsets = np.ascontiguousarray(offsets, dtype=np.int32)
+    rows, K = a.shape
+    E, K2, N = w_bits.shape
+    assert K2 == K and counts.shape[0] == E
+    c = np.full((rows, N), np.nan)
+    _check((lib or _lib()).moe_oracle_gemm_nn(_p(a, _f64p), _p(w_bits, _u16p), _p(counts, _i32p),
+                                              _p(offsets, _i32p), E, K, N, _p(c, _f64p)), "gemm_nn")
+    return c
+
+
+def wgrad(a, b, counts, offsets, lib=None):
+    """dW [E, M, N] = sum over each expert's routed rows of a[p]^T b[p]."""
+    a, b = _f64(a), _f64(b)
+    counts = np.ascontiguousarray(counts, dtype=np.int32)
+    offsets = np.ascontiguousarray(offsets, dtype=np.int32)
+    E = counts.shape[0]
+    M, N = a.shape[1], b.shape[1]
+    assert a.shape[0] == b.shape[0]
+    dW = np.empty((E, M, N))
+    _check((lib or _lib()).moe_oracle_wgrad(_p(a, _f64p), _p(b, _f64p), _p(counts, _i32p),
+                                            _p(offsets, _i32p), E, M, N, _p(dW, _f64p)), "wgrad")
+    return dW
+
+
+def permute_bwd(dx_perm, route_row, T: int, k: int, lib=None):
+    """dx [T, H] = sum_j dx_perm[route_row[t*k+j]]."""
+    dx_perm = _f64(dx_perm)
+    route_row = np.ascontiguousarray(route_row, dtype=np.int32).reshape(-1)
+    P_max, H = dx_perm.shape
+    dx = np.empty((T, H))
+    _check((lib or _lib()).moe_oracle_permute_bwd(_p(dx_perm, _f64p), _p(route_row, _i32p), T, H, k,
+                                                  P_max, _p(dx, _f64p)), "permute_bwd")
+    return dx
+
+
+def backward(x_bits, logits, w_gu_bits, w_d_bits, dout, k: int, lib=None):
+    """The whole backward as a per-token loop: (dx [T,H], dlogits [T,E],
+    dw_gu [E,2I,H], dw_d [E,H,I]), all float64."""
+    x_bits, w_gu_bits, w_d_bits = _u16(x_bits), _u16(w_gu_bits), _u16(w_d_bits)
+    logits = np.ascontiguousarray(logits, dtype=np.float32)
+    dout = _f64(dout)
+    T, H = x_bits.shape
+    E, two_i, _ = w_gu_bits.shape
+    I = two_i // 2
+    assert logits.shape == (T, E) and w_d_bits.shape == (E, H, I) and dout.shape == (T, H)
+    dx, dl = np.empty((T, H)), np.empty((T, E))
+    dwgu, dwd = np.empty((E, 2 * I, H)), np.empty((E, H, I))
+    _check((lib or _lib()).moe_oracle_backward(_p(x_bits, _u16p), _p(logits, _f32p), _p(w_gu_bits, _u16p),
+                                               _p(w_d_bits, _u16p), _p(dout, _f64p), T, H, E, k, I,
+                                               _p(dx, _f64p), _p(dl, _f64p), _p(dwgu, _f64p),
+                                               _p(dwd, _f64p)), "backward")
+    return dx, dl, dwgu, dwd
+
+
 class Oracle:
     """The oracle's functions bound to one built library (the default build, or
     a variant that a test compiled from an edited copy of the source)."""
@@ -331,3 +455,27 @@ class Oracle:
 
     def down_w64(self, *a, **kw):
         return down_w64(*a, lib=self.lib, **kw)
+
+    def combine_bwd(self, *a, **kw):
+        return combine_bwd(*a, lib=self.lib, **kw)
+
+    def route_bwd(self, *a, **kw):
+        return route_bwd(*a, lib=self.lib, **kw)
+
+    def swiglu(self, *a, **kw):
+        return swiglu(*a, lib=self.lib, **kw)
+
+    def swiglu_bwd(self, *a, **kw):
+        return swiglu_bwd(*a, lib=self.lib, **kw)
+
+    def gemm_nn(self, *a, **kw):
+        return gemm_nn(*a, lib=self.lib, **kw)
+
+    def wgrad(self, *a, **kw):
+        return wgrad(*a, lib=self.lib, **kw)
+
+    def permute_bwd(self, *a, **kw):
+        return permute_bwd(*a, lib=self.lib, **kw)
+
+    def backward(self, *a, **kw):
+        return backward(*a, lib=self.lib, **kw)

@@ -14,7 +14,8 @@
  *               Changes; Known numerics
  *
  * What is computed, for T tokens of hidden size H, E experts, top-k routing and
- * expert intermediate size I (all tensors row-major):
+ * expert intermediate size I (all tensors row-major) -- the forward below, and
+ * its backward further down:
  *   routing   per token, the k experts with the largest router logits, and their
  *             weights = softmax over those k logits;
  *   layout    a padded, expert-grouped row layout of the routed tokens, built by a
@@ -460,6 +461,253 @@ int moe_oracle_down_w64(const double *h, const double *w_d, const int32_t *count
             }
         }
     }
+    return 0;
+}
+
+/*
+ * ---------------------------------------------------------------------------
+ * Backward of the path [prime-rl PR 3885, Changes: the single-pass layout gathers
+ * in backward too; grouped GEMMs for the forward, dgrad and wgrad; weight
+ * gradients accumulated in fp32; the forward keeps its gate/up output so that
+ * the backward does not recompute it].  For a loss with gradient dout [T, H]
+ * with respect to the layer output (chain rule through each forward step):
+ *   combine   dw[t,j] = <dout[t], y[route_row[t*k+j]]>
+ *             dy[route_row[t*k+j]] = w[t,j] dout[t]      (every other row 0)
+ *   routing   softmax over the k selected logits:
+ *             dlogits[t, idx[t,j]] = w[t,j] (dw[t,j] - sum_i w[t,i] dw[t,i]);
+ *             0 for the experts not selected (the selection is piecewise constant)
+ *   down      dh[p] = dy[p] W_d[e]            dW_d[e] = sum_p dy[p]^T h[p]
+ *   SwiGLU    h = silu(g) u:  dg = dh u silu'(g),  du = dh silu(g),
+ *             silu'(g) = s (1 + g (1 - s)) with s = sigmoid(g)
+ *   gate/up   dx_perm[p] = dg[p] W_gate[e] + du[p] W_up[e]
+ *             dW_gu[e] = sum_p [dg[p], du[p]]^T x_perm[p]
+ *   permute   dx[t] = sum_j dx_perm[route_row[t*k+j]]   (a gather per token)
+ * Sums over rows p run over an expert's routed rows in ascending order, which
+ * is ascending token order (the layout is stable), so the step functions and
+ * the per-token loop add the same terms in the same order.
+ * ---------------------------------------------------------------------------
+ */
+
+int moe_oracle_combine_bwd(const double *dout, const double *y, const int32_t *route_row,
+                           const double *topk_w, int64_t T, int32_t H, int32_t k, int64_t P_max,
+                           double *dy, double *dw) {
+    if (!dout || !y || !route_row || !topk_w || !dy || !dw || T < 0 || H < 1 || k < 1 || P_max < 0)
+        return ORACLE_EINVAL;
+    for (int64_t r = 0; r < T * (int64_t)k; ++r)
+        if (route_row[r] < 0 || route_row[r] >= P_max) return ORACLE_ERANGE;
+    for (int64_t i = 0; i < P_max * (int64_t)H; ++i) dy[i] = 0.0;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        const double *g = dout + t * H;
+        for (int32_t j = 0; j < k; ++j) {
+            const int64_t p = route_row[t * k + j];
+            const double w = topk_w[t * k + j];
+            double s = 0.0;
+            for (int32_t c = 0; c < H; ++c) {
+                s += g[c] * y[p * H + c];
+                dy[p * H + c] = w * g[c];
+            }
+            dw[t * k + j] = s;
+        }
+    }
+    return 0;
+}
+
+int moe_oracle_route_bwd(const int32_t *topk_idx, const double *topk_w, const double *dw, int64_t T,
+                         int32_t E, int32_t k, double *dlogits) {
+    if (!topk_idx || !topk_w || !dw || !dlogits || T < 0 || E < 1 || k < 1 || k > E)
+        return ORACLE_EINVAL;
+    for (int64_t r = 0; r < T * (int64_t)k; ++r)
+        if (topk_idx[r] < 0 || topk_idx[r] >= E) return ORACLE_ERANGE;
+    for (int64_t t = 0; t < T; ++t) {
+        double s = 0.0;
+        for (int32_t j = 0; j < k; ++j) s += topk_w[t * k + j] * dw[t * k + j];
+        for (int32_t e = 0; e < E; ++e) dlogits[t * E + e] = 0.0;
+        for (int32_t j = 0; j < k; ++j)
+            dlogits[t * E + topk_idx[t * k + j]] = topk_w[t * k + j] * (dw[t * k + j] - s);
+    }
+    return 0;
+}
+
+/* derivative of silu: d/dg [g sigmoid(g)] = s + g s (1 - s) */
+static double silu_grad(double g) {
+    const double s = 1.0 / (1.0 + exp(-g));
+    return s * (1.0 + g * (1.0 - s));
+}
+
+/* SwiGLU forward and backward on rows of gu = [g | u] ([rows, 2I]):
+ *   h[p,i] = silu(g) u;   dgu[p,i] = dh u silu'(g),  dgu[p,I+i] = dh silu(g). */
+int moe_oracle_swiglu(const double *gu, int64_t rows, int32_t I, double *h) {
+    if (!gu || !h || rows < 0 || I < 1) return ORACLE_EINVAL;
+    for (int64_t p = 0; p < rows; ++p)
+        for (int32_t i = 0; i < I; ++i)
+            h[p * I + i] = silu(gu[p * 2 * I + i]) * gu[p * 2 * I + I + i];
+    return 0;
+}
+
+int moe_oracle_swiglu_bwd(const double *dh, const double *gu, int64_t rows, int32_t I, double *dgu) {
+    if (!dh || !gu || !dgu || rows < 0 || I < 1) return ORACLE_EINVAL;
+    for (int64_t p = 0; p < rows; ++p)
+        for (int32_t i = 0; i < I; ++i) {
+            const double g = gu[p * 2 * I + i], u = gu[p * 2 * I + I + i], d = dh[p * I + i];
+            dgu[p * 2 * I + i] = d * u * silu_grad(g);
+            dgu[p * 2 * I + I + i] = d * silu(g);
+        }
+    return 0;
+}
+
+/* Grouped GEMM with the weight as stored (dgrad): C[p,n] = sum_k A[p,k] W[e,k,n],
+ * W [E, K, N], on each expert's routed rows.  dh = dy W_d uses W_d [E, H, I];
+ * dx_perm = dgu W_gu uses W_gu [E, 2I, H]. */
+int moe_oracle_gemm_nn(const double *A, const uint16_t *W, const int32_t *counts,
+                       const int32_t *offsets, int32_t E, int32_t K, int32_t N, double *C) {
+    if (!A || !W || !counts || !offsets || !C || E < 1 || K < 1 || N < 1) return ORACLE_EINVAL;
+    for (int32_t e = 0; e < E; ++e) {
+        const uint16_t *We = W + (int64_t)e * K * N;
+        const int64_t p0 = offsets[e], n = counts[e];
+#pragma omp parallel for schedule(static)
+        for (int64_t p = p0; p < p0 + n; ++p)
+            for (int32_t c = 0; c < N; ++c) {
+                double s = 0.0;
+                for (int32_t kk = 0; kk < K; ++kk) s += A[p * K + kk] * bf(We[(int64_t)kk * N + c]);
+                C[p * N + c] = s;
+            }
+    }
+    return 0;
+}
+
+/* Weight gradient, K-grouped over each expert's rows:
+ *   dW[e,m,n] = sum over routed rows p of e (ascending) of A[p,m] B[p,n]
+ * A [rows, M], B [rows, N], dW [E, M, N]; an expert with no rows gets zeros. */
+int moe_oracle_wgrad(const double *A, const double *B, const int32_t *counts,
+                     const int32_t *offsets, int32_t E, int32_t M, int32_t N, double *dW) {
+    if (!A || !B || !counts || !offsets || !dW || E < 1 || M < 1 || N < 1) return ORACLE_EINVAL;
+    for (int32_t e = 0; e < E; ++e) {
+        double *D = dW + (int64_t)e * M * N;
+        const int64_t p0 = offsets[e], n = counts[e];
+#pragma omp parallel for schedule(static)
+        for (int32_t m = 0; m < M; ++m)
+            for (int32_t c = 0; c < N; ++c) {
+                double s = 0.0;
+                for (int64_t p = p0; p < p0 + n; ++p) s += A[p * M + m] * B[p * N + c];
+                D[(int64_t)m * N + c] = s;
+            }
+    }
+    return 0;
+}
+
+/* The permute's backward: dx[t,c] = sum_j dx_perm[route_row[t*k+j], c], j ascending. */
+int moe_oracle_permute_bwd(const double *dx_perm, const int32_t *route_row, int64_t T, int32_t H,
+                           int32_t k, int64_t P_max, double *dx) {
+    if (!dx_perm || !route_row || !dx || T < 0 || H < 1 || k < 1) return ORACLE_EINVAL;
+    for (int64_t r = 0; r < T * (int64_t)k; ++r)
+        if (route_row[r] < 0 || route_row[r] >= P_max) return ORACLE_ERANGE;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t)
+        for (int32_t c = 0; c < H; ++c) {
+            double s = 0.0;
+            for (int32_t j = 0; j < k; ++j) s += dx_perm[(int64_t)route_row[t * k + j] * H + c];
+            dx[t * H + c] = s;
+        }
+    return 0;
+}
+
+/*
+ * The whole backward as a per-token loop (no layout): route the token, recompute
+ * each of its k experts (g, u, h, y), then apply the chain rule above; weight
+ * gradients accumulate over tokens in ascending order.  dout [T, H] in double;
+ * outputs dx [T, H], dlogits [T, E], dw_gu [E, 2I, H], dw_d [E, H, I].
+ */
+int moe_oracle_backward(const uint16_t *x, const float *logits, const uint16_t *w_gu,
+                        const uint16_t *w_d, const double *dout, int64_t T, int32_t H, int32_t E,
+                        int32_t k, int32_t I, double *dx, double *dlogits, double *dw_gu,
+                        double *dw_d) {
+    if (!x || !logits || !w_gu || !w_d || !dout || !dx || !dlogits || !dw_gu || !dw_d || T < 0 ||
+        H < 1 || E < 1 || k < 1 || k > E || I < 1)
+        return ORACLE_EINVAL;
+    for (int64_t i = 0; i < T * (int64_t)E; ++i)
+        if (!isfinite(logits[i])) return ORACLE_ENONFINITE;
+    for (int64_t i = 0; i < (int64_t)E * 2 * I * H; ++i) dw_gu[i] = 0.0;
+    for (int64_t i = 0; i < (int64_t)E * H * I; ++i) dw_d[i] = 0.0;
+    int32_t *idx = (int32_t *)malloc(sizeof(int32_t) * (size_t)k);
+    double *w = (double *)malloc(sizeof(double) * (size_t)k);
+    double *dwt = (double *)malloc(sizeof(double) * (size_t)k);
+    double *g = (double *)malloc(sizeof(double) * (size_t)I * k);
+    double *u = (double *)malloc(sizeof(double) * (size_t)I * k);
+    double *a = (double *)malloc(sizeof(double) * (size_t)I * k);
+    double *dh = (double *)malloc(sizeof(double) * (size_t)I);
+    if (!idx || !w || !dwt || !g || !u || !a || !dh) {
+        free(idx); free(w); free(dwt); free(g); free(u); free(a); free(dh);
+        return ORACLE_EINVAL;
+    }
+    for (int64_t t = 0; t < T; ++t) {
+        const uint16_t *xr = x + t * H;
+        const double *gr = dout + t * H;
+        moe_oracle_route_topk(logits + t * E, 1, E, k, idx, w);
+        /* forward of each route, and dw */
+        for (int32_t j = 0; j < k; ++j) {
+            const uint16_t *Wgu = w_gu + (int64_t)idx[j] * 2 * I * H;
+            const uint16_t *Wd = w_d + (int64_t)idx[j] * H * I;
+            for (int32_t i = 0; i < I; ++i) {
+                double gg = 0.0, uu = 0.0;
+                for (int32_t c = 0; c < H; ++c) {
+                    gg += bf(xr[c]) * bf(Wgu[(int64_t)i * H + c]);
+                    uu += bf(xr[c]) * bf(Wgu[(int64_t)(I + i) * H + c]);
+                }
+                g[j * I + i] = gg;
+                u[j * I + i] = uu;
+                a[j * I + i] = silu(gg) * uu;
+            }
+            double s = 0.0;
+            for (int32_t c = 0; c < H; ++c) {
+                double yc = 0.0;
+                for (int32_t i = 0; i < I; ++i) yc += a[j * I + i] * bf(Wd[(int64_t)c * I + i]);
+                s += gr[c] * yc;
+            }
+            dwt[j] = s;
+        }
+        double sw = 0.0;
+        for (int32_t j = 0; j < k; ++j) sw += w[j] * dwt[j];
+        for (int32_t e = 0; e < E; ++e) dlogits[t * E + e] = 0.0;
+        for (int32_t j = 0; j < k; ++j) dlogits[t * E + idx[j]] = w[j] * (dwt[j] - sw);
+        for (int32_t c = 0; c < H; ++c) dx[t * H + c] = 0.0;
+        /* backward of each route */
+        for (int32_t j = 0; j < k; ++j) {
+            const uint16_t *Wd = w_d + (int64_t)idx[j] * H * I;
+            double *dWgu = dw_gu + (int64_t)idx[j] * 2 * I * H;
+            double *dWd = dw_d + (int64_t)idx[j] * H * I;
+            for (int32_t i = 0; i < I; ++i) {
+                double sdh = 0.0;
+                for (int32_t c = 0; c < H; ++c) sdh += (w[j] * gr[c]) * bf(Wd[(int64_t)c * I + i]);
+                dh[i] = sdh;
+            }
+            for (int32_t c = 0; c < H; ++c)
+                for (int32_t i = 0; i < I; ++i) dWd[(int64_t)c * I + i] += (w[j] * gr[c]) * a[j * I + i];
+            for (int32_t i = 0; i < I; ++i) {
+                const double dg = dh[i] * u[j * I + i] * silu_grad(g[j * I + i]);
+                const double du = dh[i] * silu(g[j * I + i]);
+                for (int32_t c = 0; c < H; ++c) {
+                    dWgu[(int64_t)i * H + c] += dg * bf(xr[c]);
+                    dWgu[(int64_t)(I + i) * H + c] += du * bf(xr[c]);
+                }
+                g[j * I + i] = dg; /* keep dg, du for dx below */
+                u[j * I + i] = du;
+            }
+        }
+        /* dx[t] = sum_j of that route's dx_perm row, j ascending */
+        for (int32_t j = 0; j < k; ++j) {
+            const uint16_t *Wgu = w_gu + (int64_t)idx[j] * 2 * I * H;
+            for (int32_t c = 0; c < H; ++c) {
+                double s = 0.0;
+                for (int32_t i = 0; i < 2 * I; ++i) {
+                    const double d = i < I ? g[j * I + i] : u[j * I + i - I];
+                    s += d * bf(Wgu[(int64_t)i * H + c]);
+                }
+                dx[t * H + c] += s;
+            }
+        }
+    }
+    free(idx); free(w); free(dwt); free(g); free(u); free(a); free(dh);
     return 0;
 }
 

@@ -63,6 +63,42 @@ MUTANTS = {
     # fp8 weights: gate rows read from the up half
     "w64_gate_from_up": ([("const double *wg = W + (int64_t)i * H;", "const double *wg = W + (int64_t)(I + i) * H;")],
                          [pins.check_glu_down_w64]),
+    # backward: silu' loses its second term (used by both the loop and the steps)
+    "bwd_silu_grad_first_term_only": ([("return s * (1.0 + g * (1.0 - s));", "return s;")],
+                                      [pins.check_backward_finite_differences,
+                                       pins.check_swiglu_bwd_derivative]),
+    # backward loop: dy without the routing weight
+    "bwd_dy_unweighted": ([("sdh += (w[j] * gr[c]) * bf(Wd[(int64_t)c * I + i]);",
+                            "sdh += gr[c] * bf(Wd[(int64_t)c * I + i]);")],
+                          [pins.check_backward_finite_differences]),
+    # backward loop: W_down gradient written transposed
+    "bwd_dwd_transposed": ([("dWd[(int64_t)c * I + i] += (w[j] * gr[c]) * a[j * I + i];",
+                             "dWd[(int64_t)i * H + c] += (w[j] * gr[c]) * a[j * I + i];")],
+                           [pins.check_backward_finite_differences]),
+    # backward loop: dx misses the up projection's share
+    "bwd_dx_drops_up": ([("const double d = i < I ? g[j * I + i] : u[j * I + i - I];",
+                          "const double d = i < I ? g[j * I + i] : 0.0;")],
+                        [pins.check_backward_finite_differences]),
+    # backward loop: softmax gradient without the mean term
+    "bwd_loop_softmax_no_mean": ([("dlogits[t * E + idx[j]] = w[j] * (dwt[j] - sw);",
+                                   "dlogits[t * E + idx[j]] = w[j] * dwt[j];")],
+                                 [pins.check_backward_finite_differences, pins.check_backward_invariants]),
+    # backward steps: softmax gradient without the mean term
+    "bwd_step_softmax_no_mean": ([("= topk_w[t * k + j] * (dw[t * k + j] - s);",
+                                   "= topk_w[t * k + j] * dw[t * k + j];")],
+                                 [pins.check_backward_steps_compose]),
+    # backward steps: gate and up gradients swapped
+    "bwd_step_swiglu_swapped": ([("dgu[p * 2 * I + i] = d * u * silu_grad(g);\n            dgu[p * 2 * I + I + i] = d * silu(g);",
+                                  "dgu[p * 2 * I + I + i] = d * u * silu_grad(g);\n            dgu[p * 2 * I + i] = d * silu(g);")],
+                                [pins.check_backward_steps_compose, pins.check_swiglu_bwd_derivative]),
+    # backward steps: permute backward drops the first route of each token
+    "bwd_step_permute_drops_route": ([("for (int32_t j = 0; j < k; ++j) s += dx_perm[",
+                                       "for (int32_t j = 1; j < k; ++j) s += dx_perm[")],
+                                     [pins.check_backward_steps_compose, pins.check_backward_invariants]),
+    # backward steps: wgrad sums one row short per expert
+    "bwd_step_wgrad_short": ([("for (int64_t p = p0; p < p0 + n; ++p) s += A[p * M + m] * B[p * N + c];",
+                               "for (int64_t p = p0; p + 1 < p0 + n; ++p) s += A[p * M + m] * B[p * N + c];")],
+                             [pins.check_backward_steps_compose, pins.check_backward_invariants]),
 }
 
 

@@ -415,6 +415,156 @@ def check_glu_down_w64(orc):
 
 
 # --------------------------------------------------------------------------------------
+# backward
+# --------------------------------------------------------------------------------------
+
+def dense_forward64(X, L, Wgu, Wd, k):
+    """The layer on float64 arrays (every expert on every token, then the top-k
+    gate matrix), for finite differences: no bf16 anywhere."""
+    T, H = X.shape
+    E, two_i, _ = Wgu.shape
+    I = two_i // 2
+    gate = np.zeros((T, E))
+    for t in range(T):
+        sel = np.lexsort((np.arange(E), -L[t]))[:k]
+        z = np.exp(L[t, sel] - L[t, sel[0]])
+        gate[t, sel] = z / z.sum()
+    out = np.zeros((T, H))
+    for e in range(E):
+        out += gate[:, e:e + 1] * ((_silu(X @ Wgu[e, :I].T) * (X @ Wgu[e, I:].T)) @ Wd[e].T)
+    return out
+
+
+def _bwd_case(seed=31, T=7, H=8, E=4, k=2, I=6, std=0.4):
+    rng = np.random.default_rng(seed)
+    x = gen.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    w_gu = gen.f32_to_bf16_bits((rng.standard_normal((E, 2 * I, H)) * std).astype(np.float32))
+    w_d = gen.f32_to_bf16_bits((rng.standard_normal((E, H, I)) * std).astype(np.float32))
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    dout = rng.standard_normal((T, H))
+    return x, logits, w_gu, w_d, dout, k
+
+
+def check_backward_finite_differences(orc):
+    """Every gradient of the per-token backward against central differences of an
+    independent float64 forward, on random elements of x, logits, W_gu and W_d."""
+    x, logits, w_gu, w_d, dout, k = _bwd_case()
+    X, L = f32(x).astype(np.float64), logits.astype(np.float64)
+    Wgu, Wd = f32(w_gu).astype(np.float64), f32(w_d).astype(np.float64)
+    srt = np.sort(L, axis=1)[:, ::-1]
+    assert np.all(srt[:, k - 1] - srt[:, k] > 1e-4)   # no selection change under the probe
+    dx, dl, dwgu, dwd = orc.backward(x, logits, w_gu, w_d, dout, k)
+    args = [X, L, Wgu, Wd]
+    grads = [dx, dl, dwgu, dwd]
+    rng = np.random.default_rng(5)
+    eps = 1e-6
+    for a_i, (A, G) in enumerate(zip(args, grads)):
+        flat = rng.choice(A.size, size=min(A.size, 24), replace=False)
+        scale = np.max(np.abs(G))
+        assert scale > 0
+        for f in flat:
+            ix = np.unravel_index(f, A.shape)
+            vals = []
+            for sgn in (1, -1):
+                B = [a.copy() for a in args]
+                B[a_i][ix] += sgn * eps
+                vals.append(np.sum(dout * dense_forward64(*B, k)))
+            fd = (vals[0] - vals[1]) / (2 * eps)
+            assert abs(fd - G[ix]) <= 1e-6 * scale, (a_i, ix, fd, G[ix])
+
+
+def _oracle_forward_intermediates(orc, x, logits, w_gu, w_d, k, align=4):
+    T, H = x.shape
+    E, two_i, _ = w_gu.shape
+    I = two_i // 2
+    idx, w = orc.route_topk(logits, k)
+    counts, offsets, route_row, row_token = orc.layout(idx, E, align)
+    xp = orc.gather(x, row_token)
+    gu = np.nan_to_num(orc.down(f32(xp).astype(np.float64), w_gu, counts, offsets))  # [g | u] = x_perm W_gu^T
+    h = orc.swiglu(gu)
+    y = np.nan_to_num(orc.down(h, w_d, counts, offsets))
+    return idx, w, counts, offsets, route_row, row_token, xp, gu, h, y
+
+
+def check_backward_steps_compose(orc):
+    """combine_bwd -> route_bwd, gemm_nn (dh) -> swiglu_bwd -> gemm_nn (dx_perm) ->
+    permute_bwd, and wgrad for both weights, equal the per-token loop (same
+    terms in the same order)."""
+    for case in (_bwd_case(), _bwd_case(seed=32, T=20, H=16, E=6, k=3, I=10, std=0.1)):
+        x, logits, w_gu, w_d, dout, k = case
+        T, H = x.shape
+        E = w_gu.shape[0]
+        idx, w, counts, offsets, route_row, row_token, xp, gu, h, y = \
+            _oracle_forward_intermediates(orc, x, logits, w_gu, w_d, k)
+        dy, dw = orc.combine_bwd(dout, y, route_row, w)
+        dl = orc.route_bwd(idx, w, dw, E)
+        dh = np.nan_to_num(orc.gemm_nn(dy, w_d, counts, offsets))
+        dgu = orc.swiglu_bwd(dh, gu)
+        dxp = np.nan_to_num(orc.gemm_nn(dgu, w_gu, counts, offsets))
+        dx = orc.permute_bwd(dxp, route_row, T, k)
+        dwd = orc.wgrad(dy, h, counts, offsets)
+        dwgu = orc.wgrad(dgu, f32(xp).astype(np.float64), counts, offsets)
+        ref = orc.backward(x, logits, w_gu, w_d, dout, k)
+        for name, a, b in zip(("dx", "dlogits", "dw_gu", "dw_d"), (dx, dl, dwgu, dwd), ref):
+            assert np.max(np.abs(a - b)) <= 1e-12 * max(1e-300, np.max(np.abs(b))), name
+
+
+def check_backward_invariants(orc):
+    """Softmax gradient rows sum to zero; k = 1 leaves no logit gradient; the
+    backward is linear in dout (doubling is exact); unrouted experts get zero
+    weight gradients; the steps match numpy matmuls on their own."""
+    x, logits, w_gu, w_d, dout, k = _bwd_case(seed=33, T=12, E=6, k=3)
+    dx, dl, dwgu, dwd = orc.backward(x, logits, w_gu, w_d, dout, k)
+    assert np.all(np.abs(dl.sum(axis=1)) <= 1e-15 * max(1.0, np.max(np.abs(dl))) * 8)
+    sel = np.zeros_like(dl, dtype=bool)
+    idx, _ = orc.route_topk(logits, k)
+    np.put_along_axis(sel, idx.astype(np.int64), True, axis=1)
+    assert np.all(dl[~sel] == 0)
+    for a, b in zip(orc.backward(x, logits, w_gu, w_d, 2 * dout, k), (dx, dl, dwgu, dwd)):
+        assert np.array_equal(a, 2 * b)
+    _, dl1, _, _ = orc.backward(x, logits, w_gu, w_d, dout, 1)
+    assert np.all(dl1 == 0)
+    # experts no token selects get zero weight gradients
+    L2 = logits.copy()
+    L2[:, 0] = -50.0
+    _, _, dwgu2, dwd2 = orc.backward(x, L2, w_gu, w_d, dout, k)
+    assert np.all(dwgu2[0] == 0) and np.all(dwd2[0] == 0)
+    # gemm_nn and wgrad against numpy matmuls, per expert
+    idx, w, counts, offsets, route_row, row_token, xp, gu, h, y = \
+        _oracle_forward_intermediates(orc, x, logits, w_gu, w_d, k)
+    rng = np.random.default_rng(1)
+    A = rng.standard_normal((len(row_token), w_d.shape[1]))
+    C = orc.gemm_nn(A, w_d, counts, offsets)
+    Wd = f32(w_d).astype(np.float64)
+    B = rng.standard_normal((len(row_token), 5))
+    dW = orc.wgrad(A, B, counts, offsets)
+    for e in range(len(counts)):
+        rows = np.arange(offsets[e], offsets[e] + counts[e])
+        assert np.allclose(C[rows], A[rows] @ Wd[e], rtol=1e-13, atol=1e-13)
+        assert np.allclose(dW[e], A[rows].T @ B[rows], rtol=1e-13, atol=1e-13)
+    # permute_bwd against numpy's scatter-add of routed rows back to tokens
+    dxp = rng.standard_normal((len(row_token), 4))
+    ref = np.zeros((x.shape[0], 4))
+    np.add.at(ref, np.repeat(np.arange(x.shape[0]), k), dxp[route_row])
+    assert np.allclose(orc.permute_bwd(dxp, route_row, x.shape[0], k), ref, rtol=1e-14, atol=1e-14)
+
+
+def check_swiglu_bwd_derivative(orc):
+    """swiglu_bwd against central differences of swiglu itself."""
+    rng = np.random.default_rng(4)
+    gu = rng.standard_normal((5, 12)) * 3
+    dh = rng.standard_normal((5, 6))
+    dgu = orc.swiglu_bwd(dh, gu)
+    eps = 1e-6
+    for i in range(12):
+        P, M = gu.copy(), gu.copy()
+        P[:, i] += eps
+        M[:, i] -= eps
+        fd = (np.sum(dh * orc.swiglu(P), axis=1) - np.sum(dh * orc.swiglu(M), axis=1)) / (2 * eps)
+        assert np.allclose(dgu[:, i], fd, rtol=1e-7, atol=1e-8), i
+
+
+# --------------------------------------------------------------------------------------
 # tests
 # --------------------------------------------------------------------------------------
 
@@ -488,6 +638,22 @@ def test_fp8_quantize(orc):
 
 def test_glu_down_w64(orc):
     check_glu_down_w64(orc)
+
+
+def test_backward_finite_differences(orc):
+    check_backward_finite_differences(orc)
+
+
+def test_backward_steps_compose(orc):
+    check_backward_steps_compose(orc)
+
+
+def test_backward_invariants(orc):
+    check_backward_invariants(orc)
+
+
+def test_swiglu_bwd_derivative(orc):
+    check_swiglu_bwd_derivative(orc)
 
 
 def test_rejects_bad_inputs(orc):
