@@ -20,6 +20,12 @@
  *   moe_grouped_glu_gemm_fp8w, moe_grouped_glu_gemm_gather_fp8w,
  *   moe_grouped_down_gemm_fp8w
  *
+ * Training (the forward with its gate/up output kept, and the backward):
+ *   moe_grouped_gemm       plain grouped GEMM C[p] = A[p] W[e]^T (gate/up output
+ *                          gu = x_perm W_gu^T; input gradients on transposed weights)
+ *   moe_swiglu, moe_swiglu_backward, moe_transpose_experts, moe_combine_backward,
+ *   moe_route_backward, moe_permute_backward, moe_grouped_wgrad
+ *
  * Sources (page title, section):
  *   [Halo]      Halo, "Performance": Levers that help (grouped GEMM instead of a
  *               per-expert loop; the atomic-free expert permute; fused GLU);
@@ -32,7 +38,9 @@
  *               gather into the padded expert-grouped layout and one fp32
  *               score-weighted gather-sum back; 32-bit row offsets must not
  *               overflow silently; FP8 expert weights quantized once per
- *               optimizer step, blockwise FP8 grouped GEMMs)
+ *               optimizer step, blockwise FP8 grouped GEMMs; the layout's gathers
+ *               in backward too; forward, dgrad and wgrad grouped GEMMs; weight
+ *               gradients in fp32; the forward keeps its gate/up output)
  *
  * Conventions
  *   - Every tensor pointer is a DEVICE pointer, row-major, 16-byte aligned.
@@ -258,6 +266,99 @@ moe_status moe_grouped_down_gemm_fp8w(const moe_bf16 *h, const uint8_t *w8_down,
                                       const float *scale_down, const int32_t *expert_counts,
                                       const int32_t *expert_offsets, int32_t E, int32_t H, int32_t I,
                                       int64_t P_max, moe_bf16 *y, moe_stream_t stream);
+
+/*
+ * ---- training: forward with saved gate/up output, and the backward ----
+ *
+ * Backward recipe for one layer (gradients of a loss with dL/dout = dout):
+ *   forward:  moe_route_topk, moe_permute, gu = moe_grouped_gemm(x_perm, w_gate_up)
+ *             [P_max, 2I], h = moe_swiglu(gu), y = moe_grouped_down_gemm(h, w_down),
+ *             out = moe_combine(y)
+ *   backward: dy, dw = moe_combine_backward(dout, y); dlogits = moe_route_backward(dw);
+ *             dh = moe_grouped_gemm(dy, w_down^T); dgu = moe_swiglu_backward(dh, gu);
+ *             dx_perm = moe_grouped_gemm(dgu, w_gate_up^T); dx = moe_permute_backward;
+ *             dW_down = moe_grouped_wgrad(dy, h); dW_gate_up = moe_grouped_wgrad(dgu, x_perm)
+ *   where w^T comes from moe_transpose_experts once per weight update.
+ * Pad rows: moe_combine_backward zeroes dy's pad rows, so every later step may run
+ * over whole padded segments and the weight gradients get nothing from them.
+ */
+
+/*
+ * Plain grouped GEMM: for every row p of expert e's padded segment,
+ *   c[p, n] = bf16_rne( sum_k a[p, k] w[e, n, k] )     (fp32 accumulation)
+ *   a [P_max, K] bf16;  w [E, N, K] bf16;  c [P_max, N] bf16 out (rows past offsets[E]
+ *   not written).  The gate/up output: a = x_perm, w = w_gate_up, N = 2I, K = H.
+ *   The input gradients: a = dy, w = w_down^T [E, I, H] (N = I, K = H) for dh, and
+ *   a = dgu, w = w_gate_up^T [E, H, 2I] (N = H, K = 2I) for dx_perm.
+ * Shapes: K % 64 == 0, N % 64 == 0, 4*N*K < 2^32, 1 <= E <= MOE_MAX_E, 0 < P_max < 2^31.
+ */
+moe_status moe_grouped_gemm(const moe_bf16 *a, const moe_bf16 *w, const int32_t *expert_counts,
+                            const int32_t *expert_offsets, int32_t E, int32_t K, int32_t N, int64_t P_max,
+                            moe_bf16 *c, moe_stream_t stream);
+
+/*
+ * SwiGLU on saved gate/up rows, gu = [g | u] ([P_max, 2I], g the first I columns):
+ *   moe_swiglu:           h[p, i] = bf16_rne(silu(g) u)
+ *   moe_swiglu_backward:  dgu[p, i] = bf16_rne(dh u silu'(g)),  dgu[p, I+i] = bf16_rne(dh silu(g)),
+ *                         silu'(g) = s (1 + g (1 - s)),  s = sigmoid(g)
+ * over the rows p < offsets[E] (fp32 arithmetic); h, dh [P_max, I].  I % 64 == 0.
+ */
+moe_status moe_swiglu(const moe_bf16 *gu, const int32_t *expert_offsets, int32_t E, int32_t I,
+                      int64_t P_max, moe_bf16 *h, moe_stream_t stream);
+moe_status moe_swiglu_backward(const moe_bf16 *dh, const moe_bf16 *gu, const int32_t *expert_offsets,
+                               int32_t E, int32_t I, int64_t P_max, moe_bf16 *dgu, moe_stream_t stream);
+
+/*
+ * Expert weight transpose, once per weight update: wt[e, c, r] = w[e, r, c].
+ *   w [E, R, C] bf16;  wt [E, C, R] bf16 out.  R % 64 == 0, C % 64 == 0.
+ */
+moe_status moe_transpose_experts(const moe_bf16 *w, int64_t E, int32_t R, int32_t C, moe_bf16 *wt,
+                                 moe_stream_t stream);
+
+/*
+ * Backward of the combine [prime-rl, Changes: gathers in backward too]:
+ *   dw[t, j] = sum_c dout[t, c] y[route_row[t*k+j], c]          (fp32; fixed order)
+ *   dy[route_row[t*k+j], c] = bf16_rne(topk_w[t, j] dout[t, c])
+ *   dy[p, :] = 0 for every pad row p < offsets[E] (row_token[p] == -1)
+ *   dout [T, H] bf16;  y [P_max, H] bf16;  dy [P_max, H] bf16 out;  dw [T, k] fp32 out
+ *   route_row, topk_w, row_token, expert_offsets as from the forward.
+ * Shapes: H % 64 == 0, 1 <= k <= min(E, MOE_MAX_K), 0 < P_max < 2^31.
+ */
+moe_status moe_combine_backward(const moe_bf16 *dout, const moe_bf16 *y, const int32_t *route_row,
+                                const float *topk_w, const int32_t *row_token,
+                                const int32_t *expert_offsets, int64_t T, int32_t H, int32_t E, int32_t k,
+                                int64_t P_max, moe_bf16 *dy, float *dw, moe_stream_t stream);
+
+/*
+ * Backward of the routing softmax (over the k selected logits):
+ *   dlogits[t, topk_idx[t, j]] = topk_w[t, j] (dw[t, j] - sum_i topk_w[t, i] dw[t, i]),
+ *   dlogits[t, e] = 0 for every expert not selected.   dlogits [T, E] fp32 out.
+ */
+moe_status moe_route_backward(const int32_t *topk_idx, const float *topk_w, const float *dw, int64_t T,
+                              int32_t E, int32_t k, float *dlogits, moe_stream_t stream);
+
+/*
+ * Backward of the permute: dx[t, c] = bf16_rne( sum_j dx_perm[route_row[t*k+j], c] ),
+ * summed in fp32 in ascending j (the combine's gather with unit weights).
+ *   dx_perm [P_max, H] bf16;  dx [T, H] bf16 out.  Shapes as for moe_combine.
+ */
+moe_status moe_permute_backward(const moe_bf16 *dx_perm, const int32_t *route_row, int64_t T, int32_t H,
+                                int32_t k, int64_t P_max, moe_bf16 *dx, moe_stream_t stream);
+
+/*
+ * Expert weight gradients, K-grouped over each expert's padded segment [prime-rl,
+ * Changes: one K-grouped GEMM per weight; weight gradients into fp32]:
+ *   dw[e, m, n] = sum over rows p of e's segment of a[p, m] b[p, n]   (fp32 out)
+ *   a [P_max, M] bf16 (pad rows must be zero: dy and dgu from this recipe are);
+ *   b [P_max, N] bf16, or with row_token non-NULL the token matrix x [T, N] read as
+ *   b[p] = x[row_token[p]] (a zero row where row_token[p] == -1);
+ *   dw [E, M, N] fp32 out; an expert with no rows gets zeros.
+ *   dW_down: a = dy, b = h (M = H, N = I).  dW_gate_up: a = dgu, b = x_perm (M = 2I, N = H).
+ * Shapes: M % 64 == 0, N % 64 == 0, 1 <= E <= MOE_MAX_E, 0 < P_max < 2^31.
+ */
+moe_status moe_grouped_wgrad(const moe_bf16 *a, const moe_bf16 *b, const int32_t *row_token,
+                             const int32_t *expert_counts, const int32_t *expert_offsets, int32_t E,
+                             int32_t M, int32_t N, int64_t P_max, float *dw, moe_stream_t stream);
 
 #ifdef __cplusplus
 }

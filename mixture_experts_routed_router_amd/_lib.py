@@ -66,10 +66,22 @@ def load():
                                                      _c_i32, _c_i32, _c_i32, _c_i64, _c_vp, _c_vp]
     lib.moe_grouped_down_gemm_fp8w.argtypes = [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32,
                                                _c_i32, _c_i64, _c_vp, _c_vp]
+    lib.moe_grouped_gemm.argtypes = [_c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i64, _c_vp, _c_vp]
+    lib.moe_swiglu.argtypes = [_c_vp, _c_vp, _c_i32, _c_i32, _c_i64, _c_vp, _c_vp]
+    lib.moe_swiglu_backward.argtypes = [_c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i64, _c_vp, _c_vp]
+    lib.moe_transpose_experts.argtypes = [_c_vp, _c_i64, _c_i32, _c_i32, _c_vp, _c_vp]
+    lib.moe_combine_backward.argtypes = [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i32, _c_i32,
+                                         _c_i32, _c_i64, _c_vp, _c_vp, _c_vp]
+    lib.moe_route_backward.argtypes = [_c_vp, _c_vp, _c_vp, _c_i64, _c_i32, _c_i32, _c_vp, _c_vp]
+    lib.moe_permute_backward.argtypes = [_c_vp, _c_vp, _c_i64, _c_i32, _c_i32, _c_i64, _c_vp, _c_vp]
+    lib.moe_grouped_wgrad.argtypes = [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i64,
+                                      _c_vp, _c_vp]
     for fn in ("moe_permute_workspace_size", "moe_route_topk", "moe_permute",
                "moe_grouped_glu_gemm", "moe_grouped_glu_gemm_gather", "moe_grouped_down_gemm",
                "moe_combine", "moe_quantize_fp8", "moe_grouped_glu_gemm_fp8w",
-               "moe_grouped_glu_gemm_gather_fp8w", "moe_grouped_down_gemm_fp8w"):
+               "moe_grouped_glu_gemm_gather_fp8w", "moe_grouped_down_gemm_fp8w", "moe_grouped_gemm",
+               "moe_swiglu", "moe_swiglu_backward", "moe_transpose_experts", "moe_combine_backward",
+               "moe_route_backward", "moe_permute_backward", "moe_grouped_wgrad"):
         getattr(lib, fn).restype = ctypes.c_int
     _LIB = lib
     return lib
@@ -351,6 +363,155 @@ class MoELayer:
         down(self.h, w_down, L.counts, L.offsets, y=self.y, stream=stream)
         combine(self.y, L.route_row, self.topk_w, out=self.out, stream=stream)
         return self.out
+
+
+# ---- training: forward with saved gate/up output, and the backward -------------------
+
+def grouped_gemm(a, w, counts, offsets, c=None, stream=None):
+    """c[p] = a[p] w[e]^T on each expert's padded segment; w [E, N, K]."""
+    P_max, K = a.shape
+    E, N, K2 = w.shape
+    if K2 != K:
+        raise ValueError("w must be [E, N, K] with K = a.shape[1]")
+    if c is None:
+        c = torch.empty((P_max, N), dtype=torch.bfloat16, device=a.device)
+    _call("moe_grouped_gemm", _ptr(a, torch.bfloat16, "a"), _ptr(w, torch.bfloat16, "w"),
+          _ptr(counts, torch.int32, "counts", (E,)), _ptr(offsets, torch.int32, "offsets", (E + 1,)),
+          E, K, N, P_max, _ptr(c, torch.bfloat16, "c", (P_max, N)), _stream(stream))
+    return c
+
+
+def swiglu(gu, offsets, h=None, stream=None):
+    P_max, two_i = gu.shape
+    E = offsets.shape[0] - 1
+    if h is None:
+        h = torch.empty((P_max, two_i // 2), dtype=torch.bfloat16, device=gu.device)
+    _call("moe_swiglu", _ptr(gu, torch.bfloat16, "gu"), _ptr(offsets, torch.int32, "offsets", (E + 1,)), E,
+          two_i // 2, P_max, _ptr(h, torch.bfloat16, "h", (P_max, two_i // 2)), _stream(stream))
+    return h
+
+
+def swiglu_backward(dh, gu, offsets, dgu=None, stream=None):
+    P_max, I = dh.shape
+    E = offsets.shape[0] - 1
+    if dgu is None:
+        dgu = torch.empty((P_max, 2 * I), dtype=torch.bfloat16, device=dh.device)
+    _call("moe_swiglu_backward", _ptr(dh, torch.bfloat16, "dh"), _ptr(gu, torch.bfloat16, "gu", (P_max, 2 * I)),
+          _ptr(offsets, torch.int32, "offsets", (E + 1,)), E, I, P_max,
+          _ptr(dgu, torch.bfloat16, "dgu", (P_max, 2 * I)), _stream(stream))
+    return dgu
+
+
+def transpose_experts(w, wt=None, stream=None):
+    """wt [E, C, R] = w [E, R, C] transposed per expert (once per weight update)."""
+    E, R, C = w.shape
+    if wt is None:
+        wt = torch.empty((E, C, R), dtype=torch.bfloat16, device=w.device)
+    _call("moe_transpose_experts", _ptr(w, torch.bfloat16, "w"), E, R, C,
+          _ptr(wt, torch.bfloat16, "wt", (E, C, R)), _stream(stream))
+    return wt
+
+
+def combine_backward(dout, y, route_row, topk_w, row_token, offsets, dy=None, dw=None, stream=None):
+    T, H = dout.shape
+    P_max = y.shape[0]
+    k = topk_w.shape[1]
+    E = offsets.shape[0] - 1
+    if dy is None:
+        dy = torch.empty((P_max, H), dtype=torch.bfloat16, device=y.device)
+    if dw is None:
+        dw = torch.empty((T, k), dtype=torch.float32, device=y.device)
+    _call("moe_combine_backward", _ptr(dout, torch.bfloat16, "dout"), _ptr(y, torch.bfloat16, "y", (P_max, H)),
+          _ptr(route_row, torch.int32, "route_row", (T * k,)), _ptr(topk_w, torch.float32, "topk_w", (T, k)),
+          _ptr(row_token, torch.int32, "row_token", (P_max,)), _ptr(offsets, torch.int32, "offsets", (E + 1,)),
+          T, H, E, k, P_max, _ptr(dy, torch.bfloat16, "dy", (P_max, H)), _ptr(dw, torch.float32, "dw", (T, k)),
+          _stream(stream))
+    return dy, dw
+
+
+def route_backward(topk_idx, topk_w, dw, E: int, dlogits=None, stream=None):
+    T, k = topk_idx.shape
+    if dlogits is None:
+        dlogits = torch.empty((T, E), dtype=torch.float32, device=dw.device)
+    _call("moe_route_backward", _ptr(topk_idx, torch.int32, "topk_idx"), _ptr(topk_w, torch.float32, "topk_w", (T, k)),
+          _ptr(dw, torch.float32, "dw", (T, k)), T, E, k, _ptr(dlogits, torch.float32, "dlogits", (T, E)),
+          _stream(stream))
+    return dlogits
+
+
+def permute_backward(dx_perm, route_row, T: int, k: int, dx=None, stream=None):
+    P_max, H = dx_perm.shape
+    if dx is None:
+        dx = torch.empty((T, H), dtype=torch.bfloat16, device=dx_perm.device)
+    _call("moe_permute_backward", _ptr(dx_perm, torch.bfloat16, "dx_perm"),
+          _ptr(route_row, torch.int32, "route_row", (T * k,)), T, H, k, P_max,
+          _ptr(dx, torch.bfloat16, "dx", (T, H)), _stream(stream))
+    return dx
+
+
+def grouped_wgrad(a, b, counts, offsets, row_token=None, dw=None, stream=None):
+    """dw [E, M, N] fp32 = sum over each expert's padded segment of a[p]^T b[p]; with
+    row_token, b is the token matrix read as b[p] = x[row_token[p]]."""
+    P_max, M = a.shape
+    N = b.shape[1]
+    E = counts.shape[0]
+    if dw is None:
+        dw = torch.empty((E, M, N), dtype=torch.float32, device=a.device)
+    _call("moe_grouped_wgrad", _ptr(a, torch.bfloat16, "a"), _ptr(b, torch.bfloat16, "b"),
+          _ptr(row_token, torch.int32, "row_token", (P_max,)) if row_token is not None else None,
+          _ptr(counts, torch.int32, "counts", (E,)), _ptr(offsets, torch.int32, "offsets", (E + 1,)),
+          E, M, N, P_max, _ptr(dw, torch.float32, "dw", (E, M, N)), _stream(stream))
+    return dw
+
+
+class MoETrainingLayer:
+    """Forward that keeps what the backward needs (x_perm, gu = [g | u], h, y), and
+    the backward: dx, dlogits and fp32 weight gradients. All buffers are
+    preallocated; forward() and backward() only enqueue library calls.
+    The backward takes the weights transposed once per update (transpose_experts)."""
+
+    def __init__(self, T: int, H: int, E: int, k: int, I: int, align: int = 32, device="cuda"):
+        self.T, self.H, self.E, self.k, self.I, self.align = T, H, E, k, I, align
+        self.P_max = padded_rows_max(T, k, E, align)
+        dev = torch.device(device)
+        bf = dict(dtype=torch.bfloat16, device=dev)
+        f32 = dict(dtype=torch.float32, device=dev)
+        self.topk_idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+        self.topk_w = torch.empty((T, k), **f32)
+        self.layout = alloc_layout(T, H, E, k, self.P_max, dev)
+        self.workspace = torch.empty(max(permute_workspace_size(T, k, E), 256), dtype=torch.uint8, device=dev)
+        P = self.P_max
+        self.gu, self.h, self.y = torch.empty((P, 2 * I), **bf), torch.empty((P, I), **bf), torch.empty((P, H), **bf)
+        self.out = torch.empty((T, H), **bf)
+        self.dy, self.dh = torch.empty((P, H), **bf), torch.empty((P, I), **bf)
+        self.dgu, self.dx_perm = torch.empty((P, 2 * I), **bf), torch.empty((P, H), **bf)
+        self.dw, self.dlogits = torch.empty((T, k), **f32), torch.empty((T, E), **f32)
+        self.dx = torch.empty((T, H), **bf)
+        self.dw_gu, self.dw_d = torch.empty((E, 2 * I, H), **f32), torch.empty((E, H, I), **f32)
+
+    def forward(self, x, logits, w_gate_up, w_down, stream=None):
+        route_topk(logits, self.k, self.topk_idx, self.topk_w, stream=stream)
+        L = permute(x, self.topk_idx, self.E, self.align, self.P_max, out=self.layout, workspace=self.workspace,
+                    stream=stream)
+        grouped_gemm(L.x_perm, w_gate_up, L.counts, L.offsets, c=self.gu, stream=stream)
+        swiglu(self.gu, L.offsets, h=self.h, stream=stream)
+        grouped_down_gemm(self.h, w_down, L.counts, L.offsets, y=self.y, stream=stream)
+        combine(self.y, L.route_row, self.topk_w, out=self.out, stream=stream)
+        return self.out
+
+    def backward(self, dout, w_gate_up_t, w_down_t, stream=None):
+        """w_gate_up_t [E, H, 2I] and w_down_t [E, I, H] from transpose_experts."""
+        L = self.layout
+        combine_backward(dout, self.y, L.route_row, self.topk_w, L.row_token, L.offsets, dy=self.dy, dw=self.dw,
+                         stream=stream)
+        route_backward(self.topk_idx, self.topk_w, self.dw, self.E, dlogits=self.dlogits, stream=stream)
+        grouped_gemm(self.dy, w_down_t, L.counts, L.offsets, c=self.dh, stream=stream)
+        swiglu_backward(self.dh, self.gu, L.offsets, dgu=self.dgu, stream=stream)
+        grouped_gemm(self.dgu, w_gate_up_t, L.counts, L.offsets, c=self.dx_perm, stream=stream)
+        permute_backward(self.dx_perm, L.route_row, self.T, self.k, dx=self.dx, stream=stream)
+        grouped_wgrad(self.dy, self.h, L.counts, L.offsets, dw=self.dw_d, stream=stream)
+        grouped_wgrad(self.dgu, L.x_perm, L.counts, L.offsets, dw=self.dw_gu, stream=stream)
+        return self.dx, self.dlogits, self.dw_gu, self.dw_d
 
 
 def moe_forward(x, logits, w_gate_up, w_down, k: int, align: int = 32):

@@ -20,6 +20,14 @@ hipError_t launch_grouped_down_gemm(const uint16_t*, const void*, const float*, 
 hipError_t launch_quantize_fp8(const uint16_t*, int64_t, int, int, uint8_t*, float*, hipStream_t);
 hipError_t launch_grouped_gemm_small(bool, const uint16_t*, const int32_t*, const void*, const float*,
                                      const int32_t*, int, int, int, uint16_t*, hipStream_t);
+hipError_t launch_combine_bwd(const uint16_t*, const uint16_t*, const int32_t*, const float*, const int32_t*,
+                              const int32_t*, int64_t, int, int, int, int64_t, uint16_t*, float*, hipStream_t);
+hipError_t launch_route_bwd(const int32_t*, const float*, const float*, int64_t, int, int, float*, hipStream_t);
+hipError_t launch_swiglu(const uint16_t*, const uint16_t*, const int32_t*, int, int, int64_t, uint16_t*,
+                         hipStream_t);
+hipError_t launch_transpose(const uint16_t*, int64_t, int, int, uint16_t*, hipStream_t);
+hipError_t launch_wgrad(const uint16_t*, const uint16_t*, const int32_t*, const int32_t*, int, int, int, float*,
+                        hipStream_t);
 hipError_t launch_combine(const uint16_t*, const int32_t*, const float*, int64_t, int, int,
                           int64_t, uint16_t*, hipStream_t);
 }  // namespace moe
@@ -301,6 +309,129 @@ moe_status moe_grouped_down_gemm_fp8w(const moe_bf16* h, const uint8_t* w8_down,
     return hip_status(launch_down(h, w8_down, scale_down, expert_offsets, E, H, I, P_max, y,
                                   (hipStream_t)stream),
                       "moe_grouped_down_gemm_fp8w launch");
+}
+
+moe_status moe_grouped_gemm(const moe_bf16* a, const moe_bf16* w, const int32_t* expert_counts,
+                            const int32_t* expert_offsets, int32_t E, int32_t K, int32_t N, int64_t P_max,
+                            moe_bf16* c, moe_stream_t stream) {
+    // the down GEMM's kernel is the plain grouped GEMM: (H, I) = (N, K)
+    moe_status s = check_gemm(a, w, expert_counts, expert_offsets, E, N, K, P_max, c);
+    if (s != MOE_OK) return s;
+    return hip_status(launch_down(a, w, nullptr, expert_offsets, E, N, K, P_max, c, (hipStream_t)stream),
+                      "moe_grouped_gemm launch");
+}
+
+static moe_status check_swiglu(const int32_t* offsets, int32_t E, int32_t I, int64_t P_max) {
+    REQUIRE_PTR(offsets);
+    if (E < 1 || E > MOE_MAX_E) return fail(MOE_ERR_INVALID_SHAPE, "E=%d outside [1, %d]", E, MOE_MAX_E);
+    moe_status s;
+    if ((s = check_dim64("I", I)) != MOE_OK) return s;
+    return check_pmax(P_max);
+}
+
+moe_status moe_swiglu(const moe_bf16* gu, const int32_t* expert_offsets, int32_t E, int32_t I,
+                      int64_t P_max, moe_bf16* h, moe_stream_t stream) {
+    REQUIRE_PTR(gu);
+    REQUIRE_PTR(h);
+    moe_status s = check_swiglu(expert_offsets, E, I, P_max);
+    if (s != MOE_OK) return s;
+    return hip_status(moe::launch_swiglu(gu, nullptr, expert_offsets, E, I, P_max, h, (hipStream_t)stream),
+                      "moe_swiglu launch");
+}
+
+moe_status moe_swiglu_backward(const moe_bf16* dh, const moe_bf16* gu, const int32_t* expert_offsets,
+                               int32_t E, int32_t I, int64_t P_max, moe_bf16* dgu, moe_stream_t stream) {
+    REQUIRE_PTR(dh);
+    REQUIRE_PTR(gu);
+    REQUIRE_PTR(dgu);
+    moe_status s = check_swiglu(expert_offsets, E, I, P_max);
+    if (s != MOE_OK) return s;
+    return hip_status(moe::launch_swiglu(gu, dh, expert_offsets, E, I, P_max, dgu, (hipStream_t)stream),
+                      "moe_swiglu_backward launch");
+}
+
+moe_status moe_transpose_experts(const moe_bf16* w, int64_t E, int32_t R, int32_t C, moe_bf16* wt,
+                                 moe_stream_t stream) {
+    REQUIRE_PTR(w);
+    REQUIRE_PTR(wt);
+    if (E < 1 || E > ((int64_t)1 << 20)) return fail(MOE_ERR_INVALID_SHAPE, "E=%lld outside [1, 2^20]", (long long)E);
+    moe_status s;
+    if ((s = check_dim64("R", R)) != MOE_OK) return s;
+    if ((s = check_dim64("C", C)) != MOE_OK) return s;
+    if (E * (R / 64) * (C / 64) >= ((int64_t)1 << 31))
+        return fail(MOE_ERR_SIZE_OVERFLOW, "E*R*C/4096 tiles reach 2^31");
+    return hip_status(moe::launch_transpose(w, E, R, C, wt, (hipStream_t)stream), "moe_transpose_experts launch");
+}
+
+moe_status moe_combine_backward(const moe_bf16* dout, const moe_bf16* y, const int32_t* route_row,
+                                const float* topk_w, const int32_t* row_token, const int32_t* expert_offsets,
+                                int64_t T, int32_t H, int32_t E, int32_t k, int64_t P_max, moe_bf16* dy,
+                                float* dw, moe_stream_t stream) {
+    REQUIRE_PTR_UNLESS_EMPTY(dout, T == 0);
+    REQUIRE_PTR(y);
+    REQUIRE_PTR_UNLESS_EMPTY(route_row, T == 0);
+    REQUIRE_PTR_UNLESS_EMPTY(topk_w, T == 0);
+    REQUIRE_PTR(row_token);
+    REQUIRE_PTR(expert_offsets);
+    REQUIRE_PTR(dy);
+    REQUIRE_PTR_UNLESS_EMPTY(dw, T == 0);
+    if (T < 0 || T >= ((int64_t)1 << 31)) return fail(MOE_ERR_INVALID_SHAPE, "T=%lld outside [0, 2^31)", (long long)T);
+    moe_status s = check_ek(E, k);
+    if (s != MOE_OK) return s;
+    if ((s = check_dim64("H", H)) != MOE_OK) return s;
+    if ((s = check_pmax(P_max)) != MOE_OK) return s;
+    return hip_status(moe::launch_combine_bwd(dout, y, route_row, topk_w, row_token, expert_offsets, T, H, k, E,
+                                              P_max, dy, dw, (hipStream_t)stream),
+                      "moe_combine_backward launch");
+}
+
+moe_status moe_route_backward(const int32_t* topk_idx, const float* topk_w, const float* dw, int64_t T,
+                              int32_t E, int32_t k, float* dlogits, moe_stream_t stream) {
+    REQUIRE_PTR_UNLESS_EMPTY(topk_idx, T == 0);
+    REQUIRE_PTR_UNLESS_EMPTY(topk_w, T == 0);
+    REQUIRE_PTR_UNLESS_EMPTY(dw, T == 0);
+    REQUIRE_PTR_UNLESS_EMPTY(dlogits, T == 0);
+    if (T < 0 || T >= ((int64_t)1 << 31)) return fail(MOE_ERR_INVALID_SHAPE, "T=%lld outside [0, 2^31)", (long long)T);
+    moe_status s = check_ek(E, k);
+    if (s != MOE_OK) return s;
+    return hip_status(moe::launch_route_bwd(topk_idx, topk_w, dw, T, E, k, dlogits, (hipStream_t)stream),
+                      "moe_route_backward launch");
+}
+
+moe_status moe_permute_backward(const moe_bf16* dx_perm, const int32_t* route_row, int64_t T, int32_t H,
+                                int32_t k, int64_t P_max, moe_bf16* dx, moe_stream_t stream) {
+    // the combine kernel with every weight 1
+    REQUIRE_PTR(dx_perm);
+    REQUIRE_PTR_UNLESS_EMPTY(route_row, T == 0);
+    REQUIRE_PTR_UNLESS_EMPTY(dx, T == 0);
+    if (T < 0 || T >= ((int64_t)1 << 31)) return fail(MOE_ERR_INVALID_SHAPE, "T=%lld outside [0, 2^31)", (long long)T);
+    if (k < 1 || k > MOE_MAX_K) return fail(MOE_ERR_INVALID_SHAPE, "k=%d outside [1, %d]", k, MOE_MAX_K);
+    moe_status s;
+    if ((s = check_dim64("H", H)) != MOE_OK) return s;
+    if ((s = check_pmax(P_max)) != MOE_OK) return s;
+    return hip_status(moe::launch_combine(dx_perm, route_row, nullptr, T, H, k, P_max, dx, (hipStream_t)stream),
+                      "moe_permute_backward launch");
+}
+
+moe_status moe_grouped_wgrad(const moe_bf16* a, const moe_bf16* b, const int32_t* row_token,
+                             const int32_t* expert_counts, const int32_t* expert_offsets, int32_t E, int32_t M,
+                             int32_t N, int64_t P_max, float* dw, moe_stream_t stream) {
+    REQUIRE_PTR(a);
+    REQUIRE_PTR(b);
+    REQUIRE_PTR(expert_counts);
+    REQUIRE_PTR(expert_offsets);
+    REQUIRE_PTR(dw);
+    if (row_token && !aligned16(row_token))
+        return fail(MOE_ERR_MISALIGNED_POINTER, "row_token is not 16-byte aligned");
+    if (E < 1 || E > MOE_MAX_E) return fail(MOE_ERR_INVALID_SHAPE, "E=%d outside [1, %d]", E, MOE_MAX_E);
+    moe_status s;
+    if ((s = check_dim64("M", M)) != MOE_OK) return s;
+    if ((s = check_dim64("N", N)) != MOE_OK) return s;
+    if ((s = check_pmax(P_max)) != MOE_OK) return s;
+    const int64_t tiles = (int64_t)E * ((M + 127) / 128) * ((N + 127) / 128);
+    if (tiles >= ((int64_t)1 << 31)) return fail(MOE_ERR_SIZE_OVERFLOW, "E*M*N/16384 tiles reach 2^31");
+    return hip_status(moe::launch_wgrad(a, b, row_token, expert_offsets, E, M, N, dw, (hipStream_t)stream),
+                      "moe_grouped_wgrad launch");
 }
 
 moe_status moe_combine(const moe_bf16* y, const int32_t* route_row, const float* topk_w, int64_t T,

@@ -1,0 +1,225 @@
+// backward.hip -- the memory-bound steps of the backward pass, and the saved
+// SwiGLU of the training forward.
+//
+// Backward of the path [prime-rl PR 3885, Changes: the single-pass layout gathers
+// in backward too; the forward keeps the gate/up output so that the backward
+// does not recompute it]. With dout = dL/dout [T, H]:
+//   combine    dw[t,j] = <dout[t], y[route_row[t*k+j]]>;  dy[route_row[t*k+j]] =
+//              w[t,j] dout[t]; every pad row of a segment is zeroed, so the K-grouped
+//              weight-gradient GEMMs may sum over whole padded segments
+//   routing    dlogits[t, idx[t,j]] = w[t,j] (dw[t,j] - sum_i w[t,i] dw[t,i]), 0 for
+//              the experts not selected (softmax over the selected logits)
+//   SwiGLU     forward h = silu(g) u from gu = [g | u]; backward dgu = [dh u silu'(g) |
+//              dh silu(g)], silu'(g) = s (1 + g (1 - s)), s = sigmoid(g)
+//   transpose  expert weights [E, R, C] -> [E, C, R] once per weight update, so
+//              the input-gradient GEMMs are the forward's grouped GEMM
+// fp32 arithmetic, bf16 storage (rounded to nearest even), fp32 dw and dlogits.
+// Every reduction runs in a fixed order (no atomics): results are deterministic.
+#include "common.hpp"
+
+namespace moe {
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+// ---- combine backward: one wavefront per token, its k routes in ascending j ----
+__global__ __launch_bounds__(256) void combine_bwd_kernel(const uint4* __restrict__ dout,
+                                                          const uint4* __restrict__ y,
+                                                          const int32_t* __restrict__ route_row,
+                                                          const float* __restrict__ topk_w, int64_t T,
+                                                          int pieces, int k, uint4* __restrict__ dy,
+                                                          float* __restrict__ dw) {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int64_t t = (int64_t)blockIdx.x * 4 + wave;
+    if (t >= T) return;
+    const int lane = lane_id();
+    const uint4* g = dout + t * pieces;
+    for (int j = 0; j < k; ++j) {
+        const int64_t row = route_row[t * k + j];  // wave-uniform
+        const float w = topk_w[t * k + j];
+        float dot = 0.0f;
+        for (int c = lane; c < pieces; c += kWave) {
+            const uint4 gv = g[c], yv = y[row * pieces + c];
+            const uint32_t gp[4] = {gv.x, gv.y, gv.z, gv.w}, yp[4] = {yv.x, yv.y, yv.z, yv.w};
+            uint32_t o[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float g0 = bf16_lo(gp[q]), g1 = bf16_hi(gp[q]);
+                dot = fmaf(g0, bf16_lo(yp[q]), dot);
+                dot = fmaf(g1, bf16_hi(yp[q]), dot);
+                o[q] = pack_bf16x2(w * g0, w * g1);
+            }
+            dy[row * pieces + c] = make_uint4(o[0], o[1], o[2], o[3]);
+        }
+        dot = wave_sum(dot);
+        if (lane == 0) dw[t * k + j] = dot;
+    }
+}
+
+// Pad rows of the used layout (row_token == -1 below offsets[E]) -> 0.
+__global__ __launch_bounds__(256) void zero_pad_rows_kernel(const int32_t* __restrict__ row_token,
+                                                            const int32_t* __restrict__ offsets, int E,
+                                                            int64_t P_max, int pieces,
+                                                            uint4* __restrict__ dst) {
+    const int64_t used = offsets[E];
+    const int64_t n = (used < P_max ? used : P_max) * pieces;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t p = i / pieces;
+        if (row_token[p] < 0) dst[i] = make_uint4(0u, 0u, 0u, 0u);
+    }
+}
+
+// ---- routing backward: one wavefront per token ----
+__global__ __launch_bounds__(256) void route_bwd_kernel(const int32_t* __restrict__ topk_idx,
+                                                        const float* __restrict__ topk_w,
+                                                        const float* __restrict__ dw, int64_t T, int E,
+                                                        int k, float* __restrict__ dlogits) {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int64_t t = (int64_t)blockIdx.x * 4 + wave;
+    if (t >= T) return;
+    const int lane = lane_id();
+    const float wl = lane < k ? topk_w[t * k + lane] : 0.0f;
+    const float dl = lane < k ? dw[t * k + lane] : 0.0f;
+    const float s = wave_sum(wl * dl);
+    for (int e = lane; e < E; e += kWave) {
+        float v = 0.0f;
+        for (int j = 0; j < k; ++j)  // wave-uniform loads
+            if (topk_idx[t * k + j] == e) v = topk_w[t * k + j] * (dw[t * k + j] - s);
+        dlogits[t * E + e] = v;
+    }
+}
+
+// ---- SwiGLU forward (BWD false) and backward (BWD true) over used rows ----
+__device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
+
+template <bool BWD>
+__global__ __launch_bounds__(256) void swiglu_kernel(const uint4* __restrict__ gu, const uint4* __restrict__ dh,
+                                                     const int32_t* __restrict__ offsets, int E,
+                                                     int64_t P_max, int pieces_i, uint4* __restrict__ out) {
+    const int64_t used = offsets[E];
+    const int64_t n = (used < P_max ? used : P_max) * pieces_i;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t p = i / pieces_i;
+        const int c = (int)(i - p * pieces_i);
+        const uint4 gv = gu[p * 2 * pieces_i + c], uv = gu[p * 2 * pieces_i + pieces_i + c];
+        const uint32_t gp[4] = {gv.x, gv.y, gv.z, gv.w}, up[4] = {uv.x, uv.y, uv.z, uv.w};
+        if (!BWD) {
+            uint32_t o[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                o[q] = pack_bf16x2(silu_f(bf16_lo(gp[q])) * bf16_lo(up[q]),
+                                   silu_f(bf16_hi(gp[q])) * bf16_hi(up[q]));
+            out[i] = make_uint4(o[0], o[1], o[2], o[3]);
+        } else {
+            const uint4 dv = dh[i];
+            const uint32_t dp[4] = {dv.x, dv.y, dv.z, dv.w};
+            uint32_t og[4], ou[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                float dg[2], du[2];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const float g = h ? bf16_hi(gp[q]) : bf16_lo(gp[q]);
+                    const float u = h ? bf16_hi(up[q]) : bf16_lo(up[q]);
+                    const float d = h ? bf16_hi(dp[q]) : bf16_lo(dp[q]);
+                    const float sg = 1.0f / (1.0f + __expf(-g));
+                    dg[h] = d * u * (sg * (1.0f + g * (1.0f - sg)));
+                    du[h] = d * (g * sg);
+                }
+                og[q] = pack_bf16x2(dg[0], dg[1]);
+                ou[q] = pack_bf16x2(du[0], du[1]);
+            }
+            out[p * 2 * pieces_i + c] = make_uint4(og[0], og[1], og[2], og[3]);
+            out[p * 2 * pieces_i + pieces_i + c] = make_uint4(ou[0], ou[1], ou[2], ou[3]);
+        }
+    }
+}
+
+// ---- expert weight transpose [E, R, C] -> [E, C, R], 64x64 tiles through LDS ----
+__global__ __launch_bounds__(256) void transpose_kernel(const uint16_t* __restrict__ w, int R, int C,
+                                                        uint16_t* __restrict__ wt) {
+    __shared__ uint16_t tile[64][64 + 2];
+    const int tiles_c = C / 64, tiles_r = R / 64;
+    const int64_t b = blockIdx.x;
+    const int64_t e = b / ((int64_t)tiles_r * tiles_c);
+    const int rem = (int)(b - e * tiles_r * tiles_c);
+    const int r0 = (rem / tiles_c) * 64, c0 = (rem % tiles_c) * 64;
+    const uint16_t* src = w + e * R * C;
+    uint16_t* dst = wt + e * R * C;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int r = tid / 8 + 32 * i, cp = (tid % 8) * 8;
+        const uint4 v = *(const uint4*)(src + (int64_t)(r0 + r) * C + c0 + cp);
+        const uint32_t q[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            tile[r][cp + 2 * j] = (uint16_t)(q[j] & 0xffffu);
+            tile[r][cp + 2 * j + 1] = (uint16_t)(q[j] >> 16);
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int c = tid / 8 + 32 * i, rp = (tid % 8) * 8;
+        uint32_t q[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            q[j] = (uint32_t)tile[rp + 2 * j][c] | ((uint32_t)tile[rp + 2 * j + 1][c] << 16);
+        *(uint4*)(dst + (int64_t)(c0 + c) * R + r0 + rp) = make_uint4(q[0], q[1], q[2], q[3]);
+    }
+}
+
+static unsigned grid_for(int64_t n, int64_t cap) {
+    const int64_t g = (n + 255) / 256;
+    return (unsigned)(g < 1 ? 1 : (g > cap ? cap : g));
+}
+
+hipError_t launch_combine_bwd(const uint16_t* dout, const uint16_t* y, const int32_t* route_row,
+                              const float* topk_w, const int32_t* row_token, const int32_t* offsets,
+                              int64_t T, int H, int k, int E, int64_t P_max, uint16_t* dy, float* dw,
+                              hipStream_t stream) {
+    const int pieces = H / 8;
+    hipLaunchKernelGGL(zero_pad_rows_kernel, dim3(grid_for(P_max * pieces, 8192)), dim3(256), 0, stream,
+                       row_token, offsets, E, P_max, pieces, (uint4*)dy);
+    if (T > 0)
+        hipLaunchKernelGGL(combine_bwd_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, stream,
+                           (const uint4*)dout, (const uint4*)y, route_row, topk_w, T, pieces, k,
+                           (uint4*)dy, dw);
+    return hipGetLastError();
+}
+
+hipError_t launch_route_bwd(const int32_t* topk_idx, const float* topk_w, const float* dw, int64_t T, int E,
+                            int k, float* dlogits, hipStream_t stream) {
+    if (T == 0) return hipSuccess;
+    hipLaunchKernelGGL(route_bwd_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, stream, topk_idx,
+                       topk_w, dw, T, E, k, dlogits);
+    return hipGetLastError();
+}
+
+hipError_t launch_swiglu(const uint16_t* gu, const uint16_t* dh, const int32_t* offsets, int E, int I,
+                         int64_t P_max, uint16_t* out, hipStream_t stream) {
+    const int pi = I / 8;
+    const dim3 grid(grid_for(P_max * pi, 8192)), block(256);
+    if (dh)
+        hipLaunchKernelGGL(swiglu_kernel<true>, grid, block, 0, stream, (const uint4*)gu, (const uint4*)dh,
+                           offsets, E, P_max, pi, (uint4*)out);
+    else
+        hipLaunchKernelGGL(swiglu_kernel<false>, grid, block, 0, stream, (const uint4*)gu,
+                           (const uint4*)nullptr, offsets, E, P_max, pi, (uint4*)out);
+    return hipGetLastError();
+}
+
+hipError_t launch_transpose(const uint16_t* w, int64_t E, int R, int C, uint16_t* wt, hipStream_t stream) {
+    const int64_t blocks = E * (R / 64) * (C / 64);
+    if (blocks == 0) return hipSuccess;
+    hipLaunchKernelGGL(transpose_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, w, R, C, wt);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -7,6 +7,9 @@
 //
 // One wavefront per token; a lane owns two 16-byte pieces (8 columns each) per
 // pass and has all k row pieces of both in flight before it sums them.
+//
+// With topk_w NULL every weight is 1: the unweighted sum of a token's k layout
+// rows is the permute's backward (dx[t] = sum_j dx_perm[route_row[t*k+j]]).
 #include "common.hpp"
 
 namespace moe {
@@ -25,7 +28,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ 
     if (t >= T) return;
     const int lane = lane_id();
     const int32_t* rows = route_row + t * k;   // wave-uniform addresses: scalar loads
-    const float* ws = topk_w + t * k;
+    const float* ws = topk_w ? topk_w + t * k : nullptr;
     for (int c0 = lane; c0 < pieces_per_row; c0 += kWave * CP) {
         float acc[CP][8];
 #pragma unroll
@@ -41,7 +44,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ 
                 const int32_t row = j < k ? rows[j] : -1;
                 // a row outside [0, P_max) contributes nothing (never read)
                 const bool ok = row >= 0 && row < P_max;
-                w[jj] = ok ? ws[j] : 0.0f;
+                w[jj] = ok ? (ws ? ws[j] : 1.0f) : 0.0f;
 #pragma unroll
                 for (int u = 0; u < CP; ++u) {
                     const int c = c0 + u * kWave;

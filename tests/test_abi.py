@@ -45,6 +45,14 @@ def lib():
     lib.moe_grouped_down_gemm_fp8w.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i64, vp, vp]
     lib.moe_grouped_glu_gemm_gather_fp8w.argtypes = [vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i64,
                                                      vp, vp]
+    lib.moe_grouped_gemm.argtypes = [vp, vp, vp, vp, i32, i32, i32, i64, vp, vp]
+    lib.moe_swiglu.argtypes = [vp, vp, i32, i32, i64, vp, vp]
+    lib.moe_swiglu_backward.argtypes = [vp, vp, vp, i32, i32, i64, vp, vp]
+    lib.moe_transpose_experts.argtypes = [vp, i64, i32, i32, vp, vp]
+    lib.moe_combine_backward.argtypes = [vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i64, vp, vp, vp]
+    lib.moe_route_backward.argtypes = [vp, vp, vp, i64, i32, i32, vp, vp]
+    lib.moe_permute_backward.argtypes = [vp, vp, i64, i32, i32, i64, vp, vp]
+    lib.moe_grouped_wgrad.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i64, vp, vp]
     return lib
 
 
@@ -165,6 +173,26 @@ def test_fp8_gemm_validation(lib):
     assert fn(FAKE, FAKE, FAKE, None, FAKE, FAKE, 100, 8, 128, 256, 1000, FAKE, None) == NULLP
     assert fn(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 8, 128, 256, 1000, FAKE, None) == SHAPE
     assert fn(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, 8, 2048, 256, 1000, FAKE, None) == OVERFLOW
+
+
+def test_training_validation(lib):
+    assert lib.moe_grouped_gemm(FAKE, FAKE, FAKE, FAKE, 8, 128, 256, 1000, None, None) == NULLP
+    assert lib.moe_grouped_gemm(FAKE, FAKE, FAKE, FAKE, 8, 100, 256, 1000, FAKE, None) == SHAPE   # K % 64
+    assert lib.moe_swiglu(FAKE, FAKE, 4, 96, 100, FAKE, None) == SHAPE                             # I % 64
+    assert lib.moe_swiglu_backward(FAKE, None, FAKE, 4, 128, 100, FAKE, None) == NULLP
+    assert lib.moe_transpose_experts(FAKE, 2, 64, 100, FAKE, None) == SHAPE
+    assert lib.moe_transpose_experts(FAKE + 8, 2, 64, 64, FAKE, None) == MISALIGNED
+    assert lib.moe_combine_backward(FAKE, FAKE, FAKE, FAKE, None, FAKE, 4, 128, 8, 2, 100, FAKE, FAKE,
+                                    None) == NULLP                                                  # row_token
+    assert lib.moe_combine_backward(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 128, 8, 9, 100, FAKE, FAKE,
+                                    None) == SHAPE                                                  # k > E
+    assert lib.moe_route_backward(FAKE, FAKE, FAKE, 4, 8, 0, FAKE, None) == SHAPE
+    assert lib.moe_route_backward(None, None, None, 0, 8, 2, None, None) == OK                    # no tokens
+    assert lib.moe_permute_backward(FAKE, FAKE, 4, 130, 2, 100, FAKE, None) == SHAPE
+    assert lib.moe_grouped_wgrad(FAKE, FAKE, None, FAKE, FAKE, 8, 128, 96, 1000, FAKE, None) == SHAPE  # N % 64
+    assert lib.moe_grouped_wgrad(FAKE, FAKE, FAKE + 4, FAKE, FAKE, 8, 128, 128, 1000, FAKE,
+                                 None) == MISALIGNED
+    assert lib.moe_grouped_wgrad(FAKE, FAKE, None, FAKE, FAKE, 8, 128, 128, 1000, None, None) == NULLP
 
 
 def test_combine_validation(lib):

@@ -1,0 +1,263 @@
+"""GPU parity of the training path -- the forward that keeps its gate/up output and
+the backward -- through the C ABI, against the CPU oracle's backward (steps and
+per-token loop) on the same seeded inputs.  Tolerances as in gpu_util.py: one
+bf16 rounding per step is held to 2^-8 of the largest reference value; fp32
+outputs (dw, dlogits, weight gradients) and whole chains to the layer gate
+|gpu - ref| <= 1e-2 max|ref| + 1e-3."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mixture_experts_routed_router_amd import inputs as gen
+from gpu_util import assert_close_bf16, dev, dev_bf16, host_bits, host_f64, sample_tokens
+from test_gpu_parity import _many_counts, _rows_of, _synthetic_layout
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _close(gpu, ref, what):
+    """fp32 outputs: the layer gate, and a much tighter relative check (no bf16
+    rounding of the result itself)."""
+    gpu, ref = np.asarray(gpu, np.float64), np.asarray(ref, np.float64)
+    assert gpu.shape == ref.shape, (what, gpu.shape, ref.shape)
+    assert np.isfinite(gpu).all(), what
+    scale = float(np.max(np.abs(ref))) if ref.size else 0.0
+    err = float(np.max(np.abs(gpu - ref))) if ref.size else 0.0
+    assert err <= 1e-2 * scale + 1e-3, f"{what}: max|d| {err:.3e} vs max|ref| {scale:.3e}"
+    return err / scale if scale > 0 else 0.0
+
+
+def _layout(counts, align, extra=64):
+    counts, offsets = _synthetic_layout(counts, align)
+    E, P = len(counts), int(offsets[-1])
+    return counts, offsets, E, P, P + extra
+
+
+def _row_token_of(counts, offsets, P_max, T, seed):
+    """A row_token consistent with the layout: routed rows get tokens, pad rows -1."""
+    rt = np.full(P_max, -1, np.int32)
+    rows = _rows_of(counts, offsets)
+    rt[rows] = np.random.default_rng(seed).integers(0, T, size=len(rows))
+    return rt
+
+
+# --------------------------------------------------------------------------------------
+# single steps
+# --------------------------------------------------------------------------------------
+
+GG_CASES = [
+    # name, counts, align, K, N
+    ("gu_out", _many_counts(40, 300, 41), 32, 256, 512),
+    ("dgrad_dh", [0, 130, 257, 31, 64], 32, 512, 192),
+    ("dgrad_dx", [5, 0, 129, 3, 300], 8, 384, 256),
+    ("K2880_N640", [16, 9, 28, 0, 40], 32, 2880, 640),
+]
+
+
+@pytest.mark.parametrize("case", GG_CASES, ids=[c[0] for c in GG_CASES])
+def test_grouped_gemm_plain(gpu_lib, case):
+    name, counts, align, K, N = case
+    _say(f"plain grouped gemm {name}")
+    counts, offsets, E, P, P_max = _layout(counts, align)
+    rows = _rows_of(counts, offsets)
+    a = np.zeros((P_max, K), np.uint16)
+    a[rows] = gen.random_bf16((len(rows), K), seed=7)
+    w = gen.random_bf16((E, N, K), seed=8, std=0.02)
+    c = gpu_lib.grouped_gemm(dev_bf16(a), dev_bf16(w), dev(counts), dev(offsets))
+    torch.cuda.synchronize()
+    ref = oracle.down(gen.bf16_bits_to_f32(a).astype(np.float64), w, counts, offsets)
+    assert_close_bf16(host_f64(c[:P])[rows], ref[rows], f"c[{name}]")
+
+
+@pytest.mark.parametrize("E,R,C", [(1, 64, 64), (3, 128, 320), (2, 2880, 640)])
+def test_transpose_experts(gpu_lib, E, R, C):
+    w = gen.random_bf16((E, R, C), seed=R + C)
+    wt = gpu_lib.transpose_experts(dev_bf16(w))
+    torch.cuda.synchronize()
+    assert (host_bits(wt) == np.ascontiguousarray(np.transpose(w, (0, 2, 1)))).all()
+
+
+@pytest.mark.parametrize("P_used,I", [(96, 64), (1000, 768), (37 * 8, 2880)])
+def test_swiglu_forward_backward(gpu_lib, P_used, I):
+    E = 4
+    offsets = np.array([0, P_used // 4, P_used // 2, 3 * P_used // 4, P_used], np.int32)
+    P_max = P_used + 16
+    gu = gen.random_bf16((P_max, 2 * I), seed=I, std=2.0)
+    dh = gen.random_bf16((P_max, I), seed=I + 1)
+    h = gpu_lib.swiglu(dev_bf16(gu), dev(offsets))
+    dgu = gpu_lib.swiglu_backward(dev_bf16(dh), dev_bf16(gu), dev(offsets))
+    torch.cuda.synchronize()
+    gu64 = gen.bf16_bits_to_f32(gu[:P_used]).astype(np.float64)
+    dh64 = gen.bf16_bits_to_f32(dh[:P_used]).astype(np.float64)
+    assert_close_bf16(host_f64(h[:P_used]), oracle.swiglu(gu64), "h")
+    ref = oracle.swiglu_bwd(dh64, gu64)
+    got = host_f64(dgu[:P_used])
+    assert_close_bf16(got[:, :I], ref[:, :I], "dg")
+    assert_close_bf16(got[:, I:], ref[:, I:], "du")
+
+
+COMB_CASES = [(64, 128, 8, 2, 32), (300, 2880, 32, 4, 8), (257, 640, 512, 10, 1), (100, 64, 40, 32, 32)]
+
+
+@pytest.mark.parametrize("T,H,E,k,align", COMB_CASES)
+def test_combine_and_route_backward(gpu_lib, T, H, E, k, align):
+    _say(f"combine/route backward T={T} H={H} E={E} k={k} align={align}")
+    rng = np.random.default_rng(T + H)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    idx, w64 = oracle.route_topk(logits, k)
+    w32 = w64.astype(np.float32)
+    P_max = T * k + E * (align - 1)
+    counts, offsets, route_row, row_token = oracle.layout(idx, E, align, P_max)
+    y = gen.random_bf16((P_max, H), seed=11)
+    dout = gen.random_bf16((T, H), seed=12)
+    dy_init = np.full((P_max, H), 0x7fc0, np.uint16)   # NaN everywhere: pad rows must be overwritten
+    dy_d = dev_bf16(dy_init)
+    dy, dw = gpu_lib.combine_backward(dev_bf16(dout), dev_bf16(y), dev(route_row), dev(w32), dev(row_token),
+                                      dev(offsets), dy=dy_d)
+    dl = gpu_lib.route_backward(dev(idx), dev(w32), dw, E)
+    torch.cuda.synchronize()
+    f = lambda b: gen.bf16_bits_to_f32(b).astype(np.float64)  # noqa: E731
+    dy_ref, dw_ref = oracle.combine_bwd(f(dout), f(y), route_row, w32.astype(np.float64))
+    used = int(offsets[-1])
+    got = host_f64(dy[:used])
+    routed = route_row.reshape(-1)
+    assert_close_bf16(got[routed], dy_ref[routed], "dy")
+    pad = np.setdiff1d(np.arange(used), routed)
+    assert (host_bits(dy[:used])[pad] == 0).all(), "pad rows of dy must be zero"
+    _close(dw.cpu().numpy(), dw_ref, "dw")
+    # the routing backward on the GPU's own fp32 dw vs the oracle on the same dw
+    dw32 = dw.cpu().numpy().astype(np.float64)
+    _close(dl.cpu().numpy(), oracle.route_bwd(idx, w32.astype(np.float64), dw32, E), "dlogits")
+
+
+@pytest.mark.parametrize("T,H,E,k", [(64, 128, 8, 2), (300, 2880, 32, 4), (100, 64, 40, 32)])
+def test_permute_backward(gpu_lib, T, H, E, k):
+    logits = np.random.default_rng(T).standard_normal((T, E)).astype(np.float32)
+    idx, _ = oracle.route_topk(logits, k)
+    P_max = T * k + E * 31
+    counts, offsets, route_row, row_token = oracle.layout(idx, E, 32, P_max)
+    dxp = gen.random_bf16((P_max, H), seed=13)
+    dx = gpu_lib.permute_backward(dev_bf16(dxp), dev(route_row), T, k)
+    torch.cuda.synchronize()
+    ref = oracle.permute_bwd(gen.bf16_bits_to_f32(dxp).astype(np.float64), route_row, T, k)
+    assert_close_bf16(host_f64(dx), ref, "dx")
+
+
+WG_CASES = [
+    # name, counts, align, M, N
+    ("ragged_align32", [0, 1, 130, 257, 31, 64], 32, 192, 320),
+    ("align1_tails", [7, 1, 200, 0, 45], 1, 128, 128),
+    ("align8_many", _many_counts(30, 120, 44), 8, 64, 256),
+    ("M2880_N640", [16, 9, 28, 40], 32, 2880, 640),
+]
+
+
+@pytest.mark.parametrize("gather", [False, True], ids=["layout", "gather"])
+@pytest.mark.parametrize("case", WG_CASES, ids=[c[0] for c in WG_CASES])
+def test_grouped_wgrad(gpu_lib, case, gather):
+    name, counts, align, M, N = case
+    _say(f"wgrad {name} gather={gather}")
+    counts, offsets, E, P, P_max = _layout(counts, align)
+    rows = _rows_of(counts, offsets)
+    a = np.zeros((P_max, M), np.uint16)
+    a[rows] = gen.random_bf16((len(rows), M), seed=21)
+    if gather:
+        T = max(1, len(rows) // 2 + 5)
+        rt = _row_token_of(counts, offsets, P_max, T, seed=22)
+        x = gen.random_bf16((T, N), seed=23)
+        b_ref = oracle.gather(x, rt, rows=P_max)
+        dw = gpu_lib.grouped_wgrad(dev_bf16(a), dev_bf16(x), dev(counts), dev(offsets), row_token=dev(rt))
+    else:
+        b_ref = np.zeros((P_max, N), np.uint16)
+        b_ref[rows] = gen.random_bf16((len(rows), N), seed=24)
+        b_ref[np.setdiff1d(np.arange(P), rows)] = gen.random_bf16((P - len(rows), N), seed=25)  # pad rows of b: any value
+        dw = gpu_lib.grouped_wgrad(dev_bf16(a), dev_bf16(b_ref), dev(counts), dev(offsets))
+    torch.cuda.synchronize()
+    f = lambda b: gen.bf16_bits_to_f32(b).astype(np.float64)  # noqa: E731
+    ref = oracle.wgrad(f(a), f(b_ref), counts, offsets)
+    got = dw.cpu().numpy()
+    for e in range(E):
+        if counts[e] == 0:
+            assert (got[e] == 0).all(), f"expert {e} has no rows: its gradient must be zero"
+        else:
+            _close(got[e], ref[e], f"dW[{name}][{e}]")
+
+
+# --------------------------------------------------------------------------------------
+# the whole training step
+# --------------------------------------------------------------------------------------
+
+def _train(gpu_lib, d):
+    cfg = d["cfg"]
+    layer = gpu_lib.MoETrainingLayer(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.align)
+    w_gu, w_d = dev_bf16(d["w_gu"]), dev_bf16(d["w_d"])
+    out = layer.forward(dev_bf16(d["x"]), dev(d["logits"]), w_gu, w_d)
+    dout = gen.random_bf16((cfg.T, cfg.H), seed=cfg.seed + 500)
+    grads = layer.backward(dev_bf16(dout), gpu_lib.transpose_experts(w_gu), gpu_lib.transpose_experts(w_d))
+    torch.cuda.synchronize()
+    return layer, out, dout, grads
+
+
+TRAIN_SMALL = [
+    gen.CONFIGS["tiny"],
+    gen.CONFIGS["tiny"].with_(name="tiny_hot", weight_std=0.2, seed=10),
+    gen.MoEConfig("k1", 200, 256, 16, 1, 128, 21, "gaussian"),
+    gen.MoEConfig("align8", 333, 256, 24, 3, 320, 25, "gaussian", align=8),
+    gen.MoEConfig("sparse_experts", 12, 192, 64, 2, 128, 24, "gaussian"),
+    gen.MoEConfig("skewed_small", 2048, 256, 32, 4, 128, 26, "zipf"),
+]
+
+
+@pytest.mark.parametrize("cfg", TRAIN_SMALL, ids=[c.name for c in TRAIN_SMALL])
+def test_training_step_small(gpu_lib, cfg):
+    """Forward output and every gradient against the oracle's per-token backward."""
+    _say(f"training step {cfg.name}")
+    d = gen.make_inputs(cfg)
+    layer, out, dout, (dx, dl, dwgu, dwd) = _train(gpu_lib, d)
+    ref_out = oracle.forward(d["x"], d["logits"], d["w_gu"], d["w_d"], cfg.k)
+    assert_close_bf16(host_f64(out), ref_out, f"out[{cfg.name}]", tight=False)
+    f = lambda b: gen.bf16_bits_to_f32(b).astype(np.float64)  # noqa: E731
+    rdx, rdl, rdwgu, rdwd = oracle.backward(d["x"], d["logits"], d["w_gu"], d["w_d"], f(dout), cfg.k)
+    rels = [assert_close_bf16(host_f64(dx), rdx, f"dx[{cfg.name}]", tight=False),
+            _close(dl.cpu().numpy(), rdl, f"dlogits[{cfg.name}]"),
+            _close(dwgu.cpu().numpy(), rdwgu, f"dW_gu[{cfg.name}]"),
+            _close(dwd.cpu().numpy(), rdwd, f"dW_d[{cfg.name}]")]
+    _say(f"  {cfg.name}: max|d|/max|ref| dx {rels[0]:.2e} dlogits {rels[1]:.2e} "
+         f"dW_gu {rels[2]:.2e} dW_d {rels[3]:.2e}")
+
+
+def test_training_step_full_size_sampled(gpu_lib):
+    """30B-A3B shape: dx and dlogits of sampled tokens (a token's input gradients
+    depend on no other token), and the weight gradients of three experts (every
+    token routed to an expert is in its sum), against the oracle."""
+    cfg = gen.CONFIGS["qwen3_30b_a3b"]
+    _say("full-size training step: generating inputs")
+    d = gen.make_inputs(cfg)
+    _say("full-size training step: running")
+    layer, out, dout, (dx, dl, dwgu, dwd) = _train(gpu_lib, d)
+    f = lambda b: gen.bf16_bits_to_f32(b).astype(np.float64)  # noqa: E731
+    toks = sample_tokens(cfg.T, 48, cfg.seed)
+    rdx, rdl, _, _ = oracle.backward(d["x"][toks], d["logits"][toks], d["w_gu"], d["w_d"], f(dout[toks]), cfg.k)
+    assert_close_bf16(host_f64(dx)[toks], rdx, "dx[sampled]", tight=False)
+    _close(dl.cpu().numpy()[toks], rdl, "dlogits[sampled]")
+    idx, w = oracle.route_topk(d["logits"], cfg.k)
+    for e in (0, 61, cfg.E - 1):
+        tj = np.argwhere(idx == e)            # (token, slot) pairs routed to e, ascending token
+        t_e, j_e = tj[:, 0], tj[:, 1]
+        n = len(t_e)
+        counts1, offsets1 = np.array([n], np.int32), np.array([0, n], np.int32)
+        xr = d["x"][t_e]
+        gu = oracle.down(f(xr), d["w_gu"][e:e + 1], counts1, offsets1)   # [g | u] of these rows
+        h = oracle.swiglu(gu)
+        dy = w[t_e, j_e][:, None] * f(dout[t_e])
+        dh = oracle.gemm_nn(dy, d["w_d"][e:e + 1], counts1, offsets1)
+        dgu = oracle.swiglu_bwd(dh, gu)
+        _close(dwd.cpu().numpy()[e], oracle.wgrad(dy, h, counts1, offsets1)[0], f"dW_d[{e}]")
+        _close(dwgu.cpu().numpy()[e], oracle.wgrad(dgu, f(xr), counts1, offsets1)[0], f"dW_gu[{e}]")
