@@ -83,3 +83,30 @@ def step_work(T: int, H: int, E: int, k: int, I: int, P: int, active_experts: in
     )
     combine = StepWork("combine", 0.0, R * H * bf + R * (i32 + f32) + T * H * bf)
     return [route, permute, glu, down, combine]
+
+
+def training_work(T: int, H: int, E: int, k: int, I: int, P: int, active_experts: int):
+    """Per-kernel algorithmic work of one training step (forward that keeps its
+    gate/up output, then the backward), in launch order. Weight gradients are
+    fp32 (4 bytes per element), everything else as in step_work."""
+    R = T * k
+    bf, i32, f32 = 2, 4, 4
+    wgu = active_experts * 2 * I * H
+    wd = active_experts * H * I
+    maps = (2 * E + 1) * i32
+    fwd = step_work(T, H, E, k, I, P, active_experts)
+    route, permute, _, down, combine = fwd
+    return [
+        route, permute,
+        StepWork("gate_up_gemm", 4.0 * R * H * I, wgu * bf + P * H * bf + P * 2 * I * bf + maps),
+        StepWork("swiglu", 0.0, P * 2 * I * bf + P * I * bf),
+        down, combine,
+        StepWork("combine_backward", 0.0, T * H * bf + R * H * bf + P * H * bf + R * (2 * i32 + 2 * f32)),
+        StepWork("route_backward", 0.0, R * (i32 + 2 * f32) + T * E * f32),
+        StepWork("dgrad_down", 2.0 * R * H * I, wd * bf + P * H * bf + P * I * bf + maps),
+        StepWork("swiglu_backward", 0.0, P * I * bf + 2 * P * 2 * I * bf),
+        StepWork("dgrad_gate_up", 4.0 * R * H * I, wgu * bf + P * 2 * I * bf + P * H * bf + maps),
+        StepWork("permute_backward", 0.0, R * H * bf + R * i32 + T * H * bf),
+        StepWork("wgrad_down", 2.0 * R * H * I, P * H * bf + P * I * bf + wd * f32 + maps),
+        StepWork("wgrad_gate_up", 4.0 * R * H * I, P * 2 * I * bf + P * H * bf + wgu * f32 + maps),
+    ]
