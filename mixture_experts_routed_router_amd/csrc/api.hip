@@ -428,8 +428,8 @@ moe_status moe_grouped_wgrad(const moe_bf16* a, const moe_bf16* b, const int32_t
     if ((s = check_dim64("M", M)) != MOE_OK) return s;
     if ((s = check_dim64("N", N)) != MOE_OK) return s;
     if ((s = check_pmax(P_max)) != MOE_OK) return s;
-    const int64_t tiles = (int64_t)E * ((M + 127) / 128) * ((N + 127) / 128);
-    if (tiles >= ((int64_t)1 << 31)) return fail(MOE_ERR_SIZE_OVERFLOW, "E*M*N/16384 tiles reach 2^31");
+    const int64_t tiles = (int64_t)E * ((M + 255) / 256) * ((N + 255) / 256);
+    if (tiles >= ((int64_t)1 << 31)) return fail(MOE_ERR_SIZE_OVERFLOW, "E*M*N/65536 tiles reach 2^31");
     return hip_status(moe::launch_wgrad(a, b, row_token, expert_offsets, E, M, N, dw, (hipStream_t)stream),
                       "moe_grouped_wgrad launch");
 }

@@ -12,26 +12,43 @@
 // so each 32-row chunk is transposed on its way into LDS: a thread loads 16 bytes
 // (8 columns) of two consecutive rows and writes the 8 (row, row+1) pairs as
 // 32-bit words at [column][row], so the MFMA fragments (8 consecutive rows of
-// one column) are single 128-bit LDS reads. Tile 128 x 128 per workgroup of four
-// waves (2 x 2 waves of 64 x 64, v_mfma_f32_32x32x16_bf16), LDS double-buffered
-// with the next chunk's global loads in flight during the MFMAs. One workgroup
-// per (expert, tile); an expert with no rows writes zeros.
+// one column) are single 128-bit LDS reads. Tile 256 x 256 per workgroup of eight
+// waves (2 x 4 waves of 128 x 64, v_mfma_f32_32x32x16_bf16: 12 fragment reads per
+// 16 MFMAs; a 128 x 128 tile of four 64 x 64 waves read 8 per 8 and was bound by
+// LDS traffic). LDS is double-buffered, and the chunks' global loads go through
+// a ring of kWgDepth register slots, so the loads of the next kWgDepth chunks are
+// in flight during the MFMAs (one chunk ahead left every chunk waiting on its
+// loads). One workgroup per (expert, tile), tiles dealt to the XCDs in
+// contiguous runs so that an expert's tiles, which read the same rows, share an
+// L2; an expert with no rows writes zeros.
 #include "common.hpp"
 
 namespace moe {
 
-constexpr int kWgBM = 128, kWgBN = 128, kWgBK = 32;
+constexpr int kWgBM = 256, kWgBN = 256, kWgBK = 32;
+constexpr int kWgThreads = 512;
+constexpr int kWgDepth = 3;  // chunks of global loads in flight
+
+// Workgroup barrier after this wave's LDS accesses have completed. Unlike
+// __syncthreads() it does not wait for the global loads in flight (those land
+// in registers, and the compiler waits for each before its first use), so the
+// load ring stays full across barriers.
+__device__ __forceinline__ void wg_lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 constexpr int kWgStride = kWgBK + 8;  // bf16 per LDS row (80 bytes: 16-byte aligned, spreads banks)
 
 template <bool GATHER_B>
-__global__ __launch_bounds__(256) void wgrad_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
+__global__ __launch_bounds__(kWgThreads, 1) void wgrad_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
                                                     const int32_t* __restrict__ row_token,
                                                     const int32_t* __restrict__ offsets, int M, int N,
                                                     int tiles_m, int tiles_n, float* __restrict__ dW) {
     __shared__ __attribute__((aligned(16))) uint16_t at[2][kWgBM][kWgStride];
     __shared__ __attribute__((aligned(16))) uint16_t bt[2][kWgBN][kWgStride];
 
-    const int64_t b = blockIdx.x;
+    // XCD-aware order: block b runs on XCD b % 8; XCD x takes tiles
+    // [start_x, start_x + count_x) in order, count_x = blocks on XCD x
+    const int64_t nb = gridDim.x, bx = blockIdx.x % 8;
+    int64_t b = blockIdx.x / 8;
+    for (int x = 0; x < bx; ++x) b += (nb - x + 7) / 8;
     const int e = (int)(b / ((int64_t)tiles_m * tiles_n));
     const int rem = (int)(b - (int64_t)e * tiles_m * tiles_n);
     const int m0 = (rem / tiles_n) * kWgBM, n0 = (rem % tiles_n) * kWgBN;
@@ -39,37 +56,51 @@ __global__ __launch_bounds__(256) void wgrad_kernel(const uint16_t* __restrict__
     const int nchunks = (seg1 - seg0 + kWgBK - 1) / kWgBK;
 
     const int tid = threadIdx.x, lane = lane_id();
-    const int wave = tid / kWave, wm = wave >> 1, wn = wave & 1;
-    // staging: thread -> row pair (2pp, 2pp+1) of the chunk, 16-byte column piece cp
+    const int wave = tid / kWave, wm = wave >> 2, wn = wave & 3;
+    // staging: thread -> row pair (2pp, 2pp+1) of the chunk, 16-byte column piece cp (0..31)
     const int pp = tid & 15, cp = tid >> 4;
     const int ca = m0 + 8 * cp, cb = n0 + 8 * cp;
     const bool a_col = ca < M, b_col = cb < N;
 
-    u32x4_t ra[2], rb[2];
-    auto load = [&](int ch) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int p = seg0 + ch * kWgBK + 2 * pp + h;
-            const bool in = p < seg1;
-            ra[h] = (in && a_col) ? *(const u32x4_t*)(A + (int64_t)p * M + ca) : u32x4_t{0u, 0u, 0u, 0u};
-            int64_t rowb = p;
-            bool okb = in && b_col;
-            if (GATHER_B) {
-                const int32_t tk = in ? row_token[p] : -1;
-                okb = okb && tk >= 0;
-                rowb = tk;
-            }
-            rb[h] = okb ? *(const u32x4_t*)(B + rowb * N + cb) : u32x4_t{0u, 0u, 0u, 0u};
-        }
-    };
+    // Chunk ch's loads go to register slot ch % kWgDepth. The loads themselves are
+    // unconditional (a row past the segment, or a chunk past the last, reads the
+    // segment's first row; a column past the matrix reads column 0) and the values
+    // are zeroed when they are used, so no load sits under a branch and the
+    // compiler's waits keep the ring in flight. (Gathering B needs the token
+    // before its row can be read; that variant waits for it.)
+    u32x4_t ra[kWgDepth][2], rb[kWgDepth][2];
+    bool oka[kWgDepth][2], okb[kWgDepth][2];
+    const int ca_ld = a_col ? ca : 0, cb_ld = b_col ? cb : 0;
+#define MOE_WG_LOAD(slot, ch)                                                                     \
+    do {                                                                                          \
+        _Pragma("unroll") for (int h = 0; h < 2; ++h) {                                           \
+            const int p = seg0 + (ch) * kWgBK + 2 * pp + h;                                       \
+            const bool in = p < seg1;                                                             \
+            const int pl = in ? p : seg0;                                                         \
+            ra[slot][h] = *(const u32x4_t*)(A + (int64_t)pl * M + ca_ld);                         \
+            oka[slot][h] = in && a_col;                                                           \
+            if (GATHER_B) {                                                                       \
+                const int32_t tk = in ? row_token[p] : -1;                                        \
+                okb[slot][h] = in && b_col && tk >= 0;                                            \
+                rb[slot][h] = okb[slot][h] ? *(const u32x4_t*)(B + (int64_t)tk * N + cb)          \
+                                           : u32x4_t{0u, 0u, 0u, 0u};                             \
+            } else {                                                                              \
+                rb[slot][h] = *(const u32x4_t*)(B + (int64_t)pl * N + cb_ld);                     \
+                okb[slot][h] = in && b_col;                                                       \
+            }                                                                                     \
+        }                                                                                         \
+    } while (0)
     // (row 2pp, row 2pp+1) pairs of column 8cp+q as one 32-bit word at [8cp+q][2pp]
-    auto store = [&](int buf) {
+    auto store = [&](const u32x4_t (&ra2)[2], const u32x4_t (&rb2)[2], const bool (&oa)[2],
+                     const bool (&ob)[2], int buf) {
 #pragma unroll
         for (int d = 0; d < 4; ++d) {
-            const uint32_t alo = __builtin_amdgcn_perm(ra[1][d], ra[0][d], 0x05040100u);  // col 2d
-            const uint32_t ahi = __builtin_amdgcn_perm(ra[1][d], ra[0][d], 0x07060302u);  // col 2d+1
-            const uint32_t blo = __builtin_amdgcn_perm(rb[1][d], rb[0][d], 0x05040100u);
-            const uint32_t bhi = __builtin_amdgcn_perm(rb[1][d], rb[0][d], 0x07060302u);
+            const uint32_t a0 = oa[0] ? ra2[0][d] : 0u, a1 = oa[1] ? ra2[1][d] : 0u;
+            const uint32_t b0 = ob[0] ? rb2[0][d] : 0u, b1 = ob[1] ? rb2[1][d] : 0u;
+            const uint32_t alo = __builtin_amdgcn_perm(a1, a0, 0x05040100u);  // col 2d
+            const uint32_t ahi = __builtin_amdgcn_perm(a1, a0, 0x07060302u);  // col 2d+1
+            const uint32_t blo = __builtin_amdgcn_perm(b1, b0, 0x05040100u);
+            const uint32_t bhi = __builtin_amdgcn_perm(b1, b0, 0x07060302u);
             *(uint32_t*)&at[buf][8 * cp + 2 * d][2 * pp] = alo;
             *(uint32_t*)&at[buf][8 * cp + 2 * d + 1][2 * pp] = ahi;
             *(uint32_t*)&bt[buf][8 * cp + 2 * d][2 * pp] = blo;
@@ -77,52 +108,74 @@ __global__ __launch_bounds__(256) void wgrad_kernel(const uint16_t* __restrict__
         }
     };
 
-    floatx16_t acc[2][2];
+    floatx16_t acc[4][2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    if (nchunks > 0) {
-        load(0);
-        store(0);
-        __syncthreads();
-    }
     const int lrow = lane & 31, kh = 8 * (lane >> 5);
-    for (int ch = 0; ch < nchunks; ++ch) {
-        const int buf = ch & 1;
-        if (ch + 1 < nchunks) load(ch + 1);
+    if (nchunks > 0) {
+        // chunk 0 straight to LDS buffer 0; chunks 1 .. kWgDepth into their slots
+        MOE_WG_LOAD(0, 0);
+        store(ra[0], rb[0], oka[0], okb[0], 0);
 #pragma unroll
-        for (int ks = 0; ks < kWgBK / 16; ++ks) {
-            bf16x8_t fa[2], fb[2];
-#pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                fa[i] = *(const bf16x8_t*)&at[buf][wm * 64 + i * 32 + lrow][ks * 16 + kh];
-                fb[i] = *(const bf16x8_t*)&bt[buf][wn * 64 + i * 32 + lrow][ks * 16 + kh];
-            }
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
-        }
-        if (ch + 1 < nchunks) store(buf ^ 1);
-        __syncthreads();
+        for (int d = 1; d < kWgDepth; ++d) MOE_WG_LOAD(d, d);
+        MOE_WG_LOAD(0, kWgDepth);
+        wg_lds_barrier();
     }
+    // iteration ch: MFMAs on LDS buffer ch & 1; chunk ch+1 from its slot into the
+    // other buffer (free since the last barrier); that slot refilled with chunk
+    // ch+1+kWgDepth; one barrier. Full rounds of kWgDepth chunks run without
+    // branches (a branch inside the ring makes the compiler's waits drain it);
+    // the last partial round is guarded. Scheduling barriers keep each chunk's
+    // store where it is: hoisted to the top of a round, the stores of later
+    // chunks would wait there for loads issued only one chunk earlier.
+#define MOE_WG_CHUNK(d, ch)                                                                       \
+    do {                                                                                          \
+        const int buf_ = (ch) & 1;                                                                \
+        _Pragma("unroll") for (int ks = 0; ks < kWgBK / 16; ++ks) {                               \
+            bf16x8_t fa[4], fb[2];                                                                \
+            _Pragma("unroll") for (int i = 0; i < 4; ++i)                                         \
+                fa[i] = *(const bf16x8_t*)&at[buf_][wm * 128 + i * 32 + lrow][ks * 16 + kh];      \
+            _Pragma("unroll") for (int j = 0; j < 2; ++j)                                         \
+                fb[j] = *(const bf16x8_t*)&bt[buf_][wn * 64 + j * 32 + lrow][ks * 16 + kh];       \
+            _Pragma("unroll") for (int i = 0; i < 4; ++i)                                         \
+                _Pragma("unroll") for (int j = 0; j < 2; ++j)                                     \
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0); \
+        }                                                                                         \
+        constexpr int nxt_ = ((d) + 1) % kWgDepth;                                                \
+        __builtin_amdgcn_sched_barrier(0);                                                        \
+        store(ra[nxt_], rb[nxt_], oka[nxt_], okb[nxt_], buf_ ^ 1);                                \
+        MOE_WG_LOAD(nxt_, (ch) + 1 + kWgDepth);                                                   \
+        wg_lds_barrier();                                                                         \
+        __builtin_amdgcn_sched_barrier(0);                                                        \
+    } while (0)
+    static_assert(kWgDepth == 3, "the chunk loop below is unrolled for a ring of 3");
+    int ch0 = 0;
+    for (; ch0 + kWgDepth <= nchunks; ch0 += kWgDepth) {
+        MOE_WG_CHUNK(0, ch0);
+        MOE_WG_CHUNK(1, ch0 + 1);
+        MOE_WG_CHUNK(2, ch0 + 2);
+    }
+    if (ch0 < nchunks) MOE_WG_CHUNK(0, ch0);
+    if (ch0 + 1 < nchunks) MOE_WG_CHUNK(1, ch0 + 1);
+#undef MOE_WG_CHUNK
+#undef MOE_WG_LOAD
 
     // MFMA 32x32 output: lane l, register r -> row (r/4)*8 + (l/32)*4 + r%4, column l%32
     float* out = dW + (int64_t)e * M * N;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const int n = n0 + wn * 64 + j * 32 + lrow;
             if (n >= N) continue;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int m = m0 + wm * 64 + i * 32 + (r / 4) * 8 + (lane >> 5) * 4 + r % 4;
+                const int m = m0 + wm * 128 + i * 32 + (r / 4) * 8 + (lane >> 5) * 4 + r % 4;
                 if (m < M) out[(int64_t)m * N + n] = acc[i][j][r];
             }
         }
@@ -133,10 +186,10 @@ hipError_t launch_wgrad(const uint16_t* A, const uint16_t* B, const int32_t* row
     const int tm = (M + kWgBM - 1) / kWgBM, tn = (N + kWgBN - 1) / kWgBN;
     const int64_t blocks = (int64_t)E * tm * tn;
     if (row_token)
-        hipLaunchKernelGGL(wgrad_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream, A, B, row_token,
+        hipLaunchKernelGGL(wgrad_kernel<true>, dim3((unsigned)blocks), dim3(kWgThreads), 0, stream, A, B, row_token,
                            offsets, M, N, tm, tn, dW);
     else
-        hipLaunchKernelGGL(wgrad_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream, A, B,
+        hipLaunchKernelGGL(wgrad_kernel<false>, dim3((unsigned)blocks), dim3(kWgThreads), 0, stream, A, B,
                            (const int32_t*)nullptr, offsets, M, N, tm, tn, dW);
     return hipGetLastError();
 }
