@@ -108,12 +108,19 @@ def draw_x(cfg: MoEConfig) -> np.ndarray:
     return _normal_bf16(_rng(cfg.seed, _S_X), (cfg.T, cfg.H), 1.0)
 
 
+def draw_router_weight(cfg: MoEConfig) -> np.ndarray:
+    """The router weight W_r [H, E] fp32 ~ N(0, weight_std) (the one the
+    "projection" configs form their logits from)."""
+    rng = _rng(cfg.seed, _S_ROUTER)
+    return rng.standard_normal(size=(cfg.H, cfg.E), dtype=np.float32) * np.float32(cfg.weight_std)
+
+
 def draw_logits(cfg: MoEConfig, x_bits: np.ndarray | None = None) -> np.ndarray:
     rng = _rng(cfg.seed, _S_ROUTER)
     if cfg.router == "projection":
         if x_bits is None:
             x_bits = draw_x(cfg)
-        w_r = rng.standard_normal(size=(cfg.H, cfg.E), dtype=np.float32) * np.float32(cfg.weight_std)
+        w_r = draw_router_weight(cfg)
         # Router projection (outside the layer's path): exact products in float64,
         # numpy's fixed pairwise summation, then one rounding to float32.
         prod = bf16_bits_to_f32(x_bits).astype(np.float64)[:, :, None] * w_r.astype(np.float64)[None]

@@ -73,6 +73,7 @@ def _load(path: str):
     lib.moe_oracle_permute_bwd.argtypes = [_f64p, _i32p, i64, i32, i32, i64, _f64p]
     lib.moe_oracle_backward.argtypes = [_u16p, _f32p, _u16p, _u16p, _f64p, i64, i32, i32, i32, i32,
                                         _f64p, _f64p, _f64p, _f64p]
+    lib.moe_oracle_router_logits.argtypes = [_u16p, _f32p, i64, i32, i32, _f64p]
     lib.moe_oracle_num_threads.argtypes = []
     lib.moe_oracle_num_threads.restype = ctypes.c_int
     for name in ("moe_oracle_route_topk", "moe_oracle_layout", "moe_oracle_gather",
@@ -81,7 +82,8 @@ def _load(path: str):
                  "moe_oracle_quantize_fp8", "moe_oracle_dequantize_fp8", "moe_oracle_glu_w64",
                  "moe_oracle_down_w64", "moe_oracle_combine_bwd", "moe_oracle_route_bwd",
                  "moe_oracle_swiglu", "moe_oracle_swiglu_bwd", "moe_oracle_gemm_nn",
-                 "moe_oracle_wgrad", "moe_oracle_permute_bwd", "moe_oracle_backward"):
+                 "moe_oracle_wgrad", "moe_oracle_permute_bwd", "moe_oracle_backward",
+                 "moe_oracle_router_logits"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
 
@@ -299,6 +301,19 @@ def down_w64(h: np.ndarray, w_d, counts, offsets, lib=None) -> np.ndarray:
     return y
 
 
+def router_logits(x_bits, w_r, lib=None) -> np.ndarray:
+    """logits [T, E] (float64) = x W_r with x bf16 bits [T, H], W_r fp32 [H, E]."""
+    x_bits = _u16(x_bits)
+    w_r = np.ascontiguousarray(w_r, dtype=np.float32)
+    T, H = x_bits.shape
+    H2, E = w_r.shape
+    assert H2 == H
+    out = np.empty((T, E))
+    _check((lib or _lib()).moe_oracle_router_logits(_p(x_bits, _u16p), _p(w_r, _f32p), T, H, E, _p(out, _f64p)),
+           "router_logits")
+    return out
+
+
 # ---- backward ----------------------------------------------------------------------
 
 def _f64(a):
@@ -479,3 +494,6 @@ class Oracle:
 
     def backward(self, *a, **kw):
         return backward(*a, lib=self.lib, **kw)
+
+    def router_logits(self, *a, **kw):
+        return router_logits(*a, lib=self.lib, **kw)

@@ -101,6 +101,24 @@ int moe_oracle_route_topk(const float *logits, int64_t T, int32_t E, int32_t k,
 }
 
 /*
+ * Router projection [PocketLLM, Remaining prefill attribution: the router is a
+ * phase of its own]: logits[t,e] = sum_h x[t,h] W_r[h,e], x bf16 [T, H] widened
+ * exactly, W_r fp32 [H, E], summed in double in ascending h.
+ */
+int moe_oracle_router_logits(const uint16_t *x, const float *w_r, int64_t T, int32_t H, int32_t E,
+                             double *logits) {
+    if (!x || !w_r || !logits || T < 0 || H < 1 || E < 1) return ORACLE_EINVAL;
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t)
+        for (int32_t e = 0; e < E; ++e) {
+            double s = 0.0;
+            for (int32_t h = 0; h < H; ++h) s += bf(x[t * H + h]) * (double)w_r[(int64_t)h * E + e];
+            logits[t * E + e] = s;
+        }
+    return 0;
+}
+
+/*
  * Padded expert-grouped layout [prime-rl, Changes: single-pass local layout --
  * one gather into the padded expert-grouped layout; Halo, Levers that help:
  * the atomic-free expert permute].

@@ -656,6 +656,22 @@ def test_swiglu_bwd_derivative(orc):
     check_swiglu_bwd_derivative(orc)
 
 
+def test_router_logits(orc):
+    """The router projection against numpy's float64 matmul, and against the
+    generator's own logits for the projection-routed config (which sums in
+    another order and rounds once to fp32: at most one fp32 ulp apart)."""
+    rng = np.random.default_rng(8)
+    x = gen.random_bf16((33, 96), seed=8)
+    w = rng.standard_normal((96, 20)).astype(np.float32) * np.float32(0.05)
+    ref = f32(x).astype(np.float64) @ w.astype(np.float64)
+    assert np.allclose(orc.router_logits(x, w), ref, rtol=1e-13, atol=1e-15)
+    cfg = gen.CONFIGS["tiny"]
+    d = gen.make_inputs(cfg)
+    lg = orc.router_logits(d["x"], gen.draw_router_weight(cfg)).astype(np.float32)
+    ulp = np.spacing(np.abs(d["logits"]))
+    assert np.all(np.abs(lg - d["logits"]) <= ulp)
+
+
 def test_rejects_bad_inputs(orc):
     bad = np.zeros((2, 4), np.float32)
     bad[1, 2] = np.inf
