@@ -20,6 +20,9 @@
  *   moe_grouped_glu_gemm_fp8w, moe_grouped_glu_gemm_gather_fp8w,
  *   moe_grouped_down_gemm_fp8w
  *
+ * The router projection fused with top-k (logits need not reach memory):
+ *   moe_router_prepare, moe_router_topk
+ *
  * Training (the forward with its gate/up output kept, and the backward):
  *   moe_grouped_gemm       plain grouped GEMM C[p] = A[p] W[e]^T (gate/up output
  *                          gu = x_perm W_gu^T; input gradients on transposed weights)
@@ -266,6 +269,25 @@ moe_status moe_grouped_down_gemm_fp8w(const moe_bf16 *h, const uint8_t *w8_down,
                                       const float *scale_down, const int32_t *expert_counts,
                                       const int32_t *expert_offsets, int32_t E, int32_t H, int32_t I,
                                       int64_t P_max, moe_bf16 *y, moe_stream_t stream);
+
+/*
+ * Router projection fused with top-k routing [PocketLLM, Remaining prefill
+ * attribution: the router is a phase of its own].  The fp32 router weight
+ * w_router [H, E] is prepared once per weight update into two bf16 matrices
+ * stored expert-major, w_hi = bf16_rne(w_router^T) and w_lo = bf16_rne(w_router^T
+ * - w_hi) ([E, H] each).  moe_router_topk then computes, per token,
+ *   logits[t, e] = sum_h x[t, h] (w_hi[e, h] + w_lo[e, h])   (fp32 accumulation;
+ *                  within about 2^-16 relative of the fp32 projection per term)
+ * and routes on them exactly as moe_route_topk does on its input logits (same
+ * order, ties and softmax).  logits [T, E] fp32 is written only if non-NULL.
+ *   x [T, H] bf16;  topk_idx [T, k] int32, topk_w [T, k] fp32 out.
+ * Shapes: H % 64 == 0, 1 <= k <= min(E, MOE_MAX_K), 1 <= E <= MOE_MAX_E.
+ */
+moe_status moe_router_prepare(const float *w_router, int32_t H, int32_t E, moe_bf16 *w_hi, moe_bf16 *w_lo,
+                              moe_stream_t stream);
+moe_status moe_router_topk(const moe_bf16 *x, const moe_bf16 *w_hi, const moe_bf16 *w_lo, int64_t T, int32_t H,
+                           int32_t E, int32_t k, float *logits, int32_t *topk_idx, float *topk_w,
+                           moe_stream_t stream);
 
 /*
  * ---- training: forward with saved gate/up output, and the backward ----

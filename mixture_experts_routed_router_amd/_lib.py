@@ -76,12 +76,16 @@ def load():
     lib.moe_permute_backward.argtypes = [_c_vp, _c_vp, _c_i64, _c_i32, _c_i32, _c_i64, _c_vp, _c_vp]
     lib.moe_grouped_wgrad.argtypes = [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i64,
                                       _c_vp, _c_vp]
+    lib.moe_router_prepare.argtypes = [_c_vp, _c_i32, _c_i32, _c_vp, _c_vp, _c_vp]
+    lib.moe_router_topk.argtypes = [_c_vp, _c_vp, _c_vp, _c_i64, _c_i32, _c_i32, _c_i32, _c_vp, _c_vp, _c_vp,
+                                    _c_vp]
     for fn in ("moe_permute_workspace_size", "moe_route_topk", "moe_permute",
                "moe_grouped_glu_gemm", "moe_grouped_glu_gemm_gather", "moe_grouped_down_gemm",
                "moe_combine", "moe_quantize_fp8", "moe_grouped_glu_gemm_fp8w",
                "moe_grouped_glu_gemm_gather_fp8w", "moe_grouped_down_gemm_fp8w", "moe_grouped_gemm",
                "moe_swiglu", "moe_swiglu_backward", "moe_transpose_experts", "moe_combine_backward",
-               "moe_route_backward", "moe_permute_backward", "moe_grouped_wgrad"):
+               "moe_route_backward", "moe_permute_backward", "moe_grouped_wgrad", "moe_router_prepare",
+               "moe_router_topk"):
         getattr(lib, fn).restype = ctypes.c_int
     _LIB = lib
     return lib
@@ -139,6 +143,33 @@ def route_topk(logits: torch.Tensor, k: int, topk_idx=None, topk_w=None, stream=
     _call("moe_route_topk", _ptr(logits, torch.float32, "logits"), T, E, k,
           _ptr(topk_idx, torch.int32, "topk_idx", (T, k)),
           _ptr(topk_w, torch.float32, "topk_w", (T, k)), _stream(stream))
+    return topk_idx, topk_w
+
+
+def router_prepare(w_router, stream=None):
+    """(w_hi, w_lo) bf16 [E, H] from the fp32 router weight [H, E], once per weight update."""
+    H, E = w_router.shape
+    w_hi = torch.empty((E, H), dtype=torch.bfloat16, device=w_router.device)
+    w_lo = torch.empty((E, H), dtype=torch.bfloat16, device=w_router.device)
+    _call("moe_router_prepare", _ptr(w_router, torch.float32, "w_router"), H, E,
+          _ptr(w_hi, torch.bfloat16, "w_hi"), _ptr(w_lo, torch.bfloat16, "w_lo"), _stream(stream))
+    return w_hi, w_lo
+
+
+def router_topk(x, w_hi, w_lo, k: int, topk_idx=None, topk_w=None, logits=None, stream=None):
+    """Router projection and top-k in one kernel; logits [T, E] fp32 written only if given."""
+    T, H = x.shape
+    E = w_hi.shape[0]
+    dev = x.device
+    if topk_idx is None:
+        topk_idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    if topk_w is None:
+        topk_w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    _call("moe_router_topk", _ptr(x, torch.bfloat16, "x"), _ptr(w_hi, torch.bfloat16, "w_hi", (E, H)),
+          _ptr(w_lo, torch.bfloat16, "w_lo", (E, H)), T, H, E, k,
+          _ptr(logits, torch.float32, "logits", (T, E)) if logits is not None else None,
+          _ptr(topk_idx, torch.int32, "topk_idx", (T, k)), _ptr(topk_w, torch.float32, "topk_w", (T, k)),
+          _stream(stream))
     return topk_idx, topk_w
 
 

@@ -26,6 +26,9 @@ hipError_t launch_route_bwd(const int32_t*, const float*, const float*, int64_t,
 hipError_t launch_swiglu(const uint16_t*, const uint16_t*, const int32_t*, int, int, int64_t, uint16_t*,
                          hipStream_t);
 hipError_t launch_transpose(const uint16_t*, int64_t, int, int, uint16_t*, hipStream_t);
+hipError_t launch_router_prepare(const float*, int, int, uint16_t*, uint16_t*, hipStream_t);
+hipError_t launch_router_topk(const uint16_t*, const uint16_t*, const uint16_t*, int64_t, int, int, int, float*,
+                              int32_t*, float*, hipStream_t);
 hipError_t launch_wgrad(const uint16_t*, const uint16_t*, const int32_t*, const int32_t*, int, int, int, float*,
                         hipStream_t);
 hipError_t launch_combine(const uint16_t*, const int32_t*, const float*, int64_t, int, int,
@@ -432,6 +435,36 @@ moe_status moe_grouped_wgrad(const moe_bf16* a, const moe_bf16* b, const int32_t
     if (tiles >= ((int64_t)1 << 31)) return fail(MOE_ERR_SIZE_OVERFLOW, "E*M*N/65536 tiles reach 2^31");
     return hip_status(moe::launch_wgrad(a, b, row_token, expert_offsets, E, M, N, dw, (hipStream_t)stream),
                       "moe_grouped_wgrad launch");
+}
+
+moe_status moe_router_prepare(const float* w_router, int32_t H, int32_t E, moe_bf16* w_hi, moe_bf16* w_lo,
+                              moe_stream_t stream) {
+    REQUIRE_PTR(w_router);
+    REQUIRE_PTR(w_hi);
+    REQUIRE_PTR(w_lo);
+    if (E < 1 || E > MOE_MAX_E) return fail(MOE_ERR_INVALID_SHAPE, "E=%d outside [1, %d]", E, MOE_MAX_E);
+    moe_status s;
+    if ((s = check_dim64("H", H)) != MOE_OK) return s;
+    return hip_status(moe::launch_router_prepare(w_router, H, E, w_hi, w_lo, (hipStream_t)stream),
+                      "moe_router_prepare launch");
+}
+
+moe_status moe_router_topk(const moe_bf16* x, const moe_bf16* w_hi, const moe_bf16* w_lo, int64_t T, int32_t H,
+                           int32_t E, int32_t k, float* logits, int32_t* topk_idx, float* topk_w,
+                           moe_stream_t stream) {
+    REQUIRE_PTR_UNLESS_EMPTY(x, T == 0);
+    REQUIRE_PTR(w_hi);
+    REQUIRE_PTR(w_lo);
+    REQUIRE_PTR_UNLESS_EMPTY(topk_idx, T == 0);
+    REQUIRE_PTR_UNLESS_EMPTY(topk_w, T == 0);
+    if (logits && !aligned16(logits)) return fail(MOE_ERR_MISALIGNED_POINTER, "logits is not 16-byte aligned");
+    if (T < 0 || T >= ((int64_t)1 << 31)) return fail(MOE_ERR_INVALID_SHAPE, "T=%lld outside [0, 2^31)", (long long)T);
+    moe_status s = check_ek(E, k);
+    if (s != MOE_OK) return s;
+    if ((s = check_dim64("H", H)) != MOE_OK) return s;
+    return hip_status(moe::launch_router_topk(x, w_hi, w_lo, T, H, E, k, logits, topk_idx, topk_w,
+                                              (hipStream_t)stream),
+                      "moe_router_topk launch");
 }
 
 moe_status moe_combine(const moe_bf16* y, const int32_t* route_row, const float* topk_w, int64_t T,

@@ -1,0 +1,119 @@
+// router.hip -- the router projection fused with top-k routing: logits = x W_r
+// are formed 32 tokens at a time in registers and LDS and never reach HBM
+// (unless asked for) [PocketLLM "Qwen4-Exp Heterogeneous TP4 Performance",
+// Remaining prefill attribution: the router is a phase of its own; prime-rl
+// PR 3885, Changes: top-k weights feed the layer].
+//
+// The fp32 router weight W_r [H, E] is split once per weight update into two
+// bf16 matrices stored expert-major, W_hi = bf16(W_r) and W_lo = bf16(W_r - W_hi)
+// ([E, H] each), so x W_r = x W_hi + x W_lo runs on bf16 MFMAs with fp32
+// accumulation: x is bf16 and exact, W_hi + W_lo carries 16 significant bits of
+// each weight, so the logits are within about 2^-16 relative of the fp32
+// projection per product.
+//
+// One workgroup of four waves per 32 tokens: wave w computes the 32-expert
+// blocks w, w+4, ... (v_mfma_f32_32x32x16_bf16, tokens as rows, experts as
+// columns, k over H), writes them to an LDS tile [32][E rounded up to 32], and
+// after a barrier each token's 8 lanes run the routing step's top-k on its LDS
+// row (topk_core.hpp).
+#include "topk_core.hpp"
+
+namespace moe {
+
+constexpr int kRouterThreads = 256;
+constexpr int kRouterTokens = 32;
+
+__global__ __launch_bounds__(256) void router_prepare_kernel(const float* __restrict__ w, int H, int E,
+                                                             uint16_t* __restrict__ w_hi,
+                                                             uint16_t* __restrict__ w_lo) {
+    const int64_t n = (int64_t)H * E;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t e = i / H, h = i - e * H;  // output [E, H]
+        const float v = w[h * E + e];
+        const uint32_t hi = f32_to_bf16_rne(v);
+        const float rest = v - __uint_as_float(hi << 16);
+        w_hi[i] = (uint16_t)hi;
+        w_lo[i] = (uint16_t)f32_to_bf16_rne(rest);
+    }
+}
+
+template <int KL>
+__global__ __launch_bounds__(kRouterThreads) void router_topk_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ w_hi, const uint16_t* __restrict__ w_lo,
+    int64_t T, int H, int E, int k, float* __restrict__ logits_out, int32_t* __restrict__ topk_idx,
+    float* __restrict__ topk_w) {
+    extern __shared__ __attribute__((aligned(16))) float lg[];  // [32][ep]
+    const int ep = (E + 31) / 32 * 32;
+    const int nblk = ep / 32;
+    const int64_t t0 = (int64_t)blockIdx.x * kRouterTokens;
+    const int lane = lane_id(), wave = threadIdx.x / kWave;
+    const int lr = lane & 31, kg = 8 * (lane >> 5);
+    // this lane's token row (past the last token: the last one; never stored)
+    const int64_t tr = t0 + lr < T ? t0 + lr : T - 1;
+    const uint16_t* xa = x + tr * H + kg;
+    for (int b = wave; b < nblk; b += kRouterThreads / kWave) {
+        const int er = b * 32 + lr < E ? b * 32 + lr : E - 1;  // this lane's expert row
+        const uint16_t* wh = w_hi + (int64_t)er * H + kg;
+        const uint16_t* wl = w_lo + (int64_t)er * H + kg;
+        floatx16_t acc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+#pragma unroll 4
+        for (int k0 = 0; k0 < H; k0 += 16) {
+            const bf16x8_t a = *(const bf16x8_t*)(xa + k0);
+            const bf16x8_t bh = *(const bf16x8_t*)(wh + k0);
+            const bf16x8_t bl = *(const bf16x8_t*)(wl + k0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bh, acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bl, acc, 0, 0, 0);
+        }
+        // MFMA 32x32 output: lane l, register r -> token row (r/4)*8 + (l/32)*4 + r%4, expert l%32
+        const int col = b * 32 + lr;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int row = (r / 4) * 8 + (lane >> 5) * 4 + r % 4;
+            lg[row * ep + col] = col < E ? acc[r] : -INFINITY;
+            if (logits_out && col < E && t0 + row < T) logits_out[(t0 + row) * E + col] = acc[r];
+        }
+    }
+    __syncthreads();
+    // 8 lanes per token: token tid / 8 of the tile
+    const int tok = threadIdx.x / 8, sub = threadIdx.x & 7;
+    const int64_t t = t0 + tok;
+    const bool live = t < T;
+    topk_token<KL, 4, 8>(lg + tok * ep, live, E, k, sub, topk_idx + t * k, topk_w + t * k);
+}
+
+hipError_t launch_router_prepare(const float* w, int H, int E, uint16_t* w_hi, uint16_t* w_lo, hipStream_t stream) {
+    const int64_t n = (int64_t)H * E;
+    const int64_t blocks = (n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096;
+    hipLaunchKernelGGL(router_prepare_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, w, H, E, w_hi, w_lo);
+    return hipGetLastError();
+}
+
+hipError_t launch_router_topk(const uint16_t* x, const uint16_t* w_hi, const uint16_t* w_lo, int64_t T, int H,
+                              int E, int k, float* logits, int32_t* topk_idx, float* topk_w, hipStream_t stream) {
+    if (T == 0) return hipSuccess;
+    const int ep = (E + 31) / 32 * 32;
+    const size_t lds = (size_t)kRouterTokens * ep * sizeof(float);
+    const dim3 grid((unsigned)((T + kRouterTokens - 1) / kRouterTokens)), block(kRouterThreads);
+    // more than 64 KB of dynamic LDS (E > 512) has to be allowed per kernel
+#define MOE_ROUTER_CASE(KL)                                                                          \
+    if (k <= KL) {                                                                                   \
+        if (lds > 65536) {                                                                           \
+            const hipError_t e_ = hipFuncSetAttribute((const void*)router_topk_kernel<KL>,            \
+                                                      hipFuncAttributeMaxDynamicSharedMemorySize,    \
+                                                      (int)lds);                                     \
+            if (e_ != hipSuccess) return e_;                                                         \
+        }                                                                                            \
+        hipLaunchKernelGGL((router_topk_kernel<KL>), grid, block, lds, stream, x, w_hi, w_lo, T, H, E, k, \
+                           logits, topk_idx, topk_w);                                                \
+        return hipGetLastError();                                                                    \
+    }
+    MOE_ROUTER_CASE(8)
+    MOE_ROUTER_CASE(16)
+    MOE_ROUTER_CASE(32)
+#undef MOE_ROUTER_CASE
+    return hipErrorInvalidValue;
+}
+
+}  // namespace moe

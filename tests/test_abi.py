@@ -53,6 +53,8 @@ def lib():
     lib.moe_route_backward.argtypes = [vp, vp, vp, i64, i32, i32, vp, vp]
     lib.moe_permute_backward.argtypes = [vp, vp, i64, i32, i32, i64, vp, vp]
     lib.moe_grouped_wgrad.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i64, vp, vp]
+    lib.moe_router_prepare.argtypes = [vp, i32, i32, vp, vp, vp]
+    lib.moe_router_topk.argtypes = [vp, vp, vp, i64, i32, i32, i32, vp, vp, vp, vp]
     return lib
 
 
@@ -193,6 +195,16 @@ def test_training_validation(lib):
     assert lib.moe_grouped_wgrad(FAKE, FAKE, FAKE + 4, FAKE, FAKE, 8, 128, 128, 1000, FAKE,
                                  None) == MISALIGNED
     assert lib.moe_grouped_wgrad(FAKE, FAKE, None, FAKE, FAKE, 8, 128, 128, 1000, None, None) == NULLP
+
+
+def test_router_validation(lib):
+    assert lib.moe_router_prepare(None, 128, 8, FAKE, FAKE, None) == NULLP
+    assert lib.moe_router_prepare(FAKE, 100, 8, FAKE, FAKE, None) == SHAPE          # H % 64
+    assert lib.moe_router_prepare(FAKE, 128, 2048, FAKE, FAKE, None) == SHAPE       # E > 1024
+    assert lib.moe_router_topk(FAKE, FAKE, FAKE, 4, 128, 8, 9, None, FAKE, FAKE, None) == SHAPE  # k > E
+    assert lib.moe_router_topk(FAKE, FAKE, FAKE, 4, 128, 8, 2, FAKE + 4, FAKE, FAKE, None) == MISALIGNED
+    assert lib.moe_router_topk(FAKE, None, FAKE, 4, 128, 8, 2, None, FAKE, FAKE, None) == NULLP
+    assert lib.moe_router_topk(None, FAKE, FAKE, 0, 128, 8, 2, None, None, None, None) == OK     # no tokens
 
 
 def test_combine_validation(lib):
