@@ -15,13 +15,16 @@
 // blocks w, w+4, ... (v_mfma_f32_32x32x16_bf16, tokens as rows, experts as
 // columns, k over H), writes them to an LDS tile [32][E rounded up to 32], and
 // after a barrier each token's 8 lanes run the routing step's top-k on its LDS
-// row (topk_core.hpp).
+// row (topk_core.hpp).  Splitting k over more waves per workgroup (2 or 4
+// groups, partial tiles added in a fixed order) measured no faster: the time
+// goes to streaming W_hi and W_lo through each workgroup, not to load latency.
 #include "topk_core.hpp"
 
 namespace moe {
 
 constexpr int kRouterThreads = 256;
 constexpr int kRouterTokens = 32;
+constexpr int kRouterDepth = 4;  // k steps of loads in flight per wave (divides H / 16)
 
 __global__ __launch_bounds__(256) void router_prepare_kernel(const float* __restrict__ w, int H, int E,
                                                              uint16_t* __restrict__ w_hi,
@@ -51,31 +54,58 @@ __global__ __launch_bounds__(kRouterThreads) void router_topk_kernel(
     // this lane's token row (past the last token: the last one; never stored)
     const int64_t tr = t0 + lr < T ? t0 + lr : T - 1;
     const uint16_t* xa = x + tr * H + kg;
+    const int nsteps = H / 16;  // a multiple of kRouterDepth (H % 64 == 0)
     for (int b = wave; b < nblk; b += kRouterThreads / kWave) {
-        const int er = b * 32 + lr < E ? b * 32 + lr : E - 1;  // this lane's expert row
-        const uint16_t* wh = w_hi + (int64_t)er * H + kg;
-        const uint16_t* wl = w_lo + (int64_t)er * H + kg;
-        floatx16_t acc;
+        // k steps of 16 through a ring of kRouterDepth register slots (step s in
+        // slot s % kRouterDepth, refilled right after its MFMAs, the scheduling
+        // barriers keeping it so), two accumulators so that consecutive MFMAs do
+        // not wait on each other
+        floatx16_t acc0, acc1;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
-#pragma unroll 4
-        for (int k0 = 0; k0 < H; k0 += 16) {
-            const bf16x8_t a = *(const bf16x8_t*)(xa + k0);
-            const bf16x8_t bh = *(const bf16x8_t*)(wh + k0);
-            const bf16x8_t bl = *(const bf16x8_t*)(wl + k0);
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bh, acc, 0, 0, 0);
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bl, acc, 0, 0, 0);
+        for (int r = 0; r < 16; ++r) acc0[r] = acc1[r] = 0.0f;
+        {
+            const int er = b * 32 + lr < E ? b * 32 + lr : E - 1;  // this lane's expert row
+            const uint16_t* wh = w_hi + (int64_t)er * H + kg;
+            const uint16_t* wl = w_lo + (int64_t)er * H + kg;
+            bf16x8_t ra[kRouterDepth], rh[kRouterDepth], rl[kRouterDepth];
+#pragma unroll
+            for (int d = 0; d < kRouterDepth; ++d) {
+                ra[d] = *(const bf16x8_t*)(xa + 16 * d);
+                rh[d] = *(const bf16x8_t*)(wh + 16 * d);
+                rl[d] = *(const bf16x8_t*)(wl + 16 * d);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            for (int s0 = 0; s0 < nsteps; s0 += kRouterDepth) {
+#pragma unroll
+                for (int d = 0; d < kRouterDepth; ++d) {
+                    floatx16_t& acc = (d & 1) ? acc1 : acc0;
+                    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[d], rh[d], acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[d], rl[d], acc, 0, 0, 0);
+                    __builtin_amdgcn_sched_barrier(0);
+                    // past the last step: re-read the last one (in bounds, never used)
+                    const int sn = s0 + d + kRouterDepth < nsteps ? s0 + d + kRouterDepth : nsteps - 1;
+                    ra[d] = *(const bf16x8_t*)(xa + 16 * sn);
+                    rh[d] = *(const bf16x8_t*)(wh + 16 * sn);
+                    rl[d] = *(const bf16x8_t*)(wl + 16 * sn);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
         }
         // MFMA 32x32 output: lane l, register r -> token row (r/4)*8 + (l/32)*4 + r%4, expert l%32
         const int col = b * 32 + lr;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
             const int row = (r / 4) * 8 + (lane >> 5) * 4 + r % 4;
-            lg[row * ep + col] = col < E ? acc[r] : -INFINITY;
-            if (logits_out && col < E && t0 + row < T) logits_out[(t0 + row) * E + col] = acc[r];
+            lg[row * ep + col] = col < E ? acc0[r] + acc1[r] : -INFINITY;
         }
     }
     __syncthreads();
+    if (logits_out) {
+        for (int i = threadIdx.x; i < kRouterTokens * E; i += kRouterThreads) {
+            const int row = i / E, col = i - row * E;
+            if (t0 + row < T) logits_out[(t0 + row) * E + col] = lg[row * ep + col];
+        }
+    }
     // 8 lanes per token: token tid / 8 of the tile
     const int tok = threadIdx.x / 8, sub = threadIdx.x & 7;
     const int64_t t = t0 + tok;
