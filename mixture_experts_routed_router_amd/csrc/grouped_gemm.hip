@@ -17,7 +17,9 @@
 // expert-major order (expert, then row tile, then column tile), so an expert's
 // weights are read about once and stay in cache while its row tiles run [prime-rl
 // PR 3885, Required kernel commits: expert-major task order]; consecutive tiles
-// share a row tile of A.  The tile list is
+// share a row tile of A.  An expert's rows are cut into ceil(rows / 256) row
+// tiles of nearly equal size (whole 32-row blocks), not 256-row tiles and a
+// remainder.  The tile list is
 // dealt in contiguous runs per XCD (workgroup b runs on XCD b % 8), so each
 // expert's tiles share one XCD's L2.  Counts and offsets are read on the device;
 // an expert with no rows owns no tiles and reads no weights [PocketLLM "Qwen4-Exp
@@ -174,6 +176,14 @@ __device__ __forceinline__ uint32_t quad_xor2(uint32_t v) {
 }
 __device__ __forceinline__ uint32_t quad_xor1(uint32_t v) {
     return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true);  // [1,0,3,2]
+}
+
+// The value of lane l ^ 4 (same 16-lane DPP row): row_shl:4 gives lane l the
+// value of lane l + 4, row_shr:4 that of lane l - 4; `odd` = lane bit 2.
+__device__ __forceinline__ uint32_t lane_xor4(uint32_t v, bool odd) {
+    const uint32_t from_up = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x104, 0xF, 0xF, true);
+    const uint32_t from_dn = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x114, 0xF, 0xF, true);
+    return odd ? from_dn : from_up;
 }
 
 __device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
@@ -557,8 +567,9 @@ __device__ __forceinline__ int run_tile(const WaveCtx& w, const TileArgs& ta, co
     //   row = (r / 4) * 8 + (l / 32) * 4 + r % 4,  column = l % 32,
     // so registers 4q..4q+3 of the quad of lanes 4c..4c+3 form the 4x4 block of rows
     // 8q + 4(l/32) + 0..3 and columns 4c + 0..3. Every store instruction covers 8 rows
-    // of one 32-column block; those with no row inside the segment are not issued,
-    // and the rest are counted.
+    // of the wave's columns (GLU: one 32-column block; plain: both blocks, 64
+    // columns); those with no row inside the segment are not issued, and the rest
+    // are counted.
     int stores = 0;
     if (NV > 0) {
         // The tile's scalars pass through an empty asm here, so the compiler cannot
@@ -575,42 +586,82 @@ __device__ __forceinline__ int run_tile(const WaveCtx& w, const TileArgs& ta, co
         const uint32_t out_off = (uint32_t)((out_row * n_cols + ((ln & 31) >> 2) * 4) * 2);
         constexpr int OB = GLU ? NBN / 2 : NBN;    // 32-column output blocks per wave
         const int col0 = GLU ? nt * 128 + wn * (WTN / 2) : nt * BN + wn * WTN;
+        if (GLU) {
 #pragma unroll
-        for (int i = 0; i < NV; ++i) {
+            for (int i = 0; i < NV; ++i) {
 #pragma unroll
-            for (int jb = 0; jb < OB; ++jb) {
-                const int cb = col0 + jb * 32;
-                if (cb >= n_cols) continue;
-                // FP8 weights: a 32-column block lies inside one 64-row scale block
-                // (gate rows cb.., up rows n_cols + cb..), so its scales are wave-uniform
-                float sg = 1.0f, su = 1.0f;
-                if (W8) {
-                    sg = w_scale[cb >> 6];
-                    if (GLU) su = w_scale[(n_cols + cb) >> 6];
-                }
+                for (int jb = 0; jb < OB; ++jb) {
+                    const int cb = col0 + jb * 32;
+                    if (cb >= n_cols) continue;
+                    // FP8 weights: a 32-column block lies inside one 64-row scale block
+                    // (gate rows cb.., up rows n_cols + cb..), so its scales are wave-uniform
+                    float sg = 1.0f, su = 1.0f;
+                    if (W8) {
+                        sg = w_scale[cb >> 6];
+                        su = w_scale[(n_cols + cb) >> 6];
+                    }
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int r0 = (2 * i + wm) * 32 + q * 8;
-                    if (r0 >= rows_valid) continue;
-                    float v[4];
+                    for (int q = 0; q < 4; ++q) {
+                        const int r0 = (2 * i + wm) * 32 + q * 8;
+                        if (r0 >= rows_valid) continue;
+                        float v[4];
 #pragma unroll
-                    for (int m = 0; m < 4; ++m) {
-                        if (GLU) {
+                        for (int m = 0; m < 4; ++m) {
                             float g = acc[i][jb][4 * q + m], u = acc[i][jb + NBN / 2][4 * q + m];
                             if (W8) {
                                 g *= sg;
                                 u *= su;
                             }
                             v[m] = g / (1.0f + __expf(-g)) * u;
-                        } else {
-                            v[m] = W8 ? acc[i][jb][4 * q + m] * sg : acc[i][jb][4 * q + m];
                         }
+                        uint32_t w0, w1;
+                        quad_transpose_bf16(v[0], v[1], v[2], v[3], qs, w0, w1);
+                        char* grp0 = (char*)(c_tile + ((int64_t)r0 * n_cols + cb));
+                        if (out_row < rows_valid - r0)
+                            *(uint2*)(grp0 + out_off) = make_uint2(w0, w1);
+                        ++stores;
                     }
-                    uint32_t w0, w1;
-                    quad_transpose_bf16(v[0], v[1], v[2], v[3], qs, w0, w1);
-                    char* grp0 = (char*)(c_tile + ((int64_t)r0 * n_cols + cb));
-                    if (out_row < rows_valid - r0)
-                        *(uint2*)(grp0 + out_off) = make_uint2(w0, w1);
+                }
+            }
+        } else if (col0 < n_cols) {
+            // Plain GEMM: the wave's two 32-column blocks are adjacent (64 columns, one
+            // 128-byte line per row; N is a multiple of 64, so both exist). After the
+            // quad transposes a lane holds columns 4c..4c+3 of both blocks for one row;
+            // lanes c = 2j and 2j+1 (lane ^ 4) trade halves, so the even lane holds
+            // columns 8j..8j+7 and the odd one 32+8j..32+8j+7, and each store
+            // instruction writes 8 whole 128-byte rows, 16 bytes per lane. (Stores of
+            // 8 bytes per lane, 64 bytes per row and instruction, made the down GEMM
+            // about 25% slower.)
+            static_assert(GLU || OB == 2, "two 32-column blocks per wave");
+            const bool odd = (ln & 4) != 0;
+            // byte offset of this lane's 16 bytes from the group's (row 0, column 0)
+            const uint32_t st_off =
+                (uint32_t)((out_row * n_cols + (odd ? 32 : 0) + ((ln & 31) >> 3) * 8) * 2);
+            float s0 = 1.0f, s1 = 1.0f;
+            if (W8) {
+                s0 = w_scale[col0 >> 6];
+                s1 = w_scale[(col0 + 32) >> 6];
+            }
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int r0 = (2 * i + wm) * 32 + q * 8;
+                    if (r0 >= rows_valid) continue;
+                    float v0[4], v1[4];
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        v0[m] = W8 ? acc[i][0][4 * q + m] * s0 : acc[i][0][4 * q + m];
+                        v1[m] = W8 ? acc[i][1][4 * q + m] * s1 : acc[i][1][4 * q + m];
+                    }
+                    uint32_t a0, a1, b0, b1;
+                    quad_transpose_bf16(v0[0], v0[1], v0[2], v0[3], qs, a0, a1);
+                    quad_transpose_bf16(v1[0], v1[1], v1[2], v1[3], qs, b0, b1);
+                    const uint32_t g0 = lane_xor4(odd ? a0 : b0, odd);
+                    const uint32_t g1 = lane_xor4(odd ? a1 : b1, odd);
+                    const uint4 o = odd ? make_uint4(g0, g1, b0, b1) : make_uint4(a0, a1, g0, g1);
+                    char* grp0 = (char*)(c_tile + ((int64_t)r0 * n_cols + col0));
+                    if (out_row < rows_valid - r0) *(uint4*)(grp0 + st_off) = o;
                     ++stores;
                 }
             }
@@ -709,8 +760,14 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_kernel(
         const int seg0 = __builtin_amdgcn_readfirstlane(seg_start[e]);
         const int seg1 = __builtin_amdgcn_readfirstlane(seg_start[e + 1]);
         const int q = t - __builtin_amdgcn_readfirstlane(tile_start[e]);
+        // The segment's 32-row blocks are spread evenly over its ceil(rows / 256)
+        // row tiles (17 blocks -> 6, 6, 5 rather than 8, 8, 1): the same MFMA
+        // work, but no nearly empty tile that still streams all of its weights.
+        const int nb = (seg1 - seg0 + 31) / 32;
+        const int m = (nb + BM / 32 - 1) / (BM / 32);
         const int mt = q / NT, nt = q - mt * NT;  // row tile, then column tile
-        const int row0 = seg0 + mt * BM;
+        const int bq = nb / m, br = nb - bq * m;  // row tile mt has bq + (mt < br) blocks
+        const int row0 = seg0 + 32 * (mt * bq + min(mt, br));
         TileArgs ta;
         ta.a_tile = GATHER ? A : A + (int64_t)row0 * K;
         ta.row0 = row0;
@@ -718,7 +775,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_kernel(
         ta.w_scale = W8 ? w_scale + (int64_t)e * (NW / 64) : w_scale;
         ta.c_tile = C + (int64_t)row0 * N;
         ta.nt = nt;
-        ta.rows_valid = min(BM, seg1 - row0);
+        ta.rows_valid = min(32 * (bq + (mt < br ? 1 : 0)), seg1 - row0);
         // live 32-row blocks of this wave: wave row wm owns blocks 2i + wm
         ta.nvb = max(0, min(4, ((ta.rows_valid + 31) / 32 - w.wm + 1) / 2));
         return ta;
@@ -730,6 +787,13 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_kernel(
     int tb = 0;  // gathering A: the current tile's token buffer
     int t = xcd * chunk + slot;
     if (t >= t_end) return;
+#if defined(MOE_GEMM_STAGGER) && MOE_GEMM_STAGGER > 0
+    if (slot & 1) {
+        const uint64_t t0 = wall_clock64();
+        const uint64_t until = t0 + (uint64_t)w.nk * MOE_GEMM_STAGGER;
+        while (wall_clock64() < until) __builtin_amdgcn_s_sleep(8);
+    }
+#endif
     TileArgs cur = tile_args(t);
     int base = 0, s_prev = 0;
     bool prefetched = false;
