@@ -787,13 +787,6 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_kernel(
     int tb = 0;  // gathering A: the current tile's token buffer
     int t = xcd * chunk + slot;
     if (t >= t_end) return;
-#if defined(MOE_GEMM_STAGGER) && MOE_GEMM_STAGGER > 0
-    if (slot & 1) {
-        const uint64_t t0 = wall_clock64();
-        const uint64_t until = t0 + (uint64_t)w.nk * MOE_GEMM_STAGGER;
-        while (wall_clock64() < until) __builtin_amdgcn_s_sleep(8);
-    }
-#endif
     TileArgs cur = tile_args(t);
     int base = 0, s_prev = 0;
     bool prefetched = false;
