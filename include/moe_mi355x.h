@@ -377,6 +377,7 @@ moe_status moe_permute_backward(const moe_bf16 *dx_perm, const int32_t *route_ro
  *   dw [E, M, N] fp32 out; an expert with no rows gets zeros.
  *   dW_down: a = dy, b = h (M = H, N = I).  dW_gate_up: a = dgu, b = x_perm (M = 2I, N = H).
  * Shapes: M % 64 == 0, N % 64 == 0, 1 <= E <= MOE_MAX_E, 0 < P_max < 2^31.
+ * dw must be 16-byte aligned (MOE_ERR_MISALIGNED_POINTER otherwise).
  */
 moe_status moe_grouped_wgrad(const moe_bf16 *a, const moe_bf16 *b, const int32_t *row_token,
                              const int32_t *expert_counts, const int32_t *expert_offsets, int32_t E,

@@ -424,6 +424,7 @@ moe_status moe_grouped_wgrad(const moe_bf16* a, const moe_bf16* b, const int32_t
     REQUIRE_PTR(expert_counts);
     REQUIRE_PTR(expert_offsets);
     REQUIRE_PTR(dw);
+    if (!aligned16(dw)) return fail(MOE_ERR_MISALIGNED_POINTER, "dw is not 16-byte aligned");
     if (row_token && !aligned16(row_token))
         return fail(MOE_ERR_MISALIGNED_POINTER, "row_token is not 16-byte aligned");
     if (E < 1 || E > MOE_MAX_E) return fail(MOE_ERR_INVALID_SHAPE, "E=%d outside [1, %d]", E, MOE_MAX_E);

@@ -32,6 +32,14 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
+// The value of lane l ^ 2 / l ^ 1 inside each quad of lanes (DPP quad_perm).
+__device__ __forceinline__ uint32_t quad_xor2(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true);  // [2,3,0,1]
+}
+__device__ __forceinline__ uint32_t quad_xor1(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true);  // [1,0,3,2]
+}
+
 // Lanes of this wave whose 32-bit key equals mine (the whole key is compared
 // bit by bit with ballots, so no atomics and no LDS are needed). `nbits` is the
 // number of low key bits that can differ.

@@ -171,12 +171,6 @@ __device__ __forceinline__ void wait_vmcnt_dyn(int n) {
 }
 
 // Lane exchange inside each quad of lanes (DPP quad_perm): partner lane ^ 2 or ^ 1.
-__device__ __forceinline__ uint32_t quad_xor2(uint32_t v) {
-    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true);  // [2,3,0,1]
-}
-__device__ __forceinline__ uint32_t quad_xor1(uint32_t v) {
-    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true);  // [1,0,3,2]
-}
 
 // The value of lane l ^ 4 (same 16-lane DPP row): row_shl:4 gives lane l the
 // value of lane l + 4, row_shr:4 that of lane l - 4; `odd` = lane bit 2.

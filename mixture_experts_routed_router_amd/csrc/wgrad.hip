@@ -165,18 +165,34 @@ __global__ __launch_bounds__(kWgThreads, 1) void wgrad_kernel(const uint16_t* __
 #undef MOE_WG_CHUNK
 #undef MOE_WG_LOAD
 
-    // MFMA 32x32 output: lane l, register r -> row (r/4)*8 + (l/32)*4 + r%4, column l%32
+    // MFMA 32x32 output: lane l, register r -> row (r/4)*8 + (l/32)*4 + r%4, column l%32.
+    // Registers 4q..4q+3 of the quad of lanes 4c..4c+3 are the 4x4 block of rows
+    // 8q + 4(l/32) + 0..3 and columns 4c..4c+3; a transpose inside the quad (an
+    // exchange with lane ^ 1, then with lane ^ 2) leaves lane 4c+p with row
+    // 8q + 4(l/32) + p, columns 4c..4c+3: one 16-byte store per lane, 8 whole
+    // 128-byte rows per instruction (4-byte stores, 2 rows per instruction, took
+    // four times the store instructions).
     float* out = dW + (int64_t)e * M * N;
+    const bool p0 = (lane & 1) != 0, p1 = (lane & 2) != 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            const int n = n0 + wn * 64 + j * 32 + lrow;
-            if (n >= N) continue;
+            const int nb = n0 + wn * 64 + j * 32;  // N % 64 == 0: a block is all in or all out
+            if (nb >= N) continue;
+            const int n = nb + ((lane & 31) >> 2) * 4;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int m = m0 + wm * 128 + i * 32 + (r / 4) * 8 + (lane >> 5) * 4 + r % 4;
-                if (m < M) out[(int64_t)m * N + n] = acc[i][j][r];
+            for (int q = 0; q < 4; ++q) {
+                const int m = m0 + wm * 128 + i * 32 + q * 8 + (lane >> 5) * 4 + (lane & 3);
+                const uint32_t v0 = __float_as_uint(acc[i][j][4 * q + 0]), v1 = __float_as_uint(acc[i][j][4 * q + 1]);
+                const uint32_t v2 = __float_as_uint(acc[i][j][4 * q + 2]), v3 = __float_as_uint(acc[i][j][4 * q + 3]);
+                // lane ^ 1: the odd lane takes its partner's even rows, the even lane its partner's odd rows
+                const uint32_t x0 = quad_xor1(p0 ? v0 : v1), x1 = quad_xor1(p0 ? v2 : v3);
+                const uint32_t t0 = p0 ? x0 : v0, t1 = p0 ? v1 : x0, t2 = p0 ? x1 : v2, t3 = p0 ? v3 : x1;
+                // lane ^ 2: the same for pairs of rows
+                const uint32_t y0 = quad_xor2(p1 ? t0 : t2), y1 = quad_xor2(p1 ? t1 : t3);
+                const uint4 o = p1 ? make_uint4(y0, y1, t2, t3) : make_uint4(t0, t1, y0, y1);
+                if (m < M) *(uint4*)(out + (int64_t)m * N + n) = o;
             }
         }
 }

@@ -195,6 +195,7 @@ def test_training_validation(lib):
     assert lib.moe_grouped_wgrad(FAKE, FAKE, FAKE + 4, FAKE, FAKE, 8, 128, 128, 1000, FAKE,
                                  None) == MISALIGNED
     assert lib.moe_grouped_wgrad(FAKE, FAKE, None, FAKE, FAKE, 8, 128, 128, 1000, None, None) == NULLP
+    assert lib.moe_grouped_wgrad(FAKE, FAKE, None, FAKE, FAKE, 8, 128, 128, 1000, FAKE + 4, None) == MISALIGNED
 
 
 def test_router_validation(lib):
