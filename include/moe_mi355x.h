@@ -26,6 +26,8 @@
  * Training (the forward with its gate/up output kept, and the backward):
  *   moe_grouped_gemm       plain grouped GEMM C[p] = A[p] W[e]^T (gate/up output
  *                          gu = x_perm W_gu^T; input gradients on transposed weights)
+ *   moe_grouped_gemm_swiglu_backward  dh = dy W_down and the SwiGLU backward in one
+ *                          GEMM (dh never reaches memory)
  *   moe_swiglu, moe_swiglu_backward, moe_transpose_experts, moe_combine_backward,
  *   moe_route_backward, moe_permute_backward, moe_grouped_wgrad
  *
@@ -297,7 +299,8 @@ moe_status moe_router_topk(const moe_bf16 *x, const moe_bf16 *w_hi, const moe_bf
  *             [P_max, 2I], h = moe_swiglu(gu), y = moe_grouped_down_gemm(h, w_down),
  *             out = moe_combine(y)
  *   backward: dy, dw = moe_combine_backward(dout, y); dlogits = moe_route_backward(dw);
- *             dh = moe_grouped_gemm(dy, w_down^T); dgu = moe_swiglu_backward(dh, gu);
+ *             dgu = moe_grouped_gemm_swiglu_backward(dy, w_down^T, gu)  (or, in two
+ *             steps, dh = moe_grouped_gemm(dy, w_down^T); dgu = moe_swiglu_backward(dh, gu));
  *             dx_perm = moe_grouped_gemm(dgu, w_gate_up^T); dx = moe_permute_backward;
  *             dW_down = moe_grouped_wgrad(dy, h); dW_gate_up = moe_grouped_wgrad(dgu, x_perm)
  *   where w^T comes from moe_transpose_experts once per weight update.
@@ -317,6 +320,27 @@ moe_status moe_router_topk(const moe_bf16 *x, const moe_bf16 *w_hi, const moe_bf
 moe_status moe_grouped_gemm(const moe_bf16 *a, const moe_bf16 *w, const int32_t *expert_counts,
                             const int32_t *expert_offsets, int32_t E, int32_t K, int32_t N, int64_t P_max,
                             moe_bf16 *c, moe_stream_t stream);
+
+/*
+ * The input-gradient GEMM of the down projection with the SwiGLU backward in its
+ * epilogue [prime-rl PR 3885, Changes: grouped dgrad GEMMs of the expert path; the
+ * SwiGLU backward folded into the GEMM that produces dh]: for every row p of
+ * expert e's padded segment and 0 <= i < I,
+ *   dh[p, i]      = bf16_rne( sum_c dy[p, c] w_down_t[e, i, c] )   (fp32 accumulation)
+ *   dgu[p, i]     = bf16_rne( dh[p, i] u silu'(g) ),  dgu[p, I + i] = bf16_rne( dh[p, i] silu(g) )
+ * with g = gu[p, i], u = gu[p, I + i] and the fp32 arithmetic of moe_swiglu_backward,
+ * so dgu equals moe_swiglu_backward(moe_grouped_gemm(dy, w_down_t), gu) bit for bit;
+ * dh itself is never written.
+ *   dy [P_max, H] bf16;  w_down_t [E, I, H] bf16 (moe_transpose_experts of w_down);
+ *   gu [P_max, 2I] bf16 (the forward's saved gate/up output);  dgu [P_max, 2I] bf16 out
+ *   (rows past offsets[E] not written).
+ * Shapes: H % 64 == 0, I % 64 == 0, 4*H*I < 2^32, 1 <= E <= MOE_MAX_E, 0 < P_max < 2^31;
+ * every pointer 16-byte aligned.
+ */
+moe_status moe_grouped_gemm_swiglu_backward(const moe_bf16 *dy, const moe_bf16 *w_down_t, const moe_bf16 *gu,
+                                            const int32_t *expert_counts, const int32_t *expert_offsets,
+                                            int32_t E, int32_t H, int32_t I, int64_t P_max, moe_bf16 *dgu,
+                                            moe_stream_t stream);
 
 /*
  * SwiGLU on saved gate/up rows, gu = [g | u] ([P_max, 2I], g the first I columns):

@@ -85,10 +85,13 @@ def step_work(T: int, H: int, E: int, k: int, I: int, P: int, active_experts: in
     return [route, permute, glu, down, combine]
 
 
-def training_work(T: int, H: int, E: int, k: int, I: int, P: int, active_experts: int):
+def training_work(T: int, H: int, E: int, k: int, I: int, P: int, active_experts: int,
+                  fused_swiglu_backward: bool = False):
     """Per-kernel algorithmic work of one training step (forward that keeps its
     gate/up output, then the backward), in launch order. Weight gradients are
-    fp32 (4 bytes per element), everything else as in step_work."""
+    fp32 (4 bytes per element), everything else as in step_work. With the fused
+    SwiGLU backward, dh = dy W_d and its SwiGLU backward are one kernel that reads
+    dy, W_d and gu and writes dgu (dh never reaches memory)."""
     R = T * k
     bf, i32, f32 = 2, 4, 4
     wgu = active_experts * 2 * I * H
@@ -103,8 +106,12 @@ def training_work(T: int, H: int, E: int, k: int, I: int, P: int, active_experts
         down, combine,
         StepWork("combine_backward", 0.0, T * H * bf + R * H * bf + P * H * bf + R * (2 * i32 + 2 * f32)),
         StepWork("route_backward", 0.0, R * (i32 + 2 * f32) + T * E * f32),
+    ] + ([
+        StepWork("dgrad_down_swiglu_backward", 2.0 * R * H * I, wd * bf + P * H * bf + 2 * P * 2 * I * bf + maps),
+    ] if fused_swiglu_backward else [
         StepWork("dgrad_down", 2.0 * R * H * I, wd * bf + P * H * bf + P * I * bf + maps),
         StepWork("swiglu_backward", 0.0, P * I * bf + 2 * P * 2 * I * bf),
+    ]) + [
         StepWork("dgrad_gate_up", 4.0 * R * H * I, wgu * bf + P * 2 * I * bf + P * H * bf + maps),
         StepWork("permute_backward", 0.0, R * H * bf + R * i32 + T * H * bf),
         StepWork("wgrad_down", 2.0 * R * H * I, P * H * bf + P * I * bf + wd * f32 + maps),

@@ -23,6 +23,8 @@ hipError_t launch_grouped_gemm_small(bool, const uint16_t*, const int32_t*, cons
 hipError_t launch_combine_bwd(const uint16_t*, const uint16_t*, const int32_t*, const float*, const int32_t*,
                               const int32_t*, int64_t, int, int, int, int64_t, uint16_t*, float*, hipStream_t);
 hipError_t launch_route_bwd(const int32_t*, const float*, const float*, int64_t, int, int, float*, hipStream_t);
+hipError_t launch_grouped_gemm_swiglu_bwd(const uint16_t*, const uint16_t*, const uint16_t*, const int32_t*, int,
+                                          int, int, uint16_t*, hipStream_t);
 hipError_t launch_swiglu(const uint16_t*, const uint16_t*, const int32_t*, int, int, int64_t, uint16_t*,
                          hipStream_t);
 hipError_t launch_transpose(const uint16_t*, int64_t, int, int, uint16_t*, hipStream_t);
@@ -351,6 +353,17 @@ moe_status moe_swiglu_backward(const moe_bf16* dh, const moe_bf16* gu, const int
     if (s != MOE_OK) return s;
     return hip_status(moe::launch_swiglu(gu, dh, expert_offsets, E, I, P_max, dgu, (hipStream_t)stream),
                       "moe_swiglu_backward launch");
+}
+
+moe_status moe_grouped_gemm_swiglu_backward(const moe_bf16* dy, const moe_bf16* w_down_t, const moe_bf16* gu,
+                                            const int32_t* expert_counts, const int32_t* expert_offsets, int32_t E,
+                                            int32_t H, int32_t I, int64_t P_max, moe_bf16* dgu, moe_stream_t stream) {
+    moe_status s = check_gemm(dy, w_down_t, expert_counts, expert_offsets, E, H, I, P_max, dgu);
+    if (s != MOE_OK) return s;
+    REQUIRE_PTR(gu);
+    return hip_status(moe::launch_grouped_gemm_swiglu_bwd(dy, w_down_t, gu, expert_offsets, E, H, I, dgu,
+                                                          (hipStream_t)stream),
+                      "moe_grouped_gemm_swiglu_backward launch");
 }
 
 moe_status moe_transpose_experts(const moe_bf16* w, int64_t E, int32_t R, int32_t C, moe_bf16* wt,

@@ -116,26 +116,10 @@ __global__ __launch_bounds__(256) void swiglu_kernel(const uint4* __restrict__ g
                                    silu_f(bf16_hi(gp[q])) * bf16_hi(up[q]));
             out[i] = make_uint4(o[0], o[1], o[2], o[3]);
         } else {
-            const uint4 dv = dh[i];
-            const uint32_t dp[4] = {dv.x, dv.y, dv.z, dv.w};
-            uint32_t og[4], ou[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                float dg[2], du[2];
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const float g = h ? bf16_hi(gp[q]) : bf16_lo(gp[q]);
-                    const float u = h ? bf16_hi(up[q]) : bf16_lo(up[q]);
-                    const float d = h ? bf16_hi(dp[q]) : bf16_lo(dp[q]);
-                    const float sg = 1.0f / (1.0f + __expf(-g));
-                    dg[h] = d * u * (sg * (1.0f + g * (1.0f - sg)));
-                    du[h] = d * (g * sg);
-                }
-                og[q] = pack_bf16x2(dg[0], dg[1]);
-                ou[q] = pack_bf16x2(du[0], du[1]);
-            }
-            out[p * 2 * pieces_i + c] = make_uint4(og[0], og[1], og[2], og[3]);
-            out[p * 2 * pieces_i + pieces_i + c] = make_uint4(ou[0], ou[1], ou[2], ou[3]);
+            uint4 og, ou;
+            swiglu_bwd_x8(gv, uv, dh[i], og, ou);
+            out[p * 2 * pieces_i + c] = og;
+            out[p * 2 * pieces_i + pieces_i + c] = ou;
         }
     }
 }

@@ -57,4 +57,30 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
     return l == 0 ? 0ull : (~0ull >> (64 - l));
 }
 
+// SwiGLU backward of 8 elements, 16 bytes of bf16 each of g, u and dh, in fp32:
+//   dg = dh u silu'(g),  du = dh silu(g),  silu(g) = g s,  silu'(g) = s (1 + g (1 - s)),
+//   s = 1 / (1 + e^-g); results rounded to bf16 (nearest even).
+__device__ __forceinline__ void swiglu_bwd_x8(uint4 gv, uint4 uv, uint4 dv, uint4& og, uint4& ou) {
+    const uint32_t gp[4] = {gv.x, gv.y, gv.z, gv.w}, up[4] = {uv.x, uv.y, uv.z, uv.w};
+    const uint32_t dp[4] = {dv.x, dv.y, dv.z, dv.w};
+    uint32_t rg[4], ru[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        float dg[2], du[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const float g = h ? bf16_hi(gp[q]) : bf16_lo(gp[q]);
+            const float u = h ? bf16_hi(up[q]) : bf16_lo(up[q]);
+            const float d = h ? bf16_hi(dp[q]) : bf16_lo(dp[q]);
+            const float sg = 1.0f / (1.0f + __expf(-g));
+            dg[h] = d * u * (sg * (1.0f + g * (1.0f - sg)));
+            du[h] = d * (g * sg);
+        }
+        rg[q] = pack_bf16x2(dg[0], dg[1]);
+        ru[q] = pack_bf16x2(du[0], du[1]);
+    }
+    og = make_uint4(rg[0], rg[1], rg[2], rg[3]);
+    ou = make_uint4(ru[0], ru[1], ru[2], ru[3]);
+}
+
 }  // namespace moe

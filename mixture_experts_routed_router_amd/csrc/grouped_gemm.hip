@@ -229,7 +229,8 @@ struct TileArgs {
     const uint16_t* a_tile;   // A + row0 * K (gathering A: the token matrix x itself)
     const char* w_exp;        // W + e * (W rows per expert) * K elements (as bytes)
     const float* w_scale;     // FP8 weights: the expert's scales, one per 64 W rows
-    uint16_t* c_tile;         // C + row0 * N
+    uint16_t* c_tile;         // C + row0 * N (SwiGLU backward: dgu + row0 * 2N)
+    const uint16_t* gu_tile;  // SwiGLU backward: gu + row0 * 2N
     int row0, nt, rows_valid;
     int nvb;                  // this wave's 32-row blocks that hold segment rows (0..4)
 };
@@ -366,7 +367,7 @@ struct WaveCtx {
 // an 8-byte store. This wave's stores of the previous tile (s_prev of them) were
 // issued after the prefetched stages; vector-memory operations complete in issue
 // order, so a wait for a prefetched stage may leave those stores in flight.
-template <bool GLU, bool GATHER, bool W8, int NV>
+template <bool GLU, bool GATHER, bool W8, bool SWB, int NV>
 __device__ __forceinline__ int run_tile(const WaveCtx& w, const TileArgs& ta, const TileArgs& tn,
                                         int base, bool prefetched, bool pf_next, int s_prev,
                                         const int32_t* __restrict__ row_token, int tb) {
@@ -574,6 +575,7 @@ __device__ __forceinline__ int run_tile(const WaveCtx& w, const TileArgs& ta, co
         asm volatile("" : "+s"(rows_valid), "+s"(n_cols), "+s"(nt), "+s"(zero), "+v"(ln));
         const float* w_scale = ta.w_scale + zero;
         uint16_t* c_tile = ta.c_tile + zero;
+        const uint16_t* gu_tile = ta.gu_tile + zero;
         const QuadSel qs = quad_sel(ln);
         const int out_row = (ln >> 5) * 4 + (ln & 3);  // this lane's row in an 8-row group
         // byte offset of this lane's 8 bytes from the group's (row 0, column 0)
@@ -629,8 +631,8 @@ __device__ __forceinline__ int run_tile(const WaveCtx& w, const TileArgs& ta, co
             static_assert(GLU || OB == 2, "two 32-column blocks per wave");
             const bool odd = (ln & 4) != 0;
             // byte offset of this lane's 16 bytes from the group's (row 0, column 0)
-            const uint32_t st_off =
-                (uint32_t)((out_row * n_cols + (odd ? 32 : 0) + ((ln & 31) >> 3) * 8) * 2);
+            const int st_off_col = (odd ? 32 : 0) + ((ln & 31) >> 3) * 8;  // this lane's first column
+            const uint32_t st_off = (uint32_t)((out_row * n_cols + st_off_col) * 2);
             float s0 = 1.0f, s1 = 1.0f;
             if (W8) {
                 s0 = w_scale[col0 >> 6];
@@ -654,9 +656,25 @@ __device__ __forceinline__ int run_tile(const WaveCtx& w, const TileArgs& ta, co
                     const uint32_t g0 = lane_xor4(odd ? a0 : b0, odd);
                     const uint32_t g1 = lane_xor4(odd ? a1 : b1, odd);
                     const uint4 o = odd ? make_uint4(g0, g1, b0, b1) : make_uint4(a0, a1, g0, g1);
-                    char* grp0 = (char*)(c_tile + ((int64_t)r0 * n_cols + col0));
-                    if (out_row < rows_valid - r0) *(uint4*)(grp0 + st_off) = o;
-                    ++stores;
+                    if (SWB) {
+                        // o = this lane's 8 columns of dh (bf16, as the unfused path stores
+                        // them); g and u at the same row and columns of gu [rows, 2N] give
+                        // dg and du, written to the same places of dgu
+                        const int64_t roff = (int64_t)(r0 + out_row) * (2 * n_cols) + col0 + (st_off_col);
+                        if (out_row < rows_valid - r0) {
+                            const uint4 gv = *(const uint4*)(gu_tile + roff);
+                            const uint4 uv = *(const uint4*)(gu_tile + roff + n_cols);
+                            uint4 og, ou;
+                            swiglu_bwd_x8(gv, uv, o, og, ou);
+                            *(uint4*)(c_tile + roff) = og;
+                            *(uint4*)(c_tile + roff + n_cols) = ou;
+                        }
+                        stores += 2;
+                    } else {
+                        char* grp0 = (char*)(c_tile + ((int64_t)r0 * n_cols + col0));
+                        if (out_row < rows_valid - r0) *(uint4*)(grp0 + st_off) = o;
+                        ++stores;
+                    }
                 }
             }
         }
@@ -664,11 +682,12 @@ __device__ __forceinline__ int run_tile(const WaveCtx& w, const TileArgs& ta, co
     return stores;
 }
 
-template <bool GLU, bool GATHER, bool W8>
+template <bool GLU, bool GATHER, bool W8, bool SWB>
 __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ row_token,
     const void* __restrict__ W, const float* __restrict__ w_scale, const int32_t* __restrict__ offsets,
-    int E, int K, int N, uint16_t* __restrict__ C) {
+    int E, int K, int N, uint16_t* __restrict__ C, const uint16_t* __restrict__ gu) {
+    static_assert(!SWB || (!GLU && !GATHER && !W8), "the SwiGLU backward epilogue follows the plain bf16 GEMM");
     __shared__ __attribute__((aligned(1024))) uint16_t lds[kLdsElems];
     __shared__ int32_t tile_start[kMaxE + 1];
     __shared__ int32_t seg_start[kMaxE + 1];
@@ -767,7 +786,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_kernel(
         ta.row0 = row0;
         ta.w_exp = (const char*)W + (int64_t)e * w_stride;
         ta.w_scale = W8 ? w_scale + (int64_t)e * (NW / 64) : w_scale;
-        ta.c_tile = C + (int64_t)row0 * N;
+        ta.c_tile = C + (int64_t)row0 * (SWB ? 2 * N : N);
+        ta.gu_tile = SWB ? gu + (int64_t)row0 * 2 * N : gu;
         ta.nt = nt;
         ta.rows_valid = min(32 * (bq + (mt < br ? 1 : 0)), seg1 - row0);
         // live 32-row blocks of this wave: wave row wm owns blocks 2i + wm
@@ -791,11 +811,11 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_kernel(
         const bool pf_next = has_next && cross;
         int s;
         switch (cur.nvb) {
-            case 4: s = run_tile<GLU, GATHER, W8, 4>(w, cur, nxt, base, prefetched, pf_next, s_prev, row_token, tb); break;
-            case 3: s = run_tile<GLU, GATHER, W8, 3>(w, cur, nxt, base, prefetched, pf_next, s_prev, row_token, tb); break;
-            case 2: s = run_tile<GLU, GATHER, W8, 2>(w, cur, nxt, base, prefetched, pf_next, s_prev, row_token, tb); break;
-            case 1: s = run_tile<GLU, GATHER, W8, 1>(w, cur, nxt, base, prefetched, pf_next, s_prev, row_token, tb); break;
-            default: s = run_tile<GLU, GATHER, W8, 0>(w, cur, nxt, base, prefetched, pf_next, s_prev, row_token, tb); break;
+            case 4: s = run_tile<GLU, GATHER, W8, SWB, 4>(w, cur, nxt, base, prefetched, pf_next, s_prev, row_token, tb); break;
+            case 3: s = run_tile<GLU, GATHER, W8, SWB, 3>(w, cur, nxt, base, prefetched, pf_next, s_prev, row_token, tb); break;
+            case 2: s = run_tile<GLU, GATHER, W8, SWB, 2>(w, cur, nxt, base, prefetched, pf_next, s_prev, row_token, tb); break;
+            case 1: s = run_tile<GLU, GATHER, W8, SWB, 1>(w, cur, nxt, base, prefetched, pf_next, s_prev, row_token, tb); break;
+            default: s = run_tile<GLU, GATHER, W8, SWB, 0>(w, cur, nxt, base, prefetched, pf_next, s_prev, row_token, tb); break;
         }
         if (!has_next) break;
         s_prev = s;
@@ -832,13 +852,13 @@ hipError_t launch_grouped_glu_gemm(const uint16_t* x_perm, const void* w_gu, con
                                    const int32_t* offsets, int E, int H, int I, uint16_t* h,
                                    hipStream_t stream) {
     if (scale)
-        hipLaunchKernelGGL((grouped_gemm_kernel<true, false, true>), dim3(persistent_grid()),
+        hipLaunchKernelGGL((grouped_gemm_kernel<true, false, true, false>), dim3(persistent_grid()),
                            dim3(kGemmThreads), 0, stream, x_perm, (const int32_t*)nullptr, w_gu, scale,
-                           offsets, E, H, I, h);
+                           offsets, E, H, I, h, (const uint16_t*)nullptr);
     else
-        hipLaunchKernelGGL((grouped_gemm_kernel<true, false, false>), dim3(persistent_grid()),
+        hipLaunchKernelGGL((grouped_gemm_kernel<true, false, false, false>), dim3(persistent_grid()),
                            dim3(kGemmThreads), 0, stream, x_perm, (const int32_t*)nullptr, w_gu, scale,
-                           offsets, E, H, I, h);
+                           offsets, E, H, I, h, (const uint16_t*)nullptr);
     return hipGetLastError();
 }
 
@@ -846,11 +866,11 @@ hipError_t launch_grouped_glu_gemm_gather(const uint16_t* x, const int32_t* row_
                                           const float* scale, const int32_t* offsets, int E, int H,
                                           int I, uint16_t* h, hipStream_t stream) {
     if (scale)
-        hipLaunchKernelGGL((grouped_gemm_kernel<true, true, true>), dim3(persistent_grid()),
-                           dim3(kGemmThreads), 0, stream, x, row_token, w_gu, scale, offsets, E, H, I, h);
+        hipLaunchKernelGGL((grouped_gemm_kernel<true, true, true, false>), dim3(persistent_grid()),
+                           dim3(kGemmThreads), 0, stream, x, row_token, w_gu, scale, offsets, E, H, I, h, (const uint16_t*)nullptr);
     else
-        hipLaunchKernelGGL((grouped_gemm_kernel<true, true, false>), dim3(persistent_grid()),
-                           dim3(kGemmThreads), 0, stream, x, row_token, w_gu, scale, offsets, E, H, I, h);
+        hipLaunchKernelGGL((grouped_gemm_kernel<true, true, false, false>), dim3(persistent_grid()),
+                           dim3(kGemmThreads), 0, stream, x, row_token, w_gu, scale, offsets, E, H, I, h, (const uint16_t*)nullptr);
     return hipGetLastError();
 }
 
@@ -858,13 +878,24 @@ hipError_t launch_grouped_down_gemm(const uint16_t* h, const void* w_d, const fl
                                     const int32_t* offsets, int E, int H, int I, uint16_t* y,
                                     hipStream_t stream) {
     if (scale)
-        hipLaunchKernelGGL((grouped_gemm_kernel<false, false, true>), dim3(persistent_grid()),
+        hipLaunchKernelGGL((grouped_gemm_kernel<false, false, true, false>), dim3(persistent_grid()),
                            dim3(kGemmThreads), 0, stream, h, (const int32_t*)nullptr, w_d, scale,
-                           offsets, E, I, H, y);
+                           offsets, E, I, H, y, (const uint16_t*)nullptr);
     else
-        hipLaunchKernelGGL((grouped_gemm_kernel<false, false, false>), dim3(persistent_grid()),
+        hipLaunchKernelGGL((grouped_gemm_kernel<false, false, false, false>), dim3(persistent_grid()),
                            dim3(kGemmThreads), 0, stream, h, (const int32_t*)nullptr, w_d, scale,
-                           offsets, E, I, H, y);
+                           offsets, E, I, H, y, (const uint16_t*)nullptr);
+    return hipGetLastError();
+}
+
+// dgu = SwiGLU backward of dh = dy W_d^T-as-stored, without writing dh: the plain
+// GEMM over W_d_t [E, I, H] (K = H, N = I) whose epilogue reads gu [P_max, 2I].
+hipError_t launch_grouped_gemm_swiglu_bwd(const uint16_t* dy, const uint16_t* w_d_t, const uint16_t* gu,
+                                          const int32_t* offsets, int E, int H, int I, uint16_t* dgu,
+                                          hipStream_t stream) {
+    hipLaunchKernelGGL((grouped_gemm_kernel<false, false, false, true>), dim3(persistent_grid()),
+                       dim3(kGemmThreads), 0, stream, dy, (const int32_t*)nullptr, (const void*)w_d_t,
+                       (const float*)nullptr, offsets, E, H, I, dgu, gu);
     return hipGetLastError();
 }
 

@@ -48,6 +48,7 @@ def lib():
     lib.moe_grouped_gemm.argtypes = [vp, vp, vp, vp, i32, i32, i32, i64, vp, vp]
     lib.moe_swiglu.argtypes = [vp, vp, i32, i32, i64, vp, vp]
     lib.moe_swiglu_backward.argtypes = [vp, vp, vp, i32, i32, i64, vp, vp]
+    lib.moe_grouped_gemm_swiglu_backward.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i64, vp, vp]
     lib.moe_transpose_experts.argtypes = [vp, i64, i32, i32, vp, vp]
     lib.moe_combine_backward.argtypes = [vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i64, vp, vp, vp]
     lib.moe_route_backward.argtypes = [vp, vp, vp, i64, i32, i32, vp, vp]
@@ -182,6 +183,12 @@ def test_training_validation(lib):
     assert lib.moe_grouped_gemm(FAKE, FAKE, FAKE, FAKE, 8, 100, 256, 1000, FAKE, None) == SHAPE   # K % 64
     assert lib.moe_swiglu(FAKE, FAKE, 4, 96, 100, FAKE, None) == SHAPE                             # I % 64
     assert lib.moe_swiglu_backward(FAKE, None, FAKE, 4, 128, 100, FAKE, None) == NULLP
+    fn = lib.moe_grouped_gemm_swiglu_backward
+    assert fn(FAKE, FAKE, None, FAKE, FAKE, 8, 128, 256, 1000, FAKE, None) == NULLP          # gu
+    assert fn(FAKE, FAKE, FAKE + 8, FAKE, FAKE, 8, 128, 256, 1000, FAKE, None) == MISALIGNED  # gu
+    assert fn(FAKE, FAKE, FAKE, FAKE, FAKE, 8, 128, 200, 1000, FAKE, None) == SHAPE           # I % 64
+    assert fn(FAKE, FAKE, FAKE, FAKE, FAKE, 8, 100, 256, 1000, FAKE, None) == SHAPE           # H % 64
+    assert fn(FAKE, FAKE, FAKE, FAKE, FAKE, 8, 128, 256, 1000, None, None) == NULLP           # dgu
     assert lib.moe_transpose_experts(FAKE, 2, 64, 100, FAKE, None) == SHAPE
     assert lib.moe_transpose_experts(FAKE + 8, 2, 64, 64, FAKE, None) == MISALIGNED
     assert lib.moe_combine_backward(FAKE, FAKE, FAKE, FAKE, None, FAKE, 4, 128, 8, 2, 100, FAKE, FAKE,

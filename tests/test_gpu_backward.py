@@ -76,6 +76,43 @@ def test_grouped_gemm_plain(gpu_lib, case):
     assert_close_bf16(host_f64(c[:P])[rows], ref[rows], f"c[{name}]")
 
 
+SWB_CASES = [
+    # name, counts, align, H (the GEMM's K), I (its N)
+    ("dh_small", [0, 130, 257, 31, 64], 32, 512, 192),
+    ("align8", [5, 0, 129, 3, 300], 8, 384, 256),
+    ("H2880_I640", [16, 9, 28, 0, 40], 32, 2880, 640),
+    ("many_experts", _many_counts(40, 200, 43), 32, 256, 128),
+]
+
+
+@pytest.mark.parametrize("case", SWB_CASES, ids=[c[0] for c in SWB_CASES])
+def test_grouped_gemm_swiglu_backward(gpu_lib, case):
+    """dgu from the dh GEMM with the SwiGLU backward in its epilogue: bit for bit
+    the two-step result (grouped_gemm, then swiglu_backward), and against the
+    oracle's SwiGLU backward of its float64 dh (two roundings: dh and dgu)."""
+    name, counts, align, H, I = case
+    _say(f"grouped gemm + swiglu backward {name}")
+    counts, offsets, E, P, P_max = _layout(counts, align)
+    rows = _rows_of(counts, offsets)
+    dy = np.zeros((P_max, H), np.uint16)          # pad rows zero, as moe_combine_backward leaves them
+    dy[rows] = gen.random_bf16((len(rows), H), seed=31)
+    w_d_t = gen.random_bf16((E, I, H), seed=32, std=0.02)
+    gu = gen.random_bf16((P_max, 2 * I), seed=33, std=2.0)
+    cd, od = dev(counts), dev(offsets)
+    dgu = gpu_lib.grouped_gemm_swiglu_backward(dev_bf16(dy), dev_bf16(w_d_t), dev_bf16(gu), cd, od)
+    dh2 = gpu_lib.grouped_gemm(dev_bf16(dy), dev_bf16(w_d_t), cd, od)
+    dgu2 = gpu_lib.swiglu_backward(dh2, dev_bf16(gu), od)
+    torch.cuda.synchronize()
+    got, two = host_bits(dgu[:P]), host_bits(dgu2[:P])
+    assert (got == two).all(), f"fused and two-step dgu differ in {int((got != two).sum())} elements"
+    f = lambda b: gen.bf16_bits_to_f32(b).astype(np.float64)  # noqa: E731
+    dh_ref = oracle.down(f(dy), w_d_t, counts, offsets)
+    ref = oracle.swiglu_bwd(dh_ref[rows], f(gu)[rows])
+    g = host_f64(dgu[:P])[rows]
+    assert_close_bf16(g[:, :I], ref[:, :I], f"dg[{name}]", tight=False)
+    assert_close_bf16(g[:, I:], ref[:, I:], f"du[{name}]", tight=False)
+
+
 @pytest.mark.parametrize("E,R,C", [(1, 64, 64), (3, 128, 320), (2, 2880, 640)])
 def test_transpose_experts(gpu_lib, E, R, C):
     w = gen.random_bf16((E, R, C), seed=R + C)
@@ -194,9 +231,9 @@ def test_grouped_wgrad(gpu_lib, case, gather):
 # the whole training step
 # --------------------------------------------------------------------------------------
 
-def _train(gpu_lib, d):
+def _train(gpu_lib, d, fuse=True):
     cfg = d["cfg"]
-    layer = gpu_lib.MoETrainingLayer(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.align)
+    layer = gpu_lib.MoETrainingLayer(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.align, fuse_swiglu_backward=fuse)
     w_gu, w_d = dev_bf16(d["w_gu"]), dev_bf16(d["w_d"])
     out = layer.forward(dev_bf16(d["x"]), dev(d["logits"]), w_gu, w_d)
     dout = gen.random_bf16((cfg.T, cfg.H), seed=cfg.seed + 500)
@@ -231,6 +268,21 @@ def test_training_step_small(gpu_lib, cfg):
             _close(dwd.cpu().numpy(), rdwd, f"dW_d[{cfg.name}]")]
     _say(f"  {cfg.name}: max|d|/max|ref| dx {rels[0]:.2e} dlogits {rels[1]:.2e} "
          f"dW_gu {rels[2]:.2e} dW_d {rels[3]:.2e}")
+
+
+@pytest.mark.parametrize("cfg", [TRAIN_SMALL[3], TRAIN_SMALL[5]], ids=["align8", "skewed_small"])
+def test_training_step_fused_matches_two_step(gpu_lib, cfg):
+    """The backward with the fused dh GEMM + SwiGLU backward gives the same
+    gradients, bit for bit, as the two-step backward (dh written, then
+    swiglu_backward)."""
+    _say(f"fused vs two-step backward {cfg.name}")
+    d = gen.make_inputs(cfg)
+    _, _, _, a = _train(gpu_lib, d, fuse=True)
+    a = [t.clone() for t in a]
+    _, _, _, b = _train(gpu_lib, d, fuse=False)
+    for name, x, y in zip(("dx", "dlogits", "dW_gu", "dW_d"), a, b):
+        assert torch.equal(x.view(torch.int16) if x.dtype == torch.bfloat16 else x.view(torch.int32),
+                           y.view(torch.int16) if y.dtype == torch.bfloat16 else y.view(torch.int32)), name
 
 
 def test_training_step_full_size_sampled(gpu_lib):
