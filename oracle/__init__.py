@@ -68,6 +68,7 @@ def _load(path: str):
     lib.moe_oracle_route_bwd.argtypes = [_i32p, _f64p, _f64p, i64, i32, i32, _f64p]
     lib.moe_oracle_swiglu.argtypes = [_f64p, i64, i32, _f64p]
     lib.moe_oracle_swiglu_bwd.argtypes = [_f64p, _f64p, i64, i32, _f64p]
+    lib.moe_oracle_swiglu_clamped.argtypes = [_f64p, i64, i32, ctypes.c_double, _f64p]
     lib.moe_oracle_gemm_nn.argtypes = [_f64p, _u16p, _i32p, _i32p, i32, i32, i32, _f64p]
     lib.moe_oracle_wgrad.argtypes = [_f64p, _f64p, _i32p, _i32p, i32, i32, i32, _f64p]
     lib.moe_oracle_permute_bwd.argtypes = [_f64p, _i32p, i64, i32, i32, i64, _f64p]
@@ -81,7 +82,7 @@ def _load(path: str):
                  "moe_oracle_forward", "moe_oracle_fp8_encode", "moe_oracle_fp8_decode",
                  "moe_oracle_quantize_fp8", "moe_oracle_dequantize_fp8", "moe_oracle_glu_w64",
                  "moe_oracle_down_w64", "moe_oracle_combine_bwd", "moe_oracle_route_bwd",
-                 "moe_oracle_swiglu", "moe_oracle_swiglu_bwd", "moe_oracle_gemm_nn",
+                 "moe_oracle_swiglu", "moe_oracle_swiglu_bwd", "moe_oracle_swiglu_clamped", "moe_oracle_gemm_nn",
                  "moe_oracle_wgrad", "moe_oracle_permute_bwd", "moe_oracle_backward",
                  "moe_oracle_router_logits"):
         getattr(lib, name).restype = ctypes.c_int
@@ -355,6 +356,16 @@ def swiglu(gu, lib=None):
     return h
 
 
+def swiglu_clamped(gu, limit: float, lib=None):
+    """h [rows, I] = silu(min(g, limit)) * clip(u, -limit, limit) from gu = [g | u]."""
+    gu = _f64(gu)
+    rows, two_i = gu.shape
+    h = np.empty((rows, two_i // 2))
+    _check((lib or _lib()).moe_oracle_swiglu_clamped(_p(gu, _f64p), rows, two_i // 2, float(limit), _p(h, _f64p)),
+           "swiglu_clamped")
+    return h
+
+
 def swiglu_bwd(dh, gu, lib=None):
     """dgu [rows, 2I] = [dh u silu'(g) | dh silu(g)]."""
     dh, gu = _f64(dh), _f64(gu)
@@ -482,6 +493,9 @@ class Oracle:
 
     def swiglu_bwd(self, *a, **kw):
         return swiglu_bwd(*a, lib=self.lib, **kw)
+
+    def swiglu_clamped(self, *a, **kw):
+        return swiglu_clamped(*a, lib=self.lib, **kw)
 
     def gemm_nn(self, *a, **kw):
         return gemm_nn(*a, lib=self.lib, **kw)

@@ -563,6 +563,25 @@ int moe_oracle_swiglu(const double *gu, int64_t rows, int32_t I, double *h) {
     return 0;
 }
 
+/* Clamped SwiGLU on rows of gu = [g | u] [prime-rl PR 3885, Changes: the
+ * DeepSeek-V4.1 recipes run a clamped SwiGLU]. The page names the clamp but not
+ * its form or constant; read here as a cap of the gate pre-activation at +limit
+ * and a clip of the up projection to [-limit, +limit] ahead of the plain SwiGLU:
+ *   h[p,i] = silu(min(g, limit)) * min(max(u, -limit), limit),   limit >= 0.
+ * limit = +inf is the plain SwiGLU. */
+int moe_oracle_swiglu_clamped(const double *gu, int64_t rows, int32_t I, double limit, double *h) {
+    if (!gu || !h || rows < 0 || I < 1 || !(limit >= 0.0)) return ORACLE_EINVAL;
+    for (int64_t p = 0; p < rows; ++p)
+        for (int32_t i = 0; i < I; ++i) {
+            double g = gu[p * 2 * I + i], u = gu[p * 2 * I + I + i];
+            if (g > limit) g = limit;
+            if (u > limit) u = limit;
+            if (u < -limit) u = -limit;
+            h[p * I + i] = silu(g) * u;
+        }
+    return 0;
+}
+
 int moe_oracle_swiglu_bwd(const double *dh, const double *gu, int64_t rows, int32_t I, double *dgu) {
     if (!dh || !gu || !dgu || rows < 0 || I < 1) return ORACLE_EINVAL;
     for (int64_t p = 0; p < rows; ++p)

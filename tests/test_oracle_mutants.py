@@ -11,6 +11,17 @@ from mixture_experts_routed_router_amd import inputs as gen
 import test_oracle_pins as pins
 
 MUTANTS = {
+    # clamped SwiGLU: the up projection clipped from above only
+    "clamp_up_one_sided": ([("            if (u < -limit) u = -limit;\n", "")], [pins.check_swiglu_clamped]),
+    # clamped SwiGLU: the gate clipped from below too
+    "clamp_gate_both_sides": ([("            if (g > limit) g = limit;\n",
+                                "            if (g > limit) g = limit;\n            if (g < -limit) g = -limit;\n")],
+                              [pins.check_swiglu_clamped]),
+    # clamped SwiGLU: the cap applied to silu(g) instead of g
+    "clamp_after_silu": ([("            if (g > limit) g = limit;\n", ""),
+                          ("if (u < -limit) u = -limit;\n            h[p * I + i] = silu(g) * u;",
+                           "if (u < -limit) u = -limit;\n            h[p * I + i] = fmin(silu(g), limit) * u;")],
+                         [pins.check_swiglu_clamped]),
     # routing: ties to the higher id instead of the lower
     "tie_to_higher_id": ([("return a < b;", "return a > b;")], [pins.check_topk_brute_force]),
     # routing: a dropped term in the softmax denominator

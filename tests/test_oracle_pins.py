@@ -564,6 +564,32 @@ def check_swiglu_bwd_derivative(orc):
         assert np.allclose(dgu[:, i], fd, rtol=1e-7, atol=1e-8), i
 
 
+def check_swiglu_clamped(orc):
+    """Clamped SwiGLU: textbook sigmoid values where the gate is capped and where it
+    is not, the up clip on both sides, a zero limit, and limit = +inf and
+    in-range inputs reducing to the plain SwiGLU."""
+    sig1 = 0.7310585786300049      # 1 / (1 + e^-1)
+    sigm3 = 0.04742587317756678    # 1 / (1 + e^3)
+    # rows of [g | u] with I = 1
+    gu = np.array([[50.0, 5.0],     # g capped to 1, u clipped to 1: silu(1) * 1 = sigma(1)
+                   [50.0, -5.0],    # u clipped to -1 from below
+                   [-3.0, -0.5],    # nothing clamped (g below the cap, |u| < 1): silu(-3) * -0.5
+                   [1.0, 1.0]])     # exactly at the limit: unchanged
+    h = orc.swiglu_clamped(gu, 1.0)[:, 0]
+    assert h[0] == pytest.approx(sig1, rel=1e-15)
+    assert h[1] == pytest.approx(-sig1, rel=1e-15)
+    assert h[2] == pytest.approx(-3.0 * sigm3 * -0.5, rel=1e-14)
+    assert h[3] == pytest.approx(sig1, rel=1e-15)
+    rng = np.random.default_rng(9)
+    big = rng.standard_normal((7, 10)) * 20
+    assert np.all(orc.swiglu_clamped(big, 0.0) == 0.0)                         # u clipped to 0
+    assert np.array_equal(orc.swiglu_clamped(big, np.inf), orc.swiglu(big))  # no clamp
+    small = rng.uniform(-0.9, 0.9, (7, 10))
+    assert np.array_equal(orc.swiglu_clamped(small, 1.0), orc.swiglu(small))  # inside the limits
+    with pytest.raises(RuntimeError):
+        orc.swiglu_clamped(small, -1.0)
+
+
 # --------------------------------------------------------------------------------------
 # tests
 # --------------------------------------------------------------------------------------
@@ -731,3 +757,7 @@ def test_gaussian_generator_balanced(orc):
     idx, _ = orc.route_topk(gen.draw_logits(cfg), cfg.k)
     counts = np.bincount(idx.reshape(-1), minlength=cfg.E)
     assert counts.min() > 400 and counts.max() < 640  # mean 512, binomial spread
+
+
+def test_swiglu_clamped(orc):
+    check_swiglu_clamped(orc)
