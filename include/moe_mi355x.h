@@ -20,6 +20,9 @@
  *   moe_grouped_glu_gemm_fp8w, moe_grouped_glu_gemm_gather_fp8w,
  *   moe_grouped_down_gemm_fp8w
  *
+ * The clamped-SwiGLU variant of the gate/up GEMM:
+ *   moe_grouped_glu_gemm_clamped
+ *
  * The router projection fused with top-k (logits need not reach memory):
  *   moe_router_prepare, moe_router_topk
  *
@@ -89,7 +92,8 @@ typedef enum moe_status {
     MOE_ERR_SIZE_OVERFLOW = 4,      /* P_max too small, or rows would reach 2^31 */
     MOE_ERR_MISALIGNED_POINTER = 5, /* a tensor pointer is not 16-byte aligned */
     MOE_ERR_WORKSPACE_TOO_SMALL = 6,
-    MOE_ERR_HIP = 7                 /* a HIP call failed; see moe_last_error_message */
+    MOE_ERR_HIP = 7,                /* a HIP call failed; see moe_last_error_message */
+    MOE_ERR_INVALID_VALUE = 8       /* a scalar argument is out of range (see each call) */
 } moe_status;
 
 #define MOE_MAX_K 32    /* largest top-k */
@@ -290,6 +294,21 @@ moe_status moe_router_prepare(const float *w_router, int32_t H, int32_t E, moe_b
 moe_status moe_router_topk(const moe_bf16 *x, const moe_bf16 *w_hi, const moe_bf16 *w_lo, int64_t T, int32_t H,
                            int32_t E, int32_t k, float *logits, int32_t *topk_idx, float *topk_w,
                            moe_stream_t stream);
+
+/*
+ * The gate/up GEMM with a clamped SwiGLU [prime-rl PR 3885, Changes: the V4.1
+ * recipes run a clamped SwiGLU]; the pages give neither its form nor its constant,
+ * so the limit is an argument and the form is the plainest reading -- the gate
+ * pre-activation capped at +limit, the up projection clipped to [-limit, limit]:
+ *   h[p, i] = bf16_rne( silu(min(g, limit)) * min(max(u, -limit), limit) )
+ * with g, u the fp32 sums of moe_grouped_glu_gemm.  limit = +inf is exactly
+ * moe_grouped_glu_gemm.  Arguments and shapes as moe_grouped_glu_gemm; limit
+ * must be >= 0 (a NaN or negative limit: MOE_ERR_INVALID_VALUE).
+ */
+moe_status moe_grouped_glu_gemm_clamped(const moe_bf16 *x_perm, const moe_bf16 *w_gate_up,
+                                        const int32_t *expert_counts, const int32_t *expert_offsets, int32_t E,
+                                        int32_t H, int32_t I, int64_t P_max, float limit, moe_bf16 *h,
+                                        moe_stream_t stream);
 
 /*
  * ---- training: forward with saved gate/up output, and the backward ----

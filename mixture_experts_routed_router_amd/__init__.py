@@ -12,7 +12,7 @@ _API = ("route_topk", "permute", "grouped_glu_gemm", "grouped_down_gemm", "combi
         "moe_forward", "MoELayer", "MoEError", "Layout", "padded_rows_max",
         "permute_workspace_size", "load", "grouped_glu_gemm_gather", "FP8Weights", "quantize_fp8",
         "grouped_glu_gemm_fp8w", "grouped_glu_gemm_gather_fp8w", "grouped_down_gemm_fp8w",
-        "grouped_gemm", "grouped_gemm_swiglu_backward", "swiglu", "swiglu_backward", "transpose_experts", "combine_backward",
+        "grouped_gemm", "grouped_gemm_swiglu_backward", "grouped_glu_gemm_clamped", "swiglu", "swiglu_backward", "transpose_experts", "combine_backward",
         "route_backward", "permute_backward", "grouped_wgrad", "MoETrainingLayer", "router_prepare",
         "router_topk")
 

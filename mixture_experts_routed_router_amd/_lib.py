@@ -67,6 +67,8 @@ def load():
     lib.moe_grouped_down_gemm_fp8w.argtypes = [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32,
                                                _c_i32, _c_i64, _c_vp, _c_vp]
     lib.moe_grouped_gemm.argtypes = [_c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i64, _c_vp, _c_vp]
+    lib.moe_grouped_glu_gemm_clamped.argtypes = [_c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i64,
+                                                 ctypes.c_float, _c_vp, _c_vp]
     lib.moe_grouped_gemm_swiglu_backward.argtypes = [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32,
                                                      _c_i64, _c_vp, _c_vp]
     lib.moe_swiglu.argtypes = [_c_vp, _c_vp, _c_i32, _c_i32, _c_i64, _c_vp, _c_vp]
@@ -87,7 +89,7 @@ def load():
                "moe_grouped_glu_gemm_gather_fp8w", "moe_grouped_down_gemm_fp8w", "moe_grouped_gemm",
                "moe_swiglu", "moe_swiglu_backward", "moe_transpose_experts", "moe_combine_backward",
                "moe_route_backward", "moe_permute_backward", "moe_grouped_wgrad", "moe_router_prepare",
-               "moe_router_topk", "moe_grouped_gemm_swiglu_backward"):
+               "moe_router_topk", "moe_grouped_gemm_swiglu_backward", "moe_grouped_glu_gemm_clamped"):
         getattr(lib, fn).restype = ctypes.c_int
     _LIB = lib
     return lib
@@ -231,6 +233,22 @@ def grouped_glu_gemm(x_perm, w_gate_up, counts, offsets, h=None, stream=None):
     _call("moe_grouped_glu_gemm", _ptr(x_perm, torch.bfloat16, "x_perm"),
           _ptr(w_gate_up, torch.bfloat16, "w_gate_up"), _ptr(counts, torch.int32, "counts", (E,)),
           _ptr(offsets, torch.int32, "offsets", (E + 1,)), E, H, I, P_max,
+          _ptr(h, torch.bfloat16, "h", (P_max, I)), _stream(stream))
+    return h
+
+
+def grouped_glu_gemm_clamped(x_perm, w_gate_up, counts, offsets, limit: float, h=None, stream=None):
+    """grouped_glu_gemm with a clamped SwiGLU: h = silu(min(g, limit)) * clip(u, -limit, limit)."""
+    P_max, H = x_perm.shape
+    E, two_i, H2 = w_gate_up.shape
+    I = two_i // 2
+    if H2 != H or two_i != 2 * I:
+        raise ValueError("w_gate_up must be [E, 2I, H]")
+    if h is None:
+        h = torch.empty((P_max, I), dtype=torch.bfloat16, device=x_perm.device)
+    _call("moe_grouped_glu_gemm_clamped", _ptr(x_perm, torch.bfloat16, "x_perm"),
+          _ptr(w_gate_up, torch.bfloat16, "w_gate_up"), _ptr(counts, torch.int32, "counts", (E,)),
+          _ptr(offsets, torch.int32, "offsets", (E + 1,)), E, H, I, P_max, float(limit),
           _ptr(h, torch.bfloat16, "h", (P_max, I)), _stream(stream))
     return h
 

@@ -23,6 +23,8 @@ hipError_t launch_grouped_gemm_small(bool, const uint16_t*, const int32_t*, cons
 hipError_t launch_combine_bwd(const uint16_t*, const uint16_t*, const int32_t*, const float*, const int32_t*,
                               const int32_t*, int64_t, int, int, int, int64_t, uint16_t*, float*, hipStream_t);
 hipError_t launch_route_bwd(const int32_t*, const float*, const float*, int64_t, int, int, float*, hipStream_t);
+hipError_t launch_grouped_glu_gemm_clamped(const uint16_t*, const uint16_t*, const int32_t*, int, int, int, float,
+                                           uint16_t*, hipStream_t);
 hipError_t launch_grouped_gemm_swiglu_bwd(const uint16_t*, const uint16_t*, const uint16_t*, const int32_t*, int,
                                           int, int, uint16_t*, hipStream_t);
 hipError_t launch_swiglu(const uint16_t*, const uint16_t*, const int32_t*, int, int, int64_t, uint16_t*,
@@ -136,6 +138,7 @@ const char* moe_status_string(int s) {
         case MOE_ERR_MISALIGNED_POINTER: return "MOE_ERR_MISALIGNED_POINTER";
         case MOE_ERR_WORKSPACE_TOO_SMALL: return "MOE_ERR_WORKSPACE_TOO_SMALL";
         case MOE_ERR_HIP: return "MOE_ERR_HIP";
+        case MOE_ERR_INVALID_VALUE: return "MOE_ERR_INVALID_VALUE";
         default: return "MOE_ERR_UNKNOWN";
     }
 }
@@ -238,6 +241,18 @@ static moe_status check_gather(const int32_t* row_token, int64_t T, int32_t H) {
         return fail(MOE_ERR_SIZE_OVERFLOW, "T*H*2 = %llu bytes of x reach 2^32 (32-bit offsets)",
                     (unsigned long long)((uint64_t)T * (uint64_t)H * 2u));
     return MOE_OK;
+}
+
+moe_status moe_grouped_glu_gemm_clamped(const moe_bf16* x_perm, const moe_bf16* w_gate_up,
+                                        const int32_t* expert_counts, const int32_t* expert_offsets, int32_t E,
+                                        int32_t H, int32_t I, int64_t P_max, float limit, moe_bf16* h,
+                                        moe_stream_t stream) {
+    moe_status s = check_gemm(x_perm, w_gate_up, expert_counts, expert_offsets, E, H, I, P_max, h);
+    if (s != MOE_OK) return s;
+    if (!(limit >= 0.0f)) return fail(MOE_ERR_INVALID_VALUE, "limit=%g must be >= 0", (double)limit);
+    return hip_status(moe::launch_grouped_glu_gemm_clamped(x_perm, w_gate_up, expert_offsets, E, H, I, limit, h,
+                                                           (hipStream_t)stream),
+                      "moe_grouped_glu_gemm_clamped launch");
 }
 
 moe_status moe_grouped_glu_gemm_gather(const moe_bf16* x, const int32_t* row_token,

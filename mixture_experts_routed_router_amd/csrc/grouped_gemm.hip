@@ -350,6 +350,7 @@ struct WaveCtx {
     int rd_off[KSTEPS];
     int rd8_off;         // FP8 B: byte offset of this lane's 16 codes within a 32-row block
     int32_t* tok_lds;    // gathering A: [2][kWaves][kTokSlots] token buffers
+    float glu_limit;     // GLU: clamp limit (+inf: the plain SwiGLU)
 };
 
 // One tile: the k loop through the LDS ring, then the epilogue. NV = number of
@@ -583,6 +584,8 @@ __device__ __forceinline__ int run_tile(const WaveCtx& w, const TileArgs& ta, co
         constexpr int OB = GLU ? NBN / 2 : NBN;    // 32-column output blocks per wave
         const int col0 = GLU ? nt * 128 + wn * (WTN / 2) : nt * BN + wn * WTN;
         if (GLU) {
+            const float lim = w.glu_limit;
+            const bool clamp = lim < INFINITY;  // uniform over the launch
 #pragma unroll
             for (int i = 0; i < NV; ++i) {
 #pragma unroll
@@ -607,6 +610,10 @@ __device__ __forceinline__ int run_tile(const WaveCtx& w, const TileArgs& ta, co
                             if (W8) {
                                 g *= sg;
                                 u *= su;
+                            }
+                            if (clamp) {  // gate capped at +limit, up clipped to [-limit, limit]
+                                g = fminf(g, lim);
+                                u = fminf(fmaxf(u, -lim), lim);
                             }
                             v[m] = g / (1.0f + __expf(-g)) * u;
                         }
@@ -686,7 +693,7 @@ template <bool GLU, bool GATHER, bool W8, bool SWB>
 __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ row_token,
     const void* __restrict__ W, const float* __restrict__ w_scale, const int32_t* __restrict__ offsets,
-    int E, int K, int N, uint16_t* __restrict__ C, const uint16_t* __restrict__ gu) {
+    int E, int K, int N, uint16_t* __restrict__ C, const uint16_t* __restrict__ gu, float glu_limit) {
     static_assert(!SWB || (!GLU && !GATHER && !W8), "the SwiGLU backward epilogue follows the plain bf16 GEMM");
     __shared__ __attribute__((aligned(1024))) uint16_t lds[kLdsElems];
     __shared__ int32_t tile_start[kMaxE + 1];
@@ -738,6 +745,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_kernel(
     w.wn = w.wave % WGN;
     w.grp = w.wave >> 2;  // == wm
     w.tok_lds = tok_lds;
+    w.glu_limit = glu_limit;
     // lane-constant parts of the MFMA operand addresses: logical piece
     // (2*ks + lane/32) of row (lane % 32) of each 32-row block
     {
@@ -854,11 +862,11 @@ hipError_t launch_grouped_glu_gemm(const uint16_t* x_perm, const void* w_gu, con
     if (scale)
         hipLaunchKernelGGL((grouped_gemm_kernel<true, false, true, false>), dim3(persistent_grid()),
                            dim3(kGemmThreads), 0, stream, x_perm, (const int32_t*)nullptr, w_gu, scale,
-                           offsets, E, H, I, h, (const uint16_t*)nullptr);
+                           offsets, E, H, I, h, (const uint16_t*)nullptr, INFINITY);
     else
         hipLaunchKernelGGL((grouped_gemm_kernel<true, false, false, false>), dim3(persistent_grid()),
                            dim3(kGemmThreads), 0, stream, x_perm, (const int32_t*)nullptr, w_gu, scale,
-                           offsets, E, H, I, h, (const uint16_t*)nullptr);
+                           offsets, E, H, I, h, (const uint16_t*)nullptr, INFINITY);
     return hipGetLastError();
 }
 
@@ -867,10 +875,10 @@ hipError_t launch_grouped_glu_gemm_gather(const uint16_t* x, const int32_t* row_
                                           int I, uint16_t* h, hipStream_t stream) {
     if (scale)
         hipLaunchKernelGGL((grouped_gemm_kernel<true, true, true, false>), dim3(persistent_grid()),
-                           dim3(kGemmThreads), 0, stream, x, row_token, w_gu, scale, offsets, E, H, I, h, (const uint16_t*)nullptr);
+                           dim3(kGemmThreads), 0, stream, x, row_token, w_gu, scale, offsets, E, H, I, h, (const uint16_t*)nullptr, INFINITY);
     else
         hipLaunchKernelGGL((grouped_gemm_kernel<true, true, false, false>), dim3(persistent_grid()),
-                           dim3(kGemmThreads), 0, stream, x, row_token, w_gu, scale, offsets, E, H, I, h, (const uint16_t*)nullptr);
+                           dim3(kGemmThreads), 0, stream, x, row_token, w_gu, scale, offsets, E, H, I, h, (const uint16_t*)nullptr, INFINITY);
     return hipGetLastError();
 }
 
@@ -880,11 +888,11 @@ hipError_t launch_grouped_down_gemm(const uint16_t* h, const void* w_d, const fl
     if (scale)
         hipLaunchKernelGGL((grouped_gemm_kernel<false, false, true, false>), dim3(persistent_grid()),
                            dim3(kGemmThreads), 0, stream, h, (const int32_t*)nullptr, w_d, scale,
-                           offsets, E, I, H, y, (const uint16_t*)nullptr);
+                           offsets, E, I, H, y, (const uint16_t*)nullptr, INFINITY);
     else
         hipLaunchKernelGGL((grouped_gemm_kernel<false, false, false, false>), dim3(persistent_grid()),
                            dim3(kGemmThreads), 0, stream, h, (const int32_t*)nullptr, w_d, scale,
-                           offsets, E, I, H, y, (const uint16_t*)nullptr);
+                           offsets, E, I, H, y, (const uint16_t*)nullptr, INFINITY);
     return hipGetLastError();
 }
 
@@ -895,7 +903,17 @@ hipError_t launch_grouped_gemm_swiglu_bwd(const uint16_t* dy, const uint16_t* w_
                                           hipStream_t stream) {
     hipLaunchKernelGGL((grouped_gemm_kernel<false, false, false, true>), dim3(persistent_grid()),
                        dim3(kGemmThreads), 0, stream, dy, (const int32_t*)nullptr, (const void*)w_d_t,
-                       (const float*)nullptr, offsets, E, H, I, dgu, gu);
+                       (const float*)nullptr, offsets, E, H, I, dgu, gu, INFINITY);
+    return hipGetLastError();
+}
+
+// The gate/up GEMM with a clamped SwiGLU in its epilogue: h = silu(min(g, limit)) *
+// clip(u, -limit, limit), bf16 x_perm and weights.
+hipError_t launch_grouped_glu_gemm_clamped(const uint16_t* x_perm, const uint16_t* w_gu, const int32_t* offsets,
+                                           int E, int H, int I, float limit, uint16_t* h, hipStream_t stream) {
+    hipLaunchKernelGGL((grouped_gemm_kernel<true, false, false, false>), dim3(persistent_grid()),
+                       dim3(kGemmThreads), 0, stream, x_perm, (const int32_t*)nullptr, (const void*)w_gu,
+                       (const float*)nullptr, offsets, E, H, I, h, (const uint16_t*)nullptr, limit);
     return hipGetLastError();
 }
 

@@ -13,7 +13,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "moe_mi355x.h")
 LIB = os.path.join(ROOT, "mixture_experts_routed_router_amd", "libmoe_mi355x.so")
 
-OK, NULLP, SHAPE, ALIGN, OVERFLOW, MISALIGNED, WORKSPACE, HIP = range(8)
+OK, NULLP, SHAPE, ALIGN, OVERFLOW, MISALIGNED, WORKSPACE, HIP, VALUE = range(9)
 
 
 def declared_functions():
@@ -49,6 +49,7 @@ def lib():
     lib.moe_swiglu.argtypes = [vp, vp, i32, i32, i64, vp, vp]
     lib.moe_swiglu_backward.argtypes = [vp, vp, vp, i32, i32, i64, vp, vp]
     lib.moe_grouped_gemm_swiglu_backward.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i64, vp, vp]
+    lib.moe_grouped_glu_gemm_clamped.argtypes = [vp, vp, vp, vp, i32, i32, i32, i64, ctypes.c_float, vp, vp]
     lib.moe_transpose_experts.argtypes = [vp, i64, i32, i32, vp, vp]
     lib.moe_combine_backward.argtypes = [vp, vp, vp, vp, vp, vp, i64, i32, i32, i32, i64, vp, vp, vp]
     lib.moe_route_backward.argtypes = [vp, vp, vp, i64, i32, i32, vp, vp]
@@ -75,6 +76,7 @@ def test_status_strings(lib):
     assert lib.moe_status_string(0) == b"MOE_OK"
     assert lib.moe_status_string(OVERFLOW) == b"MOE_ERR_SIZE_OVERFLOW"
     assert lib.moe_status_string(99) == b"MOE_ERR_UNKNOWN"
+    assert lib.moe_status_string(VALUE) == b"MOE_ERR_INVALID_VALUE"
 
 
 def test_padded_rows_and_workspace(lib):
@@ -133,6 +135,15 @@ def test_gemm_validation(lib):
         assert fn(FAKE, FAKE, FAKE, FAKE, 0, 128, 256, 1000, FAKE, None) == SHAPE
         assert fn(FAKE, FAKE, FAKE, FAKE, 8, 128, 256, 0, FAKE, None) == OVERFLOW
         assert fn(FAKE, FAKE + 8, FAKE, FAKE, 8, 128, 256, 1000, FAKE, None) == MISALIGNED
+
+
+def test_gemm_clamped_validation(lib):
+    fn = lib.moe_grouped_glu_gemm_clamped
+    assert fn(FAKE, FAKE, FAKE, FAKE, 8, 128, 256, 1000, 1.0, None, None) == NULLP
+    assert fn(FAKE, FAKE, FAKE, FAKE, 8, 128, 200, 1000, 1.0, FAKE, None) == SHAPE     # I % 64
+    assert fn(FAKE, FAKE, FAKE, FAKE, 8, 128, 256, 1000, -1.0, FAKE, None) == VALUE
+    assert fn(FAKE, FAKE, FAKE, FAKE, 8, 128, 256, 1000, float("nan"), FAKE, None) == VALUE
+    assert b"limit" in lib.moe_last_error_message()
 
 
 def test_gemm_gather_validation(lib):

@@ -193,6 +193,42 @@ def test_grouped_glu_gemm(gpu_lib, case):
     assert (hg[pad] == 0).all()  # zero pad rows give silu(0) * 0 = 0
 
 
+CLAMP_CASES = [
+    # name, counts, align, H, I, limit
+    ("ragged_L0.5", [0, 130, 257, 31, 64], 32, 256, 128, 0.5),
+    ("many_L2", _many_counts(20, 200, 5), 32, 512, 192, 2.0),
+    ("align8_L0", [33, 7, 0, 90], 8, 128, 64, 0.0),
+]
+
+
+@pytest.mark.parametrize("case", CLAMP_CASES, ids=[c[0] for c in CLAMP_CASES])
+def test_grouped_glu_gemm_clamped(gpu_lib, case):
+    """Clamped SwiGLU in the gate/up epilogue: against the oracle's clamped SwiGLU
+    of its float64 gate/up sums (the clamp is continuous, so near the limit the
+    fp32/fp64 difference stays within one rounding); limit = +inf is the plain
+    GEMM bit for bit."""
+    name, counts, align, H, I, limit = case
+    _say(f"clamped glu gemm case {name}")
+    counts, offsets = _synthetic_layout(counts, align)
+    E, P = len(counts), int(offsets[-1])
+    P_max = P + 64
+    rows = _rows_of(counts, offsets)
+    x_perm = np.zeros((P_max, H), np.uint16)
+    x_perm[rows] = gen.random_bf16((len(rows), H), seed=3)
+    w_gu = gen.random_bf16((E, 2 * I, H), seed=4, std=0.1)   # |g|, |u| ~ 1-2: many values past the limit
+    xd, wd, cd, od = dev_bf16(x_perm), dev_bf16(w_gu), dev(counts), dev(offsets)
+    h = gpu_lib.grouped_glu_gemm_clamped(xd, wd, cd, od, limit)
+    h_inf = gpu_lib.grouped_glu_gemm_clamped(xd, wd, cd, od, float("inf"))
+    h_plain = gpu_lib.grouped_glu_gemm(xd, wd, cd, od)
+    torch.cuda.synchronize()
+    gu = oracle.down(gen.bf16_bits_to_f32(x_perm).astype(np.float64), w_gu, counts, offsets)
+    ref = oracle.swiglu_clamped(gu[rows], limit)
+    clamped = np.mean((np.abs(gu[rows][:, I:]) > limit) | (gu[rows][:, :I] > limit))
+    assert clamped > 0.2, f"only {clamped:.0%} of the elements reach the limit"
+    assert_close_bf16(host_f64(h[:P])[rows], ref, f"h[{name}]")
+    assert torch.equal(h_inf[:P].view(torch.int16), h_plain[:P].view(torch.int16))
+
+
 @pytest.mark.parametrize("case", GEMM_CASES, ids=[c[0] for c in GEMM_CASES])
 def test_grouped_glu_gemm_gather(gpu_lib, case):
     """The gate/up GEMM reading layout rows x[row_token[p]] in place equals the
