@@ -33,7 +33,11 @@
 // accumulator registers).  16-byte pieces are XOR-swizzled in LDS so that the
 // MFMA operand reads are conflict-free.  The ring runs on from one tile to the
 // next (the next tile's first stages load during the last k steps), and the
-// output is written from registers, 8 bytes per lane, while the next tile runs.
+// output is written straight from registers while the next tile runs (plain
+// GEMM: 16 bytes per lane, whole 128-byte rows per instruction; GLU: 8 bytes per
+// lane, as a wave owns 32 output columns). Variants of the epilogue: SwiGLU
+// (GLU, optionally clamped at a runtime limit) and the SwiGLU backward of the
+// plain GEMM's output (SWB: dh = dy W_d never leaves registers).
 //
 // FP8-weight variant (W8): W holds OCP E4M3 codes with one fp32 scale per 64
 // consecutive W rows of an expert [Halo "Performance", Levers that do not help
