@@ -345,6 +345,12 @@ __device__ __forceinline__ bf16x8_t fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
     return bf16x8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
+// A compile-time bool passed as a value (selects a copy of a generic lambda).
+template <bool B>
+struct BoolTag {
+    static constexpr bool value = B;
+};
+
 // Wave-constant values of the whole launch.
 struct WaveCtx {
     uint16_t* lds;
@@ -588,51 +594,58 @@ __device__ __forceinline__ int run_tile(const WaveCtx& w, const TileArgs& ta, co
         constexpr int OB = GLU ? NBN / 2 : NBN;    // 32-column output blocks per wave
         const int col0 = GLU ? nt * 128 + wn * (WTN / 2) : nt * BN + wn * WTN;
         if (GLU) {
+            // The clamp is a separate copy of the loop, picked by a branch on the
+            // launch-uniform limit: as one loop with a runtime test, the compiler
+            // computed the clamp for every element and then selected.
             const float lim = w.glu_limit;
-            const bool clamp = lim < INFINITY;  // uniform over the launch
+            auto glu_epilogue = [&](auto clamp_tag) {
+                constexpr bool CLAMP = decltype(clamp_tag)::value;
 #pragma unroll
-            for (int i = 0; i < NV; ++i) {
+                for (int i = 0; i < NV; ++i) {
 #pragma unroll
-                for (int jb = 0; jb < OB; ++jb) {
-                    const int cb = col0 + jb * 32;
-                    if (cb >= n_cols) continue;
-                    // FP8 weights: a 32-column block lies inside one 64-row scale block
-                    // (gate rows cb.., up rows n_cols + cb..), so its scales are wave-uniform
-                    float sg = 1.0f, su = 1.0f;
-                    if (W8) {
-                        sg = w_scale[cb >> 6];
-                        su = w_scale[(n_cols + cb) >> 6];
-                    }
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const int r0 = (2 * i + wm) * 32 + q * 8;
-                        if (r0 >= rows_valid) continue;
-                        float v[4];
-#pragma unroll
-                        for (int m = 0; m < 4; ++m) {
-                            float g = acc[i][jb][4 * q + m], u = acc[i][jb + NBN / 2][4 * q + m];
-                            if (W8) {
-                                g *= sg;
-                                u *= su;
-                            }
-                            if (clamp) {  // gate capped at +limit, up clipped to [-limit, limit]
-                                g = fminf(g, lim);
-                                u = fminf(fmaxf(u, -lim), lim);
-                            }
-                            // silu(g) = g * 1/(1 + e^-g) with the hardware reciprocal
-                            // (v_rcp_f32, within 1 ulp): 2-6% faster than IEEE division
-                            // here, an error far below h's bf16 rounding
-                            v[m] = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+                    for (int jb = 0; jb < OB; ++jb) {
+                        const int cb = col0 + jb * 32;
+                        if (cb >= n_cols) continue;
+                        // FP8 weights: a 32-column block lies inside one 64-row scale block
+                        // (gate rows cb.., up rows n_cols + cb..), so its scales are wave-uniform
+                        float sg = 1.0f, su = 1.0f;
+                        if (W8) {
+                            sg = w_scale[cb >> 6];
+                            su = w_scale[(n_cols + cb) >> 6];
                         }
-                        uint32_t w0, w1;
-                        quad_transpose_bf16(v[0], v[1], v[2], v[3], qs, w0, w1);
-                        char* grp0 = (char*)(c_tile + ((int64_t)r0 * n_cols + cb));
-                        if (out_row < rows_valid - r0)
-                            *(uint2*)(grp0 + out_off) = make_uint2(w0, w1);
-                        ++stores;
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            const int r0 = (2 * i + wm) * 32 + q * 8;
+                            if (r0 >= rows_valid) continue;
+                            float v[4];
+#pragma unroll
+                            for (int m = 0; m < 4; ++m) {
+                                float g = acc[i][jb][4 * q + m], u = acc[i][jb + NBN / 2][4 * q + m];
+                                if (W8) {
+                                    g *= sg;
+                                    u *= su;
+                                }
+                                if (CLAMP) {  // gate capped at +limit, up clipped to [-limit, limit]
+                                    g = __builtin_amdgcn_fmed3f(g, -INFINITY, lim);
+                                    u = __builtin_amdgcn_fmed3f(u, -lim, lim);
+                                }
+                                // silu(g) = g * 1/(1 + e^-g) with the hardware reciprocal
+                                // (v_rcp_f32, within 1 ulp): 2-6% faster than IEEE division
+                                // here, an error far below h's bf16 rounding
+                                v[m] = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+                            }
+                            uint32_t w0, w1;
+                            quad_transpose_bf16(v[0], v[1], v[2], v[3], qs, w0, w1);
+                            char* grp0 = (char*)(c_tile + ((int64_t)r0 * n_cols + cb));
+                            if (out_row < rows_valid - r0)
+                                *(uint2*)(grp0 + out_off) = make_uint2(w0, w1);
+                            ++stores;
+                        }
                     }
                 }
-            }
+            };
+            if (lim < INFINITY) glu_epilogue(BoolTag<true>{});
+            else glu_epilogue(BoolTag<false>{});
         } else if (col0 < n_cols) {
             // Plain GEMM: the wave's two 32-column blocks are adjacent (64 columns, one
             // 128-byte line per row; N is a multiple of 64, so both exist). After the
