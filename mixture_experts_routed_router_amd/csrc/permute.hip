@@ -17,8 +17,8 @@
 //               chunk c's routes to e; pad rows get row_token = -1
 //   3. scatter: route_row[r] = base + rank among earlier equal ids (stable in r),
 //               row_token[route_row[r]] = r / k
-//   4. gather:  x_perm[p] = x[row_token[p]] (zero row if -1), 16-byte lanes over
-//               consecutive layout bytes
+//   4. gather:  x_perm[p] = x[row_token[p]] (zero row if -1), written token-major:
+//               each token's row is read once and stored to its k rows
 #include "common.hpp"
 
 namespace moe {
@@ -160,45 +160,60 @@ __global__ __launch_bounds__(256) void permute_scatter_kernel(const int32_t* __r
     }
 }
 
-// The gather, one 16-byte piece per lane: piece q of the layout is row q / ppr,
-// column piece q % ppr, so a wavefront covers 1 KB of consecutive layout bytes
-// (coalesced stores) read from the matching piece of the token's row. Each
-// thread has kGatherUnroll pieces in flight before its first store. A layout
-// far larger than the 256 MB Infinity Cache is written with non-temporal
-// stores (NT), which do not evict the token rows still being read.
-constexpr int kGatherUnroll = 4;
-constexpr int kGatherThreads = 256;
+// The gather, token-major: one wavefront per token reads the token's row of x
+// once (kCopyUnroll 16-byte pieces per lane in flight, 1 KB per wave-wide load)
+// and writes it to the token's k layout rows (route_row), so x is read once
+// rather than k times; each store instruction writes 1 KB of one row. The last
+// E workgroups zero the pad rows of the experts' segments. A layout far larger
+// than the 256 MB Infinity Cache is written with non-temporal stores (NT).
+constexpr int kCopyUnroll = 4;
+constexpr int kCopyThreads = 256;
+constexpr int kCopyWaves = kCopyThreads / kWave;
 constexpr int64_t kStreamingLayoutBytes = 512ll << 20;
 
 template <bool NT>
-__global__ __launch_bounds__(kGatherThreads) void permute_gather_kernel(
-    const uint4* __restrict__ x, const int32_t* __restrict__ row_token,
-    const int32_t* __restrict__ offsets, int E, int ppr, uint4* __restrict__ x_perm) {
-    const int64_t used = (int64_t)offsets[E] * ppr;  // pieces of the used rows
-    const int64_t stride = (int64_t)gridDim.x * kGatherThreads * kGatherUnroll;
-    for (int64_t base = (int64_t)blockIdx.x * kGatherThreads * kGatherUnroll + threadIdx.x; base < used;
-         base += stride) {
-        uint4 v[kGatherUnroll];
+__device__ __forceinline__ void store_piece(uint4* dst, const uint4& v) {
+    if (NT) {
+        const u32x4_t t4 = {v.x, v.y, v.z, v.w};
+        __builtin_nontemporal_store(t4, (u32x4_t*)dst);
+    } else {
+        *dst = v;
+    }
+}
+
+template <bool NT>
+__global__ __launch_bounds__(kCopyThreads) void permute_copy_rows_kernel(
+    const uint4* __restrict__ x, const int32_t* __restrict__ route_row, const int32_t* __restrict__ counts,
+    const int32_t* __restrict__ offsets, int64_t T, int k, int ppr, int64_t token_blocks,
+    uint4* __restrict__ x_perm) {
+    const int lane = lane_id();
+    if ((int64_t)blockIdx.x >= token_blocks) {
+        // pad rows [offsets[e] + counts[e], offsets[e+1]) of expert e
+        const int e = (int)((int64_t)blockIdx.x - token_blocks);
+        const int64_t p0 = (int64_t)offsets[e] + counts[e], p1 = offsets[e + 1];
+        const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+        for (int64_t q = p0 * ppr + threadIdx.x; q < p1 * ppr; q += kCopyThreads) store_piece<NT>(x_perm + q, z);
+        return;
+    }
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int64_t t = (int64_t)blockIdx.x * kCopyWaves + wave;
+    if (t >= T) return;
+    const uint4* src = x + t * ppr;
+    for (int c0 = 0; c0 < ppr; c0 += kWave * kCopyUnroll) {
+        uint4 v[kCopyUnroll];
 #pragma unroll
-        for (int u = 0; u < kGatherUnroll; ++u) {
-            const int64_t q = base + u * kGatherThreads;
-            v[u] = make_uint4(0u, 0u, 0u, 0u);
-            if (q < used) {
-                const int64_t p = q / ppr;
-                const int32_t t = row_token[p];
-                if (t >= 0) v[u] = x[(int64_t)t * ppr + (q - p * ppr)];
-            }
+        for (int u = 0; u < kCopyUnroll; ++u) {
+            const int c = c0 + u * kWave + lane;
+            v[u] = c < ppr ? src[c] : make_uint4(0u, 0u, 0u, 0u);
         }
+        for (int j = 0; j < k; ++j) {
+            const int32_t row = __builtin_amdgcn_readfirstlane(route_row[t * k + j]);  // wave-uniform
+            if (row < 0) continue;  // an out-of-range expert id has no row
+            uint4* dst = x_perm + (int64_t)row * ppr;
 #pragma unroll
-        for (int u = 0; u < kGatherUnroll; ++u) {
-            const int64_t q = base + u * kGatherThreads;
-            if (q < used) {
-                if (NT) {
-                    const u32x4_t t4 = {v[u].x, v[u].y, v[u].z, v[u].w};
-                    __builtin_nontemporal_store(t4, (u32x4_t*)(x_perm + q));
-                } else {
-                    x_perm[q] = v[u];
-                }
+            for (int u = 0; u < kCopyUnroll; ++u) {
+                const int c = c0 + u * kWave + lane;
+                if (c < ppr) store_piece<NT>(dst + c, v[u]);
             }
         }
     }
@@ -238,19 +253,17 @@ hipError_t launch_permute(const uint16_t* x, const int32_t* topk_idx, int64_t T,
     }
     if (!x_perm) return hipGetLastError();  // the layout only
     const int ppr = H / 8;  // 16-byte pieces per row
-    // enough workgroups to cover P_max rows once, capped at a few waves of the chip
-    const int64_t pieces = P_max * (int64_t)ppr;
-    const int64_t per_wg = kGatherThreads * kGatherUnroll;
-    const int64_t want = (pieces + per_wg - 1) / per_wg;
-    const unsigned grid = (unsigned)(want < 4096 ? want : 4096);
+    // one wavefront per token, then one workgroup per expert for its pad rows
+    const int64_t token_blocks = (T + kCopyWaves - 1) / kCopyWaves;
+    const dim3 grid((unsigned)(token_blocks + E));
     if (P_max * (int64_t)H * 2 > kStreamingLayoutBytes)
-        hipLaunchKernelGGL(permute_gather_kernel<true>, dim3(grid), dim3(kGatherThreads), 0, stream,
-                           (const uint4*)x, (const int32_t*)row_token, (const int32_t*)offsets, E,
-                           ppr, (uint4*)x_perm);
+        hipLaunchKernelGGL(permute_copy_rows_kernel<true>, grid, dim3(kCopyThreads), 0, stream,
+                           (const uint4*)x, (const int32_t*)route_row, (const int32_t*)counts,
+                           (const int32_t*)offsets, T, k, ppr, token_blocks, (uint4*)x_perm);
     else
-        hipLaunchKernelGGL(permute_gather_kernel<false>, dim3(grid), dim3(kGatherThreads), 0, stream,
-                           (const uint4*)x, (const int32_t*)row_token, (const int32_t*)offsets, E,
-                           ppr, (uint4*)x_perm);
+        hipLaunchKernelGGL(permute_copy_rows_kernel<false>, grid, dim3(kCopyThreads), 0, stream,
+                           (const uint4*)x, (const int32_t*)route_row, (const int32_t*)counts,
+                           (const int32_t*)offsets, T, k, ppr, token_blocks, (uint4*)x_perm);
     return hipGetLastError();
 }
 
