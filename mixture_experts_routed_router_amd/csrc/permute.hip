@@ -12,11 +12,13 @@
 // update the same counter in one step and nothing needs an atomic.
 //
 //   1. hist:    per chunk c and expert e, the count hist[c][e]        (workspace)
-//   2. scan:    counts[e] = sum_c hist[c][e]; offsets = exclusive scan of the
-//               counts rounded up to align; hist[c][e] becomes the first row of
-//               chunk c's routes to e; pad rows get row_token = -1
-//   3. scatter: route_row[r] = base + rank among earlier equal ids (stable in r),
-//               row_token[route_row[r]] = r / k
+//   2. scan:    per expert e, counts[e] = sum_c hist[c][e], and hist[c][e] becomes
+//               the number of e's routes in chunks before c (one workgroup per 64
+//               experts)
+//   3. scatter: every workgroup derives offsets = exclusive scan of the counts
+//               rounded up to align; route_row[r] = offsets[e] + hist[c][e] + rank
+//               among earlier equal ids (stable in r), row_token[route_row[r]] =
+//               r / k; offsets are published and pad rows get row_token = -1
 //   4. gather:  x_perm[p] = x[row_token[p]] (zero row if -1), written token-major:
 //               each token's row is read once and stored to its k rows
 #include "common.hpp"
@@ -57,55 +59,40 @@ __global__ __launch_bounds__(256) void permute_hist_kernel(const int32_t* __rest
     for (int e = lane; e < E; e += kWave) out[e] = h[e];
 }
 
-// One workgroup of 1024 threads. Thread (s, e) owns expert e over the s-th
-// contiguous range of chunks, so the chunk loop reads hist rows coalesced.
-__global__ __launch_bounds__(kScanThreads) void permute_scan_kernel(
-    int32_t* __restrict__ hist, int64_t nchunks, int E, int align, int64_t P_max,
-    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ row_token) {
-    __shared__ int32_t part[kScanThreads];
-    __shared__ int32_t scan[kScanThreads];
-    __shared__ int32_t cnt[kScanThreads];
-    const int tid = threadIdx.x;
-    const int nseg = E >= kScanThreads ? 1 : kScanThreads / E;
-    const int e = tid % E, s = tid / E;
-    const bool owner = s < nseg;
-    const int64_t per = (nchunks + nseg - 1) / nseg;
-    const int64_t c0 = owner ? s * per : 0;
-    const int64_t c1 = owner ? (c0 + per < nchunks ? c0 + per : nchunks) : 0;
+// One workgroup of 1024 threads per 64 experts: lane l of every wave owns
+// expert 64 * blockIdx.x + l, wave w a contiguous range of chunks, so each load
+// reads 256 consecutive bytes of a hist row and the passes over the histogram
+// are spread over E / 64 CUs.
+constexpr int kScanWaves = kScanThreads / kWave;
 
+__global__ __launch_bounds__(kScanThreads) void permute_scan_kernel(int32_t* __restrict__ hist,
+                                                                    int64_t nchunks, int E,
+                                                                    int32_t* __restrict__ counts) {
+    __shared__ int32_t part[kScanWaves][kWave];
+    const int lane = lane_id(), wave = threadIdx.x / kWave;
+    const int e = blockIdx.x * kWave + lane;
+    const bool live = e < E;
+    const int64_t per = (nchunks + kScanWaves - 1) / kScanWaves;
+    const int64_t c0 = min(nchunks, (int64_t)wave * per), c1 = min(nchunks, c0 + per);
     int32_t sum = 0;
+    if (live) {
 #pragma unroll 8
-    for (int64_t c = c0; c < c1; ++c) sum += hist[c * E + e];
-    if (owner) part[s * E + e] = sum;
+        for (int64_t c = c0; c < c1; ++c) sum += hist[c * E + e];
+    }
+    part[wave][lane] = sum;
     __syncthreads();
-
-    int32_t padded = 0;
-    if (tid < E) {
+    if (wave == 0) {  // per expert: exclusive scan over the waves' ranges, and the total
         int32_t run = 0;
-        for (int q = 0; q < nseg; ++q) {
-            const int32_t v = part[q * E + tid];
-            part[q * E + tid] = run;
+        for (int w = 0; w < kScanWaves; ++w) {
+            const int32_t v = part[w][lane];
+            part[w][lane] = run;
             run += v;
         }
-        cnt[tid] = run;
-        counts[tid] = run;
-        padded = (run + align - 1) / align * align;
+        if (live) counts[e] = run;
     }
-    // inclusive scan of the padded sizes over experts (Hillis-Steele)
-    scan[tid] = padded;
     __syncthreads();
-    for (int d = 1; d < kScanThreads; d <<= 1) {
-        const int32_t v = tid >= d ? scan[tid - d] : 0;
-        __syncthreads();
-        scan[tid] += v;
-        __syncthreads();
-    }
-    const int32_t total = scan[E - 1];
-    if (tid < E) offsets[tid] = scan[tid] - padded;
-    if (tid == 0) offsets[E] = total;
-
-    if (owner) {
-        int32_t run = (scan[e] - ((cnt[e] + align - 1) / align * align)) + part[s * E + e];
+    if (live) {
+        int32_t run = part[wave][lane];
 #pragma unroll 8
         for (int64_t c = c0; c < c1; ++c) {
             const int32_t v = hist[c * E + e];
@@ -113,27 +100,62 @@ __global__ __launch_bounds__(kScanThreads) void permute_scan_kernel(
             run += v;
         }
     }
-    // pad rows inside each segment, then every row past the last segment
-    if (tid < E) {
-        const int32_t end = scan[tid];
-        for (int32_t p = end - ((cnt[tid] + align - 1) / align * align) + cnt[tid]; p < end; ++p)
-            row_token[p] = -1;
-    }
-    for (int64_t p = (int64_t)total + tid; p < P_max; p += kScanThreads) row_token[p] = -1;
 }
 
-__global__ __launch_bounds__(256) void permute_scatter_kernel(const int32_t* __restrict__ topk_idx,
-                                                              int64_t R, int E, int k,
-                                                              int64_t nchunks,
-                                                              const int32_t* __restrict__ base,
-                                                              int32_t* __restrict__ route_row,
-                                                              int32_t* __restrict__ row_token) {
-    extern __shared__ int32_t lds_cursor[];  // [4][E]
-    const int wave = threadIdx.x / kWave, lane = lane_id();
+// Every workgroup first derives the padded expert offsets from the counts (thread
+// i takes experts 4i .. 4i+3, E <= 1024, then a workgroup scan); workgroup 0
+// publishes them, and each workgroup writes row_token = -1 on its share of the
+// pad rows (those of experts b, b + gridDim.x, ..., and every row from
+// offsets[E] to P_max). Then one wavefront per chunk as before.
+constexpr int kScatterThreads = 256;
+
+__global__ __launch_bounds__(kScatterThreads) void permute_scatter_kernel(
+    const int32_t* __restrict__ topk_idx, int64_t R, int E, int k, int align, int64_t nchunks,
+    int64_t P_max, const int32_t* __restrict__ base, const int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ route_row, int32_t* __restrict__ row_token) {
+    extern __shared__ int32_t lds_cursor[];  // [4][E] cursors, [E+1] offsets, [4] wave totals
+    int32_t* off = lds_cursor + 4 * E;
+    int32_t* wtot = off + E + 1;
+    const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
+    {
+        int32_t pc[4], local = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int e = 4 * tid + q;
+            pc[q] = e < E ? (counts[e] + align - 1) / align * align : 0;
+            local += pc[q];
+        }
+        int32_t incl = local;
+#pragma unroll
+        for (int d = 1; d < kWave; d <<= 1) {
+            const int32_t o = __shfl_up(incl, d);
+            if (lane >= d) incl += o;
+        }
+        if (lane == kWave - 1) wtot[wave] = incl;
+        __syncthreads();
+        for (int w = 0; w < wave; ++w) incl += wtot[w];
+        int32_t run = incl - local;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int e = 4 * tid + q;
+            if (e < E) off[e] = run;
+            run += pc[q];
+        }
+        if (tid == kScatterThreads - 1) off[E] = incl;
+        __syncthreads();
+    }
+    if (blockIdx.x == 0)
+        for (int e = tid; e <= E; e += kScatterThreads) offsets[e] = off[e];
+    for (int e = blockIdx.x; e < E; e += gridDim.x)
+        for (int64_t p = (int64_t)off[e] + counts[e] + tid; p < off[e + 1]; p += kScatterThreads) row_token[p] = -1;
+    for (int64_t p = (int64_t)off[E] + (int64_t)blockIdx.x * kScatterThreads + tid; p < P_max;
+         p += (int64_t)gridDim.x * kScatterThreads)
+        row_token[p] = -1;
+
     const int64_t c = (int64_t)blockIdx.x * 4 + wave;
     if (c >= nchunks) return;
     int32_t* cur = lds_cursor + wave * E;
-    for (int e = lane; e < E; e += kWave) cur[e] = base[c * E + e];
+    for (int e = lane; e < E; e += kWave) cur[e] = base[c * E + e] + off[e];
     const int nbits = key_bits(E);
     const uint64_t lt = lanemask_lt();
     const int64_t r0 = c * kChunk;
@@ -240,17 +262,18 @@ hipError_t launch_permute(const uint16_t* x, const int32_t* topk_idx, int64_t T,
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
-    hipLaunchKernelGGL(permute_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, hist, nchunks,
-                       E, align, P_max, counts, offsets, row_token);
+    hipLaunchKernelGGL(permute_scan_kernel, dim3((unsigned)((E + kWave - 1) / kWave)), dim3(kScanThreads), 0,
+                       stream, hist, nchunks, E, counts);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    if (nchunks > 0) {
-        hipLaunchKernelGGL(permute_scatter_kernel, dim3((unsigned)((nchunks + 3) / 4)), dim3(256),
-                           lds, stream, topk_idx, R, E, k, nchunks, (const int32_t*)hist,
-                           route_row, row_token);
-        err = hipGetLastError();
-        if (err != hipSuccess) return err;
-    }
+    // at least one workgroup: it also publishes the offsets and the pad rows
+    const int64_t scatter_blocks = nchunks > 0 ? (nchunks + 3) / 4 : 1;
+    const size_t scatter_lds = (4 * (size_t)E + E + 1 + 4) * sizeof(int32_t);
+    hipLaunchKernelGGL(permute_scatter_kernel, dim3((unsigned)scatter_blocks), dim3(kScatterThreads), scatter_lds,
+                       stream, topk_idx, R, E, k, align, nchunks, P_max, (const int32_t*)hist,
+                       (const int32_t*)counts, offsets, route_row, row_token);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
     if (!x_perm) return hipGetLastError();  // the layout only
     const int ppr = H / 8;  // 16-byte pieces per row
     // one wavefront per token, then one workgroup per expert for its pad rows
