@@ -193,6 +193,9 @@ WG_CASES = [
     ("align1_tails", [7, 1, 200, 0, 45], 1, 128, 128),
     ("align8_many", _many_counts(30, 120, 44), 8, 64, 256),
     ("M2880_N640", [16, 9, 28, 40], 32, 2880, 640),
+    # 576 tiles, more than one workgroup per CU, and about a fifth of the experts
+    # with no rows (their gradient tiles are written as zeros)
+    ("many_tiles_persistent", _many_counts(96, 70, 45), 32, 768, 512),
 ]
 
 
