@@ -59,18 +59,33 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const uint4* __restric
     }
 }
 
-// Pad rows of the used layout (row_token == -1 below offsets[E]) -> 0.
+// Pad rows of the used layout -> 0: one workgroup per expert. A segment's pad rows
+// (row_token == -1) are its last rows, fewer than align of them: the first wave
+// finds where they start, 64 rows per ballot from the end, then the workgroup
+// zeroes their 16-byte pieces.
 __global__ __launch_bounds__(256) void zero_pad_rows_kernel(const int32_t* __restrict__ row_token,
-                                                            const int32_t* __restrict__ offsets, int E,
-                                                            int64_t P_max, int pieces,
+                                                            const int32_t* __restrict__ offsets, int pieces,
                                                             uint4* __restrict__ dst) {
-    const int64_t used = offsets[E];
-    const int64_t n = (used < P_max ? used : P_max) * pieces;
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
-         i += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t p = i / pieces;
-        if (row_token[p] < 0) dst[i] = make_uint4(0u, 0u, 0u, 0u);
+    __shared__ int64_t pad0;
+    const int e = blockIdx.x;
+    const int64_t s0 = offsets[e], s1 = offsets[e + 1];
+    if (threadIdx.x < kWave) {
+        const int lane = lane_id();
+        int64_t start = s1;  // first pad row
+        for (int64_t hi = s1; hi > s0; hi -= kWave) {
+            const int64_t p = hi - 1 - lane;
+            const bool pad = p >= s0 && row_token[p] < 0;
+            const uint64_t m = __ballot(pad);  // lane i: row hi-1-i
+            const uint64_t run = ~m;           // lanes from 0 that are pad rows form the suffix
+            const int n = run == 0 ? kWave : __ffsll((unsigned long long)run) - 1;
+            start = hi - n;
+            if (n < kWave) break;
+        }
+        if (lane == 0) pad0 = start;
     }
+    __syncthreads();
+    const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+    for (int64_t i = pad0 * pieces + threadIdx.x; i < s1 * pieces; i += blockDim.x) dst[i] = z;
 }
 
 // ---- routing backward: one wavefront per token ----
@@ -169,8 +184,8 @@ hipError_t launch_combine_bwd(const uint16_t* dout, const uint16_t* y, const int
                               int64_t T, int H, int k, int E, int64_t P_max, uint16_t* dy, float* dw,
                               hipStream_t stream) {
     const int pieces = H / 8;
-    hipLaunchKernelGGL(zero_pad_rows_kernel, dim3(grid_for(P_max * pieces, 8192)), dim3(256), 0, stream,
-                       row_token, offsets, E, P_max, pieces, (uint4*)dy);
+    hipLaunchKernelGGL(zero_pad_rows_kernel, dim3((unsigned)E), dim3(256), 0, stream, row_token, offsets, pieces,
+                       (uint4*)dy);
     if (T > 0)
         hipLaunchKernelGGL(combine_bwd_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, stream,
                            (const uint4*)dout, (const uint4*)y, route_row, topk_w, T, pieces, k,

@@ -140,7 +140,8 @@ def test_swiglu_forward_backward(gpu_lib, P_used, I):
     assert_close_bf16(got[:, I:], ref[:, I:], "du")
 
 
-COMB_CASES = [(64, 128, 8, 2, 32), (300, 2880, 32, 4, 8), (257, 640, 512, 10, 1), (100, 64, 40, 32, 32)]
+COMB_CASES = [(64, 128, 8, 2, 32), (300, 2880, 32, 4, 8), (257, 640, 512, 10, 1), (100, 64, 40, 32, 32),
+              (50, 64, 8, 2, 128)]  # the last: pad suffixes of more than 64 rows
 
 
 @pytest.mark.parametrize("T,H,E,k,align", COMB_CASES)
