@@ -26,36 +26,81 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 // ---- combine backward: one wavefront per token, its k routes in ascending j ----
+// Passes of 4 pieces per lane (256 pieces, 4 KB of the row): the token's dout
+// pieces are loaded once per pass, and route j+1's y pieces are loaded before
+// route j's are used. Each lane accumulates its dot products over its pieces in
+// ascending order, and the k wave reductions run after the last pass. A row
+// outside [0, P_max) (no layout row) is neither read nor written.
+constexpr int kCbU = 4;  // pieces per lane and pass
+
+template <int KL>
 __global__ __launch_bounds__(256) void combine_bwd_kernel(const uint4* __restrict__ dout,
                                                           const uint4* __restrict__ y,
                                                           const int32_t* __restrict__ route_row,
                                                           const float* __restrict__ topk_w, int64_t T,
-                                                          int pieces, int k, uint4* __restrict__ dy,
-                                                          float* __restrict__ dw) {
+                                                          int pieces, int k, int64_t P_max,
+                                                          uint4* __restrict__ dy, float* __restrict__ dw) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int64_t t = (int64_t)blockIdx.x * 4 + wave;
     if (t >= T) return;
     const int lane = lane_id();
     const uint4* g = dout + t * pieces;
-    for (int j = 0; j < k; ++j) {
-        const int64_t row = route_row[t * k + j];  // wave-uniform
-        const float w = topk_w[t * k + j];
-        float dot = 0.0f;
-        for (int c = lane; c < pieces; c += kWave) {
-            const uint4 gv = g[c], yv = y[row * pieces + c];
-            const uint32_t gp[4] = {gv.x, gv.y, gv.z, gv.w}, yp[4] = {yv.x, yv.y, yv.z, yv.w};
-            uint32_t o[4];
+    float dot[KL];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const float g0 = bf16_lo(gp[q]), g1 = bf16_hi(gp[q]);
-                dot = fmaf(g0, bf16_lo(yp[q]), dot);
-                dot = fmaf(g1, bf16_hi(yp[q]), dot);
-                o[q] = pack_bf16x2(w * g0, w * g1);
-            }
-            dy[row * pieces + c] = make_uint4(o[0], o[1], o[2], o[3]);
+    for (int j = 0; j < KL; ++j) dot[j] = 0.0f;
+    const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
+    for (int c0 = 0; c0 < pieces; c0 += kWave * kCbU) {
+        uint4 gv[kCbU], yv[kCbU], yn[kCbU];
+        int64_t row = route_row[t * k];  // wave-uniform
+        bool ok = row >= 0 && row < P_max;
+#pragma unroll
+        for (int u = 0; u < kCbU; ++u) {
+            const int c = c0 + u * kWave + lane;
+            gv[u] = c < pieces ? g[c] : zero;
+            yn[u] = ok && c < pieces ? y[row * pieces + c] : zero;
         }
-        dot = wave_sum(dot);
-        if (lane == 0) dw[t * k + j] = dot;
+#pragma unroll
+        for (int j = 0; j < KL; ++j) {
+            if (j < k) {
+                const float w = topk_w[t * k + j];
+                const int64_t cur = row;
+                const bool cur_ok = ok;
+#pragma unroll
+                for (int u = 0; u < kCbU; ++u) yv[u] = yn[u];
+                if (j + 1 < k) {  // the next route's pieces, before this route's are used
+                    row = route_row[t * k + j + 1];
+                    ok = row >= 0 && row < P_max;
+#pragma unroll
+                    for (int u = 0; u < kCbU; ++u) {
+                        const int c = c0 + u * kWave + lane;
+                        yn[u] = ok && c < pieces ? y[row * pieces + c] : zero;
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < kCbU; ++u) {
+                    const int c = c0 + u * kWave + lane;
+                    if (!cur_ok || c >= pieces) continue;
+                    const uint32_t gp[4] = {gv[u].x, gv[u].y, gv[u].z, gv[u].w};
+                    const uint32_t yp[4] = {yv[u].x, yv[u].y, yv[u].z, yv[u].w};
+                    uint32_t o[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const float g0 = bf16_lo(gp[q]), g1 = bf16_hi(gp[q]);
+                        dot[j] = fmaf(g0, bf16_lo(yp[q]), dot[j]);
+                        dot[j] = fmaf(g1, bf16_hi(yp[q]), dot[j]);
+                        o[q] = pack_bf16x2(w * g0, w * g1);
+                    }
+                    dy[cur * pieces + c] = make_uint4(o[0], o[1], o[2], o[3]);
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < KL; ++j) {
+        if (j < k) {
+            const float s = wave_sum(dot[j]);
+            if (lane == 0) dw[t * k + j] = s;
+        }
     }
 }
 
@@ -186,10 +231,16 @@ hipError_t launch_combine_bwd(const uint16_t* dout, const uint16_t* y, const int
     const int pieces = H / 8;
     hipLaunchKernelGGL(zero_pad_rows_kernel, dim3((unsigned)E), dim3(256), 0, stream, row_token, offsets, pieces,
                        (uint4*)dy);
-    if (T > 0)
-        hipLaunchKernelGGL(combine_bwd_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0, stream,
-                           (const uint4*)dout, (const uint4*)y, route_row, topk_w, T, pieces, k,
-                           (uint4*)dy, dw);
+    if (T > 0) {
+        const dim3 grid((unsigned)((T + 3) / 4)), block(256);
+#define MOE_CB_LAUNCH(KL)                                                                              \
+        hipLaunchKernelGGL(combine_bwd_kernel<KL>, grid, block, 0, stream, (const uint4*)dout, (const uint4*)y, \
+                           route_row, topk_w, T, pieces, k, P_max, (uint4*)dy, dw)
+        if (k <= 8) MOE_CB_LAUNCH(8);
+        else if (k <= 16) MOE_CB_LAUNCH(16);
+        else MOE_CB_LAUNCH(32);
+#undef MOE_CB_LAUNCH
+    }
     return hipGetLastError();
 }
 
