@@ -40,6 +40,7 @@ hipError_t launch_route_topk(const float* logits, int64_t T, int E, int k, int32
         return hipGetLastError();                                                                   \
     }
     MOE_ROUTE_CASE(8)
+    MOE_ROUTE_CASE(12)  // k = 9..12 (top-10 of 512): shorter lists than 16
     MOE_ROUTE_CASE(16)
     MOE_ROUTE_CASE(32)
 #undef MOE_ROUTE_CASE

@@ -140,6 +140,7 @@ hipError_t launch_router_topk(const uint16_t* x, const uint16_t* w_hi, const uin
         return hipGetLastError();                                                                    \
     }
     MOE_ROUTER_CASE(8)
+    MOE_ROUTER_CASE(12)  // k = 9..12 (top-10 of 512): shorter lists than 16
     MOE_ROUTER_CASE(16)
     MOE_ROUTER_CASE(32)
 #undef MOE_ROUTER_CASE
