@@ -532,36 +532,72 @@ __device__ __forceinline__ int run_tile(const WaveCtx& w, const TileArgs& ta, co
     }
 
     // Each group runs its own straight-line loop; both pass two barriers per stage.
+    // The middle stages -- every stage the group issues is inside this tile, both
+    // later stages are in flight, and no wait can leave older stores or token
+    // loads outstanding -- run a copy of the loop body with those waits and
+    // issues fixed, without the branches that pick them at the edges.
+#define MOE_G0_BODY(kt, STEADY)                                                                   \
+    do {                                                                                          \
+        /* phase 2kt: compute stage kt (fragments read in the previous phase) */                  \
+        __builtin_amdgcn_s_setprio(1);                                                            \
+        if (NV > 0) MOE_MMA_STAGE();                                                              \
+        __builtin_amdgcn_s_setprio(0);                                                            \
+        if (STEADY) wait_vmcnt<2 * LPS>();                                                        \
+        else MOE_WAIT_NEXT(kt, 3);                                                                \
+        lds_barrier();                                                                            \
+        /* phase 2kt+1: refill the buffer of stage kt (both groups have read it) with */          \
+        /* stage kt+4, and read stage kt+1 */                                                     \
+        if (STEADY) {                                                                             \
+            issue_stage<W8>(w.lds0, (base + (kt) + STAGES) & (STAGES - 1), wave,                  \
+                            ta.a_tile + ((kt) + STAGES) * BK, ta.w_exp + ((kt) + STAGES) * BK * WB, oc); \
+            MOE_LOAD_STAGE_FRAGS((kt) + 1);                                                       \
+        } else {                                                                                  \
+            MOE_WAIT_TOKENS(kt, nk - STAGES, STAGES);                                             \
+            MOE_ISSUE((kt) + STAGES);                                                             \
+            if ((kt) + 1 < nk) MOE_LOAD_STAGE_FRAGS((kt) + 1);                                    \
+        }                                                                                         \
+        lds_barrier();                                                                            \
+    } while (0)
+#define MOE_G1_BODY(kt, STEADY)                                                                   \
+    do {                                                                                          \
+        /* phase 2kt: read stage kt; issue stage kt+3 into the buffer of stage kt-1 */            \
+        MOE_LOAD_STAGE_FRAGS(kt);                                                                 \
+        if (STEADY) {                                                                             \
+            issue_stage<W8>(w.lds0, (base + (kt) + STAGES - 1) & (STAGES - 1), wave,              \
+                            ta.a_tile + ((kt) + STAGES - 1) * BK,                                 \
+                            ta.w_exp + ((kt) + STAGES - 1) * BK * WB, oc);                        \
+            wait_vmcnt<2 * LPS>();                                                                \
+        } else {                                                                                  \
+            MOE_WAIT_TOKENS(kt, nk - STAGES + 1, STAGES - 1);                                     \
+            MOE_ISSUE((kt) + STAGES - 1);                                                         \
+            MOE_WAIT_NEXT(kt, 2);                                                                 \
+        }                                                                                         \
+        lds_barrier();                                                                            \
+        /* phase 2kt+1: compute stage kt */                                                       \
+        __builtin_amdgcn_s_setprio(1);                                                            \
+        if (NV > 0) MOE_MMA_STAGE();                                                              \
+        __builtin_amdgcn_s_setprio(0);                                                            \
+        lds_barrier();                                                                            \
+    } while (0)
+    static_assert(STAGES == 4, "the steady ranges below assume a four-stage ring");
     if (grp == 0) {
-        for (int kt = 0; kt < nk; ++kt) {
-            // phase 2kt: compute stage kt (fragments read in the previous phase)
-            __builtin_amdgcn_s_setprio(1);
-            if (NV > 0) MOE_MMA_STAGE();
-            __builtin_amdgcn_s_setprio(0);
-            MOE_WAIT_NEXT(kt, 3);
-            lds_barrier();
-            // phase 2kt+1: refill the buffer of stage kt (both groups have read it)
-            // with stage kt+4, and read stage kt+1
-            MOE_WAIT_TOKENS(kt, nk - STAGES, STAGES);
-            MOE_ISSUE(kt + STAGES);
-            if (kt + 1 < nk) MOE_LOAD_STAGE_FRAGS(kt + 1);
-            lds_barrier();
-        }
+        // steady: kt >= 3 (stage kt+1 >= 4 was issued in this tile, after any
+        // stores of the previous one) and kt + 4 < nk (stage kt+4 is this tile's)
+        const int lo = min(3, nk), hi = max(lo, nk - 4);
+        int kt = 0;
+        for (; kt < lo; ++kt) MOE_G0_BODY(kt, false);
+        for (; kt < hi; ++kt) MOE_G0_BODY(kt, true);
+        for (; kt < nk; ++kt) MOE_G0_BODY(kt, false);
     } else {
-        for (int kt = 0; kt < nk; ++kt) {
-            // phase 2kt: read stage kt; issue stage kt+3 into the buffer of stage kt-1
-            MOE_LOAD_STAGE_FRAGS(kt);
-            MOE_WAIT_TOKENS(kt, nk - STAGES + 1, STAGES - 1);
-            MOE_ISSUE(kt + STAGES - 1);
-            MOE_WAIT_NEXT(kt, 2);
-            lds_barrier();
-            // phase 2kt+1: compute stage kt
-            __builtin_amdgcn_s_setprio(1);
-            if (NV > 0) MOE_MMA_STAGE();
-            __builtin_amdgcn_s_setprio(0);
-            lds_barrier();
-        }
+        // steady: kt >= 2 (stage kt+1 >= 3 issued in this tile) and kt + 3 < nk
+        const int lo = min(2, nk), hi = max(lo, nk - 3);
+        int kt = 0;
+        for (; kt < lo; ++kt) MOE_G1_BODY(kt, false);
+        for (; kt < hi; ++kt) MOE_G1_BODY(kt, true);
+        for (; kt < nk; ++kt) MOE_G1_BODY(kt, false);
     }
+#undef MOE_G0_BODY
+#undef MOE_G1_BODY
 #undef MOE_ISSUE
 #undef MOE_LOAD_STAGE_FRAGS
 #undef MOE_MMA_STAGE
