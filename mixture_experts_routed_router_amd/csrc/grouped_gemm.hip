@@ -416,13 +416,9 @@ __device__ __forceinline__ int run_tile(const WaveCtx& w, const TileArgs& ta, co
         brow[j] = GLU ? (j < NBN / 2 ? 0 : 128) + wn * (WTN / 2) + (j % (NBN / 2)) * 32
                       : wn * WTN + j * 32;
 
+    // Accumulators: the first k-step of stage 0 starts each from a zero operand
+    // (no separate clearing pass); a wave with no rows never uses them.
     floatx16_t acc[NV > 0 ? NV : 1][NBN];
-#pragma unroll
-    for (int i = 0; i < (NV > 0 ? NV : 1); ++i)
-#pragma unroll
-        for (int j = 0; j < NBN; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
     // ---- main loop: two wave groups in ping-pong. Group 0 (waves 0-3) and group 1
     // (waves 4-7) put one wave on each SIMD. Stage s is computed by group 0 in
@@ -475,12 +471,13 @@ __device__ __forceinline__ int run_tile(const WaveCtx& w, const TileArgs& ta, co
             }                                                                                 \
         }                                                                                     \
     } while (0)
-#define MOE_MMA_STAGE()                                                                       \
+#define MOE_MMA_STAGE(FIRST)                                                                  \
     do {                                                                                      \
         _Pragma("unroll") for (int ks = 0; ks < 2; ++ks)                                      \
             _Pragma("unroll") for (int i = 0; i < NV; ++i)                                    \
                 _Pragma("unroll") for (int j = 0; j < NBN; ++j)                               \
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks][i], fb[ks][j], acc[i][j], 0, 0, 0); \
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(                      \
+                        fa[ks][i], fb[ks][j], ((FIRST) && ks == 0) ? floatx16_t{} : acc[i][j], 0, 0, 0); \
     } while (0)
     // Before this group's first load of the next tile (issued at iteration FIRST_),
     // wait for the next tile's token loads: since they were issued, this group has
@@ -536,11 +533,11 @@ __device__ __forceinline__ int run_tile(const WaveCtx& w, const TileArgs& ta, co
     // later stages are in flight, and no wait can leave older stores or token
     // loads outstanding -- run a copy of the loop body with those waits and
     // issues fixed, without the branches that pick them at the edges.
-#define MOE_G0_BODY(kt, STEADY)                                                                   \
+#define MOE_G0_BODY(kt, STEADY, FIRST)                                                            \
     do {                                                                                          \
         /* phase 2kt: compute stage kt (fragments read in the previous phase) */                  \
         __builtin_amdgcn_s_setprio(1);                                                            \
-        if (NV > 0) MOE_MMA_STAGE();                                                              \
+        if (NV > 0) MOE_MMA_STAGE(FIRST);                                                         \
         __builtin_amdgcn_s_setprio(0);                                                            \
         if (STEADY) wait_vmcnt<2 * LPS>();                                                        \
         else MOE_WAIT_NEXT(kt, 3);                                                                \
@@ -558,7 +555,7 @@ __device__ __forceinline__ int run_tile(const WaveCtx& w, const TileArgs& ta, co
         }                                                                                         \
         lds_barrier();                                                                            \
     } while (0)
-#define MOE_G1_BODY(kt, STEADY)                                                                   \
+#define MOE_G1_BODY(kt, STEADY, FIRST)                                                            \
     do {                                                                                          \
         /* phase 2kt: read stage kt; issue stage kt+3 into the buffer of stage kt-1 */            \
         MOE_LOAD_STAGE_FRAGS(kt);                                                                 \
@@ -575,7 +572,7 @@ __device__ __forceinline__ int run_tile(const WaveCtx& w, const TileArgs& ta, co
         lds_barrier();                                                                            \
         /* phase 2kt+1: compute stage kt */                                                       \
         __builtin_amdgcn_s_setprio(1);                                                            \
-        if (NV > 0) MOE_MMA_STAGE();                                                              \
+        if (NV > 0) MOE_MMA_STAGE(FIRST);                                                         \
         __builtin_amdgcn_s_setprio(0);                                                            \
         lds_barrier();                                                                            \
     } while (0)
@@ -584,17 +581,19 @@ __device__ __forceinline__ int run_tile(const WaveCtx& w, const TileArgs& ta, co
         // steady: kt >= 3 (stage kt+1 >= 4 was issued in this tile, after any
         // stores of the previous one) and kt + 4 < nk (stage kt+4 is this tile's)
         const int lo = min(3, nk), hi = max(lo, nk - 4);
-        int kt = 0;
-        for (; kt < lo; ++kt) MOE_G0_BODY(kt, false);
-        for (; kt < hi; ++kt) MOE_G0_BODY(kt, true);
-        for (; kt < nk; ++kt) MOE_G0_BODY(kt, false);
+        MOE_G0_BODY(0, false, true);  // nk >= 2 (K >= 64)
+        int kt = 1;
+        for (; kt < lo; ++kt) MOE_G0_BODY(kt, false, false);
+        for (; kt < hi; ++kt) MOE_G0_BODY(kt, true, false);
+        for (; kt < nk; ++kt) MOE_G0_BODY(kt, false, false);
     } else {
         // steady: kt >= 2 (stage kt+1 >= 3 issued in this tile) and kt + 3 < nk
         const int lo = min(2, nk), hi = max(lo, nk - 3);
-        int kt = 0;
-        for (; kt < lo; ++kt) MOE_G1_BODY(kt, false);
-        for (; kt < hi; ++kt) MOE_G1_BODY(kt, true);
-        for (; kt < nk; ++kt) MOE_G1_BODY(kt, false);
+        MOE_G1_BODY(0, false, true);
+        int kt = 1;
+        for (; kt < lo; ++kt) MOE_G1_BODY(kt, false, false);
+        for (; kt < hi; ++kt) MOE_G1_BODY(kt, true, false);
+        for (; kt < nk; ++kt) MOE_G1_BODY(kt, false, false);
     }
 #undef MOE_G0_BODY
 #undef MOE_G1_BODY
