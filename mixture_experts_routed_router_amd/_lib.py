@@ -415,6 +415,23 @@ class MoELayer:
         combine(self.y, L.route_row, self.topk_w, out=self.out, stream=stream)
         return self.out
 
+    def graph(self, x, logits, w_gate_up, w_down):
+        """Capture one layer call on these input and weight tensors as a HIP graph.
+        ``replay()`` reruns the five kernels' launches as one submission, writing
+        ``self.out``; to run on new inputs, copy them into ``x`` and ``logits``
+        first. The library calls allocate and clear nothing, so the graph holds
+        kernel nodes only. One eager call on a side stream (default priority)
+        precedes the capture."""
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            self(x, logits, w_gate_up, w_down)
+        torch.cuda.current_stream().wait_stream(side)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self(x, logits, w_gate_up, w_down)
+        return g
+
 
 # ---- training: forward with saved gate/up output, and the backward -------------------
 
