@@ -19,6 +19,12 @@
 
 namespace moe {
 
+// 16 bytes with a non-temporal load: for rows that nothing reads again.
+__device__ __forceinline__ uint4 ld_nt(const uint4* p) {
+    const u32x4_t r = __builtin_nontemporal_load((const u32x4_t*)p);
+    return make_uint4(r[0], r[1], r[2], r[3]);
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
     for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o);
@@ -57,7 +63,7 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const uint4* __restric
         for (int u = 0; u < kCbU; ++u) {
             const int c = c0 + u * kWave + lane;
             gv[u] = c < pieces ? g[c] : zero;
-            yn[u] = ok && c < pieces ? y[row * pieces + c] : zero;
+            yn[u] = ok && c < pieces ? ld_nt(y + row * pieces + c) : zero;
         }
 #pragma unroll
         for (int j = 0; j < KL; ++j) {
@@ -73,7 +79,7 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const uint4* __restric
 #pragma unroll
                     for (int u = 0; u < kCbU; ++u) {
                         const int c = c0 + u * kWave + lane;
-                        yn[u] = ok && c < pieces ? y[row * pieces + c] : zero;
+                        yn[u] = ok && c < pieces ? ld_nt(y + row * pieces + c) : zero;
                     }
                 }
 #pragma unroll

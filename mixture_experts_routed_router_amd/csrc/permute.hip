@@ -226,7 +226,10 @@ __global__ __launch_bounds__(kCopyThreads) void permute_copy_rows_kernel(
 #pragma unroll
         for (int u = 0; u < kCopyUnroll; ++u) {
             const int c = c0 + u * kWave + lane;
-            v[u] = c < ppr ? src[c] : make_uint4(0u, 0u, 0u, 0u);
+            // x is read once here: streaming (non-temporal) loads
+            u32x4_t r_ = {0u, 0u, 0u, 0u};
+            if (c < ppr) r_ = __builtin_nontemporal_load((const u32x4_t*)(src + c));
+            v[u] = make_uint4(r_[0], r_[1], r_[2], r_[3]);
         }
         for (int j = 0; j < k; ++j) {
             const int32_t row = __builtin_amdgcn_readfirstlane(route_row[t * k + j]);  // wave-uniform
