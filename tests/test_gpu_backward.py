@@ -299,7 +299,7 @@ def test_training_step_full_size_sampled(gpu_lib):
     _say("full-size training step: running")
     layer, out, dout, (dx, dl, dwgu, dwd) = _train(gpu_lib, d)
     f = lambda b: gen.bf16_bits_to_f32(b).astype(np.float64)  # noqa: E731
-    toks = sample_tokens(cfg.T, 48, cfg.seed)
+    toks = sample_tokens(cfg.T, 1024, cfg.seed)
     rdx, rdl, _, _ = oracle.backward(d["x"][toks], d["logits"][toks], d["w_gu"], d["w_d"], f(dout[toks]), cfg.k)
     assert_close_bf16(host_f64(dx)[toks], rdx, "dx[sampled]", tight=False)
     _close(dl.cpu().numpy()[toks], rdl, "dlogits[sampled]")
