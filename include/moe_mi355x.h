@@ -93,7 +93,9 @@ typedef enum moe_status {
     MOE_ERR_MISALIGNED_POINTER = 5, /* a tensor pointer is not 16-byte aligned */
     MOE_ERR_WORKSPACE_TOO_SMALL = 6,
     MOE_ERR_HIP = 7,                /* a HIP call failed; see moe_last_error_message */
-    MOE_ERR_INVALID_VALUE = 8       /* a scalar argument is out of range (see each call) */
+    MOE_ERR_INVALID_VALUE = 8,      /* a scalar argument is out of range (see each call) */
+    MOE_ERR_PRECONDITION = 9        /* debug build only: a precondition on device data failed
+                                       (moe_debug_status) */
 } moe_status;
 
 #define MOE_MAX_K 32    /* largest top-k */
@@ -425,6 +427,59 @@ moe_status moe_permute_backward(const moe_bf16 *dx_perm, const int32_t *route_ro
 moe_status moe_grouped_wgrad(const moe_bf16 *a, const moe_bf16 *b, const int32_t *row_token,
                              const int32_t *expert_counts, const int32_t *expert_offsets, int32_t E,
                              int32_t M, int32_t N, int64_t P_max, float *dw, moe_stream_t stream);
+
+/*
+ * Debug build [prime-rl, Changes: 32-bit row offsets overflowed silently -- a bad
+ * index must be reported, not turned into a stray write]. The debug library
+ * (libmoe_mi355x_debug.so, built with MOE_DEBUG) exports the same calls; ahead of
+ * each call's kernels it enqueues checks of the preconditions the release kernels
+ * trust without checking:
+ *   moe_route_topk            every logit finite
+ *   moe_permute               every top-k id in [0, E), a token's k ids distinct
+ *   every call taking expert_offsets   offsets[0] == 0, non-decreasing,
+ *                             offsets[E] <= P_max, and (where counts are passed)
+ *                             0 <= counts[e] <= offsets[e+1] - offsets[e]
+ *   moe_combine, moe_permute_backward, moe_combine_backward   route_row in [-1, P_max)
+ *   the gathering gate/up GEMMs   row_token in [-1, T)
+ * A failed check stores a code in a device word; from then on every kernel of the
+ * library (this call's and later calls') does nothing until moe_debug_reset, so
+ * no kernel runs on the bad data and nothing traps. The calls themselves still
+ * return MOE_OK (nothing is read back); moe_debug_status reports the word.
+ *
+ * moe_debug_build:  1 in the debug library, 0 in the release library.
+ * moe_debug_status: synchronises `stream`, reads the word: MOE_OK if no check has
+ *                   failed, else MOE_ERR_PRECONDITION with moe_last_error_message()
+ *                   naming the failed check. The release library returns MOE_OK.
+ * moe_debug_reset:  enqueues a clear of the word on `stream` (no-op in release).
+ * The word is one per device and process, shared by all streams.
+ */
+int moe_debug_build(void);
+moe_status moe_debug_status(moe_stream_t stream);
+moe_status moe_debug_reset(moe_stream_t stream);
+
+/*
+ * Measurement probes -- not part of the layer. The chip's own roofs, measured on
+ * the device at hand, so kernel times can be placed against them as well as
+ * against the published peaks [PocketLLM, Theoretical ceilings / Hardware roofs:
+ * a measured copy rate and measured GEMM rates quoted beside the spec].
+ *
+ * moe_probe_copy: dst[0 .. bytes) = src[0 .. bytes) with a grid-stride kernel of
+ * non-temporal 16-byte loads and stores (bytes read + bytes written, each once).
+ *   src, dst  device buffers of `bytes` bytes, 16-byte aligned, not overlapping
+ *   bytes     a positive multiple of 16, else MOE_ERR_INVALID_SHAPE
+ *
+ * moe_probe_mfma_bf16: a register-only loop of v_mfma_f32_32x32x16_bf16 on every
+ * compute unit (8 waves per CU, 4 independent accumulator chains per wave,
+ * `iters` rounds); no memory traffic but one float per thread written to sink.
+ *   sink         device buffer of at least moe_probe_mfma_sink_floats() floats
+ *                (MOE_ERR_WORKSPACE_TOO_SMALL otherwise); its values are meaningless
+ *   iters >= 1   (MOE_ERR_INVALID_VALUE otherwise)
+ *   *flops       host out: the launch's bf16 flops (2*32*32*16 per MFMA)
+ */
+moe_status moe_probe_copy(const void *src, void *dst, size_t bytes, moe_stream_t stream);
+moe_status moe_probe_mfma_bf16(float *sink, int64_t sink_floats, int32_t iters, double *flops,
+                               moe_stream_t stream);
+int64_t moe_probe_mfma_sink_floats(void);
 
 #ifdef __cplusplus
 }

@@ -16,6 +16,7 @@ import torch  # loads the HIP runtime that the library then shares
 from .build import library_path
 
 _LIB = None
+_HANDLES = {}  # debug flag -> loaded library
 
 _c_i32, _c_i64, _c_sz, _c_vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
 
@@ -32,15 +33,30 @@ class MoEError(RuntimeError):
 
 
 def load():
-    """Load the built library, building it first only if nothing is built.
-    A failed build or load raises: there is no fallback path."""
+    """The library every call goes to: the release library unless use_debug_library
+    switched to the debug one. Built first only if nothing is built; a failed build
+    or load raises: there is no fallback path."""
     global _LIB
-    if _LIB is not None:
-        return _LIB
-    path = library_path()
+    if _LIB is None:
+        _LIB = _open(False)
+    return _LIB
+
+
+def use_debug_library(debug: bool = True):
+    """Route every later call to the debug library (device-side precondition
+    checks, moe_debug_status) or back to the release library."""
+    global _LIB
+    _LIB = _open(debug)
+    return _LIB
+
+
+def _open(debug: bool):
+    if debug in _HANDLES:
+        return _HANDLES[debug]
+    path = library_path(debug)
     if not os.path.exists(path):
         from .build import build
-        build()
+        build(debug=debug)
     lib = ctypes.CDLL(path)
     lib.moe_status_string.argtypes = [ctypes.c_int]
     lib.moe_status_string.restype = ctypes.c_char_p
@@ -83,7 +99,18 @@ def load():
     lib.moe_router_prepare.argtypes = [_c_vp, _c_i32, _c_i32, _c_vp, _c_vp, _c_vp]
     lib.moe_router_topk.argtypes = [_c_vp, _c_vp, _c_vp, _c_i64, _c_i32, _c_i32, _c_i32, _c_vp, _c_vp, _c_vp,
                                     _c_vp]
-    for fn in ("moe_permute_workspace_size", "moe_route_topk", "moe_permute",
+    lib.moe_probe_copy.argtypes = [_c_vp, _c_vp, _c_sz, _c_vp]
+    lib.moe_probe_mfma_bf16.argtypes = [_c_vp, _c_i64, _c_i32, ctypes.POINTER(ctypes.c_double), _c_vp]
+    lib.moe_probe_mfma_sink_floats.argtypes = []
+    lib.moe_probe_mfma_sink_floats.restype = _c_i64
+    lib.moe_debug_build.argtypes = []
+    lib.moe_debug_build.restype = ctypes.c_int
+    lib.moe_debug_status.argtypes = [_c_vp]
+    lib.moe_debug_status.restype = ctypes.c_int
+    lib.moe_debug_reset.argtypes = [_c_vp]
+    lib.moe_debug_reset.restype = ctypes.c_int
+    for fn in ("moe_permute_workspace_size", "moe_route_topk", "moe_permute", "moe_probe_copy",
+               "moe_probe_mfma_bf16",
                "moe_grouped_glu_gemm", "moe_grouped_glu_gemm_gather", "moe_grouped_down_gemm",
                "moe_combine", "moe_quantize_fp8", "moe_grouped_glu_gemm_fp8w",
                "moe_grouped_glu_gemm_gather_fp8w", "moe_grouped_down_gemm_fp8w", "moe_grouped_gemm",
@@ -91,7 +118,7 @@ def load():
                "moe_route_backward", "moe_permute_backward", "moe_grouped_wgrad", "moe_router_prepare",
                "moe_router_topk", "moe_grouped_gemm_swiglu_backward", "moe_grouped_glu_gemm_clamped"):
         getattr(lib, fn).restype = ctypes.c_int
-    _LIB = lib
+    _HANDLES[debug] = lib
     return lib
 
 
@@ -615,3 +642,44 @@ def moe_forward(x, logits, w_gate_up, w_down, k: int, align: int = 32):
     E, two_i, _ = w_gate_up.shape
     layer = MoELayer(T, H, E, k, two_i // 2, align, device=x.device)
     return layer(x, logits, w_gate_up, w_down).clone()
+
+
+# ---- measurement probes (not part of the layer) ----------------------------------------
+
+def probe_copy(src: torch.Tensor, dst: torch.Tensor, stream=None):
+    """dst = src bytewise through the library's streaming copy kernel."""
+    if src.numel() * src.element_size() != dst.numel() * dst.element_size():
+        raise ValueError("src and dst must hold the same number of bytes")
+    nbytes = src.numel() * src.element_size()
+    _call("moe_probe_copy", _ptr(src, src.dtype, "src"), _ptr(dst, dst.dtype, "dst"), nbytes,
+          _stream(stream))
+
+
+def probe_mfma_sink(device=None) -> torch.Tensor:
+    return torch.empty(int(load().moe_probe_mfma_sink_floats()), dtype=torch.float32, device=device or "cuda")
+
+
+def probe_mfma_bf16(sink: torch.Tensor, iters: int, stream=None) -> float:
+    """Launches the register-only bf16 MFMA loop; returns its flops per launch."""
+    fl = ctypes.c_double(0.0)
+    _call("moe_probe_mfma_bf16", _ptr(sink, torch.float32, "sink"), sink.numel(), iters, ctypes.byref(fl),
+          _stream(stream))
+    return float(fl.value)
+
+
+# ---- debug build ------------------------------------------------------------------------
+
+def debug_build() -> bool:
+    return bool(load().moe_debug_build())
+
+
+def debug_status(stream=None):
+    """(status, message) of the device-side precondition checks; synchronises the
+    stream. The release library always reports (0, "release build: ...")."""
+    lib = load()
+    st = int(lib.moe_debug_status(_stream(stream)))
+    return st, lib.moe_last_error_message().decode()
+
+
+def debug_reset(stream=None):
+    _call("moe_debug_reset", _stream(stream))

@@ -17,13 +17,14 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 SOURCES = ["api.hip", "route_topk.hip", "permute.hip", "grouped_gemm.hip", "grouped_gemm_small.hip",
-           "combine.hip", "quantize.hip", "backward.hip", "wgrad.hip", "router.hip"]
+           "combine.hip", "quantize.hip", "backward.hip", "wgrad.hip", "router.hip", "probes.hip", "debug.hip"]
 LIB_NAME = "libmoe_mi355x.so"
+DEBUG_LIB_NAME = "libmoe_mi355x_debug.so"
 ARCH = "gfx950"
 
 
-def library_path() -> str:
-    return os.path.join(PKG, LIB_NAME)
+def library_path(debug: bool = False) -> str:
+    return os.path.join(PKG, DEBUG_LIB_NAME if debug else LIB_NAME)
 
 
 def hipcc() -> str:
@@ -40,13 +41,19 @@ def common_flags():
             "-I", os.path.join(ROOT, "include")]
 
 
-def build(verbose: bool = False, resource_usage: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, resource_usage: bool = False, debug: bool = False) -> str:
+    """Compiles every source and links the library. debug=True builds the debug
+    library instead (MOE_DEBUG: device-side precondition checks; relocatable
+    device code, so every kernel sees the one status word debug.hip defines)."""
+    bdir = BUILD + ("_debug" if debug else "")
+    os.makedirs(bdir, exist_ok=True)
     cc = hipcc()
     extra = ["-Rpass-analysis=kernel-resource-usage"] if resource_usage else []
+    if debug:
+        extra += ["-DMOE_DEBUG", "-fgpu-rdc"]
 
     def compile_one(src):
-        obj = os.path.join(BUILD, src.replace(".hip", ".o"))
+        obj = os.path.join(bdir, src.replace(".hip", ".o"))
         cmd = [cc, *common_flags(), *extra, "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
@@ -62,9 +69,10 @@ def build(verbose: bool = False, resource_usage: bool = False) -> str:
 
     with cf.ThreadPoolExecutor(len(SOURCES)) as ex:
         objs = list(ex.map(compile_one, SOURCES))
-    out = library_path()
+    out = library_path(debug)
     tmp = out + f".tmp{os.getpid()}"
-    cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
+    link = ["-fgpu-rdc", "--hip-link"] if debug else []
+    cmd = [cc, f"--offload-arch={ARCH}", *link, "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
@@ -73,4 +81,5 @@ def build(verbose: bool = False, resource_usage: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv, resource_usage="--resource-usage" in sys.argv))
+    print(build(verbose="-v" in sys.argv, resource_usage="--resource-usage" in sys.argv,
+                debug="--debug" in sys.argv))

@@ -11,6 +11,7 @@ hipError_t launch_route_topk(const float*, int64_t, int, int, int32_t*, float*, 
 hipError_t launch_permute(const uint16_t*, const int32_t*, int64_t, int, int, int, int, int64_t,
                           int32_t*, int32_t*, int32_t*, int32_t*, uint16_t*, void*, hipStream_t);
 size_t permute_workspace_bytes(int64_t R, int E);
+
 hipError_t launch_grouped_glu_gemm(const uint16_t*, const void*, const float*, const int32_t*, int,
                                    int, int, uint16_t*, hipStream_t);
 hipError_t launch_grouped_glu_gemm_gather(const uint16_t*, const int32_t*, const void*, const float*,
@@ -37,6 +38,18 @@ hipError_t launch_wgrad(const uint16_t*, const uint16_t*, const int32_t*, const 
                         hipStream_t);
 hipError_t launch_combine(const uint16_t*, const int32_t*, const float*, int64_t, int, int,
                           int64_t, uint16_t*, hipStream_t);
+hipError_t launch_probe_copy(const void*, void*, size_t, int, hipStream_t);
+hipError_t launch_probe_mfma(float*, int, int, hipStream_t);
+int probe_mfma_blocks(int);
+double probe_mfma_flops(int, int);
+#ifdef MOE_DEBUG
+hipError_t debug_check_logits(const float*, int64_t, hipStream_t);
+hipError_t debug_check_ids(const int32_t*, int64_t, int, int, hipStream_t);
+hipError_t debug_check_layout(const int32_t*, const int32_t*, int, int64_t, hipStream_t);
+hipError_t debug_check_rows(const int32_t*, int64_t, int64_t, int64_t, int32_t, hipStream_t);
+hipError_t debug_read(int32_t*, hipStream_t);
+hipError_t debug_reset(hipStream_t);
+#endif
 }  // namespace moe
 
 namespace {
@@ -62,6 +75,20 @@ moe_status hip_status(hipError_t e, const char* what) {
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Debug build: enqueue a precondition check ahead of the call's kernels (see
+// debug.hip); release builds compile these to nothing.
+#ifdef MOE_DEBUG
+#define DEBUG_CHECK(expr)                                                  \
+    do {                                                                   \
+        const hipError_t e_ = (expr);                                      \
+        if (e_ != hipSuccess) return hip_status(e_, "debug check launch"); \
+    } while (0)
+#else
+#define DEBUG_CHECK(expr) \
+    do {                  \
+    } while (0)
+#endif
 
 #define REQUIRE_PTR(p)                                                             \
     do {                                                                           \
@@ -118,6 +145,14 @@ hipError_t launch_down(const uint16_t* h, const void* w, const float* scale, con
     return moe::launch_grouped_down_gemm(h, w, scale, offsets, E, H, I, y, stream);
 }
 
+// compute units of the current device (256 on an MI355X)
+int device_cus() {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 256;
+    return n;
+}
+
 moe_status check_pmax(int64_t P_max) {
     if (P_max < 1 || P_max >= ((int64_t)1 << 31))
         return fail(MOE_ERR_SIZE_OVERFLOW, "P_max=%lld outside [1, 2^31)", (long long)P_max);
@@ -139,6 +174,7 @@ const char* moe_status_string(int s) {
         case MOE_ERR_WORKSPACE_TOO_SMALL: return "MOE_ERR_WORKSPACE_TOO_SMALL";
         case MOE_ERR_HIP: return "MOE_ERR_HIP";
         case MOE_ERR_INVALID_VALUE: return "MOE_ERR_INVALID_VALUE";
+        case MOE_ERR_PRECONDITION: return "MOE_ERR_PRECONDITION";
         default: return "MOE_ERR_UNKNOWN";
     }
 }
@@ -167,15 +203,15 @@ moe_status moe_route_topk(const float* logits, int64_t T, int32_t E, int32_t k, 
     if (T < 0 || T >= ((int64_t)1 << 31)) return fail(MOE_ERR_INVALID_SHAPE, "T=%lld outside [0, 2^31)", (long long)T);
     moe_status s = check_ek(E, k);
     if (s != MOE_OK) return s;
+    DEBUG_CHECK(moe::debug_check_logits(logits, T * (int64_t)E, (hipStream_t)stream));
     return hip_status(moe::launch_route_topk(logits, T, E, k, topk_idx, topk_w, (hipStream_t)stream),
                       "moe_route_topk launch");
 }
 
-moe_status moe_permute(const moe_bf16* x, const int32_t* topk_idx, int64_t T, int32_t H, int32_t E,
-                       int32_t k, int32_t align, int64_t P_max, int32_t* expert_counts,
-                       int32_t* expert_offsets, int32_t* route_row, int32_t* row_token,
-                       moe_bf16* x_perm, void* workspace, size_t workspace_bytes,
-                       moe_stream_t stream) {
+static moe_status check_permute(const moe_bf16* x, const int32_t* topk_idx, int64_t T, int32_t H, int32_t E,
+                                int32_t k, int32_t align, int64_t P_max, const int32_t* expert_counts,
+                                const int32_t* expert_offsets, const int32_t* route_row, const int32_t* row_token,
+                                const moe_bf16* x_perm) {
     // x_perm == NULL: the layout only (no gather), and x is not read
     REQUIRE_PTR_UNLESS_EMPTY(x, T == 0 || !x_perm);
     REQUIRE_PTR_UNLESS_EMPTY(topk_idx, T == 0);
@@ -184,7 +220,6 @@ moe_status moe_permute(const moe_bf16* x, const int32_t* topk_idx, int64_t T, in
     REQUIRE_PTR_UNLESS_EMPTY(route_row, T == 0);
     REQUIRE_PTR(row_token);
     REQUIRE_PTR_UNLESS_EMPTY(x_perm, true);
-    REQUIRE_PTR_UNLESS_EMPTY(workspace, T == 0);
     if (T < 0) return fail(MOE_ERR_INVALID_SHAPE, "T=%lld < 0", (long long)T);
     moe_status s = check_ek(E, k);
     if (s != MOE_OK) return s;
@@ -196,9 +231,22 @@ moe_status moe_permute(const moe_bf16* x, const int32_t* topk_idx, int64_t T, in
     if (need < 0 || need > P_max)
         return fail(MOE_ERR_SIZE_OVERFLOW, "P_max=%lld < T*k + E*(align-1) = %lld", (long long)P_max,
                     (long long)need);
+    return MOE_OK;
+}
+
+moe_status moe_permute(const moe_bf16* x, const int32_t* topk_idx, int64_t T, int32_t H, int32_t E,
+                       int32_t k, int32_t align, int64_t P_max, int32_t* expert_counts,
+                       int32_t* expert_offsets, int32_t* route_row, int32_t* row_token,
+                       moe_bf16* x_perm, void* workspace, size_t workspace_bytes,
+                       moe_stream_t stream) {
+    moe_status s = check_permute(x, topk_idx, T, H, E, k, align, P_max, expert_counts, expert_offsets, route_row,
+                                 row_token, x_perm);
+    if (s != MOE_OK) return s;
+    REQUIRE_PTR_UNLESS_EMPTY(workspace, T == 0);
     const size_t ws = moe::permute_workspace_bytes(T * k, E);
     if (workspace_bytes < ws)
         return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", workspace_bytes, ws);
+    DEBUG_CHECK(moe::debug_check_ids(topk_idx, T, k, E, (hipStream_t)stream));
     return hip_status(moe::launch_permute(x, topk_idx, T, H, E, k, align, P_max, expert_counts,
                                           expert_offsets, route_row, row_token, x_perm, workspace,
                                           (hipStream_t)stream),
@@ -229,6 +277,7 @@ moe_status moe_grouped_glu_gemm(const moe_bf16* x_perm, const moe_bf16* w_gate_u
                                 moe_stream_t stream) {
     moe_status s = check_gemm(x_perm, w_gate_up, expert_counts, expert_offsets, E, H, I, P_max, h);
     if (s != MOE_OK) return s;
+    DEBUG_CHECK(moe::debug_check_layout(expert_counts, expert_offsets, E, P_max, (hipStream_t)stream));
     return hip_status(launch_glu(x_perm, nullptr, w_gate_up, nullptr, expert_offsets, E, H, I, P_max, h,
                                  (hipStream_t)stream),
                       "moe_grouped_glu_gemm launch");
@@ -250,6 +299,7 @@ moe_status moe_grouped_glu_gemm_clamped(const moe_bf16* x_perm, const moe_bf16* 
     moe_status s = check_gemm(x_perm, w_gate_up, expert_counts, expert_offsets, E, H, I, P_max, h);
     if (s != MOE_OK) return s;
     if (!(limit >= 0.0f)) return fail(MOE_ERR_INVALID_VALUE, "limit=%g must be >= 0", (double)limit);
+    DEBUG_CHECK(moe::debug_check_layout(expert_counts, expert_offsets, E, P_max, (hipStream_t)stream));
     return hip_status(moe::launch_grouped_glu_gemm_clamped(x_perm, w_gate_up, expert_offsets, E, H, I, limit, h,
                                                            (hipStream_t)stream),
                       "moe_grouped_glu_gemm_clamped launch");
@@ -262,6 +312,8 @@ moe_status moe_grouped_glu_gemm_gather(const moe_bf16* x, const int32_t* row_tok
     moe_status s = check_gemm(x, w_gate_up, expert_counts, expert_offsets, E, H, I, P_max, h);
     if (s != MOE_OK) return s;
     if ((s = check_gather(row_token, T, H)) != MOE_OK) return s;
+    DEBUG_CHECK(moe::debug_check_layout(expert_counts, expert_offsets, E, P_max, (hipStream_t)stream));
+    DEBUG_CHECK(moe::debug_check_rows(row_token, P_max, -1, T, 6, (hipStream_t)stream));
     return hip_status(launch_glu(x, row_token, w_gate_up, nullptr, expert_offsets, E, H, I, P_max, h,
                                  (hipStream_t)stream),
                       "moe_grouped_glu_gemm_gather launch");
@@ -273,6 +325,7 @@ moe_status moe_grouped_down_gemm(const moe_bf16* h, const moe_bf16* w_down,
                                  moe_stream_t stream) {
     moe_status s = check_gemm(h, w_down, expert_counts, expert_offsets, E, H, I, P_max, y);
     if (s != MOE_OK) return s;
+    DEBUG_CHECK(moe::debug_check_layout(expert_counts, expert_offsets, E, P_max, (hipStream_t)stream));
     return hip_status(launch_down(h, w_down, nullptr, expert_offsets, E, H, I, P_max, y, (hipStream_t)stream),
                       "moe_grouped_down_gemm launch");
 }
@@ -299,6 +352,7 @@ moe_status moe_grouped_glu_gemm_fp8w(const moe_bf16* x_perm, const uint8_t* w8_g
     moe_status s = check_gemm(x_perm, w8_gate_up, expert_counts, expert_offsets, E, H, I, P_max, h);
     if (s != MOE_OK) return s;
     REQUIRE_PTR(scale_gate_up);
+    DEBUG_CHECK(moe::debug_check_layout(expert_counts, expert_offsets, E, P_max, (hipStream_t)stream));
     return hip_status(launch_glu(x_perm, nullptr, w8_gate_up, scale_gate_up, expert_offsets, E, H, I, P_max,
                                  h, (hipStream_t)stream),
                       "moe_grouped_glu_gemm_fp8w launch");
@@ -314,6 +368,8 @@ moe_status moe_grouped_glu_gemm_gather_fp8w(const moe_bf16* x, const int32_t* ro
     if (s != MOE_OK) return s;
     REQUIRE_PTR(scale_gate_up);
     if ((s = check_gather(row_token, T, H)) != MOE_OK) return s;
+    DEBUG_CHECK(moe::debug_check_layout(expert_counts, expert_offsets, E, P_max, (hipStream_t)stream));
+    DEBUG_CHECK(moe::debug_check_rows(row_token, P_max, -1, T, 6, (hipStream_t)stream));
     return hip_status(launch_glu(x, row_token, w8_gate_up, scale_gate_up, expert_offsets, E, H, I, P_max, h,
                                  (hipStream_t)stream),
                       "moe_grouped_glu_gemm_gather_fp8w launch");
@@ -326,6 +382,7 @@ moe_status moe_grouped_down_gemm_fp8w(const moe_bf16* h, const uint8_t* w8_down,
     moe_status s = check_gemm(h, w8_down, expert_counts, expert_offsets, E, H, I, P_max, y);
     if (s != MOE_OK) return s;
     REQUIRE_PTR(scale_down);
+    DEBUG_CHECK(moe::debug_check_layout(expert_counts, expert_offsets, E, P_max, (hipStream_t)stream));
     return hip_status(launch_down(h, w8_down, scale_down, expert_offsets, E, H, I, P_max, y,
                                   (hipStream_t)stream),
                       "moe_grouped_down_gemm_fp8w launch");
@@ -337,6 +394,7 @@ moe_status moe_grouped_gemm(const moe_bf16* a, const moe_bf16* w, const int32_t*
     // the down GEMM's kernel is the plain grouped GEMM: (H, I) = (N, K)
     moe_status s = check_gemm(a, w, expert_counts, expert_offsets, E, N, K, P_max, c);
     if (s != MOE_OK) return s;
+    DEBUG_CHECK(moe::debug_check_layout(expert_counts, expert_offsets, E, P_max, (hipStream_t)stream));
     return hip_status(launch_down(a, w, nullptr, expert_offsets, E, N, K, P_max, c, (hipStream_t)stream),
                       "moe_grouped_gemm launch");
 }
@@ -355,6 +413,7 @@ moe_status moe_swiglu(const moe_bf16* gu, const int32_t* expert_offsets, int32_t
     REQUIRE_PTR(h);
     moe_status s = check_swiglu(expert_offsets, E, I, P_max);
     if (s != MOE_OK) return s;
+    DEBUG_CHECK(moe::debug_check_layout(nullptr, expert_offsets, E, P_max, (hipStream_t)stream));
     return hip_status(moe::launch_swiglu(gu, nullptr, expert_offsets, E, I, P_max, h, (hipStream_t)stream),
                       "moe_swiglu launch");
 }
@@ -366,6 +425,7 @@ moe_status moe_swiglu_backward(const moe_bf16* dh, const moe_bf16* gu, const int
     REQUIRE_PTR(dgu);
     moe_status s = check_swiglu(expert_offsets, E, I, P_max);
     if (s != MOE_OK) return s;
+    DEBUG_CHECK(moe::debug_check_layout(nullptr, expert_offsets, E, P_max, (hipStream_t)stream));
     return hip_status(moe::launch_swiglu(gu, dh, expert_offsets, E, I, P_max, dgu, (hipStream_t)stream),
                       "moe_swiglu_backward launch");
 }
@@ -376,6 +436,7 @@ moe_status moe_grouped_gemm_swiglu_backward(const moe_bf16* dy, const moe_bf16* 
     moe_status s = check_gemm(dy, w_down_t, expert_counts, expert_offsets, E, H, I, P_max, dgu);
     if (s != MOE_OK) return s;
     REQUIRE_PTR(gu);
+    DEBUG_CHECK(moe::debug_check_layout(expert_counts, expert_offsets, E, P_max, (hipStream_t)stream));
     return hip_status(moe::launch_grouped_gemm_swiglu_bwd(dy, w_down_t, gu, expert_offsets, E, H, I, dgu,
                                                           (hipStream_t)stream),
                       "moe_grouped_gemm_swiglu_backward launch");
@@ -411,6 +472,8 @@ moe_status moe_combine_backward(const moe_bf16* dout, const moe_bf16* y, const i
     if (s != MOE_OK) return s;
     if ((s = check_dim64("H", H)) != MOE_OK) return s;
     if ((s = check_pmax(P_max)) != MOE_OK) return s;
+    DEBUG_CHECK(moe::debug_check_layout(nullptr, expert_offsets, E, P_max, (hipStream_t)stream));
+    DEBUG_CHECK(moe::debug_check_rows(route_row, T * (int64_t)k, -1, P_max, 5, (hipStream_t)stream));
     return hip_status(moe::launch_combine_bwd(dout, y, route_row, topk_w, row_token, expert_offsets, T, H, k, E,
                                               P_max, dy, dw, (hipStream_t)stream),
                       "moe_combine_backward launch");
@@ -440,6 +503,7 @@ moe_status moe_permute_backward(const moe_bf16* dx_perm, const int32_t* route_ro
     moe_status s;
     if ((s = check_dim64("H", H)) != MOE_OK) return s;
     if ((s = check_pmax(P_max)) != MOE_OK) return s;
+    DEBUG_CHECK(moe::debug_check_rows(route_row, T * (int64_t)k, -1, P_max, 5, (hipStream_t)stream));
     return hip_status(moe::launch_combine(dx_perm, route_row, nullptr, T, H, k, P_max, dx, (hipStream_t)stream),
                       "moe_permute_backward launch");
 }
@@ -462,6 +526,7 @@ moe_status moe_grouped_wgrad(const moe_bf16* a, const moe_bf16* b, const int32_t
     if ((s = check_pmax(P_max)) != MOE_OK) return s;
     const int64_t tiles = (int64_t)E * ((M + 255) / 256) * ((N + 255) / 256);
     if (tiles >= ((int64_t)1 << 31)) return fail(MOE_ERR_SIZE_OVERFLOW, "E*M*N/65536 tiles reach 2^31");
+    DEBUG_CHECK(moe::debug_check_layout(expert_counts, expert_offsets, E, P_max, (hipStream_t)stream));
     return hip_status(moe::launch_wgrad(a, b, row_token, expert_offsets, E, M, N, dw, (hipStream_t)stream),
                       "moe_grouped_wgrad launch");
 }
@@ -507,8 +572,76 @@ moe_status moe_combine(const moe_bf16* y, const int32_t* route_row, const float*
     moe_status s;
     if ((s = check_dim64("H", H)) != MOE_OK) return s;
     if ((s = check_pmax(P_max)) != MOE_OK) return s;
+    DEBUG_CHECK(moe::debug_check_rows(route_row, T * (int64_t)k, -1, P_max, 5, (hipStream_t)stream));
     return hip_status(moe::launch_combine(y, route_row, topk_w, T, H, k, P_max, out, (hipStream_t)stream),
                       "moe_combine launch");
+}
+
+moe_status moe_probe_copy(const void* src, void* dst, size_t bytes, moe_stream_t stream) {
+    REQUIRE_PTR(src);
+    REQUIRE_PTR(dst);
+    if (bytes == 0 || bytes % 16 != 0)
+        return fail(MOE_ERR_INVALID_SHAPE, "bytes=%zu must be a positive multiple of 16", bytes);
+    return hip_status(moe::launch_probe_copy(src, dst, bytes, device_cus(), (hipStream_t)stream),
+                      "moe_probe_copy launch");
+}
+
+moe_status moe_probe_mfma_bf16(float* sink, int64_t sink_floats, int32_t iters, double* flops,
+                               moe_stream_t stream) {
+    REQUIRE_PTR(sink);
+    if (!flops) return fail(MOE_ERR_NULL_POINTER, "flops is NULL");
+    if (iters < 1) return fail(MOE_ERR_INVALID_VALUE, "iters=%d < 1", iters);
+    const int cus = device_cus();
+    const int64_t need = (int64_t)moe::probe_mfma_blocks(cus) * 256;
+    if (sink_floats < need)
+        return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "sink holds %lld floats < %lld needed", (long long)sink_floats,
+                    (long long)need);
+    *flops = moe::probe_mfma_flops(cus, iters);
+    return hip_status(moe::launch_probe_mfma(sink, iters, cus, (hipStream_t)stream), "moe_probe_mfma_bf16 launch");
+}
+
+int64_t moe_probe_mfma_sink_floats(void) { return (int64_t)moe::probe_mfma_blocks(device_cus()) * 256; }
+
+int moe_debug_build(void) {
+#ifdef MOE_DEBUG
+    return 1;
+#else
+    return 0;
+#endif
+}
+
+moe_status moe_debug_status(moe_stream_t stream) {
+#ifdef MOE_DEBUG
+    int32_t code = 0;
+    moe_status s = hip_status(moe::debug_read(&code, (hipStream_t)stream), "moe_debug_status");
+    if (s != MOE_OK) return s;
+    switch (code) {
+        case 0: return ok();
+        case 1: return fail(MOE_ERR_PRECONDITION, "moe_route_topk: a logit is not finite");
+        case 2: return fail(MOE_ERR_PRECONDITION, "moe_permute: a top-k id is outside [0, E)");
+        case 3: return fail(MOE_ERR_PRECONDITION, "moe_permute: a token's top-k ids are not distinct");
+        case 4: return fail(MOE_ERR_PRECONDITION,
+                            "expert_offsets/expert_counts: offsets[0] != 0, decreasing offsets, offsets[E] > P_max, "
+                            "or a count outside [0, its segment's rows]");
+        case 5: return fail(MOE_ERR_PRECONDITION, "route_row: a value outside [-1, P_max)");
+        case 6: return fail(MOE_ERR_PRECONDITION, "row_token: a value outside [-1, T)");
+        default: return fail(MOE_ERR_PRECONDITION, "unknown check code %d", code);
+    }
+#else
+    (void)stream;
+    g_err[0] = '\0';
+    snprintf(g_err, sizeof g_err, "release build: device-side preconditions are not checked");
+    return MOE_OK;
+#endif
+}
+
+moe_status moe_debug_reset(moe_stream_t stream) {
+#ifdef MOE_DEBUG
+    return hip_status(moe::debug_reset((hipStream_t)stream), "moe_debug_reset");
+#else
+    (void)stream;
+    return ok();
+#endif
 }
 
 }  // extern "C"

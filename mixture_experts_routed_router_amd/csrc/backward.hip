@@ -46,6 +46,7 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const uint4* __restric
                                                           const float* __restrict__ topk_w, int64_t T,
                                                           int pieces, int k, int64_t P_max,
                                                           uint4* __restrict__ dy, float* __restrict__ dw) {
+    MOE_DEBUG_GUARD();
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int64_t t = (int64_t)blockIdx.x * 4 + wave;
     if (t >= T) return;
@@ -117,6 +118,7 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const uint4* __restric
 __global__ __launch_bounds__(256) void zero_pad_rows_kernel(const int32_t* __restrict__ row_token,
                                                             const int32_t* __restrict__ offsets, int pieces,
                                                             uint4* __restrict__ dst) {
+    MOE_DEBUG_GUARD();
     __shared__ int64_t pad0;
     const int e = blockIdx.x;
     const int64_t s0 = offsets[e], s1 = offsets[e + 1];
@@ -144,6 +146,7 @@ __global__ __launch_bounds__(256) void route_bwd_kernel(const int32_t* __restric
                                                         const float* __restrict__ topk_w,
                                                         const float* __restrict__ dw, int64_t T, int E,
                                                         int k, float* __restrict__ dlogits) {
+    MOE_DEBUG_GUARD();
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int64_t t = (int64_t)blockIdx.x * 4 + wave;
     if (t >= T) return;
@@ -166,6 +169,7 @@ template <bool BWD>
 __global__ __launch_bounds__(256) void swiglu_kernel(const uint4* __restrict__ gu, const uint4* __restrict__ dh,
                                                      const int32_t* __restrict__ offsets, int E,
                                                      int64_t P_max, int pieces_i, uint4* __restrict__ out) {
+    MOE_DEBUG_GUARD();
     const int64_t used = offsets[E];
     const int64_t n = (used < P_max ? used : P_max) * pieces_i;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
@@ -193,6 +197,7 @@ __global__ __launch_bounds__(256) void swiglu_kernel(const uint4* __restrict__ g
 // ---- expert weight transpose [E, R, C] -> [E, C, R], 64x64 tiles through LDS ----
 __global__ __launch_bounds__(256) void transpose_kernel(const uint16_t* __restrict__ w, int R, int C,
                                                         uint16_t* __restrict__ wt) {
+    MOE_DEBUG_GUARD();
     __shared__ uint16_t tile[64][64 + 2];
     const int tiles_c = C / 64, tiles_r = R / 64;
     const int64_t b = blockIdx.x;

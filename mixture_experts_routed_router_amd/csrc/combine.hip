@@ -25,6 +25,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ 
                                                       const float* __restrict__ topk_w,
                                                       int64_t T, int pieces_per_row, int k, int64_t P_max,
                                                       uint4* __restrict__ out) {
+    MOE_DEBUG_GUARD();
     constexpr int CP = kCombinePieces;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int64_t t = (int64_t)blockIdx.x * 4 + wave;

@@ -8,6 +8,24 @@ namespace moe {
 
 constexpr int kWave = 64;  // CDNA wavefront width
 
+// Debug build (-DMOE_DEBUG, relocatable device code): check kernels enqueued ahead
+// of a call validate its documented preconditions on device data and, on a
+// failure, store a nonzero code in this word; every kernel of the library starts
+// by reading it and does nothing once it is set, so a bad input is reported
+// instead of faulting [prime-rl PR 3885, Changes: 32-bit row offsets overflowed
+// silently]. Release builds read nothing.
+#ifdef MOE_DEBUG
+extern __device__ int32_t g_moe_debug_word;
+#define MOE_DEBUG_GUARD()                                                  \
+    do {                                                                   \
+        if (*(volatile const int32_t*)&::moe::g_moe_debug_word != 0) return; \
+    } while (0)
+#else
+#define MOE_DEBUG_GUARD() \
+    do {                  \
+    } while (0)
+#endif
+
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
 typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float floatx16_t;

@@ -756,6 +756,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ row_token,
     const void* __restrict__ W, const float* __restrict__ w_scale, const int32_t* __restrict__ offsets,
     int E, int K, int N, uint16_t* __restrict__ C, const uint16_t* __restrict__ gu, float glu_limit) {
+    MOE_DEBUG_GUARD();
     static_assert(!SWB || (!GLU && !GATHER && !W8), "the SwiGLU backward epilogue follows the plain bf16 GEMM");
     __shared__ __attribute__((aligned(1024))) uint16_t lds[kLdsElems];
     __shared__ int32_t tile_start[kMaxE + 1];

@@ -183,6 +183,7 @@ __global__ __launch_bounds__(kSmallThreads) void grouped_gemm_small_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ row_token, const void* __restrict__ W,
     const float* __restrict__ w_scale, const int32_t* __restrict__ offsets, int E, int K, int N,
     uint16_t* __restrict__ C) {
+    MOE_DEBUG_GUARD();
     const int lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     constexpr int NB = GLU ? kSmallBlocksGlu : kSmallBlocksDown;

@@ -34,6 +34,7 @@ static __device__ __forceinline__ int key_bits(int E) { return E <= 1 ? 0 : 32 -
 __global__ __launch_bounds__(256) void permute_hist_kernel(const int32_t* __restrict__ topk_idx,
                                                            int64_t R, int E, int64_t nchunks,
                                                            int32_t* __restrict__ hist) {
+    MOE_DEBUG_GUARD();
     extern __shared__ int32_t lds_hist[];  // [4][E]
     const int wave = threadIdx.x / kWave, lane = lane_id();
     const int64_t c = (int64_t)blockIdx.x * 4 + wave;
@@ -68,6 +69,7 @@ constexpr int kScanWaves = kScanThreads / kWave;
 __global__ __launch_bounds__(kScanThreads) void permute_scan_kernel(int32_t* __restrict__ hist,
                                                                     int64_t nchunks, int E,
                                                                     int32_t* __restrict__ counts) {
+    MOE_DEBUG_GUARD();
     __shared__ int32_t part[kScanWaves][kWave];
     const int lane = lane_id(), wave = threadIdx.x / kWave;
     const int e = blockIdx.x * kWave + lane;
@@ -113,6 +115,7 @@ __global__ __launch_bounds__(kScatterThreads) void permute_scatter_kernel(
     const int32_t* __restrict__ topk_idx, int64_t R, int E, int k, int align, int64_t nchunks,
     int64_t P_max, const int32_t* __restrict__ base, const int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ route_row, int32_t* __restrict__ row_token) {
+    MOE_DEBUG_GUARD();
     extern __shared__ int32_t lds_cursor[];  // [4][E] cursors, [E+1] offsets, [4] wave totals
     int32_t* off = lds_cursor + 4 * E;
     int32_t* wtot = off + E + 1;
@@ -208,6 +211,7 @@ __global__ __launch_bounds__(kCopyThreads) void permute_copy_rows_kernel(
     const uint4* __restrict__ x, const int32_t* __restrict__ route_row, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ offsets, int64_t T, int k, int ppr, int64_t token_blocks,
     uint4* __restrict__ x_perm) {
+    MOE_DEBUG_GUARD();
     const int lane = lane_id();
     if ((int64_t)blockIdx.x >= token_blocks) {
         // pad rows [offsets[e] + counts[e], offsets[e+1]) of expert e

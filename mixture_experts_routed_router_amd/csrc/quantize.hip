@@ -31,6 +31,7 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_fp8_kernel(const uint1
                                                                      int64_t block_elems,
                                                                      uint8_t* __restrict__ w8,
                                                                      float* __restrict__ scale) {
+    MOE_DEBUG_GUARD();
     const int64_t blk = blockIdx.x;
     const uint16_t* src = w + blk * block_elems;
     uint8_t* dst = w8 + blk * block_elems;

@@ -11,6 +11,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(const float* 
                                                                    int64_t T, int E, int k,
                                                                    int32_t* __restrict__ topk_idx,
                                                                    float* __restrict__ topk_w) {
+    MOE_DEBUG_GUARD();
     const int sub = lane_id() & (LPT - 1);
     const int64_t t = ((int64_t)blockIdx.x * kRouteThreads + threadIdx.x) / LPT;
     const bool live = t < T;

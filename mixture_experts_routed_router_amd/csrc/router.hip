@@ -29,6 +29,7 @@ constexpr int kRouterDepth = 4;  // k steps of loads in flight per wave (divides
 __global__ __launch_bounds__(256) void router_prepare_kernel(const float* __restrict__ w, int H, int E,
                                                              uint16_t* __restrict__ w_hi,
                                                              uint16_t* __restrict__ w_lo) {
+    MOE_DEBUG_GUARD();
     const int64_t n = (int64_t)H * E;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
         const int64_t e = i / H, h = i - e * H;  // output [E, H]
@@ -45,6 +46,7 @@ __global__ __launch_bounds__(kRouterThreads) void router_topk_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w_hi, const uint16_t* __restrict__ w_lo,
     int64_t T, int H, int E, int k, float* __restrict__ logits_out, int32_t* __restrict__ topk_idx,
     float* __restrict__ topk_w) {
+    MOE_DEBUG_GUARD();
     extern __shared__ __attribute__((aligned(16))) float lg[];  // [32][ep]
     const int ep = (E + 31) / 32 * 32;
     const int nblk = ep / 32;

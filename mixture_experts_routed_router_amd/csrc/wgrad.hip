@@ -41,6 +41,7 @@ __global__ __launch_bounds__(kWgThreads, 1) void wgrad_kernel(const uint16_t* __
                                                     const int32_t* __restrict__ row_token,
                                                     const int32_t* __restrict__ offsets, int M, int N,
                                                     int tiles_m, int tiles_n, float* __restrict__ dW) {
+    MOE_DEBUG_GUARD();
     __shared__ __attribute__((aligned(16))) uint16_t at[2][kWgBM][kWgStride];
     __shared__ __attribute__((aligned(16))) uint16_t bt[2][kWgBN][kWgStride];
 

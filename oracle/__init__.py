@@ -77,6 +77,8 @@ def _load(path: str):
     lib.moe_oracle_router_logits.argtypes = [_u16p, _f32p, i64, i32, i32, _f64p]
     lib.moe_oracle_num_threads.argtypes = []
     lib.moe_oracle_num_threads.restype = ctypes.c_int
+    lib.moe_oracle_set_num_threads.argtypes = [ctypes.c_int]
+    lib.moe_oracle_set_num_threads.restype = None
     for name in ("moe_oracle_route_topk", "moe_oracle_layout", "moe_oracle_gather",
                  "moe_oracle_glu", "moe_oracle_down", "moe_oracle_combine",
                  "moe_oracle_forward", "moe_oracle_fp8_encode", "moe_oracle_fp8_decode",
@@ -102,6 +104,11 @@ def _lib():
 def num_threads(lib=None) -> int:
     """OpenMP threads the oracle's loops run on."""
     return int((lib or _lib()).moe_oracle_num_threads())
+
+
+def set_num_threads(n: int, lib=None) -> None:
+    """OpenMP threads for later oracle calls made from this thread."""
+    (lib or _lib()).moe_oracle_set_num_threads(int(n))
 
 
 def _p(a: np.ndarray, ptype):

@@ -750,3 +750,6 @@ int moe_oracle_backward(const uint16_t *x, const float *logits, const uint16_t *
 
 /* Threads the OpenMP loops above use (for reporting the oracle's CPU time). */
 int moe_oracle_num_threads(void) { return omp_get_max_threads(); }
+
+/* Threads later calls from this thread run on (timing the oracle on one core). */
+void moe_oracle_set_num_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }

@@ -12,8 +12,9 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "moe_mi355x.h")
 LIB = os.path.join(ROOT, "mixture_experts_routed_router_amd", "libmoe_mi355x.so")
+DEBUG_LIB = os.path.join(ROOT, "mixture_experts_routed_router_amd", "libmoe_mi355x_debug.so")
 
-OK, NULLP, SHAPE, ALIGN, OVERFLOW, MISALIGNED, WORKSPACE, HIP, VALUE = range(9)
+OK, NULLP, SHAPE, ALIGN, OVERFLOW, MISALIGNED, WORKSPACE, HIP, VALUE, PRECONDITION = range(10)
 
 
 def declared_functions():
@@ -72,11 +73,42 @@ def test_every_declared_symbol_is_exported(lib):
         assert hasattr(lib, name), f"{name} declared in the header but not exported"
 
 
+@pytest.fixture(scope="module")
+def debug_lib():
+    if not os.path.exists(DEBUG_LIB):
+        from mixture_experts_routed_router_amd.build import build
+        build(debug=True)
+    return ctypes.CDLL(DEBUG_LIB)
+
+
+def test_debug_library_exports_the_same_calls(lib, debug_lib):
+    for name in declared_functions():
+        assert hasattr(debug_lib, name), f"{name} not exported by the debug library"
+    assert debug_lib.moe_debug_build() == 1
+    assert lib.moe_debug_build() == 0
+    # host validation is the same in both
+    assert debug_lib.moe_route_topk(FAKE, 4, 8, 9, FAKE, FAKE, None) == SHAPE
+    assert debug_lib.moe_combine(FAKE, FAKE, FAKE, 4, 128, 2, 100, None, None) == NULLP
+
+
+def test_probe_validation(lib):
+    assert lib.moe_probe_copy(None, FAKE, 1024, None) == NULLP
+    assert lib.moe_probe_copy(FAKE, FAKE, 1000, None) == SHAPE      # not a multiple of 16
+    assert lib.moe_probe_copy(FAKE, FAKE, 0, None) == SHAPE
+    fl = ctypes.c_double(0.0)
+    lib.moe_probe_mfma_bf16.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                                        ctypes.POINTER(ctypes.c_double), ctypes.c_void_p]
+    assert lib.moe_probe_mfma_bf16(None, 1 << 20, 10, ctypes.byref(fl), None) == NULLP
+    assert lib.moe_probe_mfma_bf16(FAKE, 1 << 20, 0, ctypes.byref(fl), None) == VALUE
+    assert lib.moe_probe_mfma_bf16(FAKE, 1 << 20, 10, None, None) == NULLP
+
+
 def test_status_strings(lib):
     assert lib.moe_status_string(0) == b"MOE_OK"
     assert lib.moe_status_string(OVERFLOW) == b"MOE_ERR_SIZE_OVERFLOW"
     assert lib.moe_status_string(99) == b"MOE_ERR_UNKNOWN"
     assert lib.moe_status_string(VALUE) == b"MOE_ERR_INVALID_VALUE"
+    assert lib.moe_status_string(PRECONDITION) == b"MOE_ERR_PRECONDITION"
 
 
 def test_padded_rows_and_workspace(lib):
@@ -233,9 +265,10 @@ def test_combine_validation(lib):
     assert lib.moe_combine(FAKE, FAKE, FAKE, 4, 128, 2, 1 << 31, FAKE, None) == OVERFLOW
 
 
-def test_library_is_gfx950_only():
+@pytest.mark.parametrize("path", [LIB, DEBUG_LIB], ids=["release", "debug"])
+def test_library_is_gfx950_only(path):
     """The code object inside the library targets gfx950 and nothing else."""
-    data = open(LIB, "rb").read()
+    data = open(path, "rb").read()
     assert b"gfx950" in data
     for other in (b"gfx942", b"gfx90a", b"gfx1100", b"sm_"):
         assert b"amdgcn-amd-amdhsa--" + other not in data
