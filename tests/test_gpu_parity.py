@@ -570,6 +570,11 @@ def _rounding_diagnostic(gpu_lib, d, layer, toks):
     flag = "FLAG > 5e-3" if rel_gpu > FLAG_REL else "ok"
     _say(f"  {cfg.name} rounding diagnostic over {len(toks)} tokens: gpu {rel_gpu:.3e}, "
          f"bf16 rounding points alone {rel_emul:.3e}; h {rel_h:.3e}, y {rel_y:.3e} [{flag}]")
+    # the GPU's fp32 sums add orders of magnitude less than the three bf16
+    # roundings, so its error must be that of the rounding points (measured equal
+    # to four digits at every size); 25% headroom for summation order
+    assert rel_gpu <= 1.25 * rel_emul + 2e-4, \
+        f"{cfg.name}: gpu error {rel_gpu:.3e} exceeds the bf16 rounding points' {rel_emul:.3e}"
     return rel_gpu, rel_emul
 
 
