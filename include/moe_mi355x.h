@@ -159,6 +159,24 @@ moe_status moe_permute(const moe_bf16 *x, const int32_t *topk_idx, int64_t T, in
                        size_t workspace_bytes, moe_stream_t stream);
 
 /*
+ * moe_permute without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the per-chunk histogram goes to a fixed device array inside
+ * the library (4 MiB per device that runs it, held until the process ends) instead
+ * of `workspace`. Arguments, outputs and errors otherwise as for moe_permute. It
+ * needs moe_permute_workspace_size(T, k, E) <= moe_permute_noalloc_max_workspace()
+ * bytes (about ceil(T*k/256) * E * 4), else MOE_ERR_WORKSPACE_TOO_SMALL and nothing
+ * is enqueued. Calls that overlap on one device (two streams or threads at once)
+ * share that array and race; serialise them. Nothing is allocated, freed or
+ * cleared: every call rewrites the whole histogram before reading it.
+ */
+moe_status moe_permute_noalloc(const moe_bf16 *x, const int32_t *topk_idx, int64_t T, int32_t H,
+                               int32_t E, int32_t k, int32_t align, int64_t P_max,
+                               int32_t *expert_counts, int32_t *expert_offsets, int32_t *route_row,
+                               int32_t *row_token, moe_bf16 *x_perm, moe_stream_t stream);
+size_t moe_permute_noalloc_max_workspace(void);
+
+/*
  * Grouped gate/up GEMM with SwiGLU [Halo, Levers that help: one grouped expert
  * matmul instead of a per-expert loop, fused GLU; prime-rl, Changes: gate and up
  * run as one GEMM ahead of a SwiGLU].  For every expert e and every row p of its

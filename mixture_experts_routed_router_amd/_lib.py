@@ -103,6 +103,11 @@ def _open(debug: bool):
     lib.moe_probe_mfma_bf16.argtypes = [_c_vp, _c_i64, _c_i32, ctypes.POINTER(ctypes.c_double), _c_vp]
     lib.moe_probe_mfma_sink_floats.argtypes = []
     lib.moe_probe_mfma_sink_floats.restype = _c_i64
+    lib.moe_permute_noalloc.argtypes = [_c_vp, _c_vp, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64,
+                                        _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp]
+    lib.moe_permute_noalloc.restype = ctypes.c_int
+    lib.moe_permute_noalloc_max_workspace.argtypes = []
+    lib.moe_permute_noalloc_max_workspace.restype = _c_sz
     lib.moe_debug_build.argtypes = []
     lib.moe_debug_build.restype = ctypes.c_int
     lib.moe_debug_status.argtypes = [_c_vp]
@@ -247,6 +252,30 @@ def permute(x: torch.Tensor, topk_idx: torch.Tensor, E: int, align: int = 32, P_
           _ptr(out.x_perm, torch.bfloat16, "x_perm", (P_max, H)) if gather else None,
           _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream))
     return out
+
+
+def permute_noalloc(x: torch.Tensor, topk_idx: torch.Tensor, E: int, align: int, out: Layout, stream=None,
+                    gather: bool = True) -> Layout:
+    """permute() without a workspace: the library's fixed device scratch holds the
+    per-chunk histogram (no allocation by the library or here; `out` is the
+    caller's). Calls that overlap on one device race on that scratch."""
+    T, H = x.shape
+    k = topk_idx.shape[1]
+    P_max = out.P_max
+    gather = gather and out.x_perm is not None
+    _call("moe_permute_noalloc", _ptr(x, torch.bfloat16, "x"), _ptr(topk_idx, torch.int32, "topk_idx", (T, k)),
+          T, H, E, k, align, P_max,
+          _ptr(out.counts, torch.int32, "counts", (E,)),
+          _ptr(out.offsets, torch.int32, "offsets", (E + 1,)),
+          _ptr(out.route_row, torch.int32, "route_row", (T * k,)),
+          _ptr(out.row_token, torch.int32, "row_token", (P_max,)),
+          _ptr(out.x_perm, torch.bfloat16, "x_perm", (P_max, H)) if gather else None, _stream(stream))
+    return out
+
+
+def permute_noalloc_max_workspace() -> int:
+    """Bytes of the fixed scratch moe_permute_noalloc has (its size limit)."""
+    return int(load().moe_permute_noalloc_max_workspace())
 
 
 def grouped_glu_gemm(x_perm, w_gate_up, counts, offsets, h=None, stream=None):

@@ -11,7 +11,9 @@ hipError_t launch_route_topk(const float*, int64_t, int, int, int32_t*, float*, 
 hipError_t launch_permute(const uint16_t*, const int32_t*, int64_t, int, int, int, int, int64_t,
                           int32_t*, int32_t*, int32_t*, int32_t*, uint16_t*, void*, hipStream_t);
 size_t permute_workspace_bytes(int64_t R, int E);
-
+size_t permute_scratch_bytes();
+hipError_t launch_permute_noalloc(const uint16_t*, const int32_t*, int64_t, int, int, int, int, int64_t, int32_t*,
+                                  int32_t*, int32_t*, int32_t*, uint16_t*, hipStream_t);
 hipError_t launch_grouped_glu_gemm(const uint16_t*, const void*, const float*, const int32_t*, int,
                                    int, int, uint16_t*, hipStream_t);
 hipError_t launch_grouped_glu_gemm_gather(const uint16_t*, const int32_t*, const void*, const float*,
@@ -251,6 +253,28 @@ moe_status moe_permute(const moe_bf16* x, const int32_t* topk_idx, int64_t T, in
                                           expert_offsets, route_row, row_token, x_perm, workspace,
                                           (hipStream_t)stream),
                       "moe_permute launch");
+}
+
+size_t moe_permute_noalloc_max_workspace(void) { return moe::permute_scratch_bytes(); }
+
+moe_status moe_permute_noalloc(const moe_bf16* x, const int32_t* topk_idx, int64_t T, int32_t H, int32_t E,
+                               int32_t k, int32_t align, int64_t P_max, int32_t* expert_counts,
+                               int32_t* expert_offsets, int32_t* route_row, int32_t* row_token,
+                               moe_bf16* x_perm, moe_stream_t stream) {
+    moe_status s = check_permute(x, topk_idx, T, H, E, k, align, P_max, expert_counts, expert_offsets, route_row,
+                                 row_token, x_perm);
+    if (s != MOE_OK) return s;
+    const size_t ws = moe::permute_workspace_bytes(T * k, E);
+    if (ws > moe::permute_scratch_bytes())
+        return fail(MOE_ERR_WORKSPACE_TOO_SMALL,
+                    "moe_permute_noalloc: T*k=%lld routes over E=%d experts need %zu bytes of scratch, more than "
+                    "the library's fixed %zu (use moe_permute with a workspace)",
+                    (long long)(T * k), E, ws, moe::permute_scratch_bytes());
+    DEBUG_CHECK(moe::debug_check_ids(topk_idx, T, k, E, (hipStream_t)stream));
+    return hip_status(moe::launch_permute_noalloc(x, topk_idx, T, H, E, k, align, P_max, expert_counts,
+                                                  expert_offsets, route_row, row_token, x_perm,
+                                                  (hipStream_t)stream),
+                      "moe_permute_noalloc launch");
 }
 
 static moe_status check_gemm(const void* a, const void* w, const int32_t* counts,

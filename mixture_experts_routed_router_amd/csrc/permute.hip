@@ -21,6 +21,8 @@
 //               r / k; offsets are published and pad rows get row_token = -1
 //   4. gather:  x_perm[p] = x[row_token[p]] (zero row if -1), written token-major:
 //               each token's row is read once and stored to its k rows
+#include <mutex>
+
 #include "common.hpp"
 
 namespace moe {
@@ -295,6 +297,47 @@ hipError_t launch_permute(const uint16_t* x, const int32_t* topk_idx, int64_t T,
                            (const uint4*)x, (const int32_t*)route_row, (const int32_t*)counts,
                            (const int32_t*)offsets, T, k, ppr, token_blocks, (uint4*)x_perm);
     return hipGetLastError();
+}
+
+// ---- the allocation-free permute ------------------------------------------------------
+//
+// For callers that cannot allocate (code under graph capture, serving loops): the
+// per-chunk histogram lives in a file-scope device array instead of a caller
+// workspace. Each device that runs this holds its own copy, for the life of the
+// process. Host code never uses the array's name as an address: its device
+// address is looked up once per device (with that device current) and kept.
+// The histogram is fully rewritten by every call before it is read, so nothing
+// needs clearing; calls that overlap on one device share the array and race.
+constexpr size_t kScratchBytes = 4u << 20;  // 4 MiB: nchunks * E int32 counters
+static __device__ __align__(256) int32_t scratch[kScratchBytes / sizeof(int32_t)];
+
+constexpr int kMaxDevices = 64;
+static void* g_scratch_ptr[kMaxDevices];
+static std::mutex g_scratch_mu;
+
+size_t permute_scratch_bytes() { return kScratchBytes; }
+
+hipError_t launch_permute_noalloc(const uint16_t* x, const int32_t* topk_idx, int64_t T, int H, int E, int k,
+                                  int align, int64_t P_max, int32_t* counts, int32_t* offsets,
+                                  int32_t* route_row, int32_t* row_token, uint16_t* x_perm, hipStream_t stream) {
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return err;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    void* ptr = nullptr;
+    {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        if (!g_scratch_ptr[dev]) {
+            err = hipGetSymbolAddress(&g_scratch_ptr[dev], HIP_SYMBOL(scratch));
+            if (err != hipSuccess) {
+                g_scratch_ptr[dev] = nullptr;
+                return err;
+            }
+        }
+        ptr = g_scratch_ptr[dev];
+    }
+    return launch_permute(x, topk_idx, T, H, E, k, align, P_max, counts, offsets, route_row, row_token, x_perm,
+                          ptr, stream);
 }
 
 }  // namespace moe
