@@ -159,6 +159,27 @@ moe_status moe_permute(const moe_bf16 *x, const int32_t *topk_idx, int64_t T, in
                        size_t workspace_bytes, moe_stream_t stream);
 
 /*
+ * Routing and the permute's counting in one kernel [prime-rl, Changes: a
+ * single-pass local layout; PocketLLM, Remaining prefill attribution: the router
+ * is a phase of its own]. moe_route_topk_hist computes exactly what
+ * moe_route_topk computes and, in the same kernel, the number of routes to each
+ * expert among each workgroup's tokens, into `workspace` (an opaque histogram of
+ * moe_route_hist_workspace_size(T, k, E) bytes). moe_permute_from_hist then
+ * builds the same layout and x_perm as moe_permute (bit for bit; arguments as
+ * there) from that histogram instead of counting topk_idx again. Pass both calls
+ * the same T, E, k, topk_idx and workspace, in stream order; the workspace is
+ * overwritten by moe_permute_from_hist.
+ */
+moe_status moe_route_hist_workspace_size(int64_t T, int32_t k, int32_t E, size_t *bytes);
+moe_status moe_route_topk_hist(const float *logits, int64_t T, int32_t E, int32_t k, int32_t *topk_idx,
+                               float *topk_w, void *workspace, size_t workspace_bytes, moe_stream_t stream);
+moe_status moe_permute_from_hist(const moe_bf16 *x, const int32_t *topk_idx, int64_t T, int32_t H,
+                                 int32_t E, int32_t k, int32_t align, int64_t P_max,
+                                 int32_t *expert_counts, int32_t *expert_offsets, int32_t *route_row,
+                                 int32_t *row_token, moe_bf16 *x_perm, void *workspace,
+                                 size_t workspace_bytes, moe_stream_t stream);
+
+/*
  * moe_permute without a workspace, for callers that cannot allocate device
  * memory (code under HIP graph capture, tight serving loops, harnesses that
  * forbid hipMalloc): the per-chunk histogram goes to a fixed device array inside

@@ -103,6 +103,13 @@ def _open(debug: bool):
     lib.moe_probe_mfma_bf16.argtypes = [_c_vp, _c_i64, _c_i32, ctypes.POINTER(ctypes.c_double), _c_vp]
     lib.moe_probe_mfma_sink_floats.argtypes = []
     lib.moe_probe_mfma_sink_floats.restype = _c_i64
+    lib.moe_route_hist_workspace_size.argtypes = [_c_i64, _c_i32, _c_i32, ctypes.POINTER(_c_sz)]
+    lib.moe_route_hist_workspace_size.restype = ctypes.c_int
+    lib.moe_route_topk_hist.argtypes = [_c_vp, _c_i64, _c_i32, _c_i32, _c_vp, _c_vp, _c_vp, _c_sz, _c_vp]
+    lib.moe_route_topk_hist.restype = ctypes.c_int
+    lib.moe_permute_from_hist.argtypes = [_c_vp, _c_vp, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64,
+                                          _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_sz, _c_vp]
+    lib.moe_permute_from_hist.restype = ctypes.c_int
     lib.moe_permute_noalloc.argtypes = [_c_vp, _c_vp, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64,
                                         _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp]
     lib.moe_permute_noalloc.restype = ctypes.c_int
@@ -244,6 +251,49 @@ def permute(x: torch.Tensor, topk_idx: torch.Tensor, E: int, align: int = 32, P_
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=x.device)
     _call("moe_permute", _ptr(x, torch.bfloat16, "x"), _ptr(topk_idx, torch.int32, "topk_idx", (T, k)),
+          T, H, E, k, align, P_max,
+          _ptr(out.counts, torch.int32, "counts", (E,)),
+          _ptr(out.offsets, torch.int32, "offsets", (E + 1,)),
+          _ptr(out.route_row, torch.int32, "route_row", (T * k,)),
+          _ptr(out.row_token, torch.int32, "row_token", (P_max,)),
+          _ptr(out.x_perm, torch.bfloat16, "x_perm", (P_max, H)) if gather else None,
+          _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream))
+    return out
+
+
+def route_hist_workspace_size(T: int, k: int, E: int) -> int:
+    n = _c_sz(0)
+    _call("moe_route_hist_workspace_size", T, k, E, ctypes.byref(n))
+    return int(n.value)
+
+
+def route_topk_hist(logits: torch.Tensor, k: int, workspace: torch.Tensor, topk_idx=None, topk_w=None,
+                    stream=None):
+    """route_topk, plus the permute's per-workgroup expert counts written into
+    `workspace` (uint8, route_hist_workspace_size bytes) for permute_from_hist."""
+    T, E = logits.shape
+    dev = logits.device
+    if topk_idx is None:
+        topk_idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    if topk_w is None:
+        topk_w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    _call("moe_route_topk_hist", _ptr(logits, torch.float32, "logits"), T, E, k,
+          _ptr(topk_idx, torch.int32, "topk_idx", (T, k)), _ptr(topk_w, torch.float32, "topk_w", (T, k)),
+          _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream))
+    return topk_idx, topk_w
+
+
+def permute_from_hist(x: torch.Tensor, topk_idx: torch.Tensor, E: int, align: int, workspace: torch.Tensor,
+                      P_max=None, out: Layout | None = None, stream=None, gather: bool = True) -> Layout:
+    """permute() starting from the histogram route_topk_hist wrote into `workspace`."""
+    T, H = x.shape
+    k = topk_idx.shape[1]
+    if P_max is None:
+        P_max = padded_rows_max(T, k, E, align)
+    if out is None:
+        out = alloc_layout(T, H, E, k, P_max, x.device, gather=gather)
+    gather = gather and out.x_perm is not None
+    _call("moe_permute_from_hist", _ptr(x, torch.bfloat16, "x"), _ptr(topk_idx, torch.int32, "topk_idx", (T, k)),
           T, H, E, k, align, P_max,
           _ptr(out.counts, torch.int32, "counts", (E,)),
           _ptr(out.offsets, torch.int32, "offsets", (E + 1,)),

@@ -8,6 +8,10 @@
 
 namespace moe {
 hipError_t launch_route_topk(const float*, int64_t, int, int, int32_t*, float*, hipStream_t);
+hipError_t launch_route_topk_hist(const float*, int64_t, int, int, int32_t*, float*, int32_t*, hipStream_t);
+size_t route_hist_workspace_bytes(int64_t T, int E);
+hipError_t launch_permute_from_hist(const uint16_t*, const int32_t*, int64_t, int, int, int, int, int64_t, int32_t*,
+                                   int32_t*, int32_t*, int32_t*, uint16_t*, void*, hipStream_t);
 hipError_t launch_permute(const uint16_t*, const int32_t*, int64_t, int, int, int, int, int64_t,
                           int32_t*, int32_t*, int32_t*, int32_t*, uint16_t*, void*, hipStream_t);
 size_t permute_workspace_bytes(int64_t R, int E);
@@ -15,21 +19,21 @@ size_t permute_scratch_bytes();
 hipError_t launch_permute_noalloc(const uint16_t*, const int32_t*, int64_t, int, int, int, int, int64_t, int32_t*,
                                   int32_t*, int32_t*, int32_t*, uint16_t*, hipStream_t);
 hipError_t launch_grouped_glu_gemm(const uint16_t*, const void*, const float*, const int32_t*, int,
-                                   int, int, uint16_t*, hipStream_t);
+                                   int, int, uint16_t*, int, hipStream_t);
 hipError_t launch_grouped_glu_gemm_gather(const uint16_t*, const int32_t*, const void*, const float*,
-                                          const int32_t*, int, int, int, uint16_t*, hipStream_t);
+                                          const int32_t*, int, int, int, uint16_t*, int, hipStream_t);
 hipError_t launch_grouped_down_gemm(const uint16_t*, const void*, const float*, const int32_t*, int,
-                                    int, int, uint16_t*, hipStream_t);
+                                    int, int, uint16_t*, int, hipStream_t);
 hipError_t launch_quantize_fp8(const uint16_t*, int64_t, int, int, uint8_t*, float*, hipStream_t);
 hipError_t launch_grouped_gemm_small(bool, const uint16_t*, const int32_t*, const void*, const float*,
-                                     const int32_t*, int, int, int, uint16_t*, hipStream_t);
+                                     const int32_t*, int, int, int, uint16_t*, int, hipStream_t);
 hipError_t launch_combine_bwd(const uint16_t*, const uint16_t*, const int32_t*, const float*, const int32_t*,
                               const int32_t*, int64_t, int, int, int, int64_t, uint16_t*, float*, hipStream_t);
 hipError_t launch_route_bwd(const int32_t*, const float*, const float*, int64_t, int, int, float*, hipStream_t);
 hipError_t launch_grouped_glu_gemm_clamped(const uint16_t*, const uint16_t*, const int32_t*, int, int, int, float,
-                                           uint16_t*, hipStream_t);
+                                           uint16_t*, int, hipStream_t);
 hipError_t launch_grouped_gemm_swiglu_bwd(const uint16_t*, const uint16_t*, const uint16_t*, const int32_t*, int,
-                                          int, int, uint16_t*, hipStream_t);
+                                          int, int, uint16_t*, int, hipStream_t);
 hipError_t launch_swiglu(const uint16_t*, const uint16_t*, const int32_t*, int, int, int64_t, uint16_t*,
                          hipStream_t);
 hipError_t launch_transpose(const uint16_t*, int64_t, int, int, uint16_t*, hipStream_t);
@@ -134,17 +138,17 @@ hipError_t launch_glu(const uint16_t* a, const int32_t* row_token, const void* w
                       const int32_t* offsets, int32_t E, int32_t H, int32_t I, int64_t P_max, uint16_t* h,
                       hipStream_t stream) {
     if (use_small_m(P_max, E, scale))
-        return moe::launch_grouped_gemm_small(true, a, row_token, w, scale, offsets, E, H, I, h, stream);
+        return moe::launch_grouped_gemm_small(true, a, row_token, w, scale, offsets, E, H, I, h, (int)P_max, stream);
     if (row_token)
-        return moe::launch_grouped_glu_gemm_gather(a, row_token, w, scale, offsets, E, H, I, h, stream);
-    return moe::launch_grouped_glu_gemm(a, w, scale, offsets, E, H, I, h, stream);
+        return moe::launch_grouped_glu_gemm_gather(a, row_token, w, scale, offsets, E, H, I, h, (int)P_max, stream);
+    return moe::launch_grouped_glu_gemm(a, w, scale, offsets, E, H, I, h, (int)P_max, stream);
 }
 
 hipError_t launch_down(const uint16_t* h, const void* w, const float* scale, const int32_t* offsets,
                        int32_t E, int32_t H, int32_t I, int64_t P_max, uint16_t* y, hipStream_t stream) {
     if (use_small_m(P_max, E, scale))
-        return moe::launch_grouped_gemm_small(false, h, nullptr, w, scale, offsets, E, I, H, y, stream);
-    return moe::launch_grouped_down_gemm(h, w, scale, offsets, E, H, I, y, stream);
+        return moe::launch_grouped_gemm_small(false, h, nullptr, w, scale, offsets, E, I, H, y, (int)P_max, stream);
+    return moe::launch_grouped_down_gemm(h, w, scale, offsets, E, H, I, y, (int)P_max, stream);
 }
 
 // compute units of the current device (256 on an MI355X)
@@ -255,6 +259,52 @@ moe_status moe_permute(const moe_bf16* x, const int32_t* topk_idx, int64_t T, in
                       "moe_permute launch");
 }
 
+moe_status moe_route_hist_workspace_size(int64_t T, int32_t k, int32_t E, size_t* bytes) {
+    if (!bytes) return fail(MOE_ERR_NULL_POINTER, "bytes is NULL");
+    if (T < 0 || T >= ((int64_t)1 << 31)) return fail(MOE_ERR_INVALID_SHAPE, "T=%lld outside [0, 2^31)", (long long)T);
+    moe_status s = check_ek(E, k);
+    if (s != MOE_OK) return s;
+    *bytes = moe::route_hist_workspace_bytes(T, E);
+    return ok();
+}
+
+moe_status moe_route_topk_hist(const float* logits, int64_t T, int32_t E, int32_t k, int32_t* topk_idx,
+                               float* topk_w, void* workspace, size_t workspace_bytes, moe_stream_t stream) {
+    REQUIRE_PTR_UNLESS_EMPTY(logits, T == 0);
+    REQUIRE_PTR_UNLESS_EMPTY(topk_idx, T == 0);
+    REQUIRE_PTR_UNLESS_EMPTY(topk_w, T == 0);
+    REQUIRE_PTR_UNLESS_EMPTY(workspace, T == 0);
+    if (T < 0 || T >= ((int64_t)1 << 31)) return fail(MOE_ERR_INVALID_SHAPE, "T=%lld outside [0, 2^31)", (long long)T);
+    moe_status s = check_ek(E, k);
+    if (s != MOE_OK) return s;
+    const size_t ws = moe::route_hist_workspace_bytes(T, E);
+    if (T > 0 && workspace_bytes < ws)
+        return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", workspace_bytes, ws);
+    DEBUG_CHECK(moe::debug_check_logits(logits, T * (int64_t)E, (hipStream_t)stream));
+    return hip_status(moe::launch_route_topk_hist(logits, T, E, k, topk_idx, topk_w, (int32_t*)workspace,
+                                                  (hipStream_t)stream),
+                      "moe_route_topk_hist launch");
+}
+
+moe_status moe_permute_from_hist(const moe_bf16* x, const int32_t* topk_idx, int64_t T, int32_t H, int32_t E,
+                                 int32_t k, int32_t align, int64_t P_max, int32_t* expert_counts,
+                                 int32_t* expert_offsets, int32_t* route_row, int32_t* row_token,
+                                 moe_bf16* x_perm, void* workspace, size_t workspace_bytes, moe_stream_t stream) {
+    moe_status s = check_permute(x, topk_idx, T, H, E, k, align, P_max, expert_counts, expert_offsets, route_row,
+                                 row_token, x_perm);
+    if (s != MOE_OK) return s;
+    if (T >= ((int64_t)1 << 31)) return fail(MOE_ERR_INVALID_SHAPE, "T=%lld outside [0, 2^31)", (long long)T);
+    REQUIRE_PTR_UNLESS_EMPTY(workspace, T == 0);
+    const size_t ws = moe::route_hist_workspace_bytes(T, E);
+    if (T > 0 && workspace_bytes < ws)
+        return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", workspace_bytes, ws);
+    DEBUG_CHECK(moe::debug_check_ids(topk_idx, T, k, E, (hipStream_t)stream));
+    return hip_status(moe::launch_permute_from_hist(x, topk_idx, T, H, E, k, align, P_max, expert_counts,
+                                                    expert_offsets, route_row, row_token, x_perm, workspace,
+                                                    (hipStream_t)stream),
+                      "moe_permute_from_hist launch");
+}
+
 size_t moe_permute_noalloc_max_workspace(void) { return moe::permute_scratch_bytes(); }
 
 moe_status moe_permute_noalloc(const moe_bf16* x, const int32_t* topk_idx, int64_t T, int32_t H, int32_t E,
@@ -325,7 +375,7 @@ moe_status moe_grouped_glu_gemm_clamped(const moe_bf16* x_perm, const moe_bf16* 
     if (!(limit >= 0.0f)) return fail(MOE_ERR_INVALID_VALUE, "limit=%g must be >= 0", (double)limit);
     DEBUG_CHECK(moe::debug_check_layout(expert_counts, expert_offsets, E, P_max, (hipStream_t)stream));
     return hip_status(moe::launch_grouped_glu_gemm_clamped(x_perm, w_gate_up, expert_offsets, E, H, I, limit, h,
-                                                           (hipStream_t)stream),
+                                                           (int)P_max, (hipStream_t)stream),
                       "moe_grouped_glu_gemm_clamped launch");
 }
 
@@ -462,7 +512,7 @@ moe_status moe_grouped_gemm_swiglu_backward(const moe_bf16* dy, const moe_bf16* 
     REQUIRE_PTR(gu);
     DEBUG_CHECK(moe::debug_check_layout(expert_counts, expert_offsets, E, P_max, (hipStream_t)stream));
     return hip_status(moe::launch_grouped_gemm_swiglu_bwd(dy, w_down_t, gu, expert_offsets, E, H, I, dgu,
-                                                          (hipStream_t)stream),
+                                                          (int)P_max, (hipStream_t)stream),
                       "moe_grouped_gemm_swiglu_backward launch");
 }
 

@@ -755,7 +755,8 @@ template <bool GLU, bool GATHER, bool W8, bool SWB>
 __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ row_token,
     const void* __restrict__ W, const float* __restrict__ w_scale, const int32_t* __restrict__ offsets,
-    int E, int K, int N, uint16_t* __restrict__ C, const uint16_t* __restrict__ gu, float glu_limit) {
+    int E, int K, int N, uint16_t* __restrict__ C, const uint16_t* __restrict__ gu, float glu_limit,
+    int rows_max) {
     MOE_DEBUG_GUARD();
     static_assert(!SWB || (!GLU && !GATHER && !W8), "the SwiGLU backward epilogue follows the plain bf16 GEMM");
     __shared__ __attribute__((aligned(1024))) uint16_t lds[kLdsElems];
@@ -771,13 +772,17 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_kernel(
     const int64_t w_stride = (int64_t)NW * K * (W8 ? 1 : 2);  // bytes per expert
 
     // ---- per-expert tile counts -> prefix (every workgroup builds its own copy)
+    // Segments are clamped to [0, rows_max) (rows_max = P_max, the rows of A and
+    // C), and an expert whose end lies before its start gets none: offsets that
+    // break their contract cannot make a tile read or write outside the buffers.
+    auto seg_bound = [&](int e) { return min(max(offsets[e], 0), rows_max); };
     {
         const int per = (E + kGemmThreads - 1) / kGemmThreads;  // <= 2
         int local = 0;
         for (int i = 0; i < per; ++i) {
             const int e = tid * per + i;
             if (e < E) {
-                const int32_t o0 = offsets[e], o1 = offsets[e + 1];
+                const int32_t o0 = seg_bound(e), o1 = max(seg_bound(e + 1), o0);
                 seg_start[e] = o0;
                 local += (o1 - o0 + BM - 1) / BM * NT;
             }
@@ -787,10 +792,11 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_kernel(
             const int e = tid * per + i;
             if (e < E) {
                 tile_start[e] = run;
-                run += (offsets[e + 1] - offsets[e] + BM - 1) / BM * NT;
+                const int32_t o0 = seg_bound(e), o1 = max(seg_bound(e + 1), o0);
+                run += (o1 - o0 + BM - 1) / BM * NT;
             }
         }
-        if (tid == 0) seg_start[E] = offsets[E];
+        if (tid == 0) seg_start[E] = seg_bound(E);
         if (tid == kGemmThreads - 1) tile_start[E] = run;
         __syncthreads();
     }
@@ -842,7 +848,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_kernel(
         // every value below is uniform over the wave: keep it in scalar registers
         const int e = __builtin_amdgcn_readfirstlane(lo);
         const int seg0 = __builtin_amdgcn_readfirstlane(seg_start[e]);
-        const int seg1 = __builtin_amdgcn_readfirstlane(seg_start[e + 1]);
+        const int seg1 = max(__builtin_amdgcn_readfirstlane(seg_start[e + 1]), seg0);
         const int q = t - __builtin_amdgcn_readfirstlane(tile_start[e]);
         // The segment's 32-row blocks are spread evenly over its ceil(rows / 256)
         // row tiles (17 blocks -> 6, 6, 5 rather than 8, 8, 1): the same MFMA
@@ -920,42 +926,44 @@ static unsigned persistent_grid() {
 
 // scale == NULL: bf16 weights; otherwise FP8 (E4M3) weights with one scale per 64 W rows.
 hipError_t launch_grouped_glu_gemm(const uint16_t* x_perm, const void* w_gu, const float* scale,
-                                   const int32_t* offsets, int E, int H, int I, uint16_t* h,
+                                   const int32_t* offsets, int E, int H, int I, uint16_t* h, int rows_max,
                                    hipStream_t stream) {
     if (scale)
         hipLaunchKernelGGL((grouped_gemm_kernel<true, false, true, false>), dim3(persistent_grid()),
                            dim3(kGemmThreads), 0, stream, x_perm, (const int32_t*)nullptr, w_gu, scale,
-                           offsets, E, H, I, h, (const uint16_t*)nullptr, INFINITY);
+                           offsets, E, H, I, h, (const uint16_t*)nullptr, INFINITY, rows_max);
     else
         hipLaunchKernelGGL((grouped_gemm_kernel<true, false, false, false>), dim3(persistent_grid()),
                            dim3(kGemmThreads), 0, stream, x_perm, (const int32_t*)nullptr, w_gu, scale,
-                           offsets, E, H, I, h, (const uint16_t*)nullptr, INFINITY);
+                           offsets, E, H, I, h, (const uint16_t*)nullptr, INFINITY, rows_max);
     return hipGetLastError();
 }
 
 hipError_t launch_grouped_glu_gemm_gather(const uint16_t* x, const int32_t* row_token, const void* w_gu,
                                           const float* scale, const int32_t* offsets, int E, int H,
-                                          int I, uint16_t* h, hipStream_t stream) {
+                                          int I, uint16_t* h, int rows_max, hipStream_t stream) {
     if (scale)
         hipLaunchKernelGGL((grouped_gemm_kernel<true, true, true, false>), dim3(persistent_grid()),
-                           dim3(kGemmThreads), 0, stream, x, row_token, w_gu, scale, offsets, E, H, I, h, (const uint16_t*)nullptr, INFINITY);
+                           dim3(kGemmThreads), 0, stream, x, row_token, w_gu, scale, offsets, E, H, I, h,
+                           (const uint16_t*)nullptr, INFINITY, rows_max);
     else
         hipLaunchKernelGGL((grouped_gemm_kernel<true, true, false, false>), dim3(persistent_grid()),
-                           dim3(kGemmThreads), 0, stream, x, row_token, w_gu, scale, offsets, E, H, I, h, (const uint16_t*)nullptr, INFINITY);
+                           dim3(kGemmThreads), 0, stream, x, row_token, w_gu, scale, offsets, E, H, I, h,
+                           (const uint16_t*)nullptr, INFINITY, rows_max);
     return hipGetLastError();
 }
 
 hipError_t launch_grouped_down_gemm(const uint16_t* h, const void* w_d, const float* scale,
-                                    const int32_t* offsets, int E, int H, int I, uint16_t* y,
+                                    const int32_t* offsets, int E, int H, int I, uint16_t* y, int rows_max,
                                     hipStream_t stream) {
     if (scale)
         hipLaunchKernelGGL((grouped_gemm_kernel<false, false, true, false>), dim3(persistent_grid()),
                            dim3(kGemmThreads), 0, stream, h, (const int32_t*)nullptr, w_d, scale,
-                           offsets, E, I, H, y, (const uint16_t*)nullptr, INFINITY);
+                           offsets, E, I, H, y, (const uint16_t*)nullptr, INFINITY, rows_max);
     else
         hipLaunchKernelGGL((grouped_gemm_kernel<false, false, false, false>), dim3(persistent_grid()),
                            dim3(kGemmThreads), 0, stream, h, (const int32_t*)nullptr, w_d, scale,
-                           offsets, E, I, H, y, (const uint16_t*)nullptr, INFINITY);
+                           offsets, E, I, H, y, (const uint16_t*)nullptr, INFINITY, rows_max);
     return hipGetLastError();
 }
 
@@ -963,20 +971,21 @@ hipError_t launch_grouped_down_gemm(const uint16_t* h, const void* w_d, const fl
 // GEMM over W_d_t [E, I, H] (K = H, N = I) whose epilogue reads gu [P_max, 2I].
 hipError_t launch_grouped_gemm_swiglu_bwd(const uint16_t* dy, const uint16_t* w_d_t, const uint16_t* gu,
                                           const int32_t* offsets, int E, int H, int I, uint16_t* dgu,
-                                          hipStream_t stream) {
+                                          int rows_max, hipStream_t stream) {
     hipLaunchKernelGGL((grouped_gemm_kernel<false, false, false, true>), dim3(persistent_grid()),
                        dim3(kGemmThreads), 0, stream, dy, (const int32_t*)nullptr, (const void*)w_d_t,
-                       (const float*)nullptr, offsets, E, H, I, dgu, gu, INFINITY);
+                       (const float*)nullptr, offsets, E, H, I, dgu, gu, INFINITY, rows_max);
     return hipGetLastError();
 }
 
 // The gate/up GEMM with a clamped SwiGLU in its epilogue: h = silu(min(g, limit)) *
 // clip(u, -limit, limit), bf16 x_perm and weights.
 hipError_t launch_grouped_glu_gemm_clamped(const uint16_t* x_perm, const uint16_t* w_gu, const int32_t* offsets,
-                                           int E, int H, int I, float limit, uint16_t* h, hipStream_t stream) {
+                                           int E, int H, int I, float limit, uint16_t* h, int rows_max,
+                                           hipStream_t stream) {
     hipLaunchKernelGGL((grouped_gemm_kernel<true, false, false, false>), dim3(persistent_grid()),
                        dim3(kGemmThreads), 0, stream, x_perm, (const int32_t*)nullptr, (const void*)w_gu,
-                       (const float*)nullptr, offsets, E, H, I, h, (const uint16_t*)nullptr, limit);
+                       (const float*)nullptr, offsets, E, H, I, h, (const uint16_t*)nullptr, limit, rows_max);
     return hipGetLastError();
 }
 

@@ -182,7 +182,7 @@ template <bool GLU, bool GATHER, bool W8>
 __global__ __launch_bounds__(kSmallThreads) void grouped_gemm_small_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ row_token, const void* __restrict__ W,
     const float* __restrict__ w_scale, const int32_t* __restrict__ offsets, int E, int K, int N,
-    uint16_t* __restrict__ C) {
+    uint16_t* __restrict__ C, int rows_max) {
     MOE_DEBUG_GUARD();
     const int lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -193,7 +193,9 @@ __global__ __launch_bounds__(kSmallThreads) void grouped_gemm_small_kernel(
     const int e = unit / units;
     if (e >= E) return;
     const int u = unit - e * units;
-    const int seg0 = offsets[e], seg1 = offsets[e + 1];
+    // clamped to [0, rows_max) (rows_max = P_max): offsets that break their
+    // contract cannot make the kernel read or write outside A or C
+    const int seg0 = min(max(offsets[e], 0), rows_max), seg1 = min(max(offsets[e + 1], 0), rows_max);
     if (seg1 <= seg0) return;  // no rows: none of this expert's weights are read
 
     const int NW = GLU ? 2 * N : N;
@@ -222,22 +224,23 @@ __global__ __launch_bounds__(kSmallThreads) void grouped_gemm_small_kernel(
 // glu: C = h [rows, N = I] from W [E, 2I, K = H]; down: C = y [rows, N = H] from W [E, H, K = I].
 hipError_t launch_grouped_gemm_small(bool glu, const uint16_t* A, const int32_t* row_token, const void* W,
                                      const float* scale, const int32_t* offsets, int E, int K, int N,
-                                     uint16_t* C, hipStream_t stream) {
+                                     uint16_t* C, int rows_max, hipStream_t stream) {
     const int64_t units = (int64_t)E * (N / (glu ? 8 * kSmallBlocksGlu : 16 * kSmallBlocksDown));
     const int waves = kSmallThreads / kWave;
     const dim3 grid((unsigned)((units + waves - 1) / waves)), block(kSmallThreads);
 #define MOE_SMALL_LAUNCH(G, GA, W8)                                                                 \
     hipLaunchKernelGGL((grouped_gemm_small_kernel<G, GA, W8>), grid, block, 0, stream, A, row_token, W, \
-                       scale, offsets, E, K, N, C)
-    const bool gather = row_token != nullptr, w8 = scale != nullptr;
+                       scale, offsets, E, K, N, C, rows_max)
+    // FP8 weights only: with bf16 weights the 256-row tiles of the tiled kernel
+    // stream the weights faster at few rows per expert (32-expert small-M layer:
+    // gate/up 222 against 260 us, down 131 against 155 us on one box), so no bf16
+    // instantiation is built
+    if (scale == nullptr) return hipErrorInvalidValue;
+    const bool gather = row_token != nullptr;
     if (glu) {
-        if (gather) {
-            if (w8) MOE_SMALL_LAUNCH(true, true, true); else MOE_SMALL_LAUNCH(true, true, false);
-        } else {
-            if (w8) MOE_SMALL_LAUNCH(true, false, true); else MOE_SMALL_LAUNCH(true, false, false);
-        }
+        if (gather) MOE_SMALL_LAUNCH(true, true, true); else MOE_SMALL_LAUNCH(true, false, true);
     } else {
-        if (w8) MOE_SMALL_LAUNCH(false, false, true); else MOE_SMALL_LAUNCH(false, false, false);
+        MOE_SMALL_LAUNCH(false, false, true);
     }
 #undef MOE_SMALL_LAUNCH
     return hipGetLastError();

@@ -111,12 +111,16 @@ __global__ __launch_bounds__(kScanThreads) void permute_scan_kernel(int32_t* __r
 // publishes them, and each workgroup writes row_token = -1 on its share of the
 // pad rows (those of experts b, b + gridDim.x, ..., and every row from
 // offsets[E] to P_max). Then one wavefront per chunk as before.
+// A chunk is `chunk_routes` consecutive routes (kChunk here; the routing
+// kernel's workgroup of tokens when the histogram comes from it), STEPS * 64 at most.
 constexpr int kScatterThreads = 256;
 
+template <int STEPS>
 __global__ __launch_bounds__(kScatterThreads) void permute_scatter_kernel(
     const int32_t* __restrict__ topk_idx, int64_t R, int E, int k, int align, int64_t nchunks,
     int64_t P_max, const int32_t* __restrict__ base, const int32_t* __restrict__ counts,
-    int32_t* __restrict__ offsets, int32_t* __restrict__ route_row, int32_t* __restrict__ row_token) {
+    int32_t* __restrict__ offsets, int32_t* __restrict__ route_row, int32_t* __restrict__ row_token,
+    int chunk_routes) {
     MOE_DEBUG_GUARD();
     extern __shared__ int32_t lds_cursor[];  // [4][E] cursors, [E+1] offsets, [4] wave totals
     int32_t* off = lds_cursor + 4 * E;
@@ -163,27 +167,31 @@ __global__ __launch_bounds__(kScatterThreads) void permute_scatter_kernel(
     for (int e = lane; e < E; e += kWave) cur[e] = base[c * E + e] + off[e];
     const int nbits = key_bits(E);
     const uint64_t lt = lanemask_lt();
-    const int64_t r0 = c * kChunk;
-    uint32_t ids[kSteps];
+    const int64_t r0 = c * chunk_routes;
+    const int64_t r_end = r0 + chunk_routes < R ? r0 + chunk_routes : R;
+    const int steps = (chunk_routes + kWave - 1) / kWave;
+    uint32_t ids[STEPS];
 #pragma unroll
-    for (int s = 0; s < kSteps; ++s) {
+    for (int s = 0; s < STEPS; ++s) {
         const int64_t r = r0 + s * kWave + lane;
-        ids[s] = r < R ? (uint32_t)topk_idx[r] : 0xffffffffu;
+        ids[s] = s < steps && r < r_end ? (uint32_t)topk_idx[r] : 0xffffffffu;
     }
 #pragma unroll
-    for (int s = 0; s < kSteps; ++s) {
-        const int64_t r = r0 + s * kWave + lane;
-        const bool active = ids[s] < (uint32_t)E;
-        const uint32_t key = active ? ids[s] : 0u;
-        const uint64_t peers = match_peers(key, nbits, active);
-        if (active) {
-            const int32_t dest = cur[key] + __popcll(peers & lt);
-            route_row[r] = dest;
-            row_token[dest] = (int32_t)(r / k);
-        } else if (r < R) {
-            route_row[r] = -1;  // an out-of-range id gets no row
+    for (int s = 0; s < STEPS; ++s) {
+        if (s < steps) {  // wave-uniform
+            const int64_t r = r0 + s * kWave + lane;
+            const bool active = ids[s] < (uint32_t)E;
+            const uint32_t key = active ? ids[s] : 0u;
+            const uint64_t peers = match_peers(key, nbits, active);
+            if (active) {
+                const int32_t dest = cur[key] + __popcll(peers & lt);
+                route_row[r] = dest;
+                row_token[dest] = (int32_t)(r / k);
+            } else if (r < r_end) {
+                route_row[r] = -1;  // an out-of-range id gets no row
+            }
+            if (active && (__ffsll((unsigned long long)peers) - 1) == lane) cur[key] += __popcll(peers);
         }
-        if (active && (__ffsll((unsigned long long)peers) - 1) == lane) cur[key] += __popcll(peers);
     }
 }
 
@@ -252,6 +260,10 @@ __global__ __launch_bounds__(kCopyThreads) void permute_copy_rows_kernel(
 
 int64_t permute_chunks(int64_t R) { return (R + kChunk - 1) / kChunk; }
 
+hipError_t launch_permute_copy(const uint16_t* x, int64_t T, int H, int E, int k, int64_t P_max,
+                               const int32_t* counts, const int32_t* offsets, const int32_t* route_row,
+                               uint16_t* x_perm, hipStream_t stream);
+
 size_t permute_workspace_bytes(int64_t R, int E) {
     const size_t b = (size_t)permute_chunks(R) * (size_t)E * sizeof(int32_t);
     return (b + 255) / 256 * 256;
@@ -278,11 +290,50 @@ hipError_t launch_permute(const uint16_t* x, const int32_t* topk_idx, int64_t T,
     // at least one workgroup: it also publishes the offsets and the pad rows
     const int64_t scatter_blocks = nchunks > 0 ? (nchunks + 3) / 4 : 1;
     const size_t scatter_lds = (4 * (size_t)E + E + 1 + 4) * sizeof(int32_t);
-    hipLaunchKernelGGL(permute_scatter_kernel, dim3((unsigned)scatter_blocks), dim3(kScatterThreads), scatter_lds,
-                       stream, topk_idx, R, E, k, align, nchunks, P_max, (const int32_t*)hist,
-                       (const int32_t*)counts, offsets, route_row, row_token);
+    hipLaunchKernelGGL(permute_scatter_kernel<kSteps>, dim3((unsigned)scatter_blocks), dim3(kScatterThreads),
+                       scatter_lds, stream, topk_idx, R, E, k, align, nchunks, P_max, (const int32_t*)hist,
+                       (const int32_t*)counts, offsets, route_row, row_token, kChunk);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
+    return launch_permute_copy(x, T, H, E, k, P_max, counts, offsets, route_row, x_perm, stream);
+}
+
+// The permute from a histogram the routing kernel already wrote (hist [nchunks][E],
+// chunk c = tokens [c * tpw, (c + 1) * tpw)): scan, scatter, gather -- no counting pass.
+int route_hist_tokens_per_chunk(int64_t T, int E);
+
+size_t route_hist_workspace_bytes(int64_t T, int E) {
+    const int64_t tpw = route_hist_tokens_per_chunk(T, E);
+    const size_t b = (size_t)((T + tpw - 1) / tpw) * (size_t)E * sizeof(int32_t);
+    return (b + 255) / 256 * 256;
+}
+
+hipError_t launch_permute_from_hist(const uint16_t* x, const int32_t* topk_idx, int64_t T, int H, int E, int k,
+                                   int align, int64_t P_max, int32_t* counts, int32_t* offsets,
+                                   int32_t* route_row, int32_t* row_token, uint16_t* x_perm, void* workspace,
+                                   hipStream_t stream) {
+    const int64_t R = T * k;
+    const int tpw = route_hist_tokens_per_chunk(T, E);
+    const int64_t nchunks = T > 0 ? (T + tpw - 1) / tpw : 0;
+    int32_t* hist = (int32_t*)workspace;
+    hipLaunchKernelGGL(permute_scan_kernel, dim3((unsigned)((E + kWave - 1) / kWave)), dim3(kScanThreads), 0,
+                       stream, hist, nchunks, E, counts);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const int64_t scatter_blocks = nchunks > 0 ? (nchunks + 3) / 4 : 1;
+    const size_t scatter_lds = (4 * (size_t)E + E + 1 + 4) * sizeof(int32_t);
+    // tpw * k <= 32 * 32 routes per chunk: 16 steps of 64
+    hipLaunchKernelGGL(permute_scatter_kernel<16>, dim3((unsigned)scatter_blocks), dim3(kScatterThreads),
+                       scatter_lds, stream, topk_idx, R, E, k, align, nchunks, P_max, (const int32_t*)hist,
+                       (const int32_t*)counts, offsets, route_row, row_token, tpw * k);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    return launch_permute_copy(x, T, H, E, k, P_max, counts, offsets, route_row, x_perm, stream);
+}
+
+hipError_t launch_permute_copy(const uint16_t* x, int64_t T, int H, int E, int k, int64_t P_max,
+                               const int32_t* counts, const int32_t* offsets, const int32_t* route_row,
+                               uint16_t* x_perm, hipStream_t stream) {
     if (!x_perm) return hipGetLastError();  // the layout only
     const int ppr = H / 8;  // 16-byte pieces per row
     // one wavefront per token, then one workgroup per expert for its pad rows

@@ -75,10 +75,12 @@ __device__ __forceinline__ void best_with(float& hv, int& hi) {
 // of its group (sub = this lane's index in the group; live = the token exists --
 // groups past the last token run the exchanges on empty lists). KL >= k list slots
 // per lane; VEC logits per load (4 needs E % 4 == 0 and a 16-byte aligned row).
-// Writes idx_out[j], w_out[j] for j < k (only when live).
+// Writes idx_out[j], w_out[j] for j < k (only when live), and idx_lds[j] too when
+// idx_lds is not NULL (an LDS copy of the ids).
 template <int KL, int VEC, int LPT>
 __device__ __forceinline__ void topk_token(const float* row, bool live, int E, int k, int sub,
-                                           int32_t* __restrict__ idx_out, float* __restrict__ w_out) {
+                                           int32_t* __restrict__ idx_out, float* __restrict__ w_out,
+                                           int32_t* idx_lds = nullptr) {
     constexpr int kLanesPerToken = LPT;
     static_assert(LPT == 8 || LPT == 16, "8 or 16 lanes per token");
     float lv[KL];
@@ -145,6 +147,7 @@ __device__ __forceinline__ void topk_token(const float* row, bool live, int E, i
             if (j < k) {
                 idx_out[j] = own_i[jj];
                 w_out[j] = own_z[jj] / sum;
+                if (idx_lds) idx_lds[j] = own_i[jj];  // the same ids, for the caller's histogram
             }
         }
     }

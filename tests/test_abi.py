@@ -91,6 +91,25 @@ def test_debug_library_exports_the_same_calls(lib, debug_lib):
     assert debug_lib.moe_combine(FAKE, FAKE, FAKE, 4, 128, 2, 100, None, None) == NULLP
 
 
+def test_route_hist_validation(lib):
+    n = ctypes.c_size_t(0)
+    assert lib.moe_route_hist_workspace_size(8192, 8, 128, ctypes.byref(n)) == OK
+    assert n.value >= (8192 // 32) * 128 * 4 and n.value % 256 == 0
+    assert lib.moe_route_hist_workspace_size(10, 9, 8, ctypes.byref(n)) == SHAPE      # k > E
+    lib.moe_route_topk_hist.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                        ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                        ctypes.c_void_p]
+    assert lib.moe_route_topk_hist(FAKE, 64, 8, 2, FAKE, FAKE, None, 1 << 20, None) == NULLP
+    assert lib.moe_route_topk_hist(FAKE, 64, 8, 2, FAKE, FAKE, FAKE, 4, None) == WORKSPACE
+    assert lib.moe_route_topk_hist(None, 0, 8, 2, None, None, None, 0, None) == OK     # no tokens
+    lib.moe_permute_from_hist.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64] + \
+        [ctypes.c_int32] * 4 + [ctypes.c_int64] + [ctypes.c_void_p] * 6 + [ctypes.c_size_t, ctypes.c_void_p]
+    assert lib.moe_permute_from_hist(FAKE, FAKE, 64, 128, 8, 2, 32, 64 * 2 + 8 * 31, FAKE, FAKE, FAKE, FAKE,
+                                     FAKE, FAKE, 4, None) == WORKSPACE
+    assert lib.moe_permute_from_hist(FAKE, FAKE, 64, 100, 8, 2, 32, 64 * 2 + 8 * 31, FAKE, FAKE, FAKE, FAKE,
+                                     FAKE, FAKE, 1 << 20, None) == SHAPE               # H % 64
+
+
 def test_probe_validation(lib):
     assert lib.moe_probe_copy(None, FAKE, 1024, None) == NULLP
     assert lib.moe_probe_copy(FAKE, FAKE, 1000, None) == SHAPE      # not a multiple of 16

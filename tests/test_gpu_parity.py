@@ -118,6 +118,49 @@ def test_permute(gpu_lib, case):
         assert L.counts[3].item() == T
 
 
+ROUTE_HIST_CASES = [
+    # name, T, H, E, k, align, logits kind
+    ("narrow_rows_T20000_E128_k8", 20000, 256, 128, 8, 32, "gauss"),   # 8 lanes per token, 32-token chunks
+    ("wide_rows_E512_k10", 3000, 128, 512, 10, 32, "gauss"),            # 16 lanes per token
+    ("k1_E40_ragged_T", 777, 128, 40, 1, 8, "gauss"),
+    ("k32_E64", 300, 64, 64, 32, 16, "gauss"),                         # 512 routes per chunk
+    ("ties_E16_k5", 500, 128, 16, 5, 32, "ties"),
+    ("hot_expert", 1000, 128, 16, 2, 32, "hot"),
+    ("T1", 1, 192, 8, 2, 32, "gauss"),
+    ("E1", 50, 64, 1, 1, 32, "gauss"),
+]
+
+
+@pytest.mark.parametrize("case", ROUTE_HIST_CASES, ids=[c[0] for c in ROUTE_HIST_CASES])
+def test_route_hist_then_permute(gpu_lib, case):
+    """Routing that also counts the permute's histogram, then the permute from it:
+    ids and weights as the oracle's routing, layout and x_perm bit for bit."""
+    name, T, H, E, k, align, kind = case
+    _say(f"route+hist / permute-from-hist case {name}")
+    if kind == "ties":
+        logits = gen.tied_logits(T, E, seed=T)
+    else:
+        logits = np.random.default_rng(T + E).standard_normal((T, E)).astype(np.float32)
+        if kind == "hot":
+            logits[:, 3] += 100.0
+    x = gen.random_bf16((T, H), seed=T + 1)
+    idx_ref, w_ref = oracle.route_topk(logits, k)
+    ws = torch.empty(max(gpu_lib.route_hist_workspace_size(T, k, E), 256), dtype=torch.uint8, device="cuda")
+    idx, w = gpu_lib.route_topk_hist(dev(logits), k, ws)
+    P_max = T * k + E * (align - 1)
+    L = gpu_lib.permute_from_hist(dev_bf16(x), idx, E, align, ws, P_max)
+    torch.cuda.synchronize()
+    assert (idx.cpu().numpy() == idx_ref).all()
+    assert np.max(np.abs(w.cpu().numpy().astype(np.float64) - w_ref)) <= 1e-6
+    c_ref, o_ref, rr_ref, rt_ref = oracle.layout(idx_ref, E, align, P_max)
+    assert (L.counts.cpu().numpy() == c_ref).all()
+    assert (L.offsets.cpu().numpy() == o_ref).all()
+    assert (L.route_row.cpu().numpy() == rr_ref).all()
+    assert (L.row_token.cpu().numpy() == rt_ref).all()
+    used = int(o_ref[-1])
+    assert (host_bits(L.x_perm[:used]) == oracle.gather(x, rt_ref, rows=used)).all()
+
+
 def test_permute_empty(gpu_lib):
     x = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
     idx = torch.empty((0, 2), dtype=torch.int32, device="cuda")
