@@ -180,6 +180,38 @@ moe_status moe_permute_from_hist(const moe_bf16 *x, const int32_t *topk_idx, int
                                  size_t workspace_bytes, moe_stream_t stream);
 
 /*
+ * The layer after routing as one persistent kernel [prime-rl, Changes: the fused
+ * "Mega MoE" op -- dispatch, experts and combine in one kernel; the page measured
+ * it slower than the split path on one node]. One cooperative launch (one
+ * workgroup per compute unit, all resident) runs, with a grid-wide barrier
+ * between phases: the permute's counting sort, scan and scatter; the gate/up GEMM
+ * reading token rows of x in place through row_token (no x_perm); the down GEMM;
+ * the combine. Outputs equal, bit for bit, those of moe_permute with x_perm NULL,
+ * moe_grouped_glu_gemm_gather, moe_grouped_down_gemm and moe_combine on the same
+ * inputs:
+ *   x [T, H] bf16, topk_idx / topk_w [T, k] from moe_route_topk,
+ *   w_gate_up [E, 2I, H], w_down [E, H, I] bf16
+ *   expert_counts [E], expert_offsets [E+1], route_row [T*k], row_token [P_max]
+ *   int32 out (as moe_permute); h [P_max, I], y [P_max, H] bf16 out (as the
+ *   GEMMs); out [T, H] bf16 out (as moe_combine)
+ *   workspace: moe_fused_layer_workspace_size(T, k, E) bytes (barrier words and
+ *   the histogram; reset by the call itself)
+ * Shapes and errors as for those calls (T >= 1, T * H * 2 < 2^32); a device
+ * without cooperative launch gives MOE_ERR_HIP. Every wait at a barrier is
+ * bounded: if a workgroup never arrives, the others stop after about a second and
+ * moe_fused_layer_status (which synchronises `stream`) returns MOE_ERR_HIP;
+ * MOE_OK otherwise. Calls that overlap on one workspace race.
+ */
+moe_status moe_fused_layer_workspace_size(int64_t T, int32_t k, int32_t E, size_t *bytes);
+moe_status moe_fused_layer(const moe_bf16 *x, const int32_t *topk_idx, const float *topk_w,
+                           const moe_bf16 *w_gate_up, const moe_bf16 *w_down, int64_t T, int32_t H, int32_t E,
+                           int32_t k, int32_t I, int32_t align, int64_t P_max, int32_t *expert_counts,
+                           int32_t *expert_offsets, int32_t *route_row, int32_t *row_token, moe_bf16 *h,
+                           moe_bf16 *y, moe_bf16 *out, void *workspace, size_t workspace_bytes,
+                           moe_stream_t stream);
+moe_status moe_fused_layer_status(const void *workspace, moe_stream_t stream);
+
+/*
  * moe_permute without a workspace, for callers that cannot allocate device
  * memory (code under HIP graph capture, tight serving loops, harnesses that
  * forbid hipMalloc): the per-chunk histogram goes to a fixed device array inside

@@ -110,6 +110,14 @@ def _open(debug: bool):
     lib.moe_permute_from_hist.argtypes = [_c_vp, _c_vp, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64,
                                           _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_sz, _c_vp]
     lib.moe_permute_from_hist.restype = ctypes.c_int
+    lib.moe_fused_layer_workspace_size.argtypes = [_c_i64, _c_i32, _c_i32, ctypes.POINTER(_c_sz)]
+    lib.moe_fused_layer_workspace_size.restype = ctypes.c_int
+    lib.moe_fused_layer.argtypes = [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32,
+                                    _c_i32, _c_i64, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_sz,
+                                    _c_vp]
+    lib.moe_fused_layer.restype = ctypes.c_int
+    lib.moe_fused_layer_status.argtypes = [_c_vp, _c_vp]
+    lib.moe_fused_layer_status.restype = ctypes.c_int
     lib.moe_permute_noalloc.argtypes = [_c_vp, _c_vp, _c_i64, _c_i32, _c_i32, _c_i32, _c_i32, _c_i64,
                                         _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp]
     lib.moe_permute_noalloc.restype = ctypes.c_int
@@ -302,6 +310,42 @@ def permute_from_hist(x: torch.Tensor, topk_idx: torch.Tensor, E: int, align: in
           _ptr(out.x_perm, torch.bfloat16, "x_perm", (P_max, H)) if gather else None,
           _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream))
     return out
+
+
+class FusedLayer:
+    """The layer after routing as one persistent kernel (moe_fused_layer): caller's
+    route_topk outputs in, out [T, H] out; the layout, h and y are kept here."""
+
+    def __init__(self, T: int, H: int, E: int, k: int, I: int, align: int = 32, device=None):
+        dev = device or torch.device("cuda")
+        self.T, self.H, self.E, self.k, self.I, self.align = T, H, E, k, I, align
+        self.P_max = padded_rows_max(T, k, E, align)
+        self.layout = alloc_layout(T, H, E, k, self.P_max, dev, gather=False)
+        self.h = torch.empty((self.P_max, I), dtype=torch.bfloat16, device=dev)
+        self.y = torch.empty((self.P_max, H), dtype=torch.bfloat16, device=dev)
+        self.out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+        n = _c_sz(0)
+        _call("moe_fused_layer_workspace_size", T, k, E, ctypes.byref(n))
+        self.workspace = torch.empty(max(int(n.value), 256), dtype=torch.uint8, device=dev)
+
+    def __call__(self, x, topk_idx, topk_w, w_gate_up, w_down, stream=None):
+        T, H, E, k, I = self.T, self.H, self.E, self.k, self.I
+        L = self.layout
+        _call("moe_fused_layer", _ptr(x, torch.bfloat16, "x", (T, H)),
+              _ptr(topk_idx, torch.int32, "topk_idx", (T, k)), _ptr(topk_w, torch.float32, "topk_w", (T, k)),
+              _ptr(w_gate_up, torch.bfloat16, "w_gate_up", (E, 2 * I, H)),
+              _ptr(w_down, torch.bfloat16, "w_down", (E, H, I)), T, H, E, k, I, self.align, self.P_max,
+              _ptr(L.counts, torch.int32, "counts", (E,)), _ptr(L.offsets, torch.int32, "offsets", (E + 1,)),
+              _ptr(L.route_row, torch.int32, "route_row", (T * k,)),
+              _ptr(L.row_token, torch.int32, "row_token", (self.P_max,)),
+              _ptr(self.h, torch.bfloat16, "h"), _ptr(self.y, torch.bfloat16, "y"),
+              _ptr(self.out, torch.bfloat16, "out"), _ptr(self.workspace, torch.uint8, "workspace"),
+              self.workspace.numel(), _stream(stream))
+        return self.out
+
+    def status(self, stream=None):
+        """Synchronises; raises MoEError if a grid barrier of the last call timed out."""
+        _call("moe_fused_layer_status", _ptr(self.workspace, torch.uint8, "workspace"), _stream(stream))
 
 
 def permute_noalloc(x: torch.Tensor, topk_idx: torch.Tensor, E: int, align: int, out: Layout, stream=None,

@@ -45,6 +45,11 @@ hipError_t launch_wgrad(const uint16_t*, const uint16_t*, const int32_t*, const 
 hipError_t launch_combine(const uint16_t*, const int32_t*, const float*, int64_t, int, int,
                           int64_t, uint16_t*, hipStream_t);
 hipError_t launch_probe_copy(const void*, void*, size_t, int, hipStream_t);
+size_t fused_layer_workspace_bytes(int64_t, int, int);
+hipError_t launch_fused_layer(const uint16_t*, const int32_t*, const float*, const uint16_t*, const uint16_t*, int64_t,
+                              int, int, int, int, int, int64_t, int32_t*, int32_t*, int32_t*, int32_t*, uint16_t*,
+                              uint16_t*, uint16_t*, void*, hipStream_t);
+hipError_t fused_layer_read_error(const void*, int32_t*, hipStream_t);
 hipError_t launch_probe_mfma(float*, int, int, hipStream_t);
 int probe_mfma_blocks(int);
 double probe_mfma_flops(int, int);
@@ -214,6 +219,15 @@ moe_status moe_route_topk(const float* logits, int64_t T, int32_t E, int32_t k, 
                       "moe_route_topk launch");
 }
 
+static moe_status check_gather(const int32_t* row_token, int64_t T, int32_t H) {
+    REQUIRE_PTR(row_token);
+    if (T < 1) return fail(MOE_ERR_INVALID_SHAPE, "T=%lld < 1", (long long)T);
+    if ((uint64_t)T * (uint64_t)H * 2u >= ((uint64_t)1 << 32))
+        return fail(MOE_ERR_SIZE_OVERFLOW, "T*H*2 = %llu bytes of x reach 2^32 (32-bit offsets)",
+                    (unsigned long long)((uint64_t)T * (uint64_t)H * 2u));
+    return MOE_OK;
+}
+
 static moe_status check_permute(const moe_bf16* x, const int32_t* topk_idx, int64_t T, int32_t H, int32_t E,
                                 int32_t k, int32_t align, int64_t P_max, const int32_t* expert_counts,
                                 const int32_t* expert_offsets, const int32_t* route_row, const int32_t* row_token,
@@ -305,6 +319,59 @@ moe_status moe_permute_from_hist(const moe_bf16* x, const int32_t* topk_idx, int
                       "moe_permute_from_hist launch");
 }
 
+moe_status moe_fused_layer_workspace_size(int64_t T, int32_t k, int32_t E, size_t* bytes) {
+    if (!bytes) return fail(MOE_ERR_NULL_POINTER, "bytes is NULL");
+    if (T < 0 || T >= ((int64_t)1 << 31)) return fail(MOE_ERR_INVALID_SHAPE, "T=%lld outside [0, 2^31)", (long long)T);
+    moe_status s = check_ek(E, k);
+    if (s != MOE_OK) return s;
+    *bytes = moe::fused_layer_workspace_bytes(T, k, E);
+    return ok();
+}
+
+moe_status moe_fused_layer(const moe_bf16* x, const int32_t* topk_idx, const float* topk_w,
+                           const moe_bf16* w_gate_up, const moe_bf16* w_down, int64_t T, int32_t H, int32_t E,
+                           int32_t k, int32_t I, int32_t align, int64_t P_max, int32_t* expert_counts,
+                           int32_t* expert_offsets, int32_t* route_row, int32_t* row_token, moe_bf16* h,
+                           moe_bf16* y, moe_bf16* out, void* workspace, size_t workspace_bytes,
+                           moe_stream_t stream) {
+    REQUIRE_PTR(x);  // read by the gathering GEMM (check_permute needs x only with x_perm)
+    if (T < 1) return fail(MOE_ERR_INVALID_SHAPE, "T=%lld < 1", (long long)T);
+    moe_status s = check_permute(x, topk_idx, T, H, E, k, align, P_max, expert_counts, expert_offsets, route_row,
+                                 row_token, nullptr);
+    if (s != MOE_OK) return s;
+    REQUIRE_PTR(topk_w);
+    REQUIRE_PTR(w_gate_up);
+    REQUIRE_PTR(w_down);
+    REQUIRE_PTR(h);
+    REQUIRE_PTR(y);
+    REQUIRE_PTR(out);
+    REQUIRE_PTR(workspace);
+    if ((s = check_dim64("I", I)) != MOE_OK) return s;
+    if ((uint64_t)H * (uint64_t)I * 4u >= ((uint64_t)1 << 32))
+        return fail(MOE_ERR_SIZE_OVERFLOW, "one expert's weights (2*I*H bf16, H=%d, I=%d) reach 2^32 bytes", H, I);
+    if ((s = check_gather(row_token, T, H)) != MOE_OK) return s;
+    const size_t ws = moe::fused_layer_workspace_bytes(T, k, E);
+    if (workspace_bytes < ws)
+        return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", workspace_bytes, ws);
+    DEBUG_CHECK(moe::debug_check_ids(topk_idx, T, k, E, (hipStream_t)stream));
+    return hip_status(moe::launch_fused_layer(x, topk_idx, topk_w, w_gate_up, w_down, T, H, E, k, I, align, P_max,
+                                              expert_counts, expert_offsets, route_row, row_token, h, y, out,
+                                              workspace, (hipStream_t)stream),
+                      "moe_fused_layer launch");
+}
+
+moe_status moe_fused_layer_status(const void* workspace, moe_stream_t stream) {
+    REQUIRE_PTR(workspace);
+    int32_t code = 0;
+    moe_status s = hip_status(moe::fused_layer_read_error(workspace, &code, (hipStream_t)stream),
+                              "moe_fused_layer_status");
+    if (s != MOE_OK) return s;
+    if (code != 0)
+        return fail(MOE_ERR_HIP, "moe_fused_layer: a grid barrier timed out (a workgroup never arrived); "
+                                 "the outputs of that call are incomplete");
+    return ok();
+}
+
 size_t moe_permute_noalloc_max_workspace(void) { return moe::permute_scratch_bytes(); }
 
 moe_status moe_permute_noalloc(const moe_bf16* x, const int32_t* topk_idx, int64_t T, int32_t H, int32_t E,
@@ -357,14 +424,6 @@ moe_status moe_grouped_glu_gemm(const moe_bf16* x_perm, const moe_bf16* w_gate_u
                       "moe_grouped_glu_gemm launch");
 }
 
-static moe_status check_gather(const int32_t* row_token, int64_t T, int32_t H) {
-    REQUIRE_PTR(row_token);
-    if (T < 1) return fail(MOE_ERR_INVALID_SHAPE, "T=%lld < 1", (long long)T);
-    if ((uint64_t)T * (uint64_t)H * 2u >= ((uint64_t)1 << 32))
-        return fail(MOE_ERR_SIZE_OVERFLOW, "T*H*2 = %llu bytes of x reach 2^32 (32-bit offsets)",
-                    (unsigned long long)((uint64_t)T * (uint64_t)H * 2u));
-    return MOE_OK;
-}
 
 moe_status moe_grouped_glu_gemm_clamped(const moe_bf16* x_perm, const moe_bf16* w_gate_up,
                                         const int32_t* expert_counts, const int32_t* expert_offsets, int32_t E,

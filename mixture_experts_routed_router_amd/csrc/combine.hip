@@ -13,11 +13,9 @@
 //
 // With topk_w NULL every weight is 1: the unweighted sum of a token's k layout
 // rows is the permute's backward (dx[t] = sum_j dx_perm[route_row[t*k+j]]).
-#include "common.hpp"
+#include "combine_core.hpp"
 
 namespace moe {
-
-constexpr int kCombinePieces = 2;  // 16-byte column pieces per lane per pass
 
 template <int KB>  // routes loaded per batch
 __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ y,
@@ -26,64 +24,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint4* __restrict__ 
                                                       int64_t T, int pieces_per_row, int k, int64_t P_max,
                                                       uint4* __restrict__ out) {
     MOE_DEBUG_GUARD();
-    constexpr int CP = kCombinePieces;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int64_t t = (int64_t)blockIdx.x * 4 + wave;
     if (t >= T) return;
-    const int lane = lane_id();
-    const int32_t* rows = route_row + t * k;   // wave-uniform addresses: scalar loads
-    const float* ws = topk_w ? topk_w + t * k : nullptr;
-    for (int c0 = lane; c0 < pieces_per_row; c0 += kWave * CP) {
-        float acc[CP][8];
-#pragma unroll
-        for (int u = 0; u < CP; ++u)
-#pragma unroll
-            for (int q = 0; q < 8; ++q) acc[u][q] = 0.0f;
-        for (int j0 = 0; j0 < k; j0 += KB) {
-            uint4 v[CP][KB];
-            float w[KB];
-#pragma unroll
-            for (int jj = 0; jj < KB; ++jj) {
-                const int j = j0 + jj;
-                const int32_t row = j < k ? rows[j] : -1;
-                // a row outside [0, P_max) contributes nothing (never read)
-                const bool ok = row >= 0 && row < P_max;
-                w[jj] = ok ? (ws ? ws[j] : 1.0f) : 0.0f;
-#pragma unroll
-                for (int u = 0; u < CP; ++u) {
-                    const int c = c0 + u * kWave;
-                    // each y row is read by exactly one token: streaming (non-temporal) loads
-                    u32x4_t r_ = {0u, 0u, 0u, 0u};
-                    if (ok && c < pieces_per_row)
-                        r_ = __builtin_nontemporal_load((const u32x4_t*)(y + (int64_t)row * pieces_per_row + c));
-                    v[u][jj] = make_uint4(r_[0], r_[1], r_[2], r_[3]);
-                }
-            }
-#pragma unroll
-            for (int jj = 0; jj < KB; ++jj)
-#pragma unroll
-                for (int u = 0; u < CP; ++u) {
-                    const uint32_t p[4] = {v[u][jj].x, v[u][jj].y, v[u][jj].z, v[u][jj].w};
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        acc[u][2 * q] = fmaf(w[jj], bf16_lo(p[q]), acc[u][2 * q]);
-                        acc[u][2 * q + 1] = fmaf(w[jj], bf16_hi(p[q]), acc[u][2 * q + 1]);
-                    }
-                }
-        }
-#pragma unroll
-        for (int u = 0; u < CP; ++u) {
-            const int c = c0 + u * kWave;
-            if (c < pieces_per_row) {
-                uint4 o;
-                o.x = pack_bf16x2(acc[u][0], acc[u][1]);
-                o.y = pack_bf16x2(acc[u][2], acc[u][3]);
-                o.z = pack_bf16x2(acc[u][4], acc[u][5]);
-                o.w = pack_bf16x2(acc[u][6], acc[u][7]);
-                out[t * pieces_per_row + c] = o;
-            }
-        }
-    }
+    combine_token<KB>(y, route_row, topk_w, t, pieces_per_row, k, P_max, out);
 }
 
 hipError_t launch_combine(const uint16_t* y, const int32_t* route_row, const float* topk_w,

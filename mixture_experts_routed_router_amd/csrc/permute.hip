@@ -23,96 +23,38 @@
 //               each token's row is read once and stored to its k rows
 #include <mutex>
 
-#include "common.hpp"
+#include "permute_core.hpp"
 
 namespace moe {
 
-constexpr int kChunk = 256;           // routes per wavefront chunk
-constexpr int kSteps = kChunk / kWave;  // all of a chunk's ids are loaded before any is used
 constexpr int kScanThreads = 1024;
-
-static __device__ __forceinline__ int key_bits(int E) { return E <= 1 ? 0 : 32 - __clz(E - 1); }
+constexpr int kScanWaves = kScanThreads / kWave;
 
 __global__ __launch_bounds__(256) void permute_hist_kernel(const int32_t* __restrict__ topk_idx,
                                                            int64_t R, int E, int64_t nchunks,
                                                            int32_t* __restrict__ hist) {
     MOE_DEBUG_GUARD();
     extern __shared__ int32_t lds_hist[];  // [4][E]
-    const int wave = threadIdx.x / kWave, lane = lane_id();
+    const int wave = threadIdx.x / kWave;
     const int64_t c = (int64_t)blockIdx.x * 4 + wave;
     if (c >= nchunks) return;
-    int32_t* h = lds_hist + wave * E;
-    for (int e = lane; e < E; e += kWave) h[e] = 0;
-    const int nbits = key_bits(E);
-    const int64_t r0 = c * kChunk;
-    uint32_t ids[kSteps];
-#pragma unroll
-    for (int s = 0; s < kSteps; ++s) {
-        const int64_t r = r0 + s * kWave + lane;
-        ids[s] = r < R ? (uint32_t)topk_idx[r] : 0xffffffffu;
-    }
-#pragma unroll
-    for (int s = 0; s < kSteps; ++s) {
-        const bool active = ids[s] < (uint32_t)E;  // out-of-range ids take no part
-        const uint32_t key = active ? ids[s] : 0u;
-        const uint64_t peers = match_peers(key, nbits, active);
-        if (active && (__ffsll((unsigned long long)peers) - 1) == lane) h[key] += __popcll(peers);
-    }
-    int32_t* out = hist + c * E;
-    for (int e = lane; e < E; e += kWave) out[e] = h[e];
+    hist_chunk(topk_idx, R, E, c, lds_hist + wave * E, hist + c * E);
 }
 
-// One workgroup of 1024 threads per 64 experts: lane l of every wave owns
-// expert 64 * blockIdx.x + l, wave w a contiguous range of chunks, so each load
-// reads 256 consecutive bytes of a hist row and the passes over the histogram
-// are spread over E / 64 CUs.
-constexpr int kScanWaves = kScanThreads / kWave;
-
+// One workgroup of 1024 threads per 64 experts (scan_group), so each load reads
+// 256 consecutive bytes of a hist row and the passes over the histogram are
+// spread over E / 64 CUs.
 __global__ __launch_bounds__(kScanThreads) void permute_scan_kernel(int32_t* __restrict__ hist,
                                                                     int64_t nchunks, int E,
                                                                     int32_t* __restrict__ counts) {
     MOE_DEBUG_GUARD();
     __shared__ int32_t part[kScanWaves][kWave];
-    const int lane = lane_id(), wave = threadIdx.x / kWave;
-    const int e = blockIdx.x * kWave + lane;
-    const bool live = e < E;
-    const int64_t per = (nchunks + kScanWaves - 1) / kScanWaves;
-    const int64_t c0 = min(nchunks, (int64_t)wave * per), c1 = min(nchunks, c0 + per);
-    int32_t sum = 0;
-    if (live) {
-#pragma unroll 8
-        for (int64_t c = c0; c < c1; ++c) sum += hist[c * E + e];
-    }
-    part[wave][lane] = sum;
-    __syncthreads();
-    if (wave == 0) {  // per expert: exclusive scan over the waves' ranges, and the total
-        int32_t run = 0;
-        for (int w = 0; w < kScanWaves; ++w) {
-            const int32_t v = part[w][lane];
-            part[w][lane] = run;
-            run += v;
-        }
-        if (live) counts[e] = run;
-    }
-    __syncthreads();
-    if (live) {
-        int32_t run = part[wave][lane];
-#pragma unroll 8
-        for (int64_t c = c0; c < c1; ++c) {
-            const int32_t v = hist[c * E + e];
-            hist[c * E + e] = run;
-            run += v;
-        }
-    }
+    scan_group<kScanWaves>(hist, nchunks, E, counts, blockIdx.x, part);
 }
 
-// Every workgroup first derives the padded expert offsets from the counts (thread
-// i takes experts 4i .. 4i+3, E <= 1024, then a workgroup scan); workgroup 0
-// publishes them, and each workgroup writes row_token = -1 on its share of the
-// pad rows (those of experts b, b + gridDim.x, ..., and every row from
-// offsets[E] to P_max). Then one wavefront per chunk as before.
-// A chunk is `chunk_routes` consecutive routes (kChunk here; the routing
-// kernel's workgroup of tokens when the histogram comes from it), STEPS * 64 at most.
+// Every workgroup first derives the padded expert offsets from the counts;
+// workgroup 0 publishes them, and each workgroup writes row_token = -1 on its
+// share of the pad rows. Then one wavefront per chunk (scatter_chunk).
 constexpr int kScatterThreads = 256;
 
 template <int STEPS>
@@ -125,74 +67,15 @@ __global__ __launch_bounds__(kScatterThreads) void permute_scatter_kernel(
     extern __shared__ int32_t lds_cursor[];  // [4][E] cursors, [E+1] offsets, [4] wave totals
     int32_t* off = lds_cursor + 4 * E;
     int32_t* wtot = off + E + 1;
-    const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
-    {
-        int32_t pc[4], local = 0;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int e = 4 * tid + q;
-            pc[q] = e < E ? (counts[e] + align - 1) / align * align : 0;
-            local += pc[q];
-        }
-        int32_t incl = local;
-#pragma unroll
-        for (int d = 1; d < kWave; d <<= 1) {
-            const int32_t o = __shfl_up(incl, d);
-            if (lane >= d) incl += o;
-        }
-        if (lane == kWave - 1) wtot[wave] = incl;
-        __syncthreads();
-        for (int w = 0; w < wave; ++w) incl += wtot[w];
-        int32_t run = incl - local;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int e = 4 * tid + q;
-            if (e < E) off[e] = run;
-            run += pc[q];
-        }
-        if (tid == kScatterThreads - 1) off[E] = incl;
-        __syncthreads();
-    }
+    const int tid = threadIdx.x, wave = tid / kWave;
+    padded_offsets(counts, E, align, off, wtot);
     if (blockIdx.x == 0)
         for (int e = tid; e <= E; e += kScatterThreads) offsets[e] = off[e];
-    for (int e = blockIdx.x; e < E; e += gridDim.x)
-        for (int64_t p = (int64_t)off[e] + counts[e] + tid; p < off[e + 1]; p += kScatterThreads) row_token[p] = -1;
-    for (int64_t p = (int64_t)off[E] + (int64_t)blockIdx.x * kScatterThreads + tid; p < P_max;
-         p += (int64_t)gridDim.x * kScatterThreads)
-        row_token[p] = -1;
-
+    pad_row_tokens(counts, off, E, P_max, blockIdx.x, gridDim.x, kScatterThreads, row_token);
     const int64_t c = (int64_t)blockIdx.x * 4 + wave;
     if (c >= nchunks) return;
-    int32_t* cur = lds_cursor + wave * E;
-    for (int e = lane; e < E; e += kWave) cur[e] = base[c * E + e] + off[e];
-    const int nbits = key_bits(E);
-    const uint64_t lt = lanemask_lt();
-    const int64_t r0 = c * chunk_routes;
-    const int64_t r_end = r0 + chunk_routes < R ? r0 + chunk_routes : R;
-    const int steps = (chunk_routes + kWave - 1) / kWave;
-    uint32_t ids[STEPS];
-#pragma unroll
-    for (int s = 0; s < STEPS; ++s) {
-        const int64_t r = r0 + s * kWave + lane;
-        ids[s] = s < steps && r < r_end ? (uint32_t)topk_idx[r] : 0xffffffffu;
-    }
-#pragma unroll
-    for (int s = 0; s < STEPS; ++s) {
-        if (s < steps) {  // wave-uniform
-            const int64_t r = r0 + s * kWave + lane;
-            const bool active = ids[s] < (uint32_t)E;
-            const uint32_t key = active ? ids[s] : 0u;
-            const uint64_t peers = match_peers(key, nbits, active);
-            if (active) {
-                const int32_t dest = cur[key] + __popcll(peers & lt);
-                route_row[r] = dest;
-                row_token[dest] = (int32_t)(r / k);
-            } else if (r < r_end) {
-                route_row[r] = -1;  // an out-of-range id gets no row
-            }
-            if (active && (__ffsll((unsigned long long)peers) - 1) == lane) cur[key] += __popcll(peers);
-        }
-    }
+    scatter_chunk<STEPS>(topk_idx, R, E, k, c, base, off, lds_cursor + wave * E, route_row, row_token,
+                         chunk_routes);
 }
 
 // The gather, token-major: one wavefront per token reads the token's row of x

@@ -110,6 +110,27 @@ def test_route_hist_validation(lib):
                                      FAKE, FAKE, 1 << 20, None) == SHAPE               # H % 64
 
 
+def test_fused_layer_validation(lib):
+    n = ctypes.c_size_t(0)
+    assert lib.moe_fused_layer_workspace_size(8192, 8, 128, ctypes.byref(n)) == OK
+    assert n.value >= 256 + (8192 * 8 // 256) * 128 * 4
+    i32, i64, vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
+    lib.moe_fused_layer.argtypes = [vp] * 5 + [i64] + [i32] * 5 + [i64] + [vp] * 8 + [ctypes.c_size_t, vp]
+
+    def call(T=64, H=128, E=8, k=2, I=128, align=32, ws=1 << 20, x=FAKE, out=FAKE):
+        return lib.moe_fused_layer(x, FAKE, FAKE, FAKE, FAKE, T, H, E, k, I, align, T * k + E * (align - 1),
+                                   FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, out, FAKE, ws, None)
+    assert call(x=None) == NULLP
+    assert call(out=None) == NULLP
+    assert call(T=0) == SHAPE
+    assert call(I=100) == SHAPE
+    assert call(k=9) == SHAPE
+    assert call(ws=16) == WORKSPACE
+    assert call(T=1 << 20, H=4096) == OVERFLOW          # T * H * 2 reaches 2^32 (32-bit gather offsets)
+    lib.moe_fused_layer_status.argtypes = [vp, vp]
+    assert lib.moe_fused_layer_status(None, None) == NULLP
+
+
 def test_probe_validation(lib):
     assert lib.moe_probe_copy(None, FAKE, 1024, None) == NULLP
     assert lib.moe_probe_copy(FAKE, FAKE, 1000, None) == SHAPE      # not a multiple of 16
