@@ -424,9 +424,10 @@ def permute_bwd(dx_perm, route_row, T: int, k: int, lib=None):
     return dx
 
 
-def backward(x_bits, logits, w_gu_bits, w_d_bits, dout, k: int, lib=None):
+def backward(x_bits, logits, w_gu_bits, w_d_bits, dout, k: int, lib=None, weights: bool = True):
     """The whole backward as a per-token loop: (dx [T,H], dlogits [T,E],
-    dw_gu [E,2I,H], dw_d [E,H,I]), all float64."""
+    dw_gu [E,2I,H], dw_d [E,H,I]), all float64.  weights=False computes only dx
+    and dlogits (tokens in parallel; the weight gradients come back as None)."""
     x_bits, w_gu_bits, w_d_bits = _u16(x_bits), _u16(w_gu_bits), _u16(w_d_bits)
     logits = np.ascontiguousarray(logits, dtype=np.float32)
     dout = _f64(dout)
@@ -435,11 +436,13 @@ def backward(x_bits, logits, w_gu_bits, w_d_bits, dout, k: int, lib=None):
     I = two_i // 2
     assert logits.shape == (T, E) and w_d_bits.shape == (E, H, I) and dout.shape == (T, H)
     dx, dl = np.empty((T, H)), np.empty((T, E))
-    dwgu, dwd = np.empty((E, 2 * I, H)), np.empty((E, H, I))
+    dwgu = np.empty((E, 2 * I, H)) if weights else None
+    dwd = np.empty((E, H, I)) if weights else None
     _check((lib or _lib()).moe_oracle_backward(_p(x_bits, _u16p), _p(logits, _f32p), _p(w_gu_bits, _u16p),
                                                _p(w_d_bits, _u16p), _p(dout, _f64p), T, H, E, k, I,
-                                               _p(dx, _f64p), _p(dl, _f64p), _p(dwgu, _f64p),
-                                               _p(dwd, _f64p)), "backward")
+                                               _p(dx, _f64p), _p(dl, _f64p),
+                                               _p(dwgu, _f64p) if weights else None,
+                                               _p(dwd, _f64p) if weights else None), "backward")
     return dx, dl, dwgu, dwd
 
 

@@ -654,98 +654,142 @@ int moe_oracle_permute_bwd(const double *dx_perm, const int32_t *route_row, int6
  * each of its k experts (g, u, h, y), then apply the chain rule above; weight
  * gradients accumulate over tokens in ascending order.  dout [T, H] in double;
  * outputs dx [T, H], dlogits [T, E], dw_gu [E, 2I, H], dw_d [E, H, I].
+ *
+ * A token's input gradients (dx, dlogits) depend on no other token.  When both
+ * weight-gradient outputs are NULL only those are computed, and the tokens run in
+ * parallel; each token's arithmetic is the same either way.
  */
-int moe_oracle_backward(const uint16_t *x, const float *logits, const uint16_t *w_gu,
-                        const uint16_t *w_d, const double *dout, int64_t T, int32_t H, int32_t E,
-                        int32_t k, int32_t I, double *dx, double *dlogits, double *dw_gu,
-                        double *dw_d) {
-    if (!x || !logits || !w_gu || !w_d || !dout || !dx || !dlogits || !dw_gu || !dw_d || T < 0 ||
-        H < 1 || E < 1 || k < 1 || k > E || I < 1)
-        return ORACLE_EINVAL;
-    for (int64_t i = 0; i < T * (int64_t)E; ++i)
-        if (!isfinite(logits[i])) return ORACLE_ENONFINITE;
-    for (int64_t i = 0; i < (int64_t)E * 2 * I * H; ++i) dw_gu[i] = 0.0;
-    for (int64_t i = 0; i < (int64_t)E * H * I; ++i) dw_d[i] = 0.0;
-    int32_t *idx = (int32_t *)malloc(sizeof(int32_t) * (size_t)k);
-    double *w = (double *)malloc(sizeof(double) * (size_t)k);
-    double *dwt = (double *)malloc(sizeof(double) * (size_t)k);
-    double *g = (double *)malloc(sizeof(double) * (size_t)I * k);
-    double *u = (double *)malloc(sizeof(double) * (size_t)I * k);
-    double *a = (double *)malloc(sizeof(double) * (size_t)I * k);
-    double *dh = (double *)malloc(sizeof(double) * (size_t)I);
-    if (!idx || !w || !dwt || !g || !u || !a || !dh) {
-        free(idx); free(w); free(dwt); free(g); free(u); free(a); free(dh);
-        return ORACLE_EINVAL;
-    }
-    for (int64_t t = 0; t < T; ++t) {
-        const uint16_t *xr = x + t * H;
-        const double *gr = dout + t * H;
-        moe_oracle_route_topk(logits + t * E, 1, E, k, idx, w);
-        /* forward of each route, and dw */
-        for (int32_t j = 0; j < k; ++j) {
-            const uint16_t *Wgu = w_gu + (int64_t)idx[j] * 2 * I * H;
-            const uint16_t *Wd = w_d + (int64_t)idx[j] * H * I;
-            for (int32_t i = 0; i < I; ++i) {
-                double gg = 0.0, uu = 0.0;
-                for (int32_t c = 0; c < H; ++c) {
-                    gg += bf(xr[c]) * bf(Wgu[(int64_t)i * H + c]);
-                    uu += bf(xr[c]) * bf(Wgu[(int64_t)(I + i) * H + c]);
-                }
-                g[j * I + i] = gg;
-                u[j * I + i] = uu;
-                a[j * I + i] = silu(gg) * uu;
-            }
-            double s = 0.0;
+typedef struct {
+    int32_t *idx;
+    double *w, *dwt, *g, *u, *a, *dh;
+} BwdScratch;
+
+static int bwd_scratch_alloc(BwdScratch *sc, int32_t k, int32_t I) {
+    sc->idx = (int32_t *)malloc(sizeof(int32_t) * (size_t)k);
+    sc->w = (double *)malloc(sizeof(double) * (size_t)k);
+    sc->dwt = (double *)malloc(sizeof(double) * (size_t)k);
+    sc->g = (double *)malloc(sizeof(double) * (size_t)I * k);
+    sc->u = (double *)malloc(sizeof(double) * (size_t)I * k);
+    sc->a = (double *)malloc(sizeof(double) * (size_t)I * k);
+    sc->dh = (double *)malloc(sizeof(double) * (size_t)I);
+    return sc->idx && sc->w && sc->dwt && sc->g && sc->u && sc->a && sc->dh;
+}
+
+static void bwd_scratch_free(BwdScratch *sc) {
+    free(sc->idx); free(sc->w); free(sc->dwt); free(sc->g); free(sc->u); free(sc->a); free(sc->dh);
+}
+
+/* Token t's dx and dlogits rows; adds its share to dw_gu, dw_d unless they are NULL. */
+static void backward_token(int64_t t, const uint16_t *x, const float *logits, const uint16_t *w_gu,
+                           const uint16_t *w_d, const double *dout, int32_t H, int32_t E, int32_t k,
+                           int32_t I, double *dx, double *dlogits, double *dw_gu, double *dw_d,
+                           const BwdScratch *sc) {
+    int32_t *idx = sc->idx;
+    double *w = sc->w, *dwt = sc->dwt, *g = sc->g, *u = sc->u, *a = sc->a, *dh = sc->dh;
+    const uint16_t *xr = x + t * H;
+    const double *gr = dout + t * H;
+    moe_oracle_route_topk(logits + t * E, 1, E, k, idx, w);
+    /* forward of each route, and dw */
+    for (int32_t j = 0; j < k; ++j) {
+        const uint16_t *Wgu = w_gu + (int64_t)idx[j] * 2 * I * H;
+        const uint16_t *Wd = w_d + (int64_t)idx[j] * H * I;
+        for (int32_t i = 0; i < I; ++i) {
+            double gg = 0.0, uu = 0.0;
             for (int32_t c = 0; c < H; ++c) {
-                double yc = 0.0;
-                for (int32_t i = 0; i < I; ++i) yc += a[j * I + i] * bf(Wd[(int64_t)c * I + i]);
-                s += gr[c] * yc;
+                gg += bf(xr[c]) * bf(Wgu[(int64_t)i * H + c]);
+                uu += bf(xr[c]) * bf(Wgu[(int64_t)(I + i) * H + c]);
             }
-            dwt[j] = s;
+            g[j * I + i] = gg;
+            u[j * I + i] = uu;
+            a[j * I + i] = silu(gg) * uu;
         }
-        double sw = 0.0;
-        for (int32_t j = 0; j < k; ++j) sw += w[j] * dwt[j];
-        for (int32_t e = 0; e < E; ++e) dlogits[t * E + e] = 0.0;
-        for (int32_t j = 0; j < k; ++j) dlogits[t * E + idx[j]] = w[j] * (dwt[j] - sw);
-        for (int32_t c = 0; c < H; ++c) dx[t * H + c] = 0.0;
-        /* backward of each route */
-        for (int32_t j = 0; j < k; ++j) {
-            const uint16_t *Wd = w_d + (int64_t)idx[j] * H * I;
-            double *dWgu = dw_gu + (int64_t)idx[j] * 2 * I * H;
-            double *dWd = dw_d + (int64_t)idx[j] * H * I;
-            for (int32_t i = 0; i < I; ++i) {
-                double sdh = 0.0;
-                for (int32_t c = 0; c < H; ++c) sdh += (w[j] * gr[c]) * bf(Wd[(int64_t)c * I + i]);
-                dh[i] = sdh;
-            }
+        double s = 0.0;
+        for (int32_t c = 0; c < H; ++c) {
+            double yc = 0.0;
+            for (int32_t i = 0; i < I; ++i) yc += a[j * I + i] * bf(Wd[(int64_t)c * I + i]);
+            s += gr[c] * yc;
+        }
+        dwt[j] = s;
+    }
+    double sw = 0.0;
+    for (int32_t j = 0; j < k; ++j) sw += w[j] * dwt[j];
+    for (int32_t e = 0; e < E; ++e) dlogits[t * E + e] = 0.0;
+    for (int32_t j = 0; j < k; ++j) dlogits[t * E + idx[j]] = w[j] * (dwt[j] - sw);
+    for (int32_t c = 0; c < H; ++c) dx[t * H + c] = 0.0;
+    /* backward of each route */
+    for (int32_t j = 0; j < k; ++j) {
+        const uint16_t *Wd = w_d + (int64_t)idx[j] * H * I;
+        double *dWgu = dw_gu ? dw_gu + (int64_t)idx[j] * 2 * I * H : NULL;
+        double *dWd = dw_d ? dw_d + (int64_t)idx[j] * H * I : NULL;
+        for (int32_t i = 0; i < I; ++i) {
+            double sdh = 0.0;
+            for (int32_t c = 0; c < H; ++c) sdh += (w[j] * gr[c]) * bf(Wd[(int64_t)c * I + i]);
+            dh[i] = sdh;
+        }
+        if (dWd)
             for (int32_t c = 0; c < H; ++c)
                 for (int32_t i = 0; i < I; ++i) dWd[(int64_t)c * I + i] += (w[j] * gr[c]) * a[j * I + i];
-            for (int32_t i = 0; i < I; ++i) {
-                const double dg = dh[i] * u[j * I + i] * silu_grad(g[j * I + i]);
-                const double du = dh[i] * silu(g[j * I + i]);
+        for (int32_t i = 0; i < I; ++i) {
+            const double dg = dh[i] * u[j * I + i] * silu_grad(g[j * I + i]);
+            const double du = dh[i] * silu(g[j * I + i]);
+            if (dWgu)
                 for (int32_t c = 0; c < H; ++c) {
                     dWgu[(int64_t)i * H + c] += dg * bf(xr[c]);
                     dWgu[(int64_t)(I + i) * H + c] += du * bf(xr[c]);
                 }
-                g[j * I + i] = dg; /* keep dg, du for dx below */
-                u[j * I + i] = du;
-            }
-        }
-        /* dx[t] = sum_j of that route's dx_perm row, j ascending */
-        for (int32_t j = 0; j < k; ++j) {
-            const uint16_t *Wgu = w_gu + (int64_t)idx[j] * 2 * I * H;
-            for (int32_t c = 0; c < H; ++c) {
-                double s = 0.0;
-                for (int32_t i = 0; i < 2 * I; ++i) {
-                    const double d = i < I ? g[j * I + i] : u[j * I + i - I];
-                    s += d * bf(Wgu[(int64_t)i * H + c]);
-                }
-                dx[t * H + c] += s;
-            }
+            g[j * I + i] = dg; /* keep dg, du for dx below */
+            u[j * I + i] = du;
         }
     }
-    free(idx); free(w); free(dwt); free(g); free(u); free(a); free(dh);
-    return 0;
+    /* dx[t] = sum_j of that route's dx_perm row, j ascending */
+    for (int32_t j = 0; j < k; ++j) {
+        const uint16_t *Wgu = w_gu + (int64_t)idx[j] * 2 * I * H;
+        for (int32_t c = 0; c < H; ++c) {
+            double s = 0.0;
+            for (int32_t i = 0; i < 2 * I; ++i) {
+                const double d = i < I ? g[j * I + i] : u[j * I + i - I];
+                s += d * bf(Wgu[(int64_t)i * H + c]);
+            }
+            dx[t * H + c] += s;
+        }
+    }
+}
+
+int moe_oracle_backward(const uint16_t *x, const float *logits, const uint16_t *w_gu,
+                        const uint16_t *w_d, const double *dout, int64_t T, int32_t H, int32_t E,
+                        int32_t k, int32_t I, double *dx, double *dlogits, double *dw_gu,
+                        double *dw_d) {
+    if (!x || !logits || !w_gu || !w_d || !dout || !dx || !dlogits || (!dw_gu) != (!dw_d) || T < 0 ||
+        H < 1 || E < 1 || k < 1 || k > E || I < 1)
+        return ORACLE_EINVAL;
+    for (int64_t i = 0; i < T * (int64_t)E; ++i)
+        if (!isfinite(logits[i])) return ORACLE_ENONFINITE;
+    if (dw_gu) {
+        for (int64_t i = 0; i < (int64_t)E * 2 * I * H; ++i) dw_gu[i] = 0.0;
+        for (int64_t i = 0; i < (int64_t)E * H * I; ++i) dw_d[i] = 0.0;
+        BwdScratch sc;
+        int ok = bwd_scratch_alloc(&sc, k, I);
+        if (ok)
+            for (int64_t t = 0; t < T; ++t)
+                backward_token(t, x, logits, w_gu, w_d, dout, H, E, k, I, dx, dlogits, dw_gu, dw_d, &sc);
+        bwd_scratch_free(&sc);
+        return ok ? 0 : ORACLE_EINVAL;
+    }
+    int failed = 0;
+#pragma omp parallel
+    {
+        BwdScratch sc;
+        const int ok = bwd_scratch_alloc(&sc, k, I);
+        if (!ok) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t t = 0; t < T; ++t)
+            if (ok) backward_token(t, x, logits, w_gu, w_d, dout, H, E, k, I, dx, dlogits, NULL, NULL, &sc);
+        bwd_scratch_free(&sc);
+    }
+    return failed ? ORACLE_EINVAL : 0;
 }
 
 /* Threads the OpenMP loops above use (for reporting the oracle's CPU time). */

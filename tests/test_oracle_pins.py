@@ -512,9 +512,14 @@ def check_backward_steps_compose(orc):
 def check_backward_invariants(orc):
     """Softmax gradient rows sum to zero; k = 1 leaves no logit gradient; the
     backward is linear in dout (doubling is exact); unrouted experts get zero
-    weight gradients; the steps match numpy matmuls on their own."""
+    weight gradients; the input gradients alone equal the full backward's; the
+    steps match numpy matmuls on their own."""
     x, logits, w_gu, w_d, dout, k = _bwd_case(seed=33, T=12, E=6, k=3)
     dx, dl, dwgu, dwd = orc.backward(x, logits, w_gu, w_d, dout, k)
+    # the input gradients alone (tokens in parallel, no weight gradients) are the same numbers
+    dx_only, dl_only, none_gu, none_d = orc.backward(x, logits, w_gu, w_d, dout, k, weights=False)
+    assert none_gu is None and none_d is None
+    assert np.array_equal(dx_only, dx) and np.array_equal(dl_only, dl)
     assert np.all(np.abs(dl.sum(axis=1)) <= 1e-15 * max(1.0, np.max(np.abs(dl))) * 8)
     sel = np.zeros_like(dl, dtype=bool)
     idx, _ = orc.route_topk(logits, k)
