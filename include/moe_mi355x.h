@@ -284,6 +284,57 @@ moe_status moe_grouped_down_gemm(const moe_bf16 *h, const moe_bf16 *w_down,
                                  moe_stream_t stream);
 
 /*
+ * Row-pair tiled operands.  The same three GEMM steps (and the permute's gather)
+ * with bf16 matrices stored in a tiled order this library defines for gfx950 --
+ * not a layout the pages use: a matrix [R, C] (R even, C % 32 == 0) is kept as
+ * 2 x 32 blocks of 128 bytes, element (r, c) at
+ *     ((r / 2) * (C / 32) + c / 32) * 64 + (r % 2) * 32 + c % 32.
+ * The GEMMs stream operands through LDS 32 columns at a time; in this order one
+ * such piece of two neighbouring rows is one whole 128-byte line, which lifts the
+ * per-CU operand stream that bounds them.  The computation is the one documented
+ * for the row-major calls, with the same fp32 summation order, so every output
+ * is bit-identical to theirs once un-tiled.
+ *
+ * moe_tile_rows / moe_untile_rows: row-major [rows, cols] <-> tiled, bf16,
+ *   rows even and >= 0, cols a positive multiple of 32, src and dst distinct
+ *   device buffers of rows * cols elements; enqueued on `stream`.
+ *   Expert weights are tiled once per weight update: w_gate_up [E, 2I, H] as
+ *   rows = E * 2I, cols = H; w_down [E, H, I] as rows = E * H, cols = I (each
+ *   expert's rows are an even count, so no block spans two experts).
+ * moe_permute_tiled: moe_permute with x_perm [P_max, H] written tiled. Every row
+ *   pair below offsets[E] is written whole, pad rows as zeros (when offsets[E]
+ *   is odd, row offsets[E] is written as zeros too); pairs past it are not
+ *   written.
+ * moe_grouped_glu_gemm_tiled: x_perm and w_gate_up tiled; h [P_max, I] written tiled.
+ * moe_grouped_glu_gemm_gather_tiled: x [T, H] row-major (read through row_token),
+ *   w_gate_up tiled, h written tiled.
+ * moe_grouped_down_gemm_tiled: h and w_down tiled; y [P_max, H] row-major, so
+ *   moe_combine reads it unchanged.
+ * Arguments, shapes and errors as for the row-major calls, plus P_max even
+ * (MOE_ERR_INVALID_SHAPE otherwise): the tiled buffers hold whole row pairs.
+ */
+moe_status moe_tile_rows(const moe_bf16 *src, int64_t rows, int32_t cols, moe_bf16 *dst, moe_stream_t stream);
+moe_status moe_untile_rows(const moe_bf16 *src, int64_t rows, int32_t cols, moe_bf16 *dst, moe_stream_t stream);
+moe_status moe_permute_tiled(const moe_bf16 *x, const int32_t *topk_idx, int64_t T, int32_t H,
+                             int32_t E, int32_t k, int32_t align, int64_t P_max,
+                             int32_t *expert_counts, int32_t *expert_offsets, int32_t *route_row,
+                             int32_t *row_token, moe_bf16 *x_perm, void *workspace,
+                             size_t workspace_bytes, moe_stream_t stream);
+moe_status moe_grouped_glu_gemm_tiled(const moe_bf16 *x_perm, const moe_bf16 *w_gate_up,
+                                      const int32_t *expert_counts, const int32_t *expert_offsets,
+                                      int32_t E, int32_t H, int32_t I, int64_t P_max, moe_bf16 *h,
+                                      moe_stream_t stream);
+moe_status moe_grouped_glu_gemm_gather_tiled(const moe_bf16 *x, const int32_t *row_token,
+                                             const moe_bf16 *w_gate_up, const int32_t *expert_counts,
+                                             const int32_t *expert_offsets, int64_t T, int32_t E,
+                                             int32_t H, int32_t I, int64_t P_max, moe_bf16 *h,
+                                             moe_stream_t stream);
+moe_status moe_grouped_down_gemm_tiled(const moe_bf16 *h, const moe_bf16 *w_down,
+                                       const int32_t *expert_counts, const int32_t *expert_offsets,
+                                       int32_t E, int32_t H, int32_t I, int64_t P_max, moe_bf16 *y,
+                                       moe_stream_t stream);
+
+/*
  * Score-weighted gather-sum [prime-rl, Changes: one fp32 score-weighted
  * gather-sum back].  Per token t, a gather (no scatter-add):
  *   out[t, c] = bf16_rne( sum_{j=0..k-1} topk_w[t, j] * y[route_row[t*k+j], c] )

@@ -72,8 +72,14 @@ def _open(debug: bool):
                                          _c_i64, _c_vp, _c_vp]
     lib.moe_grouped_glu_gemm_gather.argtypes = [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i32,
                                                 _c_i32, _c_i32, _c_i64, _c_vp, _c_vp]
+    lib.moe_tile_rows.argtypes = [_c_vp, _c_i64, _c_i32, _c_vp, _c_vp]
+    lib.moe_untile_rows.argtypes = [_c_vp, _c_i64, _c_i32, _c_vp, _c_vp]
+    lib.moe_permute_tiled.argtypes = lib.moe_permute.argtypes
+    lib.moe_grouped_glu_gemm_tiled.argtypes = lib.moe_grouped_glu_gemm.argtypes
+    lib.moe_grouped_glu_gemm_gather_tiled.argtypes = lib.moe_grouped_glu_gemm_gather.argtypes
     lib.moe_grouped_down_gemm.argtypes = [_c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32,
                                           _c_i64, _c_vp, _c_vp]
+    lib.moe_grouped_down_gemm_tiled.argtypes = lib.moe_grouped_down_gemm.argtypes
     lib.moe_combine.argtypes = [_c_vp, _c_vp, _c_vp, _c_i64, _c_i32, _c_i32, _c_i64, _c_vp, _c_vp]
     lib.moe_quantize_fp8.argtypes = [_c_vp, _c_i64, _c_i32, _c_i32, _c_vp, _c_vp, _c_vp]
     lib.moe_grouped_glu_gemm_fp8w.argtypes = [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32,
@@ -245,9 +251,10 @@ def alloc_layout(T: int, H: int, E: int, k: int, P_max: int, device, gather: boo
 
 def permute(x: torch.Tensor, topk_idx: torch.Tensor, E: int, align: int = 32, P_max=None,
             out: Layout | None = None, workspace: torch.Tensor | None = None, stream=None,
-            gather: bool = True) -> Layout:
+            gather: bool = True, tiled: bool = False) -> Layout:
     """The padded layout; with gather=False (or out.x_perm None) no x_perm is
-    written, for grouped_glu_gemm_gather."""
+    written, for grouped_glu_gemm_gather. tiled=True writes x_perm in the
+    row-pair tiled order (moe_permute_tiled; P_max must be even)."""
     T, H = x.shape
     k = topk_idx.shape[1]
     if P_max is None:
@@ -258,8 +265,8 @@ def permute(x: torch.Tensor, topk_idx: torch.Tensor, E: int, align: int = 32, P_
     ws_bytes = permute_workspace_size(T, k, E)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=x.device)
-    _call("moe_permute", _ptr(x, torch.bfloat16, "x"), _ptr(topk_idx, torch.int32, "topk_idx", (T, k)),
-          T, H, E, k, align, P_max,
+    _call("moe_permute_tiled" if tiled else "moe_permute", _ptr(x, torch.bfloat16, "x"),
+          _ptr(topk_idx, torch.int32, "topk_idx", (T, k)), T, H, E, k, align, P_max,
           _ptr(out.counts, torch.int32, "counts", (E,)),
           _ptr(out.offsets, torch.int32, "offsets", (E + 1,)),
           _ptr(out.route_row, torch.int32, "route_row", (T * k,)),
@@ -446,6 +453,102 @@ def combine(y, route_row, topk_w, out=None, stream=None):
     return out
 
 
+# ---- row-pair tiled operands ------------------------------------------------------------
+
+def even_rows(P_max: int) -> int:
+    """P_max rounded up to whole row pairs (the tiled calls need it even)."""
+    return P_max + (P_max & 1)
+
+
+def tile_rows(src: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Row-major bf16 [R, C] -> the same shape holding the row-pair tiled order."""
+    R, C = src.shape
+    if out is None:
+        out = torch.empty((R, C), dtype=torch.bfloat16, device=src.device)
+    _call("moe_tile_rows", _ptr(src, torch.bfloat16, "src"), R, C, _ptr(out, torch.bfloat16, "dst", (R, C)),
+          _stream(stream))
+    return out
+
+
+def untile_rows(src: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """The inverse of tile_rows."""
+    R, C = src.shape
+    if out is None:
+        out = torch.empty((R, C), dtype=torch.bfloat16, device=src.device)
+    _call("moe_untile_rows", _ptr(src, torch.bfloat16, "src"), R, C, _ptr(out, torch.bfloat16, "dst", (R, C)),
+          _stream(stream))
+    return out
+
+
+@dataclass
+class TiledWeights:
+    """bf16 expert weights [E, R, C] stored in the row-pair tiled order (each
+    expert's R rows tiled on their own; tile_weights)."""
+    data: torch.Tensor
+
+    @property
+    def shape(self):
+        return tuple(self.data.shape)
+
+
+def tile_weights(w: torch.Tensor, stream=None) -> TiledWeights:
+    """Expert weights [E, R, C] (w_gate_up [E, 2I, H], w_down [E, H, I]) in tiled order,
+    once per weight update."""
+    E, R, C = w.shape
+    out = torch.empty((E, R, C), dtype=torch.bfloat16, device=w.device)
+    tile_rows(w.reshape(E * R, C), out=out.view(E * R, C), stream=stream)
+    return TiledWeights(out)
+
+
+def grouped_glu_gemm_tiled(x_perm, w_gate_up: TiledWeights, counts, offsets, h=None, stream=None):
+    """grouped_glu_gemm with x_perm, the weights and h in tiled order."""
+    P_max, H = x_perm.shape
+    E, two_i, H2 = w_gate_up.shape
+    I = two_i // 2
+    if H2 != H or two_i != 2 * I:
+        raise ValueError("w_gate_up must be [E, 2I, H]")
+    if h is None:
+        h = torch.empty((P_max, I), dtype=torch.bfloat16, device=x_perm.device)
+    _call("moe_grouped_glu_gemm_tiled", _ptr(x_perm, torch.bfloat16, "x_perm"),
+          _ptr(w_gate_up.data, torch.bfloat16, "w_gate_up"), _ptr(counts, torch.int32, "counts", (E,)),
+          _ptr(offsets, torch.int32, "offsets", (E + 1,)), E, H, I, P_max,
+          _ptr(h, torch.bfloat16, "h", (P_max, I)), _stream(stream))
+    return h
+
+
+def grouped_glu_gemm_gather_tiled(x, row_token, w_gate_up: TiledWeights, counts, offsets, h=None, stream=None):
+    """grouped_glu_gemm_gather with the weights and h in tiled order (x row-major)."""
+    T, H = x.shape
+    P_max = row_token.shape[0]
+    E, two_i, H2 = w_gate_up.shape
+    I = two_i // 2
+    if H2 != H or two_i != 2 * I:
+        raise ValueError("w_gate_up must be [E, 2I, H]")
+    if h is None:
+        h = torch.empty((P_max, I), dtype=torch.bfloat16, device=x.device)
+    _call("moe_grouped_glu_gemm_gather_tiled", _ptr(x, torch.bfloat16, "x"),
+          _ptr(row_token, torch.int32, "row_token", (P_max,)),
+          _ptr(w_gate_up.data, torch.bfloat16, "w_gate_up"), _ptr(counts, torch.int32, "counts", (E,)),
+          _ptr(offsets, torch.int32, "offsets", (E + 1,)), T, E, H, I, P_max,
+          _ptr(h, torch.bfloat16, "h", (P_max, I)), _stream(stream))
+    return h
+
+
+def grouped_down_gemm_tiled(h, w_down: TiledWeights, counts, offsets, y=None, stream=None):
+    """grouped_down_gemm with h and the weights in tiled order; y row-major."""
+    P_max, I = h.shape
+    E, H, I2 = w_down.shape
+    if I2 != I:
+        raise ValueError("w_down must be [E, H, I]")
+    if y is None:
+        y = torch.empty((P_max, H), dtype=torch.bfloat16, device=h.device)
+    _call("moe_grouped_down_gemm_tiled", _ptr(h, torch.bfloat16, "h"),
+          _ptr(w_down.data, torch.bfloat16, "w_down"), _ptr(counts, torch.int32, "counts", (E,)),
+          _ptr(offsets, torch.int32, "offsets", (E + 1,)), E, H, I, P_max,
+          _ptr(y, torch.bfloat16, "y", (P_max, H)), _stream(stream))
+    return y
+
+
 # ---- FP8 expert weights ----------------------------------------------------------------
 
 @dataclass
@@ -531,13 +634,18 @@ class MoELayer:
     fused_gather=True runs the permute without its gather and the gate/up GEMM
     reading token rows in place (moe_grouped_glu_gemm_gather); no x_perm exists.
     Weights are bf16 tensors or FP8Weights (from quantize_fp8), which select the
-    FP8-weight GEMMs."""
+    FP8-weight GEMMs. tiled=True runs the row-pair tiled calls: weights must be
+    TiledWeights (tile_weights), x_perm and h are kept in tiled order, and P_max
+    is rounded up to even."""
 
     def __init__(self, T: int, H: int, E: int, k: int, I: int, align: int = 32, device="cuda",
-                 fused_gather: bool = False):
+                 fused_gather: bool = False, tiled: bool = False):
         self.T, self.H, self.E, self.k, self.I, self.align = T, H, E, k, I, align
         self.fused_gather = fused_gather
+        self.tiled = tiled
         self.P_max = padded_rows_max(T, k, E, align)
+        if tiled:
+            self.P_max = even_rows(self.P_max)
         dev = torch.device(device)
         self.topk_idx = torch.empty((T, k), dtype=torch.int32, device=dev)
         self.topk_w = torch.empty((T, k), dtype=torch.float32, device=dev)
@@ -549,10 +657,21 @@ class MoELayer:
         self.out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
 
     def __call__(self, x, logits, w_gate_up, w_down, stream=None):
+        tiled_w = isinstance(w_gate_up, TiledWeights), isinstance(w_down, TiledWeights)
+        if tiled_w != (self.tiled, self.tiled):
+            raise ValueError("a tiled layer takes TiledWeights for both weights, a row-major one neither")
         route_topk(logits, self.k, self.topk_idx, self.topk_w, stream=stream)
         permute(x, self.topk_idx, self.E, self.align, self.P_max, out=self.layout,
-                workspace=self.workspace, stream=stream, gather=not self.fused_gather)
+                workspace=self.workspace, stream=stream, gather=not self.fused_gather, tiled=self.tiled)
         L = self.layout
+        if self.tiled:
+            if self.fused_gather:
+                grouped_glu_gemm_gather_tiled(x, L.row_token, w_gate_up, L.counts, L.offsets, h=self.h, stream=stream)
+            else:
+                grouped_glu_gemm_tiled(L.x_perm, w_gate_up, L.counts, L.offsets, h=self.h, stream=stream)
+            grouped_down_gemm_tiled(self.h, w_down, L.counts, L.offsets, y=self.y, stream=stream)
+            combine(self.y, L.route_row, self.topk_w, out=self.out, stream=stream)
+            return self.out
         fp8_gu, fp8_d = isinstance(w_gate_up, FP8Weights), isinstance(w_down, FP8Weights)
         if self.fused_gather:
             glu = grouped_glu_gemm_gather_fp8w if fp8_gu else grouped_glu_gemm_gather

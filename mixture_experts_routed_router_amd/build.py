@@ -17,7 +17,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 SOURCES = ["api.hip", "route_topk.hip", "permute.hip", "grouped_gemm.hip", "grouped_gemm_small.hip",
-           "combine.hip", "quantize.hip", "backward.hip", "wgrad.hip", "router.hip", "probes.hip", "debug.hip", "fused_layer.hip"]
+           "combine.hip", "quantize.hip", "backward.hip", "wgrad.hip", "router.hip", "probes.hip", "debug.hip", "fused_layer.hip",
+           "tiled.hip"]
 LIB_NAME = "libmoe_mi355x.so"
 DEBUG_LIB_NAME = "libmoe_mi355x_debug.so"
 ARCH = "gfx950"

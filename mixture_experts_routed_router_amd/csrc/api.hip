@@ -13,7 +13,14 @@ size_t route_hist_workspace_bytes(int64_t T, int E);
 hipError_t launch_permute_from_hist(const uint16_t*, const int32_t*, int64_t, int, int, int, int, int64_t, int32_t*,
                                    int32_t*, int32_t*, int32_t*, uint16_t*, void*, hipStream_t);
 hipError_t launch_permute(const uint16_t*, const int32_t*, int64_t, int, int, int, int, int64_t,
-                          int32_t*, int32_t*, int32_t*, int32_t*, uint16_t*, void*, hipStream_t);
+                          int32_t*, int32_t*, int32_t*, int32_t*, uint16_t*, void*, bool, hipStream_t);
+hipError_t launch_tile_rows(const uint16_t*, int64_t, int, uint16_t*, bool, hipStream_t);
+hipError_t launch_grouped_glu_gemm_tiled(const uint16_t*, const uint16_t*, const int32_t*, int, int, int, uint16_t*,
+                                         int, hipStream_t);
+hipError_t launch_grouped_glu_gemm_gather_tiled(const uint16_t*, const int32_t*, const uint16_t*, const int32_t*, int,
+                                                int, int, uint16_t*, int, hipStream_t);
+hipError_t launch_grouped_down_gemm_tiled(const uint16_t*, const uint16_t*, const int32_t*, int, int, int, uint16_t*,
+                                          int, hipStream_t);
 size_t permute_workspace_bytes(int64_t R, int E);
 size_t permute_scratch_bytes();
 hipError_t launch_permute_noalloc(const uint16_t*, const int32_t*, int64_t, int, int, int, int, int64_t, int32_t*,
@@ -268,9 +275,56 @@ moe_status moe_permute(const moe_bf16* x, const int32_t* topk_idx, int64_t T, in
         return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", workspace_bytes, ws);
     DEBUG_CHECK(moe::debug_check_ids(topk_idx, T, k, E, (hipStream_t)stream));
     return hip_status(moe::launch_permute(x, topk_idx, T, H, E, k, align, P_max, expert_counts,
-                                          expert_offsets, route_row, row_token, x_perm, workspace,
+                                          expert_offsets, route_row, row_token, x_perm, workspace, false,
                                           (hipStream_t)stream),
                       "moe_permute launch");
+}
+
+// ---- row-pair tiled layouts (tiled.hip) ------------------------------------------------
+
+static moe_status check_even_pmax(int64_t P_max) {
+    if (P_max & 1) return fail(MOE_ERR_INVALID_SHAPE, "P_max=%lld must be even for row-pair tiled rows", (long long)P_max);
+    return MOE_OK;
+}
+
+static moe_status tile_or_untile(const moe_bf16* src, int64_t rows, int32_t cols, moe_bf16* dst, bool to_tiled,
+                                 moe_stream_t stream) {
+    REQUIRE_PTR_UNLESS_EMPTY(src, rows == 0);
+    REQUIRE_PTR_UNLESS_EMPTY(dst, rows == 0);
+    if (rows < 0 || (rows & 1)) return fail(MOE_ERR_INVALID_SHAPE, "rows=%lld must be even and >= 0", (long long)rows);
+    if (cols < 32 || cols % 32 != 0) return fail(MOE_ERR_INVALID_SHAPE, "cols=%d must be a positive multiple of 32", cols);
+    if (rows == 0) return ok();  // nothing to do, nothing enqueued
+    if (src == dst) return fail(MOE_ERR_INVALID_VALUE, "src and dst must not be the same buffer");
+    return hip_status(moe::launch_tile_rows(src, rows, cols, dst, to_tiled, (hipStream_t)stream),
+                      to_tiled ? "moe_tile_rows launch" : "moe_untile_rows launch");
+}
+
+moe_status moe_tile_rows(const moe_bf16* src, int64_t rows, int32_t cols, moe_bf16* dst, moe_stream_t stream) {
+    return tile_or_untile(src, rows, cols, dst, true, stream);
+}
+
+moe_status moe_untile_rows(const moe_bf16* src, int64_t rows, int32_t cols, moe_bf16* dst, moe_stream_t stream) {
+    return tile_or_untile(src, rows, cols, dst, false, stream);
+}
+
+moe_status moe_permute_tiled(const moe_bf16* x, const int32_t* topk_idx, int64_t T, int32_t H, int32_t E,
+                             int32_t k, int32_t align, int64_t P_max, int32_t* expert_counts,
+                             int32_t* expert_offsets, int32_t* route_row, int32_t* row_token,
+                             moe_bf16* x_perm, void* workspace, size_t workspace_bytes,
+                             moe_stream_t stream) {
+    moe_status s = check_permute(x, topk_idx, T, H, E, k, align, P_max, expert_counts, expert_offsets, route_row,
+                                 row_token, x_perm);
+    if (s != MOE_OK) return s;
+    if ((s = check_even_pmax(P_max)) != MOE_OK) return s;
+    REQUIRE_PTR_UNLESS_EMPTY(workspace, T == 0);
+    const size_t ws = moe::permute_workspace_bytes(T * k, E);
+    if (workspace_bytes < ws)
+        return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", workspace_bytes, ws);
+    DEBUG_CHECK(moe::debug_check_ids(topk_idx, T, k, E, (hipStream_t)stream));
+    return hip_status(moe::launch_permute(x, topk_idx, T, H, E, k, align, P_max, expert_counts,
+                                          expert_offsets, route_row, row_token, x_perm, workspace, true,
+                                          (hipStream_t)stream),
+                      "moe_permute_tiled launch");
 }
 
 moe_status moe_route_hist_workspace_size(int64_t T, int32_t k, int32_t E, size_t* bytes) {
@@ -461,6 +515,45 @@ moe_status moe_grouped_down_gemm(const moe_bf16* h, const moe_bf16* w_down,
     DEBUG_CHECK(moe::debug_check_layout(expert_counts, expert_offsets, E, P_max, (hipStream_t)stream));
     return hip_status(launch_down(h, w_down, nullptr, expert_offsets, E, H, I, P_max, y, (hipStream_t)stream),
                       "moe_grouped_down_gemm launch");
+}
+
+moe_status moe_grouped_glu_gemm_tiled(const moe_bf16* x_perm, const moe_bf16* w_gate_up,
+                                      const int32_t* expert_counts, const int32_t* expert_offsets, int32_t E,
+                                      int32_t H, int32_t I, int64_t P_max, moe_bf16* h, moe_stream_t stream) {
+    moe_status s = check_gemm(x_perm, w_gate_up, expert_counts, expert_offsets, E, H, I, P_max, h);
+    if (s != MOE_OK) return s;
+    if ((s = check_even_pmax(P_max)) != MOE_OK) return s;
+    DEBUG_CHECK(moe::debug_check_layout(expert_counts, expert_offsets, E, P_max, (hipStream_t)stream));
+    return hip_status(moe::launch_grouped_glu_gemm_tiled(x_perm, w_gate_up, expert_offsets, E, H, I, h, (int)P_max,
+                                                         (hipStream_t)stream),
+                      "moe_grouped_glu_gemm_tiled launch");
+}
+
+moe_status moe_grouped_glu_gemm_gather_tiled(const moe_bf16* x, const int32_t* row_token,
+                                             const moe_bf16* w_gate_up, const int32_t* expert_counts,
+                                             const int32_t* expert_offsets, int64_t T, int32_t E, int32_t H,
+                                             int32_t I, int64_t P_max, moe_bf16* h, moe_stream_t stream) {
+    moe_status s = check_gemm(x, w_gate_up, expert_counts, expert_offsets, E, H, I, P_max, h);
+    if (s != MOE_OK) return s;
+    if ((s = check_even_pmax(P_max)) != MOE_OK) return s;
+    if ((s = check_gather(row_token, T, H)) != MOE_OK) return s;
+    DEBUG_CHECK(moe::debug_check_layout(expert_counts, expert_offsets, E, P_max, (hipStream_t)stream));
+    DEBUG_CHECK(moe::debug_check_rows(row_token, P_max, -1, T, 6, (hipStream_t)stream));
+    return hip_status(moe::launch_grouped_glu_gemm_gather_tiled(x, row_token, w_gate_up, expert_offsets, E, H, I, h,
+                                                                (int)P_max, (hipStream_t)stream),
+                      "moe_grouped_glu_gemm_gather_tiled launch");
+}
+
+moe_status moe_grouped_down_gemm_tiled(const moe_bf16* h, const moe_bf16* w_down, const int32_t* expert_counts,
+                                       const int32_t* expert_offsets, int32_t E, int32_t H, int32_t I,
+                                       int64_t P_max, moe_bf16* y, moe_stream_t stream) {
+    moe_status s = check_gemm(h, w_down, expert_counts, expert_offsets, E, H, I, P_max, y);
+    if (s != MOE_OK) return s;
+    if ((s = check_even_pmax(P_max)) != MOE_OK) return s;
+    DEBUG_CHECK(moe::debug_check_layout(expert_counts, expert_offsets, E, P_max, (hipStream_t)stream));
+    return hip_status(moe::launch_grouped_down_gemm_tiled(h, w_down, expert_offsets, E, H, I, y, (int)P_max,
+                                                          (hipStream_t)stream),
+                      "moe_grouped_down_gemm_tiled launch");
 }
 
 moe_status moe_quantize_fp8(const moe_bf16* w, int64_t E, int32_t R, int32_t K, uint8_t* w8,

@@ -4,7 +4,7 @@
 
 namespace moe {
 
-template <bool GLU, bool GATHER, bool W8, bool SWB>
+template <bool GLU, bool GATHER, bool W8, bool SWB, bool PK = false>
 __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_kernel(
     const uint16_t* __restrict__ A, const int32_t* __restrict__ row_token,
     const void* __restrict__ W, const float* __restrict__ w_scale, const int32_t* __restrict__ offsets,
@@ -17,8 +17,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_kernel(
     __shared__ int32_t scan_tmp[kWaves];
     __shared__ __attribute__((aligned(16))) int32_t tok_lds[GATHER ? 2 * kWaves * kTokSlots : 1];
     const GemmShared sh{lds, tile_start, seg_start, scan_tmp, tok_lds};
-    grouped_gemm_body<GLU, GATHER, W8, SWB>(sh, A, row_token, W, w_scale, offsets, E, K, N, C, gu, glu_limit,
-                                            rows_max, blockIdx.x, gridDim.x);
+    grouped_gemm_body<GLU, GATHER, W8, SWB, PK>(sh, A, row_token, W, w_scale, offsets, E, K, N, C, gu, glu_limit,
+                                                rows_max, blockIdx.x, gridDim.x);
 }
 
 static int g_cu_count[64];
@@ -81,6 +81,34 @@ hipError_t launch_grouped_down_gemm(const uint16_t* h, const void* w_d, const fl
         hipLaunchKernelGGL((grouped_gemm_kernel<false, false, false, false>), dim3(persistent_grid()),
                            dim3(kGemmThreads), 0, stream, h, (const int32_t*)nullptr, w_d, scale,
                            offsets, E, I, H, y, (const uint16_t*)nullptr, INFINITY, rows_max);
+    return hipGetLastError();
+}
+
+// Row-pair tiled operands (bf16): the weights and, unless gathered, A are stored in
+// 2 x 32 blocks (the layout moe_tile_rows writes); the gate/up GEMM writes h in the
+// same layout, the down GEMM writes y row-major.
+hipError_t launch_grouped_glu_gemm_tiled(const uint16_t* x_perm_t, const uint16_t* w_gu_t, const int32_t* offsets,
+                                         int E, int H, int I, uint16_t* h_t, int rows_max, hipStream_t stream) {
+    hipLaunchKernelGGL((grouped_gemm_kernel<true, false, false, false, true>), dim3(persistent_grid()),
+                       dim3(kGemmThreads), 0, stream, x_perm_t, (const int32_t*)nullptr, (const void*)w_gu_t,
+                       (const float*)nullptr, offsets, E, H, I, h_t, (const uint16_t*)nullptr, INFINITY, rows_max);
+    return hipGetLastError();
+}
+
+hipError_t launch_grouped_glu_gemm_gather_tiled(const uint16_t* x, const int32_t* row_token, const uint16_t* w_gu_t,
+                                                const int32_t* offsets, int E, int H, int I, uint16_t* h_t,
+                                                int rows_max, hipStream_t stream) {
+    hipLaunchKernelGGL((grouped_gemm_kernel<true, true, false, false, true>), dim3(persistent_grid()),
+                       dim3(kGemmThreads), 0, stream, x, row_token, (const void*)w_gu_t, (const float*)nullptr,
+                       offsets, E, H, I, h_t, (const uint16_t*)nullptr, INFINITY, rows_max);
+    return hipGetLastError();
+}
+
+hipError_t launch_grouped_down_gemm_tiled(const uint16_t* h_t, const uint16_t* w_d_t, const int32_t* offsets,
+                                          int E, int H, int I, uint16_t* y, int rows_max, hipStream_t stream) {
+    hipLaunchKernelGGL((grouped_gemm_kernel<false, false, false, false, true>), dim3(persistent_grid()),
+                       dim3(kGemmThreads), 0, stream, h_t, (const int32_t*)nullptr, (const void*)w_d_t,
+                       (const float*)nullptr, offsets, E, I, H, y, (const uint16_t*)nullptr, INFINITY, rows_max);
     return hipGetLastError();
 }
 

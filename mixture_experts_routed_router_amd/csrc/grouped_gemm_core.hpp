@@ -255,7 +255,13 @@ struct StageOffsets {
 // row_token[p] -- the permute's gather folded into the loads. `tok` holds this
 // thread's token of each of its rows (issue_token_loads); a pad row (-1) reads
 // token 0 instead, its results are never read.
-template <bool GLU, bool GATHER, bool W8>
+//
+// PK (row-pair tiled operands): A (unless gathering) and bf16 W are stored as 2 x 32
+// blocks, row pair q and k block b at 128 * (q * K/32 + b) bytes, the even row's 64
+// bytes first. A stage's pieces of two neighbouring rows then fill one 128-byte
+// line instead of halves of two. The offsets here are those of stage 0; stage s
+// adds 128 s bytes (A: through the SGPR base, W: through the lane offset).
+template <bool GLU, bool GATHER, bool W8, bool PK = false>
 __device__ __forceinline__ StageOffsets stage_offsets(const TileArgs& ta, int K, int N, int wave, int lane,
                                                       const uint32_t (&tok)[kPiecesPerThread]) {
     StageOffsets o;
@@ -267,7 +273,13 @@ __device__ __forceinline__ StageOffsets stage_offsets(const TileArgs& ta, int K,
         if (GATHER) ar = (int32_t)tok[i] < 0 ? 0u : tok[i];
         else ar = (uint32_t)(r < ta.rows_valid ? r : 0);
         // 32-bit byte offset: the host guarantees rows * K * 2 < 2^32 (T * H * 2 when gathering)
-        o.a[i] = (ar * (uint32_t)K + (uint32_t)(piece * 8)) * 2u;
+        if (PK && !GATHER) {
+            // row ar of the tile is layout row row0 + ar; a_tile points at row0's pair
+            const uint32_t rr = ar + (uint32_t)(ta.row0 & 1);
+            o.a[i] = (rr >> 1) * (uint32_t)K * 4u + (rr & 1u) * 64u + (uint32_t)piece * 16u;
+        } else {
+            o.a[i] = (ar * (uint32_t)K + (uint32_t)(piece * 8)) * 2u;
+        }
         int wr;
         if (GLU) {
             const int c = ta.nt * 128 + (r & 127);  // output column of this W row
@@ -277,7 +289,10 @@ __device__ __forceinline__ StageOffsets stage_offsets(const TileArgs& ta, int K,
             const int c = ta.nt * BN + r;
             wr = c < N ? c : N - 1;
         }
-        if (!W8) o.b[i] = (uint32_t)(((int64_t)wr * K + piece * 8) * 2);
+        if (!W8) {
+            if (PK) o.b[i] = (uint32_t)(wr >> 1) * (uint32_t)K * 4u + (uint32_t)(wr & 1) * 64u + (uint32_t)piece * 16u;
+            else o.b[i] = (uint32_t)(((int64_t)wr * K + piece * 8) * 2);
+        }
     }
     if (W8) {
         // FP8 B: wave w fills W rows 32w .. 32w+31 of the stage, lane l row
@@ -324,16 +339,18 @@ __device__ __forceinline__ void read_tokens(const int32_t* region, int lane,
     for (int i = 0; i < kPiecesPerThread; ++i) tok[i] = (uint32_t)region[RPB * i + lane / PR];
 }
 
-// This thread's share of one stage: A and B pieces of k-stage kt of a tile into ring slot `slot`.
+// This thread's share of one stage: A and B pieces of k-stage kt of a tile into ring
+// slot `slot`. bx: bytes added to every bf16 W piece's offset (row-pair tiled W:
+// 64 per stage, the half of its 128-byte stride the SGPR base does not take).
 template <bool W8>
 __device__ __forceinline__ void issue_stage(uint32_t lds0, int slot, int wave, const uint16_t* ga,
-                                            const char* gb, const StageOffsets& o) {
+                                            const char* gb, const StageOffsets& o, uint32_t bx) {
     const uint32_t sa = lds0 + (uint32_t)(slot * kStageElems * 2);
     const uint32_t sb = sa + kAElems * 2;
 #pragma unroll
     for (int i = 0; i < kPiecesPerThread; ++i) {
         dma16(sa + (kPiecesPerThread * wave + i) * 1024, ga, o.a[i]);
-        if (!W8) dma16(sb + (kPiecesPerThread * wave + i) * 1024, gb, o.b[i]);
+        if (!W8) dma16(sb + (kPiecesPerThread * wave + i) * 1024, gb, o.b[i] + bx);
     }
     if (W8) dma16(sb + wave * 1024, gb, o.b[0]);
 }
@@ -380,7 +397,7 @@ struct WaveCtx {
 // an 8-byte store. This wave's stores of the previous tile (s_prev of them) were
 // issued after the prefetched stages; vector-memory operations complete in issue
 // order, so a wait for a prefetched stage may leave those stores in flight.
-template <bool GLU, bool GATHER, bool W8, bool SWB, int NV>
+template <bool GLU, bool GATHER, bool W8, bool SWB, bool PK, int NV>
 __device__ __forceinline__ int run_tile(const WaveCtx& w, const TileArgs& ta, const TileArgs& tn,
                                         int base, bool prefetched, bool pf_next, int s_prev,
                                         const int32_t* __restrict__ row_token, int tb) {
@@ -406,9 +423,16 @@ __device__ __forceinline__ int run_tile(const WaveCtx& w, const TileArgs& ta, co
         }
         read_tokens(tok_cur, lane, tok);
     }
-    const StageOffsets oc = stage_offsets<GLU, GATHER, W8>(ta, K, N, wave, lane, tok);
+    const StageOffsets oc = stage_offsets<GLU, GATHER, W8, PK>(ta, K, N, wave, lane, tok);
     constexpr int LPS = W8 ? kLoadsPerStageW8 : kLoadsPerStage;  // this thread's loads per stage
     constexpr int WB = W8 ? 1 : 2;                                // bytes per weight
+    // per k stage: A elements and W bytes the SGPR bases move, and bytes added to W's
+    // lane offsets (row-pair tiled operands move 128 bytes per stage)
+    constexpr int AST = (PK && !GATHER) ? 2 * BK : BK;
+    // (the gathering variant keeps W's base stride and adds the rest per lane: with the
+    // full stride in the base, the compiler runs out of SGPRs for it)
+    constexpr int WST = (PK && !W8 && !GATHER) ? 4 * BK : BK * WB;
+    constexpr uint32_t WX = (PK && !W8 && GATHER) ? 64u : 0u;
 
     // LDS B row of each of this wave's 32-column blocks. GLU: the first half of
     // the blocks are gate columns, the second half the matching up columns.
@@ -443,11 +467,12 @@ __device__ __forceinline__ int run_tile(const WaveCtx& w, const TileArgs& ta, co
         const int s_ = (s);                                                                       \
         const int slot_ = (base + s_) & (STAGES - 1);                                             \
         if (s_ < nk)                                                                              \
-            issue_stage<W8>(w.lds0, slot_, wave, ta.a_tile + s_ * BK, ta.w_exp + s_ * BK * WB, oc); \
+            issue_stage<W8>(w.lds0, slot_, wave, ta.a_tile + s_ * AST, ta.w_exp + s_ * WST, oc, \
+                            (uint32_t)s_ * WX);                                           \
         else if (pf_next) {                                                                       \
-            const StageOffsets on_ = stage_offsets<GLU, GATHER, W8>(tn, K, N, wave, lane, tkn);    \
-            issue_stage<W8>(w.lds0, slot_, wave, tn.a_tile + (s_ - nk) * BK,                      \
-                            tn.w_exp + (s_ - nk) * BK * WB, on_);                                 \
+            const StageOffsets on_ = stage_offsets<GLU, GATHER, W8, PK>(tn, K, N, wave, lane, tkn); \
+            issue_stage<W8>(w.lds0, slot_, wave, tn.a_tile + (s_ - nk) * AST,                     \
+                            tn.w_exp + (s_ - nk) * WST, on_, (uint32_t)(s_ - nk) * WX);       \
         }                                                                                         \
     } while (0)
 #define MOE_LOAD_STAGE_FRAGS(stage)                                                           \
@@ -548,7 +573,8 @@ __device__ __forceinline__ int run_tile(const WaveCtx& w, const TileArgs& ta, co
         /* stage kt+4, and read stage kt+1 */                                                     \
         if (STEADY) {                                                                             \
             issue_stage<W8>(w.lds0, (base + (kt) + STAGES) & (STAGES - 1), wave,                  \
-                            ta.a_tile + ((kt) + STAGES) * BK, ta.w_exp + ((kt) + STAGES) * BK * WB, oc); \
+                            ta.a_tile + ((kt) + STAGES) * AST, ta.w_exp + ((kt) + STAGES) * WST, oc, \
+                            (uint32_t)((kt) + STAGES) * WX);                                      \
             MOE_LOAD_STAGE_FRAGS((kt) + 1);                                                       \
         } else {                                                                                  \
             MOE_WAIT_TOKENS(kt, nk - STAGES, STAGES);                                             \
@@ -563,8 +589,9 @@ __device__ __forceinline__ int run_tile(const WaveCtx& w, const TileArgs& ta, co
         MOE_LOAD_STAGE_FRAGS(kt);                                                                 \
         if (STEADY) {                                                                             \
             issue_stage<W8>(w.lds0, (base + (kt) + STAGES - 1) & (STAGES - 1), wave,              \
-                            ta.a_tile + ((kt) + STAGES - 1) * BK,                                 \
-                            ta.w_exp + ((kt) + STAGES - 1) * BK * WB, oc);                        \
+                            ta.a_tile + ((kt) + STAGES - 1) * AST,                                \
+                            ta.w_exp + ((kt) + STAGES - 1) * WST, oc,                         \
+                            (uint32_t)((kt) + STAGES - 1) * WX);                                  \
             wait_vmcnt<2 * LPS>();                                                                \
         } else {                                                                                  \
             MOE_WAIT_TOKENS(kt, nk - STAGES + 1, STAGES - 1);                                     \
@@ -626,8 +653,15 @@ __device__ __forceinline__ int run_tile(const WaveCtx& w, const TileArgs& ta, co
         const uint16_t* gu_tile = ta.gu_tile + zero;
         const QuadSel qs = quad_sel(ln);
         const int out_row = (ln >> 5) * 4 + (ln & 3);  // this lane's row in an 8-row group
-        // byte offset of this lane's 8 bytes from the group's (row 0, column 0)
-        const uint32_t out_off = (uint32_t)((out_row * n_cols + ((ln & 31) >> 2) * 4) * 2);
+        // byte offset of this lane's 8 bytes from the group's (row 0, column 0).
+        // PK (GLU output): h is row-pair tiled and c_tile points at row0's pair; the
+        // group of tile rows r0.. (r0 even) and columns cb.. starts r0 * N + 2 cb
+        // elements in, and this lane's row lies lp = (row0 & 1) + out_row rows past
+        // it: pair lp / 2 (2N elements each), half lp % 2 of each 2 x 32 block
+        const int lp = (ta.row0 & 1) + out_row;
+        const uint32_t out_off =
+            PK && GLU ? (uint32_t)(((lp >> 1) * 2 * n_cols + (lp & 1) * 32 + ((ln & 31) >> 2) * 4) * 2)
+                      : (uint32_t)((out_row * n_cols + ((ln & 31) >> 2) * 4) * 2);
         constexpr int OB = GLU ? NBN / 2 : NBN;    // 32-column output blocks per wave
         const int col0 = GLU ? nt * 128 + wn * (WTN / 2) : nt * BN + wn * WTN;
         if (GLU) {
@@ -673,7 +707,7 @@ __device__ __forceinline__ int run_tile(const WaveCtx& w, const TileArgs& ta, co
                             }
                             uint32_t w0, w1;
                             quad_transpose_bf16(v[0], v[1], v[2], v[3], qs, w0, w1);
-                            char* grp0 = (char*)(c_tile + ((int64_t)r0 * n_cols + cb));
+                            char* grp0 = (char*)(c_tile + ((int64_t)r0 * n_cols + (PK ? 2 * cb : cb)));
                             if (out_row < rows_valid - r0)
                                 *(uint2*)(grp0 + out_off) = make_uint2(w0, w1);
                             ++stores;
@@ -765,13 +799,14 @@ struct GemmShared {
 
 // One workgroup's share of a grouped GEMM launch: workgroup `blk` of `nblk`
 // (a multiple of the 8 XCDs; workgroup b runs on XCD b % 8).
-template <bool GLU, bool GATHER, bool W8, bool SWB>
+template <bool GLU, bool GATHER, bool W8, bool SWB, bool PK = false>
 __device__ __forceinline__ void grouped_gemm_body(
     const GemmShared& sh, const uint16_t* __restrict__ A, const int32_t* __restrict__ row_token,
     const void* __restrict__ W, const float* __restrict__ w_scale, const int32_t* __restrict__ offsets,
     int E, int K, int N, uint16_t* __restrict__ C, const uint16_t* __restrict__ gu, float glu_limit,
     int rows_max, int blk, int nblk) {
     static_assert(!SWB || (!GLU && !GATHER && !W8), "the SwiGLU backward epilogue follows the plain bf16 GEMM");
+    static_assert(!PK || !SWB, "row-pair tiled operands are for the forward GEMMs");
     uint16_t* lds = sh.lds;
     int32_t* tile_start = sh.tile_start;
     int32_t* seg_start = sh.seg_start;
@@ -872,11 +907,13 @@ __device__ __forceinline__ void grouped_gemm_body(
         const int bq = nb / m, br = nb - bq * m;  // row tile mt has bq + (mt < br) blocks
         const int row0 = seg0 + 32 * (mt * bq + min(mt, br));
         TileArgs ta;
-        ta.a_tile = GATHER ? A : A + (int64_t)row0 * K;
+        // PK: A (and a GLU's h) tiled in row pairs; the tile's base is row0's pair
+        const int64_t rowb = PK ? (int64_t)(row0 >> 1) * 2 : (int64_t)row0;
+        ta.a_tile = GATHER ? A : A + rowb * K;
         ta.row0 = row0;
         ta.w_exp = (const char*)W + (int64_t)e * w_stride;
         ta.w_scale = W8 ? w_scale + (int64_t)e * (NW / 64) : w_scale;
-        ta.c_tile = C + (int64_t)row0 * (SWB ? 2 * N : N);
+        ta.c_tile = C + (PK && GLU ? rowb : (int64_t)row0) * (SWB ? 2 * N : N);
         ta.gu_tile = SWB ? gu + (int64_t)row0 * 2 * N : gu;
         ta.nt = nt;
         ta.rows_valid = min(32 * (bq + (mt < br ? 1 : 0)), seg1 - row0);
@@ -901,11 +938,11 @@ __device__ __forceinline__ void grouped_gemm_body(
         const bool pf_next = has_next && cross;
         int s;
         switch (cur.nvb) {
-            case 4: s = run_tile<GLU, GATHER, W8, SWB, 4>(w, cur, nxt, base, prefetched, pf_next, s_prev, row_token, tb); break;
-            case 3: s = run_tile<GLU, GATHER, W8, SWB, 3>(w, cur, nxt, base, prefetched, pf_next, s_prev, row_token, tb); break;
-            case 2: s = run_tile<GLU, GATHER, W8, SWB, 2>(w, cur, nxt, base, prefetched, pf_next, s_prev, row_token, tb); break;
-            case 1: s = run_tile<GLU, GATHER, W8, SWB, 1>(w, cur, nxt, base, prefetched, pf_next, s_prev, row_token, tb); break;
-            default: s = run_tile<GLU, GATHER, W8, SWB, 0>(w, cur, nxt, base, prefetched, pf_next, s_prev, row_token, tb); break;
+            case 4: s = run_tile<GLU, GATHER, W8, SWB, PK, 4>(w, cur, nxt, base, prefetched, pf_next, s_prev, row_token, tb); break;
+            case 3: s = run_tile<GLU, GATHER, W8, SWB, PK, 3>(w, cur, nxt, base, prefetched, pf_next, s_prev, row_token, tb); break;
+            case 2: s = run_tile<GLU, GATHER, W8, SWB, PK, 2>(w, cur, nxt, base, prefetched, pf_next, s_prev, row_token, tb); break;
+            case 1: s = run_tile<GLU, GATHER, W8, SWB, PK, 1>(w, cur, nxt, base, prefetched, pf_next, s_prev, row_token, tb); break;
+            default: s = run_tile<GLU, GATHER, W8, SWB, PK, 0>(w, cur, nxt, base, prefetched, pf_next, s_prev, row_token, tb); break;
         }
         if (!has_next) break;
         s_prev = s;

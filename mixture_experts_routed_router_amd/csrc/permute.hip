@@ -141,11 +141,57 @@ __global__ __launch_bounds__(kCopyThreads) void permute_copy_rows_kernel(
     }
 }
 
+// The gather into the row-pair tiled layout (tiled.hip), pair-major: one
+// wavefront per pair of layout rows (2q, 2q+1). The pair's tiled block run is 2H
+// contiguous elements in which 16-byte slot i holds piece (i/8)*4 + i%4 of row
+// 2q + (i/4)%2, so each store instruction writes 1 KB of whole 128-byte lines;
+// the two token rows (row_token, -1: zeros) are read 512 contiguous bytes at a
+// time. Every pair below offsets[E] is written whole, pad rows included (the
+// pair holding row offsets[E] - 1 gets a zero second row when offsets[E] is
+// odd); pairs past it are not touched. Token rows are read once per route here
+// (k times per token) -- from the caches, as x is far smaller than the layout.
+template <bool NT>
+__global__ __launch_bounds__(kCopyThreads) void permute_copy_pairs_kernel(
+    const uint4* __restrict__ x, const int32_t* __restrict__ row_token, const int32_t* __restrict__ offsets,
+    int E, int ppr, int64_t npairs, uint4* __restrict__ x_perm) {
+    MOE_DEBUG_GUARD();
+    const int lane = lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int64_t q = (int64_t)blockIdx.x * kCopyWaves + wave;
+    if (q >= npairs) return;
+    const int64_t used = offsets[E];
+    if (2 * q >= used) return;
+    const int32_t t0 = __builtin_amdgcn_readfirstlane(row_token[2 * q]);
+    const int32_t t1 = __builtin_amdgcn_readfirstlane(row_token[2 * q + 1]);
+    const uint4* src0 = x + (int64_t)(t0 < 0 ? 0 : t0) * ppr;
+    const uint4* src1 = x + (int64_t)(t1 < 0 ? 0 : t1) * ppr;
+    uint4* dst = x_perm + q * 2 * ppr;
+    const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+    const int n = 2 * ppr;  // 16-byte slots of the pair
+    for (int i0 = 0; i0 < n; i0 += kWave * kCopyUnroll) {
+        uint4 v[kCopyUnroll];
+#pragma unroll
+        for (int u = 0; u < kCopyUnroll; ++u) {
+            const int i = i0 + u * kWave + lane;
+            const bool second = (i >> 2) & 1;
+            const int c = ((i >> 3) << 2) | (i & 3);
+            const int32_t t = second ? t1 : t0;
+            v[u] = z;
+            if (i < n && t >= 0) v[u] = *((second ? src1 : src0) + c);
+        }
+#pragma unroll
+        for (int u = 0; u < kCopyUnroll; ++u) {
+            const int i = i0 + u * kWave + lane;
+            if (i < n) store_piece<NT>(dst + i, v[u]);
+        }
+    }
+}
+
 int64_t permute_chunks(int64_t R) { return (R + kChunk - 1) / kChunk; }
 
 hipError_t launch_permute_copy(const uint16_t* x, int64_t T, int H, int E, int k, int64_t P_max,
                                const int32_t* counts, const int32_t* offsets, const int32_t* route_row,
-                               uint16_t* x_perm, hipStream_t stream);
+                               const int32_t* row_token, uint16_t* x_perm, bool tiled, hipStream_t stream);
 
 size_t permute_workspace_bytes(int64_t R, int E) {
     const size_t b = (size_t)permute_chunks(R) * (size_t)E * sizeof(int32_t);
@@ -155,7 +201,7 @@ size_t permute_workspace_bytes(int64_t R, int E) {
 hipError_t launch_permute(const uint16_t* x, const int32_t* topk_idx, int64_t T, int H, int E,
                           int k, int align, int64_t P_max, int32_t* counts, int32_t* offsets,
                           int32_t* route_row, int32_t* row_token, uint16_t* x_perm,
-                          void* workspace, hipStream_t stream) {
+                          void* workspace, bool tiled, hipStream_t stream) {
     const int64_t R = T * k;
     const int64_t nchunks = permute_chunks(R);
     int32_t* hist = (int32_t*)workspace;
@@ -178,7 +224,7 @@ hipError_t launch_permute(const uint16_t* x, const int32_t* topk_idx, int64_t T,
                        (const int32_t*)counts, offsets, route_row, row_token, kChunk);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
-    return launch_permute_copy(x, T, H, E, k, P_max, counts, offsets, route_row, x_perm, stream);
+    return launch_permute_copy(x, T, H, E, k, P_max, counts, offsets, route_row, row_token, x_perm, tiled, stream);
 }
 
 // The permute from a histogram the routing kernel already wrote (hist [nchunks][E],
@@ -211,25 +257,38 @@ hipError_t launch_permute_from_hist(const uint16_t* x, const int32_t* topk_idx, 
                        (const int32_t*)counts, offsets, route_row, row_token, tpw * k);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
-    return launch_permute_copy(x, T, H, E, k, P_max, counts, offsets, route_row, x_perm, stream);
+    return launch_permute_copy(x, T, H, E, k, P_max, counts, offsets, route_row, row_token, x_perm, false,
+                               stream);
 }
 
 hipError_t launch_permute_copy(const uint16_t* x, int64_t T, int H, int E, int k, int64_t P_max,
                                const int32_t* counts, const int32_t* offsets, const int32_t* route_row,
-                               uint16_t* x_perm, hipStream_t stream) {
+                               const int32_t* row_token, uint16_t* x_perm, bool tiled, hipStream_t stream) {
     if (!x_perm) return hipGetLastError();  // the layout only
     const int ppr = H / 8;  // 16-byte pieces per row
     // one wavefront per token, then one workgroup per expert for its pad rows
     const int64_t token_blocks = (T + kCopyWaves - 1) / kCopyWaves;
     const dim3 grid((unsigned)(token_blocks + E));
-    if (P_max * (int64_t)H * 2 > kStreamingLayoutBytes)
-        hipLaunchKernelGGL(permute_copy_rows_kernel<true>, grid, dim3(kCopyThreads), 0, stream,
-                           (const uint4*)x, (const int32_t*)route_row, (const int32_t*)counts,
-                           (const int32_t*)offsets, T, k, ppr, token_blocks, (uint4*)x_perm);
-    else
-        hipLaunchKernelGGL(permute_copy_rows_kernel<false>, grid, dim3(kCopyThreads), 0, stream,
-                           (const uint4*)x, (const int32_t*)route_row, (const int32_t*)counts,
-                           (const int32_t*)offsets, T, k, ppr, token_blocks, (uint4*)x_perm);
+    const bool nt = P_max * (int64_t)H * 2 > kStreamingLayoutBytes;
+    if (tiled) {
+        // one wavefront per row pair (P_max is even)
+        const int64_t npairs = P_max / 2;
+        const dim3 pgrid((unsigned)((npairs + kCopyWaves - 1) / kCopyWaves));
+        if (nt)
+            hipLaunchKernelGGL(permute_copy_pairs_kernel<true>, pgrid, dim3(kCopyThreads), 0, stream,
+                               (const uint4*)x, row_token, offsets, E, ppr, npairs, (uint4*)x_perm);
+        else
+            hipLaunchKernelGGL(permute_copy_pairs_kernel<false>, pgrid, dim3(kCopyThreads), 0, stream,
+                               (const uint4*)x, row_token, offsets, E, ppr, npairs, (uint4*)x_perm);
+        return hipGetLastError();
+    }
+    auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, grid, dim3(kCopyThreads), 0, stream, (const uint4*)x, (const int32_t*)route_row,
+                           (const int32_t*)counts, (const int32_t*)offsets, T, k, ppr, token_blocks,
+                           (uint4*)x_perm);
+    };
+    if (nt) go(permute_copy_rows_kernel<true>);
+    else go(permute_copy_rows_kernel<false>);
     return hipGetLastError();
 }
 
@@ -271,7 +330,7 @@ hipError_t launch_permute_noalloc(const uint16_t* x, const int32_t* topk_idx, in
         ptr = g_scratch_ptr[dev];
     }
     return launch_permute(x, topk_idx, T, H, E, k, align, P_max, counts, offsets, route_row, row_token, x_perm,
-                          ptr, stream);
+                          ptr, false, stream);
 }
 
 }  // namespace moe

@@ -58,6 +58,12 @@ def lib():
     lib.moe_grouped_wgrad.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i64, vp, vp]
     lib.moe_router_prepare.argtypes = [vp, i32, i32, vp, vp, vp]
     lib.moe_router_topk.argtypes = [vp, vp, vp, i64, i32, i32, i32, vp, vp, vp, vp]
+    lib.moe_tile_rows.argtypes = [vp, i64, i32, vp, vp]
+    lib.moe_untile_rows.argtypes = [vp, i64, i32, vp, vp]
+    lib.moe_permute_tiled.argtypes = lib.moe_permute.argtypes
+    lib.moe_grouped_glu_gemm_tiled.argtypes = lib.moe_grouped_glu_gemm.argtypes
+    lib.moe_grouped_down_gemm_tiled.argtypes = lib.moe_grouped_down_gemm.argtypes
+    lib.moe_grouped_glu_gemm_gather_tiled.argtypes = lib.moe_grouped_glu_gemm_gather.argtypes
     return lib
 
 
@@ -312,3 +318,33 @@ def test_library_is_gfx950_only(path):
     assert b"gfx950" in data
     for other in (b"gfx942", b"gfx90a", b"gfx1100", b"sm_"):
         assert b"amdgcn-amd-amdhsa--" + other not in data
+
+
+def test_tiled_validation(lib):
+    """The row-pair tiled calls: whole row pairs (even rows / P_max), 32-column
+    blocks, distinct buffers; otherwise as their row-major counterparts."""
+    for fn in (lib.moe_tile_rows, lib.moe_untile_rows):
+        assert fn(None, 6, 64, FAKE, None) == NULLP
+        assert fn(FAKE, 5, 64, FAKE + 4096, None) == SHAPE          # odd rows
+        assert fn(FAKE, -2, 64, FAKE + 4096, None) == SHAPE
+        assert fn(FAKE, 6, 48, FAKE + 4096, None) == SHAPE          # cols % 32
+        assert fn(FAKE, 6, 0, FAKE + 4096, None) == SHAPE
+        assert fn(FAKE, 6, 64, FAKE, None) == VALUE                 # in place
+        assert fn(FAKE + 8, 6, 64, FAKE + 4096, None) == MISALIGNED
+        assert fn(None, 0, 64, None, None) == OK                    # nothing to do
+    P_max = 4 * 2 + 8 * 31
+    perm = lambda pm, xp=FAKE: lib.moe_permute_tiled(FAKE, FAKE, 4, 128, 8, 2, 32, pm, FAKE, FAKE, FAKE, FAKE,  # noqa: E731
+                                                      xp, FAKE, 1 << 20, None)
+    assert perm(P_max + 1) == SHAPE                                  # odd P_max
+    assert b"even" in lib.moe_last_error_message()
+    assert perm(P_max - 2) == OVERFLOW                               # below T*k + E*(align-1)
+    assert perm(P_max, xp=FAKE + 8) == MISALIGNED
+    for fn in (lib.moe_grouped_glu_gemm_tiled, lib.moe_grouped_down_gemm_tiled):
+        assert fn(FAKE, FAKE, FAKE, FAKE, 8, 128, 256, 1001, FAKE, None) == SHAPE   # odd P_max
+        assert fn(FAKE, FAKE, FAKE, FAKE, 8, 100, 256, 1000, FAKE, None) == SHAPE   # H % 64
+        assert fn(FAKE, FAKE, FAKE, FAKE, 8, 128, 256, 1000, None, None) == NULLP
+        assert fn(FAKE, FAKE + 8, FAKE, FAKE, 8, 128, 256, 1000, FAKE, None) == MISALIGNED
+    fn = lib.moe_grouped_glu_gemm_gather_tiled
+    assert fn(FAKE, FAKE, FAKE, FAKE, FAKE, 100, 8, 128, 256, 1001, FAKE, None) == SHAPE
+    assert fn(FAKE, None, FAKE, FAKE, FAKE, 100, 8, 128, 256, 1000, FAKE, None) == NULLP
+    assert fn(FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, 8, 2048, 256, 1000, FAKE, None) == OVERFLOW
