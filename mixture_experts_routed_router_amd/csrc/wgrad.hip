@@ -8,11 +8,18 @@
 // write straight into fp32 accumulators; one K-grouped GEMM launch per weight].
 // Pad rows of a segment contribute nothing: the backward zeroes them in A.
 //
-// The reduction runs over rows, which are the strided dimension of both operands,
-// so each 32-row chunk is transposed on its way into LDS: a thread loads 16 bytes
-// (8 columns) of two consecutive rows and writes the 8 (row, row+1) pairs as
-// 32-bit words at [column][row], so the MFMA fragments (8 consecutive rows of
-// one column) are single 128-bit LDS reads. Tile 256 x 256 per workgroup of eight
+// The reduction runs over rows, which are the strided dimension of both operands.
+// Each 32-row chunk goes into LDS as it is in memory ([row][column], 16-byte
+// stores of the 16-byte loads), and the MFMA fragments -- 8 consecutive rows of
+// one column -- are read transposed with gfx950's ds_read_b64_tr_b16: within each
+// group of 16 lanes, lane i receives element i % 4 of the 8-byte pieces addressed
+// by lanes i/4, i/4 + 4, i/4 + 8, i/4 + 12, so when lane q addresses row
+// kb + q/4, columns c + 4 (q % 4) .. +3, lane i gets rows kb .. kb+3 of column
+// c + i; two such reads make a fragment. (The version before this wrote the rows
+// transposed, as 32-bit (row, row+1) pairs at [column][row]: 4-byte LDS stores
+// with 2-way bank conflicts, 29% of its LDS cycles.) A row is padded to 576 bytes
+// so that the four rows a half-wave reads sit in four different 64-byte bank
+// groups. Tile 256 x 256 per workgroup of eight
 // waves (2 x 4 waves of 128 x 64, v_mfma_f32_32x32x16_bf16: 12 fragment reads per
 // 16 MFMAs; a 128 x 128 tile of four 64 x 64 waves read 8 per 8 and was bound by
 // LDS traffic). LDS is double-buffered, and the chunks' global loads go through
@@ -34,7 +41,20 @@ constexpr int kWgDepth = 3;  // chunks of global loads in flight
 // in registers, and the compiler waits for each before its first use), so the
 // load ring stays full across barriers.
 __device__ __forceinline__ void wg_lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-constexpr int kWgStride = kWgBK + 8;  // bf16 per LDS row (80 bytes: 16-byte aligned, spreads banks)
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef short v8i16_t __attribute__((ext_vector_type(8)));
+constexpr int kWgStride = kWgBM + 32;  // bf16 per LDS row: 576 bytes, 64 bytes past a 256-byte multiple
+
+// 4 bf16 of one column, 4 consecutive rows (see above); p: this lane's 8-byte piece
+__device__ __forceinline__ v4i16_t ds_read_tr16(const uint16_t* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16_t*)p);
+}
+
+// rows 0..3 and 4..7 of a fragment's column, as one 8 x bf16 operand
+__device__ __forceinline__ bf16x8_t frag_of(v4i16_t lo, v4i16_t hi) {
+    const v8i16_t v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8_t, v);
+}
 
 template <bool GATHER_B>
 __global__ __launch_bounds__(kWgThreads, 1) void wgrad_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
@@ -42,8 +62,9 @@ __global__ __launch_bounds__(kWgThreads, 1) void wgrad_kernel(const uint16_t* __
                                                     const int32_t* __restrict__ offsets, int M, int N,
                                                     int tiles_m, int tiles_n, float* __restrict__ dW) {
     MOE_DEBUG_GUARD();
-    __shared__ __attribute__((aligned(16))) uint16_t at[2][kWgBM][kWgStride];
-    __shared__ __attribute__((aligned(16))) uint16_t bt[2][kWgBN][kWgStride];
+    __shared__ __attribute__((aligned(16))) uint16_t at[2][kWgBK][kWgStride];
+    __shared__ __attribute__((aligned(16))) uint16_t bt[2][kWgBK][kWgStride];
+    static_assert(kWgBM == kWgBN, "A and B chunks share the staging layout");
 
     // XCD-aware order: block b runs on XCD b % 8; XCD x takes tiles
     // [start_x, start_x + count_x) in order, count_x = blocks on XCD x
@@ -58,8 +79,9 @@ __global__ __launch_bounds__(kWgThreads, 1) void wgrad_kernel(const uint16_t* __
 
     const int tid = threadIdx.x, lane = lane_id();
     const int wave = tid / kWave, wm = wave >> 2, wn = wave & 3;
-    // staging: thread -> row pair (2pp, 2pp+1) of the chunk, 16-byte column piece cp (0..31)
-    const int pp = tid & 15, cp = tid >> 4;
+    // staging: thread -> row pair (2pp, 2pp+1) of the chunk, 16-byte column piece cp
+    // (0..31); a wavefront's 32 lanes of one row read and write 512 contiguous bytes
+    const int cp = tid & 31, pp = tid >> 5;
     const int ca = m0 + 8 * cp, cb = n0 + 8 * cp;
     const bool a_col = ca < M, b_col = cb < N;
 
@@ -91,21 +113,14 @@ __global__ __launch_bounds__(kWgThreads, 1) void wgrad_kernel(const uint16_t* __
             }                                                                                     \
         }                                                                                         \
     } while (0)
-    // (row 2pp, row 2pp+1) pairs of column 8cp+q as one 32-bit word at [8cp+q][2pp]
+    // rows 2pp, 2pp+1, columns 8cp .. 8cp+7 as loaded (zero where out of range)
     auto store = [&](const u32x4_t (&ra2)[2], const u32x4_t (&rb2)[2], const bool (&oa)[2],
                      const bool (&ob)[2], int buf) {
+        const u32x4_t z = {0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int d = 0; d < 4; ++d) {
-            const uint32_t a0 = oa[0] ? ra2[0][d] : 0u, a1 = oa[1] ? ra2[1][d] : 0u;
-            const uint32_t b0 = ob[0] ? rb2[0][d] : 0u, b1 = ob[1] ? rb2[1][d] : 0u;
-            const uint32_t alo = __builtin_amdgcn_perm(a1, a0, 0x05040100u);  // col 2d
-            const uint32_t ahi = __builtin_amdgcn_perm(a1, a0, 0x07060302u);  // col 2d+1
-            const uint32_t blo = __builtin_amdgcn_perm(b1, b0, 0x05040100u);
-            const uint32_t bhi = __builtin_amdgcn_perm(b1, b0, 0x07060302u);
-            *(uint32_t*)&at[buf][8 * cp + 2 * d][2 * pp] = alo;
-            *(uint32_t*)&at[buf][8 * cp + 2 * d + 1][2 * pp] = ahi;
-            *(uint32_t*)&bt[buf][8 * cp + 2 * d][2 * pp] = blo;
-            *(uint32_t*)&bt[buf][8 * cp + 2 * d + 1][2 * pp] = bhi;
+        for (int h = 0; h < 2; ++h) {
+            *(u32x4_t*)&at[buf][2 * pp + h][8 * cp] = oa[h] ? ra2[h] : z;
+            *(u32x4_t*)&bt[buf][2 * pp + h][8 * cp] = ob[h] ? rb2[h] : z;
         }
     };
 
@@ -117,7 +132,12 @@ __global__ __launch_bounds__(kWgThreads, 1) void wgrad_kernel(const uint16_t* __
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    const int lrow = lane & 31, kh = 8 * (lane >> 5);
+    // transposed fragment reads: lane l (group g = l / 16, q = l % 16) addresses row
+    // 8 (g / 2) + q / 4 (+ 4 for the second half of the fragment, + 16 ks) and
+    // columns 16 (g % 2) + 4 (q % 4) .. +3 of the 32-column block; it receives
+    // column l % 32 of the block, rows 8 (l / 32) .. +7 of the k step
+    const int tr_row = 8 * (lane >> 5) + ((lane & 15) >> 2);
+    const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
     if (nchunks > 0) {
         // chunk 0 straight to LDS buffer 0; chunks 1 .. kWgDepth into their slots
         MOE_WG_LOAD(0, 0);
@@ -139,10 +159,14 @@ __global__ __launch_bounds__(kWgThreads, 1) void wgrad_kernel(const uint16_t* __
         const int buf_ = (ch) & 1;                                                                \
         _Pragma("unroll") for (int ks = 0; ks < kWgBK / 16; ++ks) {                               \
             bf16x8_t fa[4], fb[2];                                                                \
-            _Pragma("unroll") for (int i = 0; i < 4; ++i)                                         \
-                fa[i] = *(const bf16x8_t*)&at[buf_][wm * 128 + i * 32 + lrow][ks * 16 + kh];      \
-            _Pragma("unroll") for (int j = 0; j < 2; ++j)                                         \
-                fb[j] = *(const bf16x8_t*)&bt[buf_][wn * 64 + j * 32 + lrow][ks * 16 + kh];       \
+            _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                       \
+                const uint16_t* pa_ = &at[buf_][ks * 16 + tr_row][wm * 128 + i * 32 + tr_col];    \
+                fa[i] = frag_of(ds_read_tr16(pa_), ds_read_tr16(pa_ + 4 * kWgStride));            \
+            }                                                                                     \
+            _Pragma("unroll") for (int j = 0; j < 2; ++j) {                                       \
+                const uint16_t* pb_ = &bt[buf_][ks * 16 + tr_row][wn * 64 + j * 32 + tr_col];     \
+                fb[j] = frag_of(ds_read_tr16(pb_), ds_read_tr16(pb_ + 4 * kWgStride));            \
+            }                                                                                     \
             _Pragma("unroll") for (int i = 0; i < 4; ++i)                                         \
                 _Pragma("unroll") for (int j = 0; j < 2; ++j)                                     \
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0); \
