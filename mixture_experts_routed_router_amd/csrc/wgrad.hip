@@ -1,5 +1,9 @@
 // wgrad.hip -- expert weight gradients, K-grouped over each expert's rows.
 //
+// Two kernels: wgrad_pp_kernel (below the first; B read from the layout) and
+// wgrad_kernel (B gathered through row_token). Both compute every output with the
+// same MFMAs in the same order, so their results are identical bit for bit.
+//
 //   dW[e, m, n] = sum over the rows p of expert e's padded segment of A[p, m] B[p, n]
 //
 // with A, B row-major over the layout rows (dW_down: A = dy, B = h; dW_gate_up:
@@ -222,16 +226,286 @@ __global__ __launch_bounds__(kWgThreads, 1) void wgrad_kernel(const uint16_t* __
         }
 }
 
+// ---- the ping-pong weight-gradient kernel (B not gathered) ----------------------------
+//
+// The same tile and MFMA shapes as wgrad_kernel, on the grouped GEMM's pipeline:
+// each 32-row chunk ("stage") of A and B goes straight from global memory into a
+// four-stage LDS ring with direct-to-LDS loads (global_load_lds_dwordx4, no
+// register staging), rows as they are in memory, and the fragments are read with
+// the transposing LDS read. Two groups of four waves (one wave of each per SIMD)
+// alternate: while one group runs its MFMAs on a stage held in registers, the
+// other reads its fragments of that stage and issues its half of a later stage's
+// loads, so each SIMD's MFMA pipe is fed by one wave while the other waits on
+// memory. Per stage s: group 0 computes in phase 2s, group 1 in phase 2s+1; group
+// 1 issues its half of stage s+3 in phase 2s (into stage s-1's slot), group 0 its
+// half of stage s+4 in phase 2s+1 (into stage s's slot); each group waits for its
+// own half of stage s+1 by the end of phase 2s. One tile (expert, 256 x 256 block
+// of dW) per workgroup.
+//
+// In LDS a stage row is 256 bf16 (512 bytes) of one layout row; its 16-byte piece p
+// sits in slot p ^ 4 (row % 4), so the four rows a half-wave's transposing read
+// touches fall in four different 64-byte bank groups. A chunk that ends past the
+// expert's segment (segments not a multiple of 32 rows) is loaded whole and its
+// rows past the segment are overwritten with zeros by the waves that loaded them,
+// after their loads land and before the barrier that precedes any read.
+//
+// Order: experts ranked by rows (descending, ties to the lower id; E <= 256,
+// else by id); rank r runs on XCD r % 8, each XCD takes its experts in rank order
+// and an expert's tiles one after another -- the longest tiles start first, and
+// an expert's tiles, which read the same rows, share one L2.
+constexpr int kPpStages = 4;
+constexpr int kPpRowElems = kWgBM;                  // 256 bf16 per stage row
+constexpr int kPpOpElems = kWgBK * kPpRowElems;     // one operand's stage, 16 KB
+constexpr int kPpStageElems = 2 * kPpOpElems;       // A then B, 32 KB
+constexpr int kPpLoads = 4;                         // this thread's loads per stage (2 A + 2 B)
+constexpr int kPpRankMaxE = 256;
+
+__device__ __forceinline__ uint32_t pp_lds_addr(const uint16_t* p) {
+    return (uint32_t)(size_t)(__attribute__((address_space(3))) const uint16_t*)p;
+}
+
+// 16 bytes per lane from global memory straight into LDS at lds_base + 16 * lane
+// (M0 holds the wave's LDS base). Every wait on these loads is an explicit vmcnt.
+__device__ __forceinline__ void pp_dma16(uint32_t lds_base, const void* sbase, uint32_t voff) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" :: "s"(lds_base), "v"(voff), "s"(sbase)
+                 : "memory");
+}
+template <int N>
+__device__ __forceinline__ void pp_wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+// at most `later` stages of this thread's loads left in flight
+__device__ __forceinline__ void pp_wait_stages(int later) {
+    if (later >= 3) pp_wait_vmcnt<3 * kPpLoads>();
+    else if (later == 2) pp_wait_vmcnt<2 * kPpLoads>();
+    else if (later == 1) pp_wait_vmcnt<kPpLoads>();
+    else pp_wait_vmcnt<0>();
+}
+
+__global__ __launch_bounds__(kWgThreads, 1) void wgrad_pp_kernel(const uint16_t* __restrict__ A,
+                                                                 const uint16_t* __restrict__ B,
+                                                                 const int32_t* __restrict__ offsets, int E, int M,
+                                                                 int N, int tiles_m, int tiles_n,
+                                                                 float* __restrict__ dW) {
+    MOE_DEBUG_GUARD();
+    __shared__ __attribute__((aligned(1024))) uint16_t ring[kPpStages * kPpStageElems];
+    __shared__ int32_t rows_lds[kPpRankMaxE];
+    __shared__ int32_t pick;
+
+    // ---- this block's tile
+    const int tiles = tiles_m * tiles_n;
+    const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
+    const int r = (slot / tiles) * 8 + xcd;  // the expert rank this block serves
+    if (r >= E) return;                      // uniform over the block
+    const int tile = slot % tiles;
+    const int tid = threadIdx.x;
+    int e = r;
+    if (E <= kPpRankMaxE) {
+        for (int i = tid; i < E; i += kWgThreads) rows_lds[i] = max(offsets[i + 1] - offsets[i], 0);
+        __syncthreads();
+        if (tid < E) {
+            const int mine = rows_lds[tid];
+            int rank = 0;
+            for (int i = 0; i < E; ++i) {
+                const int o = rows_lds[i];
+                rank += (o > mine) || (o == mine && i < tid);
+            }
+            if (rank == r) pick = tid;
+        }
+        __syncthreads();
+        e = pick;
+    }
+    const int m0 = (tile / tiles_n) * kWgBM, n0 = (tile % tiles_n) * kWgBN;
+    const int seg0 = offsets[e];
+    const int rows = max(offsets[e + 1] - seg0, 0);
+    const int nk = (rows + kWgBK - 1) / kWgBK;
+    const int valid_last = rows - (nk - 1) * kWgBK;  // rows of the last stage inside the segment
+
+    const int lane = lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int wm = wave >> 2, wn = wave & 3, grp = wm;
+    const uint32_t ring0 = pp_lds_addr(ring);
+
+    // ---- this thread's load pieces: wave w, load i fills stage rows 4w + 2i + (0, 1);
+    // lane l: row 4w + 2i + l/32, physical slot l%32 = logical piece (l%32) ^ 4 (row%4)
+    // (the last stage's rows past the segment read its last row inside it instead --
+    // never a row past P_max -- and are zeroed in LDS once loaded; columns past M or N
+    // read column 0, and their results are never stored)
+    uint32_t a_off[2], b_off[2], a_off_last[2], b_off_last[2];
+    int ld_row[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int row = 4 * wave + 2 * i + (lane >> 5);
+        const int row_last = row < valid_last ? row : valid_last - 1;
+        const int piece = (lane & 31) ^ (4 * (row & 3));
+        const int ca = m0 + 8 * piece, cb = n0 + 8 * piece;
+        const int cca = ca < M ? ca : 0, ccb = cb < N ? cb : 0;
+        ld_row[i] = row;
+        a_off[i] = (uint32_t)(row * M + cca) * 2u;
+        b_off[i] = (uint32_t)(row * N + ccb) * 2u;
+        a_off_last[i] = (uint32_t)(row_last * M + cca) * 2u;
+        b_off_last[i] = (uint32_t)(row_last * N + ccb) * 2u;
+    }
+    const char* a_base = (const char*)(A + (int64_t)seg0 * M);
+    const char* b_base = (const char*)(B + (int64_t)seg0 * N);
+    const int64_t a_step = (int64_t)kWgBK * M * 2, b_step = (int64_t)kWgBK * N * 2;  // bytes per stage
+
+    auto issue = [&](int st) {  // this thread's pieces of stage st
+        const uint32_t sa = ring0 + (uint32_t)((st & (kPpStages - 1)) * kPpStageElems * 2);
+        const bool last = st == nk - 1;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            pp_dma16(sa + (uint32_t)((2 * wave + i) * 1024), a_base + st * a_step, last ? a_off_last[i] : a_off[i]);
+            pp_dma16(sa + (uint32_t)(kPpOpElems * 2 + (2 * wave + i) * 1024), b_base + st * b_step,
+                     last ? b_off_last[i] : b_off[i]);
+        }
+    };
+    // after this thread's loads of the last stage landed: zero its rows past the segment
+    auto zero_tail = [&](int st) {
+        if (valid_last >= kWgBK || st != nk - 1) return;
+        uint16_t* sa = ring + (st & (kPpStages - 1)) * kPpStageElems;
+        const u32x4_t z = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            if (ld_row[i] >= valid_last) {
+                const int off = ld_row[i] * kPpRowElems + 8 * (lane & 31);
+                *(u32x4_t*)(sa + off) = z;
+                *(u32x4_t*)(sa + kPpOpElems + off) = z;
+            }
+    };
+
+    // ---- fragment reads (transposing): lane l addresses row 8 (l/32) + (l%16)/4 (+4 for
+    // the upper half) of the k step and columns 16 ((l/16)%2) + 4 (l%4) .. +3 of a
+    // 32-column block; the row's swizzle 4 (row%4) depends on (l%16)/4 alone
+    const int tr_row = 8 * (lane >> 5) + ((lane & 15) >> 2);
+    const int tr_swz = 4 * (((lane & 15) >> 2) & 3);
+    const int tr_colp = 2 * ((lane >> 4) & 1) + ((lane & 3) >> 1);  // piece within the 32-column block
+    const int tr_half = 4 * (lane & 1);                              // element offset within the piece
+    // element offset of this lane's 8-byte piece for the 32-column block starting at piece pb
+    auto tr_off = [&](int pb, int ks) {
+        return (ks * 16 + tr_row) * kPpRowElems + (((pb + tr_colp) ^ tr_swz) << 3) + tr_half;
+    };
+    bf16x8_t fa[2][4], fb[2][2];
+    // (macros rather than lambdas: a lambda capturing the fragments or accumulators by
+    // reference kept them in scratch memory)
+#define MOE_PP_READ_FRAGS(st)                                                                   \
+    do {                                                                                        \
+        const uint16_t* sa_ = ring + ((st) & (kPpStages - 1)) * kPpStageElems;                  \
+        const uint16_t* sb_ = sa_ + kPpOpElems;                                                 \
+        _Pragma("unroll") for (int ks = 0; ks < 2; ++ks) {                                      \
+            _Pragma("unroll") for (int i = 0; i < 4; ++i) {                                     \
+                const uint16_t* pa_ = sa_ + tr_off(wm * 16 + i * 4, ks);                        \
+                fa[ks][i] = frag_of(ds_read_tr16(pa_), ds_read_tr16(pa_ + 4 * kPpRowElems));    \
+            }                                                                                   \
+            _Pragma("unroll") for (int j = 0; j < 2; ++j) {                                     \
+                const uint16_t* pb_ = sb_ + tr_off(wn * 8 + j * 4, ks);                         \
+                fb[ks][j] = frag_of(ds_read_tr16(pb_), ds_read_tr16(pb_ + 4 * kPpRowElems));    \
+            }                                                                                   \
+        }                                                                                       \
+    } while (0)
+    floatx16_t acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = floatx16_t{};
+#define MOE_PP_MMA()                                                                            \
+    do {                                                                                        \
+        _Pragma("unroll") for (int ks = 0; ks < 2; ++ks)                                        \
+            _Pragma("unroll") for (int i = 0; i < 4; ++i)                                       \
+                _Pragma("unroll") for (int j = 0; j < 2; ++j)                                   \
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[ks][i], fb[ks][j], acc[i][j], 0, 0, 0); \
+    } while (0)
+    // stages st+1.. of this group still in flight after its loads up to stage `upto`
+    auto later = [&](int st, int upto) { return max(0, min(upto, nk - 1) - st); };
+
+    if (nk > 0) {
+        // prologue: both groups issue their halves of stages 0..2, group 0 also of 3
+        for (int st = 0; st < kPpStages - 1; ++st)
+            if (st < nk) issue(st);
+        if (grp == 0 && kPpStages - 1 < nk) issue(kPpStages - 1);
+        pp_wait_stages(later(0, grp == 0 ? kPpStages - 1 : kPpStages - 2));
+        zero_tail(0);
+        wg_lds_barrier();
+        if (grp == 0) MOE_PP_READ_FRAGS(0);
+        wg_lds_barrier();
+        // each group runs its own loop (a branch on the group inside one loop made the
+        // compiler keep two copies of the accumulators)
+        if (grp == 0) {
+            for (int kt = 0; kt < nk; ++kt) {
+                // phase 2kt: compute stage kt; wait for own half of stage kt+1
+                __builtin_amdgcn_s_setprio(1);
+                MOE_PP_MMA();
+                __builtin_amdgcn_s_setprio(0);
+                if (kt + 1 < nk) {
+                    pp_wait_stages(later(kt + 1, kt + 3));
+                    zero_tail(kt + 1);
+                }
+                wg_lds_barrier();
+                // phase 2kt+1: refill stage kt's slot with stage kt+4; read stage kt+1
+                if (kt + 4 < nk) issue(kt + 4);
+                if (kt + 1 < nk) MOE_PP_READ_FRAGS(kt + 1);
+                wg_lds_barrier();
+            }
+        } else {
+            for (int kt = 0; kt < nk; ++kt) {
+                // phase 2kt: read stage kt; issue stage kt+3 into stage kt-1's slot; wait for kt+1
+                MOE_PP_READ_FRAGS(kt);
+                if (kt + 3 < nk) issue(kt + 3);
+                if (kt + 1 < nk) {
+                    pp_wait_stages(later(kt + 1, kt + 3));
+                    zero_tail(kt + 1);
+                }
+                wg_lds_barrier();
+                // phase 2kt+1: compute stage kt
+                __builtin_amdgcn_s_setprio(1);
+                MOE_PP_MMA();
+                __builtin_amdgcn_s_setprio(0);
+                wg_lds_barrier();
+            }
+        }
+    }
+
+#undef MOE_PP_READ_FRAGS
+#undef MOE_PP_MMA
+
+    // ---- epilogue (as wgrad_kernel's): 16-byte fp32 stores, 8 whole 128-byte rows each
+    float* out = dW + (int64_t)e * M * N;
+    const bool p0 = (lane & 1) != 0, p1 = (lane & 2) != 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int nb = n0 + wn * 64 + j * 32;
+            if (nb >= N) continue;
+            const int n = nb + ((lane & 31) >> 2) * 4;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int m = m0 + wm * 128 + i * 32 + q * 8 + (lane >> 5) * 4 + (lane & 3);
+                const uint32_t v0 = __float_as_uint(acc[i][j][4 * q + 0]), v1 = __float_as_uint(acc[i][j][4 * q + 1]);
+                const uint32_t v2 = __float_as_uint(acc[i][j][4 * q + 2]), v3 = __float_as_uint(acc[i][j][4 * q + 3]);
+                const uint32_t x0 = quad_xor1(p0 ? v0 : v1), x1 = quad_xor1(p0 ? v2 : v3);
+                const uint32_t t0 = p0 ? x0 : v0, t1 = p0 ? v1 : x0, t2 = p0 ? x1 : v2, t3 = p0 ? v3 : x1;
+                const uint32_t y0 = quad_xor2(p1 ? t0 : t2), y1 = quad_xor2(p1 ? t1 : t3);
+                const uint4 o = p1 ? make_uint4(y0, y1, t2, t3) : make_uint4(t0, t1, y0, y1);
+                if (m < M) *(uint4*)(out + (int64_t)m * N + n) = o;
+            }
+        }
+}
+
 hipError_t launch_wgrad(const uint16_t* A, const uint16_t* B, const int32_t* row_token, const int32_t* offsets,
                         int E, int M, int N, float* dW, hipStream_t stream) {
     const int tm = (M + kWgBM - 1) / kWgBM, tn = (N + kWgBN - 1) / kWgBN;
     const int64_t blocks = (int64_t)E * tm * tn;
-    if (row_token)
+    if (row_token) {
         hipLaunchKernelGGL(wgrad_kernel<true>, dim3((unsigned)blocks), dim3(kWgThreads), 0, stream, A, B, row_token,
                            offsets, M, N, tm, tn, dW);
-    else
-        hipLaunchKernelGGL(wgrad_kernel<false>, dim3((unsigned)blocks), dim3(kWgThreads), 0, stream, A, B,
-                           (const int32_t*)nullptr, offsets, M, N, tm, tn, dW);
+    } else {
+        // ranks are dealt to the 8 XCDs: 8 * ceil(E / 8) ranks, blocks past E return at once
+        const int64_t pp_blocks = (int64_t)((E + 7) / 8) * 8 * tm * tn;
+        hipLaunchKernelGGL(wgrad_pp_kernel, dim3((unsigned)pp_blocks), dim3(kWgThreads), 0, stream, A, B, offsets, E,
+                           M, N, tm, tn, dW);
+    }
     return hipGetLastError();
 }
 
