@@ -335,6 +335,31 @@ moe_status moe_grouped_down_gemm_tiled(const moe_bf16 *h, const moe_bf16 *w_down
                                        moe_stream_t stream);
 
 /*
+ * FP8 expert weights (moe_quantize_fp8's codes) in tiled order: a code matrix
+ * [R, K] (R % 4 == 0, K % 32 == 0) kept as 4 x 32-byte blocks, code (r, c) at
+ *     ((r / 4) * (K / 32) + c / 32) * 128 + (r % 4) * 32 + c % 32,
+ * so one 32-code k stage of four neighbouring rows is one 128-byte line. The
+ * scales are unchanged (one per 64 rows, row-major). moe_tile_fp8_rows /
+ * moe_untile_fp8_rows convert [rows, cols] codes (w8_gate_up as rows = E * 2I,
+ * cols = H; w8_down as E * H, I), once per weight update; rows a multiple of 4.
+ * The two GEMMs take those codes with x_perm / h as for the bf16 tiled calls
+ * and compute what the *_fp8w calls compute, always on the 256-row MFMA tiles
+ * (never the weight-streaming kernel), so they equal the *_fp8w calls bit for
+ * bit wherever those use the MFMA tiles (P_max > 64 E). (No gathering variant:
+ * with tiled FP8 weights that kernel does not fit its scalar registers.)
+ */
+moe_status moe_tile_fp8_rows(const uint8_t *src, int64_t rows, int32_t cols, uint8_t *dst, moe_stream_t stream);
+moe_status moe_untile_fp8_rows(const uint8_t *src, int64_t rows, int32_t cols, uint8_t *dst, moe_stream_t stream);
+moe_status moe_grouped_glu_gemm_fp8w_tiled(const moe_bf16 *x_perm, const uint8_t *w8_gate_up,
+                                           const float *scale_gate_up, const int32_t *expert_counts,
+                                           const int32_t *expert_offsets, int32_t E, int32_t H, int32_t I,
+                                           int64_t P_max, moe_bf16 *h, moe_stream_t stream);
+moe_status moe_grouped_down_gemm_fp8w_tiled(const moe_bf16 *h, const uint8_t *w8_down, const float *scale_down,
+                                            const int32_t *expert_counts, const int32_t *expert_offsets,
+                                            int32_t E, int32_t H, int32_t I, int64_t P_max, moe_bf16 *y,
+                                            moe_stream_t stream);
+
+/*
  * Score-weighted gather-sum [prime-rl, Changes: one fp32 score-weighted
  * gather-sum back].  Per token t, a gather (no scatter-add):
  *   out[t, c] = bf16_rne( sum_{j=0..k-1} topk_w[t, j] * y[route_row[t*k+j], c] )

@@ -15,7 +15,8 @@ _API = ("route_topk", "permute", "grouped_glu_gemm", "grouped_down_gemm", "combi
         "grouped_gemm", "grouped_gemm_swiglu_backward", "grouped_glu_gemm_clamped", "swiglu", "swiglu_backward", "transpose_experts", "combine_backward",
         "route_backward", "permute_backward", "grouped_wgrad", "MoETrainingLayer", "router_prepare",
         "router_topk", "tile_rows", "untile_rows", "tile_weights", "TiledWeights", "even_rows",
-        "grouped_glu_gemm_tiled", "grouped_glu_gemm_gather_tiled", "grouped_down_gemm_tiled")
+        "grouped_glu_gemm_tiled", "grouped_glu_gemm_gather_tiled", "grouped_down_gemm_tiled",
+        "tile_fp8_weights", "untile_fp8_rows")
 
 
 def __getattr__(name):

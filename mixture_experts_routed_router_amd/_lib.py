@@ -80,12 +80,18 @@ def _open(debug: bool):
     lib.moe_grouped_down_gemm.argtypes = [_c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32,
                                           _c_i64, _c_vp, _c_vp]
     lib.moe_grouped_down_gemm_tiled.argtypes = lib.moe_grouped_down_gemm.argtypes
+    lib.moe_tile_fp8_rows.argtypes = [_c_vp, _c_i64, _c_i32, _c_vp, _c_vp]
+    lib.moe_untile_fp8_rows.argtypes = [_c_vp, _c_i64, _c_i32, _c_vp, _c_vp]
     lib.moe_combine.argtypes = [_c_vp, _c_vp, _c_vp, _c_i64, _c_i32, _c_i32, _c_i64, _c_vp, _c_vp]
     lib.moe_quantize_fp8.argtypes = [_c_vp, _c_i64, _c_i32, _c_i32, _c_vp, _c_vp, _c_vp]
     lib.moe_grouped_glu_gemm_fp8w.argtypes = [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32,
                                               _c_i32, _c_i64, _c_vp, _c_vp]
     lib.moe_grouped_glu_gemm_gather_fp8w.argtypes = [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64,
                                                      _c_i32, _c_i32, _c_i32, _c_i64, _c_vp, _c_vp]
+    lib.moe_grouped_glu_gemm_fp8w_tiled.argtypes = [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32,
+                                                     _c_i64, _c_vp, _c_vp]
+    lib.moe_grouped_down_gemm_fp8w_tiled.argtypes = [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32,
+                                                      _c_i64, _c_vp, _c_vp]
     lib.moe_grouped_down_gemm_fp8w.argtypes = [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32,
                                                _c_i32, _c_i64, _c_vp, _c_vp]
     lib.moe_grouped_gemm.argtypes = [_c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i64, _c_vp, _c_vp]
@@ -554,9 +560,11 @@ def grouped_down_gemm_tiled(h, w_down: TiledWeights, counts, offsets, y=None, st
 @dataclass
 class FP8Weights:
     """Block-scaled E4M3 expert weights: codes [E, R, K] uint8, one fp32 scale per
-    64 rows, scale [E, R // 64]."""
+    64 rows, scale [E, R // 64]. tiled: the codes in 4-row tiled order
+    (tile_fp8_weights), for the *_fp8w_tiled GEMMs."""
     w8: torch.Tensor
     scale: torch.Tensor
+    tiled: bool = False
 
     @property
     def shape(self):
@@ -575,6 +583,27 @@ def quantize_fp8(w: torch.Tensor, out: FP8Weights | None = None, stream=None) ->
     return out
 
 
+def tile_fp8_weights(wq: FP8Weights, stream=None) -> FP8Weights:
+    """The same weights with the codes in 4-row tiled order (once per weight update)."""
+    if wq.tiled:
+        raise ValueError("already tiled")
+    E, R, K = wq.w8.shape
+    out = torch.empty((E, R, K), dtype=torch.uint8, device=wq.w8.device)
+    _call("moe_tile_fp8_rows", _ptr(wq.w8, torch.uint8, "w8"), E * R, K, _ptr(out, torch.uint8, "dst", (E, R, K)),
+          _stream(stream))
+    return FP8Weights(out, wq.scale, tiled=True)
+
+
+def untile_fp8_rows(src: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Tiled FP8 codes [R, K] back to row-major."""
+    R, K = src.shape
+    if out is None:
+        out = torch.empty((R, K), dtype=torch.uint8, device=src.device)
+    _call("moe_untile_fp8_rows", _ptr(src, torch.uint8, "src"), R, K, _ptr(out, torch.uint8, "dst", (R, K)),
+          _stream(stream))
+    return out
+
+
 def _fp8_args(wq: FP8Weights, name: str):
     E, R, K = wq.w8.shape
     return (_ptr(wq.w8, torch.uint8, f"{name}.w8"),
@@ -582,6 +611,7 @@ def _fp8_args(wq: FP8Weights, name: str):
 
 
 def grouped_glu_gemm_fp8w(x_perm, w_gate_up: FP8Weights, counts, offsets, h=None, stream=None):
+    """With tiled FP8 weights (tile_fp8_weights) x_perm and h are in row-pair tiled order."""
     P_max, H = x_perm.shape
     E, two_i, H2 = w_gate_up.shape
     I = two_i // 2
@@ -589,7 +619,7 @@ def grouped_glu_gemm_fp8w(x_perm, w_gate_up: FP8Weights, counts, offsets, h=None
         raise ValueError("w_gate_up must be [E, 2I, H]")
     if h is None:
         h = torch.empty((P_max, I), dtype=torch.bfloat16, device=x_perm.device)
-    _call("moe_grouped_glu_gemm_fp8w", _ptr(x_perm, torch.bfloat16, "x_perm"),
+    _call("moe_grouped_glu_gemm_fp8w" + ("_tiled" if w_gate_up.tiled else ""), _ptr(x_perm, torch.bfloat16, "x_perm"),
           *_fp8_args(w_gate_up, "w_gate_up"), _ptr(counts, torch.int32, "counts", (E,)),
           _ptr(offsets, torch.int32, "offsets", (E + 1,)), E, H, I, P_max,
           _ptr(h, torch.bfloat16, "h", (P_max, I)), _stream(stream))
@@ -599,6 +629,8 @@ def grouped_glu_gemm_fp8w(x_perm, w_gate_up: FP8Weights, counts, offsets, h=None
 def grouped_glu_gemm_gather_fp8w(x, row_token, w_gate_up: FP8Weights, counts, offsets, h=None,
                                  stream=None):
     T, H = x.shape
+    if w_gate_up.tiled:
+        raise ValueError("the gathering gate/up GEMM takes row-major FP8 weights (no tiled variant)")
     P_max = row_token.shape[0]
     E, two_i, H2 = w_gate_up.shape
     I = two_i // 2
@@ -614,13 +646,15 @@ def grouped_glu_gemm_gather_fp8w(x, row_token, w_gate_up: FP8Weights, counts, of
 
 
 def grouped_down_gemm_fp8w(h, w_down: FP8Weights, counts, offsets, y=None, stream=None):
+    """With tiled FP8 weights h is in row-pair tiled order (y row-major either way)."""
     P_max, I = h.shape
     E, H, I2 = w_down.shape
     if I2 != I:
         raise ValueError("w_down must be [E, H, I]")
     if y is None:
         y = torch.empty((P_max, H), dtype=torch.bfloat16, device=h.device)
-    _call("moe_grouped_down_gemm_fp8w", _ptr(h, torch.bfloat16, "h"), *_fp8_args(w_down, "w_down"),
+    _call("moe_grouped_down_gemm_fp8w" + ("_tiled" if w_down.tiled else ""), _ptr(h, torch.bfloat16, "h"),
+          *_fp8_args(w_down, "w_down"),
           _ptr(counts, torch.int32, "counts", (E,)), _ptr(offsets, torch.int32, "offsets", (E + 1,)),
           E, H, I, P_max, _ptr(y, torch.bfloat16, "y", (P_max, H)), _stream(stream))
     return y
@@ -657,19 +691,25 @@ class MoELayer:
         self.out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
 
     def __call__(self, x, logits, w_gate_up, w_down, stream=None):
-        tiled_w = isinstance(w_gate_up, TiledWeights), isinstance(w_down, TiledWeights)
-        if tiled_w != (self.tiled, self.tiled):
-            raise ValueError("a tiled layer takes TiledWeights for both weights, a row-major one neither")
+        def is_tiled(w):
+            return isinstance(w, TiledWeights) or (isinstance(w, FP8Weights) and w.tiled)
+        if (is_tiled(w_gate_up), is_tiled(w_down)) != (self.tiled, self.tiled):
+            raise ValueError("a tiled layer takes tiled weights (TiledWeights, or FP8Weights from "
+                             "tile_fp8_weights) for both, a row-major one neither")
         route_topk(logits, self.k, self.topk_idx, self.topk_w, stream=stream)
         permute(x, self.topk_idx, self.E, self.align, self.P_max, out=self.layout,
                 workspace=self.workspace, stream=stream, gather=not self.fused_gather, tiled=self.tiled)
         L = self.layout
         if self.tiled:
+            f8_gu, f8_d = isinstance(w_gate_up, FP8Weights), isinstance(w_down, FP8Weights)
             if self.fused_gather:
-                grouped_glu_gemm_gather_tiled(x, L.row_token, w_gate_up, L.counts, L.offsets, h=self.h, stream=stream)
+                glu = grouped_glu_gemm_gather_fp8w if f8_gu else grouped_glu_gemm_gather_tiled
+                glu(x, L.row_token, w_gate_up, L.counts, L.offsets, h=self.h, stream=stream)
             else:
-                grouped_glu_gemm_tiled(L.x_perm, w_gate_up, L.counts, L.offsets, h=self.h, stream=stream)
-            grouped_down_gemm_tiled(self.h, w_down, L.counts, L.offsets, y=self.y, stream=stream)
+                glu = grouped_glu_gemm_fp8w if f8_gu else grouped_glu_gemm_tiled
+                glu(L.x_perm, w_gate_up, L.counts, L.offsets, h=self.h, stream=stream)
+            down = grouped_down_gemm_fp8w if f8_d else grouped_down_gemm_tiled
+            down(self.h, w_down, L.counts, L.offsets, y=self.y, stream=stream)
             combine(self.y, L.route_row, self.topk_w, out=self.out, stream=stream)
             return self.out
         fp8_gu, fp8_d = isinstance(w_gate_up, FP8Weights), isinstance(w_down, FP8Weights)

@@ -15,12 +15,13 @@ hipError_t launch_permute_from_hist(const uint16_t*, const int32_t*, int64_t, in
 hipError_t launch_permute(const uint16_t*, const int32_t*, int64_t, int, int, int, int, int64_t,
                           int32_t*, int32_t*, int32_t*, int32_t*, uint16_t*, void*, bool, hipStream_t);
 hipError_t launch_tile_rows(const uint16_t*, int64_t, int, uint16_t*, bool, hipStream_t);
-hipError_t launch_grouped_glu_gemm_tiled(const uint16_t*, const uint16_t*, const int32_t*, int, int, int, uint16_t*,
-                                         int, hipStream_t);
-hipError_t launch_grouped_glu_gemm_gather_tiled(const uint16_t*, const int32_t*, const uint16_t*, const int32_t*, int,
-                                                int, int, uint16_t*, int, hipStream_t);
-hipError_t launch_grouped_down_gemm_tiled(const uint16_t*, const uint16_t*, const int32_t*, int, int, int, uint16_t*,
-                                          int, hipStream_t);
+hipError_t launch_tile_fp8_rows(const uint8_t*, int64_t, int, uint8_t*, bool, hipStream_t);
+hipError_t launch_grouped_glu_gemm_tiled(const uint16_t*, const void*, const float*, const int32_t*, int, int, int,
+                                         uint16_t*, int, hipStream_t);
+hipError_t launch_grouped_glu_gemm_gather_tiled(const uint16_t*, const int32_t*, const void*, const float*,
+                                                const int32_t*, int, int, int, uint16_t*, int, hipStream_t);
+hipError_t launch_grouped_down_gemm_tiled(const uint16_t*, const void*, const float*, const int32_t*, int, int, int,
+                                          uint16_t*, int, hipStream_t);
 size_t permute_workspace_bytes(int64_t R, int E);
 size_t permute_scratch_bytes();
 hipError_t launch_permute_noalloc(const uint16_t*, const int32_t*, int64_t, int, int, int, int, int64_t, int32_t*,
@@ -524,8 +525,8 @@ moe_status moe_grouped_glu_gemm_tiled(const moe_bf16* x_perm, const moe_bf16* w_
     if (s != MOE_OK) return s;
     if ((s = check_even_pmax(P_max)) != MOE_OK) return s;
     DEBUG_CHECK(moe::debug_check_layout(expert_counts, expert_offsets, E, P_max, (hipStream_t)stream));
-    return hip_status(moe::launch_grouped_glu_gemm_tiled(x_perm, w_gate_up, expert_offsets, E, H, I, h, (int)P_max,
-                                                         (hipStream_t)stream),
+    return hip_status(moe::launch_grouped_glu_gemm_tiled(x_perm, w_gate_up, nullptr, expert_offsets, E, H, I, h,
+                                                         (int)P_max, (hipStream_t)stream),
                       "moe_grouped_glu_gemm_tiled launch");
 }
 
@@ -539,8 +540,8 @@ moe_status moe_grouped_glu_gemm_gather_tiled(const moe_bf16* x, const int32_t* r
     if ((s = check_gather(row_token, T, H)) != MOE_OK) return s;
     DEBUG_CHECK(moe::debug_check_layout(expert_counts, expert_offsets, E, P_max, (hipStream_t)stream));
     DEBUG_CHECK(moe::debug_check_rows(row_token, P_max, -1, T, 6, (hipStream_t)stream));
-    return hip_status(moe::launch_grouped_glu_gemm_gather_tiled(x, row_token, w_gate_up, expert_offsets, E, H, I, h,
-                                                                (int)P_max, (hipStream_t)stream),
+    return hip_status(moe::launch_grouped_glu_gemm_gather_tiled(x, row_token, w_gate_up, nullptr, expert_offsets, E,
+                                                                H, I, h, (int)P_max, (hipStream_t)stream),
                       "moe_grouped_glu_gemm_gather_tiled launch");
 }
 
@@ -551,7 +552,7 @@ moe_status moe_grouped_down_gemm_tiled(const moe_bf16* h, const moe_bf16* w_down
     if (s != MOE_OK) return s;
     if ((s = check_even_pmax(P_max)) != MOE_OK) return s;
     DEBUG_CHECK(moe::debug_check_layout(expert_counts, expert_offsets, E, P_max, (hipStream_t)stream));
-    return hip_status(moe::launch_grouped_down_gemm_tiled(h, w_down, expert_offsets, E, H, I, y, (int)P_max,
+    return hip_status(moe::launch_grouped_down_gemm_tiled(h, w_down, nullptr, expert_offsets, E, H, I, y, (int)P_max,
                                                           (hipStream_t)stream),
                       "moe_grouped_down_gemm_tiled launch");
 }
@@ -612,6 +613,53 @@ moe_status moe_grouped_down_gemm_fp8w(const moe_bf16* h, const uint8_t* w8_down,
     return hip_status(launch_down(h, w8_down, scale_down, expert_offsets, E, H, I, P_max, y,
                                   (hipStream_t)stream),
                       "moe_grouped_down_gemm_fp8w launch");
+}
+
+static moe_status tile_fp8(const uint8_t* src, int64_t rows, int32_t cols, uint8_t* dst, bool to_tiled,
+                          moe_stream_t stream) {
+    REQUIRE_PTR_UNLESS_EMPTY(src, rows == 0);
+    REQUIRE_PTR_UNLESS_EMPTY(dst, rows == 0);
+    if (rows < 0 || (rows & 3)) return fail(MOE_ERR_INVALID_SHAPE, "rows=%lld must be a multiple of 4, >= 0", (long long)rows);
+    if (cols < 32 || cols % 32 != 0) return fail(MOE_ERR_INVALID_SHAPE, "cols=%d must be a positive multiple of 32", cols);
+    if (rows == 0) return ok();
+    if (src == dst) return fail(MOE_ERR_INVALID_VALUE, "src and dst must not be the same buffer");
+    return hip_status(moe::launch_tile_fp8_rows(src, rows, cols, dst, to_tiled, (hipStream_t)stream),
+                      to_tiled ? "moe_tile_fp8_rows launch" : "moe_untile_fp8_rows launch");
+}
+
+moe_status moe_tile_fp8_rows(const uint8_t* src, int64_t rows, int32_t cols, uint8_t* dst, moe_stream_t stream) {
+    return tile_fp8(src, rows, cols, dst, true, stream);
+}
+
+moe_status moe_untile_fp8_rows(const uint8_t* src, int64_t rows, int32_t cols, uint8_t* dst, moe_stream_t stream) {
+    return tile_fp8(src, rows, cols, dst, false, stream);
+}
+
+moe_status moe_grouped_glu_gemm_fp8w_tiled(const moe_bf16* x_perm, const uint8_t* w8_gate_up,
+                                           const float* scale_gate_up, const int32_t* expert_counts,
+                                           const int32_t* expert_offsets, int32_t E, int32_t H, int32_t I,
+                                           int64_t P_max, moe_bf16* h, moe_stream_t stream) {
+    moe_status s = check_gemm(x_perm, w8_gate_up, expert_counts, expert_offsets, E, H, I, P_max, h);
+    if (s != MOE_OK) return s;
+    REQUIRE_PTR(scale_gate_up);
+    if ((s = check_even_pmax(P_max)) != MOE_OK) return s;
+    DEBUG_CHECK(moe::debug_check_layout(expert_counts, expert_offsets, E, P_max, (hipStream_t)stream));
+    return hip_status(moe::launch_grouped_glu_gemm_tiled(x_perm, w8_gate_up, scale_gate_up, expert_offsets, E, H, I, h,
+                                                         (int)P_max, (hipStream_t)stream),
+                      "moe_grouped_glu_gemm_fp8w_tiled launch");
+}
+
+moe_status moe_grouped_down_gemm_fp8w_tiled(const moe_bf16* h, const uint8_t* w8_down, const float* scale_down,
+                                            const int32_t* expert_counts, const int32_t* expert_offsets, int32_t E,
+                                            int32_t H, int32_t I, int64_t P_max, moe_bf16* y, moe_stream_t stream) {
+    moe_status s = check_gemm(h, w8_down, expert_counts, expert_offsets, E, H, I, P_max, y);
+    if (s != MOE_OK) return s;
+    REQUIRE_PTR(scale_down);
+    if ((s = check_even_pmax(P_max)) != MOE_OK) return s;
+    DEBUG_CHECK(moe::debug_check_layout(expert_counts, expert_offsets, E, P_max, (hipStream_t)stream));
+    return hip_status(moe::launch_grouped_down_gemm_tiled(h, w8_down, scale_down, expert_offsets, E, H, I, y,
+                                                          (int)P_max, (hipStream_t)stream),
+                      "moe_grouped_down_gemm_fp8w_tiled launch");
 }
 
 moe_status moe_grouped_gemm(const moe_bf16* a, const moe_bf16* w, const int32_t* expert_counts,

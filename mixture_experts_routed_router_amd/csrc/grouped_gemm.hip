@@ -84,31 +84,46 @@ hipError_t launch_grouped_down_gemm(const uint16_t* h, const void* w_d, const fl
     return hipGetLastError();
 }
 
-// Row-pair tiled operands (bf16): the weights and, unless gathered, A are stored in
-// 2 x 32 blocks (the layout moe_tile_rows writes); the gate/up GEMM writes h in the
-// same layout, the down GEMM writes y row-major.
-hipError_t launch_grouped_glu_gemm_tiled(const uint16_t* x_perm_t, const uint16_t* w_gu_t, const int32_t* offsets,
-                                         int E, int H, int I, uint16_t* h_t, int rows_max, hipStream_t stream) {
-    hipLaunchKernelGGL((grouped_gemm_kernel<true, false, false, false, true>), dim3(persistent_grid()),
-                       dim3(kGemmThreads), 0, stream, x_perm_t, (const int32_t*)nullptr, (const void*)w_gu_t,
-                       (const float*)nullptr, offsets, E, H, I, h_t, (const uint16_t*)nullptr, INFINITY, rows_max);
+// Tiled operands: the weights (bf16 in row pairs, or FP8 codes in row quads, with
+// `scale` non-NULL) and, unless gathered, A in 2 x 32 blocks (the layouts
+// moe_tile_rows / moe_tile_fp8_rows write); the gate/up GEMM writes h in row-pair
+// order, the down GEMM writes y row-major.
+hipError_t launch_grouped_glu_gemm_tiled(const uint16_t* x_perm_t, const void* w_gu_t, const float* scale,
+                                         const int32_t* offsets, int E, int H, int I, uint16_t* h_t, int rows_max,
+                                         hipStream_t stream) {
+    if (scale)
+        hipLaunchKernelGGL((grouped_gemm_kernel<true, false, true, false, true>), dim3(persistent_grid()),
+                           dim3(kGemmThreads), 0, stream, x_perm_t, (const int32_t*)nullptr, w_gu_t, scale, offsets,
+                           E, H, I, h_t, (const uint16_t*)nullptr, INFINITY, rows_max);
+    else
+        hipLaunchKernelGGL((grouped_gemm_kernel<true, false, false, false, true>), dim3(persistent_grid()),
+                           dim3(kGemmThreads), 0, stream, x_perm_t, (const int32_t*)nullptr, w_gu_t, scale, offsets,
+                           E, H, I, h_t, (const uint16_t*)nullptr, INFINITY, rows_max);
     return hipGetLastError();
 }
 
-hipError_t launch_grouped_glu_gemm_gather_tiled(const uint16_t* x, const int32_t* row_token, const uint16_t* w_gu_t,
-                                                const int32_t* offsets, int E, int H, int I, uint16_t* h_t,
-                                                int rows_max, hipStream_t stream) {
+// (bf16 weights only: the gathering kernel with tiled FP8 weights runs out of SGPRs)
+hipError_t launch_grouped_glu_gemm_gather_tiled(const uint16_t* x, const int32_t* row_token, const void* w_gu_t,
+                                                const float* scale, const int32_t* offsets, int E, int H, int I,
+                                                uint16_t* h_t, int rows_max, hipStream_t stream) {
+    if (scale) return hipErrorInvalidValue;
     hipLaunchKernelGGL((grouped_gemm_kernel<true, true, false, false, true>), dim3(persistent_grid()),
-                       dim3(kGemmThreads), 0, stream, x, row_token, (const void*)w_gu_t, (const float*)nullptr,
-                       offsets, E, H, I, h_t, (const uint16_t*)nullptr, INFINITY, rows_max);
+                       dim3(kGemmThreads), 0, stream, x, row_token, w_gu_t, scale, offsets, E, H, I, h_t,
+                       (const uint16_t*)nullptr, INFINITY, rows_max);
     return hipGetLastError();
 }
 
-hipError_t launch_grouped_down_gemm_tiled(const uint16_t* h_t, const uint16_t* w_d_t, const int32_t* offsets,
-                                          int E, int H, int I, uint16_t* y, int rows_max, hipStream_t stream) {
-    hipLaunchKernelGGL((grouped_gemm_kernel<false, false, false, false, true>), dim3(persistent_grid()),
-                       dim3(kGemmThreads), 0, stream, h_t, (const int32_t*)nullptr, (const void*)w_d_t,
-                       (const float*)nullptr, offsets, E, I, H, y, (const uint16_t*)nullptr, INFINITY, rows_max);
+hipError_t launch_grouped_down_gemm_tiled(const uint16_t* h_t, const void* w_d_t, const float* scale,
+                                          const int32_t* offsets, int E, int H, int I, uint16_t* y, int rows_max,
+                                          hipStream_t stream) {
+    if (scale)
+        hipLaunchKernelGGL((grouped_gemm_kernel<false, false, true, false, true>), dim3(persistent_grid()),
+                           dim3(kGemmThreads), 0, stream, h_t, (const int32_t*)nullptr, w_d_t, scale, offsets, E,
+                           I, H, y, (const uint16_t*)nullptr, INFINITY, rows_max);
+    else
+        hipLaunchKernelGGL((grouped_gemm_kernel<false, false, false, false, true>), dim3(persistent_grid()),
+                           dim3(kGemmThreads), 0, stream, h_t, (const int32_t*)nullptr, w_d_t, scale, offsets, E,
+                           I, H, y, (const uint16_t*)nullptr, INFINITY, rows_max);
     return hipGetLastError();
 }
 

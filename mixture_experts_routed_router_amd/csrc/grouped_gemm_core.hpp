@@ -256,11 +256,13 @@ struct StageOffsets {
 // thread's token of each of its rows (issue_token_loads); a pad row (-1) reads
 // token 0 instead, its results are never read.
 //
-// PK (row-pair tiled operands): A (unless gathering) and bf16 W are stored as 2 x 32
+// PK (tiled operands): A (unless gathering) and bf16 W are stored as 2 x 32
 // blocks, row pair q and k block b at 128 * (q * K/32 + b) bytes, the even row's 64
-// bytes first. A stage's pieces of two neighbouring rows then fill one 128-byte
-// line instead of halves of two. The offsets here are those of stage 0; stage s
-// adds 128 s bytes (A: through the SGPR base, W: through the lane offset).
+// bytes first; FP8 W as 4 x 32-byte blocks, row quad q and k block b at
+// 128 * (q * K/32 + b). A stage's pieces of two (four) neighbouring rows then fill
+// one 128-byte line instead of halves (quarters) of two (four). The offsets here
+// are those of stage 0; stage s adds 128 s bytes (through the SGPR base, or part
+// of it through the lane offset).
 template <bool GLU, bool GATHER, bool W8, bool PK = false>
 __device__ __forceinline__ StageOffsets stage_offsets(const TileArgs& ta, int K, int N, int wave, int lane,
                                                       const uint32_t (&tok)[kPiecesPerThread]) {
@@ -309,7 +311,9 @@ __device__ __forceinline__ StageOffsets stage_offsets(const TileArgs& ta, int K,
             const int c = ta.nt * BN + r;
             wr = c < N ? c : N - 1;
         }
-        o.b[0] = (uint32_t)wr * (uint32_t)K + (uint32_t)(piece * 16);
+        // PK: the codes in 4-row tiled order, 4 rows x 32 bytes per 128-byte block
+        if (PK) o.b[0] = (uint32_t)(wr >> 2) * (uint32_t)K * 4u + (uint32_t)(wr & 3) * 32u + (uint32_t)piece * 16u;
+        else o.b[0] = (uint32_t)wr * (uint32_t)K + (uint32_t)(piece * 16);
     }
     return o;
 }
@@ -340,8 +344,8 @@ __device__ __forceinline__ void read_tokens(const int32_t* region, int lane,
 }
 
 // This thread's share of one stage: A and B pieces of k-stage kt of a tile into ring
-// slot `slot`. bx: bytes added to every bf16 W piece's offset (row-pair tiled W:
-// 64 per stage, the half of its 128-byte stride the SGPR base does not take).
+// slot `slot`. bx: bytes added to every W piece's offset (tiled W in the gathering
+// variant: the part of its 128-byte stride the SGPR base does not take).
 template <bool W8>
 __device__ __forceinline__ void issue_stage(uint32_t lds0, int slot, int wave, const uint16_t* ga,
                                             const char* gb, const StageOffsets& o, uint32_t bx) {
@@ -352,7 +356,7 @@ __device__ __forceinline__ void issue_stage(uint32_t lds0, int slot, int wave, c
         dma16(sa + (kPiecesPerThread * wave + i) * 1024, ga, o.a[i]);
         if (!W8) dma16(sb + (kPiecesPerThread * wave + i) * 1024, gb, o.b[i] + bx);
     }
-    if (W8) dma16(sb + wave * 1024, gb, o.b[0]);
+    if (W8) dma16(sb + wave * 1024, gb, o.b[0] + bx);
 }
 
 // 8 E4M3 codes (two dwords, k order) -> 8 bf16, exactly (every E4M3 value is a bf16 value).
@@ -431,8 +435,8 @@ __device__ __forceinline__ int run_tile(const WaveCtx& w, const TileArgs& ta, co
     constexpr int AST = (PK && !GATHER) ? 2 * BK : BK;
     // (the gathering variant keeps W's base stride and adds the rest per lane: with the
     // full stride in the base, the compiler runs out of SGPRs for it)
-    constexpr int WST = (PK && !W8 && !GATHER) ? 4 * BK : BK * WB;
-    constexpr uint32_t WX = (PK && !W8 && GATHER) ? 64u : 0u;
+    constexpr int WST = (PK && !GATHER) ? 4 * BK : BK * WB;
+    constexpr uint32_t WX = (PK && GATHER) ? (uint32_t)(4 * BK - BK * WB) : 0u;
 
     // LDS B row of each of this wave's 32-column blocks. GLU: the first half of
     // the blocks are gate columns, the second half the matching up columns.

@@ -51,4 +51,38 @@ hipError_t launch_tile_rows(const uint16_t* src, int64_t rows, int cols, uint16_
     return hipGetLastError();
 }
 
+// FP8 codes [R, K] (R % 4 == 0, K % 32 == 0) in 4-row tiled order: 4 x 32-byte
+// blocks, code (r, c) at ((r / 4) * (K / 32) + c / 32) * 128 + (r % 4) * 32 + c % 32.
+// Thread step: 16-byte piece q = (r, c16) -> slot ((r/4)(K/32) + c16/2) * 8 + (r%4) * 2 + c16 % 2.
+template <bool TO_TILED>
+__global__ __launch_bounds__(kTileThreads) void tile_quads_kernel(const uint4* __restrict__ src, int64_t rows,
+                                                                  int cols, uint4* __restrict__ dst) {
+    MOE_DEBUG_GUARD();
+    const int ppr = cols / 16;
+    const int64_t total = rows * (int64_t)ppr;
+    const int64_t stride = (int64_t)gridDim.x * kTileThreads;
+    for (int64_t q = (int64_t)blockIdx.x * kTileThreads + threadIdx.x; q < total; q += stride) {
+        const int64_t r = q / ppr;
+        const int c = (int)(q - r * ppr);
+        const int64_t t = ((r >> 2) * (ppr >> 1) + (c >> 1)) * 8 + (r & 3) * 2 + (c & 1);
+        if (TO_TILED) dst[t] = src[q];
+        else dst[q] = src[t];
+    }
+}
+
+hipError_t launch_tile_fp8_rows(const uint8_t* src, int64_t rows, int cols, uint8_t* dst, bool to_tiled,
+                                hipStream_t stream) {
+    const int64_t total = rows * (int64_t)(cols / 16);
+    if (total == 0) return hipGetLastError();
+    const int64_t want = (total + kTileThreads - 1) / kTileThreads;
+    const unsigned grid = (unsigned)(want < 8192 ? want : 8192);
+    if (to_tiled)
+        hipLaunchKernelGGL(tile_quads_kernel<true>, dim3(grid), dim3(kTileThreads), 0, stream, (const uint4*)src,
+                           rows, cols, (uint4*)dst);
+    else
+        hipLaunchKernelGGL(tile_quads_kernel<false>, dim3(grid), dim3(kTileThreads), 0, stream, (const uint4*)src,
+                           rows, cols, (uint4*)dst);
+    return hipGetLastError();
+}
+
 }  // namespace moe

@@ -64,6 +64,10 @@ def lib():
     lib.moe_grouped_glu_gemm_tiled.argtypes = lib.moe_grouped_glu_gemm.argtypes
     lib.moe_grouped_down_gemm_tiled.argtypes = lib.moe_grouped_down_gemm.argtypes
     lib.moe_grouped_glu_gemm_gather_tiled.argtypes = lib.moe_grouped_glu_gemm_gather.argtypes
+    lib.moe_tile_fp8_rows.argtypes = [vp, i64, i32, vp, vp]
+    lib.moe_untile_fp8_rows.argtypes = [vp, i64, i32, vp, vp]
+    lib.moe_grouped_glu_gemm_fp8w_tiled.argtypes = lib.moe_grouped_glu_gemm_fp8w.argtypes
+    lib.moe_grouped_down_gemm_fp8w_tiled.argtypes = lib.moe_grouped_down_gemm_fp8w.argtypes
     return lib
 
 
@@ -348,3 +352,16 @@ def test_tiled_validation(lib):
     assert fn(FAKE, FAKE, FAKE, FAKE, FAKE, 100, 8, 128, 256, 1001, FAKE, None) == SHAPE
     assert fn(FAKE, None, FAKE, FAKE, FAKE, 100, 8, 128, 256, 1000, FAKE, None) == NULLP
     assert fn(FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, 8, 2048, 256, 1000, FAKE, None) == OVERFLOW
+
+
+def test_tiled_fp8_validation(lib):
+    for fn in (lib.moe_tile_fp8_rows, lib.moe_untile_fp8_rows):
+        assert fn(None, 8, 64, FAKE, None) == NULLP
+        assert fn(FAKE, 6, 64, FAKE + 4096, None) == SHAPE        # rows % 4
+        assert fn(FAKE, 8, 48, FAKE + 4096, None) == SHAPE        # cols % 32
+        assert fn(FAKE, 8, 64, FAKE, None) == VALUE               # in place
+        assert fn(None, 0, 64, None, None) == OK
+    for fn in (lib.moe_grouped_glu_gemm_fp8w_tiled, lib.moe_grouped_down_gemm_fp8w_tiled):
+        assert fn(FAKE, FAKE, FAKE, FAKE, FAKE, 8, 128, 256, 1001, FAKE, None) == SHAPE   # odd P_max
+        assert fn(FAKE, FAKE, None, FAKE, FAKE, 8, 128, 256, 1000, FAKE, None) == NULLP   # no scales
+        assert fn(FAKE, FAKE, FAKE, FAKE, FAKE, 8, 100, 256, 1000, FAKE, None) == SHAPE   # H % 64

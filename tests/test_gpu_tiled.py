@@ -210,3 +210,92 @@ def test_tiled_layer_rejects_mixed_weights(gpu_lib):
     til = gpu_lib.MoELayer(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.align, tiled=True)
     with pytest.raises(ValueError):
         til(dev_bf16(d["x"]), dev(d["logits"]), dev_bf16(d["w_gu"]), dev_bf16(d["w_d"]))
+
+
+# --------------------------------------------------------------------------------------
+# FP8 weights in 4-row tiled order
+# --------------------------------------------------------------------------------------
+
+def _np_tile_fp8(a: np.ndarray) -> np.ndarray:
+    """Codes [R, K] -> 4-row tiled order, from the formula
+    ((r/4)(K/32) + c/32) * 128 + (r%4) * 32 + c%32."""
+    R, K = a.shape
+    r = np.arange(R)[:, None]
+    c = np.arange(K)[None, :]
+    idx = ((r // 4) * (K // 32) + c // 32) * 128 + (r % 4) * 32 + c % 32
+    out = np.empty(R * K, a.dtype)
+    out[idx.ravel()] = a.ravel()
+    return out.reshape(R, K)
+
+
+@pytest.mark.parametrize("R,K", [(4, 32), (8, 64), (132, 96), (2048, 2880)], ids=["4x32", "8x64", "132x96", "2048x2880"])
+def test_tile_fp8_rows(gpu_lib, R, K):
+    _say(f"tile_fp8_rows {R}x{K}")
+    a = np.random.default_rng(R + K).integers(0, 256, size=(R, K), dtype=np.uint8)
+    if R * K <= 8 * 64:
+        flat = _np_tile_fp8(a).ravel()
+        for r in range(R):
+            for c in range(K):
+                assert flat[((r // 4) * (K // 32) + c // 32) * 128 + (r % 4) * 32 + c % 32] == a[r, c]
+    q = gpu_lib.FP8Weights(dev(a.reshape(1, R, K)), torch.zeros((1, max(R // 64, 1)), device="cuda"))
+    t = gpu_lib.tile_fp8_weights(q)
+    back = gpu_lib.untile_fp8_rows(t.w8.view(R, K))
+    torch.cuda.synchronize()
+    assert (t.w8.view(R, K).cpu().numpy() == _np_tile_fp8(a)).all()
+    assert (back.cpu().numpy() == a).all()
+
+
+@pytest.mark.parametrize("case", GEMM_CASES, ids=[c[0] for c in GEMM_CASES])
+def test_tiled_fp8_gemms(gpu_lib, case):
+    """FP8-weight gate/up and down GEMMs on tiled operands against the row-major
+    FP8 calls: bit for bit where those run the MFMA tiles (P_max > 64 E), within
+    one bf16 rounding where they run the weight-streaming kernel."""
+    name, counts, align, H, I = case
+    _say(f"tiled fp8 gemms case {name}")
+    counts, offsets = _synthetic_layout(counts, align)
+    E, P = len(counts), int(offsets[-1])
+    P_max = gpu_lib.even_rows(P + 64)
+    rows = _rows_of(counts, offsets)
+    x_perm = np.zeros((P_max, H), np.uint16)
+    x_perm[rows] = gen.random_bf16((len(rows), H), seed=1)
+    h_in = np.zeros((P_max, I), np.uint16)
+    h_in[rows] = gen.random_bf16((len(rows), I), seed=3)
+    q_gu = gpu_lib.quantize_fp8(dev_bf16(gen.random_bf16((E, 2 * I, H), seed=2, std=0.02)))
+    q_d = gpu_lib.quantize_fp8(dev_bf16(gen.random_bf16((E, H, I), seed=4, std=0.02)))
+    t_gu, t_d = gpu_lib.tile_fp8_weights(q_gu), gpu_lib.tile_fp8_weights(q_d)
+    cd, od = dev(counts), dev(offsets)
+    xd, hd = dev_bf16(x_perm), dev_bf16(h_in)
+    h = gpu_lib.grouped_glu_gemm_fp8w(xd, q_gu, cd, od)
+    h_t = gpu_lib.grouped_glu_gemm_fp8w(gpu_lib.tile_rows(xd), t_gu, cd, od)
+    y = gpu_lib.grouped_down_gemm_fp8w(hd, q_d, cd, od)
+    y_t = gpu_lib.grouped_down_gemm_fp8w(gpu_lib.tile_rows(hd), t_d, cd, od)
+    torch.cuda.synchronize()
+    h_u = gpu_lib.untile_rows(h_t)
+    ri = dev(rows)
+    if P_max > 64 * E:
+        assert _same_bits(h_u[:P], h[:P]), "gate/up"
+        assert _same_bits(y_t[:P], y[:P]), "down"
+    else:
+        assert_close_bf16(host_f64(h_u[ri]), host_f64(h[ri]), f"h_fp8_tiled[{name}]")
+        assert_close_bf16(host_f64(y_t[ri]), host_f64(y[ri]), f"y_fp8_tiled[{name}]")
+
+
+@pytest.mark.parametrize("cfg", SMALL_LAYERS + [gen.CONFIGS[n] for n, _ in FULL_SIZE],
+                         ids=[c.name for c in SMALL_LAYERS] + [n for n, _ in FULL_SIZE])
+def test_tiled_fp8_layer(gpu_lib, cfg):
+    """The tiled layer with tiled FP8 weights against the row-major FP8 layer: bit for
+    bit where the latter runs the MFMA tiles, else within the layer gate."""
+    _say(f"tiled fp8 layer {cfg.name}")
+    d = gen.make_inputs(cfg)
+    x, logits = dev_bf16(d["x"]), dev(d["logits"])
+    q_gu, q_d = gpu_lib.quantize_fp8(dev_bf16(d["w_gu"])), gpu_lib.quantize_fp8(dev_bf16(d["w_d"]))
+    ref = gpu_lib.MoELayer(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.align)
+    ref(x, logits, q_gu, q_d)
+    til = gpu_lib.MoELayer(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.align, tiled=True)
+    til(x, logits, gpu_lib.tile_fp8_weights(q_gu), gpu_lib.tile_fp8_weights(q_d))
+    torch.cuda.synchronize()
+    assert torch.equal(til.layout.offsets, ref.layout.offsets)
+    if ref.P_max > 64 * cfg.E:
+        assert _same_bits(til.out, ref.out), "out"
+    else:
+        assert_close_bf16(host_f64(til.out), host_f64(ref.out), f"tiled fp8 out[{cfg.name}]", tight=False)
