@@ -197,6 +197,12 @@ WG_CASES = [
     # 576 tiles, more than one workgroup per CU, and about a fifth of the experts
     # with no rows (their gradient tiles are written as zeros)
     ("many_tiles_persistent", _many_counts(96, 70, 45), 32, 768, 512),
+    # two tile rows per expert: units (tile rows) dealt to the XCDs in snake order
+    # over several rounds, under skewed row counts
+    ("zipf_snake_units", np.random.default_rng(47).permutation([int(900 / (i + 1) ** 1.2) for i in range(40)]).tolist(),
+     32, 512, 256),
+    # more than 256 experts: no ranking, experts taken by id
+    ("e300_by_id", _many_counts(300, 40, 46), 32, 512, 128),
 ]
 
 
