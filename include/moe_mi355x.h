@@ -33,6 +33,8 @@
  *                          GEMM (dh never reaches memory)
  *   moe_swiglu, moe_swiglu_backward, moe_transpose_experts, moe_combine_backward,
  *   moe_route_backward, moe_permute_backward, moe_grouped_wgrad
+ *   on row-pair tiled operands: moe_grouped_gemm_tiled, moe_swiglu_tiled,
+ *   moe_swiglu_backward_tiled, moe_grouped_wgrad_tiled
  *
  * Sources (page title, section):
  *   [Halo]      Halo, "Performance": Levers that help (grouped GEMM instead of a
@@ -574,6 +576,49 @@ moe_status moe_permute_backward(const moe_bf16 *dx_perm, const int32_t *route_ro
 moe_status moe_grouped_wgrad(const moe_bf16 *a, const moe_bf16 *b, const int32_t *row_token,
                              const int32_t *expert_counts, const int32_t *expert_offsets, int32_t E,
                              int32_t M, int32_t N, int64_t P_max, float *dw, moe_stream_t stream);
+
+/*
+ * The training steps on row-pair tiled operands (the order moe_tile_rows writes,
+ * see "Row-pair tiled operands" above). Each call computes exactly what its
+ * row-major counterpart computes -- the same MFMAs, the same fp32 order, the same
+ * roundings -- so its outputs are those of that call bit for bit once un-tiled;
+ * only where operands are read from and written to changes. Recipe (the weights
+ * tiled once per update: w_gate_up and w_down as for the tiled forward, and
+ * w_gate_up^T [E, H, 2I] from moe_transpose_experts, then moe_tile_rows):
+ *   forward:  moe_route_topk, moe_permute_tiled (x_perm tiled),
+ *             gu = moe_grouped_gemm_tiled(x_perm, w_gate_up) (gu row-major),
+ *             h = moe_swiglu_tiled(gu) (h tiled), y = moe_grouped_down_gemm_tiled(h, w_down),
+ *             out = moe_combine(y)
+ *   backward: dy, dw = moe_combine_backward(dout, y) (row-major), moe_route_backward,
+ *             dh = moe_grouped_gemm(dy, w_down^T) (row-major operands),
+ *             dgu = moe_swiglu_backward_tiled(dh, gu) (dgu tiled),
+ *             dx_perm = moe_grouped_gemm_tiled(dgu, w_gate_up^T tiled) (dx_perm row-major),
+ *             moe_permute_backward,
+ *             dW_down = moe_grouped_wgrad_tiled(dy, 0, h, 1),
+ *             dW_gate_up = moe_grouped_wgrad_tiled(dgu, 1, x_perm, 1).
+ *
+ * moe_grouped_gemm_tiled: moe_grouped_gemm with a [P_max, K] and w [E, N, K] tiled;
+ *   c [P_max, N] row-major out.
+ * moe_swiglu_tiled: moe_swiglu with h [P_max, I] written tiled; a row of the last
+ *   pair at or past offsets[E] is written as zeros.
+ * moe_swiglu_backward_tiled: moe_swiglu_backward (dh and gu row-major) with
+ *   dgu [P_max, 2I] written tiled; a row of the last pair at or past offsets[E] is
+ *   written as zeros.
+ * moe_grouped_wgrad_tiled: moe_grouped_wgrad (no row_token) with a, b each
+ *   row-major (0) or tiled (1): a_tiled, b_tiled outside {0, 1}: MOE_ERR_INVALID_SHAPE.
+ * Shapes as for the row-major calls; P_max must be even where an operand is tiled
+ * (MOE_ERR_INVALID_SHAPE otherwise).
+ */
+moe_status moe_grouped_gemm_tiled(const moe_bf16 *a, const moe_bf16 *w, const int32_t *expert_counts,
+                                  const int32_t *expert_offsets, int32_t E, int32_t K, int32_t N, int64_t P_max,
+                                  moe_bf16 *c, moe_stream_t stream);
+moe_status moe_swiglu_tiled(const moe_bf16 *gu, const int32_t *expert_offsets, int32_t E, int32_t I,
+                            int64_t P_max, moe_bf16 *h, moe_stream_t stream);
+moe_status moe_swiglu_backward_tiled(const moe_bf16 *dh, const moe_bf16 *gu, const int32_t *expert_offsets,
+                                     int32_t E, int32_t I, int64_t P_max, moe_bf16 *dgu, moe_stream_t stream);
+moe_status moe_grouped_wgrad_tiled(const moe_bf16 *a, int32_t a_tiled, const moe_bf16 *b, int32_t b_tiled,
+                                   const int32_t *expert_counts, const int32_t *expert_offsets, int32_t E, int32_t M,
+                                   int32_t N, int64_t P_max, float *dw, moe_stream_t stream);
 
 /*
  * Debug build [prime-rl, Changes: 32-bit row offsets overflowed silently -- a bad

@@ -16,7 +16,8 @@ _API = ("route_topk", "permute", "grouped_glu_gemm", "grouped_down_gemm", "combi
         "route_backward", "permute_backward", "grouped_wgrad", "MoETrainingLayer", "router_prepare",
         "router_topk", "tile_rows", "untile_rows", "tile_weights", "TiledWeights", "even_rows",
         "grouped_glu_gemm_tiled", "grouped_glu_gemm_gather_tiled", "grouped_down_gemm_tiled",
-        "tile_fp8_weights", "untile_fp8_rows")
+        "tile_fp8_weights", "untile_fp8_rows", "grouped_gemm_tiled", "swiglu_tiled", "swiglu_backward_tiled",
+        "grouped_wgrad_tiled", "training_weights")
 
 
 def __getattr__(name):

@@ -108,6 +108,11 @@ def _open(debug: bool):
     lib.moe_permute_backward.argtypes = [_c_vp, _c_vp, _c_i64, _c_i32, _c_i32, _c_i64, _c_vp, _c_vp]
     lib.moe_grouped_wgrad.argtypes = [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32, _c_i64,
                                       _c_vp, _c_vp]
+    lib.moe_grouped_wgrad_tiled.argtypes = [_c_vp, _c_i32, _c_vp, _c_i32, _c_vp, _c_vp, _c_i32, _c_i32, _c_i32,
+                                            _c_i64, _c_vp, _c_vp]
+    lib.moe_grouped_gemm_tiled.argtypes = lib.moe_grouped_gemm.argtypes
+    lib.moe_swiglu_tiled.argtypes = lib.moe_swiglu.argtypes
+    lib.moe_swiglu_backward_tiled.argtypes = lib.moe_swiglu_backward.argtypes
     lib.moe_router_prepare.argtypes = [_c_vp, _c_i32, _c_i32, _c_vp, _c_vp, _c_vp]
     lib.moe_router_topk.argtypes = [_c_vp, _c_vp, _c_vp, _c_i64, _c_i32, _c_i32, _c_i32, _c_vp, _c_vp, _c_vp,
                                     _c_vp]
@@ -148,7 +153,9 @@ def _open(debug: bool):
                "moe_grouped_glu_gemm_gather_fp8w", "moe_grouped_down_gemm_fp8w", "moe_grouped_gemm",
                "moe_swiglu", "moe_swiglu_backward", "moe_transpose_experts", "moe_combine_backward",
                "moe_route_backward", "moe_permute_backward", "moe_grouped_wgrad", "moe_router_prepare",
-               "moe_router_topk", "moe_grouped_gemm_swiglu_backward", "moe_grouped_glu_gemm_clamped"):
+               "moe_router_topk", "moe_grouped_gemm_swiglu_backward", "moe_grouped_glu_gemm_clamped",
+               "moe_grouped_gemm_tiled", "moe_swiglu_tiled", "moe_swiglu_backward_tiled",
+               "moe_grouped_wgrad_tiled"):
         getattr(lib, fn).restype = ctypes.c_int
     _HANDLES[debug] = lib
     return lib
@@ -857,21 +864,99 @@ def grouped_wgrad(a, b, counts, offsets, row_token=None, dw=None, stream=None):
     return dw
 
 
+# the training steps on row-pair tiled operands (each bit for bit its row-major
+# counterpart once un-tiled)
+
+def grouped_gemm_tiled(a, w: TiledWeights, counts, offsets, c=None, stream=None):
+    """grouped_gemm with a [P_max, K] and the weights [E, N, K] tiled; c row-major."""
+    P_max, K = a.shape
+    E, N, K2 = w.shape
+    if not isinstance(w, TiledWeights):
+        raise TypeError("w must be TiledWeights (tile_weights)")
+    if K2 != K:
+        raise ValueError("w must be [E, N, K] with K = a.shape[1]")
+    if c is None:
+        c = torch.empty((P_max, N), dtype=torch.bfloat16, device=a.device)
+    _call("moe_grouped_gemm_tiled", _ptr(a, torch.bfloat16, "a"), _ptr(w.data, torch.bfloat16, "w"),
+          _ptr(counts, torch.int32, "counts", (E,)), _ptr(offsets, torch.int32, "offsets", (E + 1,)),
+          E, K, N, P_max, _ptr(c, torch.bfloat16, "c", (P_max, N)), _stream(stream))
+    return c
+
+
+def swiglu_tiled(gu, offsets, h=None, stream=None):
+    """swiglu with h written in tiled order."""
+    P_max, two_i = gu.shape
+    E = offsets.shape[0] - 1
+    if h is None:
+        h = torch.empty((P_max, two_i // 2), dtype=torch.bfloat16, device=gu.device)
+    _call("moe_swiglu_tiled", _ptr(gu, torch.bfloat16, "gu"), _ptr(offsets, torch.int32, "offsets", (E + 1,)), E,
+          two_i // 2, P_max, _ptr(h, torch.bfloat16, "h", (P_max, two_i // 2)), _stream(stream))
+    return h
+
+
+def swiglu_backward_tiled(dh, gu, offsets, dgu=None, stream=None):
+    """swiglu_backward (dh, gu row-major) with dgu written in tiled order."""
+    P_max, I = dh.shape
+    E = offsets.shape[0] - 1
+    if dgu is None:
+        dgu = torch.empty((P_max, 2 * I), dtype=torch.bfloat16, device=dh.device)
+    _call("moe_swiglu_backward_tiled", _ptr(dh, torch.bfloat16, "dh"),
+          _ptr(gu, torch.bfloat16, "gu", (P_max, 2 * I)), _ptr(offsets, torch.int32, "offsets", (E + 1,)), E, I,
+          P_max, _ptr(dgu, torch.bfloat16, "dgu", (P_max, 2 * I)), _stream(stream))
+    return dgu
+
+
+def grouped_wgrad_tiled(a, b, counts, offsets, a_tiled: bool, b_tiled: bool, dw=None, stream=None):
+    """grouped_wgrad with a and / or b in tiled order (no row_token)."""
+    P_max, M = a.shape
+    N = b.shape[1]
+    E = counts.shape[0]
+    if dw is None:
+        dw = torch.empty((E, M, N), dtype=torch.float32, device=a.device)
+    _call("moe_grouped_wgrad_tiled", _ptr(a, torch.bfloat16, "a"), int(bool(a_tiled)),
+          _ptr(b, torch.bfloat16, "b", (P_max, N)), int(bool(b_tiled)), _ptr(counts, torch.int32, "counts", (E,)),
+          _ptr(offsets, torch.int32, "offsets", (E + 1,)), E, M, N, P_max,
+          _ptr(dw, torch.float32, "dw", (E, M, N)), _stream(stream))
+    return dw
+
+
+def training_weights(w_gate_up, w_down, tiled: bool = False, stream=None):
+    """The four weight operands of MoETrainingLayer, made once per weight update:
+    (w_gate_up, w_down) for forward() and (w_gate_up^T, w_down^T) for backward().
+    tiled: the forward's pair and w_gate_up^T as TiledWeights; w_down^T stays
+    row-major (its GEMM reads dy, which the combine backward writes row-major)."""
+    wgu_t = transpose_experts(w_gate_up, stream=stream)
+    wd_t = transpose_experts(w_down, stream=stream)
+    if not tiled:
+        return w_gate_up, w_down, wgu_t, wd_t
+    return (tile_weights(w_gate_up, stream=stream), tile_weights(w_down, stream=stream),
+            tile_weights(wgu_t, stream=stream), wd_t)
+
+
 class MoETrainingLayer:
     """Forward that keeps what the backward needs (x_perm, gu = [g | u], h, y), and
     the backward: dx, dlogits and fp32 weight gradients. All buffers are
     preallocated; forward() and backward() only enqueue library calls.
-    The backward takes the weights transposed once per update (transpose_experts).
+    The backward takes the weights transposed once per update (transpose_experts;
+    training_weights makes all four).
     fuse_swiglu_backward: dh and its SwiGLU backward in one GEMM
     (grouped_gemm_swiglu_backward), or, by default, grouped_gemm + swiglu_backward
     with dh written to memory -- the two steps measured faster on MI355X (the fused
-    epilogue's gu loads wait behind the next tile's prefetched stages)."""
+    epilogue's gu loads wait behind the next tile's prefetched stages).
+    tiled=True: x_perm, h and dgu in row-pair tiled order and the GEMMs on tiled
+    operands (training_weights(..., tiled=True)); P_max is rounded up to even. Every
+    output is bit for bit the row-major layer's."""
 
     def __init__(self, T: int, H: int, E: int, k: int, I: int, align: int = 32, device="cuda",
-                 fuse_swiglu_backward: bool = False):
+                 fuse_swiglu_backward: bool = False, tiled: bool = False):
         self.T, self.H, self.E, self.k, self.I, self.align = T, H, E, k, I, align
+        if tiled and fuse_swiglu_backward:
+            raise ValueError("the fused dh GEMM has no tiled form: tiled layers run the two steps")
         self.fuse_swiglu_backward = fuse_swiglu_backward
+        self.tiled = tiled
         self.P_max = padded_rows_max(T, k, E, align)
+        if tiled:
+            self.P_max = even_rows(self.P_max)
         dev = torch.device(device)
         bf = dict(dtype=torch.bfloat16, device=dev)
         f32 = dict(dtype=torch.float32, device=dev)
@@ -889,22 +974,45 @@ class MoETrainingLayer:
         self.dx = torch.empty((T, H), **bf)
         self.dw_gu, self.dw_d = torch.empty((E, 2 * I, H), **f32), torch.empty((E, H, I), **f32)
 
+    def _check_weights(self, *ws, row_major_last=False):
+        for i, w in enumerate(ws):
+            want = self.tiled and not (row_major_last and i == len(ws) - 1)
+            if isinstance(w, TiledWeights) != want:
+                raise ValueError("a tiled training layer takes the weights of training_weights(..., tiled=True), "
+                                 "a row-major one plain tensors")
+
     def forward(self, x, logits, w_gate_up, w_down, stream=None):
+        self._check_weights(w_gate_up, w_down)
         route_topk(logits, self.k, self.topk_idx, self.topk_w, stream=stream)
         L = permute(x, self.topk_idx, self.E, self.align, self.P_max, out=self.layout, workspace=self.workspace,
-                    stream=stream)
-        grouped_gemm(L.x_perm, w_gate_up, L.counts, L.offsets, c=self.gu, stream=stream)
-        swiglu(self.gu, L.offsets, h=self.h, stream=stream)
-        grouped_down_gemm(self.h, w_down, L.counts, L.offsets, y=self.y, stream=stream)
+                    stream=stream, tiled=self.tiled)
+        if self.tiled:
+            grouped_gemm_tiled(L.x_perm, w_gate_up, L.counts, L.offsets, c=self.gu, stream=stream)
+            swiglu_tiled(self.gu, L.offsets, h=self.h, stream=stream)
+            grouped_down_gemm_tiled(self.h, w_down, L.counts, L.offsets, y=self.y, stream=stream)
+        else:
+            grouped_gemm(L.x_perm, w_gate_up, L.counts, L.offsets, c=self.gu, stream=stream)
+            swiglu(self.gu, L.offsets, h=self.h, stream=stream)
+            grouped_down_gemm(self.h, w_down, L.counts, L.offsets, y=self.y, stream=stream)
         combine(self.y, L.route_row, self.topk_w, out=self.out, stream=stream)
         return self.out
 
     def backward(self, dout, w_gate_up_t, w_down_t, stream=None):
-        """w_gate_up_t [E, H, 2I] and w_down_t [E, I, H] from transpose_experts."""
+        """w_gate_up_t [E, H, 2I] and w_down_t [E, I, H] from transpose_experts
+        (tiled layer: w_gate_up_t as TiledWeights, w_down_t row-major)."""
+        self._check_weights(w_gate_up_t, w_down_t, row_major_last=True)
         L = self.layout
         combine_backward(dout, self.y, L.route_row, self.topk_w, L.row_token, L.offsets, dy=self.dy, dw=self.dw,
                          stream=stream)
         route_backward(self.topk_idx, self.topk_w, self.dw, self.E, dlogits=self.dlogits, stream=stream)
+        if self.tiled:
+            grouped_gemm(self.dy, w_down_t, L.counts, L.offsets, c=self.dh, stream=stream)
+            swiglu_backward_tiled(self.dh, self.gu, L.offsets, dgu=self.dgu, stream=stream)
+            grouped_gemm_tiled(self.dgu, w_gate_up_t, L.counts, L.offsets, c=self.dx_perm, stream=stream)
+            permute_backward(self.dx_perm, L.route_row, self.T, self.k, dx=self.dx, stream=stream)
+            grouped_wgrad_tiled(self.dy, self.h, L.counts, L.offsets, False, True, dw=self.dw_d, stream=stream)
+            grouped_wgrad_tiled(self.dgu, L.x_perm, L.counts, L.offsets, True, True, dw=self.dw_gu, stream=stream)
+            return self.dx, self.dlogits, self.dw_gu, self.dw_d
         if self.fuse_swiglu_backward:
             grouped_gemm_swiglu_backward(self.dy, w_down_t, self.gu, L.counts, L.offsets, dgu=self.dgu,
                                          stream=stream)

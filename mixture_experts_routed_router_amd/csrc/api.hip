@@ -43,13 +43,13 @@ hipError_t launch_grouped_glu_gemm_clamped(const uint16_t*, const uint16_t*, con
 hipError_t launch_grouped_gemm_swiglu_bwd(const uint16_t*, const uint16_t*, const uint16_t*, const int32_t*, int,
                                           int, int, uint16_t*, int, hipStream_t);
 hipError_t launch_swiglu(const uint16_t*, const uint16_t*, const int32_t*, int, int, int64_t, uint16_t*,
-                         hipStream_t);
+                         hipStream_t, bool tiled_out);
 hipError_t launch_transpose(const uint16_t*, int64_t, int, int, uint16_t*, hipStream_t);
 hipError_t launch_router_prepare(const float*, int, int, uint16_t*, uint16_t*, hipStream_t);
 hipError_t launch_router_topk(const uint16_t*, const uint16_t*, const uint16_t*, int64_t, int, int, int, float*,
                               int32_t*, float*, hipStream_t);
 hipError_t launch_wgrad(const uint16_t*, const uint16_t*, const int32_t*, const int32_t*, int, int, int, float*,
-                        hipStream_t);
+                        hipStream_t, bool a_tiled, bool b_tiled);
 hipError_t launch_combine(const uint16_t*, const int32_t*, const float*, int64_t, int, int,
                           int64_t, uint16_t*, hipStream_t);
 hipError_t launch_probe_copy(const void*, void*, size_t, int, hipStream_t);
@@ -673,6 +673,18 @@ moe_status moe_grouped_gemm(const moe_bf16* a, const moe_bf16* w, const int32_t*
                       "moe_grouped_gemm launch");
 }
 
+moe_status moe_grouped_gemm_tiled(const moe_bf16* a, const moe_bf16* w, const int32_t* expert_counts,
+                                  const int32_t* expert_offsets, int32_t E, int32_t K, int32_t N, int64_t P_max,
+                                  moe_bf16* c, moe_stream_t stream) {
+    moe_status s = check_gemm(a, w, expert_counts, expert_offsets, E, N, K, P_max, c);
+    if (s != MOE_OK) return s;
+    if ((s = check_even_pmax(P_max)) != MOE_OK) return s;
+    DEBUG_CHECK(moe::debug_check_layout(expert_counts, expert_offsets, E, P_max, (hipStream_t)stream));
+    return hip_status(moe::launch_grouped_down_gemm_tiled(a, w, nullptr, expert_offsets, E, N, K, c, (int)P_max,
+                                                          (hipStream_t)stream),
+                      "moe_grouped_gemm_tiled launch");
+}
+
 static moe_status check_swiglu(const int32_t* offsets, int32_t E, int32_t I, int64_t P_max) {
     REQUIRE_PTR(offsets);
     if (E < 1 || E > MOE_MAX_E) return fail(MOE_ERR_INVALID_SHAPE, "E=%d outside [1, %d]", E, MOE_MAX_E);
@@ -688,7 +700,7 @@ moe_status moe_swiglu(const moe_bf16* gu, const int32_t* expert_offsets, int32_t
     moe_status s = check_swiglu(expert_offsets, E, I, P_max);
     if (s != MOE_OK) return s;
     DEBUG_CHECK(moe::debug_check_layout(nullptr, expert_offsets, E, P_max, (hipStream_t)stream));
-    return hip_status(moe::launch_swiglu(gu, nullptr, expert_offsets, E, I, P_max, h, (hipStream_t)stream),
+    return hip_status(moe::launch_swiglu(gu, nullptr, expert_offsets, E, I, P_max, h, (hipStream_t)stream, false),
                       "moe_swiglu launch");
 }
 
@@ -700,8 +712,33 @@ moe_status moe_swiglu_backward(const moe_bf16* dh, const moe_bf16* gu, const int
     moe_status s = check_swiglu(expert_offsets, E, I, P_max);
     if (s != MOE_OK) return s;
     DEBUG_CHECK(moe::debug_check_layout(nullptr, expert_offsets, E, P_max, (hipStream_t)stream));
-    return hip_status(moe::launch_swiglu(gu, dh, expert_offsets, E, I, P_max, dgu, (hipStream_t)stream),
+    return hip_status(moe::launch_swiglu(gu, dh, expert_offsets, E, I, P_max, dgu, (hipStream_t)stream, false),
                       "moe_swiglu_backward launch");
+}
+
+moe_status moe_swiglu_tiled(const moe_bf16* gu, const int32_t* expert_offsets, int32_t E, int32_t I,
+                            int64_t P_max, moe_bf16* h, moe_stream_t stream) {
+    REQUIRE_PTR(gu);
+    REQUIRE_PTR(h);
+    moe_status s = check_swiglu(expert_offsets, E, I, P_max);
+    if (s != MOE_OK) return s;
+    if ((s = check_even_pmax(P_max)) != MOE_OK) return s;
+    DEBUG_CHECK(moe::debug_check_layout(nullptr, expert_offsets, E, P_max, (hipStream_t)stream));
+    return hip_status(moe::launch_swiglu(gu, nullptr, expert_offsets, E, I, P_max, h, (hipStream_t)stream, true),
+                      "moe_swiglu_tiled launch");
+}
+
+moe_status moe_swiglu_backward_tiled(const moe_bf16* dh, const moe_bf16* gu, const int32_t* expert_offsets,
+                                     int32_t E, int32_t I, int64_t P_max, moe_bf16* dgu, moe_stream_t stream) {
+    REQUIRE_PTR(dh);
+    REQUIRE_PTR(gu);
+    REQUIRE_PTR(dgu);
+    moe_status s = check_swiglu(expert_offsets, E, I, P_max);
+    if (s != MOE_OK) return s;
+    if ((s = check_even_pmax(P_max)) != MOE_OK) return s;
+    DEBUG_CHECK(moe::debug_check_layout(nullptr, expert_offsets, E, P_max, (hipStream_t)stream));
+    return hip_status(moe::launch_swiglu(gu, dh, expert_offsets, E, I, P_max, dgu, (hipStream_t)stream, true),
+                      "moe_swiglu_backward_tiled launch");
 }
 
 moe_status moe_grouped_gemm_swiglu_backward(const moe_bf16* dy, const moe_bf16* w_down_t, const moe_bf16* gu,
@@ -782,9 +819,9 @@ moe_status moe_permute_backward(const moe_bf16* dx_perm, const int32_t* route_ro
                       "moe_permute_backward launch");
 }
 
-moe_status moe_grouped_wgrad(const moe_bf16* a, const moe_bf16* b, const int32_t* row_token,
-                             const int32_t* expert_counts, const int32_t* expert_offsets, int32_t E, int32_t M,
-                             int32_t N, int64_t P_max, float* dw, moe_stream_t stream) {
+static moe_status check_wgrad(const moe_bf16* a, const moe_bf16* b, const int32_t* row_token,
+                              const int32_t* expert_counts, const int32_t* expert_offsets, int32_t E, int32_t M,
+                              int32_t N, int64_t P_max, float* dw) {
     REQUIRE_PTR(a);
     REQUIRE_PTR(b);
     REQUIRE_PTR(expert_counts);
@@ -800,9 +837,31 @@ moe_status moe_grouped_wgrad(const moe_bf16* a, const moe_bf16* b, const int32_t
     if ((s = check_pmax(P_max)) != MOE_OK) return s;
     const int64_t tiles = (int64_t)E * ((M + 255) / 256) * ((N + 255) / 256);
     if (tiles >= ((int64_t)1 << 31)) return fail(MOE_ERR_SIZE_OVERFLOW, "E*M*N/65536 tiles reach 2^31");
+    return ok();
+}
+
+moe_status moe_grouped_wgrad(const moe_bf16* a, const moe_bf16* b, const int32_t* row_token,
+                             const int32_t* expert_counts, const int32_t* expert_offsets, int32_t E, int32_t M,
+                             int32_t N, int64_t P_max, float* dw, moe_stream_t stream) {
+    moe_status s = check_wgrad(a, b, row_token, expert_counts, expert_offsets, E, M, N, P_max, dw);
+    if (s != MOE_OK) return s;
     DEBUG_CHECK(moe::debug_check_layout(expert_counts, expert_offsets, E, P_max, (hipStream_t)stream));
-    return hip_status(moe::launch_wgrad(a, b, row_token, expert_offsets, E, M, N, dw, (hipStream_t)stream),
+    return hip_status(moe::launch_wgrad(a, b, row_token, expert_offsets, E, M, N, dw, (hipStream_t)stream, false, false),
                       "moe_grouped_wgrad launch");
+}
+
+moe_status moe_grouped_wgrad_tiled(const moe_bf16* a, int32_t a_tiled, const moe_bf16* b, int32_t b_tiled,
+                                   const int32_t* expert_counts, const int32_t* expert_offsets, int32_t E, int32_t M,
+                                   int32_t N, int64_t P_max, float* dw, moe_stream_t stream) {
+    moe_status s = check_wgrad(a, b, nullptr, expert_counts, expert_offsets, E, M, N, P_max, dw);
+    if (s != MOE_OK) return s;
+    if ((a_tiled != 0 && a_tiled != 1) || (b_tiled != 0 && b_tiled != 1))
+        return fail(MOE_ERR_INVALID_SHAPE, "a_tiled=%d, b_tiled=%d: each must be 0 or 1", a_tiled, b_tiled);
+    if ((a_tiled || b_tiled) && (s = check_even_pmax(P_max)) != MOE_OK) return s;
+    DEBUG_CHECK(moe::debug_check_layout(expert_counts, expert_offsets, E, P_max, (hipStream_t)stream));
+    return hip_status(moe::launch_wgrad(a, b, nullptr, expert_offsets, E, M, N, dw, (hipStream_t)stream,
+                                        a_tiled != 0, b_tiled != 0),
+                      "moe_grouped_wgrad_tiled launch");
 }
 
 moe_status moe_router_prepare(const float* w_router, int32_t H, int32_t E, moe_bf16* w_hi, moe_bf16* w_lo,

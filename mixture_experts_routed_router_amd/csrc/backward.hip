@@ -163,19 +163,44 @@ __global__ __launch_bounds__(256) void route_bwd_kernel(const int32_t* __restric
 }
 
 // ---- SwiGLU forward (BWD false) and backward (BWD true) over used rows ----
+// gu [P_max, 2I] and dh [P_max, I] row-major. TO: the output (h, or dgu = [dg | du])
+// in row pairs (element (p, c) of a C-column matrix at (p/2)*2C + (c/32)*64 +
+// (p%2)*32 + c%32, the order moe_tile_rows writes), produced in storage order: the
+// forward's i-th 16-byte piece is h's i-th; the backward's i-th is dg's piece of the
+// pair's first I columns, du's sits 2I/8 pieces after it. A row of the last pair at
+// or past the used rows is written as zeros.
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
 
-template <bool BWD>
+template <bool BWD, bool TO>
 __global__ __launch_bounds__(256) void swiglu_kernel(const uint4* __restrict__ gu, const uint4* __restrict__ dh,
                                                      const int32_t* __restrict__ offsets, int E,
                                                      int64_t P_max, int pieces_i, uint4* __restrict__ out) {
     MOE_DEBUG_GUARD();
-    const int64_t used = offsets[E];
-    const int64_t n = (used < P_max ? used : P_max) * pieces_i;
+    const int64_t used = min((int64_t)offsets[E], P_max);
+    // TO: pieces over whole pairs (2 * pieces_i per pair: I/32 blocks of 8 pieces)
+    const int64_t n = TO ? (used + 1) / 2 * 2 * pieces_i : used * pieces_i;
+    const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
          i += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t p = i / pieces_i;
-        const int c = (int)(i - p * pieces_i);
+        int64_t p;
+        int c;
+        if (TO) {
+            const int64_t pr = i / (2 * pieces_i);
+            const int rem = (int)(i - pr * 2 * pieces_i);  // block rem / 8, piece rem % 8 of the block
+            p = 2 * pr + ((rem >> 2) & 1);
+            c = (rem >> 3) * 4 + (rem & 3);  // the row's 16-byte piece (8 columns)
+        } else {
+            p = i / pieces_i;
+            c = (int)(i - p * pieces_i);
+        }
+        // where the output piece(s) go
+        const int64_t o_g = TO ? (BWD ? i + (i / (2 * pieces_i)) * 2 * pieces_i : i) : (BWD ? p * 2 * pieces_i + c : i);
+        const int64_t o_u = TO ? o_g + 2 * pieces_i : o_g + pieces_i;
+        if (TO && p >= used) {
+            out[o_g] = zero;
+            if (BWD) out[o_u] = zero;
+            continue;
+        }
         const uint4 gv = gu[p * 2 * pieces_i + c], uv = gu[p * 2 * pieces_i + pieces_i + c];
         const uint32_t gp[4] = {gv.x, gv.y, gv.z, gv.w}, up[4] = {uv.x, uv.y, uv.z, uv.w};
         if (!BWD) {
@@ -184,12 +209,12 @@ __global__ __launch_bounds__(256) void swiglu_kernel(const uint4* __restrict__ g
             for (int q = 0; q < 4; ++q)
                 o[q] = pack_bf16x2(silu_f(bf16_lo(gp[q])) * bf16_lo(up[q]),
                                    silu_f(bf16_hi(gp[q])) * bf16_hi(up[q]));
-            out[i] = make_uint4(o[0], o[1], o[2], o[3]);
+            out[o_g] = make_uint4(o[0], o[1], o[2], o[3]);
         } else {
             uint4 og, ou;
-            swiglu_bwd_x8(gv, uv, dh[i], og, ou);
-            out[p * 2 * pieces_i + c] = og;
-            out[p * 2 * pieces_i + pieces_i + c] = ou;
+            swiglu_bwd_x8(gv, uv, dh[p * pieces_i + c], og, ou);
+            out[o_g] = og;
+            out[o_u] = ou;
         }
     }
 }
@@ -264,15 +289,17 @@ hipError_t launch_route_bwd(const int32_t* topk_idx, const float* topk_w, const 
 }
 
 hipError_t launch_swiglu(const uint16_t* gu, const uint16_t* dh, const int32_t* offsets, int E, int I,
-                         int64_t P_max, uint16_t* out, hipStream_t stream) {
+                         int64_t P_max, uint16_t* out, hipStream_t stream, bool tiled_out) {
     const int pi = I / 8;
     const dim3 grid(grid_for(P_max * pi, 8192)), block(256);
-    if (dh)
-        hipLaunchKernelGGL(swiglu_kernel<true>, grid, block, 0, stream, (const uint4*)gu, (const uint4*)dh,
-                           offsets, E, P_max, pi, (uint4*)out);
-    else
-        hipLaunchKernelGGL(swiglu_kernel<false>, grid, block, 0, stream, (const uint4*)gu,
-                           (const uint4*)nullptr, offsets, E, P_max, pi, (uint4*)out);
+#define MOE_SWIGLU_LAUNCH(BWD, TO)                                                                     \
+    hipLaunchKernelGGL((swiglu_kernel<BWD, TO>), grid, block, 0, stream, (const uint4*)gu, (const uint4*)dh, \
+                       offsets, E, P_max, pi, (uint4*)out)
+    if (dh && tiled_out) MOE_SWIGLU_LAUNCH(true, true);
+    else if (dh) MOE_SWIGLU_LAUNCH(true, false);
+    else if (tiled_out) MOE_SWIGLU_LAUNCH(false, true);
+    else MOE_SWIGLU_LAUNCH(false, false);
+#undef MOE_SWIGLU_LAUNCH
     return hipGetLastError();
 }
 

@@ -289,6 +289,12 @@ __device__ __forceinline__ void pp_wait_stages(int later) {
     else pp_wait_vmcnt<0>();
 }
 
+// AT / BT: A / B stored in row pairs (element (p, c) of a C-column operand at
+// (p/2)*2C + (c/32)*64 + (p%2)*32 + c%32, the order moe_tile_rows writes). Only the
+// global addresses change: a 32-row stage still starts 32*C elements after the
+// previous one, and each lane's 16 bytes land in the same LDS slot as for a
+// row-major operand, so the MFMAs and every result bit are the same.
+template <bool AT, bool BT>
 __global__ __launch_bounds__(kWgThreads, 1) void wgrad_pp_kernel(const uint16_t* __restrict__ A,
                                                                  const uint16_t* __restrict__ B,
                                                                  const int32_t* __restrict__ offsets, int E, int M,
@@ -339,6 +345,13 @@ __global__ __launch_bounds__(kWgThreads, 1) void wgrad_pp_kernel(const uint16_t*
     // (the last stage's rows past the segment read its last row inside it instead --
     // never a row past P_max -- and are zeroed in LDS once loaded; columns past M or N
     // read column 0, and their results are never stored)
+    // (row pairs: the bases are the pair of the segment's first row, and a stage row r
+    // lies r + seg0 % 2 rows past it)
+    const int par = seg0 & 1;
+    // element offset of (row r, column c) from the base of a C-column operand
+    auto off_of = [](bool tiled, int r, int c, int C) {
+        return tiled ? (r >> 1) * 2 * C + (c >> 5) * 64 + (r & 1) * 32 + (c & 31) : r * C + c;
+    };
     uint32_t a_off[2], b_off[2], a_off_last[2], b_off_last[2];
     int ld_row[2];
 #pragma unroll
@@ -349,13 +362,13 @@ __global__ __launch_bounds__(kWgThreads, 1) void wgrad_pp_kernel(const uint16_t*
         const int ca = m0 + 8 * piece, cb = n0 + 8 * piece;
         const int cca = ca < M ? ca : 0, ccb = cb < N ? cb : 0;
         ld_row[i] = row;
-        a_off[i] = (uint32_t)(row * M + cca) * 2u;
-        b_off[i] = (uint32_t)(row * N + ccb) * 2u;
-        a_off_last[i] = (uint32_t)(row_last * M + cca) * 2u;
-        b_off_last[i] = (uint32_t)(row_last * N + ccb) * 2u;
+        a_off[i] = (uint32_t)off_of(AT, AT ? row + par : row, cca, M) * 2u;
+        b_off[i] = (uint32_t)off_of(BT, BT ? row + par : row, ccb, N) * 2u;
+        a_off_last[i] = (uint32_t)off_of(AT, AT ? row_last + par : row_last, cca, M) * 2u;
+        b_off_last[i] = (uint32_t)off_of(BT, BT ? row_last + par : row_last, ccb, N) * 2u;
     }
-    const char* a_base = (const char*)(A + (int64_t)seg0 * M);
-    const char* b_base = (const char*)(B + (int64_t)seg0 * N);
+    const char* a_base = (const char*)(A + (int64_t)(AT ? seg0 - par : seg0) * M);
+    const char* b_base = (const char*)(B + (int64_t)(BT ? seg0 - par : seg0) * N);
     const int64_t a_step = (int64_t)kWgBK * M * 2, b_step = (int64_t)kWgBK * N * 2;  // bytes per stage
 
     auto issue = [&](int st) {  // this thread's pieces of stage st
@@ -501,10 +514,11 @@ __global__ __launch_bounds__(kWgThreads, 1) void wgrad_pp_kernel(const uint16_t*
 }
 
 hipError_t launch_wgrad(const uint16_t* A, const uint16_t* B, const int32_t* row_token, const int32_t* offsets,
-                        int E, int M, int N, float* dW, hipStream_t stream) {
+                        int E, int M, int N, float* dW, hipStream_t stream, bool a_tiled, bool b_tiled) {
     const int tm = (M + kWgBM - 1) / kWgBM, tn = (N + kWgBN - 1) / kWgBN;
     const int64_t blocks = (int64_t)E * tm * tn;
     if (row_token) {
+        if (a_tiled || b_tiled) return hipErrorInvalidValue;  // the gathering kernel reads row-major A
         hipLaunchKernelGGL(wgrad_kernel<true>, dim3((unsigned)blocks), dim3(kWgThreads), 0, stream, A, B, row_token,
                            offsets, M, N, tm, tn, dW);
     } else {
@@ -512,8 +526,18 @@ hipError_t launch_wgrad(const uint16_t* A, const uint16_t* B, const int32_t* row
         // blocks past the last unit return at once
         const int64_t units = ((int64_t)E * tm + 7) / 8 * 8;
         const int64_t pp_blocks = units * tn;
-        hipLaunchKernelGGL(wgrad_pp_kernel, dim3((unsigned)pp_blocks), dim3(kWgThreads), 0, stream, A, B, offsets, E,
-                           M, N, tm, tn, dW);
+        const dim3 grid((unsigned)pp_blocks), block(kWgThreads);
+        if (a_tiled && b_tiled)
+            hipLaunchKernelGGL((wgrad_pp_kernel<true, true>), grid, block, 0, stream, A, B, offsets, E, M, N, tm, tn, dW);
+        else if (a_tiled)
+            hipLaunchKernelGGL((wgrad_pp_kernel<true, false>), grid, block, 0, stream, A, B, offsets, E, M, N, tm, tn,
+                               dW);
+        else if (b_tiled)
+            hipLaunchKernelGGL((wgrad_pp_kernel<false, true>), grid, block, 0, stream, A, B, offsets, E, M, N, tm, tn,
+                               dW);
+        else
+            hipLaunchKernelGGL((wgrad_pp_kernel<false, false>), grid, block, 0, stream, A, B, offsets, E, M, N, tm, tn,
+                               dW);
     }
     return hipGetLastError();
 }

@@ -68,6 +68,10 @@ def lib():
     lib.moe_untile_fp8_rows.argtypes = [vp, i64, i32, vp, vp]
     lib.moe_grouped_glu_gemm_fp8w_tiled.argtypes = lib.moe_grouped_glu_gemm_fp8w.argtypes
     lib.moe_grouped_down_gemm_fp8w_tiled.argtypes = lib.moe_grouped_down_gemm_fp8w.argtypes
+    lib.moe_grouped_gemm_tiled.argtypes = lib.moe_grouped_gemm.argtypes
+    lib.moe_swiglu_tiled.argtypes = lib.moe_swiglu.argtypes
+    lib.moe_swiglu_backward_tiled.argtypes = lib.moe_swiglu_backward.argtypes
+    lib.moe_grouped_wgrad_tiled.argtypes = [vp, i32, vp, i32, vp, vp, i32, i32, i32, i64, vp, vp]
     return lib
 
 
@@ -352,6 +356,31 @@ def test_tiled_validation(lib):
     assert fn(FAKE, FAKE, FAKE, FAKE, FAKE, 100, 8, 128, 256, 1001, FAKE, None) == SHAPE
     assert fn(FAKE, None, FAKE, FAKE, FAKE, 100, 8, 128, 256, 1000, FAKE, None) == NULLP
     assert fn(FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 20, 8, 2048, 256, 1000, FAKE, None) == OVERFLOW
+
+
+def test_tiled_training_validation(lib):
+    """The training steps on tiled operands: as their row-major counterparts, plus
+    whole row pairs (even P_max) wherever an operand is tiled."""
+    fn = lib.moe_grouped_gemm_tiled
+    assert fn(FAKE, FAKE, FAKE, FAKE, 8, 128, 256, 1001, FAKE, None) == SHAPE        # odd P_max
+    assert fn(FAKE, FAKE, FAKE, FAKE, 8, 100, 256, 1000, FAKE, None) == SHAPE        # K % 64
+    assert fn(FAKE, FAKE, FAKE, FAKE, 8, 128, 256, 1000, None, None) == NULLP
+    assert fn(FAKE, FAKE + 8, FAKE, FAKE, 8, 128, 256, 1000, FAKE, None) == MISALIGNED
+    assert lib.moe_swiglu_tiled(FAKE, FAKE, 4, 128, 101, FAKE, None) == SHAPE        # odd P_max
+    assert lib.moe_swiglu_tiled(FAKE, FAKE, 4, 96, 100, FAKE, None) == SHAPE         # I % 64
+    assert lib.moe_swiglu_tiled(FAKE, FAKE, 4, 128, 100, None, None) == NULLP
+    fn = lib.moe_swiglu_backward_tiled
+    assert fn(FAKE, FAKE, FAKE, 4, 128, 101, FAKE, None) == SHAPE                     # odd P_max
+    assert fn(FAKE, FAKE, FAKE, 4, 128, 100, None, None) == NULLP
+    assert fn(None, FAKE, FAKE, 4, 128, 100, FAKE, None) == NULLP
+    fn = lib.moe_grouped_wgrad_tiled
+    assert fn(FAKE, 2, FAKE, 1, FAKE, FAKE, 8, 128, 128, 1000, FAKE, None) == SHAPE   # flag not 0 / 1
+    assert fn(FAKE, 1, FAKE, -1, FAKE, FAKE, 8, 128, 128, 1000, FAKE, None) == SHAPE
+    assert fn(FAKE, 1, FAKE, 0, FAKE, FAKE, 8, 128, 128, 1001, FAKE, None) == SHAPE   # odd P_max, a tiled
+    assert fn(FAKE, 0, FAKE, 1, FAKE, FAKE, 8, 128, 128, 1001, FAKE, None) == SHAPE   # odd P_max, b tiled
+    assert fn(FAKE, 1, FAKE, 1, FAKE, FAKE, 8, 128, 96, 1000, FAKE, None) == SHAPE    # N % 64
+    assert fn(FAKE, 1, FAKE, 1, FAKE, FAKE, 8, 128, 128, 1000, None, None) == NULLP
+    assert fn(FAKE, 1, FAKE, 1, FAKE, FAKE, 8, 128, 128, 1000, FAKE + 4, None) == MISALIGNED
 
 
 def test_tiled_fp8_validation(lib):

@@ -299,3 +299,117 @@ def test_tiled_fp8_layer(gpu_lib, cfg):
         assert _same_bits(til.out, ref.out), "out"
     else:
         assert_close_bf16(host_f64(til.out), host_f64(ref.out), f"tiled fp8 out[{cfg.name}]", tight=False)
+
+
+# --------------------------------------------------------------------------------------
+# training steps on tiled operands: == row-major, bit for bit
+# --------------------------------------------------------------------------------------
+
+TRAIN_STEP_CASES = [c for c in GEMM_CASES
+                    if c[0] in ("many_tiles_k256", "many_tiles_align1", "ragged", "tails_align8", "align1",
+                                "wide_H2880")]
+
+
+def _same_f32(a: torch.Tensor, b: torch.Tensor) -> bool:
+    return torch.equal(a.view(torch.int32), b.view(torch.int32))
+
+
+@pytest.mark.parametrize("case", TRAIN_STEP_CASES, ids=[c[0] for c in TRAIN_STEP_CASES])
+def test_tiled_training_steps_equal_row_major(gpu_lib, case):
+    """The plain GEMM, the SwiGLU forward / backward and the weight gradient on
+    tiled operands against the row-major calls (odd segment starts included: the
+    align-1 cases), and the last pair's row past the used rows written as zeros."""
+    name, counts, align, H, I = case
+    _say(f"tiled training steps case {name}")
+    counts, offsets = _synthetic_layout(counts, align)
+    E, P = len(counts), int(offsets[-1])
+    P_max = gpu_lib.even_rows(P + 64)
+    rows = _rows_of(counts, offsets)
+    cd, od = dev(counts), dev(offsets)
+    x_perm = np.zeros((P_max, H), np.uint16)
+    x_perm[rows] = gen.random_bf16((len(rows), H), seed=11)
+    w_gu = dev_bf16(gen.random_bf16((E, 2 * I, H), seed=12, std=0.02))
+    w_gu_t = gpu_lib.transpose_experts(w_gu)
+    gu = dev_bf16(gen.random_bf16((P_max, 2 * I), seed=13))
+    dh = dev_bf16(gen.random_bf16((P_max, I), seed=14))
+    xd = dev_bf16(x_perm)
+
+    # gate/up output (K = H, N = 2I) and the input gradient (K = 2I, N = H)
+    c = gpu_lib.grouped_gemm(xd, w_gu, cd, od)
+    c_t = gpu_lib.grouped_gemm_tiled(gpu_lib.tile_rows(xd), gpu_lib.tile_weights(w_gu), cd, od)
+    dgu_in = gpu_lib.grouped_gemm(c, w_gu_t, cd, od)
+    dgu_in_t = gpu_lib.grouped_gemm_tiled(gpu_lib.tile_rows(c), gpu_lib.tile_weights(w_gu_t), cd, od)
+    # SwiGLU forward and backward with tiled outputs
+    h = gpu_lib.swiglu(gu, od)
+    h_t = gpu_lib.swiglu_tiled(gu, od)
+    dgu = gpu_lib.swiglu_backward(dh, gu, od)
+    dgu_t = gpu_lib.swiglu_backward_tiled(dh, gu, od)
+    torch.cuda.synchronize()
+    assert _same_bits(c_t[:P], c[:P]), "grouped_gemm_tiled, K = H"
+    assert _same_bits(dgu_in_t[:P], dgu_in[:P]), "grouped_gemm_tiled, K = 2I"
+    h_u, dgu_u = gpu_lib.untile_rows(h_t), gpu_lib.untile_rows(dgu_t)
+    assert _same_bits(h_u[:P], h[:P]), "swiglu_tiled"
+    assert _same_bits(dgu_u[:P], dgu[:P]), "swiglu_backward_tiled"
+    if P % 2:
+        assert not h_u[P].view(torch.int16).any() and not dgu_u[P].view(torch.int16).any()
+
+    # weight gradients with every combination of tiled operands; a's pad rows zero
+    for M, N, a_bits, b_bits in ((H, I, gen.random_bf16((len(rows), H), seed=15), gen.random_bf16((P_max, I), seed=16)),
+                                 (2 * I, H, gen.random_bf16((len(rows), 2 * I), seed=17), x_perm)):
+        a = np.zeros((P_max, M), np.uint16)
+        a[rows] = a_bits
+        ad, bd = dev_bf16(a), dev_bf16(b_bits)
+        ref = gpu_lib.grouped_wgrad(ad, bd, cd, od)
+        at_, bt_ = gpu_lib.tile_rows(ad), gpu_lib.tile_rows(bd)
+        for a_tiled in (False, True):
+            for b_tiled in (False, True):
+                got = gpu_lib.grouped_wgrad_tiled(at_ if a_tiled else ad, bt_ if b_tiled else bd, cd, od,
+                                                  a_tiled, b_tiled)
+                torch.cuda.synchronize()
+                assert _same_f32(got, ref), f"wgrad M={M} N={N} a_tiled={a_tiled} b_tiled={b_tiled}"
+
+
+TRAIN_LAYERS = [
+    gen.CONFIGS["tiny"],
+    gen.MoEConfig("k1", 200, 256, 16, 1, 128, 21, "gaussian"),
+    gen.MoEConfig("align1_odd_starts", 301, 256, 12, 3, 192, 27, "gaussian", align=1),
+    gen.MoEConfig("sparse_experts", 12, 192, 64, 2, 128, 24, "gaussian"),
+    gen.MoEConfig("skewed_small", 2048, 256, 32, 4, 128, 26, "zipf"),
+    gen.CONFIGS["qwen3_30b_a3b"],
+]
+
+
+def _train_layer(gpu_lib, d, tiled):
+    cfg = d["cfg"]
+    layer = gpu_lib.MoETrainingLayer(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.align, tiled=tiled)
+    w_gu, w_d, w_gu_t, w_d_t = gpu_lib.training_weights(dev_bf16(d["w_gu"]), dev_bf16(d["w_d"]), tiled=tiled)
+    out = layer.forward(dev_bf16(d["x"]), dev(d["logits"]), w_gu, w_d).clone()
+    dout = dev_bf16(gen.random_bf16((cfg.T, cfg.H), seed=cfg.seed + 500))
+    grads = [g.clone() for g in layer.backward(dout, w_gu_t, w_d_t)]
+    torch.cuda.synchronize()
+    return [out] + grads
+
+
+@pytest.mark.parametrize("cfg", TRAIN_LAYERS, ids=[c.name for c in TRAIN_LAYERS])
+def test_tiled_training_layer_equals_row_major(gpu_lib, cfg):
+    """The whole training step on tiled operands gives the row-major step's output
+    and gradients bit for bit (the row-major step is held to the oracle by the
+    backward tests)."""
+    _say(f"tiled training layer {cfg.name}")
+    d = gen.make_inputs(cfg)
+    a = _train_layer(gpu_lib, d, tiled=False)
+    b = _train_layer(gpu_lib, d, tiled=True)
+    for name, x, y in zip(("out", "dx", "dlogits", "dW_gu", "dW_d"), a, b):
+        same = _same_bits(x, y) if x.dtype == torch.bfloat16 else _same_f32(x, y)
+        assert same, f"{name}[{cfg.name}]"
+
+
+def test_tiled_training_layer_rejects_row_major_weights(gpu_lib):
+    cfg = gen.CONFIGS["tiny"]
+    d = gen.make_inputs(cfg)
+    layer = gpu_lib.MoETrainingLayer(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.align, tiled=True)
+    w_gu, w_d = dev_bf16(d["w_gu"]), dev_bf16(d["w_d"])
+    with pytest.raises(ValueError):
+        layer.forward(dev_bf16(d["x"]), dev(d["logits"]), w_gu, w_d)
+    with pytest.raises(ValueError):
+        gpu_lib.MoETrainingLayer(cfg.T, cfg.H, cfg.E, cfg.k, cfg.I, cfg.align, tiled=True, fuse_swiglu_backward=True)
