@@ -48,8 +48,8 @@ hipError_t launch_transpose(const uint16_t*, int64_t, int, int, uint16_t*, hipSt
 hipError_t launch_router_prepare(const float*, int, int, uint16_t*, uint16_t*, hipStream_t);
 hipError_t launch_router_topk(const uint16_t*, const uint16_t*, const uint16_t*, int64_t, int, int, int, float*,
                               int32_t*, float*, hipStream_t);
-hipError_t launch_wgrad(const uint16_t*, const uint16_t*, const int32_t*, const int32_t*, int, int, int, float*,
-                        hipStream_t, bool a_tiled, bool b_tiled);
+hipError_t launch_wgrad(const uint16_t*, const uint16_t*, const int32_t*, const int32_t*, int, int, int,
+                        int rows_max, float*, hipStream_t, bool a_tiled, bool b_tiled);
 hipError_t launch_combine(const uint16_t*, const int32_t*, const float*, int64_t, int, int,
                           int64_t, uint16_t*, hipStream_t);
 hipError_t launch_probe_copy(const void*, void*, size_t, int, hipStream_t);
@@ -846,7 +846,8 @@ moe_status moe_grouped_wgrad(const moe_bf16* a, const moe_bf16* b, const int32_t
     moe_status s = check_wgrad(a, b, row_token, expert_counts, expert_offsets, E, M, N, P_max, dw);
     if (s != MOE_OK) return s;
     DEBUG_CHECK(moe::debug_check_layout(expert_counts, expert_offsets, E, P_max, (hipStream_t)stream));
-    return hip_status(moe::launch_wgrad(a, b, row_token, expert_offsets, E, M, N, dw, (hipStream_t)stream, false, false),
+    return hip_status(moe::launch_wgrad(a, b, row_token, expert_offsets, E, M, N, (int)P_max, dw,
+                                        (hipStream_t)stream, false, false),
                       "moe_grouped_wgrad launch");
 }
 
@@ -859,7 +860,7 @@ moe_status moe_grouped_wgrad_tiled(const moe_bf16* a, int32_t a_tiled, const moe
         return fail(MOE_ERR_INVALID_SHAPE, "a_tiled=%d, b_tiled=%d: each must be 0 or 1", a_tiled, b_tiled);
     if ((a_tiled || b_tiled) && (s = check_even_pmax(P_max)) != MOE_OK) return s;
     DEBUG_CHECK(moe::debug_check_layout(expert_counts, expert_offsets, E, P_max, (hipStream_t)stream));
-    return hip_status(moe::launch_wgrad(a, b, nullptr, expert_offsets, E, M, N, dw, (hipStream_t)stream,
+    return hip_status(moe::launch_wgrad(a, b, nullptr, expert_offsets, E, M, N, (int)P_max, dw, (hipStream_t)stream,
                                         a_tiled != 0, b_tiled != 0),
                       "moe_grouped_wgrad_tiled launch");
 }

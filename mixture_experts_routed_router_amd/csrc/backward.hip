@@ -117,11 +117,14 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(const uint4* __restric
 // zeroes their 16-byte pieces.
 __global__ __launch_bounds__(256) void zero_pad_rows_kernel(const int32_t* __restrict__ row_token,
                                                             const int32_t* __restrict__ offsets, int pieces,
-                                                            uint4* __restrict__ dst) {
+                                                            int64_t rows_max, uint4* __restrict__ dst) {
     MOE_DEBUG_GUARD();
     __shared__ int64_t pad0;
     const int e = blockIdx.x;
-    const int64_t s0 = offsets[e], s1 = offsets[e + 1];
+    // the segment clamped to [0, rows_max): offsets that break their contract cannot
+    // make it read or write outside row_token or dst
+    const int64_t s0 = min(max((int64_t)offsets[e], (int64_t)0), rows_max);
+    const int64_t s1 = max(min((int64_t)offsets[e + 1], rows_max), s0);
     if (threadIdx.x < kWave) {
         const int lane = lane_id();
         int64_t start = s1;  // first pad row
@@ -266,7 +269,7 @@ hipError_t launch_combine_bwd(const uint16_t* dout, const uint16_t* y, const int
                               hipStream_t stream) {
     const int pieces = H / 8;
     hipLaunchKernelGGL(zero_pad_rows_kernel, dim3((unsigned)E), dim3(256), 0, stream, row_token, offsets, pieces,
-                       (uint4*)dy);
+                       P_max, (uint4*)dy);
     if (T > 0) {
         const dim3 grid((unsigned)((T + 3) / 4)), block(256);
 #define MOE_CB_LAUNCH(KL)                                                                              \

@@ -64,7 +64,7 @@ template <bool GATHER_B>
 __global__ __launch_bounds__(kWgThreads, 1) void wgrad_kernel(const uint16_t* __restrict__ A, const uint16_t* __restrict__ B,
                                                     const int32_t* __restrict__ row_token,
                                                     const int32_t* __restrict__ offsets, int M, int N,
-                                                    int tiles_m, int tiles_n, float* __restrict__ dW) {
+                                                    int tiles_m, int tiles_n, int rows_max, float* __restrict__ dW) {
     MOE_DEBUG_GUARD();
     __shared__ __attribute__((aligned(16))) uint16_t at[2][kWgBK][kWgStride];
     __shared__ __attribute__((aligned(16))) uint16_t bt[2][kWgBK][kWgStride];
@@ -78,7 +78,9 @@ __global__ __launch_bounds__(kWgThreads, 1) void wgrad_kernel(const uint16_t* __
     const int e = (int)(b / ((int64_t)tiles_m * tiles_n));
     const int rem = (int)(b - (int64_t)e * tiles_m * tiles_n);
     const int m0 = (rem / tiles_n) * kWgBM, n0 = (rem % tiles_n) * kWgBN;
-    const int seg0 = offsets[e], seg1 = offsets[e + 1];
+    // the segment clamped to [0, rows_max): offsets that break their contract cannot
+    // make a load leave A or B
+    const int seg0 = min(max(offsets[e], 0), rows_max), seg1 = max(min(offsets[e + 1], rows_max), seg0);
     const int nchunks = (seg1 - seg0 + kWgBK - 1) / kWgBK;
 
     const int tid = threadIdx.x, lane = lane_id();
@@ -298,7 +300,7 @@ template <bool AT, bool BT>
 __global__ __launch_bounds__(kWgThreads, 1) void wgrad_pp_kernel(const uint16_t* __restrict__ A,
                                                                  const uint16_t* __restrict__ B,
                                                                  const int32_t* __restrict__ offsets, int E, int M,
-                                                                 int N, int tiles_m, int tiles_n,
+                                                                 int N, int tiles_m, int tiles_n, int rows_max,
                                                                  float* __restrict__ dW) {
     MOE_DEBUG_GUARD();
     __shared__ __attribute__((aligned(1024))) uint16_t ring[kPpStages * kPpStageElems];
@@ -330,8 +332,9 @@ __global__ __launch_bounds__(kWgThreads, 1) void wgrad_pp_kernel(const uint16_t*
         e = pick;
     }
     const int m0 = tile_m * kWgBM, n0 = tile_n * kWgBN;
-    const int seg0 = offsets[e];
-    const int rows = max(offsets[e + 1] - seg0, 0);
+    // the segment clamped to [0, rows_max), as in wgrad_kernel
+    const int seg0 = min(max(offsets[e], 0), rows_max);
+    const int rows = max(min(offsets[e + 1], rows_max) - seg0, 0);
     const int nk = (rows + kWgBK - 1) / kWgBK;
     const int valid_last = rows - (nk - 1) * kWgBK;  // rows of the last stage inside the segment
 
@@ -514,13 +517,14 @@ __global__ __launch_bounds__(kWgThreads, 1) void wgrad_pp_kernel(const uint16_t*
 }
 
 hipError_t launch_wgrad(const uint16_t* A, const uint16_t* B, const int32_t* row_token, const int32_t* offsets,
-                        int E, int M, int N, float* dW, hipStream_t stream, bool a_tiled, bool b_tiled) {
+                        int E, int M, int N, int rows_max, float* dW, hipStream_t stream, bool a_tiled,
+                        bool b_tiled) {
     const int tm = (M + kWgBM - 1) / kWgBM, tn = (N + kWgBN - 1) / kWgBN;
     const int64_t blocks = (int64_t)E * tm * tn;
     if (row_token) {
         if (a_tiled || b_tiled) return hipErrorInvalidValue;  // the gathering kernel reads row-major A
         hipLaunchKernelGGL(wgrad_kernel<true>, dim3((unsigned)blocks), dim3(kWgThreads), 0, stream, A, B, row_token,
-                           offsets, M, N, tm, tn, dW);
+                           offsets, M, N, tm, tn, rows_max, dW);
     } else {
         // E * tm units (tile rows) dealt to the 8 XCDs, 8 * ceil(E * tm / 8) of them;
         // blocks past the last unit return at once
@@ -528,16 +532,17 @@ hipError_t launch_wgrad(const uint16_t* A, const uint16_t* B, const int32_t* row
         const int64_t pp_blocks = units * tn;
         const dim3 grid((unsigned)pp_blocks), block(kWgThreads);
         if (a_tiled && b_tiled)
-            hipLaunchKernelGGL((wgrad_pp_kernel<true, true>), grid, block, 0, stream, A, B, offsets, E, M, N, tm, tn, dW);
+            hipLaunchKernelGGL((wgrad_pp_kernel<true, true>), grid, block, 0, stream, A, B, offsets, E, M, N, tm, tn,
+                               rows_max, dW);
         else if (a_tiled)
             hipLaunchKernelGGL((wgrad_pp_kernel<true, false>), grid, block, 0, stream, A, B, offsets, E, M, N, tm, tn,
-                               dW);
+                               rows_max, dW);
         else if (b_tiled)
             hipLaunchKernelGGL((wgrad_pp_kernel<false, true>), grid, block, 0, stream, A, B, offsets, E, M, N, tm, tn,
-                               dW);
+                               rows_max, dW);
         else
             hipLaunchKernelGGL((wgrad_pp_kernel<false, false>), grid, block, 0, stream, A, B, offsets, E, M, N, tm, tn,
-                               dW);
+                               rows_max, dW);
     }
     return hipGetLastError();
 }
