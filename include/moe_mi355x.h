@@ -660,6 +660,14 @@ moe_status moe_debug_reset(moe_stream_t stream);
  *   src, dst  device buffers of `bytes` bytes, 16-byte aligned, not overlapping
  *   bytes     a positive multiple of 16, else MOE_ERR_INVALID_SHAPE
  *
+ * moe_probe_read: reads src[0 .. bytes) once with the copy's grid-stride walk of
+ * non-temporal 16-byte loads and writes only a 16-byte XOR of each thread's loads
+ * to sink (the read-only HBM rate).
+ *   src          device buffer of `bytes` bytes, 16-byte aligned
+ *   bytes        a positive multiple of 16, else MOE_ERR_INVALID_SHAPE
+ *   sink         device buffer of at least moe_probe_read_sink_bytes() bytes, 16-byte
+ *                aligned (MOE_ERR_WORKSPACE_TOO_SMALL otherwise); its values are meaningless
+ *
  * moe_probe_mfma_bf16: a register-only loop of v_mfma_f32_32x32x16_bf16 on every
  * compute unit (8 waves per CU, 4 independent accumulator chains per wave,
  * `iters` rounds); no memory traffic but one float per thread written to sink.
@@ -669,6 +677,8 @@ moe_status moe_debug_reset(moe_stream_t stream);
  *   *flops       host out: the launch's bf16 flops (2*32*32*16 per MFMA)
  */
 moe_status moe_probe_copy(const void *src, void *dst, size_t bytes, moe_stream_t stream);
+moe_status moe_probe_read(const void *src, size_t bytes, void *sink, size_t sink_bytes, moe_stream_t stream);
+size_t moe_probe_read_sink_bytes(void);
 moe_status moe_probe_mfma_bf16(float *sink, int64_t sink_floats, int32_t iters, double *flops,
                                moe_stream_t stream);
 int64_t moe_probe_mfma_sink_floats(void);

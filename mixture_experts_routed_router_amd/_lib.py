@@ -118,6 +118,10 @@ def _open(debug: bool):
                                     _c_vp]
     lib.moe_probe_copy.argtypes = [_c_vp, _c_vp, _c_sz, _c_vp]
     lib.moe_probe_mfma_bf16.argtypes = [_c_vp, _c_i64, _c_i32, ctypes.POINTER(ctypes.c_double), _c_vp]
+    lib.moe_probe_read.argtypes = [_c_vp, _c_sz, _c_vp, _c_sz, _c_vp]
+    lib.moe_probe_read.restype = ctypes.c_int
+    lib.moe_probe_read_sink_bytes.argtypes = []
+    lib.moe_probe_read_sink_bytes.restype = _c_sz
     lib.moe_probe_mfma_sink_floats.argtypes = []
     lib.moe_probe_mfma_sink_floats.restype = _c_i64
     lib.moe_route_hist_workspace_size.argtypes = [_c_i64, _c_i32, _c_i32, ctypes.POINTER(_c_sz)]
@@ -1043,6 +1047,17 @@ def probe_copy(src: torch.Tensor, dst: torch.Tensor, stream=None):
     nbytes = src.numel() * src.element_size()
     _call("moe_probe_copy", _ptr(src, src.dtype, "src"), _ptr(dst, dst.dtype, "dst"), nbytes,
           _stream(stream))
+
+
+def probe_read_sink(device=None) -> torch.Tensor:
+    return torch.empty(int(load().moe_probe_read_sink_bytes()), dtype=torch.uint8, device=device or "cuda")
+
+
+def probe_read(src: torch.Tensor, sink: torch.Tensor, stream=None):
+    """Reads every byte of src once through the library's read-only streaming kernel."""
+    nbytes = src.numel() * src.element_size()
+    _call("moe_probe_read", _ptr(src, src.dtype, "src"), nbytes, _ptr(sink, torch.uint8, "sink"),
+          sink.numel(), _stream(stream))
 
 
 def probe_mfma_sink(device=None) -> torch.Tensor:

@@ -59,6 +59,8 @@ hipError_t launch_fused_layer(const uint16_t*, const int32_t*, const float*, con
                               uint16_t*, uint16_t*, void*, hipStream_t);
 hipError_t fused_layer_read_error(const void*, int32_t*, hipStream_t);
 hipError_t launch_probe_mfma(float*, int, int, hipStream_t);
+hipError_t launch_probe_read(const void*, size_t, void*, int, hipStream_t);
+int probe_read_blocks(int);
 int probe_mfma_blocks(int);
 double probe_mfma_flops(int, int);
 #ifdef MOE_DEBUG
@@ -919,6 +921,21 @@ moe_status moe_probe_copy(const void* src, void* dst, size_t bytes, moe_stream_t
     return hip_status(moe::launch_probe_copy(src, dst, bytes, device_cus(), (hipStream_t)stream),
                       "moe_probe_copy launch");
 }
+
+moe_status moe_probe_read(const void* src, size_t bytes, void* sink, size_t sink_bytes, moe_stream_t stream) {
+    REQUIRE_PTR(src);
+    REQUIRE_PTR(sink);
+    if (bytes == 0 || bytes % 16 != 0)
+        return fail(MOE_ERR_INVALID_SHAPE, "bytes=%zu must be a positive multiple of 16", bytes);
+    if (!aligned16(src) || !aligned16(sink)) return fail(MOE_ERR_MISALIGNED_POINTER, "src or sink not 16-byte aligned");
+    const int cus = device_cus();
+    const size_t need = (size_t)moe::probe_read_blocks(cus) * 256 * 16;
+    if (sink_bytes < need)
+        return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "sink holds %zu bytes < %zu needed", sink_bytes, need);
+    return hip_status(moe::launch_probe_read(src, bytes, sink, cus, (hipStream_t)stream), "moe_probe_read launch");
+}
+
+size_t moe_probe_read_sink_bytes(void) { return (size_t)moe::probe_read_blocks(device_cus()) * 256 * 16; }
 
 moe_status moe_probe_mfma_bf16(float* sink, int64_t sink_floats, int32_t iters, double* flops,
                                moe_stream_t stream) {

@@ -1,6 +1,6 @@
-// probes.hip -- two measurement kernels that give the chip's own roofs beside its
-// published ones: a device copy (HBM read + write stream) and a register-only
-// bf16 MFMA loop. Neither is part of the layer; the bench reports each kernel's
+// probes.hip -- measurement kernels that give the chip's own roofs beside its
+// published ones: a device copy (HBM read + write stream), a read-only stream and
+// a register-only bf16 MFMA loop. Neither is part of the layer; the bench reports each kernel's
 // roofline fraction against both the spec and these measured roofs [PocketLLM
 // "Qwen4-Exp Heterogeneous TP4 Performance", Theoretical ceilings / Hardware roofs:
 // measured copy and GEMM roofs quoted beside the spec figures].
@@ -30,6 +30,37 @@ __global__ __launch_bounds__(kProbeThreads) void probe_copy_kernel(const u32x4_t
             if (i < n) __builtin_nontemporal_store(v[u], dst + i);
         }
     }
+}
+
+// Read-only stream: the same grid-stride walk as the copy, kCopyPieces non-temporal
+// 16-byte loads in flight per lane; each thread XORs what it read and writes the
+// result to its own 16 bytes of sink, so every load is live.
+constexpr int kReadBlocksPerCu = 8;
+
+__global__ __launch_bounds__(kProbeThreads) void probe_read_kernel(const u32x4_t* __restrict__ src, int64_t n,
+                                                                   u32x4_t* __restrict__ sink) {
+    const int64_t stride = (int64_t)gridDim.x * kProbeThreads * kCopyPieces;
+    u32x4_t acc = {0u, 0u, 0u, 0u};
+    for (int64_t base = (int64_t)blockIdx.x * kProbeThreads * kCopyPieces + threadIdx.x; base < n;
+         base += stride) {
+        u32x4_t v[kCopyPieces];
+#pragma unroll
+        for (int u = 0; u < kCopyPieces; ++u) {
+            const int64_t i = base + (int64_t)u * kProbeThreads;
+            v[u] = i < n ? __builtin_nontemporal_load(src + i) : u32x4_t{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int u = 0; u < kCopyPieces; ++u) acc ^= v[u];
+    }
+    sink[(int64_t)blockIdx.x * kProbeThreads + threadIdx.x] = acc;
+}
+
+int probe_read_blocks(int cus) { return cus * kReadBlocksPerCu; }
+
+hipError_t launch_probe_read(const void* src, size_t bytes, void* sink, int cus, hipStream_t stream) {
+    hipLaunchKernelGGL(probe_read_kernel, dim3((unsigned)probe_read_blocks(cus)), dim3(kProbeThreads), 0, stream,
+                       (const u32x4_t*)src, (int64_t)(bytes / 16), (u32x4_t*)sink);
+    return hipGetLastError();
 }
 
 // Register-only bf16 MFMA loop: each wave runs kChains independent accumulator

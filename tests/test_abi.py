@@ -155,6 +155,12 @@ def test_probe_validation(lib):
     assert lib.moe_probe_mfma_bf16(None, 1 << 20, 10, ctypes.byref(fl), None) == NULLP
     assert lib.moe_probe_mfma_bf16(FAKE, 1 << 20, 0, ctypes.byref(fl), None) == VALUE
     assert lib.moe_probe_mfma_bf16(FAKE, 1 << 20, 10, None, None) == NULLP
+    lib.moe_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_size_t,
+                                   ctypes.c_void_p]
+    assert lib.moe_probe_read(None, 1024, FAKE, 1 << 30, None) == NULLP
+    assert lib.moe_probe_read(FAKE, 1000, FAKE, 1 << 30, None) == SHAPE          # not a multiple of 16
+    assert lib.moe_probe_read(FAKE, 1024, FAKE + 4, 1 << 30, None) == MISALIGNED
+    assert lib.moe_probe_read(FAKE, 1024, FAKE, 16, None) == WORKSPACE            # sink too small
 
 
 def test_status_strings(lib):
