@@ -36,6 +36,23 @@
  *   on row-pair tiled operands: moe_grouped_gemm_tiled, moe_swiglu_tiled,
  *   moe_swiglu_backward_tiled, moe_grouped_wgrad_tiled
  *
+ * The forward on row-pair tiled operands (this library's faster memory order for
+ * x_perm, h and the expert weights; every result bit for bit the row-major
+ * call's):
+ *   moe_tile_rows, moe_untile_rows, moe_permute_tiled, moe_grouped_glu_gemm_tiled,
+ *   moe_grouped_glu_gemm_gather_tiled, moe_grouped_down_gemm_tiled,
+ *   moe_tile_fp8_rows, moe_untile_fp8_rows, moe_grouped_glu_gemm_fp8w_tiled,
+ *   moe_grouped_down_gemm_fp8w_tiled
+ *
+ * Routing that also counts the permute's histogram:
+ *   moe_route_hist_workspace_size, moe_route_topk_hist, moe_permute_from_hist
+ * The layer after routing as one persistent kernel:
+ *   moe_fused_layer_workspace_size, moe_fused_layer, moe_fused_layer_status
+ * The permute without a workspace, for callers that cannot allocate:
+ *   moe_permute_noalloc, moe_permute_noalloc_max_workspace
+ * The debug build's queries: moe_debug_build, moe_debug_status, moe_debug_reset
+ * Measurement probes: moe_probe_copy, moe_probe_read, moe_probe_mfma_bf16
+ *
  * Sources (page title, section):
  *   [Halo]      Halo, "Performance": Levers that help (grouped GEMM instead of a
  *               per-expert loop; the atomic-free expert permute; fused GLU);
