@@ -375,6 +375,10 @@ TRAIN_LAYERS = [
     gen.MoEConfig("align1_odd_starts", 301, 256, 12, 3, 192, 27, "gaussian", align=1),
     gen.MoEConfig("sparse_experts", 12, 192, 64, 2, 128, 24, "gaussian"),
     gen.MoEConfig("skewed_small", 2048, 256, 32, 4, 128, 26, "zipf"),
+    # degenerate: one token, one expert, top-1 (P_max 1 rounded up to a pair)
+    gen.MoEConfig("one_token", 1, 128, 1, 1, 64, 31, "gaussian"),
+    # more than 256 experts (weight gradients take experts by id), most of them empty
+    gen.MoEConfig("e300_mostly_empty", 200, 128, 300, 2, 64, 32, "gaussian"),
     gen.CONFIGS["qwen3_30b_a3b"],
 ]
 
