@@ -397,10 +397,12 @@ struct WaveCtx {
 // and no prologue.
 //
 // The epilogue writes straight from registers (no LDS): after a 4x4 transpose
-// inside each quad of lanes, a lane holds 4 consecutive bf16 of one output row,
-// an 8-byte store. This wave's stores of the previous tile (s_prev of them) were
-// issued after the prefetched stages; vector-memory operations complete in issue
-// order, so a wait for a prefetched stage may leave those stores in flight.
+// inside each quad of lanes, a lane holds 4 consecutive bf16 of one output row
+// (the gate/up GEMM stores those 8 bytes; the plain GEMM first trades halves with
+// lane ^ 4 and stores 16). This wave's stores of the previous tile (s_prev of
+// them) were issued after the prefetched stages; vector-memory operations
+// complete in issue order, so a wait for a prefetched stage may leave those
+// stores in flight.
 template <bool GLU, bool GATHER, bool W8, bool SWB, bool PK, int NV>
 __device__ __forceinline__ int run_tile(const WaveCtx& w, const TileArgs& ta, const TileArgs& tn,
                                         int base, bool prefetched, bool pf_next, int s_prev,
