@@ -11,16 +11,20 @@ namespace moe {
 
 constexpr int kCombinePieces = 2;  // 16-byte column pieces per lane per pass
 
-// Token t by the calling wavefront (wave-uniform t < T). topk_w NULL: weights 1.
+// Token t by the calling wavefront (wave-uniform t < T), its 16-byte column
+// pieces [c_begin, c_end) (c_end < 0: to the end of the row). topk_w NULL:
+// weights 1.
 template <int KB>  // routes loaded per batch
 __device__ __forceinline__ void combine_token(const uint4* __restrict__ y, const int32_t* __restrict__ route_row,
                                               const float* __restrict__ topk_w, int64_t t, int pieces_per_row,
-                                              int k, int64_t P_max, uint4* __restrict__ out) {
+                                              int k, int64_t P_max, uint4* __restrict__ out, int c_begin = 0,
+                                              int c_end = -1) {
     constexpr int CP = kCombinePieces;
     const int lane = lane_id();
     const int32_t* rows = route_row + t * k;   // wave-uniform addresses: scalar loads
     const float* ws = topk_w ? topk_w + t * k : nullptr;
-    for (int c0 = lane; c0 < pieces_per_row; c0 += kWave * CP) {
+    if (c_end < 0) c_end = pieces_per_row;
+    for (int c0 = c_begin + lane; c0 < c_end; c0 += kWave * CP) {
         float acc[CP][8];
 #pragma unroll
         for (int u = 0; u < CP; ++u)
@@ -41,7 +45,7 @@ __device__ __forceinline__ void combine_token(const uint4* __restrict__ y, const
                     const int c = c0 + u * kWave;
                     // each y row is read by exactly one token: streaming (non-temporal) loads
                     u32x4_t r_ = {0u, 0u, 0u, 0u};
-                    if (ok && c < pieces_per_row)
+                    if (ok && c < c_end)
                         r_ = __builtin_nontemporal_load((const u32x4_t*)(y + (int64_t)row * pieces_per_row + c));
                     v[u][jj] = make_uint4(r_[0], r_[1], r_[2], r_[3]);
                 }
@@ -61,7 +65,7 @@ __device__ __forceinline__ void combine_token(const uint4* __restrict__ y, const
 #pragma unroll
         for (int u = 0; u < CP; ++u) {
             const int c = c0 + u * kWave;
-            if (c < pieces_per_row) {
+            if (c < c_end) {
                 uint4 o;
                 o.x = pack_bf16x2(acc[u][0], acc[u][1]);
                 o.y = pack_bf16x2(acc[u][2], acc[u][3]);

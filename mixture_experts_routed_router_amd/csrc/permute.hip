@@ -21,6 +21,7 @@
 //               r / k; offsets are published and pad rows get row_token = -1
 //   4. gather:  x_perm[p] = x[row_token[p]] (zero row if -1), written token-major:
 //               each token's row is read once and stored to its k rows
+#include <algorithm>
 #include <mutex>
 
 #include "permute_core.hpp"
@@ -256,6 +257,146 @@ __global__ __launch_bounds__(kCopyThreads) void permute_copy_token_pairs_kernel(
 
 int64_t permute_chunks(int64_t R) { return (R + kChunk - 1) / kChunk; }
 
+// The permute of a small batch in one launch (at most kSmallRoutes routes, a
+// layout bound of at most kSmallRows rows), where the four launches of the split
+// path would cost more than their work. Every workgroup builds the whole layout
+// in its own LDS with the split path's own steps -- per-chunk histograms
+// (hist_chunk), the scan over chunks, padded_offsets and the stable scatter
+// (scatter_chunk) -- so the results are the same bits. Workgroup 0 then
+// publishes counts, offsets, route_row and the used rows of row_token, every
+// workgroup writes row_token = -1 on its share of the rows from offsets[E] to
+// P_max, and gathers its share of the used layout rows (TILED: row pairs, as
+// permute_copy_pairs_kernel does) from row_token in LDS. Nothing is read from
+// another workgroup, so no workgroup waits on another.
+constexpr int64_t kSmallRoutes = 2048;
+constexpr int64_t kSmallRows = 8192;
+constexpr int kSmallThreads = 256;
+constexpr int kSmallWaves = kSmallThreads / kWave;
+constexpr size_t kSmallLdsBytes = 64 << 10;
+
+static size_t small_permute_lds_bytes(int64_t R, int E, int64_t rows_cap) {
+    const int64_t nchunks = (R + kChunk - 1) / kChunk;
+    // hist [nchunks][E], cur [4][E], off [E + 1], wtot [4], cnt [E], route_row [R], row_token [rows_cap]
+    return (size_t)(nchunks * E + kSmallWaves * E + (E + 1) + 4 + E + R + rows_cap) * sizeof(int32_t);
+}
+
+static bool use_small_permute(int64_t R, int E, int64_t rows_cap) {
+    return R > 0 && R <= kSmallRoutes && rows_cap <= kSmallRows &&
+           small_permute_lds_bytes(R, E, rows_cap) <= kSmallLdsBytes;
+}
+
+template <bool TILED>
+__global__ __launch_bounds__(kSmallThreads) void permute_small_kernel(
+    const uint4* __restrict__ x, const int32_t* __restrict__ topk_idx, int64_t R, int E, int k, int align,
+    int64_t P_max, int rows_cap, int ppr, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ route_row, int32_t* __restrict__ row_token, uint4* __restrict__ x_perm) {
+    MOE_DEBUG_GUARD();
+    extern __shared__ int32_t lds_small[];
+    const int nchunks = (int)((R + kChunk - 1) / kChunk);
+    int32_t* hist = lds_small;               // [nchunks][E]
+    int32_t* cur = hist + nchunks * E;       // [kSmallWaves][E], per wave
+    int32_t* off = cur + kSmallWaves * E;    // [E + 1]
+    int32_t* wtot = off + E + 1;             // [4]
+    int32_t* cnt = wtot + 4;                 // [E]
+    int32_t* rrow = cnt + E;                 // [R]
+    int32_t* rtok = rrow + R;                // [rows_cap]
+    const int tid = threadIdx.x, wave = tid / kWave, lane = lane_id();
+
+    // 1. per-chunk histograms; every row starts as a pad row
+    for (int c = wave; c < nchunks; c += kSmallWaves) hist_chunk(topk_idx, R, E, c, cur + wave * E, hist + c * E);
+    for (int p = tid; p < rows_cap; p += kSmallThreads) rtok[p] = -1;
+    __syncthreads();
+    // 2. per expert: its count, and each chunk's routes to it in earlier chunks
+    for (int e = tid; e < E; e += kSmallThreads) {
+        int32_t run = 0;
+        for (int c = 0; c < nchunks; ++c) {
+            const int32_t v = hist[c * E + e];
+            hist[c * E + e] = run;
+            run += v;
+        }
+        cnt[e] = run;
+    }
+    __syncthreads();
+    // 3. the padded offsets (two barriers inside)
+    padded_offsets(cnt, E, align, off, wtot);
+    // 4. the stable scatter, into LDS
+    for (int c = wave; c < nchunks; c += kSmallWaves)
+        scatter_chunk<kSteps>(topk_idx, R, E, k, c, hist, off, cur + wave * E, rrow, rtok, (int)kChunk);
+    __syncthreads();
+    const int64_t used = off[E];
+
+    // 5. publish the layout
+    if (blockIdx.x == 0) {
+        for (int e = tid; e <= E; e += kSmallThreads) {
+            offsets[e] = off[e];
+            if (e < E) counts[e] = cnt[e];
+        }
+        for (int64_t r = tid; r < R; r += kSmallThreads) route_row[r] = rrow[r];
+        for (int64_t p = tid; p < used; p += kSmallThreads) row_token[p] = rtok[p];
+    }
+    for (int64_t p = used + (int64_t)blockIdx.x * kSmallThreads + tid; p < P_max;
+         p += (int64_t)gridDim.x * kSmallThreads)
+        row_token[p] = -1;
+    if (!x_perm) return;  // the layout only
+
+    // 6. the gather: one wavefront per slice of kWave * kCopyUnroll 16-byte slots
+    // of a layout row (TILED: of a row pair), all of its loads in flight at once
+    const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+    const int n = TILED ? 2 * ppr : ppr;  // 16-byte slots per row (pair)
+    const int slices = (n + kWave * kCopyUnroll - 1) / (kWave * kCopyUnroll);
+    const int64_t units = (TILED ? (used + 1) / 2 : used) * slices;
+    for (int64_t w = (int64_t)blockIdx.x * kSmallWaves + wave; w < units; w += (int64_t)gridDim.x * kSmallWaves) {
+        const int64_t q = w / slices;
+        const int i0 = (int)(w - q * slices) * kWave * kCopyUnroll;
+        const int64_t p0 = TILED ? 2 * q : q;
+        const int32_t t0 = rtok[p0];
+        const int32_t t1 = TILED && p0 + 1 < used ? rtok[p0 + 1] : -1;
+        const uint4* src0 = x + (int64_t)(t0 < 0 ? 0 : t0) * ppr;
+        const uint4* src1 = x + (int64_t)(t1 < 0 ? 0 : t1) * ppr;
+        uint4* dst = x_perm + q * n;
+        {
+            uint4 v[kCopyUnroll];
+#pragma unroll
+            for (int u = 0; u < kCopyUnroll; ++u) {
+                const int i = i0 + u * kWave + lane;
+                // tiled: slot i holds piece (i/8)*4 + i%4 of the pair's row (i/4)%2
+                const bool second = TILED && ((i >> 2) & 1);
+                const int c = TILED ? (((i >> 3) << 2) | (i & 3)) : i;
+                const int32_t t = second ? t1 : t0;
+                v[u] = z;
+                if (i < n && t >= 0) v[u] = *((second ? src1 : src0) + c);
+            }
+#pragma unroll
+            for (int u = 0; u < kCopyUnroll; ++u) {
+                const int i = i0 + u * kWave + lane;
+                if (i < n) dst[i] = v[u];
+            }
+        }
+    }
+}
+
+static hipError_t launch_permute_small(const uint16_t* x, const int32_t* topk_idx, int64_t R, int H, int E, int k,
+                                       int align, int64_t P_max, int64_t rows_cap, int32_t* counts,
+                                       int32_t* offsets, int32_t* route_row, int32_t* row_token, uint16_t* x_perm,
+                                       bool tiled, hipStream_t stream) {
+    const int ppr = H / 8;
+    const int n = tiled ? 2 * ppr : ppr;
+    const int64_t slices = (n + kWave * kCopyUnroll - 1) / (kWave * kCopyUnroll);
+    const int64_t units = x_perm ? (tiled ? (rows_cap + 1) / 2 : rows_cap) * slices : 0;
+    // one wavefront per gather unit, up to 1024 workgroups; at least one (it publishes the layout)
+    const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>(1024, (units + kSmallWaves - 1) / kSmallWaves));
+    const size_t lds = small_permute_lds_bytes(R, E, rows_cap);
+    auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, dim3((unsigned)blocks), dim3(kSmallThreads), lds, stream, (const uint4*)x, topk_idx,
+                           R, E, k, align, P_max, (int)rows_cap, ppr, counts, offsets, route_row, row_token,
+                           (uint4*)x_perm);
+    };
+    if (tiled) go(permute_small_kernel<true>);
+    else go(permute_small_kernel<false>);
+    return hipGetLastError();
+}
+
+
 hipError_t launch_permute_copy(const uint16_t* x, int64_t T, int H, int E, int k, int64_t P_max,
                                const int32_t* counts, const int32_t* offsets, const int32_t* route_row,
                                const int32_t* row_token, uint16_t* x_perm, bool tiled, hipStream_t stream);
@@ -270,6 +411,10 @@ hipError_t launch_permute(const uint16_t* x, const int32_t* topk_idx, int64_t T,
                           int32_t* route_row, int32_t* row_token, uint16_t* x_perm,
                           void* workspace, bool tiled, hipStream_t stream) {
     const int64_t R = T * k;
+    const int64_t rows_cap = R + (int64_t)E * (align - 1);  // no layout is longer
+    if (use_small_permute(R, E, rows_cap))
+        return launch_permute_small(x, topk_idx, R, H, E, k, align, P_max, rows_cap, counts, offsets, route_row,
+                                    row_token, x_perm, tiled, stream);
     const int64_t nchunks = permute_chunks(R);
     int32_t* hist = (int32_t*)workspace;
     const size_t lds = 4 * (size_t)E * sizeof(int32_t);

@@ -92,6 +92,11 @@ PERMUTE_CASES = [
     ("E1", 50, 64, 1, 1, 32, "gauss"),
     ("T1", 1, 192, 8, 2, 32, "gauss"),
     ("several_chunks", 5000, 64, 128, 8, 32, "gauss"),
+    # at most 2048 routes and 8192 layout rows: the one-launch permute; just past it, the split one
+    ("one_launch_2048_routes", 256, 128, 64, 8, 32, "gauss"),
+    ("split_2056_routes", 257, 128, 64, 8, 32, "gauss"),
+    ("one_launch_E1024", 100, 64, 1024, 2, 4, "gauss"),
+    ("one_launch_align1_odd_rows", 77, 128, 8, 3, 1, "gauss"),
     # a layout above 512 MiB (266112 rows x 4 KB): the gather's non-temporal-store copy
     ("nt_stores_1GiB_layout", 32768, 2048, 128, 8, 32, "gauss"),
 ]
