@@ -142,64 +142,27 @@ __global__ __launch_bounds__(kCopyThreads) void permute_copy_rows_kernel(
     }
 }
 
-// The gather into the row-pair tiled layout (tiled.hip), pair-major: one
-// wavefront per pair of layout rows (2q, 2q+1). The pair's tiled block run is 2H
-// contiguous elements in which 16-byte slot i holds piece (i/8)*4 + i%4 of row
-// 2q + (i/4)%2, so each store instruction writes 1 KB of whole 128-byte lines;
-// the two token rows (row_token, -1: zeros) are read 512 contiguous bytes at a
-// time. Every pair below offsets[E] is written whole, pad rows included (the
-// pair holding row offsets[E] - 1 gets a zero second row when offsets[E] is
-// odd); pairs past it are not touched. Token rows are read once per route here
-// (k times per token) -- from the caches, as x is far smaller than the layout.
-template <bool NT>
-__global__ __launch_bounds__(kCopyThreads) void permute_copy_pairs_kernel(
-    const uint4* __restrict__ x, const int32_t* __restrict__ row_token, const int32_t* __restrict__ offsets,
-    int E, int ppr, int64_t npairs, uint4* __restrict__ x_perm) {
-    MOE_DEBUG_GUARD();
-    const int lane = lane_id();
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int64_t q = (int64_t)blockIdx.x * kCopyWaves + wave;
-    if (q >= npairs) return;
-    const int64_t used = offsets[E];
-    if (2 * q >= used) return;
-    const int32_t t0 = __builtin_amdgcn_readfirstlane(row_token[2 * q]);
-    const int32_t t1 = __builtin_amdgcn_readfirstlane(row_token[2 * q + 1]);
-    const uint4* src0 = x + (int64_t)(t0 < 0 ? 0 : t0) * ppr;
-    const uint4* src1 = x + (int64_t)(t1 < 0 ? 0 : t1) * ppr;
-    uint4* dst = x_perm + q * 2 * ppr;
-    const uint4 z = make_uint4(0u, 0u, 0u, 0u);
-    const int n = 2 * ppr;  // 16-byte slots of the pair
-    for (int i0 = 0; i0 < n; i0 += kWave * kCopyUnroll) {
-        uint4 v[kCopyUnroll];
-#pragma unroll
-        for (int u = 0; u < kCopyUnroll; ++u) {
-            const int i = i0 + u * kWave + lane;
-            const bool second = (i >> 2) & 1;
-            const int c = ((i >> 3) << 2) | (i & 3);
-            const int32_t t = second ? t1 : t0;
-            v[u] = z;
-            if (i < n && t >= 0) v[u] = *((second ? src1 : src0) + c);
-        }
-#pragma unroll
-        for (int u = 0; u < kCopyUnroll; ++u) {
-            const int i = i0 + u * kWave + lane;
-            if (i < n) store_piece<NT>(dst + i, v[u]);
-        }
-    }
-}
-
-// The gather into the tiled layout for layouts past the Infinity Cache (the
-// non-temporal case), token-major: one wavefront per token, and per route row p
-// the wavefront writes p's whole pair -- its own row and the partner row p ^ 1,
-// read through row_token (a pad or past-the-end partner: zeros) -- unless p is
-// odd and its partner is a routed row, whose token writes the pair instead. So
-// every pair is written by exactly one wavefront, 1 KB of whole lines per store,
-// and a token row is read once for itself plus once per pair it shares with an
-// earlier route of the same expert (a nearby token). Pairs of two pad rows --
-// inside one segment's padding, or its last pad row and row offsets[E] -- are
-// zeroed by the last E workgroups, each pair by its even row. Measured on the
-// 1 GB skewed layout: 297 us against 326 for the pair-major copy; on smaller
-// layouts the pair-major copy is faster (94 vs 99 us at 8192 tokens).
+// The gather into the row-pair tiled layout (tiled.hip), token-major: one
+// wavefront per token, and per route row p the wavefront writes p's whole pair
+// -- its own row and the partner row p ^ 1, read through row_token (a pad or
+// past-the-end partner: zeros) -- unless p is odd and its partner is a routed
+// row, whose token writes the pair instead. So every pair is written by exactly
+// one wavefront, 1 KB of whole 128-byte lines per store. In a pair's 2H
+// contiguous elements 16-byte slot i holds piece (i/8)*4 + i%4 of row
+// 2q + (i/4)%2. Pairs of two pad rows -- inside one segment's padding, or its
+// last pad row and row offsets[E] -- are zeroed by the last E workgroups, each
+// pair by its even row.
+//
+// Token blocks are dealt to the XCDs in contiguous runs (workgroup b runs on
+// XCD b % 8), so the tokens in flight on one XCD are neighbours: a pair's
+// partner is usually a nearby token of the same expert, whose row this XCD's
+// L2 has just read. Timed alone, back to back (x resident in the Infinity
+// Cache), the whole permute went from 297 to 248 us on the skewed layer's 1 GB
+// layout, 99 -> 86 us at the bench-sized layer and 153 -> 136 us at 512
+// experts against plain token order (a pair-major copy, one wavefront per pair
+// reading both token rows, took 326, 94 and 147 us). Inside the layer, where x
+// comes from HBM, the skewed permute is bound by its HBM writes (290 -> 287 us);
+// the other two gain 4 and 7 us over the pair-major copy.
 template <bool NT>
 __global__ __launch_bounds__(kCopyThreads) void permute_copy_token_pairs_kernel(
     const uint4* __restrict__ x, const int32_t* __restrict__ route_row, const int32_t* __restrict__ row_token,
@@ -222,7 +185,10 @@ __global__ __launch_bounds__(kCopyThreads) void permute_copy_token_pairs_kernel(
         return;
     }
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    const int64_t t = (int64_t)blockIdx.x * kCopyWaves + wave;
+    int64_t tb = blockIdx.x;  // token block: XCD-contiguous runs over the first whole multiple of 8 blocks
+    const int64_t nb8 = token_blocks / 8 * 8;
+    if (tb < nb8) tb = (tb % 8) * (nb8 / 8) + tb / 8;
+    const int64_t t = tb * kCopyWaves + wave;
     if (t >= T) return;
     const uint4* src = x + t * ppr;
     for (int j = 0; j < k; ++j) {
@@ -266,7 +232,7 @@ int64_t permute_chunks(int64_t R) { return (R + kChunk - 1) / kChunk; }
 // publishes counts, offsets, route_row and the used rows of row_token, every
 // workgroup writes row_token = -1 on its share of the rows from offsets[E] to
 // P_max, and gathers its share of the used layout rows (TILED: row pairs, as
-// permute_copy_pairs_kernel does) from row_token in LDS. Nothing is read from
+// the split path's copy lays them out) from row_token in LDS. Nothing is read from
 // another workgroup, so no workgroup waits on another.
 constexpr int64_t kSmallRoutes = 2048;
 constexpr int64_t kSmallRows = 8192;
@@ -482,19 +448,14 @@ hipError_t launch_permute_copy(const uint16_t* x, int64_t T, int H, int E, int k
     const int64_t token_blocks = (T + kCopyWaves - 1) / kCopyWaves;
     const dim3 grid((unsigned)(token_blocks + E));
     const bool nt = P_max * (int64_t)H * 2 > kStreamingLayoutBytes;
-    if (tiled && nt) {
-        // token-major, whole pairs (P_max is even); then the pad-pair workgroups
-        hipLaunchKernelGGL(permute_copy_token_pairs_kernel<true>, grid, dim3(kCopyThreads), 0, stream,
-                           (const uint4*)x, route_row, row_token, counts, offsets, T, k, ppr, token_blocks,
-                           (uint4*)x_perm);
-        return hipGetLastError();
-    }
     if (tiled) {
-        // one wavefront per row pair (P_max is even)
-        const int64_t npairs = P_max / 2;
-        const dim3 pgrid((unsigned)((npairs + kCopyWaves - 1) / kCopyWaves));
-        hipLaunchKernelGGL(permute_copy_pairs_kernel<false>, pgrid, dim3(kCopyThreads), 0, stream,
-                           (const uint4*)x, row_token, offsets, E, ppr, npairs, (uint4*)x_perm);
+        // token-major, whole pairs (P_max is even); then the pad-pair workgroups
+        auto go_pairs = [&](auto kern) {
+            hipLaunchKernelGGL(kern, grid, dim3(kCopyThreads), 0, stream, (const uint4*)x, route_row, row_token,
+                               counts, offsets, T, k, ppr, token_blocks, (uint4*)x_perm);
+        };
+        if (nt) go_pairs(permute_copy_token_pairs_kernel<true>);
+        else go_pairs(permute_copy_token_pairs_kernel<false>);
         return hipGetLastError();
     }
     auto go = [&](auto kern) {
