@@ -23,8 +23,10 @@ namespace moe {
 
 constexpr int kNoExpert = 0x7fffffff;  // empty list slot (value -inf)
 
+// Bitwise, not short-circuit: the lanes' comparisons combine as masks instead of
+// as branches around each list slot.
 __device__ __forceinline__ bool ranks_before(float va, int ia, float vb, int ib) {
-    return va > vb || (va == vb && ia < ib);
+    return (va > vb) | ((va == vb) & (ia < ib));
 }
 
 template <int CTRL>
@@ -44,10 +46,8 @@ __device__ __forceinline__ void insert_sorted(float (&lv)[KL], int (&li)[KL], fl
     bool before_prev = ranks_before(v, e, lv[0], li[0]);
     float pv = lv[0];
     int pi = li[0];
-    if (before_prev) {
-        lv[0] = v;
-        li[0] = e;
-    }
+    lv[0] = before_prev ? v : pv;
+    li[0] = before_prev ? e : pi;
 #pragma unroll
     for (int j = 1; j < KL; ++j) {
         const bool before = ranks_before(v, e, lv[j], li[j]);
