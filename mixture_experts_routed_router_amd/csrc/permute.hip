@@ -20,7 +20,12 @@
 //               among earlier equal ids (stable in r), row_token[route_row[r]] =
 //               r / k; offsets are published and pad rows get row_token = -1
 //   4. gather:  x_perm[p] = x[row_token[p]] (zero row if -1), written token-major:
-//               each token's row is read once and stored to its k rows
+//               each token's row is read once and stored to its k rows (the
+//               row-pair tiled layout: each route row's whole pair, see
+//               permute_copy_token_pairs_kernel)
+//
+// A small batch runs all four steps in one launch (permute_small_kernel), each
+// workgroup building the layout in its own LDS with the same device functions.
 #include <algorithm>
 #include <mutex>
 
