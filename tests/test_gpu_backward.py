@@ -203,6 +203,9 @@ WG_CASES = [
      32, 512, 256),
     # more than 256 experts: no ranking, experts taken by id
     ("e300_by_id", _many_counts(300, 40, 46), 32, 512, 128),
+    # one expert with the skewed layer's hottest row count: a 1008-chunk k loop
+    # beside nearly empty experts
+    ("hot_expert_32k_rows", [32231, 5, 0, 300, 2], 32, 256, 256),
 ]
 
 

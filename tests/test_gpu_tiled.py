@@ -382,6 +382,9 @@ TRAIN_LAYERS = [
     # more than 256 experts (weight gradients take experts by id), most of them empty
     gen.MoEConfig("e300_mostly_empty", 200, 128, 300, 2, 64, 32, "gaussian"),
     gen.CONFIGS["qwen3_30b_a3b"],
+    # the skewed layer at full size: a 32k-row expert's weight gradients, the
+    # non-temporal tiled gather
+    gen.CONFIGS["skewed_zipf"],
 ]
 
 
